@@ -1,0 +1,171 @@
+"""Jagged generalized dot-product attention, forward, in float64 (oracle).
+
+TEST INFRASTRUCTURE ONLY (see the package docstring for the page names).
+
+What is computed -- the plain definition, sample by sample and head by head:
+
+  Jagged inputs: values [sum(L), H, D] + int32 offsets [B+1]; no padding to the
+  maximum length ([GEM-T] "なぜLLM向けのインフラをそのまま使えないのか": padding wastes
+  up to half the compute; [GEM-R] "効率向上はモデルとシステムの協調設計から生まれた").
+
+  Three shapes share one definition ([GEM-T] same section: self-attention over
+  long histories with a short window, cross-attention with long queries and short
+  K/V, PMA with short queries and long K/V; [GEM-T] "Generalized Dot-Product
+  Attention（GDPA）": one kernel for all three).
+
+  For sample b and head h, with Q (Lq x D), K, V (Lk x D):
+    S = Q K^T / sqrt(D)
+    softmax:   O = softmax_rows(S restricted to the allowed keys) V
+    gelu_tanh: Q, K are RMS-normalised per token and head first (the QK-norm of
+               [GEM-T] GDPA section, which bounds the activation input), then
+               O = gelu_tanh(S) V / Lk   (no max, no row sum)
+  Block window ([GEM-T] "BlockAttention"; [GEM-S] "深いソフトウェア・ハードウェア
+  協調設計によるスケーラブルなアーキテクチャ": 64-token blocks, window a whole number
+  of blocks): query in block i sees every key of blocks i-W/64+1 .. i, blocks
+  counted from the sample's first token, the last block possibly partial.
+
+Readings where the pages are silent (each listed in the design notes):
+  * no causal mask inside a block or in full attention; window 0 = no window;
+  * scale 1/sqrt(D) for every variant, no bias or positional term;
+  * RMSNorm has unit weight and eps inside the square root (default 1e-6);
+  * Lk == 0 gives O == 0; Lq == 0 gives no rows.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+BLOCK = 64
+DEFAULT_EPS = 1e-6
+
+
+def gelu_tanh(x):
+    """0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))  -- the tanh form of GELU."""
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (x + 0.044715 * x ** 3)))
+
+
+def rms_normalise(x, eps: float = DEFAULT_EPS):
+    """Unit-weight RMSNorm over the last axis: x / sqrt(mean(x^2) + eps)."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+def block_window_allowed(lq: int, lk: int, window: int) -> np.ndarray:
+    """Boolean [lq, lk]: may query i attend key j?
+
+    window == 0: every key.  window > 0 (a multiple of 64): key block j//64 must
+    lie in [i//64 - window/64 + 1, i//64]."""
+    if window == 0:
+        return np.ones((lq, lk), dtype=bool)
+    if window % BLOCK:
+        raise ValueError("window must be a multiple of 64")
+    nb = window // BLOCK
+    qi = (np.arange(lq) // BLOCK)[:, None]
+    kj = (np.arange(lk) // BLOCK)[None, :]
+    return (kj <= qi) & (kj >= qi - nb + 1)
+
+
+def attention_dense(Q, K, V, act: str, window: int = 0, eps: float = DEFAULT_EPS):
+    """One (sample, head): Q [Lq,D], K, V [Lk,D] -> O [Lq,D] in float64."""
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    lq, d = Q.shape
+    lk = K.shape[0]
+    if lq == 0:
+        return np.zeros((0, d))
+    if lk == 0:
+        return np.zeros((lq, d))
+    if act == "softmax":
+        S = (Q @ K.T) / math.sqrt(d)
+        allowed = block_window_allowed(lq, lk, window)
+        S = np.where(allowed, S, -np.inf)
+        m = S.max(axis=1, keepdims=True)
+        P = np.exp(S - m)            # exp(-inf) = 0 for disallowed keys
+        P /= P.sum(axis=1, keepdims=True)
+        return P @ V
+    if act == "gelu_tanh":
+        if window:
+            raise ValueError("windowed GELU attention is not defined")
+        S = (rms_normalise(Q, eps) @ rms_normalise(K, eps).T) / math.sqrt(d)
+        return (gelu_tanh(S) @ V) / lk
+    raise ValueError(f"unknown activation {act!r}")
+
+
+def _check(q, k, v, q_offsets, kv_offsets, variant, act, window):
+    qo = np.asarray(q_offsets, dtype=np.int64)
+    ko = np.asarray(kv_offsets, dtype=np.int64)
+    if qo.ndim != 1 or ko.shape != qo.shape or qo[0] != 0 or ko[0] != 0:
+        raise ValueError("offsets must be [B+1] and start at 0")
+    if np.any(np.diff(qo) < 0) or np.any(np.diff(ko) < 0):
+        raise ValueError("offsets must be non-decreasing")
+    if qo[-1] != q.shape[0] or ko[-1] != k.shape[0] or k.shape != v.shape:
+        raise ValueError("offsets do not match the value tensors")
+    if variant not in ("self", "cross", "pma"):
+        raise ValueError(variant)
+    if variant == "self" and not np.array_equal(qo, ko):
+        raise ValueError("self-attention needs identical query and key offsets")
+    if window and (variant != "self" or act != "softmax"):
+        raise ValueError("a window applies to softmax self-attention only")
+    return qo, ko
+
+
+def gdpa_forward(q, k, v, q_offsets, kv_offsets, variant: str = "self", act: str = "softmax",
+                 window: int = 0, eps: float = DEFAULT_EPS) -> np.ndarray:
+    """q [Nq,H,D], k/v [Nk,H,D] (any float dtype) -> out float64 [Nq,H,D]."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    qo, ko = _check(q, k, v, q_offsets, kv_offsets, variant, act, window)
+    out = np.zeros(q.shape, dtype=np.float64)
+    for b in range(len(qo) - 1):
+        for h in range(q.shape[1]):
+            out[qo[b]:qo[b + 1], h, :] = attention_dense(
+                q[qo[b]:qo[b + 1], h, :], k[ko[b]:ko[b + 1], h, :], v[ko[b]:ko[b + 1], h, :],
+                act, window, eps)
+    return out
+
+
+def gdpa_rows(q, k, v, q_offsets, kv_offsets, rows, variant: str = "self", act: str = "softmax",
+              window: int = 0, eps: float = DEFAULT_EPS) -> np.ndarray:
+    """Selected output rows only: rows = iterable of (token index t, head h).
+    Returns float64 [len(rows), D]; row r is out[t, h, :] of gdpa_forward."""
+    q = np.asarray(q)
+    qo, ko = _check(q, k, v, q_offsets, kv_offsets, variant, act, window)
+    res = []
+    for t, h in rows:
+        b = int(np.searchsorted(qo, t, side="right") - 1)
+        i = t - qo[b]                                   # position inside the sample
+        Qs = np.asarray(q[qo[b]:qo[b + 1], h, :], dtype=np.float64)
+        Ks = np.asarray(k[ko[b]:ko[b + 1], h, :], dtype=np.float64)
+        Vs = np.asarray(v[ko[b]:ko[b + 1], h, :], dtype=np.float64)
+        lk = Ks.shape[0]
+        if lk == 0:
+            res.append(np.zeros(q.shape[2]))
+            continue
+        if act == "gelu_tanh":
+            Qs, Ks = rms_normalise(Qs[i:i + 1], eps), rms_normalise(Ks, eps)
+            s = (Qs @ Ks.T)[0] / math.sqrt(q.shape[2])
+            res.append(gelu_tanh(s) @ Vs / lk)
+            continue
+        allowed = block_window_allowed(Qs.shape[0], lk, window)[i]
+        s = (Ks @ Qs[i]) / math.sqrt(q.shape[2])
+        s = np.where(allowed, s, -np.inf)
+        p = np.exp(s - s.max())
+        res.append((p / p.sum()) @ Vs)
+    return np.array(res, dtype=np.float64).reshape(len(res), q.shape[2])
+
+
+def attended_pairs(q_offsets, kv_offsets, act: str = "softmax", window: int = 0) -> int:
+    """Number of (query, key) pairs that enter the output, per head:
+    sum over samples of the allowed-mask population (dense count)."""
+    qo = np.asarray(q_offsets, dtype=np.int64)
+    ko = np.asarray(kv_offsets, dtype=np.int64)
+    total = 0
+    for b in range(len(qo) - 1):
+        lq, lk = int(qo[b + 1] - qo[b]), int(ko[b + 1] - ko[b])
+        if lq and lk:
+            total += int(block_window_allowed(lq, lk, window).sum())
+    return total

@@ -1,0 +1,47 @@
+"""Work accounting for jagged attention (host side, counts only).
+
+Useful FLOPs count every (query, key) pair that enters the output once, at
+4*D FLOPs per pair per head (2*D for the score dot product, 2*D for the
+weighted sum of values); softmax/GELU/normalisation FLOPs and every padded or
+masked element are excluded.  Compulsory bytes read each input once and write
+the output once.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+BLOCK = 64
+
+
+def attended_pairs(lq, lk, window: int = 0) -> int:
+    """Pairs per head for samples with query lengths lq and key lengths lk."""
+    lq = np.asarray(lq, dtype=np.int64)
+    lk = np.asarray(lk, dtype=np.int64)
+    if window == 0:
+        return int(np.sum(lq * lk))
+    nb = window // BLOCK
+    total = 0
+    for L, K in zip(lq.tolist(), lk.tolist()):
+        if L == 0 or K == 0:
+            continue
+        for blk in range((L + BLOCK - 1) // BLOCK):
+            rows = min(L, BLOCK * (blk + 1)) - BLOCK * blk
+            k0 = BLOCK * max(0, blk - nb + 1)
+            k1 = min(K, BLOCK * (blk + 1))
+            total += rows * max(0, k1 - k0)
+    return total
+
+
+def useful_flops(lq, lk, H: int, D: int, window: int = 0) -> int:
+    return 4 * D * H * attended_pairs(lq, lk, window)
+
+
+def compulsory_bytes(total_q: int, total_kv: int, H: int, D: int, in_bytes: float,
+                     out_bytes: int, mx_scales: bool = False) -> int:
+    """Q read + K,V read + O written, each once (MX: plus one scale byte per 32 elements)."""
+    elems_q = total_q * H * D
+    elems_kv = total_kv * H * D
+    b = (elems_q + 2 * elems_kv) * in_bytes + elems_q * out_bytes
+    if mx_scales:
+        b += (elems_q + 2 * elems_kv) // 32
+    return int(b)
