@@ -1,0 +1,128 @@
+/*
+ * jagged_attn.h -- C ABI of the MI355X (gfx950) jagged generalized dot-product
+ * attention forward library (libjagged_attn.so).
+ *
+ * What it computes.  For every sample b and head h of a jagged batch, with
+ * Q (Lq x D) and K, V (Lk x D) the sample's rows of that head:
+ *   softmax:    O = softmax(Q K^T / sqrt(D)) V over the allowed keys;
+ *   gelu_tanh:  O = gelu_tanh(rms(Q) rms(K)^T / sqrt(D)) V / Lk, where rms()
+ *               is unit-weight RMSNorm per token and head (the QK-norm that
+ *               bounds the activation input) and there is no max and no sum.
+ * Sources: techfeed.io summary of "GEM Training: How Meta Doubled the
+ * Efficiency of Its LLM-Scale Ads Foundation Model", sections "なぜLLM向けの
+ * インフラをそのまま使えないのか" (jagged histories; the three shapes: self with a
+ * short window, cross with long Q / short K,V, PMA with short Q / long K,V),
+ * "Generalized Dot-Product Attention（GDPA）" (one kernel for the three shapes,
+ * GELU with QK-norm), "BlockAttention" (fixed 64-token blocks, window a whole
+ * number of blocks) and "MXFP8による超低精度トレーニング" (microscaling FP8
+ * attention); remio.ai "Meta Engineering、広告モデルの拡大とともにGEMの学習効率を
+ * 2倍にしたと説明", section "効率向上はモデルとシステムの協調設計から生まれた" (GDPA
+ * replaces softmax by other activations).
+ *
+ * Readings where the pages are silent: no causal mask (window 0 = full
+ * attention over the sample's keys); scale 1/sqrt(D) everywhere; a window W>0
+ * lets a query in 64-token block i see every key of blocks i-W/64+1 .. i, with
+ * blocks counted from the sample's first token; Lk == 0 gives O == 0.
+ *
+ * Layouts (all device memory, row-major, contiguous):
+ *   q   [total_q , H, D]     k, v [total_kv, H, D]     out [total_q, H, D]
+ *   element type by io->dtype: JA_F32 -> float in and out;
+ *   JA_BF16 -> bfloat16 in and out; JA_MXFP8_E4M3 -> e4m3 ("fn") bytes in,
+ *   with E8M0 scale bytes q_scale/k_scale/v_scale [rows, H, D/32] (one scale
+ *   per 32 contiguous elements along D), bfloat16 out.
+ *   q_offsets, kv_offsets: device int32 [B+1], offsets[0] == 0, non-decreasing,
+ *   offsets[B] == total_q / total_kv.  Sample b owns rows [off[b], off[b+1]).
+ *   JA_SELF needs q_offsets and kv_offsets to hold the same values (the same
+ *   pointer may be passed twice).  Buffers need 16-byte alignment.
+ *
+ * Ownership.  The caller owns every buffer, including the workspace.  The
+ * library allocates nothing inside jagged_attn_fwd and keeps only a per-device
+ * cache of device properties.  Calls on different streams with different
+ * workspaces and outputs are independent; calls sharing a workspace must be
+ * ordered on one stream.
+ *
+ * Errors.  Every entry point returns JA_OK (0) or a negative ja_status.
+ * Argument errors are detected on the host before anything is launched.
+ * jagged_attn_fwd is asynchronous on io->stream and never synchronises; the
+ * offsets are validated on the device, which writes a status word into the
+ * workspace and then skips all work (out is left unspecified); read it with
+ * jagged_attn_check.  Output contents are unspecified whenever the status is
+ * not JA_OK.
+ */
+#ifndef JAGGED_ATTN_H
+#define JAGGED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum ja_variant {
+  JA_SELF = 0,  /* q and kv share offsets; optional block window            */
+  JA_CROSS = 1, /* long queries, short keys/values: work split by q tiles    */
+  JA_PMA = 2    /* short queries (<=32 per sample), long keys/values: work
+                   split by key chunks, partial results merged on device      */
+};
+
+enum ja_act {
+  JA_SOFTMAX = 0,   /* softmax over the allowed keys                         */
+  JA_GELU_TANH = 1  /* QK-RMSNorm, gelu_tanh score, 1/Lk normalisation        */
+};
+
+enum ja_dtype { JA_F32 = 0, JA_BF16 = 1, JA_MXFP8_E4M3 = 2 };
+
+enum ja_status {
+  JA_OK = 0,
+  JA_EINVAL = -1,       /* bad argument (null pointer, B<1, H<1, bad enum...)  */
+  JA_EUNSUPPORTED = -2, /* valid but not implemented (D not in {32,64,128},
+                           windowed GELU, window not a multiple of 64 ...)     */
+  JA_EWORKSPACE = -3,   /* workspace missing or smaller than required         */
+  JA_EHIP = -4,         /* a HIP runtime call or kernel launch failed         */
+  JA_EOFFSETS = -5      /* device found offsets that are not monotone, do not
+                           start at 0, do not end at total, or (JA_SELF) differ */
+};
+
+typedef struct ja_io {
+  int dtype;                 /* enum ja_dtype                                  */
+  const uint8_t *q_scale;    /* JA_MXFP8_E4M3 only: E8M0 [total_q , H, D/32]    */
+  const uint8_t *k_scale;    /*                     E8M0 [total_kv, H, D/32]    */
+  const uint8_t *v_scale;    /*                     E8M0 [total_kv, H, D/32]    */
+  void *workspace;           /* device memory, >= jagged_attn_workspace_size() */
+  size_t workspace_bytes;
+  void *stream;              /* hipStream_t to launch on; NULL = null stream    */
+  int32_t total_q;           /* rows of q/out  (= q_offsets[B])                 */
+  int32_t total_kv;          /* rows of k/v    (= kv_offsets[B])                */
+  float rms_eps;             /* JA_GELU_TANH: RMSNorm epsilon; <= 0 -> 1e-6     */
+} ja_io;
+
+/* The forward pass.  Arguments as described above; window is 0 (no window) or
+ * a positive multiple of 64 (JA_SELF + JA_SOFTMAX only). */
+int jagged_attn_fwd(const void *q, const void *k, const void *v,
+                    const int32_t *q_offsets, const int32_t *kv_offsets,
+                    int B, int H, int D, int variant, int act, int window,
+                    void *out, const ja_io *io);
+
+/* Bytes of workspace jagged_attn_fwd needs for these arguments (0 on invalid
+ * arguments).  Depends on the arguments only, not on the device. */
+size_t jagged_attn_workspace_size(int B, int H, int D, int variant, int act,
+                                  int window, int dtype, int32_t total_q,
+                                  int32_t total_kv);
+
+/* Synchronises `stream` (a hipStream_t or NULL) and returns the device status
+ * word the last jagged_attn_fwd on this workspace wrote (JA_OK or
+ * JA_EOFFSETS), or JA_EHIP / JA_EINVAL if it cannot be read. */
+int jagged_attn_check(const void *workspace, void *stream);
+
+/* Static description of a status code; never NULL. */
+const char *jagged_attn_strerror(int status);
+
+/* Library ABI version (major*100 + minor). */
+int jagged_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JAGGED_ATTN_H */

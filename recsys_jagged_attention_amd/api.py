@@ -1,0 +1,95 @@
+"""torch-tensor front end of the C ABI (argument marshalling only).
+
+``forward(q, k, v, q_offsets, kv_offsets, ...)`` checks dtypes/devices/shapes,
+passes ``data_ptr()`` values and the current HIP stream to
+``jagged_attn_fwd`` and returns ``out``.  PyTorch provides device memory and
+streams; all attention arithmetic runs in libjagged_attn's kernels.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+_IN_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "mxfp8": torch.uint8}
+
+
+class Workspace:
+    """A reusable device workspace (grown on demand, never shrunk)."""
+
+    def __init__(self, device=None):
+        self.device = torch.device(device if device is not None else "cuda")
+        self.buf: Optional[torch.Tensor] = None
+
+    def get(self, nbytes: int) -> torch.Tensor:
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        return self.buf
+
+
+def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+            q_offsets: torch.Tensor, kv_offsets: torch.Tensor,
+            variant: str = "self", act: str = "softmax", window: int = 0,
+            dtype: str = "bf16", scales=None, out: Optional[torch.Tensor] = None,
+            workspace: Optional[Workspace] = None, rms_eps: float = 1e-6,
+            stream: Optional[torch.cuda.Stream] = None, check: bool = False) -> torch.Tensor:
+    """Jagged GDPA forward.  q [Nq,H,D], k/v [Nk,H,D] on one GPU; offsets int32 [B+1].
+
+    dtype "f32"/"bf16": q/k/v of that dtype; "mxfp8": uint8 e4m3 codes with
+    ``scales=(q_scale, k_scale, v_scale)`` uint8 [rows,H,D/32].  Output is
+    float32 for "f32", else bfloat16.  With ``check=True`` the call
+    synchronises and raises on a device-side status (e.g. bad offsets)."""
+    if dtype not in _IN_DTYPES:
+        raise ValueError(f"dtype must be one of {list(_IN_DTYPES)}")
+    want = _IN_DTYPES[dtype]
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != want or not t.is_cuda or not t.is_contiguous() or t.dim() != 3:
+            raise ValueError(f"{name} must be a contiguous 3-D {want} CUDA tensor")
+    for name, t in (("q_offsets", q_offsets), ("kv_offsets", kv_offsets)):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous() or t.dim() != 1:
+            raise ValueError(f"{name} must be a contiguous 1-D int32 CUDA tensor")
+    Nq, H, D = q.shape
+    Nk = k.shape[0]
+    if k.shape != (Nk, H, D) or v.shape != k.shape:
+        raise ValueError("k and v must be [Nk, H, D] with q's H and D")
+    B = q_offsets.numel() - 1
+    if kv_offsets.numel() != B + 1:
+        raise ValueError("q_offsets and kv_offsets must both have B+1 entries")
+    out_dtype = torch.float32 if dtype == "f32" else torch.bfloat16
+    if out is None:
+        out = torch.empty((Nq, H, D), dtype=out_dtype, device=q.device)
+    elif out.shape != (Nq, H, D) or out.dtype != out_dtype or not out.is_contiguous():
+        raise ValueError("out has the wrong shape or dtype")
+    v_id, a_id, d_id = _lib.VARIANTS[variant], _lib.ACTS[act], _lib.DTYPES[dtype]
+    nbytes = _lib.jagged_attn_workspace_size(B, H, D, v_id, a_id, window, d_id, Nq, Nk)
+    if nbytes == 0:
+        # invalid or unsupported arguments: let the library report which
+        nbytes = 256
+    ws = (workspace or Workspace(q.device)).get(nbytes)
+    io = _lib.JaIo()
+    io.dtype = d_id
+    if dtype == "mxfp8":
+        if scales is None or len(scales) != 3:
+            raise ValueError("mxfp8 needs scales=(q_scale, k_scale, v_scale)")
+        for name, s, rows in zip("qkv", scales, (Nq, Nk, Nk)):
+            if s.dtype != torch.uint8 or not s.is_cuda or s.shape != (rows, H, D // 32) or not s.is_contiguous():
+                raise ValueError(f"{name}_scale must be a contiguous uint8 [rows,H,D/32] CUDA tensor")
+        io.q_scale, io.k_scale, io.v_scale = (s.data_ptr() for s in scales)
+    io.workspace = ws.data_ptr()
+    io.workspace_bytes = ws.numel()
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    io.stream = st.cuda_stream
+    io.total_q = Nq
+    io.total_kv = Nk
+    io.rms_eps = rms_eps
+    status = _lib.jagged_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), q_offsets.data_ptr(),
+                                  kv_offsets.data_ptr(), B, H, D, v_id, a_id, window, out.data_ptr(), io)
+    if status != _lib.JA_OK:
+        raise _lib.JaggedAttnError(status, "jagged_attn_fwd")
+    if check:
+        status = _lib.jagged_attn_check(ws.data_ptr(), st.cuda_stream)
+        if status != _lib.JA_OK:
+            raise _lib.JaggedAttnError(status, "jagged_attn_check")
+    return out

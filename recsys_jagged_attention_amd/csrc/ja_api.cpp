@@ -1,0 +1,222 @@
+// C ABI of libjagged_attn: argument validation, schedule choice, workspace
+// layout and launches on the caller's stream.  No allocation, no host read
+// of the offsets, no synchronisation on the forward path.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+
+#include "ja_internal.h"
+#include "jagged_attn.h"
+
+namespace ja {
+hipError_t launch_plan(const PlanArgs& a, hipStream_t st);
+hipError_t launch_attn_mfma(int D, int in, int shape, int act, const AttnArgs& a, int grid, hipStream_t st);
+hipError_t launch_combine(int D, const CombineArgs& a, hipStream_t st);
+hipError_t launch_attn_f32(int D, int act, bool window, const AttnArgs& a, int grid, hipStream_t st);
+
+namespace {
+
+constexpr int kShapeQTiled = 0, kShapeWindow = 1, kShapeKvSplit = 2, kShapeF32 = 3;
+constexpr int kMaxGrid = 1 << 20;
+
+struct Plan {
+  int shape;
+  int bm;
+  int kvc;
+  WsLayout ws;
+};
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Key chunk for the key-split shape: about 2048 work items per call, a
+// power of two between 512 and 8192 keys (long samples are split, short ones
+// are not), so skewed K/V lengths still spread over every CU.
+int choose_kvc(int H, int32_t total_kv) {
+  const int64_t target = cdiv(int64_t(H) * total_kv, 2048);
+  int kvc = 512;
+  while (kvc < target && kvc < 8192) kvc <<= 1;
+  return kvc;
+}
+
+int validate(int B, int H, int D, int variant, int act, int window, int dtype, int32_t total_q,
+             int32_t total_kv) {
+  if (B < 1 || H < 1 || total_q < 0 || total_kv < 0) return JA_EINVAL;
+  if (variant < JA_SELF || variant > JA_PMA) return JA_EINVAL;
+  if (act < JA_SOFTMAX || act > JA_GELU_TANH) return JA_EINVAL;
+  if (dtype < JA_F32 || dtype > JA_MXFP8_E4M3) return JA_EINVAL;
+  if (window < 0) return JA_EINVAL;
+  if (variant == JA_SELF && total_q != total_kv) return JA_EINVAL;
+  if (window > 0 && variant != JA_SELF) return JA_EINVAL;
+  if (D != 32 && D != 64 && D != 128) return JA_EUNSUPPORTED;
+  if (window > 0 && (window % kBlock != 0 || act != JA_SOFTMAX)) return JA_EUNSUPPORTED;
+  if (int64_t(B) * H > (int64_t(1) << 30) || H > 4096) return JA_EUNSUPPORTED;
+  return JA_OK;
+}
+
+Plan make_plan(int B, int H, int D, int variant, int window, int dtype, int32_t total_q,
+               int32_t total_kv) {
+  Plan p{};
+  if (dtype == JA_F32) {
+    p.shape = kShapeF32;
+    p.bm = 64;
+  } else if (window > 0) {
+    p.shape = kShapeWindow;
+    p.bm = 64;
+  } else if (variant == JA_PMA) {
+    p.shape = kShapeKvSplit;
+    p.bm = kPmaRows;
+    p.kvc = choose_kvc(H, total_kv);
+  } else {
+    p.shape = kShapeQTiled;
+    p.bm = 128;
+  }
+  WsLayout& w = p.ws;
+  w.max_items = int64_t(H) * (cdiv(total_q, p.bm) + B);
+  w.max_slots = 0;
+  if (p.kvc > 0) {
+    w.max_slots = int64_t(H) * (cdiv(total_kv, p.kvc) + B);
+    w.max_items += w.max_slots;
+  }
+  size_t off = align256(sizeof(WsHeader));
+  w.nsplit_off = off;
+  off = align256(off + sizeof(int32_t) * size_t(B));
+  w.pbase_off = off;
+  off = align256(off + sizeof(int32_t) * size_t(B));
+  w.items_off = off;
+  off = align256(off + sizeof(int4) * size_t(w.max_items));
+  w.part_o_off = off;
+  off = align256(off + sizeof(float) * size_t(w.max_slots) * kPmaRows * D);
+  w.part_ml_off = off;
+  off = align256(off + sizeof(float2) * size_t(w.max_slots) * kPmaRows);
+  w.total = off;
+  return p;
+}
+
+}  // namespace
+}  // namespace ja
+
+using namespace ja;
+
+extern "C" {
+
+int jagged_attn_version(void) { return 100; }
+
+const char* jagged_attn_strerror(int status) {
+  switch (status) {
+    case JA_OK: return "ok";
+    case JA_EINVAL: return "invalid argument";
+    case JA_EUNSUPPORTED: return "unsupported argument combination";
+    case JA_EWORKSPACE: return "workspace missing or too small";
+    case JA_EHIP: return "HIP runtime error";
+    case JA_EOFFSETS: return "invalid offsets (not starting at 0, decreasing, not ending at total, or self offsets differ)";
+    default: return "unknown status";
+  }
+}
+
+size_t jagged_attn_workspace_size(int B, int H, int D, int variant, int act, int window, int dtype,
+                                  int32_t total_q, int32_t total_kv) {
+  if (validate(B, H, D, variant, act, window, dtype, total_q, total_kv) != JA_OK) return 0;
+  return make_plan(B, H, D, variant, window, dtype, total_q, total_kv).ws.total;
+}
+
+int jagged_attn_fwd(const void* q, const void* k, const void* v, const int32_t* q_offsets,
+                    const int32_t* kv_offsets, int B, int H, int D, int variant, int act, int window,
+                    void* out, const ja_io* io) {
+  if (io == nullptr) return JA_EINVAL;
+  const int st = validate(B, H, D, variant, act, window, io->dtype, io->total_q, io->total_kv);
+  if (st != JA_OK) return st;
+  if (!q || !k || !v || !q_offsets || !kv_offsets || !out) return JA_EINVAL;
+  if (io->dtype == JA_MXFP8_E4M3 && (!io->q_scale || !io->k_scale || !io->v_scale)) return JA_EINVAL;
+  const Plan p = make_plan(B, H, D, variant, window, io->dtype, io->total_q, io->total_kv);
+  if (io->workspace == nullptr || io->workspace_bytes < p.ws.total) return JA_EWORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v) |
+       reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(io->workspace)) & 15)
+    return JA_EINVAL;
+
+  hipStream_t stream = reinterpret_cast<hipStream_t>(io->stream);
+  unsigned char* ws = reinterpret_cast<unsigned char*>(io->workspace);
+  WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
+  int32_t* nsplit = reinterpret_cast<int32_t*>(ws + p.ws.nsplit_off);
+  int32_t* pbase = reinterpret_cast<int32_t*>(ws + p.ws.pbase_off);
+  int4* items = reinterpret_cast<int4*>(ws + p.ws.items_off);
+  float* part_o = reinterpret_cast<float*>(ws + p.ws.part_o_off);
+  float2* part_ml = reinterpret_cast<float2*>(ws + p.ws.part_ml_off);
+
+  PlanArgs pa{};
+  pa.qo = q_offsets;
+  pa.ko = kv_offsets;
+  pa.B = B;
+  pa.H = H;
+  pa.total_q = io->total_q;
+  pa.total_kv = io->total_kv;
+  pa.bm = p.bm;
+  pa.kvc = p.kvc;
+  pa.self_check = variant == JA_SELF;
+  pa.max_items = p.ws.max_items;
+  pa.max_slots = p.ws.max_slots;
+  pa.hdr = hdr;
+  pa.nsplit = nsplit;
+  pa.pbase = pbase;
+  pa.items = items;
+  if (launch_plan(pa, stream) != hipSuccess) return JA_EHIP;
+
+  AttnArgs aa{};
+  aa.q = q;
+  aa.k = k;
+  aa.v = v;
+  aa.qs = io->q_scale;
+  aa.ks = io->k_scale;
+  aa.vs = io->v_scale;
+  aa.out = out;
+  aa.qo = q_offsets;
+  aa.ko = kv_offsets;
+  aa.hdr = hdr;
+  aa.items = items;
+  aa.nsplit = nsplit;
+  aa.pbase = pbase;
+  aa.part_o = part_o;
+  aa.part_ml = part_ml;
+  aa.H = H;
+  aa.window_blocks = window / kBlock;
+  aa.kvc = p.kvc;
+  aa.eps = io->rms_eps > 0.f ? io->rms_eps : 1e-6f;
+  const float inv_sqrt_d = 1.0f / std::sqrt(float(D));
+  aa.score_scale = act == JA_SOFTMAX ? inv_sqrt_d * 1.4426950408889634f : inv_sqrt_d;
+
+  const int grid = int(p.ws.max_items < kMaxGrid ? (p.ws.max_items > 0 ? p.ws.max_items : 1) : kMaxGrid);
+  hipError_t e;
+  if (p.shape == kShapeF32) {
+    e = launch_attn_f32(D, act, window > 0, aa, grid, stream);
+  } else {
+    const int in = io->dtype == JA_BF16 ? IN_BF16 : IN_MX;
+    e = launch_attn_mfma(D, in, p.shape, act, aa, grid, stream);
+  }
+  if (e != hipSuccess) return JA_EHIP;
+  if (p.shape == kShapeKvSplit) {
+    CombineArgs ca{};
+    ca.out = out;
+    ca.qo = q_offsets;
+    ca.ko = kv_offsets;
+    ca.hdr = hdr;
+    ca.nsplit = nsplit;
+    ca.pbase = pbase;
+    ca.part_o = part_o;
+    ca.part_ml = part_ml;
+    ca.B = B;
+    ca.H = H;
+    ca.act = act;
+    if (launch_combine(D, ca, stream) != hipSuccess) return JA_EHIP;
+  }
+  return JA_OK;
+}
+
+int jagged_attn_check(const void* workspace, void* stream) {
+  if (workspace == nullptr) return JA_EINVAL;
+  if (hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return JA_EHIP;
+  int32_t status = 0;
+  if (hipMemcpy(&status, workspace, sizeof(status), hipMemcpyDeviceToHost) != hipSuccess) return JA_EHIP;
+  return status;
+}
+
+}  // extern "C"

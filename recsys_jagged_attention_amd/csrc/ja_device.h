@@ -1,0 +1,57 @@
+// Device helpers for the gfx950 (CDNA4) jagged attention kernels.
+#pragma once
+
+#include "ja_internal.h"
+
+namespace ja {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// D(32x32) += A(32x16) * B(16x32), bf16 operands, fp32 accumulate.
+// Lane l supplies A[l%32][8*(l/32) .. +8) and B[8*(l/32) .. +8)[l%32]; the
+// result register i of lane l holds C[8*(i/4) + 4*(l/32) + i%4][l%32].
+__device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float other_half(float x) { return __shfl_xor(x, 32, 64); }
+
+// Decode 8 e4m3 ("fn") codes (little-endian in a u32x2) scaled by 2^(e8m0-127)
+// into bf16.  Exact: an e4m3 value has at most 4 significant bits and the
+// product with a power of two fits bf16 unless it leaves bf16's exponent range.
+__device__ __forceinline__ bf16x8 decode_mx8(u32x2 codes, unsigned scale_byte) {
+  // 2^(E-127) as a float; E == 0 gives the subnormal 2^-127, E == 255 is NaN.
+  const unsigned sb = scale_byte & 0xFFu;
+  const float s = sb == 0 ? __uint_as_float(0x00400000u)
+                          : (sb == 255u ? __builtin_nanf("") : __uint_as_float(sb << 23));
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const unsigned c = (codes[j >> 2] >> (8 * (j & 3))) & 0xFFu;
+    const unsigned e = (c >> 3) & 0xFu, m = c & 7u;
+    // |value| = (e ? 8+m : m) * 2^(max(e,1) - 10)
+    const float mag = float(e ? (8u + m) : m) * __uint_as_float((max(e, 1u) + 117u) << 23);
+    float v = (c & 0x80u) ? -mag : mag;
+    if (e == 15u && m == 7u) v = __builtin_nanf("");
+    r[j] = (__bf16)(v * s);
+  }
+  return r;
+}
+
+// gelu_tanh(x) = x * sigmoid(2u), u = sqrt(2/pi) (x + 0.044715 x^3):
+// the identity 1 + tanh(u) = 2 sigmoid(2u) needs one exp2 and one reciprocal.
+__device__ __forceinline__ float gelu_tanh(float x) {
+  constexpr float kC = 0.7978845608028654f;            // sqrt(2/pi)
+  constexpr float kNeg2Log2e = -2.0f * 1.4426950408889634f;
+  const float u = kC * fmaf(0.044715f * x, x * x, x);
+  const float e = fast_exp2(kNeg2Log2e * u);
+  return x * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+}  // namespace ja

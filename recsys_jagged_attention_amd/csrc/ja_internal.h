@@ -1,0 +1,97 @@
+// Internal definitions shared by the host launcher and the device kernels of
+// libjagged_attn.  Not part of the public ABI (include/jagged_attn.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ja {
+
+constexpr int kBlock = 64;        // token block of block-aligned attention
+constexpr int kMxBlock = 32;      // elements per E8M0 scale along D
+constexpr int kWaveSize = 64;
+constexpr int kThreads = 256;     // every MFMA kernel runs 4 waves per workgroup
+constexpr int kPmaRows = 32;      // query rows per key-split work item
+
+enum Act { ACT_SOFTMAX = 0, ACT_GELU = 1 };
+enum In { IN_F32 = 0, IN_BF16 = 1, IN_MX = 2 };
+
+// ---------------------------------------------------------------------------
+// Workspace layout (caller-owned device memory; every section 256-B aligned)
+//   [0, 256)            WsHeader
+//   sample_nsplit[B]    key-split count per sample (1 = written directly)
+//   sample_pbase[B]     first partial slot of the sample
+//   items[max_items]    int4 {b, h, q0, split}
+//   part_o[max_slots][32][D] float, part_ml[max_slots][32] float2
+// ---------------------------------------------------------------------------
+struct WsHeader {
+  int32_t status;      // JA_OK or JA_EOFFSETS, written by the plan kernel
+  int32_t n_items;     // work items for the attention kernel
+  int32_t n_slots;     // partial slots in use
+  int32_t pad[61];
+};
+
+struct WsLayout {
+  size_t nsplit_off, pbase_off, items_off, part_o_off, part_ml_off, total;
+  int64_t max_items, max_slots;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Work decomposition chosen on the host from the arguments alone.
+struct Schedule {
+  int bm;        // query rows per work item
+  int kvc;       // key chunk per work item (0 = whole sample)
+  int grid_cap;  // upper bound on work items
+};
+
+struct PlanArgs {
+  const int32_t* qo;
+  const int32_t* ko;
+  int B, H;
+  int32_t total_q, total_kv;
+  int bm, kvc, self_check;
+  int64_t max_items, max_slots;
+  WsHeader* hdr;
+  int32_t* nsplit;
+  int32_t* pbase;
+  int4* items;
+};
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const uint8_t* qs;  // MX scales (IN_MX only)
+  const uint8_t* ks;
+  const uint8_t* vs;
+  void* out;
+  const int32_t* qo;
+  const int32_t* ko;
+  const WsHeader* hdr;
+  const int4* items;
+  const int32_t* nsplit;
+  const int32_t* pbase;
+  float* part_o;
+  float2* part_ml;
+  int H;
+  int window_blocks;  // 0 = no window
+  int kvc;
+  float score_scale;  // softmax: log2(e)/sqrt(D); GELU: 1/sqrt(D)
+  float eps;
+};
+
+struct CombineArgs {
+  void* out;
+  const int32_t* qo;
+  const int32_t* ko;
+  const WsHeader* hdr;
+  const int32_t* nsplit;
+  const int32_t* pbase;
+  const float* part_o;
+  const float2* part_ml;
+  int B, H, act;
+};
+
+}  // namespace ja

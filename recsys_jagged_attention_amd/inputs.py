@@ -132,7 +132,7 @@ class Workload:
 
 WORKLOADS = ("tiny_full", "block_window", "full_self", "cross_gelu", "pma", "mxfp8_window")
 DEFAULT_SEED = {"tiny_full": 1001, "block_window": 1002, "full_self": 1002,
-                "cross_gelu": 1003, "pma": 1004, "mxfp8_window": 1005}
+                "cross_gelu": 1003, "pma": 1004, "mxfp8_window": 1002}
 
 
 def make_workload(name: str, seed: Optional[int] = None, scale: float = 1.0) -> Workload:
@@ -199,3 +199,32 @@ def random_jagged(seed: int, lengths_q, lengths_kv, H: int, D: int):
     k = normal_values(rng, int(ko[-1]), H, D)
     v = normal_values(rng, int(ko[-1]), H, D)
     return qo, ko, q, k, v
+
+
+def device_tensors(w: Workload, device):
+    """Move a workload to the GPU in its input dtype (casts only; RNE for bf16).
+
+    Returns (q, k, v, q_offsets, kv_offsets, scales) as torch tensors; scales is
+    None except for mxfp8 (then (q_scale, k_scale, v_scale) uint8)."""
+    import torch
+
+    qo = torch.from_numpy(np.ascontiguousarray(w.q_offsets, dtype=np.int32)).to(device)
+    ko = torch.from_numpy(np.ascontiguousarray(w.kv_offsets, dtype=np.int32)).to(device)
+    if w.dtype == "mxfp8":
+        t = [torch.from_numpy(np.ascontiguousarray(w.mx[n][0])).to(device) for n in "qkv"]
+        s = tuple(torch.from_numpy(np.ascontiguousarray(w.mx[n][1])).to(device) for n in "qkv")
+        return t[0], t[1], t[2], qo, ko, s
+    dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    t = [torch.from_numpy(x).to(dt).to(device) for x in (w.q, w.k, w.v)]
+    return t[0], t[1], t[2], qo, ko, None
+
+
+def cast_values(x: np.ndarray, dtype: str) -> np.ndarray:
+    """float32 values as the device receives them for f32/bf16 inputs (exact, float32)."""
+    import torch
+
+    if dtype == "f32":
+        return x
+    if dtype == "bf16":
+        return torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    raise ValueError(dtype)

@@ -1,0 +1,91 @@
+"""Helpers shared by the GPU parity tests: run the HIP path, build the exact
+float64 inputs the oracle needs, compare at the tolerance of each dtype."""
+import numpy as np
+import torch
+
+import oracle
+from recsys_jagged_attention_amd import forward
+from recsys_jagged_attention_amd.inputs import cast_values, device_tensors
+
+# max|O_gpu - O_ref| <= TOL * max|O_ref|  (fp32 / bf16 / MXFP8 against the
+# oracle run on the dequantised inputs)
+TOL = {"f32": 1e-5, "bf16": 1e-2, "mxfp8": 5e-2}
+
+
+def oracle_values(w):
+    """float64 q, k, v exactly as the device receives them."""
+    if w.dtype == "mxfp8":
+        return tuple(oracle.mx_dequantise(*w.mx[n]) for n in "qkv")
+    return tuple(cast_values(x, w.dtype).astype(np.float64) for x in (w.q, w.k, w.v))
+
+
+def run_gpu(w, device="cuda", check=True, **kw):
+    q, k, v, qo, ko, scales = device_tensors(w, device)
+    out = forward(q, k, v, qo, ko, variant=w.variant, act=w.act, window=w.window, dtype=w.dtype,
+                  scales=scales, check=check, **kw)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64)
+
+
+def rel_err(got, ref):
+    scale = np.abs(ref).max()
+    if scale == 0:
+        return float(np.abs(got).max())
+    return float(np.abs(got - ref).max() / scale)
+
+
+def full_parity(w):
+    got = run_gpu(w)
+    q, k, v = oracle_values(w)
+    ref = oracle.gdpa_forward(q, k, v, w.q_offsets, w.kv_offsets, w.variant, w.act, w.window)
+    assert np.all(np.isfinite(got))
+    err = rel_err(got, ref)
+    assert err <= TOL[w.dtype], f"{w.name}: rel err {err:.3e} > {TOL[w.dtype]:.0e}"
+    return err
+
+
+def sample_rows(w, n, seed=0):
+    """n random (token, head) rows plus the first/last row of a few samples."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    rows = set()
+    nq = w.total_q
+    for t in rng.integers(0, nq, size=n):
+        rows.add((int(t), int(rng.integers(0, w.H))))
+    lens = np.diff(w.q_offsets)
+    for b in rng.choice(len(lens), size=min(8, len(lens)), replace=False):
+        if lens[b]:
+            rows.add((int(w.q_offsets[b]), 0))
+            rows.add((int(w.q_offsets[b + 1] - 1), w.H - 1))
+    return sorted(rows)
+
+
+def sampled_parity(w, out, n=96, seed=0):
+    """Compare selected rows of a full-size GPU output against the oracle's
+    row-by-row evaluation (only the samples those rows belong to are decoded)."""
+    rows = sample_rows(w, n, seed)
+    got = np.stack([out[t, h] for t, h in rows]).astype(np.float64)
+    qo, ko = w.q_offsets, w.kv_offsets
+    ref = []
+    for t, h in rows:
+        b = int(np.searchsorted(qo, t, side="right") - 1)
+        sub = _sample_values(w, b)
+        ref.append(oracle.gdpa_rows(*sub, [(t - int(qo[b]), h)], w.variant, w.act, w.window)[0])
+    ref = np.stack(ref)
+    err = rel_err(got, ref)
+    assert np.all(np.isfinite(got))
+    assert err <= TOL[w.dtype], f"{w.name}: sampled rel err {err:.3e}"
+    return err
+
+
+def _sample_values(w, b):
+    q0, q1 = int(w.q_offsets[b]), int(w.q_offsets[b + 1])
+    k0, k1 = int(w.kv_offsets[b]), int(w.kv_offsets[b + 1])
+    if w.dtype == "mxfp8":
+        q = oracle.mx_dequantise(w.mx["q"][0][q0:q1], w.mx["q"][1][q0:q1])
+        k = oracle.mx_dequantise(w.mx["k"][0][k0:k1], w.mx["k"][1][k0:k1])
+        v = oracle.mx_dequantise(w.mx["v"][0][k0:k1], w.mx["v"][1][k0:k1])
+    else:
+        q = cast_values(w.q[q0:q1], w.dtype).astype(np.float64)
+        k = cast_values(w.k[k0:k1], w.dtype).astype(np.float64)
+        v = cast_values(w.v[k0:k1], w.dtype).astype(np.float64)
+    return q, k, v, np.array([0, q1 - q0]), np.array([0, k1 - k0])

@@ -1,0 +1,91 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host (these paths return before any HIP call, so no GPU is
+needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from recsys_jagged_attention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "jagged_attn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(jagged_attn_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert _lib.jagged_attn_version() == 100
+
+
+def test_strerror_covers_all_codes():
+    for code in (0, -1, -2, -3, -4, -5):
+        assert _lib.strerror(code) != "unknown status"
+    assert _lib.strerror(-99) == "unknown status"
+
+
+def ws(*a):
+    return _lib.jagged_attn_workspace_size(*a)
+
+
+def test_workspace_size_rejects_bad_arguments():
+    ok = ws(4, 2, 32, _lib.JA_SELF, _lib.JA_SOFTMAX, 0, _lib.JA_F32, 100, 100)
+    assert ok > 0
+    assert ws(0, 2, 32, 0, 0, 0, 0, 100, 100) == 0                 # B < 1
+    assert ws(4, 2, 48, 0, 0, 0, 0, 100, 100) == 0                 # unsupported D
+    assert ws(4, 2, 32, 0, 0, 100, 0, 100, 100) == 0               # window not a multiple of 64
+    assert ws(4, 2, 32, 1, 0, 64, 0, 100, 100) == 0                # window on cross
+    assert ws(4, 2, 32, 0, 1, 64, 0, 100, 100) == 0                # windowed GELU
+    assert ws(4, 2, 32, 0, 0, 0, 0, 100, 99) == 0                  # self with different totals
+    assert ws(4, 2, 32, 3, 0, 0, 0, 100, 100) == 0                 # bad variant
+    assert ws(4, 2, 32, 0, 0, 0, 7, 100, 100) == 0                 # bad dtype
+
+
+def test_workspace_grows_with_key_split_partials():
+    small = ws(512, 8, 64, _lib.JA_PMA, _lib.JA_SOFTMAX, 0, _lib.JA_BF16, 512 * 32, 1000)
+    big = ws(512, 8, 64, _lib.JA_PMA, _lib.JA_SOFTMAX, 0, _lib.JA_BF16, 512 * 32, 2_000_000)
+    assert big > small > 0
+
+
+def call(B=2, H=1, D=32, variant=0, act=0, window=0, dtype=0, tq=10, tk=10, ws_bytes=1 << 20,
+         ptr=4096, io=True, scales=False):
+    j = _lib.JaIo()
+    j.dtype = dtype
+    j.total_q, j.total_kv = tq, tk
+    j.workspace = 1 << 20
+    j.workspace_bytes = ws_bytes
+    if scales:
+        j.q_scale = j.k_scale = j.v_scale = 4096
+    lib = _lib.load()
+    return lib.jagged_attn_fwd(ptr, ptr, ptr, ptr, ptr, B, H, D, variant, act, window, ptr,
+                               ctypes.byref(j) if io else None)
+
+
+def test_fwd_host_validation():
+    assert call(io=False) == _lib.JA_EINVAL
+    assert call(B=0) == _lib.JA_EINVAL
+    assert call(D=96) == _lib.JA_EUNSUPPORTED
+    assert call(window=32) == _lib.JA_EUNSUPPORTED
+    assert call(variant=_lib.JA_CROSS, window=64) == _lib.JA_EINVAL
+    assert call(act=_lib.JA_GELU_TANH, window=64) == _lib.JA_EUNSUPPORTED
+    assert call(tq=10, tk=11) == _lib.JA_EINVAL
+    assert call(ptr=0) == _lib.JA_EINVAL
+    assert call(dtype=_lib.JA_MXFP8_E4M3) == _lib.JA_EINVAL          # scales missing
+    assert call(ws_bytes=16) == _lib.JA_EWORKSPACE
+    assert call(ptr=4100) == _lib.JA_EINVAL                            # misaligned
+    assert call(dtype=_lib.JA_MXFP8_E4M3, scales=True, ws_bytes=16) == _lib.JA_EWORKSPACE
+
+
+def test_check_rejects_null_workspace():
+    assert _lib.jagged_attn_check(None, None) == _lib.JA_EINVAL
