@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Benchmark of the jagged GDPA forward on one MI355X.
+
+One step = one jagged_attn_fwd call (device-side plan + attention kernel
+[+ split merge]) over one batch of seeded synthetic input already resident in
+HBM.  Several copies of the batch are cycled so that no step reads data a
+previous step left in the 256 MB last-level cache.
+
+Prints ONE JSON line: useful (unpadded) TFLOPS of the whole job, the
+roofline of the dominant (attention) kernel timed live with HIP events
+recorded around that kernel's launch, and the float64 CPU oracle timed on a
+bounded sample of the same workload.
+
+  python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload block_window]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0, "f32": 157.3}  # dense MFMA/vector peaks
+PEAK_HBM_GBS = 8000.0
+METRIC = "useful TFLOPS (unpadded) & % bf16 MFMA peak, jagged GDPA fwd, 1 MI355X"
+KERNEL_NAME = {  # dominant kernel per workload (template instance of attn_kernel)
+    "tiny_full": "attn_f32_kernel<32,softmax,nowindow>",
+    "block_window": "attn_kernel<128,NWQ=2,NWK=2,softmax,bf16,window>",
+    "full_self": "attn_kernel<128,NWQ=4,NWK=1,softmax,bf16>",
+    "cross_gelu": "attn_kernel<128,NWQ=4,NWK=1,gelu,bf16>",
+    "pma": "attn_kernel<64,NWQ=1,NWK=4,softmax,bf16,split>",
+    "mxfp8_window": "attn_kernel<128,NWQ=2,NWK=2,softmax,mx,window>",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """Raw hipEvent_t handles, created through the HIP runtime."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self) -> int:
+        e = ctypes.c_void_p()
+        if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, e: int):
+        self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas"]
+        return int(max(n)) if n else 1
+    except Exception:  # pragma: no cover
+        return 1
+
+
+def cpu_baseline(w, budget_s: float):
+    """Time the float64 oracle on whole samples of the workload (seeded order)
+    until about budget_s seconds of CPU work; report useful TFLOPS."""
+    import oracle
+    from recsys_jagged_attention_amd.inputs import cast_values
+    from recsys_jagged_attention_amd import workload as wl
+
+    rng = np.random.Generator(np.random.PCG64(w.seed + 7))
+    order = rng.permutation(w.B)
+    spent, flops, used = 0.0, 0, []
+    for b in order:
+        q0, q1 = int(w.q_offsets[b]), int(w.q_offsets[b + 1])
+        k0, k1 = int(w.kv_offsets[b]), int(w.kv_offsets[b + 1])
+        if w.dtype == "mxfp8":
+            q = oracle.mx_dequantise(w.mx["q"][0][q0:q1], w.mx["q"][1][q0:q1])
+            k = oracle.mx_dequantise(w.mx["k"][0][k0:k1], w.mx["k"][1][k0:k1])
+            v = oracle.mx_dequantise(w.mx["v"][0][k0:k1], w.mx["v"][1][k0:k1])
+        else:
+            q, k, v = (cast_values(x, w.dtype).astype(np.float64)
+                       for x in (w.q[q0:q1], w.k[k0:k1], w.v[k0:k1]))
+        qo, ko = np.array([0, q1 - q0]), np.array([0, k1 - k0])
+        t0 = time.perf_counter()
+        oracle.gdpa_forward(q, k, v, qo, ko, w.variant, w.act, w.window)
+        spent += time.perf_counter() - t0
+        flops += wl.useful_flops([q1 - q0], [k1 - k0], w.H, w.D, w.window)
+        used.append(int(b))
+        if spent >= budget_s:
+            break
+    return {
+        "value": flops / spent / 1e12 if spent > 0 else None,
+        "unit": "TFLOPS",
+        "cores": blas_threads(),
+        "kind": "oracle",
+        "sample": f"{len(used)} of {w.B} samples of the {w.name} batch (seeded order), "
+                  f"{flops / 1e9:.2f} useful GFLOP in {spent:.1f} s, numpy float64",
+    }
+
+
+def load_traffic(kernel_tag: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, only if
+    they were taken on the current kernel sources (matching source hash)."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            a, b = line.split(":", 1)
+            kv[a.strip()] = b.strip()
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "recsys_jagged_attention_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    if kv.get("source_sha256") != h.hexdigest() or kv.get("kernel") != kernel_tag:
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="block_window")
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rotate-bytes", type=float, default=1.2e9,
+                    help="bytes of input copies cycled through (defeats cache reuse across steps)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the forward kernel runs on one device); "
+              f"--gpus {args.gpus} is not supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from recsys_jagged_attention_amd import forward, Workspace
+    from recsys_jagged_attention_amd import workload as wl
+    from recsys_jagged_attention_amd.inputs import make_workload, device_tensors, WORKLOADS
+
+    if args.workload not in WORKLOADS:
+        raise SystemExit(f"unknown workload {args.workload}; choose from {WORKLOADS}")
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    t_gen = time.perf_counter()
+    w = make_workload(args.workload, seed=args.seed)
+    log(f"[bench] workload {w.name}: B={w.B} H={w.H} D={w.D} window={w.window} "
+        f"tokens q={w.total_q} kv={w.total_kv} dtype={w.dtype} (generated in {time.perf_counter() - t_gen:.1f}s)")
+    q, k, v, qo, ko, scales = device_tensors(w, dev)
+    in_bytes = {"f32": 4, "bf16": 2, "mxfp8": 1}[w.dtype]
+    out_bytes = 4 if w.dtype == "f32" else 2
+    alg_bytes = wl.compulsory_bytes(w.total_q, w.total_kv, w.H, w.D, in_bytes, out_bytes,
+                                    mx_scales=w.dtype == "mxfp8")
+    lq, lk = np.diff(w.q_offsets), np.diff(w.kv_offsets)
+    flops = wl.useful_flops(lq, lk, w.H, w.D, w.window)
+    n_copies = int(max(2, min(8, math.ceil(args.rotate_bytes / max(alg_bytes, 1)))))
+    sets = [(q, k, v, scales)]
+    for _ in range(n_copies - 1):
+        sets.append((q.clone(), k.clone(), v.clone(),
+                     None if scales is None else tuple(s.clone() for s in scales)))
+    outs = [torch.empty(q.shape, dtype=torch.float32 if w.dtype == "f32" else torch.bfloat16, device=dev)
+            for _ in range(n_copies)]
+    wsp = Workspace(dev)
+    ev = HipEvents()
+    K, W = args.steps, args.warmup
+    starts = [ev.create() for _ in range(K)]
+    stops = [ev.create() for _ in range(K)]
+
+    def step(i, events=None):
+        qq, kk, vv, ss = sets[i % n_copies]
+        forward(qq, kk, vv, qo, ko, variant=w.variant, act=w.act, window=w.window, dtype=w.dtype,
+                scales=ss, out=outs[i % n_copies], workspace=wsp, events=events)
+
+    forward(q, k, v, qo, ko, variant=w.variant, act=w.act, window=w.window, dtype=w.dtype,
+            scales=scales, out=outs[0], workspace=wsp, check=True)   # validates offsets once
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({W} steps), timing {K} steps over {n_copies} input copies")
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i, (starts[i], stops[i]))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern_ms = [ev.elapsed_ms(starts[i], stops[i]) for i in range(K)]
+    for e in starts + stops:
+        ev.destroy(e)
+    ms_per_step = (t1 - t0) * 1e3 / K
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    kern_avg_s = float(np.mean(kern_ms)) * 1e-3
+    intensity = flops / alg_bytes
+    ridge = PEAK_TFLOPS[w.dtype] * 1e12 / (PEAK_HBM_GBS * 1e9)
+    kernel_tag = KERNEL_NAME[w.name]
+    if intensity < ridge:
+        achieved = alg_bytes / kern_avg_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    else:
+        achieved = flops / kern_avg_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_TFLOPS[w.dtype],
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS[w.dtype], 4)}
+    roof["traffic"] = load_traffic(kernel_tag, w.name)
+    roof["kernel"] = kernel_tag
+    roof["kernel_avg_us"] = round(kern_avg_s * 1e6, 2)
+    roof["algorithmic_bytes_per_launch"] = int(alg_bytes)
+    roof["useful_flops_per_launch"] = int(flops)
+    log(f"[bench] {ms_per_step * 1e3:.1f} us/step, kernel {kern_avg_s * 1e6:.1f} us, "
+        f"{value:.1f} useful TFLOPS, {roof['achieved']} {roof['unit']} ({roof['frac'] * 100:.1f}% of peak)")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        t_cpu = time.perf_counter()
+        cpu = cpu_baseline(w, args.cpu_seconds)
+        log(f"[bench] cpu oracle baseline {cpu['value']:.4g} TFLOPS on {cpu['cores']} threads "
+            f"({time.perf_counter() - t_cpu:.1f}s)")
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "pct_bf16_peak": round(100 * value / PEAK_TFLOPS["bf16"], 2),
+        "config": {"workload": w.name, "variant": w.variant, "act": w.act, "B": w.B, "H": w.H, "D": w.D,
+                   "window": w.window, "total_q": w.total_q, "total_kv": w.total_kv, "seed": w.seed,
+                   "useful_gflop": round(flops / 1e9, 3), "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

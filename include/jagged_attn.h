@@ -95,6 +95,11 @@ typedef struct ja_io {
   int32_t total_q;           /* rows of q/out  (= q_offsets[B])                 */
   int32_t total_kv;          /* rows of k/v    (= kv_offsets[B])                */
   float rms_eps;             /* JA_GELU_TANH: RMSNorm epsilon; <= 0 -> 1e-6     */
+  void *ev_start;            /* optional profiling hipEvent_t pair (or NULL):   */
+  void *ev_stop;             /* recorded on `stream` right before and right     */
+                             /* after the attention kernel (not the plan or the */
+                             /* split-merge kernel), so its duration can be     */
+                             /* timed without a profiler                        */
 } ja_io;
 
 /* The forward pass.  Arguments as described above; window is 0 (no window) or

@@ -38,6 +38,8 @@ class JaIo(ctypes.Structure):
         ("total_q", ctypes.c_int32),
         ("total_kv", ctypes.c_int32),
         ("rms_eps", ctypes.c_float),
+        ("ev_start", ctypes.c_void_p),
+        ("ev_stop", ctypes.c_void_p),
     ]
 
 

@@ -34,13 +34,16 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             variant: str = "self", act: str = "softmax", window: int = 0,
             dtype: str = "bf16", scales=None, out: Optional[torch.Tensor] = None,
             workspace: Optional[Workspace] = None, rms_eps: float = 1e-6,
-            stream: Optional[torch.cuda.Stream] = None, check: bool = False) -> torch.Tensor:
+            stream: Optional[torch.cuda.Stream] = None, check: bool = False,
+            events=None) -> torch.Tensor:
     """Jagged GDPA forward.  q [Nq,H,D], k/v [Nk,H,D] on one GPU; offsets int32 [B+1].
 
     dtype "f32"/"bf16": q/k/v of that dtype; "mxfp8": uint8 e4m3 codes with
     ``scales=(q_scale, k_scale, v_scale)`` uint8 [rows,H,D/32].  Output is
     float32 for "f32", else bfloat16.  With ``check=True`` the call
-    synchronises and raises on a device-side status (e.g. bad offsets)."""
+    synchronises and raises on a device-side status (e.g. bad offsets).
+    ``events=(start, stop)`` are raw hipEvent_t handles recorded around the
+    attention kernel."""
     if dtype not in _IN_DTYPES:
         raise ValueError(f"dtype must be one of {list(_IN_DTYPES)}")
     want = _IN_DTYPES[dtype]
@@ -84,6 +87,8 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     io.total_q = Nq
     io.total_kv = Nk
     io.rms_eps = rms_eps
+    if events is not None:
+        io.ev_start, io.ev_stop = events   # raw hipEvent_t handles (ints)
     status = _lib.jagged_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), q_offsets.data_ptr(),
                                   kv_offsets.data_ptr(), B, H, D, v_id, a_id, window, out.data_ptr(), io)
     if status != _lib.JA_OK:

@@ -185,6 +185,8 @@ int jagged_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
   aa.score_scale = act == JA_SOFTMAX ? inv_sqrt_d * 1.4426950408889634f : inv_sqrt_d;
 
   const int grid = int(p.ws.max_items < kMaxGrid ? (p.ws.max_items > 0 ? p.ws.max_items : 1) : kMaxGrid);
+  if (io->ev_start && hipEventRecord(reinterpret_cast<hipEvent_t>(io->ev_start), stream) != hipSuccess)
+    return JA_EHIP;
   hipError_t e;
   if (p.shape == kShapeF32) {
     e = launch_attn_f32(D, act, window > 0, aa, grid, stream);
@@ -193,6 +195,8 @@ int jagged_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
     e = launch_attn_mfma(D, in, p.shape, act, aa, grid, stream);
   }
   if (e != hipSuccess) return JA_EHIP;
+  if (io->ev_stop && hipEventRecord(reinterpret_cast<hipEvent_t>(io->ev_stop), stream) != hipSuccess)
+    return JA_EHIP;
   if (p.shape == kShapeKvSplit) {
     CombineArgs ca{};
     ca.out = out;
