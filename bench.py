@@ -154,7 +154,21 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotate-bytes", type=float, default=1.2e9,
                     help="bytes of input copies cycled through (defeats cache reuse across steps)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes 5 times (the reference "
+                         "for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE counters) and exit")
     args = ap.parse_args()
+
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {n} bytes 5 times")
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the forward kernel runs on one device); "

@@ -11,7 +11,8 @@
 
 namespace ja {
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st);
-hipError_t launch_attn_mfma(int D, int in, int shape, int act, const AttnArgs& a, int grid, hipStream_t st);
+hipError_t launch_attn_mfma(int D, int in, int shape, int act, const AttnArgs& a, int num_cu,
+                            int64_t max_items, hipStream_t st);
 hipError_t launch_combine(int D, const CombineArgs& a, hipStream_t st);
 hipError_t launch_attn_f32(int D, int act, bool window, const AttnArgs& a, int grid, hipStream_t st);
 
@@ -28,6 +29,19 @@ struct Plan {
 };
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Compute units of the current device (cached per device id).
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
 
 // Key chunk for the key-split shape: about 2048 work items per call, a
 // power of two between 512 and 8192 keys (long samples are split, short ones
@@ -153,6 +167,7 @@ int jagged_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
   pa.bm = p.bm;
   pa.kvc = p.kvc;
   pa.self_check = variant == JA_SELF;
+  pa.window_blocks = window / kBlock;
   pa.max_items = p.ws.max_items;
   pa.max_slots = p.ws.max_slots;
   pa.hdr = hdr;
@@ -192,7 +207,7 @@ int jagged_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
     e = launch_attn_f32(D, act, window > 0, aa, grid, stream);
   } else {
     const int in = io->dtype == JA_BF16 ? IN_BF16 : IN_MX;
-    e = launch_attn_mfma(D, in, p.shape, act, aa, grid, stream);
+    e = launch_attn_mfma(D, in, p.shape, act, aa, device_cus(), p.ws.max_items, stream);
   }
   if (e != hipSuccess) return JA_EHIP;
   if (io->ev_stop && hipEventRecord(reinterpret_cast<hipEvent_t>(io->ev_stop), stream) != hipSuccess)

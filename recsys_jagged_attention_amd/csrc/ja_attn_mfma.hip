@@ -10,22 +10,29 @@
 // NWQ=2 x NWK=2 (one query block, its window split over two wave pairs) and
 // PMA (32 queries, long keys) uses NWK=4 plus a key split across workgroups.
 //
+// Data path.  K and V tiles go from HBM straight into LDS (global_load_lds,
+// 16 bytes per lane, no register staging), row-major with the 16-byte chunks
+// of each row XOR-swizzled so that the MFMA operand reads below are free of
+// bank conflicts.  Q stays in registers for the whole item.
+//
 // Score tiles are computed transposed, S^T = K Q^T, with K from LDS as the A
-// operand and Q resident in registers as the B operand: the 32x32 result then
-// leaves every lane holding one query's scores, so softmax row statistics need
-// only one exchange between the two half-waves, and P^T is already the B
-// operand of O^T = V^T P^T.  V is stored transposed in LDS for that product.
-// Two free index permutations are used:
+// operand and Q as the B operand: the 32x32 result leaves every lane holding
+// one query's scores, so softmax row statistics need one exchange between the
+// two half-waves, and P^T is already the B operand of O^T = V^T P^T.  The V^T
+// operand is read from the row-major V tile with the LDS transpose read
+// (ds_read_b64_tr_b16: within 16 lanes, lane i gets element i%4 of the 8-byte
+// chunks addressed by lanes 4j + i/4).  Two free index permutations are used:
 //  * the A rows of S^T (keys) are fed with bits 2 and 3 of the row swapped, so
-//    lane-half g ends up holding keys 16*(i/8) + 8g + i%8 in register i -- eight
-//    consecutive keys per MFMA k-chunk, read from V^T with one 16-byte load;
-//  * the A rows of O^T (head dims) of output tile t are chosen so that lane-half
-//    g holds dims (D/2)g + 16t + i: each lane owns a contiguous half row of O,
-//    and Q is loaded the same way (contraction order is free for a dot product).
-// Softmax (online, base 2) is kept per lane; GELU needs no statistics
-// (techfeed.io GDPA section: the QK-norm bounds the activation input, and no
-// correction stage is needed); the block window needs no element mask because
-// 64-key tiles coincide with the 64-token blocks ("BlockAttention" section).
+//    lane-half g holds keys 16*(i/8) + 8g + i%8 in register i -- eight
+//    consecutive keys per MFMA k-chunk;
+//  * the A rows of O^T (head dims) of output tile t are chosen so lane-half g
+//    holds dims (D/2)g + 16t + i: each lane owns a contiguous half row of O,
+//    and Q is loaded the same way (the contraction order is free).
+// Softmax is online in base 2 and rescales only when some row's max moved;
+// GELU needs no statistics (techfeed.io GDPA section: the QK-norm bounds the
+// activation input, no correction stage); the block window needs no element
+// mask because 64-key tiles coincide with the 64-token blocks (same page,
+// "BlockAttention"); only a sample's ragged last tile is masked.
 #include "ja_device.h"
 #include "jagged_attn.h"
 
@@ -33,22 +40,8 @@ namespace ja {
 
 namespace {
 
-constexpr int kVtStride = 80;  // bf16 per V^T row: 64 keys + 16 pad (bank spread)
-
-template <int D>
-struct Lds {
-  static constexpr int kKStride = D + 8;                 // bf16 per K row
-  static constexpr int kKSize = 64 * kKStride;           // bf16 elements
-  static constexpr int kVtSize = D * kVtStride + 8;      // rows >= D/2 shifted by 8
-  static constexpr int kGroup = kKSize + kVtSize;        // one key tile (K + V^T)
-};
-
-// V^T row offset (bf16 units): rows of the upper half start 16 bytes later so
-// that a 16-lane LDS phase reading dims {d, d + D/2} hits distinct banks.
-template <int D>
-__device__ __forceinline__ int vt_row(int d) {
-  return d * kVtStride + (d >= D / 2 ? 8 : 0);
-}
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 // Key row feeding A row r of S^T: bits 2 and 3 of r swapped.
 __device__ __forceinline__ int key_perm(int r) {
@@ -61,15 +54,20 @@ __device__ __forceinline__ int dim_perm(int t, int r) {
   return (D / 2) * ((r >> 2) & 1) + 16 * t + ((r >> 3) << 2) + (r & 3);
 }
 
-template <int IN>
-__device__ __forceinline__ bf16x8 load_row8(const void* base, size_t elem, const uint8_t* scales,
-                                            size_t scale_idx) {
-  if constexpr (IN == IN_BF16) {
-    return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(base) + elem);
-  } else {
-    const u32x2 c = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(base) + elem);
-    return decode_mx8(c, scales[scale_idx]);
-  }
+// Chunk swizzles (16-byte chunk index XOR) of the K and V tiles, chosen so that
+// a 16-lane phase of the K operand reads and a 32-lane phase of the V
+// transpose reads touch 64 distinct banks.
+template <int D>
+__device__ __forceinline__ int swz_k(int row) {
+  if constexpr (D == 128) return row & 15;
+  else if constexpr (D == 64) return (row >> 1) & 7;
+  else return (row >> 2) & 3;
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int row) {
+  if constexpr (D == 128) return 2 * (row & 3);
+  else if constexpr (D == 64) return 2 * ((row >> 1) & 1);
+  else return 0;
 }
 
 __device__ __forceinline__ bf16x8 zero8() {
@@ -79,74 +77,83 @@ __device__ __forceinline__ bf16x8 zero8() {
   return z;
 }
 
+__device__ __forceinline__ void wait_vmem() {
+  // s_waitcnt vmcnt(0): direct-to-LDS loads complete before the barrier
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
 template <int D, int NWQ, int NWK, int ACT, int IN, bool WINDOW, bool SPLIT>
 struct Attn {
-  using L = Lds<D>;
-  static constexpr int kQChunks = D / 16;   // MFMA k-chunks over D
-  static constexpr int kOTiles = D / 32;    // 32-dim output tiles
+  static constexpr int kRowBytes = 2 * D;               // one bf16 row in LDS
+  static constexpr int kTileBytes = 64 * kRowBytes;      // 64 keys
+  static constexpr int kGroupBytes = 2 * kTileBytes;     // K tile + V tile
+  static constexpr int kSegs = kTileBytes / 1024;        // 1 KB direct-load segments per tile
+  static constexpr int kQChunks = D / 16;                // MFMA k-chunks over D
+  static constexpr int kOTiles = D / 32;                 // 32-dim output tiles
+  static constexpr int kChunks = D / 8;                  // 16-byte chunks per row
 
-  // Cooperative load of 64 key rows [key0, key0+64) of (sample, head) into
-  // K (row-major) and V^T; rows at or beyond kv_end are zero.  GELU also
-  // stores each key's RMSNorm factor.
-  static __device__ __forceinline__ void load_tile(const AttnArgs& a, __bf16* grp, float* kscale,
-                                                   size_t kv_row0, int h, int key0, int kv_end) {
-    const int tid = threadIdx.x;
-    __bf16* ks = grp;
-    __bf16* vt = grp + L::kKSize;
-    constexpr int kChunks = D / 8;             // 8-element chunks per row
-    constexpr int kKUnits = 64 * kChunks;
+  // Issue the loads of one key tile (keys [key0, key0+64) of the item, rows
+  // at or beyond kv_end replaced by row kv_end-1, which the mask removes).
+  static __device__ __forceinline__ void issue_tile(unsigned char* grp, const __bf16* kb,
+                                                    const __bf16* vb, const uint8_t* ksb,
+                                                    const uint8_t* vsb, size_t rs, int key0,
+                                                    int kv_end) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if constexpr (IN == IN_BF16) {
+      // 2 * kSegs segments of 1 KB (K then V), 4 waves round-robin.
 #pragma unroll
-    for (int u0 = 0; u0 < kKUnits; u0 += kThreads) {
-      const int u = u0 + tid;
-      const int key = u / kChunks, ch = u % kChunks;
-      bf16x8 x = zero8();
-      if (key0 + key < kv_end) {
-        const size_t row = (kv_row0 + key0 + key) * a.H + h;
-        x = load_row8<IN>(a.k, row * D + 8 * ch, a.ks, row * (D / kMxBlock) + (8 * ch) / kMxBlock);
+      for (int s = wave; s < 2 * kSegs; s += 4) {
+        const bool is_v = s >= kSegs;
+        const int seg = is_v ? s - kSegs : s;
+        const int byte = seg * 1024 + 16 * lane;
+        const int row = byte / kRowBytes;
+        const int phys = (byte % kRowBytes) / 16;
+        const int c = phys ^ (is_v ? swz_v<D>(row) : swz_k<D>(row));
+        const int key = min(key0 + row, kv_end - 1);
+        const __bf16* src = (is_v ? vb : kb) + size_t(key) * rs + 8 * c;
+        unsigned char* dst = grp + (is_v ? kTileBytes : 0) + seg * 1024;
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
       }
-      *reinterpret_cast<bf16x8*>(ks + key * L::kKStride + 8 * ch) = x;
-      if constexpr (ACT == ACT_GELU) {
-        float ss = 0.f;
+    } else {
+      // MX: decode 8 e4m3 codes x 2^(E-127) to bf16 through registers.
 #pragma unroll
-        for (int j = 0; j < 8; ++j) ss = fmaf(float(x[j]), float(x[j]), ss);
-#pragma unroll
-        for (int o = 1; o < kChunks; o <<= 1) ss += __shfl_xor(ss, o, 64);
-        if (ch == 0) kscale[key] = __builtin_amdgcn_rsqf(ss * (1.0f / D) + a.eps);
-      }
-    }
-    constexpr int kVUnits = 32 * kChunks;      // (key pair, chunk)
-#pragma unroll
-    for (int u0 = 0; u0 < kVUnits; u0 += kThreads) {
-      const int u = u0 + tid;
-      if (kVUnits % kThreads == 0 || u < kVUnits) {
-        const int p = u % 32, ch = u / 32;
-        bf16x8 x0 = zero8(), x1 = zero8();
-        const int k0 = key0 + 2 * p;
-        if (k0 < kv_end) {
-          const size_t row = (kv_row0 + k0) * a.H + h;
-          x0 = load_row8<IN>(a.v, row * D + 8 * ch, a.vs, row * (D / kMxBlock) + (8 * ch) / kMxBlock);
-        }
-        if (k0 + 1 < kv_end) {
-          const size_t row = (kv_row0 + k0 + 1) * a.H + h;
-          x1 = load_row8<IN>(a.v, row * D + 8 * ch, a.vs, row * (D / kMxBlock) + (8 * ch) / kMxBlock);
-        }
-        // Pair element j of key 2p (low half) with element j of key 2p+1 (high
-        // half).  Whole-vector casts only: hipcc folds a bit_cast of a single
-        // bf16 vector element to element 0.
-        const u32x4 w0 = __builtin_bit_cast(u32x4, x0), w1 = __builtin_bit_cast(u32x4, x1);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          *reinterpret_cast<unsigned*>(vt + vt_row<D>(8 * ch + 2 * i) + 2 * p) =
-              (w0[i] & 0xFFFFu) | (w1[i] << 16);
-          *reinterpret_cast<unsigned*>(vt + vt_row<D>(8 * ch + 2 * i + 1) + 2 * p) =
-              (w0[i] >> 16) | (w1[i] & 0xFFFF0000u);
-        }
+      for (int u0 = 0; u0 < 2 * 64 * kChunks; u0 += kThreads) {
+        const int u = u0 + tid;
+        const bool is_v = u >= 64 * kChunks;
+        const int uu = is_v ? u - 64 * kChunks : u;
+        const int row = uu / kChunks, c = uu % kChunks;
+        const int key = min(key0 + row, kv_end - 1);
+        const size_t e = size_t(key) * rs + 8 * c;
+        const uint8_t* codes = reinterpret_cast<const uint8_t*>(is_v ? (const void*)vb : (const void*)kb);
+        const uint8_t* sc = is_v ? vsb : ksb;
+        const bf16x8 x = decode_mx8(*reinterpret_cast<const u32x2*>(codes + e),
+                                    sc[size_t(key) * (rs / kMxBlock) + (8 * c) / kMxBlock]);
+        const int phys = c ^ (is_v ? swz_v<D>(row) : swz_k<D>(row));
+        *reinterpret_cast<bf16x8*>(grp + (is_v ? kTileBytes : 0) + row * kRowBytes + 16 * phys) = x;
       }
     }
   }
 
-  static __device__ void run_item(const AttnArgs& a, const int4 item, __bf16* lds, float* kscale_all,
-                                  float* cbuf) {
+  // RMSNorm factor of every key of a loaded K tile (GELU).
+  static __device__ __forceinline__ void key_scales(float eps, const unsigned char* grp, float* kscale) {
+    const int tid = threadIdx.x;
+    const int row = tid >> 2, part = tid & 3;
+    constexpr int kPer = kChunks / 4;
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int c = part * kPer + i;
+      const bf16x8 x = *reinterpret_cast<const bf16x8*>(grp + row * kRowBytes + 16 * (c ^ swz_k<D>(row)));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ss = fmaf(float(x[j]), float(x[j]), ss);
+    }
+    ss += __shfl_xor(ss, 1, 64);
+    ss += __shfl_xor(ss, 2, 64);
+    if (part == 0) kscale[row] = __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
+  }
+
+  static __device__ void run_item(const AttnArgs& a, const int4 item, unsigned char* lds,
+                                  float* kscale_all) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wq = wave % NWQ, wk = wave / NWQ;
     const int l32 = lane & 31, g = lane >> 5;
@@ -174,6 +181,24 @@ struct Attn {
     const bool qvalid = qrow < lq;
     const int wblk = qrow_w / kBlock;
 
+    // Per-item base pointers: key row r of head h starts at base + r * rs.
+    const size_t rs = size_t(a.H) * D;
+    const size_t kv_off = size_t(kbeg) * rs + size_t(h) * D;
+    const __bf16* kb;
+    const __bf16* vb;
+    const uint8_t* ksb = nullptr;
+    const uint8_t* vsb = nullptr;
+    if constexpr (IN == IN_BF16) {
+      kb = reinterpret_cast<const __bf16*>(a.k) + kv_off;
+      vb = reinterpret_cast<const __bf16*>(a.v) + kv_off;
+    } else {
+      // e4m3 codes are bytes: the element offset is the byte offset
+      kb = reinterpret_cast<const __bf16*>(reinterpret_cast<const uint8_t*>(a.k) + kv_off);
+      vb = reinterpret_cast<const __bf16*>(reinterpret_cast<const uint8_t*>(a.v) + kv_off);
+      ksb = a.ks + (size_t(kbeg) * a.H + h) * (D / kMxBlock);
+      vsb = a.vs + (size_t(kbeg) * a.H + h) * (D / kMxBlock);
+    }
+
     // Q fragment: lane holds dims [(D/2)g, (D/2)g + D/2) of its query row.
     bf16x8 qf[kQChunks];
     if (qvalid) {
@@ -181,7 +206,12 @@ struct Attn {
 #pragma unroll
       for (int c = 0; c < kQChunks; ++c) {
         const int d0 = (D / 2) * g + 8 * c;
-        qf[c] = load_row8<IN>(a.q, row * D + d0, a.qs, row * (D / kMxBlock) + d0 / kMxBlock);
+        if constexpr (IN == IN_BF16) {
+          qf[c] = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(a.q) + row * D + d0);
+        } else {
+          qf[c] = decode_mx8(*reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(a.q) + row * D + d0),
+                             a.qs[row * (D / kMxBlock) + d0 / kMxBlock]);
+        }
       }
     } else {
 #pragma unroll
@@ -198,6 +228,19 @@ struct Attn {
       rq = __builtin_amdgcn_rsqf(ss * (1.0f / D) + a.eps) * a.score_scale;
     }
 
+    // Lane-constant LDS byte offsets of the MFMA operand reads.
+    const int kp = key_perm(l32);
+    int k_off[kQChunks];
+#pragma unroll
+    for (int c = 0; c < kQChunks; ++c) k_off[c] = kp * kRowBytes + 16 * ((kQChunks * g + c) ^ swz_k<D>(kp));
+    const int v_row = (8 * g + ((lane & 15) >> 2)) * kRowBytes;
+    int v_col[kOTiles];
+#pragma unroll
+    for (int t = 0; t < kOTiles; ++t) {
+      const int col = dim_perm<D>(t, 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+      v_col[t] = 16 * ((col >> 3) ^ swz_v<D>((lane & 15) >> 2)) + 8 * ((col & 7) >> 2);
+    }
+
     f32x16 o[kOTiles];
 #pragma unroll
     for (int t = 0; t < kOTiles; ++t)
@@ -205,24 +248,29 @@ struct Attn {
       for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
     float m = -__builtin_huge_valf(), l = 0.f;
 
-    const size_t kv_row0 = size_t(kbeg);
     for (int t0 = 0; t0 < ntiles; t0 += NWK) {
       __syncthreads();  // the previous tiles are no longer read
 #pragma unroll
       for (int kg = 0; kg < NWK; ++kg)
         if (t0 + kg < ntiles)
-          load_tile(a, lds + kg * L::kGroup, kscale_all + kg * 64, kv_row0, h,
-                    kv_lo + 64 * (t0 + kg), kv_hi);
+          issue_tile(lds + kg * kGroupBytes, kb, vb, ksb, vsb, rs, kv_lo + 64 * (t0 + kg), kv_hi);
+      wait_vmem();
       __syncthreads();
+      if constexpr (ACT == ACT_GELU) {
+#pragma unroll
+        for (int kg = 0; kg < NWK; ++kg)
+          if (t0 + kg < ntiles) key_scales(a.eps, lds + kg * kGroupBytes, kscale_all + kg * 64);
+        __syncthreads();
+      }
       const int tile = t0 + wk;
       if (tile >= ntiles || !wave_has_rows) continue;
       const int key0 = kv_lo + 64 * tile;
       if constexpr (WINDOW) {
-        const int kb = key0 / kBlock;
-        if (kb > wblk || kb < wblk - a.window_blocks + 1) continue;
+        const int kblk = key0 / kBlock;
+        if (kblk > wblk || kblk < wblk - a.window_blocks + 1) continue;
       }
-      const __bf16* ks = lds + wk * L::kGroup;
-      const __bf16* vt = ks + L::kKSize;
+      const unsigned char* ks = lds + wk * kGroupBytes;
+      const unsigned char* vs = ks + kTileBytes;
       const float* kscale = kscale_all + wk * 64;
 
       // S^T for two 32-key halves of the tile.
@@ -231,33 +279,46 @@ struct Attn {
       for (int st = 0; st < 2; ++st) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[st][i] = 0.f;
-        const __bf16* krow = ks + (32 * st + key_perm(l32)) * L::kKStride + (D / 2) * g;
 #pragma unroll
         for (int c = 0; c < kQChunks; ++c)
-          s[st] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(krow + 8 * c), qf[c], s[st]);
+          s[st] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(ks + st * 32 * kRowBytes + k_off[c]),
+                                qf[c], s[st]);
       }
       // Register i of half st holds key 32*st + 16*(i/8) + 8g + i%8 of the tile.
       const int nvalid = kv_hi - key0;  // keys at or beyond this index are outside
+      const bool ragged = nvalid < 64;
       if constexpr (ACT == ACT_SOFTMAX) {
         float mt = -__builtin_huge_valf();
+        if (ragged) {
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+          for (int st = 0; st < 2; ++st)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int kk = 32 * st + 16 * (i >> 3) + 8 * g + (i & 7);
-            const float x = kk < nvalid ? s[st][i] * a.score_scale : -__builtin_huge_valf();
-            s[st][i] = x;
-            mt = fmaxf(mt, x);
-          }
+            for (int i = 0; i < 16; ++i) {
+              const int kk = 32 * st + 16 * (i >> 3) + 8 * g + (i & 7);
+              s[st][i] = kk < nvalid ? s[st][i] * a.score_scale : -__builtin_huge_valf();
+              mt = fmaxf(mt, s[st][i]);
+            }
+        } else {
+#pragma unroll
+          for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              s[st][i] *= a.score_scale;
+              mt = fmaxf(mt, s[st][i]);
+            }
+        }
         mt = fmaxf(mt, other_half(mt));
         const float m_new = fmaxf(m, mt);
         const float m_use = m_new == -__builtin_huge_valf() ? 0.f : m_new;
-        const float alpha = fast_exp2(m - m_use);
-        l *= alpha;
+        if (__any(m_new != m)) {
+          const float alpha = fast_exp2(m - m_use);
+          l *= alpha;
 #pragma unroll
-        for (int t = 0; t < kOTiles; ++t)
+          for (int t = 0; t < kOTiles; ++t)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
+            for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
+          m = m_new;
+        }
 #pragma unroll
         for (int st = 0; st < 2; ++st)
 #pragma unroll
@@ -266,14 +327,14 @@ struct Attn {
             s[st][i] = p;
             l += p;
           }
-        m = m_new;
       } else {
 #pragma unroll
         for (int st = 0; st < 2; ++st)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int kk = 32 * st + 16 * (i >> 3) + 8 * g + (i & 7);
-            s[st][i] = kk < nvalid ? gelu_tanh(s[st][i] * rq * kscale[kk]) : 0.f;
+            const float gl = gelu_tanh(s[st][i] * rq * kscale[kk]);
+            s[st][i] = (!ragged || kk < nvalid) ? gl : 0.f;
           }
       }
       // O^T += V^T P^T over four 16-key chunks.
@@ -284,9 +345,16 @@ struct Attn {
         for (int j = 0; j < 8; ++j) pf[j] = (__bf16)s[kc >> 1][8 * (kc & 1) + j];
 #pragma unroll
         for (int t = 0; t < kOTiles; ++t) {
-          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(
-              vt + vt_row<D>(dim_perm<D>(t, l32)) + 16 * kc + 8 * g);
-          o[t] = mfma_32x32x16(vf, pf, o[t]);
+          const unsigned char* p0 = vs + v_row + kc * 16 * kRowBytes + v_col[t];
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 4 * kRowBytes));
+          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+          u32x4 w;
+          w[0] = lo2[0];
+          w[1] = lo2[1];
+          w[2] = hi2[0];
+          w[3] = hi2[1];
+          o[t] = mfma_32x32x16(__builtin_bit_cast(bf16x8, w), pf, o[t]);
         }
       }
     }
@@ -294,6 +362,7 @@ struct Attn {
     // Merge the key groups of a query group (NWK > 1) through LDS.
     if constexpr (NWK > 1) {
       constexpr int kRec = D / 2 + 2;  // floats per lane record: O half row, m, l
+      float* cbuf = reinterpret_cast<float*>(lds);
       __syncthreads();
       if (wk > 0) {
         float* rec = cbuf + (((wk - 1) * NWQ + wq) * 64 + lane) * kRec;
@@ -369,16 +438,19 @@ struct Attn {
 template <int D, int NWQ, int NWK, int ACT, int IN, bool WINDOW, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   using K = Attn<D, NWQ, NWK, ACT, IN, WINDOW, SPLIT>;
-  using L = Lds<D>;
-  constexpr int kTileBytes = NWK * L::kGroup * 2;
+  constexpr int kTileBytes = NWK * K::kGroupBytes;
   constexpr int kCombBytes = NWK > 1 ? (NWK - 1) * NWQ * 64 * (D / 2 + 2) * 4 : 0;
   constexpr int kBytes = kTileBytes > kCombBytes ? kTileBytes : kCombBytes;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kBytes];
   __shared__ float kscale[ACT == ACT_GELU ? NWK * 64 : 1];
-  const int n_items = a.hdr->n_items;
-  for (int idx = blockIdx.x; idx < n_items; idx += gridDim.x) {
-    K::run_item(a, a.items[idx], reinterpret_cast<__bf16*>(smem), kscale,
-                reinterpret_cast<float*>(smem));
+  // Items [xcd_begin[x], xcd_begin[x+1]) belong to XCD x = blockIdx.x % 8.
+  const int n = a.hdr->n_items;
+  const int x = blockIdx.x % kXcds;
+  const int beg = min(a.hdr->xcd_begin[x], n);
+  const int end = min(max(a.hdr->xcd_begin[x + 1], beg), n);
+  const int stride = gridDim.x / kXcds;
+  for (int idx = beg + int(blockIdx.x) / kXcds; idx < end; idx += stride) {
+    K::run_item(a, a.items[idx], smem, kscale);
     __syncthreads();
   }
 }
@@ -388,10 +460,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
 // plain sums.  Fixed split order, so the result is deterministic.
 template <int D>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
+  if (a.hdr->status != JA_OK) return;
   const int bh = blockIdx.x;
   const int b = bh / a.H, h = bh % a.H;
   const int ns = a.nsplit[b];
-  if (ns <= 1 || a.hdr->status != JA_OK) return;
+  if (ns <= 1) return;
   const int qbeg = a.qo[b], lq = a.qo[b + 1] - qbeg;
   const int lk = a.ko[b + 1] - a.ko[b];
   constexpr int kPer = D / 8;               // threads per row, 8 dims each
@@ -432,39 +505,61 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   }
 }
 
+// Workgroups resident per CU for one kernel instance (queried once).
 template <int D, int NWQ, int NWK, int ACT, int IN, bool WINDOW, bool SPLIT>
-hipError_t launch(const AttnArgs& a, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((attn_kernel<D, NWQ, NWK, ACT, IN, WINDOW, SPLIT>), dim3(grid), dim3(kThreads), 0, st, a);
+int resident_per_cu() {
+  static int cached = 0;
+  if (cached == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, attn_kernel<D, NWQ, NWK, ACT, IN, WINDOW, SPLIT>, kThreads, 0) != hipSuccess || n < 1)
+      n = 1;
+    cached = n;
+  }
+  return cached;
+}
+
+template <int D, int NWQ, int NWK, int ACT, int IN, bool WINDOW, bool SPLIT>
+hipError_t launch(const AttnArgs& a, int num_cu, int64_t max_items, hipStream_t st) {
+  // Persistent grid: each resident slot once, a multiple of the XCD count.
+  int64_t grid = int64_t(num_cu) * resident_per_cu<D, NWQ, NWK, ACT, IN, WINDOW, SPLIT>();
+  const int64_t need = ((max_items + kXcds - 1) / kXcds) * kXcds;
+  if (grid > need) grid = need;
+  grid = (grid / kXcds) * kXcds;
+  if (grid < kXcds) grid = kXcds;
+  hipLaunchKernelGGL((attn_kernel<D, NWQ, NWK, ACT, IN, WINDOW, SPLIT>), dim3(unsigned(grid)),
+                     dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
 template <int D, int IN>
-hipError_t launch_for_shape(int shape, int act, const AttnArgs& a, int grid, hipStream_t st) {
+hipError_t launch_for_shape(int shape, int act, const AttnArgs& a, int num_cu, int64_t max_items,
+                            hipStream_t st) {
   switch (shape) {
     case 0:  // query-tiled (self full, cross)
-      return act == ACT_SOFTMAX ? launch<D, 4, 1, ACT_SOFTMAX, IN, false, false>(a, grid, st)
-                                : launch<D, 4, 1, ACT_GELU, IN, false, false>(a, grid, st);
+      return act == ACT_SOFTMAX ? launch<D, 4, 1, ACT_SOFTMAX, IN, false, false>(a, num_cu, max_items, st)
+                                : launch<D, 4, 1, ACT_GELU, IN, false, false>(a, num_cu, max_items, st);
     case 1:  // block window (softmax only)
-      return launch<D, 2, 2, ACT_SOFTMAX, IN, true, false>(a, grid, st);
+      return launch<D, 2, 2, ACT_SOFTMAX, IN, true, false>(a, num_cu, max_items, st);
     default:  // key-split (PMA)
-      return act == ACT_SOFTMAX ? launch<D, 1, 4, ACT_SOFTMAX, IN, false, true>(a, grid, st)
-                                : launch<D, 1, 4, ACT_GELU, IN, false, true>(a, grid, st);
+      return act == ACT_SOFTMAX ? launch<D, 1, 4, ACT_SOFTMAX, IN, false, true>(a, num_cu, max_items, st)
+                                : launch<D, 1, 4, ACT_GELU, IN, false, true>(a, num_cu, max_items, st);
   }
 }
 
 }  // namespace
 
 // shape: 0 = query-tiled, 1 = block window, 2 = key-split.
-hipError_t launch_attn_mfma(int D, int in, int shape, int act, const AttnArgs& a, int grid,
-                            hipStream_t st) {
+hipError_t launch_attn_mfma(int D, int in, int shape, int act, const AttnArgs& a, int num_cu,
+                            int64_t max_items, hipStream_t st) {
   if (in == IN_BF16) {
-    if (D == 32) return launch_for_shape<32, IN_BF16>(shape, act, a, grid, st);
-    if (D == 64) return launch_for_shape<64, IN_BF16>(shape, act, a, grid, st);
-    return launch_for_shape<128, IN_BF16>(shape, act, a, grid, st);
+    if (D == 32) return launch_for_shape<32, IN_BF16>(shape, act, a, num_cu, max_items, st);
+    if (D == 64) return launch_for_shape<64, IN_BF16>(shape, act, a, num_cu, max_items, st);
+    return launch_for_shape<128, IN_BF16>(shape, act, a, num_cu, max_items, st);
   }
-  if (D == 32) return launch_for_shape<32, IN_MX>(shape, act, a, grid, st);
-  if (D == 64) return launch_for_shape<64, IN_MX>(shape, act, a, grid, st);
-  return launch_for_shape<128, IN_MX>(shape, act, a, grid, st);
+  if (D == 32) return launch_for_shape<32, IN_MX>(shape, act, a, num_cu, max_items, st);
+  if (D == 64) return launch_for_shape<64, IN_MX>(shape, act, a, num_cu, max_items, st);
+  return launch_for_shape<128, IN_MX>(shape, act, a, num_cu, max_items, st);
 }
 
 hipError_t launch_combine(int D, const CombineArgs& a, hipStream_t st) {

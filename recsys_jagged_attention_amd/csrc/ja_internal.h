@@ -25,11 +25,15 @@ enum In { IN_F32 = 0, IN_BF16 = 1, IN_MX = 2 };
 //   items[max_items]    int4 {b, h, q0, split}
 //   part_o[max_slots][32][D] float, part_ml[max_slots][32] float2
 // ---------------------------------------------------------------------------
+constexpr int kXcds = 8;           // workgroup w runs on XCD w % 8 (round-robin dispatch)
+
 struct WsHeader {
-  int32_t status;      // JA_OK or JA_EOFFSETS, written by the plan kernel
-  int32_t n_items;     // work items for the attention kernel
-  int32_t n_slots;     // partial slots in use
-  int32_t pad[61];
+  int32_t status;              // JA_OK or JA_EOFFSETS, written by the plan kernel
+  int32_t n_items;             // work items for the attention kernel
+  int32_t n_slots;             // partial slots in use
+  int32_t pad0;
+  int32_t xcd_begin[kXcds + 1];  // items [xcd_begin[x], xcd_begin[x+1]) run on XCD x
+  int32_t pad[64 - 4 - (kXcds + 1)];
 };
 
 struct WsLayout {
@@ -52,6 +56,7 @@ struct PlanArgs {
   int B, H;
   int32_t total_q, total_kv;
   int bm, kvc, self_check;
+  int window_blocks;   // 0 = no window (used for the per-item cost estimate)
   int64_t max_items, max_slots;
   WsHeader* hdr;
   int32_t* nsplit;

@@ -5,9 +5,13 @@
 // summary of "GEM Training: How Meta Doubled the Efficiency of Its LLM-Scale
 // Ads Foundation Model", section "Generalized Dot-Product Attention（GDPA）").
 // Here the enumeration runs on the GPU, on the caller's stream, so the host
-// never reads the offsets: one workgroup validates the offsets, counts the
-// work items of every sample (zero-length samples produce none), scans the
-// counts and writes the item list the attention kernel walks.
+// never reads the offsets.  One workgroup:
+//  1. validates the offsets and sums the estimated cost of every sample;
+//  2. writes the work items (zero-length samples produce none), head-major
+//     within a sample so items that share K/V are adjacent, and
+//  3. cuts the item list into 8 contiguous ranges of equal estimated cost, one
+//     per XCD: an XCD's workgroups then share K/V through its own L2, and the
+//     XCDs finish together despite skewed lengths.
 #include "ja_internal.h"
 #include "jagged_attn.h"
 
@@ -16,111 +20,154 @@ namespace ja {
 namespace {
 
 constexpr int kPlanThreads = 1024;
+constexpr int kPlanWaves = kPlanThreads / 64;
 
-__device__ inline int wave_inclusive_scan(int x) {
+template <typename T>
+__device__ inline T wave_inclusive_scan(T x) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(x, o, 64);
+    T y = __shfl_up(x, o, 64);
     if (lane >= o) x += y;
   }
   return x;
 }
 
-// Exclusive scan of one value per thread over the whole 1024-thread block;
-// returns the exclusive prefix and writes the block total to *total.
-__device__ int block_exclusive_scan(int x, int* s_warp, int* total) {
+// Exclusive scan of one value per thread over the 1024-thread block; returns
+// the thread's exclusive prefix and the block total.
+template <typename T>
+__device__ T block_exclusive_scan(T x, T* s_warp, T* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int inc = wave_inclusive_scan(x);
+  const T inc = wave_inclusive_scan(x);
   if (lane == 63) s_warp[wave] = inc;
   __syncthreads();
   if (wave == 0) {
-    int w = lane < kPlanThreads / 64 ? s_warp[lane] : 0;
-    int wi = wave_inclusive_scan(w);
-    if (lane < kPlanThreads / 64) s_warp[16 + lane] = wi - w;
-    if (lane == kPlanThreads / 64 - 1) s_warp[32] = wi;
+    const T w = lane < kPlanWaves ? s_warp[lane] : T(0);
+    const T wi = wave_inclusive_scan(w);
+    if (lane < kPlanWaves) s_warp[kPlanWaves + lane] = wi - w;
+    if (lane == kPlanWaves - 1) s_warp[2 * kPlanWaves] = wi;
   }
   __syncthreads();
-  int r = inc - x + s_warp[16 + wave];
-  *total = s_warp[32];
+  const T r = inc - x + s_warp[kPlanWaves + wave];
+  *total = s_warp[2 * kPlanWaves];
   __syncthreads();
   return r;
+}
+
+struct SampleWork {
+  int cnt;      // work items
+  int ns;       // key splits
+  int nqt;      // query tiles
+  int slots;    // partial slots
+  double ck;    // estimated cost of one item (keys it touches + fixed overhead)
+};
+
+__device__ inline SampleWork sample_work(const PlanArgs& a, int lq, int lk) {
+  SampleWork w{0, 1, 0, 0, 0.0};
+  if (lq <= 0) return w;
+  w.nqt = (lq + a.bm - 1) / a.bm;
+  if (a.kvc > 0 && w.nqt == 1 && lk > a.kvc) w.ns = (lk + a.kvc - 1) / a.kvc;
+  w.cnt = a.H * w.nqt * w.ns;
+  w.slots = w.ns > 1 ? a.H * w.ns : 0;
+  int keys = lk;
+  if (w.ns > 1) keys = a.kvc;
+  if (a.window_blocks > 0) keys = min(lk, a.window_blocks * kBlock);
+  w.ck = double(keys) + 64.0;
+  return w;
+}
+
+__device__ inline void fail(const PlanArgs& a) {
+  a.hdr->status = JA_EOFFSETS;
+  a.hdr->n_items = 0;
+  a.hdr->n_slots = 0;
+  for (int x = 0; x <= kXcds; ++x) a.hdr->xcd_begin[x] = 0;
 }
 
 }  // namespace
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ int s_bad;
-  __shared__ int s_warp[48];
-  __shared__ int s_cnt[kPlanThreads];
-  __shared__ int s_base[kPlanThreads];
-  __shared__ int s_nqt[kPlanThreads];
-  __shared__ int s_ns[kPlanThreads];
+  __shared__ int s_iwarp[3 * kPlanWaves];
+  __shared__ double s_dwarp[3 * kPlanWaves];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   if (tid == 0) s_bad = 0;
   __syncthreads();
 
-  // 1. Validate: offsets start at 0, never decrease, end at the totals;
-  //    self-attention needs identical query and key offsets.
+  // Pass 1: validate; total items, partial slots and estimated cost.
+  // Offsets start at 0, never decrease and end at the totals; self-attention
+  // needs identical query and key offsets.
   int bad = 0;
+  long long my_items = 0, my_slots = 0;
+  double my_cost = 0.0;
   for (int b = tid; b <= a.B; b += kPlanThreads) {
     const int q = a.qo[b], k = a.ko[b];
     if (b == 0 && (q != 0 || k != 0)) bad = 1;
     if (b == a.B && (q != a.total_q || k != a.total_kv)) bad = 1;
-    if (b < a.B && (a.qo[b + 1] < q || a.ko[b + 1] < k)) bad = 1;
     if (a.self_check && q != k) bad = 1;
+    if (b < a.B) {
+      const int q1 = a.qo[b + 1], k1 = a.ko[b + 1];
+      if (q1 < q || k1 < k) bad = 1;
+      const SampleWork w = sample_work(a, q1 - q, k1 - k);
+      my_items += w.cnt;
+      my_slots += w.slots;
+      my_cost += w.cnt * w.ck;
+    }
   }
   if (bad) atomicOr(&s_bad, 1);
-  __syncthreads();
-  if (s_bad) {
-    if (tid == 0) {
-      a.hdr->status = JA_EOFFSETS;
-      a.hdr->n_items = 0;
-      a.hdr->n_slots = 0;
-    }
+  double total_cost;
+  (void)block_exclusive_scan(my_cost, s_dwarp, &total_cost);
+  long long total_items_ll = 0, total_slots_ll = 0;
+  {
+    // int sums through the double scan are exact (< 2^53)
+    double ti, ts;
+    (void)block_exclusive_scan(double(my_items), s_dwarp, &ti);
+    (void)block_exclusive_scan(double(my_slots), s_dwarp, &ts);
+    total_items_ll = (long long)ti;
+    total_slots_ll = (long long)ts;
+  }
+  if (s_bad || total_items_ll > a.max_items || total_slots_ll > a.max_slots) {
+    if (tid == 0) fail(a);
     return;
   }
 
-  // 2./3. Per chunk of 1024 samples: count, scan, write the items.
-  int64_t item_carry = 0, slot_carry = 0;
+  // Pass 2: per chunk of 1024 samples, scan and write items, splits, slot
+  // bases and the XCD cut points.
+  __shared__ int s_cnt[kPlanThreads];
+  __shared__ int s_base[kPlanThreads];
+  __shared__ int s_nqt[kPlanThreads];
+  __shared__ int s_ns[kPlanThreads];
+  int item_carry = 0, slot_carry = 0;
+  double cost_carry = 0.0;
   for (int base = 0; base < a.B; base += kPlanThreads) {
     const int b = base + tid;
-    int cnt = 0, ns = 1, nqt = 0, slots = 0;
-    if (b < a.B) {
-      const int lq = a.qo[b + 1] - a.qo[b];
-      const int lk = a.ko[b + 1] - a.ko[b];
-      if (lq > 0) {
-        nqt = (lq + a.bm - 1) / a.bm;
-        if (a.kvc > 0 && nqt == 1 && lk > a.kvc) ns = (lk + a.kvc - 1) / a.kvc;
-        cnt = a.H * nqt * ns;
-        slots = ns > 1 ? a.H * ns : 0;
-      }
-    }
+    SampleWork w{0, 1, 0, 0, 0.0};
+    if (b < a.B) w = sample_work(a, a.qo[b + 1] - a.qo[b], a.ko[b + 1] - a.ko[b]);
     int items_total, slots_total;
-    const int ibase = block_exclusive_scan(cnt, s_warp, &items_total);
-    const int sbase = block_exclusive_scan(slots, s_warp, &slots_total);
-    if (item_carry + items_total > a.max_items || slot_carry + slots_total > a.max_slots) {
-      if (tid == 0) {
-        a.hdr->status = JA_EOFFSETS;
-        a.hdr->n_items = 0;
-        a.hdr->n_slots = 0;
-      }
-      return;
-    }
+    double cost_total;
+    const int ibase = block_exclusive_scan(w.cnt, s_iwarp, &items_total) + item_carry;
+    const int sbase = block_exclusive_scan(w.slots, s_iwarp, &slots_total) + slot_carry;
+    const double cbase = block_exclusive_scan(w.cnt * w.ck, s_dwarp, &cost_total) + cost_carry;
     if (b < a.B) {
-      a.nsplit[b] = ns;
-      a.pbase[b] = int(slot_carry) + sbase;
+      a.nsplit[b] = w.ns;
+      a.pbase[b] = sbase;
+      // XCD x starts at the item holding cost x/8 of the total.
+      for (int x = 1; x < kXcds; ++x) {
+        const double target = total_cost * x / kXcds;
+        if (w.cnt > 0 && target >= cbase && target < cbase + w.cnt * w.ck) {
+          const int k = min(w.cnt - 1, int((target - cbase) / w.ck));
+          a.hdr->xcd_begin[x] = ibase + k;
+        }
+      }
     }
-    s_cnt[tid] = cnt;
-    s_base[tid] = int(item_carry) + ibase;
-    s_nqt[tid] = nqt;
-    s_ns[tid] = ns;
+    s_cnt[tid] = w.cnt;
+    s_base[tid] = ibase;
+    s_nqt[tid] = w.nqt;
+    s_ns[tid] = w.ns;
     __syncthreads();
-    // One wave per sample; its lanes write the sample's items (head-major,
-    // then query tile, then key split) so items sharing K/V stay adjacent.
+    // One wave per sample writes its items: head-major, then query tile, then split.
     const int nchunk = min(kPlanThreads, a.B - base);
-    for (int j = wave; j < nchunk; j += kPlanThreads / 64) {
+    for (int j = wave; j < nchunk; j += kPlanWaves) {
       const int c = s_cnt[j], ib = s_base[j], nq = s_nqt[j], nsj = s_ns[j];
       for (int t = lane; t < c; t += 64) {
         const int s = t % nsj;
@@ -131,20 +178,23 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     }
     item_carry += items_total;
     slot_carry += slots_total;
+    cost_carry += cost_total;
     __syncthreads();
   }
   if (tid == 0) {
     a.hdr->status = JA_OK;
-    a.hdr->n_items = int(item_carry);
-    a.hdr->n_slots = int(slot_carry);
+    a.hdr->n_items = item_carry;
+    a.hdr->n_slots = slot_carry;
+    a.hdr->xcd_begin[0] = 0;
+    a.hdr->xcd_begin[kXcds] = item_carry;
+    if (total_cost <= 0.0)
+      for (int x = 1; x < kXcds; ++x) a.hdr->xcd_begin[x] = 0;
   }
 }
 
-}  // namespace ja
-
-namespace ja {
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, st, a);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, a);
   return hipGetLastError();
 }
+
 }  // namespace ja
