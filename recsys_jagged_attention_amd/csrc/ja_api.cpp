@@ -76,7 +76,7 @@ Plan make_plan(int B, int H, int D, int variant, int window, int dtype, int32_t 
     p.bm = 64;
   } else if (window > 0) {
     p.shape = kShapeWindow;
-    p.bm = 64;
+    p.bm = 128;
   } else if (variant == JA_PMA) {
     p.shape = kShapeKvSplit;
     p.bm = kPmaRows;
@@ -168,6 +168,7 @@ int jagged_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
   pa.kvc = p.kvc;
   pa.self_check = variant == JA_SELF;
   pa.window_blocks = window / kBlock;
+  pa.kv_row_bytes = io->dtype == JA_BF16 ? int64_t(H) * D * 2 : 0;  // 32-bit DMA offsets
   pa.max_items = p.ws.max_items;
   pa.max_slots = p.ws.max_slots;
   pa.hdr = hdr;

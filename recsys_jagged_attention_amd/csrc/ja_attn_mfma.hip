@@ -7,13 +7,16 @@
 // "Generalized Dot-Product Attention（GDPA）"): the four waves of a workgroup
 // are split NWQ x NWK between query rows (32 per wave) and key tiles (64 keys
 // per tile), so long-query shapes use NWQ=4, the 64-token block window uses
-// NWQ=2 x NWK=2 (one query block, its window split over two wave pairs) and
-// PMA (32 queries, long keys) uses NWK=4 plus a key split across workgroups.
+// NWQ=4 on two consecutive query blocks (their windows share all but one key
+// block; each wave skips the one tile outside its own window) and PMA (32
+// queries, long keys) uses NWK=4 plus a key split across workgroups.
 //
 // Data path.  K and V tiles go from HBM straight into LDS (global_load_lds,
 // 16 bytes per lane, no register staging), row-major with the 16-byte chunks
 // of each row XOR-swizzled so that the MFMA operand reads below are free of
-// bank conflicts.  Q stays in registers for the whole item.
+// bank conflicts.  Two LDS stages: while the waves compute on one, the next
+// tile group -- or the next work item's first -- is already in flight into
+// the other.  Q stays in registers for the whole item.
 //
 // Score tiles are computed transposed, S^T = K Q^T, with K from LDS as the A
 // operand and Q as the B operand: the 32x32 result leaves every lane holding
@@ -77,9 +80,28 @@ __device__ __forceinline__ bf16x8 zero8() {
   return z;
 }
 
-__device__ __forceinline__ void wait_vmem() {
-  // s_waitcnt vmcnt(0): direct-to-LDS loads complete before the barrier
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+// 16 bytes per lane from global memory (SGPR base + 32-bit lane offset) into
+// LDS at M0 + 16*lane.  Issued as inline asm on purpose: the compiler does not
+// track it, so it neither drains the prefetch with a conservative vmcnt(0)
+// before every later LDS read nor keeps 64-bit lane addresses live.  Completion
+// is ordered by wait_vmcnt() + lds_barrier() below.  No compiler-generated code
+// in these kernels reads M0 (checked in the generated ISA).  `dep` only pins
+// the instruction after the value it names has been computed.
+__device__ __forceinline__ void lds_dma16(const void* sbase, unsigned voff, unsigned lds_addr, float dep) {
+  // the base and the LDS address are wave-uniform: make that explicit for the "s" operands
+  const uintptr_t p = reinterpret_cast<uintptr_t>(sbase);
+  // (readfirstlane returns int: convert through unsigned so nothing is sign-extended)
+  const uint64_t hi = unsigned(__builtin_amdgcn_readfirstlane(unsigned(p >> 32)));
+  const uint64_t lo = unsigned(__builtin_amdgcn_readfirstlane(unsigned(p)));
+  const uint64_t pu = (hi << 32) | lo;
+  const unsigned lu = unsigned(__builtin_amdgcn_readfirstlane(lds_addr));
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(reinterpret_cast<const void*>(pu)), "s"(lu), "v"(dep) : "memory", "m0");
+}
+
+__device__ __forceinline__ unsigned lds_addr_of(const void* p) {
+  return static_cast<unsigned>(reinterpret_cast<uintptr_t>(
+      (const __attribute__((address_space(3))) unsigned char*)(p)));
 }
 
 template <int D, int NWQ, int NWK, int ACT, int IN, bool WINDOW, bool SPLIT>
@@ -97,10 +119,15 @@ struct Attn {
   static __device__ __forceinline__ void issue_tile(unsigned char* grp, const __bf16* kb,
                                                     const __bf16* vb, const uint8_t* ksb,
                                                     const uint8_t* vsb, size_t rs, int key0,
-                                                    int kv_end) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+                                                    int kv_end, float dep) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     if constexpr (IN == IN_BF16) {
-      // 2 * kSegs segments of 1 KB (K then V), 4 waves round-robin.
+      // 2 * kSegs segments of 1 KB (K then V), 4 waves round-robin.  Byte
+      // offsets from the item's base fit 32 bits (the plan rejects larger
+      // samples).
+      const unsigned row_bytes = unsigned(rs) * 2u;
+      const unsigned grp_lds = lds_addr_of(grp);
 #pragma unroll
       for (int s = wave; s < 2 * kSegs; s += 4) {
         const bool is_v = s >= kSegs;
@@ -109,10 +136,9 @@ struct Attn {
         const int row = byte / kRowBytes;
         const int phys = (byte % kRowBytes) / 16;
         const int c = phys ^ (is_v ? swz_v<D>(row) : swz_k<D>(row));
-        const int key = min(key0 + row, kv_end - 1);
-        const __bf16* src = (is_v ? vb : kb) + size_t(key) * rs + 8 * c;
-        unsigned char* dst = grp + (is_v ? kTileBytes : 0) + seg * 1024;
-        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+        const unsigned key = unsigned(min(key0 + row, kv_end - 1));
+        lds_dma16(is_v ? (const void*)vb : (const void*)kb, key * row_bytes + 16u * unsigned(c),
+                  grp_lds + (is_v ? kTileBytes : 0) + seg * 1024, dep);
       }
     } else {
       // MX: decode 8 e4m3 codes x 2^(E-127) to bf16 through registers.
@@ -152,57 +178,151 @@ struct Attn {
     if (part == 0) kscale[row] = __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
   }
 
-  static __device__ void run_item(const AttnArgs& a, const int4 item, unsigned char* lds,
-                                  float* kscale_all) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wq = wave % NWQ, wk = wave / NWQ;
-    const int l32 = lane & 31, g = lane >> 5;
-    const int b = item.x, h = item.y, q0 = item.z, split = item.w;
-    const int qbeg = a.qo[b], lq = a.qo[b + 1] - qbeg;
-    const int kbeg = a.ko[b], lk = a.ko[b + 1] - kbeg;
+  // Per-item context (wave-uniform).
+  struct Item {
+    int b, h, q0, split, qbeg, lq, lk, kv_lo, kv_hi, ntiles;
+    const __bf16* kb;   // key row r of this head starts at kb + r * rs (elements; bytes for MX)
+    const __bf16* vb;
+    const uint8_t* ksb;  // MX scales of key row r start at ksb + r * rs / 32
+    const uint8_t* vsb;
+  };
 
-    int kv_lo = 0, kv_hi = lk;
+  static __device__ __forceinline__ Item make_item(const AttnArgs& a, const int4 it, size_t rs) {
+    Item c;
+    c.b = it.x;
+    c.h = it.y;
+    c.q0 = it.z;
+    c.split = it.w;
+    c.qbeg = a.qo[c.b];
+    c.lq = a.qo[c.b + 1] - c.qbeg;
+    const int kbeg = a.ko[c.b];
+    c.lk = a.ko[c.b + 1] - kbeg;
+    c.kv_lo = 0;
+    c.kv_hi = c.lk;
     if constexpr (SPLIT) {
-      if (a.nsplit[b] > 1) {
-        kv_lo = split * a.kvc;
-        kv_hi = min(lk, kv_lo + a.kvc);
+      if (a.nsplit[c.b] > 1) {
+        c.kv_lo = c.split * a.kvc;
+        c.kv_hi = min(c.lk, c.kv_lo + a.kvc);
       }
     }
     if constexpr (WINDOW) {
-      const int qlast = min(q0 + 32 * NWQ, lq) - 1;
-      kv_lo = max(0, q0 / kBlock - a.window_blocks + 1) * kBlock;
-      kv_hi = min(lk, (qlast / kBlock + 1) * kBlock);
+      const int qlast = min(c.q0 + 32 * NWQ, c.lq) - 1;
+      c.kv_lo = max(0, c.q0 / kBlock - a.window_blocks + 1) * kBlock;
+      c.kv_hi = min(c.lk, (qlast / kBlock + 1) * kBlock);
     }
-    const int ntiles = kv_hi > kv_lo ? (kv_hi - kv_lo + 63) / 64 : 0;
+    c.ntiles = c.kv_hi > c.kv_lo ? (c.kv_hi - c.kv_lo + 63) / 64 : 0;
+    const size_t kv_off = size_t(kbeg) * rs + size_t(c.h) * D;
+    if constexpr (IN == IN_BF16) {
+      c.kb = reinterpret_cast<const __bf16*>(a.k) + kv_off;
+      c.vb = reinterpret_cast<const __bf16*>(a.v) + kv_off;
+      c.ksb = nullptr;
+      c.vsb = nullptr;
+    } else {
+      c.kb = reinterpret_cast<const __bf16*>(reinterpret_cast<const uint8_t*>(a.k) + kv_off);
+      c.vb = reinterpret_cast<const __bf16*>(reinterpret_cast<const uint8_t*>(a.v) + kv_off);
+      c.ksb = a.ks + (size_t(kbeg) * a.H + c.h) * (D / kMxBlock);
+      c.vsb = a.vs + (size_t(kbeg) * a.H + c.h) * (D / kMxBlock);
+    }
+    return c;
+  }
 
-    const int qrow_w = q0 + 32 * wq;          // first row of this wave (sample-local)
-    const bool wave_has_rows = qrow_w < lq;
+  // Direct-to-LDS load instructions one wave issues per key tile.
+  static constexpr int kLoadsPerTile = IN == IN_BF16 ? (2 * kSegs) / 4 : 0;
+
+  // Issue the tiles [t0, t0 + NWK) of an item into one stage; returns the
+  // number of VMEM instructions this wave issued.
+  static __device__ __forceinline__ int issue_group(const Item& c, unsigned char* stage_base, int t0,
+                                                    size_t rs, float dep = 0.f) {
+    int n = 0;
+#pragma unroll
+    for (int kg = 0; kg < NWK; ++kg)
+      if (t0 + kg < c.ntiles) {
+        issue_tile(stage_base + kg * kGroupBytes, c.kb, c.vb, c.ksb, c.vsb, rs, c.kv_lo + 64 * (t0 + kg),
+                   c.kv_hi, dep);
+        n += kLoadsPerTile;
+      }
+    return n;
+  }
+};
+
+// Wait until at most n of this wave's VMEM instructions are outstanding.
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  // s_waitcnt encoding (gfx9): vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]
+#define JA_VMCNT(k) case k: __builtin_amdgcn_s_waitcnt(((k) & 15) | (((k) >> 4) << 14) | 0x0F70); break;
+  switch (n) {
+    JA_VMCNT(0) JA_VMCNT(1) JA_VMCNT(2) JA_VMCNT(3) JA_VMCNT(4) JA_VMCNT(5) JA_VMCNT(6) JA_VMCNT(7)
+    JA_VMCNT(8) JA_VMCNT(9) JA_VMCNT(10) JA_VMCNT(11) JA_VMCNT(12) JA_VMCNT(13) JA_VMCNT(14)
+    JA_VMCNT(15) JA_VMCNT(16)
+    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+  }
+#undef JA_VMCNT
+}
+
+// Workgroup barrier for LDS hand-offs that does not drain outstanding global
+// loads (a __syncthreads() fence would wait for the prefetch too).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+template <int D, int NWQ, int NWK, int ACT, int IN, bool WINDOW, bool SPLIT>
+__global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
+  using K = Attn<D, NWQ, NWK, ACT, IN, WINDOW, SPLIT>;
+  using Item = typename K::Item;
+  constexpr int kStageBytes = NWK * K::kGroupBytes;
+  constexpr int kQChunks = K::kQChunks, kOTiles = K::kOTiles, kRowBytes = K::kRowBytes;
+  constexpr int kTileBytes = K::kTileBytes;
+  // Two stages when they fit in LDS (prefetch overlaps compute), else one.
+  constexpr int kStages = 2 * kStageBytes <= 128 * 1024 ? 2 : 1;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages * kStageBytes];
+  __shared__ float kscale_all[ACT == ACT_GELU ? kStages * NWK * 64 : 1];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wq = wave % NWQ, wk = wave / NWQ;
+  const int l32 = lane & 31, g = lane >> 5;
+  const size_t rs = size_t(a.H) * D;
+
+  // Items [xcd_begin[x], xcd_begin[x+1]) belong to XCD x = blockIdx.x % 8.
+  const int n = a.hdr->n_items;
+  const int x = blockIdx.x % kXcds;
+  const int beg = min(a.hdr->xcd_begin[x], n);
+  const int end = min(max(a.hdr->xcd_begin[x + 1], beg), n);
+  const int stride = gridDim.x / kXcds;
+  int idx = beg + int(blockIdx.x) / kXcds;
+  if (idx >= end) return;
+
+  // Lane-constant LDS byte offsets of the MFMA operand reads.
+  const int kp = key_perm(l32);
+  int k_off[kQChunks];
+#pragma unroll
+  for (int c = 0; c < kQChunks; ++c) k_off[c] = kp * kRowBytes + 16 * ((kQChunks * g + c) ^ swz_k<D>(kp));
+  const int v_row = (8 * g + ((lane & 15) >> 2)) * kRowBytes;
+  int v_col[kOTiles];
+#pragma unroll
+  for (int t = 0; t < kOTiles; ++t) {
+    const int col = dim_perm<D>(t, 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+    v_col[t] = 16 * ((col >> 3) ^ swz_v<D>((lane & 15) >> 2)) + 8 * ((col & 7) >> 2);
+  }
+  const float c2 = a.score_scale;  // softmax: log2(e)/sqrt(D); GELU: 1/sqrt(D)
+
+  Item cur = K::make_item(a, a.items[idx], rs);
+  int stage = 0;
+  K::issue_group(cur, smem, 0, rs);
+
+  while (true) {
+    const int qrow_w = cur.q0 + 32 * wq;      // first row of this wave (sample-local)
+    const bool wave_has_rows = qrow_w < cur.lq;
     const int qrow = qrow_w + l32;
-    const bool qvalid = qrow < lq;
+    const bool qvalid = qrow < cur.lq;
     const int wblk = qrow_w / kBlock;
 
-    // Per-item base pointers: key row r of head h starts at base + r * rs.
-    const size_t rs = size_t(a.H) * D;
-    const size_t kv_off = size_t(kbeg) * rs + size_t(h) * D;
-    const __bf16* kb;
-    const __bf16* vb;
-    const uint8_t* ksb = nullptr;
-    const uint8_t* vsb = nullptr;
-    if constexpr (IN == IN_BF16) {
-      kb = reinterpret_cast<const __bf16*>(a.k) + kv_off;
-      vb = reinterpret_cast<const __bf16*>(a.v) + kv_off;
-    } else {
-      // e4m3 codes are bytes: the element offset is the byte offset
-      kb = reinterpret_cast<const __bf16*>(reinterpret_cast<const uint8_t*>(a.k) + kv_off);
-      vb = reinterpret_cast<const __bf16*>(reinterpret_cast<const uint8_t*>(a.v) + kv_off);
-      ksb = a.ks + (size_t(kbeg) * a.H + h) * (D / kMxBlock);
-      vsb = a.vs + (size_t(kbeg) * a.H + h) * (D / kMxBlock);
-    }
-
-    // Q fragment: lane holds dims [(D/2)g, (D/2)g + D/2) of its query row.
+    // Q fragment: lane holds dims [(D/2)g, (D/2)g + D/2) of its query row
+    // (rows past the sample load the last row and are zeroed).
     bf16x8 qf[kQChunks];
-    if (qvalid) {
-      const size_t row = size_t(qbeg + qrow) * a.H + h;
+    {
+      const size_t row = size_t(cur.qbeg + min(qrow, cur.lq - 1)) * a.H + cur.h;
 #pragma unroll
       for (int c = 0; c < kQChunks; ++c) {
         const int d0 = (D / 2) * g + 8 * c;
@@ -212,10 +332,8 @@ struct Attn {
           qf[c] = decode_mx8(*reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(a.q) + row * D + d0),
                              a.qs[row * (D / kMxBlock) + d0 / kMxBlock]);
         }
+        if (!qvalid) qf[c] = zero8();
       }
-    } else {
-#pragma unroll
-      for (int c = 0; c < kQChunks; ++c) qf[c] = zero8();
     }
     float rq = 1.0f;
     if constexpr (ACT == ACT_GELU) {
@@ -225,145 +343,157 @@ struct Attn {
 #pragma unroll
         for (int j = 0; j < 8; ++j) ss = fmaf(float(qf[c][j]), float(qf[c][j]), ss);
       ss += other_half(ss);
-      rq = __builtin_amdgcn_rsqf(ss * (1.0f / D) + a.eps) * a.score_scale;
+      rq = __builtin_amdgcn_rsqf(ss * (1.0f / D) + a.eps) * c2;
     }
 
-    // Lane-constant LDS byte offsets of the MFMA operand reads.
-    const int kp = key_perm(l32);
-    int k_off[kQChunks];
-#pragma unroll
-    for (int c = 0; c < kQChunks; ++c) k_off[c] = kp * kRowBytes + 16 * ((kQChunks * g + c) ^ swz_k<D>(kp));
-    const int v_row = (8 * g + ((lane & 15) >> 2)) * kRowBytes;
-    int v_col[kOTiles];
-#pragma unroll
-    for (int t = 0; t < kOTiles; ++t) {
-      const int col = dim_perm<D>(t, 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
-      v_col[t] = 16 * ((col >> 3) ^ swz_v<D>((lane & 15) >> 2)) + 8 * ((col & 7) >> 2);
-    }
+    const int next_idx = idx + stride;
+    const bool has_next = next_idx < end;
+    Item nxt = cur;
+    if (has_next) nxt = K::make_item(a, a.items[next_idx], rs);
 
     f32x16 o[kOTiles];
 #pragma unroll
     for (int t = 0; t < kOTiles; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
-    float m = -__builtin_huge_valf(), l = 0.f;
+    float m = -__builtin_huge_valf(), l = 0.f;  // m in raw score units
 
-    for (int t0 = 0; t0 < ntiles; t0 += NWK) {
-      __syncthreads();  // the previous tiles are no longer read
-#pragma unroll
-      for (int kg = 0; kg < NWK; ++kg)
-        if (t0 + kg < ntiles)
-          issue_tile(lds + kg * kGroupBytes, kb, vb, ksb, vsb, rs, kv_lo + 64 * (t0 + kg), kv_hi);
-      wait_vmem();
-      __syncthreads();
+    for (int t0 = 0; t0 < cur.ntiles; t0 += NWK) {
+      int pf = 0;
+      // Prefetch the next tile group (or the next item's first) into the other
+      // stage.  In an item's first iteration this happens after the first
+      // score MFMAs instead, once the Q loads (tracked by the compiler, which
+      // waits for all loads before their first use) have completed.
+      unsigned char* other = smem + (stage ^ 1) * kStageBytes;
+      if constexpr (kStages == 2) {
+        if (t0 > 0) {
+          if (t0 + NWK < cur.ntiles) pf = K::issue_group(cur, other, t0 + NWK, rs);
+          else if (has_next) pf = K::issue_group(nxt, other, 0, rs);
+        }
+      } else {
+        if (t0 > 0) K::issue_group(cur, smem, t0, rs);  // group 0 was issued before the item
+      }
+      wait_vmcnt(pf);
+      lds_barrier();
+      unsigned char* st_base = smem + stage * kStageBytes;
+      float* kscale_st = kscale_all + (ACT == ACT_GELU ? stage * NWK * 64 : 0);
       if constexpr (ACT == ACT_GELU) {
 #pragma unroll
         for (int kg = 0; kg < NWK; ++kg)
-          if (t0 + kg < ntiles) key_scales(a.eps, lds + kg * kGroupBytes, kscale_all + kg * 64);
-        __syncthreads();
+          if (t0 + kg < cur.ntiles) K::key_scales(a.eps, st_base + kg * K::kGroupBytes, kscale_st + kg * 64);
+        lds_barrier();
       }
       const int tile = t0 + wk;
-      if (tile >= ntiles || !wave_has_rows) continue;
-      const int key0 = kv_lo + 64 * tile;
+      bool active = tile < cur.ntiles && wave_has_rows;
+      const int key0 = cur.kv_lo + 64 * tile;
       if constexpr (WINDOW) {
         const int kblk = key0 / kBlock;
-        if (kblk > wblk || kblk < wblk - a.window_blocks + 1) continue;
+        active = active && kblk <= wblk && kblk >= wblk - a.window_blocks + 1;
       }
-      const unsigned char* ks = lds + wk * kGroupBytes;
+      const unsigned char* ks = st_base + wk * K::kGroupBytes;
       const unsigned char* vs = ks + kTileBytes;
-      const float* kscale = kscale_all + wk * 64;
-
+      const float* kscale = kscale_st + wk * 64;
       // S^T for two 32-key halves of the tile.
       f32x16 s[2];
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
+      for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[st][i] = 0.f;
+      if (active) {
 #pragma unroll
-        for (int c = 0; c < kQChunks; ++c)
-          s[st] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(ks + st * 32 * kRowBytes + k_off[c]),
-                                qf[c], s[st]);
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int c = 0; c < kQChunks; ++c)
+            s[st] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(ks + st * 32 * kRowBytes + k_off[c]),
+                                  qf[c], s[st]);
       }
-      // Register i of half st holds key 32*st + 16*(i/8) + 8g + i%8 of the tile.
-      const int nvalid = kv_hi - key0;  // keys at or beyond this index are outside
-      const bool ragged = nvalid < 64;
-      if constexpr (ACT == ACT_SOFTMAX) {
-        float mt = -__builtin_huge_valf();
-        if (ragged) {
+      if constexpr (kStages == 2) {
+        if (t0 == 0) {  // every wave issues its share of the tile loads
+          if (NWK < cur.ntiles) K::issue_group(cur, other, NWK, rs, s[1][15]);
+          else if (has_next) K::issue_group(nxt, other, 0, rs, s[1][15]);
+        }
+      }
+      if (active) {
+        // Register i of half st holds key 32*st + 16*(i/8) + 8g + i%8 of the tile.
+        const int nvalid = cur.kv_hi - key0;  // keys at or beyond this index are outside
+        const bool ragged = nvalid < 64;
+        if constexpr (ACT == ACT_SOFTMAX) {
+          if (ragged) {
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const int kk = 32 * st + 16 * (i >> 3) + 8 * g + (i & 7);
+                if (kk >= nvalid) s[st][i] = -__builtin_huge_valf();
+              }
+          }
+          float mt = -__builtin_huge_valf();
+#pragma unroll
+          for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[st][i]);
+          mt = fmaxf(mt, other_half(mt));
+          const float m_new = fmaxf(m, mt);
+          if (__any(m_new != m)) {
+            const float alpha = m == -__builtin_huge_valf() ? 0.f : fast_exp2((m - m_new) * c2);
+            l *= alpha;
+#pragma unroll
+            for (int t = 0; t < kOTiles; ++t)
+#pragma unroll
+              for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
+            m = m_new;
+          }
+          const float mc = m == -__builtin_huge_valf() ? 0.f : m * c2;
 #pragma unroll
           for (int st = 0; st < 2; ++st)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-              const int kk = 32 * st + 16 * (i >> 3) + 8 * g + (i & 7);
-              s[st][i] = kk < nvalid ? s[st][i] * a.score_scale : -__builtin_huge_valf();
-              mt = fmaxf(mt, s[st][i]);
+              const float p = fast_exp2(fmaf(s[st][i], c2, -mc));
+              s[st][i] = p;
+              l += p;
             }
         } else {
 #pragma unroll
           for (int st = 0; st < 2; ++st)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-              s[st][i] *= a.score_scale;
-              mt = fmaxf(mt, s[st][i]);
+              const int kk = 32 * st + 16 * (i >> 3) + 8 * g + (i & 7);
+              const float gl = gelu_tanh(s[st][i] * rq * kscale[kk]);
+              s[st][i] = (!ragged || kk < nvalid) ? gl : 0.f;
             }
         }
-        mt = fmaxf(mt, other_half(mt));
-        const float m_new = fmaxf(m, mt);
-        const float m_use = m_new == -__builtin_huge_valf() ? 0.f : m_new;
-        if (__any(m_new != m)) {
-          const float alpha = fast_exp2(m - m_use);
-          l *= alpha;
+        // O^T += V^T P^T over four 16-key chunks.
 #pragma unroll
-          for (int t = 0; t < kOTiles; ++t)
+        for (int kc = 0; kc < 4; ++kc) {
+          bf16x8 pf8;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
-          m = m_new;
-        }
+          for (int j = 0; j < 8; ++j) pf8[j] = (__bf16)s[kc >> 1][8 * (kc & 1) + j];
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float p = fast_exp2(s[st][i] - m_use);
-            s[st][i] = p;
-            l += p;
+          for (int t = 0; t < kOTiles; ++t) {
+            const unsigned char* p0 = vs + v_row + kc * 16 * kRowBytes + v_col[t];
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 4 * kRowBytes));
+            const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+            u32x4 w;
+            w[0] = lo2[0];
+            w[1] = lo2[1];
+            w[2] = hi2[0];
+            w[3] = hi2[1];
+            o[t] = mfma_32x32x16(__builtin_bit_cast(bf16x8, w), pf8, o[t]);
           }
-      } else {
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int kk = 32 * st + 16 * (i >> 3) + 8 * g + (i & 7);
-            const float gl = gelu_tanh(s[st][i] * rq * kscale[kk]);
-            s[st][i] = (!ragged || kk < nvalid) ? gl : 0.f;
-          }
-      }
-      // O^T += V^T P^T over four 16-key chunks.
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        bf16x8 pf;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pf[j] = (__bf16)s[kc >> 1][8 * (kc & 1) + j];
-#pragma unroll
-        for (int t = 0; t < kOTiles; ++t) {
-          const unsigned char* p0 = vs + v_row + kc * 16 * kRowBytes + v_col[t];
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 4 * kRowBytes));
-          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-          u32x4 w;
-          w[0] = lo2[0];
-          w[1] = lo2[1];
-          w[2] = hi2[0];
-          w[3] = hi2[1];
-          o[t] = mfma_32x32x16(__builtin_bit_cast(bf16x8, w), pf, o[t]);
         }
       }
+      lds_barrier();  // this stage may be refilled from the next iteration on
+      if constexpr (kStages == 2) stage ^= 1;
+    }
+    if constexpr (kStages == 2) {
+      if (cur.ntiles == 0 && has_next) K::issue_group(nxt, smem + stage * kStageBytes, 0, rs);
     }
 
-    // Merge the key groups of a query group (NWK > 1) through LDS.
+    // Merge the key groups of a query group (NWK > 1) through the free stage.
     if constexpr (NWK > 1) {
       constexpr int kRec = D / 2 + 2;  // floats per lane record: O half row, m, l
-      float* cbuf = reinterpret_cast<float*>(lds);
-      __syncthreads();
+      float* cbuf = reinterpret_cast<float*>(smem + (kStages == 2 ? (stage ^ 1) * kStageBytes : 0));
       if (wk > 0) {
         float* rec = cbuf + (((wk - 1) * NWQ + wq) * 64 + lane) * kRec;
 #pragma unroll
@@ -373,7 +503,7 @@ struct Attn {
         rec[D / 2] = m;
         rec[D / 2 + 1] = l;
       }
-      __syncthreads();
+      lds_barrier();
       if (wk == 0) {
 #pragma unroll
         for (int w = 1; w < NWK; ++w) {
@@ -381,8 +511,8 @@ struct Attn {
           if constexpr (ACT == ACT_SOFTMAX) {
             const float m2 = rec[D / 2], l2 = rec[D / 2 + 1];
             const float mn = fmaxf(m, m2);
-            const float mu = mn == -__builtin_huge_valf() ? 0.f : mn;
-            const float a1 = fast_exp2(m - mu), a2 = fast_exp2(m2 - mu);
+            const float a1 = m == -__builtin_huge_valf() ? 0.f : fast_exp2((m - mn) * c2);
+            const float a2 = m2 == -__builtin_huge_valf() ? 0.f : fast_exp2((m2 - mn) * c2);
 #pragma unroll
             for (int t = 0; t < kOTiles; ++t)
 #pragma unroll
@@ -397,61 +527,55 @@ struct Attn {
           }
         }
       }
+      lds_barrier();  // the merge buffer may be refilled by the next prefetch
     }
-    if (wk != 0 || !qvalid) return;
+    if constexpr (kStages == 1) {
+      if (has_next) K::issue_group(nxt, smem, 0, rs);  // LDS is free again
+    }
 
-    const float l_tot = l + other_half(l);
-    if constexpr (SPLIT) {
-      const int ns = a.nsplit[b];
-      if (ns > 1) {
-        const size_t slot = size_t(a.pbase[b]) + size_t(h) * ns + split;
-        float* po = a.part_o + (slot * kPmaRows + qrow) * D + (D / 2) * g;
+    if (wk == 0 && qvalid) {
+      const float l_tot = l + other_half(l);
+      bool done = false;
+      if constexpr (SPLIT) {
+        const int ns = a.nsplit[cur.b];
+        if (ns > 1) {
+          const size_t slot = size_t(a.pbase[cur.b]) + size_t(cur.h) * ns + cur.split;
+          float* po = a.part_o + (slot * kPmaRows + qrow) * D + (D / 2) * g;
+#pragma unroll
+          for (int t = 0; t < kOTiles; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; i += 4)
+              *reinterpret_cast<float4*>(po + 16 * t + i) =
+                  make_float4(o[t][i], o[t][i + 1], o[t][i + 2], o[t][i + 3]);
+          // running max stored in base-2 units
+          if (g == 0)
+            a.part_ml[slot * kPmaRows + qrow] =
+                make_float2(m == -__builtin_huge_valf() ? m : m * c2, l_tot);
+          done = true;
+        }
+      }
+      if (!done) {
+        float scale;
+        if constexpr (ACT == ACT_SOFTMAX) {
+          scale = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+        } else {
+          scale = cur.lk > 0 ? 1.0f / float(cur.lk) : 0.f;
+        }
+        __bf16* orow = reinterpret_cast<__bf16*>(a.out) + (size_t(cur.qbeg + qrow) * a.H + cur.h) * D + (D / 2) * g;
 #pragma unroll
         for (int t = 0; t < kOTiles; ++t)
 #pragma unroll
-          for (int i = 0; i < 16; i += 4)
-            *reinterpret_cast<float4*>(po + 16 * t + i) =
-                make_float4(o[t][i], o[t][i + 1], o[t][i + 2], o[t][i + 3]);
-        if (g == 0) a.part_ml[slot * kPmaRows + qrow] = make_float2(m, l_tot);
-        return;
+          for (int i = 0; i < 16; i += 8) {
+            bf16x8 ov;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) ov[j] = (__bf16)(o[t][i + j] * scale);
+            *reinterpret_cast<bf16x8*>(orow + 16 * t + i) = ov;
+          }
       }
     }
-    float scale;
-    if constexpr (ACT == ACT_SOFTMAX) {
-      scale = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-    } else {
-      scale = lk > 0 ? 1.0f / float(lk) : 0.f;
-    }
-    __bf16* orow = reinterpret_cast<__bf16*>(a.out) + (size_t(qbeg + qrow) * a.H + h) * D + (D / 2) * g;
-#pragma unroll
-    for (int t = 0; t < kOTiles; ++t)
-#pragma unroll
-      for (int i = 0; i < 16; i += 8) {
-        bf16x8 ov;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) ov[j] = (__bf16)(o[t][i + j] * scale);
-        *reinterpret_cast<bf16x8*>(orow + 16 * t + i) = ov;
-      }
-  }
-};
-
-template <int D, int NWQ, int NWK, int ACT, int IN, bool WINDOW, bool SPLIT>
-__global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
-  using K = Attn<D, NWQ, NWK, ACT, IN, WINDOW, SPLIT>;
-  constexpr int kTileBytes = NWK * K::kGroupBytes;
-  constexpr int kCombBytes = NWK > 1 ? (NWK - 1) * NWQ * 64 * (D / 2 + 2) * 4 : 0;
-  constexpr int kBytes = kTileBytes > kCombBytes ? kTileBytes : kCombBytes;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[kBytes];
-  __shared__ float kscale[ACT == ACT_GELU ? NWK * 64 : 1];
-  // Items [xcd_begin[x], xcd_begin[x+1]) belong to XCD x = blockIdx.x % 8.
-  const int n = a.hdr->n_items;
-  const int x = blockIdx.x % kXcds;
-  const int beg = min(a.hdr->xcd_begin[x], n);
-  const int end = min(max(a.hdr->xcd_begin[x + 1], beg), n);
-  const int stride = gridDim.x / kXcds;
-  for (int idx = beg + int(blockIdx.x) / kXcds; idx < end; idx += stride) {
-    K::run_item(a, a.items[idx], smem, kscale);
-    __syncthreads();
+    if (!has_next) break;
+    idx = next_idx;
+    cur = nxt;
   }
 }
 
@@ -539,8 +663,8 @@ hipError_t launch_for_shape(int shape, int act, const AttnArgs& a, int num_cu, i
     case 0:  // query-tiled (self full, cross)
       return act == ACT_SOFTMAX ? launch<D, 4, 1, ACT_SOFTMAX, IN, false, false>(a, num_cu, max_items, st)
                                 : launch<D, 4, 1, ACT_GELU, IN, false, false>(a, num_cu, max_items, st);
-    case 1:  // block window (softmax only)
-      return launch<D, 2, 2, ACT_SOFTMAX, IN, true, false>(a, num_cu, max_items, st);
+    case 1:  // block window (softmax only): two query blocks per item
+      return launch<D, 4, 1, ACT_SOFTMAX, IN, true, false>(a, num_cu, max_items, st);
     default:  // key-split (PMA)
       return act == ACT_SOFTMAX ? launch<D, 1, 4, ACT_SOFTMAX, IN, false, true>(a, num_cu, max_items, st)
                                 : launch<D, 1, 4, ACT_GELU, IN, false, true>(a, num_cu, max_items, st);

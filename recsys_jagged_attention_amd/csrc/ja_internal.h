@@ -57,6 +57,7 @@ struct PlanArgs {
   int32_t total_q, total_kv;
   int bm, kvc, self_check;
   int window_blocks;   // 0 = no window (used for the per-item cost estimate)
+  int64_t kv_row_bytes;  // >0: a sample's K/V span (Lk * row bytes) must stay below 4 GiB
   int64_t max_items, max_slots;
   WsHeader* hdr;
   int32_t* nsplit;
