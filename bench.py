@@ -33,11 +33,11 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "useful TFLOPS (unpadded) & % bf16 MFMA peak, jagged GDPA fwd, 1 MI355X"
 KERNEL_NAME = {  # dominant kernel per workload (template instance of attn_kernel)
     "tiny_full": "attn_f32_kernel<32,softmax,nowindow>",
-    "block_window": "attn_kernel<128,NWQ=2,NWK=2,softmax,bf16,window>",
+    "block_window": "attn_kernel<128,NWQ=4,NWK=1,softmax,bf16,window>",
     "full_self": "attn_kernel<128,NWQ=4,NWK=1,softmax,bf16>",
     "cross_gelu": "attn_kernel<128,NWQ=4,NWK=1,gelu,bf16>",
     "pma": "attn_kernel<64,NWQ=1,NWK=4,softmax,bf16,split>",
-    "mxfp8_window": "attn_kernel<128,NWQ=2,NWK=2,softmax,mx,window>",
+    "mxfp8_window": "attn_kernel<128,NWQ=4,NWK=1,softmax,mx,window>",
 }
 
 
