@@ -34,7 +34,7 @@ METRIC = "useful TFLOPS (unpadded) & % bf16 MFMA peak, jagged GDPA fwd, 1 MI355X
 KERNEL_NAME = {  # dominant kernel per workload (template instance of attn_kernel)
     "tiny_full": "attn_f32_kernel<32,softmax,nowindow>",
     "block_window": "attn_kernel<128,NWQ=4,NWK=1,softmax,bf16,window>",
-    "full_self": "attn_kernel<128,NWQ=4,NWK=1,softmax,bf16>",
+    "full_self": "attn_kernel<128,NWQ=8,NWK=1,softmax,bf16>",
     "cross_gelu": "attn_kernel<128,NWQ=4,NWK=1,gelu,bf16>",
     "pma": "attn_kernel<64,NWQ=1,NWK=4,softmax,bf16,split>",
     "mxfp8_window": "attn_kernel<128,NWQ=4,NWK=1,softmax,mx,window>",

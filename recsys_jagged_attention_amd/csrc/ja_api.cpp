@@ -18,7 +18,7 @@ hipError_t launch_attn_f32(int D, int act, bool window, const AttnArgs& a, int g
 
 namespace {
 
-constexpr int kShapeQTiled = 0, kShapeWindow = 1, kShapeKvSplit = 2, kShapeF32 = 3;
+constexpr int kShapeQTiled = 0, kShapeWindow = 1, kShapeKvSplit = 2, kShapeFullSelf = 3, kShapeF32 = 4;
 constexpr int kMaxGrid = 1 << 20;
 
 struct Plan {
@@ -68,7 +68,7 @@ int validate(int B, int H, int D, int variant, int act, int window, int dtype, i
   return JA_OK;
 }
 
-Plan make_plan(int B, int H, int D, int variant, int window, int dtype, int32_t total_q,
+Plan make_plan(int B, int H, int D, int variant, int act, int window, int dtype, int32_t total_q,
                int32_t total_kv) {
   Plan p{};
   if (dtype == JA_F32) {
@@ -76,14 +76,17 @@ Plan make_plan(int B, int H, int D, int variant, int window, int dtype, int32_t 
     p.bm = 64;
   } else if (window > 0) {
     p.shape = kShapeWindow;
-    p.bm = 128;
+    p.bm = 128;  // two 64-token query blocks
   } else if (variant == JA_PMA) {
     p.shape = kShapeKvSplit;
     p.bm = kPmaRows;
     p.kvc = choose_kvc(H, total_kv);
+  } else if (variant == JA_SELF && act == JA_SOFTMAX) {
+    p.shape = kShapeFullSelf;
+    p.bm = 256;  // eight waves x 32 query rows
   } else {
     p.shape = kShapeQTiled;
-    p.bm = 128;
+    p.bm = 128;  // four waves x 32 query rows
   }
   WsLayout& w = p.ws;
   w.max_items = int64_t(H) * (cdiv(total_q, p.bm) + B);
@@ -131,7 +134,7 @@ const char* jagged_attn_strerror(int status) {
 size_t jagged_attn_workspace_size(int B, int H, int D, int variant, int act, int window, int dtype,
                                   int32_t total_q, int32_t total_kv) {
   if (validate(B, H, D, variant, act, window, dtype, total_q, total_kv) != JA_OK) return 0;
-  return make_plan(B, H, D, variant, window, dtype, total_q, total_kv).ws.total;
+  return make_plan(B, H, D, variant, act, window, dtype, total_q, total_kv).ws.total;
 }
 
 int jagged_attn_fwd(const void* q, const void* k, const void* v, const int32_t* q_offsets,
@@ -142,7 +145,7 @@ int jagged_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
   if (st != JA_OK) return st;
   if (!q || !k || !v || !q_offsets || !kv_offsets || !out) return JA_EINVAL;
   if (io->dtype == JA_MXFP8_E4M3 && (!io->q_scale || !io->k_scale || !io->v_scale)) return JA_EINVAL;
-  const Plan p = make_plan(B, H, D, variant, window, io->dtype, io->total_q, io->total_kv);
+  const Plan p = make_plan(B, H, D, variant, act, window, io->dtype, io->total_q, io->total_kv);
   if (io->workspace == nullptr || io->workspace_bytes < p.ws.total) return JA_EWORKSPACE;
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v) |
        reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(io->workspace)) & 15)

@@ -4,12 +4,16 @@
 // One kernel family covers the three shapes of GDPA (techfeed.io summary of
 // "GEM Training: How Meta Doubled the Efficiency of Its LLM-Scale Ads
 // Foundation Model", sections "なぜLLM向けのインフラをそのまま使えないのか" and
-// "Generalized Dot-Product Attention（GDPA）"): the four waves of a workgroup
-// are split NWQ x NWK between query rows (32 per wave) and key tiles (64 keys
-// per tile), so long-query shapes use NWQ=4, the 64-token block window uses
-// NWQ=4 on two consecutive query blocks (their windows share all but one key
-// block; each wave skips the one tile outside its own window) and PMA (32
-// queries, long keys) uses NWK=4 plus a key split across workgroups.
+// "Generalized Dot-Product Attention（GDPA）"): the waves of a workgroup are
+// split NWQ x NWK between query rows and key tiles (64 keys per tile).  A wave
+// owns 32*QSUB query rows (QSUB = 2 feeds every K and V^T operand read to two
+// MFMAs but needs the whole register file at one wave per SIMD; measured
+// slower, so the shapes below use QSUB = 1).  Long-query shapes use 4 waves x
+// 32 rows (full self-attention 8 waves, so each key tile in LDS serves 256
+// query rows); the 64-token block window uses 4 waves on two consecutive query
+// blocks (their windows share all but one key block; each wave skips the tile
+// outside its own window); PMA (32 queries, long keys) uses 4 key groups plus
+// a key split across workgroups.
 //
 // Data path.  K and V tiles go from HBM straight into LDS (global_load_lds,
 // 16 bytes per lane, no register staging), row-major with the 16-byte chunks
@@ -104,18 +108,53 @@ __device__ __forceinline__ unsigned lds_addr_of(const void* p) {
       (const __attribute__((address_space(3))) unsigned char*)(p)));
 }
 
-template <int D, int NWQ, int NWK, int ACT, int IN, bool WINDOW, bool SPLIT>
+// Wait until at most n of this wave's VMEM instructions are outstanding.
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  // s_waitcnt encoding (gfx9): vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]
+#define JA_VMCNT(k) case k: __builtin_amdgcn_s_waitcnt(((k) & 15) | (((k) >> 4) << 14) | 0x0F70); break;
+  switch (n) {
+    JA_VMCNT(0) JA_VMCNT(1) JA_VMCNT(2) JA_VMCNT(3) JA_VMCNT(4) JA_VMCNT(5) JA_VMCNT(6) JA_VMCNT(7)
+    JA_VMCNT(8) JA_VMCNT(9) JA_VMCNT(10) JA_VMCNT(11) JA_VMCNT(12) JA_VMCNT(13) JA_VMCNT(14)
+    JA_VMCNT(15) JA_VMCNT(16)
+    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+  }
+#undef JA_VMCNT
+}
+
+// Workgroup barrier for LDS hand-offs that does not drain outstanding global
+// loads (a __syncthreads() fence would wait for the prefetch too).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// D: head dim.  NWQ x NWK waves: NWQ query groups of 32*QSUB rows each, NWK
+// key groups (each takes every NWK-th tile).  QSUB = 2 lets one wave reuse
+// every K and V^T operand read from LDS for two 32-row query blocks.
+template <int D, int NWQ, int NWK, int QSUB, int ACT, int IN, bool WINDOW, bool SPLIT>
 struct Attn {
+  static constexpr int kWaves = NWQ * NWK;
+  static constexpr int kNT = 64 * kWaves;               // threads per workgroup
+  static constexpr int kRowsPerWave = 32 * QSUB;
   static constexpr int kRowBytes = 2 * D;               // one bf16 row in LDS
   static constexpr int kTileBytes = 64 * kRowBytes;      // 64 keys
   static constexpr int kGroupBytes = 2 * kTileBytes;     // K tile + V tile
+  static constexpr int kStageBytes = NWK * kGroupBytes;
+  static constexpr int kStages = 2 * kStageBytes <= 128 * 1024 ? 2 : 1;
   static constexpr int kSegs = kTileBytes / 1024;        // 1 KB direct-load segments per tile
   static constexpr int kQChunks = D / 16;                // MFMA k-chunks over D
   static constexpr int kOTiles = D / 32;                 // 32-dim output tiles
   static constexpr int kChunks = D / 8;                  // 16-byte chunks per row
+  static_assert((2 * kSegs) % kWaves == 0, "tile segments must split evenly over the waves");
+  static_assert(NWK == 1 || QSUB == 1, "key groups are merged for single-block waves only");
 
-  // Issue the loads of one key tile (keys [key0, key0+64) of the item, rows
-  // at or beyond kv_end replaced by row kv_end-1, which the mask removes).
+  // Direct-to-LDS load instructions one wave issues per key tile.
+  static constexpr int kLoadsPerTile = IN == IN_BF16 ? (2 * kSegs) / kWaves : 0;
+
+  // Issue the loads of one key tile (keys [key0, key0+64) of the item; rows at
+  // or beyond kv_end are replaced by row kv_end-1, which the mask removes).
   static __device__ __forceinline__ void issue_tile(unsigned char* grp, const __bf16* kb,
                                                     const __bf16* vb, const uint8_t* ksb,
                                                     const uint8_t* vsb, size_t rs, int key0,
@@ -123,13 +162,12 @@ struct Attn {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     if constexpr (IN == IN_BF16) {
-      // 2 * kSegs segments of 1 KB (K then V), 4 waves round-robin.  Byte
-      // offsets from the item's base fit 32 bits (the plan rejects larger
-      // samples).
+      // 2 * kSegs segments of 1 KB (K then V), waves round-robin.  Byte offsets
+      // from the item's base fit 32 bits (the plan rejects larger samples).
       const unsigned row_bytes = unsigned(rs) * 2u;
       const unsigned grp_lds = lds_addr_of(grp);
 #pragma unroll
-      for (int s = wave; s < 2 * kSegs; s += 4) {
+      for (int s = wave; s < 2 * kSegs; s += kWaves) {
         const bool is_v = s >= kSegs;
         const int seg = is_v ? s - kSegs : s;
         const int byte = seg * 1024 + 16 * lane;
@@ -143,7 +181,7 @@ struct Attn {
     } else {
       // MX: decode 8 e4m3 codes x 2^(E-127) to bf16 through registers.
 #pragma unroll
-      for (int u0 = 0; u0 < 2 * 64 * kChunks; u0 += kThreads) {
+      for (int u0 = 0; u0 < 2 * 64 * kChunks; u0 += kNT) {
         const int u = u0 + tid;
         const bool is_v = u >= 64 * kChunks;
         const int uu = is_v ? u - 64 * kChunks : u;
@@ -160,22 +198,25 @@ struct Attn {
     }
   }
 
-  // RMSNorm factor of every key of a loaded K tile (GELU).
+  // RMSNorm factor of every key of a loaded K tile (GELU): 4 threads per row.
   static __device__ __forceinline__ void key_scales(float eps, const unsigned char* grp, float* kscale) {
-    const int tid = threadIdx.x;
-    const int row = tid >> 2, part = tid & 3;
-    constexpr int kPer = kChunks / 4;
-    float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int c = part * kPer + i;
-      const bf16x8 x = *reinterpret_cast<const bf16x8*>(grp + row * kRowBytes + 16 * (c ^ swz_k<D>(row)));
+    for (int t0 = 0; t0 < 256; t0 += kNT) {
+      const int t = t0 + int(threadIdx.x);
+      const int row = t >> 2, part = t & 3;
+      constexpr int kPer = kChunks / 4;
+      float ss = 0.f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) ss = fmaf(float(x[j]), float(x[j]), ss);
+      for (int i = 0; i < kPer; ++i) {
+        const int c = part * kPer + i;
+        const bf16x8 x = *reinterpret_cast<const bf16x8*>(grp + row * kRowBytes + 16 * (c ^ swz_k<D>(row)));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ss = fmaf(float(x[j]), float(x[j]), ss);
+      }
+      ss += __shfl_xor(ss, 1, 64);
+      ss += __shfl_xor(ss, 2, 64);
+      if (part == 0) kscale[row] = __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
     }
-    ss += __shfl_xor(ss, 1, 64);
-    ss += __shfl_xor(ss, 2, 64);
-    if (part == 0) kscale[row] = __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
   }
 
   // Per-item context (wave-uniform).
@@ -206,7 +247,7 @@ struct Attn {
       }
     }
     if constexpr (WINDOW) {
-      const int qlast = min(c.q0 + 32 * NWQ, c.lq) - 1;
+      const int qlast = min(c.q0 + kRowsPerWave * NWQ, c.lq) - 1;
       c.kv_lo = max(0, c.q0 / kBlock - a.window_blocks + 1) * kBlock;
       c.kv_hi = min(c.lk, (qlast / kBlock + 1) * kBlock);
     }
@@ -226,9 +267,6 @@ struct Attn {
     return c;
   }
 
-  // Direct-to-LDS load instructions one wave issues per key tile.
-  static constexpr int kLoadsPerTile = IN == IN_BF16 ? (2 * kSegs) / 4 : 0;
-
   // Issue the tiles [t0, t0 + NWK) of an item into one stage; returns the
   // number of VMEM instructions this wave issued.
   static __device__ __forceinline__ int issue_group(const Item& c, unsigned char* stage_base, int t0,
@@ -245,37 +283,13 @@ struct Attn {
   }
 };
 
-// Wait until at most n of this wave's VMEM instructions are outstanding.
-__device__ __forceinline__ void wait_vmcnt(int n) {
-  // s_waitcnt encoding (gfx9): vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]
-#define JA_VMCNT(k) case k: __builtin_amdgcn_s_waitcnt(((k) & 15) | (((k) >> 4) << 14) | 0x0F70); break;
-  switch (n) {
-    JA_VMCNT(0) JA_VMCNT(1) JA_VMCNT(2) JA_VMCNT(3) JA_VMCNT(4) JA_VMCNT(5) JA_VMCNT(6) JA_VMCNT(7)
-    JA_VMCNT(8) JA_VMCNT(9) JA_VMCNT(10) JA_VMCNT(11) JA_VMCNT(12) JA_VMCNT(13) JA_VMCNT(14)
-    JA_VMCNT(15) JA_VMCNT(16)
-    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-  }
-#undef JA_VMCNT
-}
-
-// Workgroup barrier for LDS hand-offs that does not drain outstanding global
-// loads (a __syncthreads() fence would wait for the prefetch too).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
-template <int D, int NWQ, int NWK, int ACT, int IN, bool WINDOW, bool SPLIT>
-__global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
-  using K = Attn<D, NWQ, NWK, ACT, IN, WINDOW, SPLIT>;
+template <int D, int NWQ, int NWK, int QSUB, int ACT, int IN, bool WINDOW, bool SPLIT>
+__global__ __launch_bounds__(64 * NWQ * NWK, QSUB == 2 ? 1 : 2) void attn_kernel(AttnArgs a) {
+  using K = Attn<D, NWQ, NWK, QSUB, ACT, IN, WINDOW, SPLIT>;
   using Item = typename K::Item;
-  constexpr int kStageBytes = NWK * K::kGroupBytes;
+  constexpr int kStageBytes = K::kStageBytes, kStages = K::kStages;
   constexpr int kQChunks = K::kQChunks, kOTiles = K::kOTiles, kRowBytes = K::kRowBytes;
   constexpr int kTileBytes = K::kTileBytes;
-  // Two stages when they fit in LDS (prefetch overlaps compute), else one.
-  constexpr int kStages = 2 * kStageBytes <= 128 * 1024 ? 2 : 1;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages * kStageBytes];
   __shared__ float kscale_all[ACT == ACT_GELU ? kStages * NWK * 64 : 1];
 
@@ -312,38 +326,39 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
   K::issue_group(cur, smem, 0, rs);
 
   while (true) {
-    const int qrow_w = cur.q0 + 32 * wq;      // first row of this wave (sample-local)
+    const int qrow_w = cur.q0 + K::kRowsPerWave * wq;   // first row of this wave (sample-local)
     const bool wave_has_rows = qrow_w < cur.lq;
-    const int qrow = qrow_w + l32;
-    const bool qvalid = qrow < cur.lq;
     const int wblk = qrow_w / kBlock;
 
-    // Q fragment: lane holds dims [(D/2)g, (D/2)g + D/2) of its query row
-    // (rows past the sample load the last row and are zeroed).
-    bf16x8 qf[kQChunks];
-    {
+    // Q fragments: lane holds dims [(D/2)g, (D/2)g + D/2) of query row
+    // qrow_w + 32*qs + l32 (rows past the sample load the last row and are zeroed).
+    bf16x8 qf[QSUB][kQChunks];
+    float rq[QSUB];
+#pragma unroll
+    for (int qs = 0; qs < QSUB; ++qs) {
+      const int qrow = qrow_w + 32 * qs + l32;
       const size_t row = size_t(cur.qbeg + min(qrow, cur.lq - 1)) * a.H + cur.h;
 #pragma unroll
       for (int c = 0; c < kQChunks; ++c) {
         const int d0 = (D / 2) * g + 8 * c;
         if constexpr (IN == IN_BF16) {
-          qf[c] = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(a.q) + row * D + d0);
+          qf[qs][c] = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(a.q) + row * D + d0);
         } else {
-          qf[c] = decode_mx8(*reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(a.q) + row * D + d0),
-                             a.qs[row * (D / kMxBlock) + d0 / kMxBlock]);
+          qf[qs][c] = decode_mx8(*reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(a.q) + row * D + d0),
+                                 a.qs[row * (D / kMxBlock) + d0 / kMxBlock]);
         }
-        if (!qvalid) qf[c] = zero8();
+        if (qrow >= cur.lq) qf[qs][c] = zero8();
       }
-    }
-    float rq = 1.0f;
-    if constexpr (ACT == ACT_GELU) {
-      float ss = 0.f;
+      rq[qs] = 1.0f;
+      if constexpr (ACT == ACT_GELU) {
+        float ss = 0.f;
 #pragma unroll
-      for (int c = 0; c < kQChunks; ++c)
+        for (int c = 0; c < kQChunks; ++c)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) ss = fmaf(float(qf[c][j]), float(qf[c][j]), ss);
-      ss += other_half(ss);
-      rq = __builtin_amdgcn_rsqf(ss * (1.0f / D) + a.eps) * c2;
+          for (int j = 0; j < 8; ++j) ss = fmaf(float(qf[qs][c][j]), float(qf[qs][c][j]), ss);
+        ss += other_half(ss);
+        rq[qs] = __builtin_amdgcn_rsqf(ss * (1.0f / D) + a.eps) * c2;
+      }
     }
 
     const int next_idx = idx + stride;
@@ -351,12 +366,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
     Item nxt = cur;
     if (has_next) nxt = K::make_item(a, a.items[next_idx], rs);
 
-    f32x16 o[kOTiles];
+    f32x16 o[QSUB][kOTiles];
 #pragma unroll
-    for (int t = 0; t < kOTiles; ++t)
+    for (int qs = 0; qs < QSUB; ++qs)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
-    float m = -__builtin_huge_valf(), l = 0.f;  // m in raw score units
+      for (int t = 0; t < kOTiles; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[qs][t][i] = 0.f;
+    float m[QSUB], l[QSUB];  // m in raw score units
+#pragma unroll
+    for (int qs = 0; qs < QSUB; ++qs) {
+      m[qs] = -__builtin_huge_valf();
+      l[qs] = 0.f;
+    }
 
     for (int t0 = 0; t0 < cur.ntiles; t0 += NWK) {
       int pf = 0;
@@ -393,81 +415,90 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
       const unsigned char* ks = st_base + wk * K::kGroupBytes;
       const unsigned char* vs = ks + kTileBytes;
       const float* kscale = kscale_st + wk * 64;
-      // S^T for two 32-key halves of the tile.
-      f32x16 s[2];
+      // S^T for two 32-key halves of the tile, each K operand read feeding QSUB MFMAs.
+      f32x16 s[QSUB][2];
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
+      for (int qs = 0; qs < QSUB; ++qs)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[st][i] = 0.f;
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) s[qs][st][i] = 0.f;
       if (active) {
 #pragma unroll
         for (int st = 0; st < 2; ++st)
 #pragma unroll
-          for (int c = 0; c < kQChunks; ++c)
-            s[st] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(ks + st * 32 * kRowBytes + k_off[c]),
-                                  qf[c], s[st]);
+          for (int c = 0; c < kQChunks; ++c) {
+            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + st * 32 * kRowBytes + k_off[c]);
+#pragma unroll
+            for (int qs = 0; qs < QSUB; ++qs) s[qs][st] = mfma_32x32x16(kf, qf[qs][c], s[qs][st]);
+          }
       }
       if constexpr (kStages == 2) {
         if (t0 == 0) {  // every wave issues its share of the tile loads
-          if (NWK < cur.ntiles) K::issue_group(cur, other, NWK, rs, s[1][15]);
-          else if (has_next) K::issue_group(nxt, other, 0, rs, s[1][15]);
+          if (NWK < cur.ntiles) K::issue_group(cur, other, NWK, rs, s[QSUB - 1][1][15]);
+          else if (has_next) K::issue_group(nxt, other, 0, rs, s[QSUB - 1][1][15]);
         }
       }
       if (active) {
         // Register i of half st holds key 32*st + 16*(i/8) + 8g + i%8 of the tile.
         const int nvalid = cur.kv_hi - key0;  // keys at or beyond this index are outside
         const bool ragged = nvalid < 64;
-        if constexpr (ACT == ACT_SOFTMAX) {
-          if (ragged) {
+#pragma unroll
+        for (int qs = 0; qs < QSUB; ++qs) {
+          if constexpr (ACT == ACT_SOFTMAX) {
+            if (ragged) {
+#pragma unroll
+              for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                  const int kk = 32 * st + 16 * (i >> 3) + 8 * g + (i & 7);
+                  if (kk >= nvalid) s[qs][st][i] = -__builtin_huge_valf();
+                }
+            }
+            float mt = -__builtin_huge_valf();
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+              for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[qs][st][i]);
+            mt = fmaxf(mt, other_half(mt));
+            const float m_new = fmaxf(m[qs], mt);
+            if (__any(m_new != m[qs])) {
+              const float alpha = m[qs] == -__builtin_huge_valf() ? 0.f : fast_exp2((m[qs] - m_new) * c2);
+              l[qs] *= alpha;
+#pragma unroll
+              for (int t = 0; t < kOTiles; ++t)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) o[qs][t][i] *= alpha;
+              m[qs] = m_new;
+            }
+            const float mc = m[qs] == -__builtin_huge_valf() ? 0.f : m[qs] * c2;
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const float p = fast_exp2(fmaf(s[qs][st][i], c2, -mc));
+                s[qs][st][i] = p;
+                l[qs] += p;
+              }
+          } else {
 #pragma unroll
             for (int st = 0; st < 2; ++st)
 #pragma unroll
               for (int i = 0; i < 16; ++i) {
                 const int kk = 32 * st + 16 * (i >> 3) + 8 * g + (i & 7);
-                if (kk >= nvalid) s[st][i] = -__builtin_huge_valf();
+                const float gl = gelu_tanh(s[qs][st][i] * rq[qs] * kscale[kk]);
+                s[qs][st][i] = (!ragged || kk < nvalid) ? gl : 0.f;
               }
           }
-          float mt = -__builtin_huge_valf();
-#pragma unroll
-          for (int st = 0; st < 2; ++st)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[st][i]);
-          mt = fmaxf(mt, other_half(mt));
-          const float m_new = fmaxf(m, mt);
-          if (__any(m_new != m)) {
-            const float alpha = m == -__builtin_huge_valf() ? 0.f : fast_exp2((m - m_new) * c2);
-            l *= alpha;
-#pragma unroll
-            for (int t = 0; t < kOTiles; ++t)
-#pragma unroll
-              for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
-            m = m_new;
-          }
-          const float mc = m == -__builtin_huge_valf() ? 0.f : m * c2;
-#pragma unroll
-          for (int st = 0; st < 2; ++st)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const float p = fast_exp2(fmaf(s[st][i], c2, -mc));
-              s[st][i] = p;
-              l += p;
-            }
-        } else {
-#pragma unroll
-          for (int st = 0; st < 2; ++st)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int kk = 32 * st + 16 * (i >> 3) + 8 * g + (i & 7);
-              const float gl = gelu_tanh(s[st][i] * rq * kscale[kk]);
-              s[st][i] = (!ragged || kk < nvalid) ? gl : 0.f;
-            }
         }
-        // O^T += V^T P^T over four 16-key chunks.
+        // O^T += V^T P^T over four 16-key chunks, each V^T read feeding QSUB MFMAs.
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
-          bf16x8 pf8;
+          bf16x8 pf8[QSUB];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) pf8[j] = (__bf16)s[kc >> 1][8 * (kc & 1) + j];
+          for (int qs = 0; qs < QSUB; ++qs)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) pf8[qs][j] = (__bf16)s[qs][kc >> 1][8 * (kc & 1) + j];
 #pragma unroll
           for (int t = 0; t < kOTiles; ++t) {
             const unsigned char* p0 = vs + v_row + kc * 16 * kRowBytes + v_col[t];
@@ -479,7 +510,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
             w[1] = lo2[1];
             w[2] = hi2[0];
             w[3] = hi2[1];
-            o[t] = mfma_32x32x16(__builtin_bit_cast(bf16x8, w), pf8, o[t]);
+            const bf16x8 vf = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+            for (int qs = 0; qs < QSUB; ++qs) o[qs][t] = mfma_32x32x16(vf, pf8[qs], o[qs][t]);
           }
         }
       }
@@ -490,7 +523,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
       if (cur.ntiles == 0 && has_next) K::issue_group(nxt, smem + stage * kStageBytes, 0, rs);
     }
 
-    // Merge the key groups of a query group (NWK > 1) through the free stage.
+    // Merge the key groups of a query group (NWK > 1, QSUB == 1) through the free stage.
     if constexpr (NWK > 1) {
       constexpr int kRec = D / 2 + 2;  // floats per lane record: O half row, m, l
       float* cbuf = reinterpret_cast<float*>(smem + (kStages == 2 ? (stage ^ 1) * kStageBytes : 0));
@@ -499,9 +532,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int t = 0; t < kOTiles; ++t)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) rec[16 * t + i] = o[t][i];
-        rec[D / 2] = m;
-        rec[D / 2 + 1] = l;
+          for (int i = 0; i < 16; ++i) rec[16 * t + i] = o[0][t][i];
+        rec[D / 2] = m[0];
+        rec[D / 2 + 1] = l[0];
       }
       lds_barrier();
       if (wk == 0) {
@@ -510,20 +543,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
           const float* rec = cbuf + (((w - 1) * NWQ + wq) * 64 + lane) * kRec;
           if constexpr (ACT == ACT_SOFTMAX) {
             const float m2 = rec[D / 2], l2 = rec[D / 2 + 1];
-            const float mn = fmaxf(m, m2);
-            const float a1 = m == -__builtin_huge_valf() ? 0.f : fast_exp2((m - mn) * c2);
+            const float mn = fmaxf(m[0], m2);
+            const float a1 = m[0] == -__builtin_huge_valf() ? 0.f : fast_exp2((m[0] - mn) * c2);
             const float a2 = m2 == -__builtin_huge_valf() ? 0.f : fast_exp2((m2 - mn) * c2);
 #pragma unroll
             for (int t = 0; t < kOTiles; ++t)
 #pragma unroll
-              for (int i = 0; i < 16; ++i) o[t][i] = o[t][i] * a1 + rec[16 * t + i] * a2;
-            l = l * a1 + l2 * a2;
-            m = mn;
+              for (int i = 0; i < 16; ++i) o[0][t][i] = o[0][t][i] * a1 + rec[16 * t + i] * a2;
+            l[0] = l[0] * a1 + l2 * a2;
+            m[0] = mn;
           } else {
 #pragma unroll
             for (int t = 0; t < kOTiles; ++t)
 #pragma unroll
-              for (int i = 0; i < 16; ++i) o[t][i] += rec[16 * t + i];
+              for (int i = 0; i < 16; ++i) o[0][t][i] += rec[16 * t + i];
           }
         }
       }
@@ -533,44 +566,49 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(AttnArgs a) {
       if (has_next) K::issue_group(nxt, smem, 0, rs);  // LDS is free again
     }
 
-    if (wk == 0 && qvalid) {
-      const float l_tot = l + other_half(l);
-      bool done = false;
-      if constexpr (SPLIT) {
-        const int ns = a.nsplit[cur.b];
-        if (ns > 1) {
-          const size_t slot = size_t(a.pbase[cur.b]) + size_t(cur.h) * ns + cur.split;
-          float* po = a.part_o + (slot * kPmaRows + qrow) * D + (D / 2) * g;
+    if (wk == 0) {
+#pragma unroll
+      for (int qs = 0; qs < QSUB; ++qs) {
+        const int qrow = qrow_w + 32 * qs + l32;
+        if (qrow >= cur.lq) continue;
+        const float l_tot = l[qs] + other_half(l[qs]);
+        bool done = false;
+        if constexpr (SPLIT) {
+          const int ns = a.nsplit[cur.b];
+          if (ns > 1) {
+            const size_t slot = size_t(a.pbase[cur.b]) + size_t(cur.h) * ns + cur.split;
+            float* po = a.part_o + (slot * kPmaRows + qrow) * D + (D / 2) * g;
+#pragma unroll
+            for (int t = 0; t < kOTiles; ++t)
+#pragma unroll
+              for (int i = 0; i < 16; i += 4)
+                *reinterpret_cast<float4*>(po + 16 * t + i) =
+                    make_float4(o[qs][t][i], o[qs][t][i + 1], o[qs][t][i + 2], o[qs][t][i + 3]);
+            // running max stored in base-2 units
+            if (g == 0)
+              a.part_ml[slot * kPmaRows + qrow] =
+                  make_float2(m[qs] == -__builtin_huge_valf() ? m[qs] : m[qs] * c2, l_tot);
+            done = true;
+          }
+        }
+        if (!done) {
+          float scale;
+          if constexpr (ACT == ACT_SOFTMAX) {
+            scale = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+          } else {
+            scale = cur.lk > 0 ? 1.0f / float(cur.lk) : 0.f;
+          }
+          __bf16* orow = reinterpret_cast<__bf16*>(a.out) + (size_t(cur.qbeg + qrow) * a.H + cur.h) * D + (D / 2) * g;
 #pragma unroll
           for (int t = 0; t < kOTiles; ++t)
 #pragma unroll
-            for (int i = 0; i < 16; i += 4)
-              *reinterpret_cast<float4*>(po + 16 * t + i) =
-                  make_float4(o[t][i], o[t][i + 1], o[t][i + 2], o[t][i + 3]);
-          // running max stored in base-2 units
-          if (g == 0)
-            a.part_ml[slot * kPmaRows + qrow] =
-                make_float2(m == -__builtin_huge_valf() ? m : m * c2, l_tot);
-          done = true;
+            for (int i = 0; i < 16; i += 8) {
+              bf16x8 ov;
+#pragma unroll
+              for (int j = 0; j < 8; ++j) ov[j] = (__bf16)(o[qs][t][i + j] * scale);
+              *reinterpret_cast<bf16x8*>(orow + 16 * t + i) = ov;
+            }
         }
-      }
-      if (!done) {
-        float scale;
-        if constexpr (ACT == ACT_SOFTMAX) {
-          scale = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-        } else {
-          scale = cur.lk > 0 ? 1.0f / float(cur.lk) : 0.f;
-        }
-        __bf16* orow = reinterpret_cast<__bf16*>(a.out) + (size_t(cur.qbeg + qrow) * a.H + cur.h) * D + (D / 2) * g;
-#pragma unroll
-        for (int t = 0; t < kOTiles; ++t)
-#pragma unroll
-          for (int i = 0; i < 16; i += 8) {
-            bf16x8 ov;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) ov[j] = (__bf16)(o[t][i + j] * scale);
-            *reinterpret_cast<bf16x8*>(orow + 16 * t + i) = ov;
-          }
       }
     }
     if (!has_next) break;
@@ -630,29 +668,30 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
 }
 
 // Workgroups resident per CU for one kernel instance (queried once).
-template <int D, int NWQ, int NWK, int ACT, int IN, bool WINDOW, bool SPLIT>
+template <int D, int NWQ, int NWK, int QSUB, int ACT, int IN, bool WINDOW, bool SPLIT>
 int resident_per_cu() {
   static int cached = 0;
   if (cached == 0) {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, attn_kernel<D, NWQ, NWK, ACT, IN, WINDOW, SPLIT>, kThreads, 0) != hipSuccess || n < 1)
+            &n, attn_kernel<D, NWQ, NWK, QSUB, ACT, IN, WINDOW, SPLIT>, 64 * NWQ * NWK, 0) != hipSuccess ||
+        n < 1)
       n = 1;
     cached = n;
   }
   return cached;
 }
 
-template <int D, int NWQ, int NWK, int ACT, int IN, bool WINDOW, bool SPLIT>
+template <int D, int NWQ, int NWK, int QSUB, int ACT, int IN, bool WINDOW, bool SPLIT>
 hipError_t launch(const AttnArgs& a, int num_cu, int64_t max_items, hipStream_t st) {
   // Persistent grid: each resident slot once, a multiple of the XCD count.
-  int64_t grid = int64_t(num_cu) * resident_per_cu<D, NWQ, NWK, ACT, IN, WINDOW, SPLIT>();
+  int64_t grid = int64_t(num_cu) * resident_per_cu<D, NWQ, NWK, QSUB, ACT, IN, WINDOW, SPLIT>();
   const int64_t need = ((max_items + kXcds - 1) / kXcds) * kXcds;
   if (grid > need) grid = need;
   grid = (grid / kXcds) * kXcds;
   if (grid < kXcds) grid = kXcds;
-  hipLaunchKernelGGL((attn_kernel<D, NWQ, NWK, ACT, IN, WINDOW, SPLIT>), dim3(unsigned(grid)),
-                     dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((attn_kernel<D, NWQ, NWK, QSUB, ACT, IN, WINDOW, SPLIT>), dim3(unsigned(grid)),
+                     dim3(64 * NWQ * NWK), 0, st, a);
   return hipGetLastError();
 }
 
@@ -660,20 +699,22 @@ template <int D, int IN>
 hipError_t launch_for_shape(int shape, int act, const AttnArgs& a, int num_cu, int64_t max_items,
                             hipStream_t st) {
   switch (shape) {
-    case 0:  // query-tiled (self full, cross)
-      return act == ACT_SOFTMAX ? launch<D, 4, 1, ACT_SOFTMAX, IN, false, false>(a, num_cu, max_items, st)
-                                : launch<D, 4, 1, ACT_GELU, IN, false, false>(a, num_cu, max_items, st);
-    case 1:  // block window (softmax only): two query blocks per item
-      return launch<D, 4, 1, ACT_SOFTMAX, IN, true, false>(a, num_cu, max_items, st);
-    default:  // key-split (PMA)
-      return act == ACT_SOFTMAX ? launch<D, 1, 4, ACT_SOFTMAX, IN, false, true>(a, num_cu, max_items, st)
-                                : launch<D, 1, 4, ACT_GELU, IN, false, true>(a, num_cu, max_items, st);
+    case 0:  // query-tiled (self full, cross): 4 waves x 32 rows
+      return act == ACT_SOFTMAX ? launch<D, 4, 1, 1, ACT_SOFTMAX, IN, false, false>(a, num_cu, max_items, st)
+                                : launch<D, 4, 1, 1, ACT_GELU, IN, false, false>(a, num_cu, max_items, st);
+    case 1:  // block window (softmax only): 4 waves x 32 rows on two 64-token query blocks
+      return launch<D, 4, 1, 1, ACT_SOFTMAX, IN, true, false>(a, num_cu, max_items, st);
+    case 3:  // full self-attention: 8 waves x 32 rows share every key tile
+      return launch<D, 8, 1, 1, ACT_SOFTMAX, IN, false, false>(a, num_cu, max_items, st);
+    default:  // key-split (PMA): 1 query group of 32 rows x 4 key groups
+      return act == ACT_SOFTMAX ? launch<D, 1, 4, 1, ACT_SOFTMAX, IN, false, true>(a, num_cu, max_items, st)
+                                : launch<D, 1, 4, 1, ACT_GELU, IN, false, true>(a, num_cu, max_items, st);
   }
 }
 
 }  // namespace
 
-// shape: 0 = query-tiled, 1 = block window, 2 = key-split.
+// shape: 0 = query-tiled, 1 = block window, 2 = key-split, 3 = full self-attention.
 hipError_t launch_attn_mfma(int D, int in, int shape, int act, const AttnArgs& a, int num_cu,
                             int64_t max_items, hipStream_t st) {
   if (in == IN_BF16) {

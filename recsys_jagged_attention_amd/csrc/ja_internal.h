@@ -11,7 +11,7 @@ namespace ja {
 constexpr int kBlock = 64;        // token block of block-aligned attention
 constexpr int kMxBlock = 32;      // elements per E8M0 scale along D
 constexpr int kWaveSize = 64;
-constexpr int kThreads = 256;     // every MFMA kernel runs 4 waves per workgroup
+constexpr int kThreads = 256;     // threads of the split-merge kernel
 constexpr int kPmaRows = 32;      // query rows per key-split work item
 
 enum Act { ACT_SOFTMAX = 0, ACT_GELU = 1 };

@@ -90,7 +90,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ int s_iwarp[3 * kPlanWaves];
   __shared__ double s_dwarp[3 * kPlanWaves];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
   if (tid == 0) {
     s_bad = 0;
     s_big = 0;
@@ -141,7 +140,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 
   // Pass 2: per chunk of 1024 samples, scan and write items, splits, slot
   // bases and the XCD cut points.
-  __shared__ int s_cnt[kPlanThreads];
   __shared__ int s_base[kPlanThreads];
   __shared__ int s_nqt[kPlanThreads];
   __shared__ int s_ns[kPlanThreads];
@@ -168,21 +166,20 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         }
       }
     }
-    s_cnt[tid] = w.cnt;
     s_base[tid] = ibase;
     s_nqt[tid] = w.nqt;
     s_ns[tid] = w.ns;
     __syncthreads();
-    // One wave per sample writes its items: head-major, then query tile, then split.
+    // One thread per (sample, head) writes that head's items (query tile, then
+    // split), so no thread divides per item.  Item order within a sample is
+    // head-major: items that share K/V stay adjacent.
     const int nchunk = min(kPlanThreads, a.B - base);
-    for (int j = wave; j < nchunk; j += kPlanWaves) {
-      const int c = s_cnt[j], ib = s_base[j], nq = s_nqt[j], nsj = s_ns[j];
-      for (int t = lane; t < c; t += 64) {
-        const int s = t % nsj;
-        const int qt = (t / nsj) % nq;
-        const int h = t / (nsj * nq);
-        a.items[ib + t] = make_int4(base + j, h, qt * a.bm, s);
-      }
+    for (int p = tid; p < nchunk * a.H; p += kPlanThreads) {
+      const int j = p / a.H, h = p - j * a.H;
+      const int nq = s_nqt[j], nsj = s_ns[j];
+      int ib = s_base[j] + h * nq * nsj;
+      for (int qt = 0; qt < nq; ++qt)
+        for (int sp = 0; sp < nsj; ++sp) a.items[ib++] = make_int4(base + j, h, qt * a.bm, sp);
     }
     item_carry += items_total;
     slot_carry += slots_total;
