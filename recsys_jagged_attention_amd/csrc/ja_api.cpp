@@ -171,7 +171,9 @@ int jagged_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
   pa.kvc = p.kvc;
   pa.self_check = variant == JA_SELF;
   pa.window_blocks = window / kBlock;
-  pa.kv_row_bytes = io->dtype == JA_BF16 ? int64_t(H) * D * 2 : 0;  // 32-bit DMA offsets
+  // 32-bit DMA offsets: bf16 rows (2 bytes/element) and fp8 code rows (D = 128)
+  pa.kv_row_bytes = io->dtype == JA_BF16 ? int64_t(H) * D * 2
+                                         : (io->dtype == JA_MXFP8_E4M3 && D == 128 ? int64_t(H) * D : 0);
   pa.max_items = p.ws.max_items;
   pa.max_slots = p.ws.max_slots;
   pa.hdr = hdr;

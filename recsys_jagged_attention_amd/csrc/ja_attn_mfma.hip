@@ -103,6 +103,32 @@ __device__ __forceinline__ void lds_dma16(const void* sbase, unsigned voff, unsi
                :: "v"(voff), "s"(reinterpret_cast<const void*>(pu)), "s"(lu), "v"(dep) : "memory", "m0");
 }
 
+// 4 bytes per lane into LDS at M0 + 4*lane (same contract as lds_dma16).
+__device__ __forceinline__ void lds_dma4(const void* sbase, unsigned voff, unsigned lds_addr) {
+  const uintptr_t p = reinterpret_cast<uintptr_t>(sbase);
+  const uint64_t hi = unsigned(__builtin_amdgcn_readfirstlane(unsigned(p >> 32)));
+  const uint64_t lo = unsigned(__builtin_amdgcn_readfirstlane(unsigned(p)));
+  const uint64_t pu = (hi << 32) | lo;
+  const unsigned lu = unsigned(__builtin_amdgcn_readfirstlane(lds_addr));
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :: "v"(voff), "s"(reinterpret_cast<const void*>(pu)), "s"(lu) : "memory", "m0");
+}
+
+// 16-byte chunk swizzle of an fp8 code tile (D bytes per row) for the fp8
+// MFMA operand reads: rows sharing a bank set get distinct chunk slots.
+template <int D>
+__device__ __forceinline__ int swz_c(int row) {
+  return (row / (256 / D)) % (D / 16);
+}
+
+__device__ __forceinline__ float e8m0_to_float(unsigned e) {
+  e &= 0xFFu;
+  return e == 0 ? __uint_as_float(0x00400000u) : (e == 255u ? __builtin_nanf("") : __uint_as_float(e << 23));
+}
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ unsigned lds_addr_of(const void* p) {
   return static_cast<unsigned>(reinterpret_cast<uintptr_t>(
       (const __attribute__((address_space(3))) unsigned char*)(p)));
@@ -140,7 +166,12 @@ struct Attn {
   static constexpr int kRowsPerWave = 32 * QSUB;
   static constexpr int kRowBytes = 2 * D;               // one bf16 row in LDS
   static constexpr int kTileBytes = 64 * kRowBytes;      // 64 keys
-  static constexpr int kGroupBytes = 2 * kTileBytes;     // K tile + V tile
+  // One key group in LDS.  bf16 / MX decoded: K tile, V tile (bf16).  MX8:
+  // K codes, V codes (fp8), K and V scale rows (4 bytes each), V as bf16.
+  static constexpr bool kMx8 = IN == IN_MX8;
+  static constexpr int kKcOff = 0, kVcOff = 64 * D, kKsOff = 128 * D, kVsOff = 128 * D + 256;
+  static constexpr int kVOff = kMx8 ? 128 * D + 512 : kTileBytes;   // bf16 V tile
+  static constexpr int kGroupBytes = kMx8 ? 128 * D + 512 + kTileBytes : 2 * kTileBytes;
   static constexpr int kStageBytes = NWK * kGroupBytes;
   static constexpr int kStages = 2 * kStageBytes <= 128 * 1024 ? 2 : 1;
   static constexpr int kSegs = kTileBytes / 1024;        // 1 KB direct-load segments per tile
@@ -148,10 +179,17 @@ struct Attn {
   static constexpr int kOTiles = D / 32;                 // 32-dim output tiles
   static constexpr int kChunks = D / 8;                  // 16-byte chunks per row
   static_assert((2 * kSegs) % kWaves == 0, "tile segments must split evenly over the waves");
+  static_assert(!kMx8 || D == 128, "fp8 MFMA path needs D = 128");
+  static constexpr int kCodeSegs = 64 * D / 1024;        // 1 KB segments of an fp8 code tile
   static_assert(NWK == 1 || QSUB == 1, "key groups are merged for single-block waves only");
 
-  // Direct-to-LDS load instructions one wave issues per key tile.
-  static constexpr int kLoadsPerTile = IN == IN_BF16 ? (2 * kSegs) / kWaves : 0;
+  // Direct-to-LDS load instructions one wave issues per key tile (MX8: wave 0
+  // also issues the two scale rows).
+  static __device__ __forceinline__ int loads_per_tile(int wave) {
+    if constexpr (IN == IN_BF16) return (2 * kSegs) / kWaves;
+    else if constexpr (IN == IN_MX8) return (2 * kCodeSegs) / kWaves + (wave == 0 ? 2 : 0);
+    else return 0;
+  }
 
   // Issue the loads of one key tile (keys [key0, key0+64) of the item; rows at
   // or beyond kv_end are replaced by row kv_end-1, which the mask removes).
@@ -178,6 +216,28 @@ struct Attn {
         lds_dma16(is_v ? (const void*)vb : (const void*)kb, key * row_bytes + 16u * unsigned(c),
                   grp_lds + (is_v ? kTileBytes : 0) + seg * 1024, dep);
       }
+    } else if constexpr (IN == IN_MX8) {
+      // fp8 code tiles (D bytes per row) and the rows' 4 scale bytes, untouched.
+      const unsigned row_bytes = unsigned(rs);            // codes: one byte per element
+      const unsigned grp_lds = lds_addr_of(grp);
+#pragma unroll
+      for (int s = wave; s < 2 * kCodeSegs; s += kWaves) {
+        const bool is_v = s >= kCodeSegs;
+        const int seg = is_v ? s - kCodeSegs : s;
+        const int byte = seg * 1024 + 16 * lane;
+        const int row = byte / D;
+        const int phys = (byte % D) / 16;
+        const int c = phys ^ swz_c<D>(row);
+        const unsigned key = unsigned(min(key0 + row, kv_end - 1));
+        lds_dma16(is_v ? (const void*)vb : (const void*)kb, key * row_bytes + 16u * unsigned(c),
+                  grp_lds + (is_v ? kVcOff : kKcOff) + seg * 1024, dep);
+      }
+      if (wave == 0) {
+        const unsigned key = unsigned(min(key0 + lane, kv_end - 1));
+        const unsigned srow = unsigned(rs / kMxBlock);    // scale bytes between key rows
+        lds_dma4(ksb, key * srow, grp_lds + kKsOff);
+        lds_dma4(vsb, key * srow, grp_lds + kVsOff);
+      }
     } else {
       // MX: decode 8 e4m3 codes x 2^(E-127) to bf16 through registers.
 #pragma unroll
@@ -198,6 +258,31 @@ struct Attn {
     }
   }
 
+  // MX8: convert the V code tile to the bf16 V tile (exact: 4-bit e4m3
+  // significands times a power of two), hardware scaled conversion.
+  static __device__ __forceinline__ void convert_v(unsigned char* grp) {
+    constexpr int kUnits = 64 * D / 8;  // 8 elements per unit
+#pragma unroll
+    for (int u0 = 0; u0 < kUnits; u0 += kNT) {
+      const int u = u0 + int(threadIdx.x);
+      const int row = u / (D / 8), j8 = u % (D / 8);
+      const int phys16 = (j8 >> 1) ^ swz_c<D>(row);
+      const u32x2 w = *reinterpret_cast<const u32x2*>(grp + kVcOff + row * D + 16 * phys16 + 8 * (j8 & 1));
+      const unsigned sw = *reinterpret_cast<const unsigned*>(grp + kVsOff + 4 * row);
+      const float sc = e8m0_to_float(sw >> (8 * ((8 * j8) / kMxBlock)));
+      const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], sc, false);
+      const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], sc, true);
+      const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], sc, false);
+      const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], sc, true);
+      u32x4 o;
+      o[0] = __builtin_bit_cast(unsigned, p0);
+      o[1] = __builtin_bit_cast(unsigned, p1);
+      o[2] = __builtin_bit_cast(unsigned, p2);
+      o[3] = __builtin_bit_cast(unsigned, p3);
+      *reinterpret_cast<u32x4*>(grp + kVOff + row * kRowBytes + 16 * (j8 ^ swz_v<D>(row))) = o;
+    }
+  }
+
   // RMSNorm factor of every key of a loaded K tile (GELU): 4 threads per row.
   static __device__ __forceinline__ void key_scales(float eps, const unsigned char* grp, float* kscale) {
 #pragma unroll
@@ -206,12 +291,32 @@ struct Attn {
       const int row = t >> 2, part = t & 3;
       constexpr int kPer = kChunks / 4;
       float ss = 0.f;
+      if constexpr (kMx8) {
+        // one thread per (row, 32-element block): decode its codes
+        const unsigned sw = *reinterpret_cast<const unsigned*>(grp + kKsOff + 4 * row);
+        const float sc = e8m0_to_float(sw >> (8 * part));
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        const int c = part * kPer + i;
-        const bf16x8 x = *reinterpret_cast<const bf16x8*>(grp + row * kRowBytes + 16 * (c ^ swz_k<D>(row)));
+        for (int h16 = 0; h16 < 2; ++h16) {
+          const u32x4 w = *reinterpret_cast<const u32x4*>(
+              grp + kKcOff + row * D + 16 * ((2 * part + h16) ^ swz_c<D>(row)));
 #pragma unroll
-        for (int j = 0; j < 8; ++j) ss = fmaf(float(x[j]), float(x[j]), ss);
+          for (int q = 0; q < 4; ++q) {
+            const bf16x2 p = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[q], sc, false);
+            const bf16x2 r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[q], sc, true);
+            ss = fmaf(float(p[0]), float(p[0]), ss);
+            ss = fmaf(float(p[1]), float(p[1]), ss);
+            ss = fmaf(float(r[0]), float(r[0]), ss);
+            ss = fmaf(float(r[1]), float(r[1]), ss);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+          const int c = part * kPer + i;
+          const bf16x8 x = *reinterpret_cast<const bf16x8*>(grp + row * kRowBytes + 16 * (c ^ swz_k<D>(row)));
+#pragma unroll
+          for (int j = 0; j < 8; ++j) ss = fmaf(float(x[j]), float(x[j]), ss);
+        }
       }
       ss += __shfl_xor(ss, 1, 64);
       ss += __shfl_xor(ss, 2, 64);
@@ -258,7 +363,7 @@ struct Attn {
       c.vb = reinterpret_cast<const __bf16*>(a.v) + kv_off;
       c.ksb = nullptr;
       c.vsb = nullptr;
-    } else {
+    } else {  // MX inputs: codes are bytes, scales one byte per 32 elements
       c.kb = reinterpret_cast<const __bf16*>(reinterpret_cast<const uint8_t*>(a.k) + kv_off);
       c.vb = reinterpret_cast<const __bf16*>(reinterpret_cast<const uint8_t*>(a.v) + kv_off);
       c.ksb = a.ks + (size_t(kbeg) * a.H + c.h) * (D / kMxBlock);
@@ -277,7 +382,7 @@ struct Attn {
       if (t0 + kg < c.ntiles) {
         issue_tile(stage_base + kg * kGroupBytes, c.kb, c.vb, c.ksb, c.vsb, rs, c.kv_lo + 64 * (t0 + kg),
                    c.kv_hi, dep);
-        n += kLoadsPerTile;
+        n += loads_per_tile(__builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6));
       }
     return n;
   }
@@ -333,11 +438,53 @@ __global__ __launch_bounds__(64 * NWQ * NWK, QSUB == 2 ? 1 : 2) void attn_kernel
     // Q fragments: lane holds dims [(D/2)g, (D/2)g + D/2) of query row
     // qrow_w + 32*qs + l32 (rows past the sample load the last row and are zeroed).
     bf16x8 qf[QSUB][kQChunks];
+    // MX8: operand c of lane-half g holds elements 64c+16g+[0,16) (bytes 0-15,
+    // scaled by the lower lane-half's scale) and 64c+32+16g+[0,16) (bytes 16-31,
+    // scaled by the upper lane-half's), so lane-half g carries the scale of
+    // 32-element block 2c+g.
+    i32x8 qc[QSUB][D / 64 > 0 ? D / 64 : 1];
+    int qsc[QSUB][D / 64 > 0 ? D / 64 : 1];
     float rq[QSUB];
 #pragma unroll
     for (int qs = 0; qs < QSUB; ++qs) {
       const int qrow = qrow_w + 32 * qs + l32;
       const size_t row = size_t(cur.qbeg + min(qrow, cur.lq - 1)) * a.H + cur.h;
+      if constexpr (IN == IN_MX8) {
+        float ss = 0.f;
+#pragma unroll
+        for (int c = 0; c < D / 64; ++c) {
+          const uint8_t* src = reinterpret_cast<const uint8_t*>(a.q) + row * D + 64 * c + 16 * g;
+          const u32x4 w0 = *reinterpret_cast<const u32x4*>(src);
+          const u32x4 w1 = *reinterpret_cast<const u32x4*>(src + 32);
+          const int sb0 = a.qs[row * (D / kMxBlock) + 2 * c];
+          const int sb1 = a.qs[row * (D / kMxBlock) + 2 * c + 1];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            qc[qs][c][i] = qrow < cur.lq ? int(w0[i]) : 0;
+            qc[qs][c][4 + i] = qrow < cur.lq ? int(w1[i]) : 0;
+          }
+          qsc[qs][c] = g ? sb1 : sb0;
+          if constexpr (ACT == ACT_GELU) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const float sc = e8m0_to_float(unsigned(i < 4 ? sb0 : sb1));
+              const bf16x2 p = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(unsigned(qc[qs][c][i]), sc, false);
+              const bf16x2 r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(unsigned(qc[qs][c][i]), sc, true);
+              ss = fmaf(float(p[0]), float(p[0]), ss);
+              ss = fmaf(float(p[1]), float(p[1]), ss);
+              ss = fmaf(float(r[0]), float(r[0]), ss);
+              ss = fmaf(float(r[1]), float(r[1]), ss);
+            }
+          }
+        }
+        if constexpr (ACT == ACT_GELU) {
+          ss += other_half(ss);
+          rq[qs] = __builtin_amdgcn_rsqf(ss * (1.0f / D) + a.eps) * c2;
+        } else {
+          rq[qs] = 1.0f;
+        }
+        continue;
+      }
 #pragma unroll
       for (int c = 0; c < kQChunks; ++c) {
         const int d0 = (D / 2) * g + 8 * c;
@@ -399,10 +546,13 @@ __global__ __launch_bounds__(64 * NWQ * NWK, QSUB == 2 ? 1 : 2) void attn_kernel
       lds_barrier();
       unsigned char* st_base = smem + stage * kStageBytes;
       float* kscale_st = kscale_all + (ACT == ACT_GELU ? stage * NWK * 64 : 0);
-      if constexpr (ACT == ACT_GELU) {
+      if constexpr (ACT == ACT_GELU || IN == IN_MX8) {
 #pragma unroll
         for (int kg = 0; kg < NWK; ++kg)
-          if (t0 + kg < cur.ntiles) K::key_scales(a.eps, st_base + kg * K::kGroupBytes, kscale_st + kg * 64);
+          if (t0 + kg < cur.ntiles) {
+            if constexpr (ACT == ACT_GELU) K::key_scales(a.eps, st_base + kg * K::kGroupBytes, kscale_st + kg * 64);
+            if constexpr (IN == IN_MX8) K::convert_v(st_base + kg * K::kGroupBytes);
+          }
         lds_barrier();
       }
       const int tile = t0 + wk;
@@ -413,7 +563,7 @@ __global__ __launch_bounds__(64 * NWQ * NWK, QSUB == 2 ? 1 : 2) void attn_kernel
         active = active && kblk <= wblk && kblk >= wblk - a.window_blocks + 1;
       }
       const unsigned char* ks = st_base + wk * K::kGroupBytes;
-      const unsigned char* vs = ks + kTileBytes;
+      const unsigned char* vs = ks + K::kVOff;
       const float* kscale = kscale_st + wk * 64;
       // S^T for two 32-key halves of the tile, each K operand read feeding QSUB MFMAs.
       f32x16 s[QSUB][2];
@@ -424,14 +574,41 @@ __global__ __launch_bounds__(64 * NWQ * NWK, QSUB == 2 ? 1 : 2) void attn_kernel
 #pragma unroll
           for (int i = 0; i < 16; ++i) s[qs][st][i] = 0.f;
       if (active) {
+        if constexpr (IN == IN_MX8) {
+          // block-scaled fp8 MFMA: key row operand laid out like the query's
+          // (16-byte chunks 4c+g and 4c+2+g), lane-half g giving block 2c+g's scale
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+          for (int st = 0; st < 2; ++st) {
+            const int krow = 32 * st + kp;
+            const unsigned ksw = *reinterpret_cast<const unsigned*>(ks + K::kKsOff + 4 * krow);
 #pragma unroll
-          for (int c = 0; c < kQChunks; ++c) {
-            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + st * 32 * kRowBytes + k_off[c]);
+            for (int c = 0; c < D / 64; ++c) {
+              const int blk = 2 * c + g;
+              const u32x4 w0 = *reinterpret_cast<const u32x4*>(ks + krow * D + 16 * ((4 * c + g) ^ swz_c<D>(krow)));
+              const u32x4 w1 = *reinterpret_cast<const u32x4*>(ks + krow * D + 16 * ((4 * c + 2 + g) ^ swz_c<D>(krow)));
+              i32x8 ka;
 #pragma unroll
-            for (int qs = 0; qs < QSUB; ++qs) s[qs][st] = mfma_32x32x16(kf, qf[qs][c], s[qs][st]);
+              for (int i = 0; i < 4; ++i) {
+                ka[i] = int(w0[i]);
+                ka[4 + i] = int(w1[i]);
+              }
+              const int kscl = int((ksw >> (8 * blk)) & 0xFFu);
+#pragma unroll
+              for (int qs = 0; qs < QSUB; ++qs)
+                s[qs][st] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qc[qs][c], s[qs][st], 0, 0, 0, kscl,
+                                                                             0, qsc[qs][c]);
+            }
           }
+        } else {
+#pragma unroll
+          for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int c = 0; c < kQChunks; ++c) {
+              const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + st * 32 * kRowBytes + k_off[c]);
+#pragma unroll
+              for (int qs = 0; qs < QSUB; ++qs) s[qs][st] = mfma_32x32x16(kf, qf[qs][c], s[qs][st]);
+            }
+        }
       }
       if constexpr (kStages == 2) {
         if (t0 == 0) {  // every wave issues its share of the tile loads
@@ -724,7 +901,7 @@ hipError_t launch_attn_mfma(int D, int in, int shape, int act, const AttnArgs& a
   }
   if (D == 32) return launch_for_shape<32, IN_MX>(shape, act, a, num_cu, max_items, st);
   if (D == 64) return launch_for_shape<64, IN_MX>(shape, act, a, num_cu, max_items, st);
-  return launch_for_shape<128, IN_MX>(shape, act, a, num_cu, max_items, st);
+  return launch_for_shape<128, IN_MX8>(shape, act, a, num_cu, max_items, st);
 }
 
 hipError_t launch_combine(int D, const CombineArgs& a, hipStream_t st) {

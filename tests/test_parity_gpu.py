@@ -113,6 +113,33 @@ def test_mxfp8_window_and_full(D):
     full_parity(adhoc("mx_full", "self", "softmax", "mxfp8", L, L, 2, D, seed=D + 1))
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("act", ["softmax", "gelu_tanh"])
+def test_mxfp8_cross_and_pma(D, act):
+    full_parity(adhoc("mx_cross", "cross", act, "mxfp8", [5, 200, 0, 33], [9, 70, 4, 130], 2, D, seed=D + 7))
+    full_parity(adhoc("mx_pma", "pma", act, "mxfp8", [32, 32, 32], [3, 3000, 65], 2, D, seed=D + 8))
+
+
+@pytest.mark.parametrize("act", ["softmax", "gelu_tanh"])
+def test_mxfp8_block_scales_far_apart(act):
+    """Every 32-element block of a row gets its own power-of-two magnitude
+    (q block b times 2^s_b, k block b times 2^-s_b, s_b in [-5, 5]), so each
+    row's scale bytes differ block to block while the scores keep their size:
+    applying one block's scale to another block's elements is then off by up
+    to 2^20 and cannot pass."""
+    D = 128
+    L = [70, 300]
+    w = adhoc("mx_spread", "self" if act == "softmax" else "cross", act, "mxfp8", L, L, 2, D,
+              window=128 if act == "softmax" else 0, seed=91)
+    s = np.array([-5, 3, 5, -2], dtype=np.float64)
+    f = np.repeat(2.0 ** s, D // 4).astype(np.float32)
+    w.q = w.q * f
+    w.k = w.k / f
+    w.mx = {n: mx_encode_e4m3(x) for n, x in (("q", w.q), ("k", w.k), ("v", w.v))}
+    assert len(np.unique(w.mx["q"][1][0, 0])) == 4
+    full_parity(w)
+
+
 def test_single_key_gives_value_row():
     w = adhoc("one_key", "pma", "softmax", "bf16", [32, 32], [1, 1], 2, 64, seed=9)
     got = run_gpu(w)
