@@ -101,7 +101,7 @@ Plan make_plan(int B, int H, int D, int variant, int act, int window, int dtype,
   w.pbase_off = off;
   off = align256(off + sizeof(int32_t) * size_t(B));
   w.items_off = off;
-  off = align256(off + sizeof(int4) * size_t(w.max_items));
+  off = align256(off + sizeof(WorkItem) * size_t(w.max_items));
   w.part_o_off = off;
   off = align256(off + sizeof(float) * size_t(w.max_slots) * kPmaRows * D);
   w.part_ml_off = off;
@@ -156,7 +156,7 @@ int jagged_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
   WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
   int32_t* nsplit = reinterpret_cast<int32_t*>(ws + p.ws.nsplit_off);
   int32_t* pbase = reinterpret_cast<int32_t*>(ws + p.ws.pbase_off);
-  int4* items = reinterpret_cast<int4*>(ws + p.ws.items_off);
+  WorkItem* items = reinterpret_cast<WorkItem*>(ws + p.ws.items_off);
   float* part_o = reinterpret_cast<float*>(ws + p.ws.part_o_off);
   float2* part_ml = reinterpret_cast<float2*>(ws + p.ws.part_ml_off);
 

@@ -27,10 +27,10 @@ __global__ __launch_bounds__(kF32Rows) void attn_f32_kernel(AttnArgs a) {
   const float* vv = reinterpret_cast<const float*>(a.v);
   float* out = reinterpret_cast<float*>(a.out);
   for (int idx = blockIdx.x; idx < n_items; idx += gridDim.x) {
-    const int4 it = a.items[idx];
-    const int b = it.x, h = it.y, q0 = it.z;
-    const int qbeg = a.qo[b], lq = a.qo[b + 1] - qbeg;
-    const int kbeg = a.ko[b], lk = a.ko[b + 1] - kbeg;
+    const WorkItem it = a.items[idx];
+    const int h = it.h, q0 = it.q0;
+    const int qbeg = it.qbeg, lq = it.lq;
+    const int kbeg = it.kbeg, lk = it.lk;
     const int qrow = q0 + int(threadIdx.x);
     if (qrow >= lq) continue;
     float q[D], o[D];

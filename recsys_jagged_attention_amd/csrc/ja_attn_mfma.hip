@@ -40,6 +40,8 @@
 // activation input, no correction stage); the block window needs no element
 // mask because 64-key tiles coincide with the 64-token blocks (same page,
 // "BlockAttention"); only a sample's ragged last tile is masked.
+#include <type_traits>
+
 #include "ja_device.h"
 #include "jagged_attn.h"
 
@@ -88,10 +90,13 @@ __device__ __forceinline__ bf16x8 zero8() {
 // LDS at M0 + 16*lane.  Issued as inline asm on purpose: the compiler does not
 // track it, so it neither drains the prefetch with a conservative vmcnt(0)
 // before every later LDS read nor keeps 64-bit lane addresses live.  Completion
-// is ordered by wait_vmcnt() + lds_barrier() below.  No compiler-generated code
-// in these kernels reads M0 (checked in the generated ISA).  `dep` only pins
-// the instruction after the value it names has been computed.
-__device__ __forceinline__ void lds_dma16(const void* sbase, unsigned voff, unsigned lds_addr, float dep) {
+// is ordered by wait_vmcnt() + lds_barrier() below, both volatile asm with a
+// memory clobber: the compiler keeps volatile asm in program order, so a load
+// can neither move above the barrier that frees its target nor below the wait
+// that consumes it, while MFMAs and LDS reads may be scheduled around it (no
+// memory clobber here).  No compiler-generated code in these kernels reads M0
+// (checked in the generated ISA).
+__device__ __forceinline__ void lds_dma16(const void* sbase, unsigned voff, unsigned lds_addr) {
   // the base and the LDS address are wave-uniform: make that explicit for the "s" operands
   const uintptr_t p = reinterpret_cast<uintptr_t>(sbase);
   // (readfirstlane returns int: convert through unsigned so nothing is sign-extended)
@@ -100,7 +105,7 @@ __device__ __forceinline__ void lds_dma16(const void* sbase, unsigned voff, unsi
   const uint64_t pu = (hi << 32) | lo;
   const unsigned lu = unsigned(__builtin_amdgcn_readfirstlane(lds_addr));
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(voff), "s"(reinterpret_cast<const void*>(pu)), "s"(lu), "v"(dep) : "memory", "m0");
+               :: "v"(voff), "s"(reinterpret_cast<const void*>(pu)), "s"(lu) : "m0");
 }
 
 // 4 bytes per lane into LDS at M0 + 4*lane (same contract as lds_dma16).
@@ -111,7 +116,20 @@ __device__ __forceinline__ void lds_dma4(const void* sbase, unsigned voff, unsig
   const uint64_t pu = (hi << 32) | lo;
   const unsigned lu = unsigned(__builtin_amdgcn_readfirstlane(lds_addr));
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
-               :: "v"(voff), "s"(reinterpret_cast<const void*>(pu)), "s"(lu) : "memory", "m0");
+               :: "v"(voff), "s"(reinterpret_cast<const void*>(pu)), "s"(lu) : "m0");
+}
+
+// Online softmax keeps exponentials below 2^kLazyLog2 (see the tile loop).
+constexpr float kLazyLog2 = 8.0f;
+
+// A wave-uniform pointer made explicit (scalar registers), through unsigned
+// halves so that nothing is sign-extended.
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+  const uintptr_t u = reinterpret_cast<uintptr_t>(p);
+  const uint64_t hi = unsigned(__builtin_amdgcn_readfirstlane(unsigned(u >> 32)));
+  const uint64_t lo = unsigned(__builtin_amdgcn_readfirstlane(unsigned(u)));
+  return reinterpret_cast<const T*>((hi << 32) | lo);
 }
 
 // 16-byte chunk swizzle of an fp8 code tile (D bytes per row) for the fp8
@@ -183,78 +201,90 @@ struct Attn {
   static constexpr int kCodeSegs = 64 * D / 1024;        // 1 KB segments of an fp8 code tile
   static_assert(NWK == 1 || QSUB == 1, "key groups are merged for single-block waves only");
 
-  // Direct-to-LDS load instructions one wave issues per key tile (MX8: wave 0
-  // also issues the two scale rows).
-  static __device__ __forceinline__ int loads_per_tile(int wave) {
-    if constexpr (IN == IN_BF16) return (2 * kSegs) / kWaves;
-    else if constexpr (IN == IN_MX8) return (2 * kCodeSegs) / kWaves + (wave == 0 ? 2 : 0);
-    else return 0;
+  // ---- Direct-to-LDS loads (bf16 and MX8) --------------------------------
+  // A key tile is loaded as 1 KB segments (K then V), shared round-robin by
+  // the waves: job k of a wave moves segment wave + kWaves*k.  The lane part of
+  // a job's source offset is the same for every full tile, so it is computed
+  // once per kernel; only a sample's ragged last tile clamps rows.
+  static constexpr int kRowLd = kMx8 ? D : kRowBytes;            // bytes per loaded row
+  static constexpr int kSegsLd = 64 * kRowLd / 1024;             // segments per K (or V) tile
+  static constexpr int kRowsPerSeg = 1024 / kRowLd;
+  static constexpr int kChunksPerRow = kRowLd / 16;
+  static constexpr int kDmaTile = (IN == IN_BF16 || kMx8) ? 2 * kSegsLd / kWaves : 0;  // jobs per wave per tile
+  static constexpr int kDmaJobs = NWK * kDmaTile;                // jobs per wave per key group
+  static constexpr int kVLoadOff = kMx8 ? kVcOff : kTileBytes;   // LDS offset of the V rows in a group
+
+  // What the next direct loads fetch: tiles [t0, t0 + NWK) of an item (none
+  // when t0 >= ntiles) into the stage at LDS byte address `lds`.  A tile that
+  // does not exist is loaded from a valid stand-in row (dk/dv) instead, so that
+  // every job is branch-free; its LDS copy is never read.
+  struct Pf {
+    const unsigned char* tk[NWK];  // first K row of tile t0 + kg (or the stand-in row)
+    const unsigned char* tv[NWK];
+    int lim[NWK];                  // last row of the tile that holds a key (0 for stand-ins)
+    const uint8_t* ksb;            // MX8 scale rows of the item's head
+    const uint8_t* vsb;
+    int kv_lo, kv_hi, t0, ntiles;
+    unsigned lds;
+  };
+
+  // Job j: segment wave + kWaves*(j % kDmaTile) of tile j / kDmaTile.  Rows of a
+  // ragged tile are clamped to the last key (min(row, lim) * row_bytes, a
+  // 24-bit product: row < 64, and H <= 4096, D <= 128 keep row_bytes <= 1 MiB).
+  static __device__ __forceinline__ void pf_job(const Pf& p, int j, unsigned row_bytes) {
+    const int kg = j / kDmaTile, k = j % kDmaTile;
+    const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+    const int lane = int(threadIdx.x) & 63;
+    const int sg = wave + kWaves * k;
+    const bool is_v = sg >= kSegsLd;
+    const int seg = is_v ? sg - kSegsLd : sg;
+    const int lim = p.lim[kg];
+    const unsigned char* tile = is_v ? p.tv[kg] : p.tk[kg];
+    const int row = seg * kRowsPerSeg + lane / kChunksPerRow;
+    const int phys = lane % kChunksPerRow;
+    int c;
+    if constexpr (kMx8) c = phys ^ swz_c<D>(row);
+    else c = phys ^ (is_v ? swz_v<D>(row) : swz_k<D>(row));
+    const unsigned off = __umul24(unsigned(min(row, lim)), row_bytes) + 16u * unsigned(c);
+    lds_dma16(tile, off, p.lds + kg * kGroupBytes + (is_v ? kVLoadOff : 0) + seg * 1024);
   }
 
-  // Issue the loads of one key tile (keys [key0, key0+64) of the item; rows at
-  // or beyond kv_end are replaced by row kv_end-1, which the mask removes).
-  static __device__ __forceinline__ void issue_tile(unsigned char* grp, const __bf16* kb,
-                                                    const __bf16* vb, const uint8_t* ksb,
-                                                    const uint8_t* vsb, size_t rs, int key0,
-                                                    int kv_end, float dep) {
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    if constexpr (IN == IN_BF16) {
-      // 2 * kSegs segments of 1 KB (K then V), waves round-robin.  Byte offsets
-      // from the item's base fit 32 bits (the plan rejects larger samples).
-      const unsigned row_bytes = unsigned(rs) * 2u;
-      const unsigned grp_lds = lds_addr_of(grp);
+  // MX8: the 4 scale bytes of each of the tile's 64 key rows (wave 0 only).
+  static __device__ __forceinline__ void pf_scales(const Pf& p, unsigned srow) {
+    if constexpr (kMx8) {
+      if (__builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6) != 0) return;
 #pragma unroll
-      for (int s = wave; s < 2 * kSegs; s += kWaves) {
-        const bool is_v = s >= kSegs;
-        const int seg = is_v ? s - kSegs : s;
-        const int byte = seg * 1024 + 16 * lane;
-        const int row = byte / kRowBytes;
-        const int phys = (byte % kRowBytes) / 16;
-        const int c = phys ^ (is_v ? swz_v<D>(row) : swz_k<D>(row));
-        const unsigned key = unsigned(min(key0 + row, kv_end - 1));
-        lds_dma16(is_v ? (const void*)vb : (const void*)kb, key * row_bytes + 16u * unsigned(c),
-                  grp_lds + (is_v ? kTileBytes : 0) + seg * 1024, dep);
+      for (int kg = 0; kg < NWK; ++kg) {
+        if (p.t0 + kg >= p.ntiles) break;
+        const int key0 = p.kv_lo + 64 * (p.t0 + kg);
+        const unsigned r = unsigned(min(int(threadIdx.x) & 63, p.kv_hi - 1 - key0));
+        lds_dma4(p.ksb + size_t(key0) * srow, r * srow, p.lds + kg * kGroupBytes + kKsOff);
+        lds_dma4(p.vsb + size_t(key0) * srow, r * srow, p.lds + kg * kGroupBytes + kVsOff);
       }
-    } else if constexpr (IN == IN_MX8) {
-      // fp8 code tiles (D bytes per row) and the rows' 4 scale bytes, untouched.
-      const unsigned row_bytes = unsigned(rs);            // codes: one byte per element
-      const unsigned grp_lds = lds_addr_of(grp);
+    }
+  }
+
+  // MX (D < 128): decode 8 e4m3 codes x 2^(E-127) to bf16 through registers,
+  // keys [key0, key0+64) of the item, rows at or beyond kv_end replaced by row
+  // kv_end-1 (removed by the mask).
+  static __device__ __forceinline__ void decode_tile(unsigned char* grp, const __bf16* kb, const __bf16* vb,
+                                                     const uint8_t* ksb, const uint8_t* vsb, size_t rs, int key0,
+                                                     int kv_end) {
+    const int tid = threadIdx.x;
 #pragma unroll
-      for (int s = wave; s < 2 * kCodeSegs; s += kWaves) {
-        const bool is_v = s >= kCodeSegs;
-        const int seg = is_v ? s - kCodeSegs : s;
-        const int byte = seg * 1024 + 16 * lane;
-        const int row = byte / D;
-        const int phys = (byte % D) / 16;
-        const int c = phys ^ swz_c<D>(row);
-        const unsigned key = unsigned(min(key0 + row, kv_end - 1));
-        lds_dma16(is_v ? (const void*)vb : (const void*)kb, key * row_bytes + 16u * unsigned(c),
-                  grp_lds + (is_v ? kVcOff : kKcOff) + seg * 1024, dep);
-      }
-      if (wave == 0) {
-        const unsigned key = unsigned(min(key0 + lane, kv_end - 1));
-        const unsigned srow = unsigned(rs / kMxBlock);    // scale bytes between key rows
-        lds_dma4(ksb, key * srow, grp_lds + kKsOff);
-        lds_dma4(vsb, key * srow, grp_lds + kVsOff);
-      }
-    } else {
-      // MX: decode 8 e4m3 codes x 2^(E-127) to bf16 through registers.
-#pragma unroll
-      for (int u0 = 0; u0 < 2 * 64 * kChunks; u0 += kNT) {
-        const int u = u0 + tid;
-        const bool is_v = u >= 64 * kChunks;
-        const int uu = is_v ? u - 64 * kChunks : u;
-        const int row = uu / kChunks, c = uu % kChunks;
-        const int key = min(key0 + row, kv_end - 1);
-        const size_t e = size_t(key) * rs + 8 * c;
-        const uint8_t* codes = reinterpret_cast<const uint8_t*>(is_v ? (const void*)vb : (const void*)kb);
-        const uint8_t* sc = is_v ? vsb : ksb;
-        const bf16x8 x = decode_mx8(*reinterpret_cast<const u32x2*>(codes + e),
-                                    sc[size_t(key) * (rs / kMxBlock) + (8 * c) / kMxBlock]);
-        const int phys = c ^ (is_v ? swz_v<D>(row) : swz_k<D>(row));
-        *reinterpret_cast<bf16x8*>(grp + (is_v ? kTileBytes : 0) + row * kRowBytes + 16 * phys) = x;
-      }
+    for (int u0 = 0; u0 < 2 * 64 * kChunks; u0 += kNT) {
+      const int u = u0 + tid;
+      const bool is_v = u >= 64 * kChunks;
+      const int uu = is_v ? u - 64 * kChunks : u;
+      const int row = uu / kChunks, c = uu % kChunks;
+      const int key = min(key0 + row, kv_end - 1);
+      const size_t e = size_t(key) * rs + 8 * c;
+      const uint8_t* codes = reinterpret_cast<const uint8_t*>(is_v ? (const void*)vb : (const void*)kb);
+      const uint8_t* sc = is_v ? vsb : ksb;
+      const bf16x8 x = decode_mx8(*reinterpret_cast<const u32x2*>(codes + e),
+                                  sc[size_t(key) * (rs / kMxBlock) + (8 * c) / kMxBlock]);
+      const int phys = c ^ (is_v ? swz_v<D>(row) : swz_k<D>(row));
+      *reinterpret_cast<bf16x8*>(grp + (is_v ? kTileBytes : 0) + row * kRowBytes + 16 * phys) = x;
     }
   }
 
@@ -333,16 +363,16 @@ struct Attn {
     const uint8_t* vsb;
   };
 
-  static __device__ __forceinline__ Item make_item(const AttnArgs& a, const int4 it, size_t rs) {
+  static __device__ __forceinline__ Item make_item(const AttnArgs& a, const WorkItem& it, size_t rs) {
     Item c;
-    c.b = it.x;
-    c.h = it.y;
-    c.q0 = it.z;
-    c.split = it.w;
-    c.qbeg = a.qo[c.b];
-    c.lq = a.qo[c.b + 1] - c.qbeg;
-    const int kbeg = a.ko[c.b];
-    c.lk = a.ko[c.b + 1] - kbeg;
+    c.b = it.b;
+    c.h = it.h;
+    c.q0 = it.q0;
+    c.split = it.split;
+    c.qbeg = it.qbeg;
+    c.lq = it.lq;
+    const int kbeg = it.kbeg;
+    c.lk = it.lk;
     c.kv_lo = 0;
     c.kv_hi = c.lk;
     if constexpr (SPLIT) {
@@ -372,19 +402,48 @@ struct Attn {
     return c;
   }
 
-  // Issue the tiles [t0, t0 + NWK) of an item into one stage; returns the
-  // number of VMEM instructions this wave issued.
-  static __device__ __forceinline__ int issue_group(const Item& c, unsigned char* stage_base, int t0,
-                                                    size_t rs, float dep = 0.f) {
-    int n = 0;
+  // `stand` is an item with at least one tile (its first row stands in for
+  // tiles that do not exist).
+  static __device__ __forceinline__ Pf make_pf(const Item& c, int t0, unsigned lds, const Item& stand,
+                                               unsigned row_bytes) {
+    Pf p;
+    const unsigned char* kb = reinterpret_cast<const unsigned char*>(c.kb);
+    const unsigned char* vb = reinterpret_cast<const unsigned char*>(c.vb);
+    const size_t stand_off = size_t(stand.kv_lo) * row_bytes;
 #pragma unroll
-    for (int kg = 0; kg < NWK; ++kg)
-      if (t0 + kg < c.ntiles) {
-        issue_tile(stage_base + kg * kGroupBytes, c.kb, c.vb, c.ksb, c.vsb, rs, c.kv_lo + 64 * (t0 + kg),
-                   c.kv_hi, dep);
-        n += loads_per_tile(__builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6));
-      }
-    return n;
+    for (int kg = 0; kg < NWK; ++kg) {
+      const bool exists = t0 + kg < c.ntiles;
+      const int key0 = c.kv_lo + 64 * (t0 + kg);
+      const size_t off = size_t(key0) * row_bytes;
+      p.tk[kg] = uniform_ptr(exists ? kb + off : reinterpret_cast<const unsigned char*>(stand.kb) + stand_off);
+      p.tv[kg] = uniform_ptr(exists ? vb + off : reinterpret_cast<const unsigned char*>(stand.vb) + stand_off);
+      p.lim[kg] = exists ? min(63, c.kv_hi - 1 - key0) : 0;
+    }
+    p.ksb = c.ksb;
+    p.vsb = c.vsb;
+    p.kv_lo = c.kv_lo;
+    p.kv_hi = c.kv_hi;
+    p.t0 = t0;
+    p.ntiles = c.ntiles;
+    p.lds = lds;
+    return p;
+  }
+
+  // Load the tiles [t0, t0 + NWK) of an item into one stage in one go.
+  static __device__ __forceinline__ void issue_group(const Item& c, unsigned char* stage_base, int t0, size_t rs,
+                                                     unsigned row_bytes, unsigned srow) {
+    if constexpr (IN == IN_MX) {
+#pragma unroll
+      for (int kg = 0; kg < NWK; ++kg)
+        if (t0 + kg < c.ntiles)
+          decode_tile(stage_base + kg * kGroupBytes, c.kb, c.vb, c.ksb, c.vsb, rs, c.kv_lo + 64 * (t0 + kg), c.kv_hi);
+    } else {
+      const Pf p = make_pf(c, t0, lds_addr_of(stage_base), c, row_bytes);
+#pragma unroll
+      for (int j = 0; j < kDmaJobs; ++j)
+        if (t0 + j / kDmaTile < c.ntiles) pf_job(p, j, row_bytes);
+      pf_scales(p, srow);
+    }
   }
 };
 
@@ -425,10 +484,15 @@ __global__ __launch_bounds__(64 * NWQ * NWK, QSUB == 2 ? 1 : 2) void attn_kernel
     v_col[t] = 16 * ((col >> 3) ^ swz_v<D>((lane & 15) >> 2)) + 8 * ((col & 7) >> 2);
   }
   const float c2 = a.score_scale;  // softmax: log2(e)/sqrt(D); GELU: 1/sqrt(D)
+  const float lazy_thr = kLazyLog2 / c2;  // raw-score growth that forces a rescale
+
+  // Direct-load geometry: bytes between key rows.
+  const unsigned row_bytes = K::kMx8 ? unsigned(rs) : 2u * unsigned(rs);  // bytes between key rows
+  const unsigned srow = unsigned(rs / kMxBlock);                            // MX scale bytes between key rows
 
   Item cur = K::make_item(a, a.items[idx], rs);
   int stage = 0;
-  K::issue_group(cur, smem, 0, rs);
+  K::issue_group(cur, smem, 0, rs, row_bytes, srow);
 
   while (true) {
     const int qrow_w = cur.q0 + K::kRowsPerWave * wq;   // first row of this wave (sample-local)
@@ -436,7 +500,9 @@ __global__ __launch_bounds__(64 * NWQ * NWK, QSUB == 2 ? 1 : 2) void attn_kernel
     const int wblk = qrow_w / kBlock;
 
     // Q fragments: lane holds dims [(D/2)g, (D/2)g + D/2) of query row
-    // qrow_w + 32*qs + l32 (rows past the sample load the last row and are zeroed).
+    // qrow_w + 32*qs + l32.  Rows past the sample load its last row: their
+    // results are finite and never stored, and nothing waits on the loads
+    // before the first score MFMA.
     bf16x8 qf[QSUB][kQChunks];
     // MX8: operand c of lane-half g holds elements 64c+16g+[0,16) (bytes 0-15,
     // scaled by the lower lane-half's scale) and 64c+32+16g+[0,16) (bytes 16-31,
@@ -460,8 +526,8 @@ __global__ __launch_bounds__(64 * NWQ * NWK, QSUB == 2 ? 1 : 2) void attn_kernel
           const int sb1 = a.qs[row * (D / kMxBlock) + 2 * c + 1];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            qc[qs][c][i] = qrow < cur.lq ? int(w0[i]) : 0;
-            qc[qs][c][4 + i] = qrow < cur.lq ? int(w1[i]) : 0;
+            qc[qs][c][i] = int(w0[i]);
+            qc[qs][c][4 + i] = int(w1[i]);
           }
           qsc[qs][c] = g ? sb1 : sb0;
           if constexpr (ACT == ACT_GELU) {
@@ -494,7 +560,6 @@ __global__ __launch_bounds__(64 * NWQ * NWK, QSUB == 2 ? 1 : 2) void attn_kernel
           qf[qs][c] = decode_mx8(*reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(a.q) + row * D + d0),
                                  a.qs[row * (D / kMxBlock) + d0 / kMxBlock]);
         }
-        if (qrow >= cur.lq) qf[qs][c] = zero8();
       }
       rq[qs] = 1.0f;
       if constexpr (ACT == ACT_GELU) {
@@ -528,21 +593,25 @@ __global__ __launch_bounds__(64 * NWQ * NWK, QSUB == 2 ? 1 : 2) void attn_kernel
     }
 
     for (int t0 = 0; t0 < cur.ntiles; t0 += NWK) {
-      int pf = 0;
-      // Prefetch the next tile group (or the next item's first) into the other
-      // stage.  In an item's first iteration this happens after the first
-      // score MFMAs instead, once the Q loads (tracked by the compiler, which
-      // waits for all loads before their first use) have completed.
+      // The next key group (or the next item's first) goes to the other stage.
+      // Direct loads are issued between the score MFMAs below, after the first
+      // half has consumed every Q fragment: the compiler waits for the Q loads
+      // with counts that do not know about these loads.
       unsigned char* other = smem + (stage ^ 1) * kStageBytes;
+      // (no next group: tiles past the end of the current item, i.e. stand-ins)
+      const bool pf_cur = t0 + NWK < cur.ntiles || !has_next;
+      const typename K::Pf pf =
+          K::make_pf(pf_cur ? cur : nxt, pf_cur ? t0 + NWK : 0, lds_addr_of(other), cur, row_bytes);
       if constexpr (kStages == 2) {
-        if (t0 > 0) {
-          if (t0 + NWK < cur.ntiles) pf = K::issue_group(cur, other, t0 + NWK, rs);
-          else if (has_next) pf = K::issue_group(nxt, other, 0, rs);
+        if constexpr (IN == IN_MX) {  // decoded through registers: done here, in one go
+          if (t0 + NWK < cur.ntiles) K::issue_group(cur, other, t0 + NWK, rs, row_bytes, srow);
+          else if (has_next) K::issue_group(nxt, other, 0, rs, row_bytes, srow);
         }
       } else {
-        if (t0 > 0) K::issue_group(cur, smem, t0, rs);  // group 0 was issued before the item
+        // group 0 was loaded before the item
+        if (t0 > 0) K::issue_group(cur, smem, t0, rs, row_bytes, srow);
       }
-      wait_vmcnt(pf);
+      wait_vmcnt(0);
       lds_barrier();
       unsigned char* st_base = smem + stage * kStageBytes;
       float* kscale_st = kscale_all + (ACT == ACT_GELU ? stage * NWK * 64 : 0);
@@ -573,49 +642,78 @@ __global__ __launch_bounds__(64 * NWQ * NWK, QSUB == 2 ? 1 : 2) void attn_kernel
         for (int st = 0; st < 2; ++st)
 #pragma unroll
           for (int i = 0; i < 16; ++i) s[qs][st][i] = 0.f;
-      if (active) {
+      // Scores for the 32-key halves st = 0, 1 of the tile.  The next group's
+      // direct loads go between the MFMAs of the second half: for a group of
+      // full tiles (kFast) one branch-free job after each MFMA, else (ragged or
+      // partial groups) all jobs between the two halves.  LDS reads are not
+      // moved across volatile asm, so the K operand is read one MFMA ahead.
+      // Direct loads run only with two stages (else the group was loaded above).
+      constexpr bool kFast = kStages == 2 && (IN == IN_BF16 || IN == IN_MX8);
+      auto scores = [&]() {
         if constexpr (IN == IN_MX8) {
           // block-scaled fp8 MFMA: key row operand laid out like the query's
           // (16-byte chunks 4c+g and 4c+2+g), lane-half g giving block 2c+g's scale
+          constexpr int kNC = D / 64;
+          auto kop = [&](int krow, int c) {
+            const u32x4 w0 = *reinterpret_cast<const u32x4*>(ks + krow * D + 16 * ((4 * c + g) ^ swz_c<D>(krow)));
+            const u32x4 w1 = *reinterpret_cast<const u32x4*>(ks + krow * D + 16 * ((4 * c + 2 + g) ^ swz_c<D>(krow)));
+            i32x8 ka;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              ka[i] = int(w0[i]);
+              ka[4 + i] = int(w1[i]);
+            }
+            return ka;
+          };
 #pragma unroll
           for (int st = 0; st < 2; ++st) {
             const int krow = 32 * st + kp;
             const unsigned ksw = *reinterpret_cast<const unsigned*>(ks + K::kKsOff + 4 * krow);
 #pragma unroll
-            for (int c = 0; c < D / 64; ++c) {
-              const int blk = 2 * c + g;
-              const u32x4 w0 = *reinterpret_cast<const u32x4*>(ks + krow * D + 16 * ((4 * c + g) ^ swz_c<D>(krow)));
-              const u32x4 w1 = *reinterpret_cast<const u32x4*>(ks + krow * D + 16 * ((4 * c + 2 + g) ^ swz_c<D>(krow)));
-              i32x8 ka;
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                ka[i] = int(w0[i]);
-                ka[4 + i] = int(w1[i]);
-              }
-              const int kscl = int((ksw >> (8 * blk)) & 0xFFu);
+            for (int c = 0; c < kNC; ++c) {
+              const i32x8 ka = kop(krow, c);  // two MFMAs per half: no read-ahead (registers)
+              const int kscl = int((ksw >> (8 * (2 * c + g))) & 0xFFu);
 #pragma unroll
               for (int qs = 0; qs < QSUB; ++qs)
                 s[qs][st] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qc[qs][c], s[qs][st], 0, 0, 0, kscl,
                                                                              0, qsc[qs][c]);
+              if constexpr (kFast) {
+                if (st == 1) {
+#pragma unroll
+                  for (int j = c * K::kDmaJobs / kNC; j < (c + 1) * K::kDmaJobs / kNC; ++j)
+                    K::pf_job(pf, j, row_bytes);
+                }
+              }
             }
           }
         } else {
 #pragma unroll
-          for (int st = 0; st < 2; ++st)
+          for (int st = 0; st < 2; ++st) {
+            bf16x8 knext = *reinterpret_cast<const bf16x8*>(ks + st * 32 * kRowBytes + k_off[0]);
 #pragma unroll
             for (int c = 0; c < kQChunks; ++c) {
-              const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + st * 32 * kRowBytes + k_off[c]);
+              const bf16x8 kf = knext;
+              if (c + 1 < kQChunks) knext = *reinterpret_cast<const bf16x8*>(ks + st * 32 * kRowBytes + k_off[c + 1]);
 #pragma unroll
               for (int qs = 0; qs < QSUB; ++qs) s[qs][st] = mfma_32x32x16(kf, qf[qs][c], s[qs][st]);
+              if constexpr (kFast) {
+                if (st == 1) {
+#pragma unroll
+                  for (int j = c * K::kDmaJobs / kQChunks; j < (c + 1) * K::kDmaJobs / kQChunks; ++j)
+                    K::pf_job(pf, j, row_bytes);
+                }
+              }
             }
+          }
         }
+      };
+      if (active) {
+        scores();
+      } else if constexpr (kFast) {
+#pragma unroll
+        for (int j = 0; j < K::kDmaJobs; ++j) K::pf_job(pf, j, row_bytes);
       }
-      if constexpr (kStages == 2) {
-        if (t0 == 0) {  // every wave issues its share of the tile loads
-          if (NWK < cur.ntiles) K::issue_group(cur, other, NWK, rs, s[QSUB - 1][1][15]);
-          else if (has_next) K::issue_group(nxt, other, 0, rs, s[QSUB - 1][1][15]);
-        }
-      }
+      if constexpr (kFast) K::pf_scales(pf, srow);
       if (active) {
         // Register i of half st holds key 32*st + 16*(i/8) + 8g + i%8 of the tile.
         const int nvalid = cur.kv_hi - key0;  // keys at or beyond this index are outside
@@ -638,8 +736,12 @@ __global__ __launch_bounds__(64 * NWQ * NWK, QSUB == 2 ? 1 : 2) void attn_kernel
 #pragma unroll
               for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[qs][st][i]);
             mt = fmaxf(mt, other_half(mt));
-            const float m_new = fmaxf(m[qs], mt);
-            if (__any(m_new != m[qs])) {
+            // Lazy rescale: the reference max moves only when a row's tile max
+            // exceeds it by more than kLazyLog2 (base 2), so exponentials stay
+            // below 2^kLazyLog2 and most tiles skip the O rescale.  Softmax is
+            // unchanged by the choice of reference; the final 1/l uses the same one.
+            if (__any(mt - m[qs] > lazy_thr)) {
+              const float m_new = fmaxf(m[qs], mt);
               const float alpha = m[qs] == -__builtin_huge_valf() ? 0.f : fast_exp2((m[qs] - m_new) * c2);
               l[qs] *= alpha;
 #pragma unroll
@@ -697,7 +799,7 @@ __global__ __launch_bounds__(64 * NWQ * NWK, QSUB == 2 ? 1 : 2) void attn_kernel
       if constexpr (kStages == 2) stage ^= 1;
     }
     if constexpr (kStages == 2) {
-      if (cur.ntiles == 0 && has_next) K::issue_group(nxt, smem + stage * kStageBytes, 0, rs);
+      if (cur.ntiles == 0 && has_next) K::issue_group(nxt, smem + stage * kStageBytes, 0, rs, row_bytes, srow);
     }
 
     // Merge the key groups of a query group (NWK > 1, QSUB == 1) through the free stage.
@@ -740,7 +842,7 @@ __global__ __launch_bounds__(64 * NWQ * NWK, QSUB == 2 ? 1 : 2) void attn_kernel
       lds_barrier();  // the merge buffer may be refilled by the next prefetch
     }
     if constexpr (kStages == 1) {
-      if (has_next) K::issue_group(nxt, smem, 0, rs);  // LDS is free again
+      if (has_next) K::issue_group(nxt, smem, 0, rs, row_bytes, srow);  // LDS is free again
     }
 
     if (wk == 0) {

@@ -24,7 +24,7 @@ enum In { IN_F32 = 0, IN_BF16 = 1, IN_MX = 2, IN_MX8 = 3 };
 //   [0, 256)            WsHeader
 //   sample_nsplit[B]    key-split count per sample (1 = written directly)
 //   sample_pbase[B]     first partial slot of the sample
-//   items[max_items]    int4 {b, h, q0, split}
+//   items[max_items]    WorkItem
 //   part_o[max_slots][32][D] float, part_ml[max_slots][32] float2
 // ---------------------------------------------------------------------------
 constexpr int kXcds = 8;           // workgroup w runs on XCD w % 8 (round-robin dispatch)
@@ -36,6 +36,14 @@ struct WsHeader {
   int32_t pad0;
   int32_t xcd_begin[kXcds + 1];  // items [xcd_begin[x], xcd_begin[x+1]) run on XCD x
   int32_t pad[64 - 4 - (kXcds + 1)];
+};
+
+// One unit of attention work: sample b, head h, first query row q0 and key
+// split, with the sample's offsets copied in so that a kernel needs a single
+// 32-byte read (no dependent loads) to start the item.
+struct WorkItem {
+  int32_t b, h, q0, split;
+  int32_t qbeg, lq, kbeg, lk;
 };
 
 struct WsLayout {
@@ -64,7 +72,7 @@ struct PlanArgs {
   WsHeader* hdr;
   int32_t* nsplit;
   int32_t* pbase;
-  int4* items;
+  WorkItem* items;
 };
 
 struct AttnArgs {
@@ -78,7 +86,7 @@ struct AttnArgs {
   const int32_t* qo;
   const int32_t* ko;
   const WsHeader* hdr;
-  const int4* items;
+  const WorkItem* items;
   const int32_t* nsplit;
   const int32_t* pbase;
   float* part_o;

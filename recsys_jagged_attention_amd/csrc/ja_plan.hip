@@ -143,12 +143,20 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ int s_base[kPlanThreads];
   __shared__ int s_nqt[kPlanThreads];
   __shared__ int s_ns[kPlanThreads];
+  __shared__ int s_qb[kPlanThreads], s_lq[kPlanThreads], s_kb[kPlanThreads], s_lk[kPlanThreads];
   int item_carry = 0, slot_carry = 0;
   double cost_carry = 0.0;
   for (int base = 0; base < a.B; base += kPlanThreads) {
     const int b = base + tid;
     SampleWork w{0, 1, 0, 0, 0.0};
-    if (b < a.B) w = sample_work(a, a.qo[b + 1] - a.qo[b], a.ko[b + 1] - a.ko[b]);
+    int qb = 0, lq = 0, kb = 0, lk = 0;
+    if (b < a.B) {
+      qb = a.qo[b];
+      lq = a.qo[b + 1] - qb;
+      kb = a.ko[b];
+      lk = a.ko[b + 1] - kb;
+      w = sample_work(a, lq, lk);
+    }
     int items_total, slots_total;
     double cost_total;
     const int ibase = block_exclusive_scan(w.cnt, s_iwarp, &items_total) + item_carry;
@@ -169,6 +177,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     s_base[tid] = ibase;
     s_nqt[tid] = w.nqt;
     s_ns[tid] = w.ns;
+    s_qb[tid] = qb;
+    s_lq[tid] = lq;
+    s_kb[tid] = kb;
+    s_lk[tid] = lk;
     __syncthreads();
     // One thread per (sample, head) writes that head's items (query tile, then
     // split), so no thread divides per item.  Item order within a sample is
@@ -178,8 +190,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       const int j = p / a.H, h = p - j * a.H;
       const int nq = s_nqt[j], nsj = s_ns[j];
       int ib = s_base[j] + h * nq * nsj;
+      const int qb = s_qb[j], lq = s_lq[j], kb = s_kb[j], lk = s_lk[j];
       for (int qt = 0; qt < nq; ++qt)
-        for (int sp = 0; sp < nsj; ++sp) a.items[ib++] = make_int4(base + j, h, qt * a.bm, sp);
+        for (int sp = 0; sp < nsj; ++sp) a.items[ib++] = WorkItem{base + j, h, qt * a.bm, sp, qb, lq, kb, lk};
     }
     item_carry += items_total;
     slot_carry += slots_total;
