@@ -116,9 +116,8 @@ size_t jagged_attn_workspace_size(int B, int H, int D, int variant, int act,
                                   int32_t total_kv);
 
 /* Synchronises `stream` (a hipStream_t or NULL) and returns the device status
- * word the last jagged_attn_fwd on this workspace wrote: JA_OK, JA_EOFFSETS,
- * or JA_EUNSUPPORTED when one sample's keys span 4 GiB or more of a bf16 K/V
- * tensor; JA_EHIP / JA_EINVAL if it cannot be read. */
+ * word the last jagged_attn_fwd on this workspace wrote: JA_OK or
+ * JA_EOFFSETS; JA_EHIP / JA_EINVAL if it cannot be read. */
 int jagged_attn_check(const void *workspace, void *stream);
 
 /* Static description of a status code; never NULL. */

@@ -15,10 +15,14 @@ hipError_t launch_attn_mfma(int D, int in, int shape, int act, const AttnArgs& a
                             int64_t max_items, hipStream_t st);
 hipError_t launch_combine(int D, const CombineArgs& a, hipStream_t st);
 hipError_t launch_attn_f32(int D, int act, bool window, const AttnArgs& a, int grid, hipStream_t st);
+hipError_t launch_attn_pp(int D, int act, const AttnArgs& a, int num_cu, int64_t max_items, hipStream_t st);
+hipError_t launch_key_rms(int D, const void* k, int64_t rows, float eps, float* out, hipStream_t st);
+int pp_rows();
 
 namespace {
 
-constexpr int kShapeQTiled = 0, kShapeWindow = 1, kShapeKvSplit = 2, kShapeFullSelf = 3, kShapeF32 = 4;
+constexpr int kShapeQTiled = 0, kShapeWindow = 1, kShapeKvSplit = 2, kShapeFullSelf = 3, kShapeF32 = 4,
+              kShapePingPong = 5;
 constexpr int kMaxGrid = 1 << 20;
 
 struct Plan {
@@ -81,6 +85,9 @@ Plan make_plan(int B, int H, int D, int variant, int act, int window, int dtype,
     p.shape = kShapeKvSplit;
     p.bm = kPmaRows;
     p.kvc = choose_kvc(H, total_kv);
+  } else if (dtype == JA_BF16) {
+    p.shape = kShapePingPong;  // self (no window) and cross: one tile stream, 8 waves x 32 rows
+    p.bm = pp_rows();
   } else if (variant == JA_SELF && act == JA_SOFTMAX) {
     p.shape = kShapeFullSelf;
     p.bm = 256;  // eight waves x 32 query rows
@@ -106,6 +113,8 @@ Plan make_plan(int B, int H, int D, int variant, int act, int window, int dtype,
   off = align256(off + sizeof(float) * size_t(w.max_slots) * kPmaRows * D);
   w.part_ml_off = off;
   off = align256(off + sizeof(float2) * size_t(w.max_slots) * kPmaRows);
+  w.kscale_off = off;
+  if (p.shape == kShapePingPong && act == JA_GELU_TANH) off = align256(off + sizeof(float) * size_t(total_kv) * H);
   w.total = off;
   return p;
 }
@@ -171,9 +180,6 @@ int jagged_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
   pa.kvc = p.kvc;
   pa.self_check = variant == JA_SELF;
   pa.window_blocks = window / kBlock;
-  // 32-bit DMA offsets: bf16 rows (2 bytes/element) and fp8 code rows (D = 128)
-  pa.kv_row_bytes = io->dtype == JA_BF16 ? int64_t(H) * D * 2
-                                         : (io->dtype == JA_MXFP8_E4M3 && D == 128 ? int64_t(H) * D : 0);
   pa.max_items = p.ws.max_items;
   pa.max_slots = p.ws.max_slots;
   pa.hdr = hdr;
@@ -202,6 +208,12 @@ int jagged_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
   aa.window_blocks = window / kBlock;
   aa.kvc = p.kvc;
   aa.eps = io->rms_eps > 0.f ? io->rms_eps : 1e-6f;
+  aa.kscale = nullptr;
+  if (p.shape == kShapePingPong && act == JA_GELU_TANH) {
+    float* ksc = reinterpret_cast<float*>(ws + p.ws.kscale_off);
+    if (launch_key_rms(D, k, int64_t(io->total_kv) * H, aa.eps, ksc, stream) != hipSuccess) return JA_EHIP;
+    aa.kscale = ksc;
+  }
   const float inv_sqrt_d = 1.0f / std::sqrt(float(D));
   aa.score_scale = act == JA_SOFTMAX ? inv_sqrt_d * 1.4426950408889634f : inv_sqrt_d;
 
@@ -211,6 +223,9 @@ int jagged_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
   hipError_t e;
   if (p.shape == kShapeF32) {
     e = launch_attn_f32(D, act, window > 0, aa, grid, stream);
+  } else if (p.shape == kShapePingPong) {
+    e = launch_attn_pp(D, act, aa, device_cus(), p.ws.max_items, stream);
+
   } else {
     const int in = io->dtype == JA_BF16 ? IN_BF16 : IN_MX;
     e = launch_attn_mfma(D, in, p.shape, act, aa, device_cus(), p.ws.max_items, stream);

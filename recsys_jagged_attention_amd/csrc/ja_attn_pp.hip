@@ -1,0 +1,533 @@
+// Ping-pong MFMA attention for the query-tiled shapes of GDPA: self-attention
+// without a window and cross-attention (long queries), bf16 inputs, softmax or
+// GELU scores (techfeed.io summary of "GEM Training: How Meta Doubled the
+// Efficiency of Its LLM-Scale Ads Foundation Model", section "Generalized
+// Dot-Product Attention（GDPA）").
+//
+// A workgroup of 8 waves owns work items of 256 query rows (32 per wave) and
+// walks the key tiles (64 keys) of all its items as one stream.  Step s of the
+// stream has one MFMA phase per wave -- O += V_{s-1} P_{s-1} followed by the
+// scores S_s = K_s Q^T -- and one VALU phase (softmax or GELU of a score tile).
+// Waves 0-3 run "MFMA(s), VALU(s)", waves 4-7 run "VALU(s-1), MFMA(s)": every
+// SIMD holds one wave of each kind, so while one wave keeps the matrix core
+// busy the other does its exponentials, with one workgroup barrier per step.
+// The stream does not stop at item boundaries: an item's Q is loaded at the
+// start of its first step and the previous item's output is written between
+// two MFMA phases.
+//
+// LDS holds a ring of 4 tiles (K and V, plus the key scales of the GELU path):
+// in step s the waves read K_s and V_{s-1}, tile s+1 has landed and tile s+2
+// is loaded by direct-to-LDS loads issued between the score MFMAs.  Operand
+// layouts, swizzles and the transposed score tile are those of the main MFMA
+// kernel (ja_attn_mfma.hip).
+#include "ja_device.h"
+#include "ja_mfma_util.h"
+#include "jagged_attn.h"
+
+namespace ja {
+
+namespace {
+
+constexpr int kPPWaves = 8;
+constexpr int kPPRows = 32 * kPPWaves;  // query rows per work item
+constexpr int kPPItemCache = 256;       // work item records staged in LDS per workgroup
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kSgMfma = 0x008, kSgDsRead = 0x100;
+
+template <int D, int ACT>
+struct PP {
+  static constexpr int kNT = 64 * kPPWaves;
+  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kTileBytes = 64 * kRowBytes;
+  static constexpr int kKsOff = 2 * kTileBytes;  // GELU: 64 fp32 key scales after K and V
+  static constexpr int kStageBytes = 2 * kTileBytes + (ACT == ACT_GELU ? 256 : 0);
+  static constexpr int kRing = 4;
+  static constexpr int kQChunks = D / 16;
+  static constexpr int kOTiles = D / 32;
+  static constexpr int kSegsLd = kTileBytes / 1024;
+  static constexpr int kRowsPerSeg = 1024 / kRowBytes;
+  static constexpr int kChunksPerRow = kRowBytes / 16;
+  static constexpr int kDmaJobs = 2 * kSegsLd / kPPWaves;  // 1 KB loads per wave per tile
+  static constexpr int kVmemPerTile = kDmaJobs + (ACT == ACT_GELU ? 1 : 0);
+  static_assert((2 * kSegsLd) % kPPWaves == 0, "tile segments must split evenly over the waves");
+  static_assert(kQChunks % kDmaJobs == 0, "loads are spread evenly over the score MFMAs");
+};
+
+// One work item as the stream needs it (wave-uniform).
+struct PItem {
+  int h, q0, qbeg, lq, lk, ntiles;
+  const unsigned char* kb;  // key row r of the head at kb + r * row_bytes
+  const unsigned char* vb;
+  const float* ksc;         // GELU: scale of key row r at ksc[r * H]
+};
+
+// Position in the tile stream: tile t of the k-th item of this workgroup.
+struct Cur {
+  int k, t;
+  bool valid;
+  PItem it;
+};
+
+typedef int i32x4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) const i32x4v lds_i32x4;
+
+struct PPCtx {
+  const WorkItem* items;
+  lds_i32x4* cache;       // LDS copy of this workgroup's first kPPItemCache records (2 x 16 B each)
+  const unsigned char* k;
+  const unsigned char* v;
+  const float* kscale;
+  __bf16* out;
+  int H;
+  int first, stride, n;   // item k of this workgroup is first + k * stride, k < n
+  unsigned row_bytes;
+};
+
+__device__ __forceinline__ WorkItem load_record(const PPCtx& c, int k) {
+  if (k < kPPItemCache) {
+    const i32x4v u = c.cache[2 * k], w = c.cache[2 * k + 1];
+    return WorkItem{u[0], u[1], u[2], u[3], w[0], w[1], w[2], w[3]};
+  }
+  return c.items[c.first + k * c.stride];
+}
+
+template <int D>
+__device__ __forceinline__ PItem make_pitem(const PPCtx& c, const WorkItem& w) {
+  PItem p;
+  p.h = __builtin_amdgcn_readfirstlane(w.h);
+  p.q0 = __builtin_amdgcn_readfirstlane(w.q0);
+  p.qbeg = __builtin_amdgcn_readfirstlane(w.qbeg);
+  p.lq = __builtin_amdgcn_readfirstlane(w.lq);
+  p.lk = __builtin_amdgcn_readfirstlane(w.lk);
+  p.ntiles = (p.lk + 63) / 64;
+  const int kbeg = __builtin_amdgcn_readfirstlane(w.kbeg);
+  const size_t off = (size_t(kbeg) * c.H + p.h) * size_t(2 * D);
+  p.kb = uniform_ptr(c.k + off);
+  p.vb = uniform_ptr(c.v + off);
+  p.ksc = c.kscale ? uniform_ptr(c.kscale + size_t(kbeg) * c.H + p.h) : nullptr;
+  return p;
+}
+
+// Rows [32*wave, 32*wave + 32) of an item with no keys: the output is zero.
+template <int D>
+__device__ __forceinline__ void write_zero_rows(const PPCtx& c, const PItem& it, int wave, int lane) {
+  const int qrow = it.q0 + 32 * wave + (lane & 31);
+  if (qrow >= it.lq) return;
+  __bf16* orow = c.out + (size_t(it.qbeg + qrow) * c.H + it.h) * D + (D / 2) * (lane >> 5);
+  bf16x8 z;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) z[j] = (__bf16)0.0f;
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) *reinterpret_cast<bf16x8*>(orow + 8 * c) = z;
+}
+
+// Move to the next tile of the stream; items without keys are skipped (their
+// rows of this wave are written as zeros on the way).
+template <int D>
+__device__ __forceinline__ void advance(const PPCtx& c, Cur& cur, int wave, int lane) {
+  if (!cur.valid) return;
+  if (++cur.t < cur.it.ntiles) return;
+  cur.t = 0;
+  while (true) {
+    ++cur.k;
+    if (cur.k >= c.n) {
+      cur.valid = false;
+      return;
+    }
+    cur.it = make_pitem<D>(c, load_record(c, cur.k));
+    if (cur.it.ntiles > 0) return;
+    write_zero_rows<D>(c, cur.it, wave, lane);
+  }
+}
+
+template <int D, int ACT>
+__global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
+  using K = PP<D, ACT>;
+  constexpr int kQChunks = K::kQChunks, kOTiles = K::kOTiles, kRowBytes = K::kRowBytes;
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[K::kRing * K::kStageBytes];
+  __shared__ WorkItem cache[kPPItemCache];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+  const bool late = wave >= 4;  // VALU phase before the MFMA phase
+
+  // Items [xcd_begin[x], xcd_begin[x+1]) belong to XCD x = blockIdx.x % 8.
+  const int n_all = a.hdr->n_items;
+  const int x = blockIdx.x % kXcds;
+  const int beg = min(a.hdr->xcd_begin[x], n_all);
+  const int end = min(max(a.hdr->xcd_begin[x + 1], beg), n_all);
+  PPCtx c;
+  c.items = a.items;
+  c.cache = (lds_i32x4*)(cache);
+  c.k = reinterpret_cast<const unsigned char*>(a.k);
+  c.v = reinterpret_cast<const unsigned char*>(a.v);
+  c.kscale = a.kscale;
+  c.out = reinterpret_cast<__bf16*>(a.out);
+  c.H = a.H;
+  c.stride = gridDim.x / kXcds;
+  c.first = beg + int(blockIdx.x) / kXcds;
+  c.n = c.first < end ? (end - c.first + c.stride - 1) / c.stride : 0;
+  c.row_bytes = 2u * unsigned(a.H) * D;
+  if (c.n == 0) return;
+  for (int k = tid; k < min(c.n, kPPItemCache); k += K::kNT) cache[k] = a.items[c.first + k * c.stride];
+  __syncthreads();
+
+  // Stream cursors: tile s (scores), s+1, s+2 (being loaded).
+  Cur c0;
+  c0.k = -1;
+  c0.t = 0;
+  c0.valid = true;
+  c0.it.ntiles = 0;
+  advance<D>(c, c0, wave, lane);
+  if (!c0.valid) return;
+  Cur c1 = c0, c2;
+  advance<D>(c, c1, wave, lane);
+  c2 = c1;
+  advance<D>(c, c2, wave, lane);
+
+  // Loads of tile `cu` into ring stage `st` (a cursor past the end loads the
+  // stand-in tile `sb`, which is never read).  Job j moves 1 KB segment
+  // wave + 8j of K|V; rows of a ragged tile are clamped to its last key.
+  auto tile_job = [&](const Cur& cu, const Cur& sb, int st, int j) __attribute__((always_inline)) {
+    // (fields selected by value: a reference to either cursor would put both on the stack)
+    const bool ok = cu.valid;
+    const int key0 = 64 * (ok ? cu.t : sb.t);
+    const int lim = min(63, (ok ? cu.it.lk : sb.it.lk) - 1 - key0);
+    const int sg = wave + kPPWaves * j;
+    const bool is_v = sg >= K::kSegsLd;
+    const int seg = is_v ? sg - K::kSegsLd : sg;
+    const unsigned char* kb = ok ? cu.it.kb : sb.it.kb;
+    const unsigned char* vb = ok ? cu.it.vb : sb.it.vb;
+    const unsigned char* tile = (is_v ? vb : kb) + size_t(key0) * c.row_bytes;
+    const int row = seg * K::kRowsPerSeg + lane / K::kChunksPerRow;
+    const int phys = lane % K::kChunksPerRow;
+    const int ch = phys ^ (is_v ? swz_v<D>(row) : swz_k<D>(row));
+    const unsigned off = __umul24(unsigned(min(row, lim)), c.row_bytes) + 16u * unsigned(ch);
+    lds_dma16(tile, off, lds_addr_of(ring) + st * K::kStageBytes + (is_v ? K::kTileBytes : 0) + seg * 1024);
+  };
+  auto tile_scales = [&](const Cur& cu, const Cur& sb, int st) __attribute__((always_inline)) {
+    if constexpr (ACT == ACT_GELU) {
+      const bool ok = cu.valid;
+      const int key0 = 64 * (ok ? cu.t : sb.t);
+      const unsigned r = unsigned(min(lane, (ok ? cu.it.lk : sb.it.lk) - 1 - key0));
+      lds_dma4((ok ? cu.it.ksc : sb.it.ksc) + size_t(key0) * a.H, r * unsigned(a.H) * 4u,
+               lds_addr_of(ring) + st * K::kStageBytes + K::kKsOff);
+    }
+  };
+
+  // Lane-constant LDS byte offsets of the MFMA operand reads.
+  const int kp = key_perm(l32);
+  int k_off[kQChunks];
+#pragma unroll
+  for (int cc = 0; cc < kQChunks; ++cc) k_off[cc] = kp * kRowBytes + 16 * ((kQChunks * g + cc) ^ swz_k<D>(kp));
+  const int v_row = (8 * g + ((lane & 15) >> 2)) * kRowBytes;
+  int v_col[kOTiles];
+#pragma unroll
+  for (int t = 0; t < kOTiles; ++t) {
+    const int col = dim_perm<D>(t, 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+    v_col[t] = 16 * ((col >> 3) ^ swz_v<D>((lane & 15) >> 2)) + 8 * ((col & 7) >> 2);
+  }
+  const float c2s = a.score_scale;  // softmax: log2(e)/sqrt(D); GELU: 1/sqrt(D)
+  const float lazy_thr = kLazyLog2 / c2s;
+
+  // Q fragments of the scores' item: lane holds dims [(D/2)g, (D/2)g + D/2) of
+  // query row q0 + 32*wave + l32 (rows past the sample load its last row).
+  bf16x8 qf[kQChunks];
+  auto load_q = [&](const PItem& it) __attribute__((always_inline)) {
+    const int qrow = min(it.q0 + 32 * wave + l32, it.lq - 1);
+    const __bf16* src = reinterpret_cast<const __bf16*>(a.q) + (size_t(it.qbeg + qrow) * a.H + it.h) * D + (D / 2) * g;
+#pragma unroll
+    for (int cc = 0; cc < kQChunks; ++cc) qf[cc] = *reinterpret_cast<const bf16x8*>(src + 8 * cc);
+  };
+  float rq = 1.f;  // GELU: RMS factor of the query row times 1/sqrt(D)
+  auto q_rms = [&]() __attribute__((always_inline)) {
+    if constexpr (ACT == ACT_GELU) {
+      float ss = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < kQChunks; ++cc)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ss = fmaf(float(qf[cc][j]), float(qf[cc][j]), ss);
+      ss += other_half(ss);
+      rq = __builtin_amdgcn_rsqf(ss * (1.0f / D) + a.eps) * c2s;
+    }
+  };
+
+  // Prologue: tiles 0 and 1 in flight, Q of the first item.
+#pragma unroll
+  for (int j = 0; j < K::kDmaJobs; ++j) tile_job(c0, c0, 0, j);
+  tile_scales(c0, c0, 0);
+#pragma unroll
+  for (int j = 0; j < K::kDmaJobs; ++j) tile_job(c1, c0, 1, j);
+  tile_scales(c1, c0, 1);
+  load_q(c0.it);
+  wait_vmcnt(0);  // (nothing may be pending on the loop's entry edge, see below)
+  bool q_fresh = true;  // Q was (re)loaded for c0's item: GELU needs its RMS factor
+
+  f32x16 o[kOTiles];
+#pragma unroll
+  for (int t = 0; t < kOTiles; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
+  float m = -__builtin_huge_valf(), l = 0.f;
+  f32x16 sc[2];      // score tile: S^T halves (keys 32*st + 16*(i/8) + 8g + i%8)
+  bf16x8 pb[4];      // P of the previous tile, 16-key chunks kc
+  PItem ipv = c0.it;  // item of tile s-1
+  bool pv_last = false;
+  int pv_nvalid = 64;  // keys of tile s-1 inside its sample
+
+  // Softmax / GELU of the score tile `sc` (nvalid keys), written to pb as bf16.
+  auto vphase = [&](int nvalid, int stage) __attribute__((always_inline)) {
+    const bool ragged = nvalid < 64;
+    if constexpr (ACT == ACT_SOFTMAX) {
+      if (ragged) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int kk = 32 * st + 16 * (i >> 3) + 8 * g + (i & 7);
+            if (kk >= nvalid) sc[st][i] = -__builtin_huge_valf();
+          }
+      }
+      float mt = -__builtin_huge_valf();
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sc[st][i]);
+      mt = fmaxf(mt, other_half(mt));
+      // lazy rescale: the reference max moves only when a row grows by more
+      // than 2^kLazyLog2 (base 2); softmax is unchanged by the reference.
+      if (__any(mt - m > lazy_thr)) {
+        const float m_new = fmaxf(m, mt);
+        const float alpha = m == -__builtin_huge_valf() ? 0.f : fast_exp2((m - m_new) * c2s);
+        l *= alpha;
+#pragma unroll
+        for (int t = 0; t < kOTiles; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
+        m = m_new;
+      }
+      const float mc = m * c2s;
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float p = fast_exp2(fmaf(sc[kc >> 1][8 * (kc & 1) + j], c2s, -mc));
+          l += p;
+          pb[kc][j] = (__bf16)p;
+        }
+    } else {
+      const float* ksl = reinterpret_cast<const float*>(ring + stage * K::kStageBytes + K::kKsOff);
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int kk = 32 * (kc >> 1) + 16 * ((kc & 1)) + 8 * g + j;
+          const float gl = gelu_tanh(sc[kc >> 1][8 * (kc & 1) + j] * rq * ksl[kk]);
+          pb[kc][j] = (__bf16)((!ragged || kk < nvalid) ? gl : 0.f);
+        }
+    }
+  };
+
+  // Output rows of item `it`: O / l (softmax) or O / Lk (GELU), then reset.
+  auto epilogue = [&](const PItem& it) __attribute__((always_inline)) {
+    const int qrow = it.q0 + 32 * wave + l32;
+    float scale;
+    if constexpr (ACT == ACT_SOFTMAX) {
+      const float l_tot = l + other_half(l);
+      scale = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    } else {
+      scale = 1.0f / float(it.lk);
+    }
+    if (qrow < it.lq) {
+      __bf16* orow = reinterpret_cast<__bf16*>(a.out) + (size_t(it.qbeg + qrow) * a.H + it.h) * D + (D / 2) * g;
+#pragma unroll
+      for (int t = 0; t < kOTiles; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; i += 8) {
+          bf16x8 ov;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) ov[j] = (__bf16)(o[t][i + j] * scale);
+          *reinterpret_cast<bf16x8*>(orow + 16 * t + i) = ov;
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < kOTiles; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
+    m = -__builtin_huge_valf();
+    l = 0.f;
+  };
+
+  for (int s = 0;; ++s) {
+    // Tile s has landed once only the loads of tile s+1 can still be pending.
+    wait_vmcnt(K::kVmemPerTile);
+    lds_barrier();
+    const int st_s = s % K::kRing, st_prev = (s + K::kRing - 1) % K::kRing, st_pf = (s + 2) % K::kRing;
+
+    // ---- late waves' VALU phase, then O += V_{s-1} P_{s-1} (and the output
+    // of an item whose last tile was s-1).
+    auto head = [&]() __attribute__((always_inline)) {
+      if (late && s > 0) vphase(pv_nvalid, st_prev);
+      if (s > 0) {
+        // 4*kOTiles MFMAs (16-key chunk kc, output tile t), the V^T operand
+        // read kAhead MFMAs early: one wave issues them alone, so the LDS
+        // transpose-read latency is not hidden by a second wave.
+        const unsigned char* vs = ring + st_prev * K::kStageBytes + K::kTileBytes;
+        auto vread = [&](int i) __attribute__((always_inline)) {
+          const int kc = i / kOTiles, t = i % kOTiles;
+          const unsigned char* p0 = vs + v_row + kc * 16 * kRowBytes + v_col[t];
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 4 * kRowBytes));
+          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+          u32x4 w;
+          w[0] = lo2[0];
+          w[1] = lo2[1];
+          w[2] = hi2[0];
+          w[3] = hi2[1];
+          return __builtin_bit_cast(bf16x8, w);
+        };
+        constexpr int kN = 4 * kOTiles, kAhead = 3;
+        bf16x8 vop[kAhead];
+#pragma unroll
+        for (int i = 0; i < kAhead; ++i) vop[i] = vread(i);
+#pragma unroll
+        for (int i = 0; i < kN; ++i) {
+          const bf16x8 op = vop[i % kAhead];
+          if (i + kAhead < kN) vop[i % kAhead] = vread(i + kAhead);
+          o[i % kOTiles] = mfma_32x32x16(op, pb[i / kOTiles], o[i % kOTiles]);
+        }
+        // keep the reads kAhead MFMAs early (the scheduler would sink them)
+        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2 * kAhead, 0);
+#pragma unroll
+        for (int i = 0; i < kN; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+          if (i + kAhead < kN) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+        }
+        if (pv_last) epilogue(ipv);
+      }
+    };
+    // A new item starts with tile s: its Q is loaded and waited for here, in
+    // one branch (once per item).  A load that may still be pending where
+    // branches meet would make the compiler wait for all later loads -- the
+    // tile loads it does not know about -- at every step's scores.
+    if (s > 0 && c0.valid && c0.t == 0) {
+      load_q(c0.it);
+      wait_vmcnt(0);
+      q_fresh = true;
+    }
+    head();
+    if (!c0.valid) break;
+    if (q_fresh) {
+      q_rms();
+      q_fresh = false;
+    }
+    {
+      const unsigned char* ks = ring + st_s * K::kStageBytes;
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[st][i] = 0.f;
+      // first half: every Q fragment is consumed (the compiler's waits for
+      // the Q loads do not count the direct loads issued after it)
+      constexpr int kAhead = kQChunks < 3 ? kQChunks : 3;
+      bf16x8 kop[kAhead];
+#pragma unroll
+      for (int i = 0; i < kAhead; ++i) kop[i] = *reinterpret_cast<const bf16x8*>(ks + k_off[i]);
+#pragma unroll
+      for (int cc = 0; cc < kQChunks; ++cc) {
+        const bf16x8 op = kop[cc % kAhead];
+        if (cc + kAhead < kQChunks) kop[cc % kAhead] = *reinterpret_cast<const bf16x8*>(ks + k_off[cc + kAhead]);
+        sc[0] = mfma_32x32x16(op, qf[cc], sc[0]);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSgDsRead, kAhead, 1);
+#pragma unroll
+      for (int cc = 0; cc < kQChunks; ++cc) {
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 1);
+        if (cc + kAhead < kQChunks) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 1);
+      }
+      // second half, with the loads of tile s+2 between the MFMAs; the K
+      // operand is read one MFMA ahead (LDS reads are not moved across asm)
+      bf16x8 knext = *reinterpret_cast<const bf16x8*>(ks + 32 * kRowBytes + k_off[0]);
+#pragma unroll
+      for (int cc = 0; cc < kQChunks; ++cc) {
+        const bf16x8 kf = knext;
+        if (cc + 1 < kQChunks) knext = *reinterpret_cast<const bf16x8*>(ks + 32 * kRowBytes + k_off[cc + 1]);
+        sc[1] = mfma_32x32x16(kf, qf[cc], sc[1]);
+        constexpr int kPer = kQChunks / K::kDmaJobs;
+        if (cc % kPer == kPer - 1) tile_job(c2, c0, st_pf, cc / kPer);
+      }
+      tile_scales(c2, c0, st_pf);
+    }
+    const bool s_last = c0.t == c0.it.ntiles - 1;
+    const int nvalid = min(64, c0.it.lk - 64 * c0.t);
+    if (!late) vphase(nvalid, st_s);
+    ipv = c0.it;
+    pv_last = s_last;
+    pv_nvalid = nvalid;
+    c0 = c1;
+    c1 = c2;
+    advance<D>(c, c2, wave, lane);
+  }
+}
+
+}  // namespace
+
+int pp_rows() { return kPPRows; }
+
+hipError_t launch_attn_pp(int D, int act, const AttnArgs& a, int num_cu, int64_t max_items, hipStream_t st) {
+  // One workgroup per CU (the tile ring takes most of the LDS), a multiple of the XCD count.
+  int64_t grid = num_cu;
+  const int64_t need = ((max_items + kXcds - 1) / kXcds) * kXcds;
+  if (grid > need) grid = need;
+  grid = (grid / kXcds) * kXcds;
+  if (grid < kXcds) grid = kXcds;
+  const dim3 gd(static_cast<unsigned>(grid)), bd(64 * kPPWaves);
+  if (act == ACT_SOFTMAX) {
+    if (D == 32) hipLaunchKernelGGL((attn_pp_kernel<32, ACT_SOFTMAX>), gd, bd, 0, st, a);
+    else if (D == 64) hipLaunchKernelGGL((attn_pp_kernel<64, ACT_SOFTMAX>), gd, bd, 0, st, a);
+    else hipLaunchKernelGGL((attn_pp_kernel<128, ACT_SOFTMAX>), gd, bd, 0, st, a);
+  } else {
+    if (D == 32) hipLaunchKernelGGL((attn_pp_kernel<32, ACT_GELU>), gd, bd, 0, st, a);
+    else if (D == 64) hipLaunchKernelGGL((attn_pp_kernel<64, ACT_GELU>), gd, bd, 0, st, a);
+    else hipLaunchKernelGGL((attn_pp_kernel<128, ACT_GELU>), gd, bd, 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ja
+
+namespace ja {
+namespace {
+
+// RMS factor (mean over D of k^2 + eps)^(-1/2) of every (key row, head): the
+// QK-RMSNorm of the keys as a per-key scale (techfeed.io GDPA section: Q and
+// K are RMS-normalised before the GELU scores).  One thread per row.
+template <int D>
+__global__ __launch_bounds__(256) void key_rms_kernel(const __bf16* k, int64_t rows, float eps, float* out) {
+  const int64_t r = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (r >= rows) return;
+  const bf16x8* p = reinterpret_cast<const bf16x8*>(k + r * D);
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < D / 8; ++c) {
+    const bf16x8 x = p[c];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ss = fmaf(float(x[j]), float(x[j]), ss);
+  }
+  out[r] = __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
+}
+
+}  // namespace
+
+hipError_t launch_key_rms(int D, const void* k, int64_t rows, float eps, float* out, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  const dim3 gd(unsigned((rows + 255) / 256)), bd(256);
+  const __bf16* kp = reinterpret_cast<const __bf16*>(k);
+  if (D == 32) hipLaunchKernelGGL((key_rms_kernel<32>), gd, bd, 0, st, kp, rows, eps, out);
+  else if (D == 64) hipLaunchKernelGGL((key_rms_kernel<64>), gd, bd, 0, st, kp, rows, eps, out);
+  else hipLaunchKernelGGL((key_rms_kernel<128>), gd, bd, 0, st, kp, rows, eps, out);
+  return hipGetLastError();
+}
+
+}  // namespace ja

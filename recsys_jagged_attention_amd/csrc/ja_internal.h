@@ -26,6 +26,7 @@ enum In { IN_F32 = 0, IN_BF16 = 1, IN_MX = 2, IN_MX8 = 3 };
 //   sample_pbase[B]     first partial slot of the sample
 //   items[max_items]    WorkItem
 //   part_o[max_slots][32][D] float, part_ml[max_slots][32] float2
+//   kscale[total_kv][H] float     RMS factor of every key row (ping-pong GELU only)
 // ---------------------------------------------------------------------------
 constexpr int kXcds = 8;           // workgroup w runs on XCD w % 8 (round-robin dispatch)
 
@@ -47,7 +48,7 @@ struct WorkItem {
 };
 
 struct WsLayout {
-  size_t nsplit_off, pbase_off, items_off, part_o_off, part_ml_off, total;
+  size_t nsplit_off, pbase_off, items_off, part_o_off, part_ml_off, kscale_off, total;
   int64_t max_items, max_slots;
 };
 
@@ -67,7 +68,6 @@ struct PlanArgs {
   int32_t total_q, total_kv;
   int bm, kvc, self_check;
   int window_blocks;   // 0 = no window (used for the per-item cost estimate)
-  int64_t kv_row_bytes;  // >0: a sample's K/V span (Lk * row bytes) must stay below 4 GiB
   int64_t max_items, max_slots;
   WsHeader* hdr;
   int32_t* nsplit;
@@ -91,6 +91,7 @@ struct AttnArgs {
   const int32_t* pbase;
   float* part_o;
   float2* part_ml;
+  const float* kscale;  // RMS factor per key row and head (ping-pong GELU), else null
   int H;
   int window_blocks;  // 0 = no window
   int kvc;

@@ -86,13 +86,12 @@ __device__ inline void fail(const PlanArgs& a, int status) {
 }  // namespace
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
-  __shared__ int s_bad, s_big;
+  __shared__ int s_bad;
   __shared__ int s_iwarp[3 * kPlanWaves];
   __shared__ double s_dwarp[3 * kPlanWaves];
   const int tid = threadIdx.x;
   if (tid == 0) {
     s_bad = 0;
-    s_big = 0;
   }
   __syncthreads();
 
@@ -110,7 +109,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     if (b < a.B) {
       const int q1 = a.qo[b + 1], k1 = a.ko[b + 1];
       if (q1 < q || k1 < k) bad = 1;
-      if (a.kv_row_bytes > 0 && int64_t(k1 - k) * a.kv_row_bytes >= (int64_t(1) << 32)) atomicOr(&s_big, 1);
       const SampleWork w = sample_work(a, q1 - q, k1 - k);
       my_items += w.cnt;
       my_slots += w.slots;
@@ -131,10 +129,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   }
   if (s_bad || total_items_ll > a.max_items || total_slots_ll > a.max_slots) {
     if (tid == 0) fail(a, JA_EOFFSETS);
-    return;
-  }
-  if (s_big) {
-    if (tid == 0) fail(a, JA_EUNSUPPORTED);
     return;
   }
 

@@ -140,6 +140,22 @@ def test_mxfp8_block_scales_far_apart(act):
     full_parity(w)
 
 
+@pytest.mark.parametrize("act", ["softmax", "gelu_tanh"])
+def test_many_items_per_workgroup(act):
+    """About 80k short cross-attention items: every workgroup of the tile-stream
+    kernel walks more items than it stages in LDS (the rest are read from the
+    workspace), with samples of 1 to 9 queries, 0 to 16 keys (empty ones
+    included) and 80 heads."""
+    rng = np.random.Generator(np.random.PCG64(77))
+    B = 1024
+    lq = rng.integers(1, 10, size=B)
+    lk = rng.integers(0, 17, size=B)
+    w = adhoc("many_items", "cross", act, "bf16", lq.tolist(), lk.tolist(), 80, 32, seed=78)
+    log(f"many items {act}: B={B} H=80 Nq={w.total_q} Nk={w.total_kv}")
+    out = run_gpu(w)
+    sampled_parity(w, out, n=160)
+
+
 def test_single_key_gives_value_row():
     w = adhoc("one_key", "pma", "softmax", "bf16", [32, 32], [1, 1], 2, 64, seed=9)
     got = run_gpu(w)
