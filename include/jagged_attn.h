@@ -68,7 +68,11 @@ enum ja_variant {
 
 enum ja_act {
   JA_SOFTMAX = 0,   /* softmax over the allowed keys                         */
-  JA_GELU_TANH = 1  /* QK-RMSNorm, gelu_tanh score, 1/Lk normalisation        */
+  JA_GELU_TANH = 1, /* QK-RMSNorm, gelu_tanh score, 1/Lk normalisation        */
+  JA_GELU_POLY = 2  /* as JA_GELU_TANH with tanh replaced by an ALU-only
+                       polynomial (GDPA section: the ALU GELU; here a fitted
+                       even polynomial on |x| < 4, x or 0 outside; max error
+                       of the activation about 2e-4)                          */
 };
 
 enum ja_dtype { JA_F32 = 0, JA_BF16 = 1, JA_MXFP8_E4M3 = 2 };
@@ -94,7 +98,7 @@ typedef struct ja_io {
   void *stream;              /* hipStream_t to launch on; NULL = null stream    */
   int32_t total_q;           /* rows of q/out  (= q_offsets[B])                 */
   int32_t total_kv;          /* rows of k/v    (= kv_offsets[B])                */
-  float rms_eps;             /* JA_GELU_TANH: RMSNorm epsilon; <= 0 -> 1e-6     */
+  float rms_eps;             /* GELU acts: RMSNorm epsilon; <= 0 -> 1e-6        */
   void *ev_start;            /* optional profiling hipEvent_t pair (or NULL):   */
   void *ev_stop;             /* recorded on `stream` right before and right     */
                              /* after the attention kernel (not the plan or the */

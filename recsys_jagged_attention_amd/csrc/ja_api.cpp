@@ -61,7 +61,7 @@ int validate(int B, int H, int D, int variant, int act, int window, int dtype, i
              int32_t total_kv) {
   if (B < 1 || H < 1 || total_q < 0 || total_kv < 0) return JA_EINVAL;
   if (variant < JA_SELF || variant > JA_PMA) return JA_EINVAL;
-  if (act < JA_SOFTMAX || act > JA_GELU_TANH) return JA_EINVAL;
+  if (act < JA_SOFTMAX || act > JA_GELU_POLY) return JA_EINVAL;
   if (dtype < JA_F32 || dtype > JA_MXFP8_E4M3) return JA_EINVAL;
   if (window < 0) return JA_EINVAL;
   if (variant == JA_SELF && total_q != total_kv) return JA_EINVAL;
@@ -114,7 +114,7 @@ Plan make_plan(int B, int H, int D, int variant, int act, int window, int dtype,
   w.part_ml_off = off;
   off = align256(off + sizeof(float2) * size_t(w.max_slots) * kPmaRows);
   w.kscale_off = off;
-  if (p.shape == kShapePingPong && act == JA_GELU_TANH) off = align256(off + sizeof(float) * size_t(total_kv) * H);
+  if (p.shape == kShapePingPong && act != JA_SOFTMAX) off = align256(off + sizeof(float) * size_t(total_kv) * H);
   w.total = off;
   return p;
 }
@@ -209,7 +209,7 @@ int jagged_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
   aa.kvc = p.kvc;
   aa.eps = io->rms_eps > 0.f ? io->rms_eps : 1e-6f;
   aa.kscale = nullptr;
-  if (p.shape == kShapePingPong && act == JA_GELU_TANH) {
+  if (p.shape == kShapePingPong && act != JA_SOFTMAX) {
     float* ksc = reinterpret_cast<float*>(ws + p.ws.kscale_off);
     if (launch_key_rms(D, k, int64_t(io->total_kv) * H, aa.eps, ksc, stream) != hipSuccess) return JA_EHIP;
     aa.kscale = ksc;

@@ -41,7 +41,7 @@ __global__ __launch_bounds__(kF32Rows) void attn_f32_kernel(AttnArgs a) {
       o[d] = 0.f;
     }
     float rq = 1.f;
-    if constexpr (ACT == ACT_GELU) {
+    if constexpr (ACT != ACT_SOFTMAX) {
       float ss = 0.f;
 #pragma unroll
       for (int d = 0; d < D; ++d) ss = fmaf(q[d], q[d], ss);
@@ -78,8 +78,12 @@ __global__ __launch_bounds__(kF32Rows) void attn_f32_kernel(AttnArgs a) {
         for (int d = 0; d < D; ++d) ss = fmaf(kp[d], kp[d], ss);
         const float rk = 1.0f / sqrtf(ss * (1.0f / D) + a.eps);
         const float x = s * rq * rk * a.score_scale;
-        constexpr float kC = 0.7978845608028654f;
-        p = 0.5f * x * (1.0f + tanhf(kC * fmaf(0.044715f * x, x * x, x)));
+        if constexpr (ACT == ACT_GELU_POLY) {
+          p = gelu_poly(x);
+        } else {
+          constexpr float kC = 0.7978845608028654f;
+          p = 0.5f * x * (1.0f + tanhf(kC * fmaf(0.044715f * x, x * x, x)));
+        }
       }
 #pragma unroll
       for (int d = 0; d < D; ++d) o[d] = fmaf(p, vp[d], o[d]);
@@ -97,6 +101,8 @@ template <int D>
 hipError_t launch_d(int act, bool window, const AttnArgs& a, int grid, hipStream_t st) {
   if (act == ACT_GELU)
     hipLaunchKernelGGL((attn_f32_kernel<D, ACT_GELU, false>), dim3(grid), dim3(kF32Rows), 0, st, a);
+  else if (act == ACT_GELU_POLY)
+    hipLaunchKernelGGL((attn_f32_kernel<D, ACT_GELU_POLY, false>), dim3(grid), dim3(kF32Rows), 0, st, a);
   else if (window)
     hipLaunchKernelGGL((attn_f32_kernel<D, ACT_SOFTMAX, true>), dim3(grid), dim3(kF32Rows), 0, st, a);
   else

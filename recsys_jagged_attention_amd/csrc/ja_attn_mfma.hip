@@ -332,7 +332,7 @@ __global__ __launch_bounds__(64 * NWQ * NWK, QSUB == 2 ? 1 : 2) void attn_kernel
   constexpr int kQChunks = K::kQChunks, kOTiles = K::kOTiles, kRowBytes = K::kRowBytes;
   constexpr int kTileBytes = K::kTileBytes;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages * kStageBytes];
-  __shared__ float kscale_all[ACT == ACT_GELU ? kStages * NWK * 64 : 1];
+  __shared__ float kscale_all[ACT != ACT_SOFTMAX ? kStages * NWK * 64 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wq = wave % NWQ, wk = wave / NWQ;
@@ -407,7 +407,7 @@ __global__ __launch_bounds__(64 * NWQ * NWK, QSUB == 2 ? 1 : 2) void attn_kernel
             qc[qs][c][4 + i] = int(w1[i]);
           }
           qsc[qs][c] = g ? sb1 : sb0;
-          if constexpr (ACT == ACT_GELU) {
+          if constexpr (ACT != ACT_SOFTMAX) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
               const float sc = e8m0_to_float(unsigned(i < 4 ? sb0 : sb1));
@@ -420,7 +420,7 @@ __global__ __launch_bounds__(64 * NWQ * NWK, QSUB == 2 ? 1 : 2) void attn_kernel
             }
           }
         }
-        if constexpr (ACT == ACT_GELU) {
+        if constexpr (ACT != ACT_SOFTMAX) {
           ss += other_half(ss);
           rq[qs] = __builtin_amdgcn_rsqf(ss * (1.0f / D) + a.eps) * c2;
         } else {
@@ -439,7 +439,7 @@ __global__ __launch_bounds__(64 * NWQ * NWK, QSUB == 2 ? 1 : 2) void attn_kernel
         }
       }
       rq[qs] = 1.0f;
-      if constexpr (ACT == ACT_GELU) {
+      if constexpr (ACT != ACT_SOFTMAX) {
         float ss = 0.f;
 #pragma unroll
         for (int c = 0; c < kQChunks; ++c)
@@ -491,12 +491,12 @@ __global__ __launch_bounds__(64 * NWQ * NWK, QSUB == 2 ? 1 : 2) void attn_kernel
       wait_vmcnt(0);
       lds_barrier();
       unsigned char* st_base = smem + stage * kStageBytes;
-      float* kscale_st = kscale_all + (ACT == ACT_GELU ? stage * NWK * 64 : 0);
-      if constexpr (ACT == ACT_GELU || IN == IN_MX8) {
+      float* kscale_st = kscale_all + (ACT != ACT_SOFTMAX ? stage * NWK * 64 : 0);
+      if constexpr (ACT != ACT_SOFTMAX || IN == IN_MX8) {
 #pragma unroll
         for (int kg = 0; kg < NWK; ++kg)
           if (t0 + kg < cur.ntiles) {
-            if constexpr (ACT == ACT_GELU) K::key_scales(a.eps, st_base + kg * K::kGroupBytes, kscale_st + kg * 64);
+            if constexpr (ACT != ACT_SOFTMAX) K::key_scales(a.eps, st_base + kg * K::kGroupBytes, kscale_st + kg * 64);
             if constexpr (IN == IN_MX8) K::convert_v(st_base + kg * K::kGroupBytes);
           }
         lds_barrier();
@@ -642,7 +642,7 @@ __global__ __launch_bounds__(64 * NWQ * NWK, QSUB == 2 ? 1 : 2) void attn_kernel
 #pragma unroll
               for (int i = 0; i < 16; ++i) {
                 const int kk = 32 * st + 16 * (i >> 3) + 8 * g + (i & 7);
-                const float gl = gelu_tanh(s[qs][st][i] * rq[qs] * kscale[kk]);
+                const float gl = gelu_act<ACT>(s[qs][st][i] * rq[qs] * kscale[kk]);
                 s[qs][st][i] = (!ragged || kk < nvalid) ? gl : 0.f;
               }
           }
@@ -856,15 +856,17 @@ hipError_t launch_for_shape(int shape, int act, const AttnArgs& a, int num_cu, i
                             hipStream_t st) {
   switch (shape) {
     case 0:  // query-tiled (self full, cross): 4 waves x 32 rows
-      return act == ACT_SOFTMAX ? launch<D, 4, 1, 1, ACT_SOFTMAX, IN, false, false>(a, num_cu, max_items, st)
-                                : launch<D, 4, 1, 1, ACT_GELU, IN, false, false>(a, num_cu, max_items, st);
+      if (act == ACT_SOFTMAX) return launch<D, 4, 1, 1, ACT_SOFTMAX, IN, false, false>(a, num_cu, max_items, st);
+      if (act == ACT_GELU_POLY) return launch<D, 4, 1, 1, ACT_GELU_POLY, IN, false, false>(a, num_cu, max_items, st);
+      return launch<D, 4, 1, 1, ACT_GELU, IN, false, false>(a, num_cu, max_items, st);
     case 1:  // block window (softmax only): 4 waves x 32 rows on two 64-token query blocks
       return launch<D, 4, 1, 1, ACT_SOFTMAX, IN, true, false>(a, num_cu, max_items, st);
     case 3:  // full self-attention: 8 waves x 32 rows share every key tile
       return launch<D, 8, 1, 1, ACT_SOFTMAX, IN, false, false>(a, num_cu, max_items, st);
     default:  // key-split (PMA): 1 query group of 32 rows x 4 key groups
-      return act == ACT_SOFTMAX ? launch<D, 1, 4, 1, ACT_SOFTMAX, IN, false, true>(a, num_cu, max_items, st)
-                                : launch<D, 1, 4, 1, ACT_GELU, IN, false, true>(a, num_cu, max_items, st);
+      if (act == ACT_SOFTMAX) return launch<D, 1, 4, 1, ACT_SOFTMAX, IN, false, true>(a, num_cu, max_items, st);
+      if (act == ACT_GELU_POLY) return launch<D, 1, 4, 1, ACT_GELU_POLY, IN, false, true>(a, num_cu, max_items, st);
+      return launch<D, 1, 4, 1, ACT_GELU, IN, false, true>(a, num_cu, max_items, st);
   }
 }
 

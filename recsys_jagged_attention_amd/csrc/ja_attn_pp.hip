@@ -40,7 +40,7 @@ struct PP {
   static constexpr int kRowBytes = 2 * D;
   static constexpr int kTileBytes = 64 * kRowBytes;
   static constexpr int kKsOff = 2 * kTileBytes;  // GELU: 64 fp32 key scales after K and V
-  static constexpr int kStageBytes = 2 * kTileBytes + (ACT == ACT_GELU ? 256 : 0);
+  static constexpr int kStageBytes = 2 * kTileBytes + (ACT != ACT_SOFTMAX ? 256 : 0);
   static constexpr int kRing = 4;
   static constexpr int kQChunks = D / 16;
   static constexpr int kOTiles = D / 32;
@@ -48,7 +48,7 @@ struct PP {
   static constexpr int kRowsPerSeg = 1024 / kRowBytes;
   static constexpr int kChunksPerRow = kRowBytes / 16;
   static constexpr int kDmaJobs = 2 * kSegsLd / kPPWaves;  // 1 KB loads per wave per tile
-  static constexpr int kVmemPerTile = kDmaJobs + (ACT == ACT_GELU ? 1 : 0);
+  static constexpr int kVmemPerTile = kDmaJobs + (ACT != ACT_SOFTMAX ? 1 : 0);
   static_assert((2 * kSegsLd) % kPPWaves == 0, "tile segments must split evenly over the waves");
   static_assert(kQChunks % kDmaJobs == 0, "loads are spread evenly over the score MFMAs");
 };
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
     lds_dma16(tile, off, lds_addr_of(ring) + st * K::kStageBytes + (is_v ? K::kTileBytes : 0) + seg * 1024);
   };
   auto tile_scales = [&](const Cur& cu, const Cur& sb, int st) __attribute__((always_inline)) {
-    if constexpr (ACT == ACT_GELU) {
+    if constexpr (ACT != ACT_SOFTMAX) {
       const bool ok = cu.valid;
       const int key0 = 64 * (ok ? cu.t : sb.t);
       const unsigned r = unsigned(min(lane, (ok ? cu.it.lk : sb.it.lk) - 1 - key0));
@@ -242,7 +242,7 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
   };
   float rq = 1.f;  // GELU: RMS factor of the query row times 1/sqrt(D)
   auto q_rms = [&]() __attribute__((always_inline)) {
-    if constexpr (ACT == ACT_GELU) {
+    if constexpr (ACT != ACT_SOFTMAX) {
       float ss = 0.f;
 #pragma unroll
       for (int cc = 0; cc < kQChunks; ++cc)
@@ -323,7 +323,7 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int kk = 32 * (kc >> 1) + 16 * ((kc & 1)) + 8 * g + j;
-          const float gl = gelu_tanh(sc[kc >> 1][8 * (kc & 1) + j] * rq * ksl[kk]);
+          const float gl = gelu_act<ACT>(sc[kc >> 1][8 * (kc & 1) + j] * rq * ksl[kk]);
           pb[kc][j] = (__bf16)((!ragged || kk < nvalid) ? gl : 0.f);
         }
     }
@@ -487,6 +487,10 @@ hipError_t launch_attn_pp(int D, int act, const AttnArgs& a, int num_cu, int64_t
     if (D == 32) hipLaunchKernelGGL((attn_pp_kernel<32, ACT_SOFTMAX>), gd, bd, 0, st, a);
     else if (D == 64) hipLaunchKernelGGL((attn_pp_kernel<64, ACT_SOFTMAX>), gd, bd, 0, st, a);
     else hipLaunchKernelGGL((attn_pp_kernel<128, ACT_SOFTMAX>), gd, bd, 0, st, a);
+  } else if (act == ACT_GELU_POLY) {
+    if (D == 32) hipLaunchKernelGGL((attn_pp_kernel<32, ACT_GELU_POLY>), gd, bd, 0, st, a);
+    else if (D == 64) hipLaunchKernelGGL((attn_pp_kernel<64, ACT_GELU_POLY>), gd, bd, 0, st, a);
+    else hipLaunchKernelGGL((attn_pp_kernel<128, ACT_GELU_POLY>), gd, bd, 0, st, a);
   } else {
     if (D == 32) hipLaunchKernelGGL((attn_pp_kernel<32, ACT_GELU>), gd, bd, 0, st, a);
     else if (D == 64) hipLaunchKernelGGL((attn_pp_kernel<64, ACT_GELU>), gd, bd, 0, st, a);

@@ -1,6 +1,7 @@
 // Device helpers for the gfx950 (CDNA4) jagged attention kernels.
 #pragma once
 
+#include "ja_gelu_poly.h"
 #include "ja_internal.h"
 
 namespace ja {
@@ -52,6 +53,13 @@ __device__ __forceinline__ float gelu_tanh(float x) {
   const float u = kC * fmaf(0.044715f * x, x * x, x);
   const float e = fast_exp2(kNeg2Log2e * u);
   return x * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// The GELU of a score for the GELU-family activations.
+template <int ACT>
+__device__ __forceinline__ float gelu_act(float x) {
+  if constexpr (ACT == ACT_GELU_POLY) return gelu_poly(x);
+  else return gelu_tanh(x);
 }
 
 }  // namespace ja

@@ -14,7 +14,8 @@ constexpr int kWaveSize = 64;
 constexpr int kThreads = 256;     // threads of the split-merge kernel
 constexpr int kPmaRows = 32;      // query rows per key-split work item
 
-enum Act { ACT_SOFTMAX = 0, ACT_GELU = 1 };
+// GELU scores: tanh form (exp + rcp) or the ALU-only polynomial (ja_gelu_poly.h).
+enum Act { ACT_SOFTMAX = 0, ACT_GELU = 1, ACT_GELU_POLY = 2 };
 // IN_MX: MX-fp8 decoded to bf16 on load; IN_MX8 (D = 128): fp8 codes stay fp8
 // for block-scaled fp8 MFMA on QK^T, V is converted to bf16 in LDS.
 enum In { IN_F32 = 0, IN_BF16 = 1, IN_MX = 2, IN_MX8 = 3 };

@@ -156,6 +156,18 @@ def test_many_items_per_workgroup(act):
     sampled_parity(w, out, n=160)
 
 
+@pytest.mark.parametrize("dtype,D", [("bf16", 32), ("bf16", 64), ("bf16", 128), ("f32", 64),
+                                     ("mxfp8", 64), ("mxfp8", 128)])
+def test_gelu_poly_cross_and_pma(dtype, D):
+    """JA_GELU_POLY on every kernel family (tile stream, key split, fp32, MX),
+    against the exact tanh GELU within the activation's error bound."""
+    lq = [0, 1, 5, 128, 129, 300, 17, 64]
+    lk = [3, 0, 1, 16, 64, 65, 200, 1]
+    full_parity(adhoc("poly_cross", "cross", "gelu_poly", dtype, lq, lk, 2, D, seed=D + 31))
+    if dtype != "f32":
+        full_parity(adhoc("poly_pma", "pma", "gelu_poly", dtype, [32, 32, 7], [1, 3000, 65], 2, D, seed=D + 32))
+
+
 def test_single_key_gives_value_row():
     w = adhoc("one_key", "pma", "softmax", "bf16", [32, 32], [1, 1], 2, 64, seed=9)
     got = run_gpu(w)
