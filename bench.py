@@ -134,7 +134,8 @@ def load_traffic(kernel_tag: str, workload: str):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "recsys_jagged_attention_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        h.update(open(os.path.join(csrc, f), "rb").read())
+        if f.endswith((".hip", ".h", ".cpp", ".py")) and os.path.isfile(os.path.join(csrc, f)):
+            h.update(open(os.path.join(csrc, f), "rb").read())
     if kv.get("source_sha256") != h.hexdigest() or kv.get("kernel") != kernel_tag:
         return None
     try:
