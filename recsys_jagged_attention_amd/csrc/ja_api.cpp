@@ -180,6 +180,7 @@ int jagged_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
   pa.kvc = p.kvc;
   pa.self_check = variant == JA_SELF;
   pa.window_blocks = window / kBlock;
+  pa.cost_order = p.shape == kShapePingPong;
   pa.max_items = p.ws.max_items;
   pa.max_slots = p.ws.max_slots;
   pa.hdr = hdr;

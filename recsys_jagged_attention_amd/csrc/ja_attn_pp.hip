@@ -13,7 +13,11 @@
 // busy the other does its exponentials, with one workgroup barrier per step.
 // The stream does not stop at item boundaries: an item's Q is loaded at the
 // start of its first step and the previous item's output is written between
-// two MFMA phases.
+// two MFMA phases.  The plan sorts the items by key tiles, most first, and
+// they are dealt out in rounds that alternate direction (workgroup positions
+// 0..G-1, then G-1..0, ...), so every workgroup gets about the same number of
+// tile steps; consecutive positions lie on one XCD, so the query tiles of one
+// (sample, head) mostly share its K/V through that XCD's L2.
 //
 // LDS holds a ring of 4 tiles (K and V, plus the key scales of the GELU path):
 // in step s the waves read K_s and V_{s-1}, tile s+1 has landed and tile s+2
@@ -79,16 +83,21 @@ struct PPCtx {
   const float* kscale;
   __bf16* out;
   int H;
-  int first, stride, n;   // item k of this workgroup is first + k * stride, k < n
+  int G, pos, n;          // item k of this workgroup is item_index(k), k < n
   unsigned row_bytes;
 };
+
+// Round k deals items [kG, kG + G) to positions 0..G-1, in reverse order on odd rounds.
+__device__ __forceinline__ int item_index(const PPCtx& c, int k) {
+  return k * c.G + ((k & 1) ? c.G - 1 - c.pos : c.pos);
+}
 
 __device__ __forceinline__ WorkItem load_record(const PPCtx& c, int k) {
   if (k < kPPItemCache) {
     const i32x4v u = c.cache[2 * k], w = c.cache[2 * k + 1];
     return WorkItem{u[0], u[1], u[2], u[3], w[0], w[1], w[2], w[3]};
   }
-  return c.items[c.first + k * c.stride];
+  return c.items[item_index(c, k)];
 }
 
 template <int D>
@@ -152,11 +161,7 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
   const int l32 = lane & 31, g = lane >> 5;
   const bool late = wave >= 4;  // VALU phase before the MFMA phase
 
-  // Items [xcd_begin[x], xcd_begin[x+1]) belong to XCD x = blockIdx.x % 8.
   const int n_all = a.hdr->n_items;
-  const int x = blockIdx.x % kXcds;
-  const int beg = min(a.hdr->xcd_begin[x], n_all);
-  const int end = min(max(a.hdr->xcd_begin[x + 1], beg), n_all);
   PPCtx c;
   c.items = a.items;
   c.cache = (lds_i32x4*)(cache);
@@ -165,12 +170,17 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
   c.kscale = a.kscale;
   c.out = reinterpret_cast<__bf16*>(a.out);
   c.H = a.H;
-  c.stride = gridDim.x / kXcds;
-  c.first = beg + int(blockIdx.x) / kXcds;
-  c.n = c.first < end ? (end - c.first + c.stride - 1) / c.stride : 0;
+  // (the grid is a multiple of 8 and workgroup w runs on XCD w % 8: positions
+  // [x G/8, (x+1) G/8) are the workgroups of XCD x)
+  c.G = gridDim.x;
+  c.pos = int(blockIdx.x % kXcds) * (c.G / kXcds) + int(blockIdx.x) / kXcds;
+  {
+    const int full = n_all / c.G;  // complete rounds
+    c.n = full + (item_index(c, full) < n_all ? 1 : 0);
+  }
   c.row_bytes = 2u * unsigned(a.H) * D;
   if (c.n == 0) return;
-  for (int k = tid; k < min(c.n, kPPItemCache); k += K::kNT) cache[k] = a.items[c.first + k * c.stride];
+  for (int k = tid; k < min(c.n, kPPItemCache); k += K::kNT) cache[k] = a.items[item_index(c, k)];
   __syncthreads();
 
   // Stream cursors: tile s (scores), s+1, s+2 (being loaded).

@@ -37,6 +37,7 @@ struct WsHeader {
   int32_t n_slots;             // partial slots in use
   int32_t pad0;
   int32_t xcd_begin[kXcds + 1];  // items [xcd_begin[x], xcd_begin[x+1]) run on XCD x
+                                 // (sample order; not used with cost order)
   int32_t pad[64 - 4 - (kXcds + 1)];
 };
 
@@ -69,6 +70,7 @@ struct PlanArgs {
   int32_t total_q, total_kv;
   int bm, kvc, self_check;
   int window_blocks;   // 0 = no window (used for the per-item cost estimate)
+  int cost_order;      // 1: items sorted by key tiles, most first (xcd_begin unused)
   int64_t max_items, max_slots;
   WsHeader* hdr;
   int32_t* nsplit;

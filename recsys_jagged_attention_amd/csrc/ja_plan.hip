@@ -12,6 +12,10 @@
 //  3. cuts the item list into 8 contiguous ranges of equal estimated cost, one
 //     per XCD: an XCD's workgroups then share K/V through its own L2, and the
 //     XCDs finish together despite skewed lengths.
+// In cost order (the tile-stream kernel) step 2 instead places the items by a
+// counting sort on their key tiles, most first, so that dealing them out in
+// rounds gives every workgroup about the same number of tile steps; the items
+// of one (sample, head) stay adjacent.
 #include "ja_internal.h"
 #include "jagged_attn.h"
 
@@ -21,6 +25,9 @@ namespace {
 
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanWaves = kPlanThreads / 64;
+constexpr int kCostBuckets = kPlanThreads;  // cost order: bucket = key tiles, clamped
+
+__device__ inline int cost_bucket(int lk) { return min((lk + kBlock - 1) / kBlock, kCostBuckets - 1); }
 
 template <typename T>
 __device__ inline T wave_inclusive_scan(T x) {
@@ -89,10 +96,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ int s_bad;
   __shared__ int s_iwarp[3 * kPlanWaves];
   __shared__ double s_dwarp[3 * kPlanWaves];
+  __shared__ int s_bucket[kCostBuckets];  // cost order: item count, then next free position
   const int tid = threadIdx.x;
   if (tid == 0) {
     s_bad = 0;
   }
+  for (int i = tid; i < kCostBuckets; i += kPlanThreads) s_bucket[i] = 0;
   __syncthreads();
 
   // Pass 1: validate; total items, partial slots and estimated cost.
@@ -113,6 +122,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       my_items += w.cnt;
       my_slots += w.slots;
       my_cost += w.cnt * w.ck;
+      if (a.cost_order && w.cnt > 0) atomicAdd(&s_bucket[cost_bucket(k1 - k)], w.cnt);
     }
   }
   if (bad) atomicOr(&s_bad, 1);
@@ -130,6 +140,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   if (s_bad || total_items_ll > a.max_items || total_slots_ll > a.max_slots) {
     if (tid == 0) fail(a, JA_EOFFSETS);
     return;
+  }
+  if (a.cost_order) {
+    // first position of every bucket, the bucket with the most key tiles first
+    // (each thread reads and writes only its own bucket)
+    static_assert(kCostBuckets == kPlanThreads, "one bucket per thread");
+    const int bk = kCostBuckets - 1 - tid;
+    int unused;
+    s_bucket[bk] = block_exclusive_scan(s_bucket[bk], s_iwarp, &unused);
+    __syncthreads();
   }
 
   // Pass 2: per chunk of 1024 samples, scan and write items, splits, slot
@@ -183,8 +202,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     for (int p = tid; p < nchunk * a.H; p += kPlanThreads) {
       const int j = p / a.H, h = p - j * a.H;
       const int nq = s_nqt[j], nsj = s_ns[j];
-      int ib = s_base[j] + h * nq * nsj;
       const int qb = s_qb[j], lq = s_lq[j], kb = s_kb[j], lk = s_lk[j];
+      if (nq == 0) continue;
+      int ib = a.cost_order ? atomicAdd(&s_bucket[cost_bucket(lk)], nq * nsj) : s_base[j] + h * nq * nsj;
       for (int qt = 0; qt < nq; ++qt)
         for (int sp = 0; sp < nsj; ++sp) a.items[ib++] = WorkItem{base + j, h, qt * a.bm, sp, qb, lq, kb, lk};
     }

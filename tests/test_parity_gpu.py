@@ -156,6 +156,18 @@ def test_many_items_per_workgroup(act):
     sampled_parity(w, out, n=160)
 
 
+@pytest.mark.parametrize("act", ["softmax", "gelu_tanh"])
+def test_cost_order_long_and_skewed_keys(act):
+    """Tile-stream items are placed by a counting sort on their key tiles: key
+    lengths past the largest bucket (1023 tiles) next to short and empty ones,
+    with more items than workgroups, so rounds are dealt in both directions."""
+    lq = [100, 5, 0, 700, 64, 1, 2000, 513]
+    lk = [70000, 66000, 10, 0, 1, 4097, 129, 64]
+    w = adhoc("cost_order", "cross", act, "bf16", lq, lk, 16, 32, seed=5)
+    log(f"cost order {act}: Nq={w.total_q} Nk={w.total_kv}")
+    full_parity(w)
+
+
 @pytest.mark.parametrize("dtype,D", [("bf16", 32), ("bf16", 64), ("bf16", 128), ("f32", 64),
                                      ("mxfp8", 64), ("mxfp8", 128)])
 def test_gelu_poly_cross_and_pma(dtype, D):
