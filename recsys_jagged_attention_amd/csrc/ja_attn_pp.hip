@@ -37,6 +37,9 @@ constexpr int kPPRows = 32 * kPPWaves;  // query rows per work item
 constexpr int kPPItemCache = 256;       // work item records staged in LDS per workgroup
 // instruction classes of __builtin_amdgcn_sched_group_barrier
 constexpr int kSgMfma = 0x008, kSgDsRead = 0x100;
+// MFMA operands are read this many MFMAs before their use (LDS latency under
+// the load of four waves reading at once is several MFMAs long).
+constexpr int kPPAhead = 5;
 
 template <int D, int ACT>
 struct PP {
@@ -57,19 +60,20 @@ struct PP {
   static_assert(kQChunks % kDmaJobs == 0, "loads are spread evenly over the score MFMAs");
 };
 
-// One work item as the stream needs it (wave-uniform).
-struct PItem {
-  int h, q0, qbeg, lq, lk, ntiles;
-  const unsigned char* kb;  // key row r of the head at kb + r * row_bytes
-  const unsigned char* vb;
-  const float* ksc;         // GELU: scale of key row r at ksc[r * H]
+// Position in the tile stream: tile t of the k-th item of this workgroup
+// (k == n: past the end), and the item's key count.  Wave-uniform.
+struct Cur {
+  int k, t, lk;
 };
 
-// Position in the tile stream: tile t of the k-th item of this workgroup.
-struct Cur {
-  int k, t;
-  bool valid;
-  PItem it;
+__device__ __forceinline__ int ntiles_of(int lk) { return (lk + 63) >> 6; }
+
+// Where the tile loads of a cursor read: key row r of the item's head at
+// kb + r * row_bytes (values at vb + ...), GELU key scales at ksc[r * H].
+struct Src {
+  const unsigned char* kb;
+  const unsigned char* vb;
+  const float* ksc;
 };
 
 typedef int i32x4v __attribute__((ext_vector_type(4)));
@@ -92,34 +96,37 @@ __device__ __forceinline__ int item_index(const PPCtx& c, int k) {
   return k * c.G + ((k & 1) ? c.G - 1 - c.pos : c.pos);
 }
 
+// Record of the k-th item, wave-uniform.
 __device__ __forceinline__ WorkItem load_record(const PPCtx& c, int k) {
+  WorkItem w;
   if (k < kPPItemCache) {
-    const i32x4v u = c.cache[2 * k], w = c.cache[2 * k + 1];
-    return WorkItem{u[0], u[1], u[2], u[3], w[0], w[1], w[2], w[3]};
+    const i32x4v u = c.cache[2 * k], x = c.cache[2 * k + 1];
+    w = WorkItem{u[0], u[1], u[2], u[3], x[0], x[1], x[2], x[3]};
+  } else {
+    w = c.items[item_index(c, k)];
   }
-  return c.items[item_index(c, k)];
+  w.h = __builtin_amdgcn_readfirstlane(w.h);
+  w.q0 = __builtin_amdgcn_readfirstlane(w.q0);
+  w.qbeg = __builtin_amdgcn_readfirstlane(w.qbeg);
+  w.lq = __builtin_amdgcn_readfirstlane(w.lq);
+  w.kbeg = __builtin_amdgcn_readfirstlane(w.kbeg);
+  w.lk = __builtin_amdgcn_readfirstlane(w.lk);
+  return w;
 }
 
 template <int D>
-__device__ __forceinline__ PItem make_pitem(const PPCtx& c, const WorkItem& w) {
-  PItem p;
-  p.h = __builtin_amdgcn_readfirstlane(w.h);
-  p.q0 = __builtin_amdgcn_readfirstlane(w.q0);
-  p.qbeg = __builtin_amdgcn_readfirstlane(w.qbeg);
-  p.lq = __builtin_amdgcn_readfirstlane(w.lq);
-  p.lk = __builtin_amdgcn_readfirstlane(w.lk);
-  p.ntiles = (p.lk + 63) / 64;
-  const int kbeg = __builtin_amdgcn_readfirstlane(w.kbeg);
-  const size_t off = (size_t(kbeg) * c.H + p.h) * size_t(2 * D);
-  p.kb = uniform_ptr(c.k + off);
-  p.vb = uniform_ptr(c.v + off);
-  p.ksc = c.kscale ? uniform_ptr(c.kscale + size_t(kbeg) * c.H + p.h) : nullptr;
-  return p;
+__device__ __forceinline__ Src make_src(const PPCtx& c, const WorkItem& w) {
+  const size_t off = (size_t(w.kbeg) * c.H + w.h) * size_t(2 * D);
+  Src r;
+  r.kb = uniform_ptr(c.k + off);
+  r.vb = uniform_ptr(c.v + off);
+  r.ksc = c.kscale ? uniform_ptr(c.kscale + size_t(w.kbeg) * c.H + w.h) : nullptr;
+  return r;
 }
 
 // Rows [32*wave, 32*wave + 32) of an item with no keys: the output is zero.
 template <int D>
-__device__ __forceinline__ void write_zero_rows(const PPCtx& c, const PItem& it, int wave, int lane) {
+__device__ __forceinline__ void write_zero_rows(const PPCtx& c, const WorkItem& it, int wave, int lane) {
   const int qrow = it.q0 + 32 * wave + (lane & 31);
   if (qrow >= it.lq) return;
   __bf16* orow = c.out + (size_t(it.qbeg + qrow) * c.H + it.h) * D + (D / 2) * (lane >> 5);
@@ -130,22 +137,24 @@ __device__ __forceinline__ void write_zero_rows(const PPCtx& c, const PItem& it,
   for (int c = 0; c < D / 16; ++c) *reinterpret_cast<bf16x8*>(orow + 8 * c) = z;
 }
 
-// Move to the next tile of the stream; items without keys are skipped (their
-// rows of this wave are written as zeros on the way).
+// Move the loading cursor to the next tile of the stream.  Items without keys
+// are skipped (their rows of this wave are written as zeros on the way).  Past
+// the end the cursor keeps the source and key count of the last item it
+// visited and points at its tile 0, so the loads it still issues read rows
+// that exist (and are never used).
 template <int D>
-__device__ __forceinline__ void advance(const PPCtx& c, Cur& cur, int wave, int lane) {
-  if (!cur.valid) return;
-  if (++cur.t < cur.it.ntiles) return;
-  cur.t = 0;
-  while (true) {
-    ++cur.k;
-    if (cur.k >= c.n) {
-      cur.valid = false;
+__device__ __forceinline__ void advance(const PPCtx& c, Cur& cu, Src& src, int wave, int lane) {
+  if (cu.k >= c.n) return;
+  if (++cu.t < ntiles_of(cu.lk)) return;
+  cu.t = 0;
+  while (++cu.k < c.n) {
+    const WorkItem w = load_record(c, cu.k);
+    if (w.lk > 0) {
+      cu.lk = w.lk;
+      src = make_src<D>(c, w);
       return;
     }
-    cur.it = make_pitem<D>(c, load_record(c, cur.k));
-    if (cur.it.ntiles > 0) return;
-    write_zero_rows<D>(c, cur.it, wave, lane);
+    write_zero_rows<D>(c, w, wave, lane);
   }
 }
 
@@ -183,46 +192,39 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
   for (int k = tid; k < min(c.n, kPPItemCache); k += K::kNT) cache[k] = a.items[item_index(c, k)];
   __syncthreads();
 
-  // Stream cursors: tile s (scores), s+1, s+2 (being loaded).
-  Cur c0;
-  c0.k = -1;
-  c0.t = 0;
-  c0.valid = true;
-  c0.it.ntiles = 0;
-  advance<D>(c, c0, wave, lane);
-  if (!c0.valid) return;
-  Cur c1 = c0, c2;
-  advance<D>(c, c1, wave, lane);
-  c2 = c1;
-  advance<D>(c, c2, wave, lane);
+  // Stream cursors: tile s (scores), s+1, s+2 (being loaded); only the
+  // loading cursor carries the addresses of its item.
+  Cur c0{-1, 0, 0};
+  Src src{};
+  advance<D>(c, c0, src, wave, lane);
+  if (c0.k >= c.n) return;
+  const Src src0 = src;
+  Cur c1 = c0;
+  advance<D>(c, c1, src, wave, lane);
+  const Src src1 = src;
+  Cur c2 = c1;
+  advance<D>(c, c2, src, wave, lane);
 
-  // Loads of tile `cu` into ring stage `st` (a cursor past the end loads the
-  // stand-in tile `sb`, which is never read).  Job j moves 1 KB segment
-  // wave + 8j of K|V; rows of a ragged tile are clamped to its last key.
-  auto tile_job = [&](const Cur& cu, const Cur& sb, int st, int j) __attribute__((always_inline)) {
-    // (fields selected by value: a reference to either cursor would put both on the stack)
-    const bool ok = cu.valid;
-    const int key0 = 64 * (ok ? cu.t : sb.t);
-    const int lim = min(63, (ok ? cu.it.lk : sb.it.lk) - 1 - key0);
+  // Loads of the loading cursor's tile into ring stage `st`.  Job j moves 1 KB
+  // segment wave + 8j of K|V; rows of a ragged tile are clamped to its last key.
+  auto tile_job = [&](const Cur& cu, const Src& sr, int st, int j) __attribute__((always_inline)) {
+    const int key0 = 64 * cu.t;
+    const int lim = min(63, cu.lk - 1 - key0);
     const int sg = wave + kPPWaves * j;
     const bool is_v = sg >= K::kSegsLd;
     const int seg = is_v ? sg - K::kSegsLd : sg;
-    const unsigned char* kb = ok ? cu.it.kb : sb.it.kb;
-    const unsigned char* vb = ok ? cu.it.vb : sb.it.vb;
-    const unsigned char* tile = (is_v ? vb : kb) + size_t(key0) * c.row_bytes;
+    const unsigned char* tile = (is_v ? sr.vb : sr.kb) + size_t(key0) * c.row_bytes;
     const int row = seg * K::kRowsPerSeg + lane / K::kChunksPerRow;
     const int phys = lane % K::kChunksPerRow;
     const int ch = phys ^ (is_v ? swz_v<D>(row) : swz_k<D>(row));
     const unsigned off = __umul24(unsigned(min(row, lim)), c.row_bytes) + 16u * unsigned(ch);
     lds_dma16(tile, off, lds_addr_of(ring) + st * K::kStageBytes + (is_v ? K::kTileBytes : 0) + seg * 1024);
   };
-  auto tile_scales = [&](const Cur& cu, const Cur& sb, int st) __attribute__((always_inline)) {
+  auto tile_scales = [&](const Cur& cu, const Src& sr, int st) __attribute__((always_inline)) {
     if constexpr (ACT != ACT_SOFTMAX) {
-      const bool ok = cu.valid;
-      const int key0 = 64 * (ok ? cu.t : sb.t);
-      const unsigned r = unsigned(min(lane, (ok ? cu.it.lk : sb.it.lk) - 1 - key0));
-      lds_dma4((ok ? cu.it.ksc : sb.it.ksc) + size_t(key0) * a.H, r * unsigned(a.H) * 4u,
-               lds_addr_of(ring) + st * K::kStageBytes + K::kKsOff);
+      const int key0 = 64 * cu.t;
+      const unsigned r = unsigned(min(lane, cu.lk - 1 - key0));
+      lds_dma4(sr.ksc + size_t(key0) * a.H, r * unsigned(a.H) * 4u, lds_addr_of(ring) + st * K::kStageBytes + K::kKsOff);
     }
   };
 
@@ -244,11 +246,12 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
   // Q fragments of the scores' item: lane holds dims [(D/2)g, (D/2)g + D/2) of
   // query row q0 + 32*wave + l32 (rows past the sample load its last row).
   bf16x8 qf[kQChunks];
-  auto load_q = [&](const PItem& it) __attribute__((always_inline)) {
+  auto load_q = [&](int k) __attribute__((always_inline)) {
+    const WorkItem it = load_record(c, k);
     const int qrow = min(it.q0 + 32 * wave + l32, it.lq - 1);
-    const __bf16* src = reinterpret_cast<const __bf16*>(a.q) + (size_t(it.qbeg + qrow) * a.H + it.h) * D + (D / 2) * g;
+    const __bf16* src_q = reinterpret_cast<const __bf16*>(a.q) + (size_t(it.qbeg + qrow) * a.H + it.h) * D + (D / 2) * g;
 #pragma unroll
-    for (int cc = 0; cc < kQChunks; ++cc) qf[cc] = *reinterpret_cast<const bf16x8*>(src + 8 * cc);
+    for (int cc = 0; cc < kQChunks; ++cc) qf[cc] = *reinterpret_cast<const bf16x8*>(src_q + 8 * cc);
   };
   float rq = 1.f;  // GELU: RMS factor of the query row times 1/sqrt(D)
   auto q_rms = [&]() __attribute__((always_inline)) {
@@ -265,12 +268,12 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
 
   // Prologue: tiles 0 and 1 in flight, Q of the first item.
 #pragma unroll
-  for (int j = 0; j < K::kDmaJobs; ++j) tile_job(c0, c0, 0, j);
-  tile_scales(c0, c0, 0);
+  for (int j = 0; j < K::kDmaJobs; ++j) tile_job(c0, src0, 0, j);
+  tile_scales(c0, src0, 0);
 #pragma unroll
-  for (int j = 0; j < K::kDmaJobs; ++j) tile_job(c1, c0, 1, j);
-  tile_scales(c1, c0, 1);
-  load_q(c0.it);
+  for (int j = 0; j < K::kDmaJobs; ++j) tile_job(c1, src1, 1, j);
+  tile_scales(c1, src1, 1);
+  load_q(c0.k);
   wait_vmcnt(0);  // (nothing may be pending on the loop's entry edge, see below)
   bool q_fresh = true;  // Q was (re)loaded for c0's item: GELU needs its RMS factor
 
@@ -282,7 +285,7 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
   float m = -__builtin_huge_valf(), l = 0.f;
   f32x16 sc[2];      // score tile: S^T halves (keys 32*st + 16*(i/8) + 8g + i%8)
   bf16x8 pb[4];      // P of the previous tile, 16-key chunks kc
-  PItem ipv = c0.it;  // item of tile s-1
+  int pv_k = c0.k;   // item of tile s-1
   bool pv_last = false;
   int pv_nvalid = 64;  // keys of tile s-1 inside its sample
 
@@ -339,8 +342,9 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
     }
   };
 
-  // Output rows of item `it`: O / l (softmax) or O / Lk (GELU), then reset.
-  auto epilogue = [&](const PItem& it) __attribute__((always_inline)) {
+  // Output rows of the k-th item: O / l (softmax) or O / Lk (GELU), then reset.
+  auto epilogue = [&](int k) __attribute__((always_inline)) {
+    const WorkItem it = load_record(c, k);
     const int qrow = it.q0 + 32 * wave + l32;
     float scale;
     if constexpr (ACT == ACT_SOFTMAX) {
@@ -379,6 +383,10 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
     // of an item whose last tile was s-1).
     auto head = [&]() __attribute__((always_inline)) {
       if (late && s > 0) vphase(pv_nvalid, st_prev);
+      // The MFMA phase runs at raised wave priority: the SIMD's other wave is
+      // in its VALU phase, and the matrix core should get the next MFMA as
+      // soon as it can take one.
+      __builtin_amdgcn_s_setprio(2);
       if (s > 0) {
         // 4*kOTiles MFMAs (16-key chunk kc, output tile t), the V^T operand
         // read kAhead MFMAs early: one wave issues them alone, so the LDS
@@ -397,7 +405,7 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
           w[3] = hi2[1];
           return __builtin_bit_cast(bf16x8, w);
         };
-        constexpr int kN = 4 * kOTiles, kAhead = 3;
+        constexpr int kN = 4 * kOTiles, kAhead = kN < kPPAhead ? kN : kPPAhead;
         bf16x8 vop[kAhead];
 #pragma unroll
         for (int i = 0; i < kAhead; ++i) vop[i] = vread(i);
@@ -414,20 +422,20 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
           __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
           if (i + kAhead < kN) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
         }
-        if (pv_last) epilogue(ipv);
+        if (pv_last) epilogue(pv_k);
       }
     };
     // A new item starts with tile s: its Q is loaded and waited for here, in
     // one branch (once per item).  A load that may still be pending where
     // branches meet would make the compiler wait for all later loads -- the
     // tile loads it does not know about -- at every step's scores.
-    if (s > 0 && c0.valid && c0.t == 0) {
-      load_q(c0.it);
+    if (s > 0 && c0.k < c.n && c0.t == 0) {
+      load_q(c0.k);
       wait_vmcnt(0);
       q_fresh = true;
     }
     head();
-    if (!c0.valid) break;
+    if (c0.k >= c.n) break;
     if (q_fresh) {
       q_rms();
       q_fresh = false;
@@ -438,46 +446,44 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int i = 0; i < 16; ++i) sc[st][i] = 0.f;
-      // first half: every Q fragment is consumed (the compiler's waits for
-      // the Q loads do not count the direct loads issued after it)
-      constexpr int kAhead = kQChunks < 3 ? kQChunks : 3;
+      // 2 x kQChunks MFMAs (score half i / kQChunks, D chunk i % kQChunks), the
+      // K operand read kAhead MFMAs early; the loads of tile s+2 go between the
+      // MFMAs of the second half.  (LDS reads are not moved across the asm of
+      // those loads, so the reads are placed early in source order.)
+      constexpr int kNS = 2 * kQChunks, kAhead = kNS < kPPAhead ? kNS : kPPAhead;
+      auto kread = [&](int i) __attribute__((always_inline)) {
+        return *reinterpret_cast<const bf16x8*>(ks + (i / kQChunks) * 32 * kRowBytes + k_off[i % kQChunks]);
+      };
       bf16x8 kop[kAhead];
 #pragma unroll
-      for (int i = 0; i < kAhead; ++i) kop[i] = *reinterpret_cast<const bf16x8*>(ks + k_off[i]);
+      for (int i = 0; i < kAhead; ++i) kop[i] = kread(i);
 #pragma unroll
-      for (int cc = 0; cc < kQChunks; ++cc) {
-        const bf16x8 op = kop[cc % kAhead];
-        if (cc + kAhead < kQChunks) kop[cc % kAhead] = *reinterpret_cast<const bf16x8*>(ks + k_off[cc + kAhead]);
-        sc[0] = mfma_32x32x16(op, qf[cc], sc[0]);
+      for (int i = 0; i < kNS; ++i) {
+        const bf16x8 op = kop[i % kAhead];
+        if (i + kAhead < kNS) kop[i % kAhead] = kread(i + kAhead);
+        sc[i / kQChunks] = mfma_32x32x16(op, qf[i % kQChunks], sc[i / kQChunks]);
+        constexpr int kPer = kQChunks / K::kDmaJobs;
+        if (i >= kQChunks && (i - kQChunks) % kPer == kPer - 1) tile_job(c2, src, st_pf, (i - kQChunks) / kPer);
       }
+      // keep the reads kAhead MFMAs early and the MFMAs in order
       __builtin_amdgcn_sched_group_barrier(kSgDsRead, kAhead, 1);
 #pragma unroll
-      for (int cc = 0; cc < kQChunks; ++cc) {
+      for (int i = 0; i < kNS; ++i) {
         __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 1);
-        if (cc + kAhead < kQChunks) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 1);
+        if (i + kAhead < kNS) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 1);
       }
-      // second half, with the loads of tile s+2 between the MFMAs; the K
-      // operand is read one MFMA ahead (LDS reads are not moved across asm)
-      bf16x8 knext = *reinterpret_cast<const bf16x8*>(ks + 32 * kRowBytes + k_off[0]);
-#pragma unroll
-      for (int cc = 0; cc < kQChunks; ++cc) {
-        const bf16x8 kf = knext;
-        if (cc + 1 < kQChunks) knext = *reinterpret_cast<const bf16x8*>(ks + 32 * kRowBytes + k_off[cc + 1]);
-        sc[1] = mfma_32x32x16(kf, qf[cc], sc[1]);
-        constexpr int kPer = kQChunks / K::kDmaJobs;
-        if (cc % kPer == kPer - 1) tile_job(c2, c0, st_pf, cc / kPer);
-      }
-      tile_scales(c2, c0, st_pf);
+      tile_scales(c2, src, st_pf);
     }
-    const bool s_last = c0.t == c0.it.ntiles - 1;
-    const int nvalid = min(64, c0.it.lk - 64 * c0.t);
+    __builtin_amdgcn_s_setprio(0);
+    const bool s_last = c0.t == ntiles_of(c0.lk) - 1;
+    const int nvalid = min(64, c0.lk - 64 * c0.t);
     if (!late) vphase(nvalid, st_s);
-    ipv = c0.it;
+    pv_k = c0.k;
     pv_last = s_last;
     pv_nvalid = nvalid;
     c0 = c1;
     c1 = c2;
-    advance<D>(c, c2, wave, lane);
+    advance<D>(c, c2, src, wave, lane);
   }
 }
 
