@@ -40,6 +40,7 @@ constexpr int kSgMfma = 0x008, kSgDsRead = 0x100;
 // MFMA operands are read this many MFMAs before their use (LDS latency under
 // the load of four waves reading at once is several MFMAs long).
 constexpr int kPPAhead = 5;
+constexpr int kPPAheadS = 8;
 
 template <int D, int ACT>
 struct PP {
@@ -450,7 +451,7 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
       // K operand read kAhead MFMAs early; the loads of tile s+2 go between the
       // MFMAs of the second half.  (LDS reads are not moved across the asm of
       // those loads, so the reads are placed early in source order.)
-      constexpr int kNS = 2 * kQChunks, kAhead = kNS < kPPAhead ? kNS : kPPAhead;
+      constexpr int kNS = 2 * kQChunks, kAhead = kNS < kPPAheadS ? kNS : kPPAheadS;
       auto kread = [&](int i) __attribute__((always_inline)) {
         return *reinterpret_cast<const bf16x8*>(ks + (i / kQChunks) * 32 * kRowBytes + k_off[i % kQChunks]);
       };
