@@ -78,6 +78,9 @@ Plan make_plan(int B, int H, int D, int variant, int act, int window, int dtype,
   if (dtype == JA_F32) {
     p.shape = kShapeF32;
     p.bm = 64;
+  } else if (dtype == JA_BF16 && variant != JA_PMA) {
+    p.shape = kShapePingPong;  // self (with or without window) and cross: one tile stream, 8 waves x 32 rows
+    p.bm = pp_rows();
   } else if (window > 0) {
     p.shape = kShapeWindow;
     p.bm = 128;  // two 64-token query blocks
@@ -85,9 +88,6 @@ Plan make_plan(int B, int H, int D, int variant, int act, int window, int dtype,
     p.shape = kShapeKvSplit;
     p.bm = kPmaRows;
     p.kvc = choose_kvc(H, total_kv);
-  } else if (dtype == JA_BF16) {
-    p.shape = kShapePingPong;  // self (no window) and cross: one tile stream, 8 waves x 32 rows
-    p.bm = pp_rows();
   } else if (variant == JA_SELF && act == JA_SOFTMAX) {
     p.shape = kShapeFullSelf;
     p.bm = 256;  // eight waves x 32 query rows

@@ -421,7 +421,7 @@ __global__ __launch_bounds__(64 * NWQ * NWK, QSUB == 2 ? 1 : 2) void attn_kernel
           }
         }
         if constexpr (ACT != ACT_SOFTMAX) {
-          ss += other_half(ss);
+          ss = sum_halves(ss);
           rq[qs] = __builtin_amdgcn_rsqf(ss * (1.0f / D) + a.eps) * c2;
         } else {
           rq[qs] = 1.0f;
@@ -445,7 +445,7 @@ __global__ __launch_bounds__(64 * NWQ * NWK, QSUB == 2 ? 1 : 2) void attn_kernel
         for (int c = 0; c < kQChunks; ++c)
 #pragma unroll
           for (int j = 0; j < 8; ++j) ss = fmaf(float(qf[qs][c][j]), float(qf[qs][c][j]), ss);
-        ss += other_half(ss);
+        ss = sum_halves(ss);
         rq[qs] = __builtin_amdgcn_rsqf(ss * (1.0f / D) + a.eps) * c2;
       }
     }
@@ -612,7 +612,7 @@ __global__ __launch_bounds__(64 * NWQ * NWK, QSUB == 2 ? 1 : 2) void attn_kernel
             for (int st = 0; st < 2; ++st)
 #pragma unroll
               for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[qs][st][i]);
-            mt = fmaxf(mt, other_half(mt));
+            mt = max_halves(mt);
             // Lazy rescale: the reference max moves only when a row's tile max
             // exceeds it by more than kLazyLog2 (base 2), so exponentials stay
             // below 2^kLazyLog2 and most tiles skip the O rescale.  Softmax is
@@ -727,7 +727,7 @@ __global__ __launch_bounds__(64 * NWQ * NWK, QSUB == 2 ? 1 : 2) void attn_kernel
       for (int qs = 0; qs < QSUB; ++qs) {
         const int qrow = qrow_w + 32 * qs + l32;
         if (qrow >= cur.lq) continue;
-        const float l_tot = l[qs] + other_half(l[qs]);
+        const float l_tot = sum_halves(l[qs]);
         bool done = false;
         if constexpr (SPLIT) {
           const int ns = a.nsplit[cur.b];

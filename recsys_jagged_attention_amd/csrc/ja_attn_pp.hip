@@ -21,7 +21,9 @@
 //
 // LDS holds a ring of 4 tiles (K and V, plus the key scales of the GELU path):
 // in step s the waves read K_s and V_{s-1}, tile s+1 has landed and tile s+2
-// is loaded by direct-to-LDS loads issued between the score MFMAs.  Operand
+// is loaded by direct-to-LDS loads issued between the score MFMAs.  The next
+// step's wait for tile s+1 lets an item's output stores, issued in this step,
+// run on.  Operand
 // layouts, swizzles and the transposed score tile are those of the main MFMA
 // kernel (ja_attn_mfma.hip).
 #include "ja_device.h"
@@ -37,6 +39,11 @@ constexpr int kPPRows = 32 * kPPWaves;  // query rows per work item
 constexpr int kPPItemCache = 256;       // work item records staged in LDS per workgroup
 // instruction classes of __builtin_amdgcn_sched_group_barrier
 constexpr int kSgMfma = 0x008, kSgDsRead = 0x100;
+// Softmax: a lane's sum of one tile's exponentials (32 keys) against the lazy
+// reference max may reach 2^12 before the reference moves up.
+constexpr float kPartCap = 4096.0f;
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+__device__ constexpr bf16x2v kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 // MFMA operands are read this many MFMAs before their use (LDS latency under
 // the load of four waves reading at once is several MFMAs long).
 constexpr int kPPAhead = 5;
@@ -57,14 +64,16 @@ struct PP {
   static constexpr int kChunksPerRow = kRowBytes / 16;
   static constexpr int kDmaJobs = 2 * kSegsLd / kPPWaves;  // 1 KB loads per wave per tile
   static constexpr int kVmemPerTile = kDmaJobs + (ACT != ACT_SOFTMAX ? 1 : 0);
+  static constexpr int kStoresPerWave = 2 * kOTiles;  // 16-byte output stores per lane of an item
   static_assert((2 * kSegsLd) % kPPWaves == 0, "tile segments must split evenly over the waves");
-  static_assert(kQChunks % kDmaJobs == 0, "loads are spread evenly over the score MFMAs");
 };
 
 // Position in the tile stream: tile t of the k-th item of this workgroup
-// (k == n: past the end), and the item's key count.  Wave-uniform.
+// (k == n: past the end), the end of the item's tiles and its key count.
+// Block windows: this wave computes tiles [wlo, whi] of the item.  Wave-uniform.
 struct Cur {
-  int k, t, lk;
+  int k, t, te, lk;
+  int wlo, whi;
 };
 
 __device__ __forceinline__ int ntiles_of(int lk) { return (lk + 63) >> 6; }
@@ -143,23 +152,39 @@ __device__ __forceinline__ void write_zero_rows(const PPCtx& c, const WorkItem& 
 // the end the cursor keeps the source and key count of the last item it
 // visited and points at its tile 0, so the loads it still issues read rows
 // that exist (and are never used).
-template <int D>
-__device__ __forceinline__ void advance(const PPCtx& c, Cur& cu, Src& src, int wave, int lane) {
+//
+// With a block window of nb blocks (self-attention, 64-token blocks counted
+// from the sample's first token) an item covers the key tiles from nb - 1
+// blocks before its first query block to its last query block, and a wave
+// computes the tiles its own query block sees (techfeed.io summary of "GEM
+// Training: ...", section "BlockAttention").
+template <int D, bool WINDOW>
+__device__ __forceinline__ void advance(const PPCtx& c, Cur& cu, Src& src, int wave, int lane, int nb) {
   if (cu.k >= c.n) return;
-  if (++cu.t < ntiles_of(cu.lk)) return;
-  cu.t = 0;
+  if (++cu.t < cu.te) return;
   while (++cu.k < c.n) {
     const WorkItem w = load_record(c, cu.k);
-    if (w.lk > 0) {
+    int t_lo = 0, t_end = ntiles_of(w.lk);
+    if constexpr (WINDOW) {
+      t_lo = max(0, w.q0 / kBlock - nb + 1);
+      t_end = min(t_end, (min(w.q0 + kPPRows, w.lq) + kBlock - 1) / kBlock);
+      const int r0 = w.q0 + 32 * wave, wblk = r0 / kBlock;
+      cu.wlo = wblk - nb + 1;
+      cu.whi = r0 < w.lq ? wblk : -1;
+    }
+    if (t_end > t_lo) {
+      cu.t = t_lo;
+      cu.te = t_end;
       cu.lk = w.lk;
       src = make_src<D>(c, w);
       return;
     }
     write_zero_rows<D>(c, w, wave, lane);
   }
+  cu.t = 0;  // past the end: tile 0 of the last item visited
 }
 
-template <int D, int ACT>
+template <int D, int ACT, bool WINDOW>
 __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
   using K = PP<D, ACT>;
   constexpr int kQChunks = K::kQChunks, kOTiles = K::kOTiles, kRowBytes = K::kRowBytes;
@@ -195,16 +220,17 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
 
   // Stream cursors: tile s (scores), s+1, s+2 (being loaded); only the
   // loading cursor carries the addresses of its item.
-  Cur c0{-1, 0, 0};
+  const int nb = a.window_blocks;
+  Cur c0{-1, 0, 0, 0, 0, 0};
   Src src{};
-  advance<D>(c, c0, src, wave, lane);
+  advance<D, WINDOW>(c, c0, src, wave, lane, nb);
   if (c0.k >= c.n) return;
   const Src src0 = src;
   Cur c1 = c0;
-  advance<D>(c, c1, src, wave, lane);
+  advance<D, WINDOW>(c, c1, src, wave, lane, nb);
   const Src src1 = src;
   Cur c2 = c1;
-  advance<D>(c, c2, src, wave, lane);
+  advance<D, WINDOW>(c, c2, src, wave, lane, nb);
 
   // Loads of the loading cursor's tile into ring stage `st`.  Job j moves 1 KB
   // segment wave + 8j of K|V; rows of a ragged tile are clamped to its last key.
@@ -242,7 +268,6 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
     v_col[t] = 16 * ((col >> 3) ^ swz_v<D>((lane & 15) >> 2)) + 8 * ((col & 7) >> 2);
   }
   const float c2s = a.score_scale;  // softmax: log2(e)/sqrt(D); GELU: 1/sqrt(D)
-  const float lazy_thr = kLazyLog2 / c2s;
 
   // Q fragments of the scores' item: lane holds dims [(D/2)g, (D/2)g + D/2) of
   // query row q0 + 32*wave + l32 (rows past the sample load its last row).
@@ -262,7 +287,7 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
       for (int cc = 0; cc < kQChunks; ++cc)
 #pragma unroll
         for (int j = 0; j < 8; ++j) ss = fmaf(float(qf[cc][j]), float(qf[cc][j]), ss);
-      ss += other_half(ss);
+      ss = sum_halves(ss);
       rq = __builtin_amdgcn_rsqf(ss * (1.0f / D) + a.eps) * c2s;
     }
   };
@@ -288,6 +313,7 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
   bf16x8 pb[4];      // P of the previous tile, 16-key chunks kc
   int pv_k = c0.k;   // item of tile s-1
   bool pv_last = false;
+  bool pv_act = true;  // this wave computed tile s-1 (block windows)
   int pv_nvalid = 64;  // keys of tile s-1 inside its sample
 
   // Softmax / GELU of the score tile `sc` (nvalid keys), written to pb as bf16.
@@ -303,15 +329,37 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
             if (kk >= nvalid) sc[st][i] = -__builtin_huge_valf();
           }
       }
-      float mt = -__builtin_huge_valf();
+      // p = 2^(s c - m c) into pb; returns this lane's sum of the bf16 p
+      // (the weights P V uses), two at a time on the dot unit.
+      auto exps = [&](float mc) __attribute__((always_inline)) {
+        float part[4] = {0.f, 0.f, 0.f, 0.f};  // (four chains)
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
+        for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sc[st][i]);
-      mt = fmaxf(mt, other_half(mt));
-      // lazy rescale: the reference max moves only when a row grows by more
-      // than 2^kLazyLog2 (base 2); softmax is unchanged by the reference.
-      if (__any(mt - m > lazy_thr)) {
+          for (int j = 0; j < 8; j += 2) {
+            pb[kc][j] = (__bf16)fast_exp2(fmaf(sc[kc >> 1][8 * (kc & 1) + j], c2s, -mc));
+            pb[kc][j + 1] = (__bf16)fast_exp2(fmaf(sc[kc >> 1][8 * (kc & 1) + j + 1], c2s, -mc));
+            const bf16x2v pr = {pb[kc][j], pb[kc][j + 1]};
+            part[j / 2] = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, part[j / 2], false);
+          }
+        return (part[0] + part[1]) + (part[2] + part[3]);
+      };
+      // Lazy reference max: the exponentials are taken against the current
+      // reference m without looking for the tile's max first.  While every
+      // lane's sum stays at most 2^kPartLog2 (so each p does), nothing moves;
+      // otherwise (and on an item's first tile) the tile's max is found, m
+      // moves up to it, O and l are rescaled and the exponentials are taken
+      // again.  Softmax is unchanged by the choice of reference.
+      const bool fresh = __any(m == -__builtin_huge_valf());
+      float part = 0.f;
+      if (!fresh) part = exps(m * c2s);
+      if (fresh || __any(!(part <= kPartCap))) {
+        float mt = -__builtin_huge_valf();
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sc[st][i]);
+        mt = max_halves(mt);
         const float m_new = fmaxf(m, mt);
         const float alpha = m == -__builtin_huge_valf() ? 0.f : fast_exp2((m - m_new) * c2s);
         l *= alpha;
@@ -320,16 +368,9 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
         m = m_new;
+        part = exps(m * c2s);
       }
-      const float mc = m * c2s;
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float p = fast_exp2(fmaf(sc[kc >> 1][8 * (kc & 1) + j], c2s, -mc));
-          l += p;
-          pb[kc][j] = (__bf16)p;
-        }
+      l += part;
     } else {
       const float* ksl = reinterpret_cast<const float*>(ring + stage * K::kStageBytes + K::kKsOff);
 #pragma unroll
@@ -344,12 +385,13 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
   };
 
   // Output rows of the k-th item: O / l (softmax) or O / Lk (GELU), then reset.
+  // Returns whether this wave issued its kStoresPerWave stores.
   auto epilogue = [&](int k) __attribute__((always_inline)) {
     const WorkItem it = load_record(c, k);
     const int qrow = it.q0 + 32 * wave + l32;
     float scale;
     if constexpr (ACT == ACT_SOFTMAX) {
-      const float l_tot = l + other_half(l);
+      const float l_tot = sum_halves(l);
       scale = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     } else {
       scale = 1.0f / float(it.lk);
@@ -372,85 +414,101 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
       for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
     m = -__builtin_huge_valf();
     l = 0.f;
+    return it.q0 + 32 * wave < it.lq;  // (lane 0 stores)
   };
 
+  bool stores_pending = false;  // the output stores of the last step follow its tile loads
   for (int s = 0;; ++s) {
-    // Tile s has landed once only the loads of tile s+1 can still be pending.
-    wait_vmcnt(K::kVmemPerTile);
+    // Tile s has landed once only the loads of tile s+1 (and the output
+    // stores issued after them) can still be pending.
+    if (stores_pending) wait_vmcnt(K::kVmemPerTile + K::kStoresPerWave);
+    else wait_vmcnt(K::kVmemPerTile);
     lds_barrier();
     const int st_s = s % K::kRing, st_prev = (s + K::kRing - 1) % K::kRing, st_pf = (s + 2) % K::kRing;
 
-    // ---- late waves' VALU phase, then O += V_{s-1} P_{s-1} (and the output
-    // of an item whose last tile was s-1).
+    // ---- late waves' VALU phase, then O += V_{s-1} P_{s-1}.
     auto head = [&]() __attribute__((always_inline)) {
-      if (late && s > 0) vphase(pv_nvalid, st_prev);
+      if (late && s > 0 && pv_act) vphase(pv_nvalid, st_prev);
       // The MFMA phase runs at raised wave priority: the SIMD's other wave is
       // in its VALU phase, and the matrix core should get the next MFMA as
       // soon as it can take one.
       __builtin_amdgcn_s_setprio(2);
       if (s > 0) {
-        // 4*kOTiles MFMAs (16-key chunk kc, output tile t), the V^T operand
-        // read kAhead MFMAs early: one wave issues them alone, so the LDS
-        // transpose-read latency is not hidden by a second wave.
-        const unsigned char* vs = ring + st_prev * K::kStageBytes + K::kTileBytes;
-        auto vread = [&](int i) __attribute__((always_inline)) {
-          const int kc = i / kOTiles, t = i % kOTiles;
-          const unsigned char* p0 = vs + v_row + kc * 16 * kRowBytes + v_col[t];
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 4 * kRowBytes));
-          const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
-          u32x4 w;
-          w[0] = lo2[0];
-          w[1] = lo2[1];
-          w[2] = hi2[0];
-          w[3] = hi2[1];
-          return __builtin_bit_cast(bf16x8, w);
-        };
-        constexpr int kN = 4 * kOTiles, kAhead = kN < kPPAhead ? kN : kPPAhead;
-        bf16x8 vop[kAhead];
+        if (!WINDOW || pv_act) {
+          // 4*kOTiles MFMAs (16-key chunk kc, output tile t), the V^T operand
+          // read kAhead MFMAs early: one wave issues them alone, so the LDS
+          // transpose-read latency is not hidden by a second wave.
+          const unsigned char* vs = ring + st_prev * K::kStageBytes + K::kTileBytes;
+          auto vread = [&](int i) __attribute__((always_inline)) {
+            const int kc = i / kOTiles, t = i % kOTiles;
+            const unsigned char* p0 = vs + v_row + kc * 16 * kRowBytes + v_col[t];
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 4 * kRowBytes));
+            const u32x2 lo2 = __builtin_bit_cast(u32x2, lo), hi2 = __builtin_bit_cast(u32x2, hi);
+            u32x4 w;
+            w[0] = lo2[0];
+            w[1] = lo2[1];
+            w[2] = hi2[0];
+            w[3] = hi2[1];
+            return __builtin_bit_cast(bf16x8, w);
+          };
+          constexpr int kN = 4 * kOTiles, kAhead = kN < kPPAhead ? kN : kPPAhead;
+          bf16x8 vop[kAhead];
 #pragma unroll
-        for (int i = 0; i < kAhead; ++i) vop[i] = vread(i);
+          for (int i = 0; i < kAhead; ++i) vop[i] = vread(i);
 #pragma unroll
-        for (int i = 0; i < kN; ++i) {
-          const bf16x8 op = vop[i % kAhead];
-          if (i + kAhead < kN) vop[i % kAhead] = vread(i + kAhead);
-          o[i % kOTiles] = mfma_32x32x16(op, pb[i / kOTiles], o[i % kOTiles]);
+          for (int i = 0; i < kN; ++i) {
+            const bf16x8 op = vop[i % kAhead];
+            if (i + kAhead < kN) vop[i % kAhead] = vread(i + kAhead);
+            o[i % kOTiles] = mfma_32x32x16(op, pb[i / kOTiles], o[i % kOTiles]);
+          }
+          // keep the reads kAhead MFMAs early (the scheduler would sink them)
+          __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2 * kAhead, 0);
+#pragma unroll
+          for (int i = 0; i < kN; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+            if (i + kAhead < kN) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+          }
         }
-        // keep the reads kAhead MFMAs early (the scheduler would sink them)
-        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2 * kAhead, 0);
-#pragma unroll
-        for (int i = 0; i < kN; ++i) {
-          __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-          if (i + kAhead < kN) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
-        }
-        if (pv_last) epilogue(pv_k);
+        // Output of an item whose last tile was s-1.  These stores are newer
+        // than the loads of tile s+1 (issued in the previous step), so the
+        // next step's wait for that tile can let them run on.
+        if (pv_last) stores_pending = epilogue(pv_k);
       }
     };
     // A new item starts with tile s: its Q is loaded and waited for here, in
     // one branch (once per item).  A load that may still be pending where
     // branches meet would make the compiler wait for all later loads -- the
     // tile loads it does not know about -- at every step's scores.
-    if (s > 0 && c0.k < c.n && c0.t == 0) {
+    if (s > 0 && c0.k < c.n && c0.k != pv_k) {
       load_q(c0.k);
       wait_vmcnt(0);
       q_fresh = true;
     }
+    stores_pending = false;
     head();
     if (c0.k >= c.n) break;
     if (q_fresh) {
       q_rms();
       q_fresh = false;
     }
-    {
+    // Loads of tile s+2 (into the stage that held tile s-2, last read in the
+    // previous step): between the MFMAs of the second score half, or all at
+    // once for a wave that skips the tile.
+    const bool act = !WINDOW || (c0.t >= c0.wlo && c0.t <= c0.whi);  // this wave computes tile s
+    if (!act) {
+#pragma unroll
+      for (int j = 0; j < K::kDmaJobs; ++j) tile_job(c2, src, st_pf, j);
+    } else {
       const unsigned char* ks = ring + st_s * K::kStageBytes;
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int i = 0; i < 16; ++i) sc[st][i] = 0.f;
       // 2 x kQChunks MFMAs (score half i / kQChunks, D chunk i % kQChunks), the
-      // K operand read kAhead MFMAs early; the loads of tile s+2 go between the
-      // MFMAs of the second half.  (LDS reads are not moved across the asm of
-      // those loads, so the reads are placed early in source order.)
+      // K operand read kAhead MFMAs early.  (LDS reads are not moved across
+      // the asm of the tile loads, so the reads are placed early in source
+      // order.)
       constexpr int kNS = 2 * kQChunks, kAhead = kNS < kPPAheadS ? kNS : kPPAheadS;
       auto kread = [&](int i) __attribute__((always_inline)) {
         return *reinterpret_cast<const bf16x8*>(ks + (i / kQChunks) * 32 * kRowBytes + k_off[i % kQChunks]);
@@ -473,18 +531,19 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
         __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 1);
         if (i + kAhead < kNS) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 1);
       }
-      tile_scales(c2, src, st_pf);
     }
+    tile_scales(c2, src, st_pf);
     __builtin_amdgcn_s_setprio(0);
-    const bool s_last = c0.t == ntiles_of(c0.lk) - 1;
+    const bool s_last = c0.t == c0.te - 1;
     const int nvalid = min(64, c0.lk - 64 * c0.t);
-    if (!late) vphase(nvalid, st_s);
+    if (!late && act) vphase(nvalid, st_s);
     pv_k = c0.k;
+    pv_act = act;
     pv_last = s_last;
     pv_nvalid = nvalid;
     c0 = c1;
     c1 = c2;
-    advance<D>(c, c2, src, wave, lane);
+    advance<D, WINDOW>(c, c2, src, wave, lane, nb);
   }
 }
 
@@ -500,18 +559,22 @@ hipError_t launch_attn_pp(int D, int act, const AttnArgs& a, int num_cu, int64_t
   grid = (grid / kXcds) * kXcds;
   if (grid < kXcds) grid = kXcds;
   const dim3 gd(static_cast<unsigned>(grid)), bd(64 * kPPWaves);
-  if (act == ACT_SOFTMAX) {
-    if (D == 32) hipLaunchKernelGGL((attn_pp_kernel<32, ACT_SOFTMAX>), gd, bd, 0, st, a);
-    else if (D == 64) hipLaunchKernelGGL((attn_pp_kernel<64, ACT_SOFTMAX>), gd, bd, 0, st, a);
-    else hipLaunchKernelGGL((attn_pp_kernel<128, ACT_SOFTMAX>), gd, bd, 0, st, a);
+  if (a.window_blocks > 0) {  // (softmax only)
+    if (D == 32) hipLaunchKernelGGL((attn_pp_kernel<32, ACT_SOFTMAX, true>), gd, bd, 0, st, a);
+    else if (D == 64) hipLaunchKernelGGL((attn_pp_kernel<64, ACT_SOFTMAX, true>), gd, bd, 0, st, a);
+    else hipLaunchKernelGGL((attn_pp_kernel<128, ACT_SOFTMAX, true>), gd, bd, 0, st, a);
+  } else if (act == ACT_SOFTMAX) {
+    if (D == 32) hipLaunchKernelGGL((attn_pp_kernel<32, ACT_SOFTMAX, false>), gd, bd, 0, st, a);
+    else if (D == 64) hipLaunchKernelGGL((attn_pp_kernel<64, ACT_SOFTMAX, false>), gd, bd, 0, st, a);
+    else hipLaunchKernelGGL((attn_pp_kernel<128, ACT_SOFTMAX, false>), gd, bd, 0, st, a);
   } else if (act == ACT_GELU_POLY) {
-    if (D == 32) hipLaunchKernelGGL((attn_pp_kernel<32, ACT_GELU_POLY>), gd, bd, 0, st, a);
-    else if (D == 64) hipLaunchKernelGGL((attn_pp_kernel<64, ACT_GELU_POLY>), gd, bd, 0, st, a);
-    else hipLaunchKernelGGL((attn_pp_kernel<128, ACT_GELU_POLY>), gd, bd, 0, st, a);
+    if (D == 32) hipLaunchKernelGGL((attn_pp_kernel<32, ACT_GELU_POLY, false>), gd, bd, 0, st, a);
+    else if (D == 64) hipLaunchKernelGGL((attn_pp_kernel<64, ACT_GELU_POLY, false>), gd, bd, 0, st, a);
+    else hipLaunchKernelGGL((attn_pp_kernel<128, ACT_GELU_POLY, false>), gd, bd, 0, st, a);
   } else {
-    if (D == 32) hipLaunchKernelGGL((attn_pp_kernel<32, ACT_GELU>), gd, bd, 0, st, a);
-    else if (D == 64) hipLaunchKernelGGL((attn_pp_kernel<64, ACT_GELU>), gd, bd, 0, st, a);
-    else hipLaunchKernelGGL((attn_pp_kernel<128, ACT_GELU>), gd, bd, 0, st, a);
+    if (D == 32) hipLaunchKernelGGL((attn_pp_kernel<32, ACT_GELU, false>), gd, bd, 0, st, a);
+    else if (D == 64) hipLaunchKernelGGL((attn_pp_kernel<64, ACT_GELU, false>), gd, bd, 0, st, a);
+    else hipLaunchKernelGGL((attn_pp_kernel<128, ACT_GELU, false>), gd, bd, 0, st, a);
   }
   return hipGetLastError();
 }

@@ -21,7 +21,18 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ float other_half(float x) { return __shfl_xor(x, 32, 64); }
+// Sum and max of lane l's value and lane l^32's (the two 32-lane halves that
+// hold one MFMA column), on the VALU: v_permlane32_swap with both operands x
+// leaves the pair {x[l], x[l^32]} in lane l (its order depends on the half,
+// which a symmetric operation does not see, so every lane gets the same bits).
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
 // Decode 8 e4m3 ("fn") codes (little-endian in a u32x2) scaled by 2^(e8m0-127)
 // into bf16.  Exact: an e4m3 value has at most 4 significant bits and the

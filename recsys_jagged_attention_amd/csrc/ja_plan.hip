@@ -27,7 +27,13 @@ constexpr int kPlanThreads = 1024;
 constexpr int kPlanWaves = kPlanThreads / 64;
 constexpr int kCostBuckets = kPlanThreads;  // cost order: bucket = key tiles, clamped
 
-__device__ inline int cost_bucket(int lk) { return min((lk + kBlock - 1) / kBlock, kCostBuckets - 1); }
+// Key tiles an item of the sample walks: all of them, or with a block window
+// at most the window plus the item's other query blocks.
+__device__ inline int cost_bucket(const PlanArgs& a, int lk) {
+  int t = (lk + kBlock - 1) / kBlock;
+  if (a.window_blocks > 0) t = min(t, a.window_blocks + a.bm / kBlock - 1);
+  return min(t, kCostBuckets - 1);
+}
 
 template <typename T>
 __device__ inline T wave_inclusive_scan(T x) {
@@ -122,7 +128,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       my_items += w.cnt;
       my_slots += w.slots;
       my_cost += w.cnt * w.ck;
-      if (a.cost_order && w.cnt > 0) atomicAdd(&s_bucket[cost_bucket(k1 - k)], w.cnt);
+      if (a.cost_order && w.cnt > 0) atomicAdd(&s_bucket[cost_bucket(a, k1 - k)], w.cnt);
     }
   }
   if (bad) atomicOr(&s_bad, 1);
@@ -204,7 +210,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       const int nq = s_nqt[j], nsj = s_ns[j];
       const int qb = s_qb[j], lq = s_lq[j], kb = s_kb[j], lk = s_lk[j];
       if (nq == 0) continue;
-      int ib = a.cost_order ? atomicAdd(&s_bucket[cost_bucket(lk)], nq * nsj) : s_base[j] + h * nq * nsj;
+      int ib = a.cost_order ? atomicAdd(&s_bucket[cost_bucket(a, lk)], nq * nsj) : s_base[j] + h * nq * nsj;
       for (int qt = 0; qt < nq; ++qt)
         for (int sp = 0; sp < nsj; ++sp) a.items[ib++] = WorkItem{base + j, h, qt * a.bm, sp, qb, lq, kb, lk};
     }

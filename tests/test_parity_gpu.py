@@ -156,6 +156,17 @@ def test_many_items_per_workgroup(act):
     sampled_parity(w, out, n=160)
 
 
+@pytest.mark.parametrize("window", [64, 256, 1024])
+def test_block_window_long_samples(window):
+    """Block windows on samples of many 256-row items: items whose first key
+    tile lies several blocks before their first query block, windows shorter
+    and longer than an item, a ragged last block and a one-block sample."""
+    L = [1500, 2049, 700, 64, 3001, 257]
+    w = adhoc("window_long", "self", "softmax", "bf16", L, L, 2, 128, window=window, seed=window + 7)
+    log(f"block window long W={window}: N={w.total_q}")
+    full_parity(w)
+
+
 @pytest.mark.parametrize("act", ["softmax", "gelu_tanh"])
 def test_cost_order_long_and_skewed_keys(act):
     """Tile-stream items are placed by a counting sort on their key tiles: key
