@@ -23,9 +23,13 @@ What is computed -- the plain definition, sample by sample and head by head:
   協調設計によるスケーラブルなアーキテクチャ": 64-token blocks, window a whole number
   of blocks): query in block i sees every key of blocks i-W/64+1 .. i, blocks
   counted from the sample's first token, the last block possibly partial.
+  Sliding window ([GEM-T] "BlockAttention": the token-level sliding window that
+  block attention grew out of, cost O(L x window)): query i sees keys j with
+  i - W < j <= i, positions counted from the sample's first token.
 
 Readings where the pages are silent (each listed in the design notes):
   * no causal mask inside a block or in full attention; window 0 = no window;
+  * the sliding window looks back: W keys ending at the query itself;
   * scale 1/sqrt(D) for every variant, no bias or positional term;
   * RMSNorm has unit weight and eps inside the square root (default 1e-6);
   * Lk == 0 gives O == 0; Lq == 0 gives no rows.
@@ -67,7 +71,24 @@ def block_window_allowed(lq: int, lk: int, window: int) -> np.ndarray:
     return (kj <= qi) & (kj >= qi - nb + 1)
 
 
-def attention_dense(Q, K, V, act: str, window: int = 0, eps: float = DEFAULT_EPS):
+def sliding_window_allowed(lq: int, lk: int, window: int) -> np.ndarray:
+    """Boolean [lq, lk] for the token sliding window (window >= 1): key j is
+    allowed for query i when i - window < j <= i."""
+    if window < 1:
+        raise ValueError("a sliding window needs window >= 1")
+    qi = np.arange(lq)[:, None]
+    kj = np.arange(lk)[None, :]
+    return (kj <= qi) & (kj > qi - window)
+
+
+def allowed_keys(lq: int, lk: int, window: int, variant: str = "self") -> np.ndarray:
+    """The softmax mask of any variant: sliding window or block window / all keys."""
+    if variant == "sliding":
+        return sliding_window_allowed(lq, lk, window)
+    return block_window_allowed(lq, lk, window)
+
+
+def attention_dense(Q, K, V, act: str, window: int = 0, eps: float = DEFAULT_EPS, variant: str = "self"):
     """One (sample, head): Q [Lq,D], K, V [Lk,D] -> O [Lq,D] in float64."""
     Q = np.asarray(Q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
@@ -80,7 +101,7 @@ def attention_dense(Q, K, V, act: str, window: int = 0, eps: float = DEFAULT_EPS
         return np.zeros((lq, d))
     if act == "softmax":
         S = (Q @ K.T) / math.sqrt(d)
-        allowed = block_window_allowed(lq, lk, window)
+        allowed = allowed_keys(lq, lk, window, variant)
         S = np.where(allowed, S, -np.inf)
         m = S.max(axis=1, keepdims=True)
         P = np.exp(S - m)            # exp(-inf) = 0 for disallowed keys
@@ -103,12 +124,14 @@ def _check(q, k, v, q_offsets, kv_offsets, variant, act, window):
         raise ValueError("offsets must be non-decreasing")
     if qo[-1] != q.shape[0] or ko[-1] != k.shape[0] or k.shape != v.shape:
         raise ValueError("offsets do not match the value tensors")
-    if variant not in ("self", "cross", "pma"):
+    if variant not in ("self", "cross", "pma", "sliding"):
         raise ValueError(variant)
-    if variant == "self" and not np.array_equal(qo, ko):
+    if variant in ("self", "sliding") and not np.array_equal(qo, ko):
         raise ValueError("self-attention needs identical query and key offsets")
-    if window and (variant != "self" or act != "softmax"):
+    if window and (variant not in ("self", "sliding") or act != "softmax"):
         raise ValueError("a window applies to softmax self-attention only")
+    if variant == "sliding" and (window < 1 or act != "softmax"):
+        raise ValueError("sliding-window attention needs window >= 1 and softmax")
     return qo, ko
 
 
@@ -124,7 +147,7 @@ def gdpa_forward(q, k, v, q_offsets, kv_offsets, variant: str = "self", act: str
         for h in range(q.shape[1]):
             out[qo[b]:qo[b + 1], h, :] = attention_dense(
                 q[qo[b]:qo[b + 1], h, :], k[ko[b]:ko[b + 1], h, :], v[ko[b]:ko[b + 1], h, :],
-                act, window, eps)
+                act, window, eps, variant)
     return out
 
 
@@ -150,7 +173,7 @@ def gdpa_rows(q, k, v, q_offsets, kv_offsets, rows, variant: str = "self", act: 
             s = (Qs @ Ks.T)[0] / math.sqrt(q.shape[2])
             res.append(gelu_tanh(s) @ Vs / lk)
             continue
-        allowed = block_window_allowed(Qs.shape[0], lk, window)[i]
+        allowed = allowed_keys(Qs.shape[0], lk, window, variant)[i]
         s = (Ks @ Qs[i]) / math.sqrt(q.shape[2])
         s = np.where(allowed, s, -np.inf)
         p = np.exp(s - s.max())
@@ -158,7 +181,7 @@ def gdpa_rows(q, k, v, q_offsets, kv_offsets, rows, variant: str = "self", act: 
     return np.array(res, dtype=np.float64).reshape(len(res), q.shape[2])
 
 
-def attended_pairs(q_offsets, kv_offsets, act: str = "softmax", window: int = 0) -> int:
+def attended_pairs(q_offsets, kv_offsets, act: str = "softmax", window: int = 0, variant: str = "self") -> int:
     """Number of (query, key) pairs that enter the output, per head:
     sum over samples of the allowed-mask population (dense count)."""
     qo = np.asarray(q_offsets, dtype=np.int64)
@@ -167,5 +190,5 @@ def attended_pairs(q_offsets, kv_offsets, act: str = "softmax", window: int = 0)
     for b in range(len(qo) - 1):
         lq, lk = int(qo[b + 1] - qo[b]), int(ko[b + 1] - ko[b])
         if lq and lk:
-            total += int(block_window_allowed(lq, lk, window).sum())
+            total += int(allowed_keys(lq, lk, window, variant).sum())
     return total
