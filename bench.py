@@ -38,6 +38,7 @@ KERNEL_NAME = {  # dominant kernel per workload (template instance)
     "cross_gelu": "attn_pp_kernel<128,gelu>",
     "pma": "attn_kernel<64,NWQ=1,NWK=4,softmax,bf16,split>",
     "mxfp8_window": "attn_kernel<128,NWQ=4,NWK=1,softmax,mx,window>",
+    "sliding_window": "attn_pp_kernel<128,softmax,sliding>",
 }
 
 
@@ -104,7 +105,7 @@ def cpu_baseline(w, budget_s: float):
         t0 = time.perf_counter()
         oracle.gdpa_forward(q, k, v, qo, ko, w.variant, w.act, w.window)
         spent += time.perf_counter() - t0
-        flops += wl.useful_flops([q1 - q0], [k1 - k0], w.H, w.D, w.window)
+        flops += wl.useful_flops([q1 - q0], [k1 - k0], w.H, w.D, w.window, w.variant)
         used.append(int(b))
         if spent >= budget_s:
             break
@@ -197,7 +198,7 @@ def main():
     alg_bytes = wl.compulsory_bytes(w.total_q, w.total_kv, w.H, w.D, in_bytes, out_bytes,
                                     mx_scales=w.dtype == "mxfp8")
     lq, lk = np.diff(w.q_offsets), np.diff(w.kv_offsets)
-    flops = wl.useful_flops(lq, lk, w.H, w.D, w.window)
+    flops = wl.useful_flops(lq, lk, w.H, w.D, w.window, w.variant)
     n_copies = int(max(2, min(8, math.ceil(args.rotate_bytes / max(alg_bytes, 1)))))
     sets = [(q, k, v, scales)]
     for _ in range(n_copies - 1):

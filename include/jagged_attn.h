@@ -23,6 +23,9 @@
  * attention over the sample's keys); scale 1/sqrt(D) everywhere; a window W>0
  * lets a query in 64-token block i see every key of blocks i-W/64+1 .. i, with
  * blocks counted from the sample's first token; Lk == 0 gives O == 0.
+ * JA_SLIDING is the token-level sliding window that block attention grew out
+ * of ("BlockAttention" section: O(L x window) self-attention): query i sees
+ * keys i-W+1 .. i, positions counted from the sample's first token.
  *
  * Layouts (all device memory, row-major, contiguous):
  *   q   [total_q , H, D]     k, v [total_kv, H, D]     out [total_q, H, D]
@@ -32,8 +35,9 @@
  *   per 32 contiguous elements along D), bfloat16 out.
  *   q_offsets, kv_offsets: device int32 [B+1], offsets[0] == 0, non-decreasing,
  *   offsets[B] == total_q / total_kv.  Sample b owns rows [off[b], off[b+1]).
- *   JA_SELF needs q_offsets and kv_offsets to hold the same values (the same
- *   pointer may be passed twice).  Buffers need 16-byte alignment.
+ *   JA_SELF and JA_SLIDING need q_offsets and kv_offsets to hold the same
+ *   values (the same pointer may be passed twice).  Buffers need 16-byte
+ *   alignment.
  *
  * Ownership.  The caller owns every buffer, including the workspace.  The
  * library allocates nothing inside jagged_attn_fwd and keeps only a per-device
@@ -62,8 +66,10 @@ extern "C" {
 enum ja_variant {
   JA_SELF = 0,  /* q and kv share offsets; optional block window            */
   JA_CROSS = 1, /* long queries, short keys/values: work split by q tiles    */
-  JA_PMA = 2    /* short queries (<=32 per sample), long keys/values: work
+  JA_PMA = 2,   /* short queries (<=32 per sample), long keys/values: work
                    split by key chunks, partial results merged on device      */
+  JA_SLIDING = 3 /* self-attention with a token sliding window: window = W >= 1
+                   keys ending at the query; JA_SOFTMAX, JA_F32 or JA_BF16     */
 };
 
 enum ja_act {
@@ -81,11 +87,13 @@ enum ja_status {
   JA_OK = 0,
   JA_EINVAL = -1,       /* bad argument (null pointer, B<1, H<1, bad enum...)  */
   JA_EUNSUPPORTED = -2, /* valid but not implemented (D not in {32,64,128},
-                           windowed GELU, window not a multiple of 64 ...)     */
+                           windowed GELU, window not a multiple of 64,
+                           JA_SLIDING with MXFP8 ...)                          */
   JA_EWORKSPACE = -3,   /* workspace missing or smaller than required         */
   JA_EHIP = -4,         /* a HIP runtime call or kernel launch failed         */
   JA_EOFFSETS = -5      /* device found offsets that are not monotone, do not
-                           start at 0, do not end at total, or (JA_SELF) differ */
+                           start at 0, do not end at total, or (JA_SELF,
+                           JA_SLIDING) differ                                  */
 };
 
 typedef struct ja_io {
@@ -107,7 +115,8 @@ typedef struct ja_io {
 } ja_io;
 
 /* The forward pass.  Arguments as described above; window is 0 (no window) or
- * a positive multiple of 64 (JA_SELF + JA_SOFTMAX only). */
+ * a positive multiple of 64 (JA_SELF + JA_SOFTMAX only), or for JA_SLIDING
+ * the window in tokens (>= 1, required). */
 int jagged_attn_fwd(const void *q, const void *k, const void *v,
                     const int32_t *q_offsets, const int32_t *kv_offsets,
                     int B, int H, int D, int variant, int act, int window,

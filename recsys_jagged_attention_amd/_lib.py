@@ -12,12 +12,12 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libjagged_attn.so")
 
-JA_SELF, JA_CROSS, JA_PMA = 0, 1, 2
+JA_SELF, JA_CROSS, JA_PMA, JA_SLIDING = 0, 1, 2, 3
 JA_SOFTMAX, JA_GELU_TANH, JA_GELU_POLY = 0, 1, 2
 JA_F32, JA_BF16, JA_MXFP8_E4M3 = 0, 1, 2
 JA_OK, JA_EINVAL, JA_EUNSUPPORTED, JA_EWORKSPACE, JA_EHIP, JA_EOFFSETS = 0, -1, -2, -3, -4, -5
 
-VARIANTS = {"self": JA_SELF, "cross": JA_CROSS, "pma": JA_PMA}
+VARIANTS = {"self": JA_SELF, "cross": JA_CROSS, "pma": JA_PMA, "sliding": JA_SLIDING}
 ACTS = {"softmax": JA_SOFTMAX, "gelu_tanh": JA_GELU_TANH, "gelu_poly": JA_GELU_POLY}
 DTYPES = {"f32": JA_F32, "bf16": JA_BF16, "mxfp8": JA_MXFP8_E4M3}
 

@@ -14,7 +14,7 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t st);
 hipError_t launch_attn_mfma(int D, int in, int shape, int act, const AttnArgs& a, int num_cu,
                             int64_t max_items, hipStream_t st);
 hipError_t launch_combine(int D, const CombineArgs& a, hipStream_t st);
-hipError_t launch_attn_f32(int D, int act, bool window, const AttnArgs& a, int grid, hipStream_t st);
+hipError_t launch_attn_f32(int D, int act, int window_mode, const AttnArgs& a, int grid, hipStream_t st);
 hipError_t launch_attn_pp(int D, int act, const AttnArgs& a, int num_cu, int64_t max_items, hipStream_t st);
 hipError_t launch_key_rms(int D, const void* k, int64_t rows, float eps, float* out, hipStream_t st);
 int pp_rows();
@@ -60,14 +60,19 @@ int choose_kvc(int H, int32_t total_kv) {
 int validate(int B, int H, int D, int variant, int act, int window, int dtype, int32_t total_q,
              int32_t total_kv) {
   if (B < 1 || H < 1 || total_q < 0 || total_kv < 0) return JA_EINVAL;
-  if (variant < JA_SELF || variant > JA_PMA) return JA_EINVAL;
+  if (variant < JA_SELF || variant > JA_SLIDING) return JA_EINVAL;
   if (act < JA_SOFTMAX || act > JA_GELU_POLY) return JA_EINVAL;
   if (dtype < JA_F32 || dtype > JA_MXFP8_E4M3) return JA_EINVAL;
   if (window < 0) return JA_EINVAL;
-  if (variant == JA_SELF && total_q != total_kv) return JA_EINVAL;
-  if (window > 0 && variant != JA_SELF) return JA_EINVAL;
+  if ((variant == JA_SELF || variant == JA_SLIDING) && total_q != total_kv) return JA_EINVAL;
+  if (variant == JA_SLIDING) {
+    if (window < 1) return JA_EINVAL;
+    if (act != JA_SOFTMAX || dtype == JA_MXFP8_E4M3) return JA_EUNSUPPORTED;
+  } else if (window > 0 && variant != JA_SELF) {
+    return JA_EINVAL;
+  }
   if (D != 32 && D != 64 && D != 128) return JA_EUNSUPPORTED;
-  if (window > 0 && (window % kBlock != 0 || act != JA_SOFTMAX)) return JA_EUNSUPPORTED;
+  if (variant == JA_SELF && window > 0 && (window % kBlock != 0 || act != JA_SOFTMAX)) return JA_EUNSUPPORTED;
   if (int64_t(B) * H > (int64_t(1) << 30) || H > 4096) return JA_EUNSUPPORTED;
   return JA_OK;
 }
@@ -178,8 +183,9 @@ int jagged_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
   pa.total_kv = io->total_kv;
   pa.bm = p.bm;
   pa.kvc = p.kvc;
-  pa.self_check = variant == JA_SELF;
-  pa.window_blocks = window / kBlock;
+  pa.self_check = variant == JA_SELF || variant == JA_SLIDING;
+  pa.window_blocks = variant == JA_SLIDING ? 0 : window / kBlock;
+  pa.window_tokens = variant == JA_SLIDING ? window : 0;
   pa.cost_order = p.shape == kShapePingPong;
   pa.max_items = p.ws.max_items;
   pa.max_slots = p.ws.max_slots;
@@ -206,7 +212,8 @@ int jagged_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
   aa.part_o = part_o;
   aa.part_ml = part_ml;
   aa.H = H;
-  aa.window_blocks = window / kBlock;
+  aa.window_blocks = variant == JA_SLIDING ? 0 : window / kBlock;
+  aa.window_tokens = variant == JA_SLIDING ? window : 0;
   aa.kvc = p.kvc;
   aa.eps = io->rms_eps > 0.f ? io->rms_eps : 1e-6f;
   aa.kscale = nullptr;
@@ -223,7 +230,7 @@ int jagged_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
     return JA_EHIP;
   hipError_t e;
   if (p.shape == kShapeF32) {
-    e = launch_attn_f32(D, act, window > 0, aa, grid, stream);
+    e = launch_attn_f32(D, act, variant == JA_SLIDING ? 2 : (window > 0 ? 1 : 0), aa, grid, stream);
   } else if (p.shape == kShapePingPong) {
     e = launch_attn_pp(D, act, aa, device_cus(), p.ws.max_items, stream);
 

@@ -8,8 +8,9 @@
 // path: softmax over the sample's keys (optionally the 64-token block window
 // of the "BlockAttention" section of the techfeed.io summary of "GEM
 // Training: How Meta Doubled the Efficiency of Its LLM-Scale Ads Foundation
-// Model"), or RMS-normalised GELU-tanh scores divided by the key count
-// (same page, "Generalized Dot-Product Attention（GDPA）").
+// Model", or the token sliding window it grew out of), or RMS-normalised
+// GELU-tanh scores divided by the key count (same page, "Generalized
+// Dot-Product Attention（GDPA）").
 #include "ja_device.h"
 #include "jagged_attn.h"
 
@@ -19,7 +20,8 @@ namespace {
 
 constexpr int kF32Rows = 64;  // query rows per work item (one wave)
 
-template <int D, int ACT, bool WINDOW>
+// WMODE: 0 all keys, 1 block window, 2 token sliding window.
+template <int D, int ACT, int WMODE>
 __global__ __launch_bounds__(kF32Rows) void attn_f32_kernel(AttnArgs a) {
   const int n_items = a.hdr->n_items;
   const float* qv = reinterpret_cast<const float*>(a.q);
@@ -48,10 +50,13 @@ __global__ __launch_bounds__(kF32Rows) void attn_f32_kernel(AttnArgs a) {
       rq = 1.0f / sqrtf(ss * (1.0f / D) + a.eps);
     }
     int lo = 0, hi = lk;
-    if constexpr (WINDOW) {
+    if constexpr (WMODE == 1) {
       const int blk = qrow / kBlock;
       lo = max(0, blk - a.window_blocks + 1) * kBlock;
       hi = min(lk, (blk + 1) * kBlock);
+    } else if constexpr (WMODE == 2) {
+      lo = max(0, qrow - a.window_tokens + 1);
+      hi = min(lk, qrow + 1);
     }
     float m = -__builtin_huge_valf(), l = 0.f;
     for (int j = lo; j < hi; ++j) {
@@ -98,24 +103,26 @@ __global__ __launch_bounds__(kF32Rows) void attn_f32_kernel(AttnArgs a) {
 }
 
 template <int D>
-hipError_t launch_d(int act, bool window, const AttnArgs& a, int grid, hipStream_t st) {
+hipError_t launch_d(int act, int window_mode, const AttnArgs& a, int grid, hipStream_t st) {
   if (act == ACT_GELU)
-    hipLaunchKernelGGL((attn_f32_kernel<D, ACT_GELU, false>), dim3(grid), dim3(kF32Rows), 0, st, a);
+    hipLaunchKernelGGL((attn_f32_kernel<D, ACT_GELU, 0>), dim3(grid), dim3(kF32Rows), 0, st, a);
   else if (act == ACT_GELU_POLY)
-    hipLaunchKernelGGL((attn_f32_kernel<D, ACT_GELU_POLY, false>), dim3(grid), dim3(kF32Rows), 0, st, a);
-  else if (window)
-    hipLaunchKernelGGL((attn_f32_kernel<D, ACT_SOFTMAX, true>), dim3(grid), dim3(kF32Rows), 0, st, a);
+    hipLaunchKernelGGL((attn_f32_kernel<D, ACT_GELU_POLY, 0>), dim3(grid), dim3(kF32Rows), 0, st, a);
+  else if (window_mode == 1)
+    hipLaunchKernelGGL((attn_f32_kernel<D, ACT_SOFTMAX, 1>), dim3(grid), dim3(kF32Rows), 0, st, a);
+  else if (window_mode == 2)
+    hipLaunchKernelGGL((attn_f32_kernel<D, ACT_SOFTMAX, 2>), dim3(grid), dim3(kF32Rows), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_f32_kernel<D, ACT_SOFTMAX, false>), dim3(grid), dim3(kF32Rows), 0, st, a);
+    hipLaunchKernelGGL((attn_f32_kernel<D, ACT_SOFTMAX, 0>), dim3(grid), dim3(kF32Rows), 0, st, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_attn_f32(int D, int act, bool window, const AttnArgs& a, int grid, hipStream_t st) {
-  if (D == 32) return launch_d<32>(act, window, a, grid, st);
-  if (D == 64) return launch_d<64>(act, window, a, grid, st);
-  return launch_d<128>(act, window, a, grid, st);
+hipError_t launch_attn_f32(int D, int act, int window_mode, const AttnArgs& a, int grid, hipStream_t st) {
+  if (D == 32) return launch_d<32>(act, window_mode, a, grid, st);
+  if (D == 64) return launch_d<64>(act, window_mode, a, grid, st);
+  return launch_d<128>(act, window_mode, a, grid, st);
 }
 
 }  // namespace ja

@@ -70,11 +70,15 @@ struct PP {
 
 // Position in the tile stream: tile t of the k-th item of this workgroup
 // (k == n: past the end), the end of the item's tiles and its key count.
-// Block windows: this wave computes tiles [wlo, whi] of the item.  Wave-uniform.
+// Windows: this wave computes tiles [wlo, whi] of the item, and its first
+// query row is r0 (sample-local).  Wave-uniform.
 struct Cur {
   int k, t, te, lk;
-  int wlo, whi;
+  int wlo, whi, r0;
 };
+
+// Window modes of the tile stream.
+enum { kWinNone = 0, kWinBlock = 1, kWinSliding = 2 };
 
 __device__ __forceinline__ int ntiles_of(int lk) { return (lk + 63) >> 6; }
 
@@ -157,20 +161,29 @@ __device__ __forceinline__ void write_zero_rows(const PPCtx& c, const WorkItem& 
 // from the sample's first token) an item covers the key tiles from nb - 1
 // blocks before its first query block to its last query block, and a wave
 // computes the tiles its own query block sees (techfeed.io summary of "GEM
-// Training: ...", section "BlockAttention").
-template <int D, bool WINDOW>
-__device__ __forceinline__ void advance(const PPCtx& c, Cur& cu, Src& src, int wave, int lane, int nb) {
+// Training: ...", section "BlockAttention").  With a sliding window of wt
+// tokens (query i sees keys i-wt+1 .. i) the tiles run from the one holding
+// key q0-wt+1 to the one holding the item's last query.
+template <int D, int WMODE>
+__device__ __forceinline__ void advance(const PPCtx& c, Cur& cu, Src& src, int wave, int lane, int nb, int wt) {
   if (cu.k >= c.n) return;
   if (++cu.t < cu.te) return;
   while (++cu.k < c.n) {
     const WorkItem w = load_record(c, cu.k);
     int t_lo = 0, t_end = ntiles_of(w.lk);
-    if constexpr (WINDOW) {
+    if constexpr (WMODE == kWinBlock) {
       t_lo = max(0, w.q0 / kBlock - nb + 1);
       t_end = min(t_end, (min(w.q0 + kPPRows, w.lq) + kBlock - 1) / kBlock);
       const int r0 = w.q0 + 32 * wave, wblk = r0 / kBlock;
       cu.wlo = wblk - nb + 1;
       cu.whi = r0 < w.lq ? wblk : -1;
+    } else if constexpr (WMODE == kWinSliding) {
+      t_lo = max(0, w.q0 - wt + 1) / kBlock;
+      t_end = min(t_end, (min(w.q0 + kPPRows, w.lq) + kBlock - 1) / kBlock);
+      const int r0 = w.q0 + 32 * wave;
+      cu.r0 = r0;
+      cu.wlo = max(0, r0 - wt + 1) / kBlock;
+      cu.whi = r0 < w.lq ? min(r0 + 31, w.lq - 1) / kBlock : -1;
     }
     if (t_end > t_lo) {
       cu.t = t_lo;
@@ -184,7 +197,7 @@ __device__ __forceinline__ void advance(const PPCtx& c, Cur& cu, Src& src, int w
   cu.t = 0;  // past the end: tile 0 of the last item visited
 }
 
-template <int D, int ACT, bool WINDOW>
+template <int D, int ACT, int WMODE>
 __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
   using K = PP<D, ACT>;
   constexpr int kQChunks = K::kQChunks, kOTiles = K::kOTiles, kRowBytes = K::kRowBytes;
@@ -220,17 +233,17 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
 
   // Stream cursors: tile s (scores), s+1, s+2 (being loaded); only the
   // loading cursor carries the addresses of its item.
-  const int nb = a.window_blocks;
-  Cur c0{-1, 0, 0, 0, 0, 0};
+  const int nb = a.window_blocks, wt = a.window_tokens;
+  Cur c0{-1, 0, 0, 0, 0, 0, 0};
   Src src{};
-  advance<D, WINDOW>(c, c0, src, wave, lane, nb);
+  advance<D, WMODE>(c, c0, src, wave, lane, nb, wt);
   if (c0.k >= c.n) return;
   const Src src0 = src;
   Cur c1 = c0;
-  advance<D, WINDOW>(c, c1, src, wave, lane, nb);
+  advance<D, WMODE>(c, c1, src, wave, lane, nb, wt);
   const Src src1 = src;
   Cur c2 = c1;
-  advance<D, WINDOW>(c, c2, src, wave, lane, nb);
+  advance<D, WMODE>(c, c2, src, wave, lane, nb, wt);
 
   // Loads of the loading cursor's tile into ring stage `st`.  Job j moves 1 KB
   // segment wave + 8j of K|V; rows of a ragged tile are clamped to its last key.
@@ -315,9 +328,11 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
   bool pv_last = false;
   bool pv_act = true;  // this wave computed tile s-1 (block windows)
   int pv_nvalid = 64;  // keys of tile s-1 inside its sample
+  int pv_key0 = 0, pv_r0 = 0;  // sliding window: tile s-1's first key, this wave's first row
 
-  // Softmax / GELU of the score tile `sc` (nvalid keys), written to pb as bf16.
-  auto vphase = [&](int nvalid, int stage) __attribute__((always_inline)) {
+  // Softmax / GELU of the score tile `sc` (nvalid keys; sliding window: keys
+  // key0.. of the tile against rows r0.. of this wave), written to pb as bf16.
+  auto vphase = [&](int nvalid, int stage, int key0, int r0) __attribute__((always_inline)) {
     const bool ragged = nvalid < 64;
     if constexpr (ACT == ACT_SOFTMAX) {
       if (ragged) {
@@ -328,6 +343,21 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
             const int kk = 32 * st + 16 * (i >> 3) + 8 * g + (i & 7);
             if (kk >= nvalid) sc[st][i] = -__builtin_huge_valf();
           }
+      }
+      if constexpr (WMODE == kWinSliding) {
+        // key j is allowed for row i when i - wt < j <= i; only a tile that
+        // reaches past the wave's first row or before its last row's window
+        // start has disallowed keys
+        if (key0 + 63 > r0 || key0 <= r0 + 31 - wt) {
+          const int row = r0 + l32;
+#pragma unroll
+          for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int j = key0 + 32 * st + 16 * (i >> 3) + 8 * g + (i & 7);
+              if (j > row || j <= row - wt) sc[st][i] = -__builtin_huge_valf();
+            }
+        }
       }
       // p = 2^(s c - m c) into pb; returns this lane's sum of the bf16 p
       // (the weights P V uses), two at a time on the dot unit.
@@ -350,6 +380,8 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
       // otherwise (and on an item's first tile) the tile's max is found, m
       // moves up to it, O and l are rescaled and the exponentials are taken
       // again.  Softmax is unchanged by the choice of reference.
+      // (a row may have no allowed key yet -- a sliding window's first tiles
+      // -- and keeps m = -inf; its exponentials are then taken against 0)
       const bool fresh = __any(m == -__builtin_huge_valf());
       float part = 0.f;
       if (!fresh) part = exps(m * c2s);
@@ -368,7 +400,7 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
         m = m_new;
-        part = exps(m * c2s);
+        part = exps(m == -__builtin_huge_valf() ? 0.f : m * c2s);
       }
       l += part;
     } else {
@@ -428,13 +460,13 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
 
     // ---- late waves' VALU phase, then O += V_{s-1} P_{s-1}.
     auto head = [&]() __attribute__((always_inline)) {
-      if (late && s > 0 && pv_act) vphase(pv_nvalid, st_prev);
+      if (late && s > 0 && pv_act) vphase(pv_nvalid, st_prev, pv_key0, pv_r0);
       // The MFMA phase runs at raised wave priority: the SIMD's other wave is
       // in its VALU phase, and the matrix core should get the next MFMA as
       // soon as it can take one.
       __builtin_amdgcn_s_setprio(2);
       if (s > 0) {
-        if (!WINDOW || pv_act) {
+        if (WMODE == kWinNone || pv_act) {
           // 4*kOTiles MFMAs (16-key chunk kc, output tile t), the V^T operand
           // read kAhead MFMAs early: one wave issues them alone, so the LDS
           // transpose-read latency is not hidden by a second wave.
@@ -495,7 +527,7 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
     // Loads of tile s+2 (into the stage that held tile s-2, last read in the
     // previous step): between the MFMAs of the second score half, or all at
     // once for a wave that skips the tile.
-    const bool act = !WINDOW || (c0.t >= c0.wlo && c0.t <= c0.whi);  // this wave computes tile s
+    const bool act = WMODE == kWinNone || (c0.t >= c0.wlo && c0.t <= c0.whi);  // this wave computes tile s
     if (!act) {
 #pragma unroll
       for (int j = 0; j < K::kDmaJobs; ++j) tile_job(c2, src, st_pf, j);
@@ -536,14 +568,16 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
     __builtin_amdgcn_s_setprio(0);
     const bool s_last = c0.t == c0.te - 1;
     const int nvalid = min(64, c0.lk - 64 * c0.t);
-    if (!late && act) vphase(nvalid, st_s);
+    if (!late && act) vphase(nvalid, st_s, 64 * c0.t, c0.r0);
     pv_k = c0.k;
     pv_act = act;
     pv_last = s_last;
     pv_nvalid = nvalid;
+    pv_key0 = 64 * c0.t;
+    pv_r0 = c0.r0;
     c0 = c1;
     c1 = c2;
-    advance<D, WINDOW>(c, c2, src, wave, lane, nb);
+    advance<D, WMODE>(c, c2, src, wave, lane, nb, wt);
   }
 }
 
@@ -559,22 +593,26 @@ hipError_t launch_attn_pp(int D, int act, const AttnArgs& a, int num_cu, int64_t
   grid = (grid / kXcds) * kXcds;
   if (grid < kXcds) grid = kXcds;
   const dim3 gd(static_cast<unsigned>(grid)), bd(64 * kPPWaves);
-  if (a.window_blocks > 0) {  // (softmax only)
-    if (D == 32) hipLaunchKernelGGL((attn_pp_kernel<32, ACT_SOFTMAX, true>), gd, bd, 0, st, a);
-    else if (D == 64) hipLaunchKernelGGL((attn_pp_kernel<64, ACT_SOFTMAX, true>), gd, bd, 0, st, a);
-    else hipLaunchKernelGGL((attn_pp_kernel<128, ACT_SOFTMAX, true>), gd, bd, 0, st, a);
+  if (a.window_tokens > 0) {  // (softmax only)
+    if (D == 32) hipLaunchKernelGGL((attn_pp_kernel<32, ACT_SOFTMAX, kWinSliding>), gd, bd, 0, st, a);
+    else if (D == 64) hipLaunchKernelGGL((attn_pp_kernel<64, ACT_SOFTMAX, kWinSliding>), gd, bd, 0, st, a);
+    else hipLaunchKernelGGL((attn_pp_kernel<128, ACT_SOFTMAX, kWinSliding>), gd, bd, 0, st, a);
+  } else if (a.window_blocks > 0) {  // (softmax only)
+    if (D == 32) hipLaunchKernelGGL((attn_pp_kernel<32, ACT_SOFTMAX, kWinBlock>), gd, bd, 0, st, a);
+    else if (D == 64) hipLaunchKernelGGL((attn_pp_kernel<64, ACT_SOFTMAX, kWinBlock>), gd, bd, 0, st, a);
+    else hipLaunchKernelGGL((attn_pp_kernel<128, ACT_SOFTMAX, kWinBlock>), gd, bd, 0, st, a);
   } else if (act == ACT_SOFTMAX) {
-    if (D == 32) hipLaunchKernelGGL((attn_pp_kernel<32, ACT_SOFTMAX, false>), gd, bd, 0, st, a);
-    else if (D == 64) hipLaunchKernelGGL((attn_pp_kernel<64, ACT_SOFTMAX, false>), gd, bd, 0, st, a);
-    else hipLaunchKernelGGL((attn_pp_kernel<128, ACT_SOFTMAX, false>), gd, bd, 0, st, a);
+    if (D == 32) hipLaunchKernelGGL((attn_pp_kernel<32, ACT_SOFTMAX, kWinNone>), gd, bd, 0, st, a);
+    else if (D == 64) hipLaunchKernelGGL((attn_pp_kernel<64, ACT_SOFTMAX, kWinNone>), gd, bd, 0, st, a);
+    else hipLaunchKernelGGL((attn_pp_kernel<128, ACT_SOFTMAX, kWinNone>), gd, bd, 0, st, a);
   } else if (act == ACT_GELU_POLY) {
-    if (D == 32) hipLaunchKernelGGL((attn_pp_kernel<32, ACT_GELU_POLY, false>), gd, bd, 0, st, a);
-    else if (D == 64) hipLaunchKernelGGL((attn_pp_kernel<64, ACT_GELU_POLY, false>), gd, bd, 0, st, a);
-    else hipLaunchKernelGGL((attn_pp_kernel<128, ACT_GELU_POLY, false>), gd, bd, 0, st, a);
+    if (D == 32) hipLaunchKernelGGL((attn_pp_kernel<32, ACT_GELU_POLY, kWinNone>), gd, bd, 0, st, a);
+    else if (D == 64) hipLaunchKernelGGL((attn_pp_kernel<64, ACT_GELU_POLY, kWinNone>), gd, bd, 0, st, a);
+    else hipLaunchKernelGGL((attn_pp_kernel<128, ACT_GELU_POLY, kWinNone>), gd, bd, 0, st, a);
   } else {
-    if (D == 32) hipLaunchKernelGGL((attn_pp_kernel<32, ACT_GELU, false>), gd, bd, 0, st, a);
-    else if (D == 64) hipLaunchKernelGGL((attn_pp_kernel<64, ACT_GELU, false>), gd, bd, 0, st, a);
-    else hipLaunchKernelGGL((attn_pp_kernel<128, ACT_GELU, false>), gd, bd, 0, st, a);
+    if (D == 32) hipLaunchKernelGGL((attn_pp_kernel<32, ACT_GELU, kWinNone>), gd, bd, 0, st, a);
+    else if (D == 64) hipLaunchKernelGGL((attn_pp_kernel<64, ACT_GELU, kWinNone>), gd, bd, 0, st, a);
+    else hipLaunchKernelGGL((attn_pp_kernel<128, ACT_GELU, kWinNone>), gd, bd, 0, st, a);
   }
   return hipGetLastError();
 }

@@ -70,6 +70,7 @@ struct PlanArgs {
   int32_t total_q, total_kv;
   int bm, kvc, self_check;
   int window_blocks;   // 0 = no window (used for the per-item cost estimate)
+  int window_tokens;   // sliding window in tokens (0 = none)
   int cost_order;      // 1: items sorted by key tiles, most first (xcd_begin unused)
   int64_t max_items, max_slots;
   WsHeader* hdr;
@@ -97,6 +98,7 @@ struct AttnArgs {
   const float* kscale;  // RMS factor per key row and head (ping-pong GELU), else null
   int H;
   int window_blocks;  // 0 = no window
+  int window_tokens;  // sliding window in tokens (0 = none)
   int kvc;
   float score_scale;  // softmax: log2(e)/sqrt(D); GELU: 1/sqrt(D)
   float eps;

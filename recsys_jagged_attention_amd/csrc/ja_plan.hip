@@ -32,6 +32,7 @@ constexpr int kCostBuckets = kPlanThreads;  // cost order: bucket = key tiles, c
 __device__ inline int cost_bucket(const PlanArgs& a, int lk) {
   int t = (lk + kBlock - 1) / kBlock;
   if (a.window_blocks > 0) t = min(t, a.window_blocks + a.bm / kBlock - 1);
+  if (a.window_tokens > 0) t = min(t, (a.window_tokens + a.bm - 2) / kBlock + 2);
   return min(t, kCostBuckets - 1);
 }
 
@@ -85,6 +86,7 @@ __device__ inline SampleWork sample_work(const PlanArgs& a, int lq, int lk) {
   int keys = lk;
   if (w.ns > 1) keys = a.kvc;
   if (a.window_blocks > 0) keys = min(lk, a.window_blocks * kBlock);
+  if (a.window_tokens > 0) keys = min(lk, a.window_tokens + a.bm - 1);
   w.ck = double(keys) + 64.0;
   return w;
 }

@@ -106,7 +106,7 @@ def mx_encode_e4m3(x: np.ndarray):
 @dataclasses.dataclass
 class Workload:
     name: str
-    variant: str            # "self" | "cross" | "pma"
+    variant: str            # "self" | "cross" | "pma" | "sliding"
     act: str                # "softmax" | "gelu_tanh"
     dtype: str              # "f32" | "bf16" | "mxfp8"
     B: int
@@ -130,9 +130,9 @@ class Workload:
         return int(self.kv_offsets[-1])
 
 
-WORKLOADS = ("tiny_full", "block_window", "full_self", "cross_gelu", "pma", "mxfp8_window")
+WORKLOADS = ("tiny_full", "block_window", "full_self", "cross_gelu", "pma", "mxfp8_window", "sliding_window")
 DEFAULT_SEED = {"tiny_full": 1001, "block_window": 1002, "full_self": 1002,
-                "cross_gelu": 1003, "pma": 1004, "mxfp8_window": 1002}
+                "cross_gelu": 1003, "pma": 1004, "mxfp8_window": 1002, "sliding_window": 1002}
 
 
 def make_workload(name: str, seed: Optional[int] = None, scale: float = 1.0) -> Workload:
@@ -152,7 +152,7 @@ def make_workload(name: str, seed: Optional[int] = None, scale: float = 1.0) -> 
         k = normal_values(rng, int(off[-1]), H, D)
         v = normal_values(rng, int(off[-1]), H, D)
         return Workload(name, "self", "softmax", "f32", B, H, D, 0, off, off, q, k, v, seed)
-    if name in ("block_window", "full_self", "mxfp8_window"):
+    if name in ("block_window", "full_self", "mxfp8_window", "sliding_window"):
         B, H, D = nb(64), 8, 128
         L = lengths_loguniform(rng, B, 100, 4096)
         off = offsets_from_lengths(L)
@@ -160,9 +160,10 @@ def make_workload(name: str, seed: Optional[int] = None, scale: float = 1.0) -> 
         q = normal_values(rng, n, H, D)
         k = normal_values(rng, n, H, D)
         v = normal_values(rng, n, H, D)
-        window = 0 if name == "full_self" else 256
+        window = 0 if name == "full_self" else 256  # (sliding_window: 256 tokens)
         dtype = "mxfp8" if name == "mxfp8_window" else "bf16"
-        w = Workload(name, "self", "softmax", dtype, B, H, D, window, off, off, q, k, v, seed)
+        variant = "sliding" if name == "sliding_window" else "self"
+        w = Workload(name, variant, "softmax", dtype, B, H, D, window, off, off, q, k, v, seed)
         if dtype == "mxfp8":
             w.mx = {}
             for nm, x in (("q", q), ("k", k), ("v", v)):

@@ -13,10 +13,15 @@ import numpy as np
 BLOCK = 64
 
 
-def attended_pairs(lq, lk, window: int = 0) -> int:
-    """Pairs per head for samples with query lengths lq and key lengths lk."""
+def attended_pairs(lq, lk, window: int = 0, variant: str = "self") -> int:
+    """Pairs per head for samples with query lengths lq and key lengths lk
+    (sliding: query i of a sample sees min(i + 1, window) keys)."""
     lq = np.asarray(lq, dtype=np.int64)
     lk = np.asarray(lk, dtype=np.int64)
+    if variant == "sliding":
+        w = int(window)
+        n = np.minimum(lq, w)
+        return int(np.sum(n * (n + 1) // 2 + (lq - n) * w))
     if window == 0:
         return int(np.sum(lq * lk))
     nb = window // BLOCK
@@ -32,8 +37,8 @@ def attended_pairs(lq, lk, window: int = 0) -> int:
     return total
 
 
-def useful_flops(lq, lk, H: int, D: int, window: int = 0) -> int:
-    return 4 * D * H * attended_pairs(lq, lk, window)
+def useful_flops(lq, lk, H: int, D: int, window: int = 0, variant: str = "self") -> int:
+    return 4 * D * H * attended_pairs(lq, lk, window, variant)
 
 
 def compulsory_bytes(total_q: int, total_kv: int, H: int, D: int, in_bytes: float,

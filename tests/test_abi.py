@@ -48,7 +48,14 @@ def test_workspace_size_rejects_bad_arguments():
     assert ws(4, 2, 32, 1, 0, 64, 0, 100, 100) == 0                # window on cross
     assert ws(4, 2, 32, 0, 1, 64, 0, 100, 100) == 0                # windowed GELU
     assert ws(4, 2, 32, 0, 0, 0, 0, 100, 99) == 0                  # self with different totals
-    assert ws(4, 2, 32, 3, 0, 0, 0, 100, 100) == 0                 # bad variant
+    assert ws(4, 2, 32, 4, 0, 0, 0, 100, 100) == 0                 # bad variant
+    sl = _lib.JA_SLIDING
+    assert ws(4, 2, 32, sl, 0, 100, _lib.JA_BF16, 100, 100) > 0     # sliding window, any W >= 1
+    assert ws(4, 2, 32, sl, 0, 1, _lib.JA_F32, 100, 100) > 0
+    assert ws(4, 2, 32, sl, 0, 0, _lib.JA_BF16, 100, 100) == 0      # sliding needs W >= 1
+    assert ws(4, 2, 32, sl, 1, 64, _lib.JA_BF16, 100, 100) == 0     # sliding GELU
+    assert ws(4, 2, 32, sl, 0, 64, _lib.JA_MXFP8_E4M3, 100, 100) == 0  # sliding MXFP8
+    assert ws(4, 2, 32, sl, 0, 64, _lib.JA_BF16, 100, 99) == 0      # sliding needs self offsets
     assert ws(4, 2, 32, 0, 0, 0, 7, 100, 100) == 0                 # bad dtype
 
 
@@ -80,6 +87,8 @@ def test_fwd_host_validation():
     assert call(variant=_lib.JA_CROSS, window=64) == _lib.JA_EINVAL
     assert call(act=_lib.JA_GELU_TANH, window=64) == _lib.JA_EUNSUPPORTED
     assert call(tq=10, tk=11) == _lib.JA_EINVAL
+    assert call(variant=_lib.JA_SLIDING) == _lib.JA_EINVAL            # window 0
+    assert call(variant=_lib.JA_SLIDING, window=5, act=_lib.JA_GELU_TANH) == _lib.JA_EUNSUPPORTED
     assert call(ptr=0) == _lib.JA_EINVAL
     assert call(dtype=_lib.JA_MXFP8_E4M3) == _lib.JA_EINVAL          # scales missing
     assert call(ws_bytes=16) == _lib.JA_EWORKSPACE

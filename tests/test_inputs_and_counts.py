@@ -51,3 +51,13 @@ def test_attended_pairs_count():
         assert wl.attended_pairs(np.diff(off), np.diff(off), w) == n
     qo, ko = offsets_from_lengths([3, 0, 5]), offsets_from_lengths([7, 2, 0])
     assert wl.attended_pairs(np.diff(qo), np.diff(ko), 0) == attended_pairs(qo, ko) == 21
+
+
+def test_sliding_pairs_count():
+    """The closed form for the sliding window against a brute-force count."""
+    L = [1, 5, 64, 300, 0]
+    off = offsets_from_lengths(L)
+    for w in (1, 7, 64, 256, 1000):
+        n = sum(1 for Ls in L for i in range(Ls) for j in range(Ls) if i - w < j <= i)
+        assert wl.attended_pairs(np.diff(off), np.diff(off), w, "sliding") == n
+        assert attended_pairs(off, off, "softmax", w, "sliding") == n

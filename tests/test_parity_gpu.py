@@ -34,7 +34,7 @@ def adhoc(name, variant, act, dtype, lq, lk, H, D, window=0, seed=0):
 
 @pytest.mark.parametrize("name,scale", [
     ("tiny_full", 1.0), ("block_window", 0.1), ("full_self", 0.06),
-    ("cross_gelu", 0.04), ("pma", 0.06), ("mxfp8_window", 0.1)])
+    ("cross_gelu", 0.04), ("pma", 0.06), ("mxfp8_window", 0.1), ("sliding_window", 0.1)])
 def test_workload_small_full_parity(name, scale):
     w = make_workload(name, scale=scale)
     log(f"parity {name} scale={scale} B={w.B} Nq={w.total_q} Nk={w.total_kv}")
@@ -42,7 +42,8 @@ def test_workload_small_full_parity(name, scale):
     log(f"  rel err {err:.3e}")
 
 
-@pytest.mark.parametrize("name", ["block_window", "cross_gelu", "pma", "mxfp8_window", "full_self"])
+@pytest.mark.parametrize("name", ["block_window", "cross_gelu", "pma", "mxfp8_window", "full_self",
+                                  "sliding_window"])
 def test_workload_full_size_sampled(name):
     w = make_workload(name)
     log(f"full-size {name} B={w.B} Nq={w.total_q} Nk={w.total_kv}")
@@ -154,6 +155,25 @@ def test_many_items_per_workgroup(act):
     log(f"many items {act}: B={B} H=80 Nq={w.total_q} Nk={w.total_kv}")
     out = run_gpu(w)
     sampled_parity(w, out, n=160)
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 32), ("bf16", 64), ("bf16", 128), ("f32", 32), ("f32", 128)])
+@pytest.mark.parametrize("window", [1, 17, 64, 100, 300])
+def test_sliding_window_edges(dtype, D, window):
+    """Token sliding window (query i sees keys i-W+1 .. i): W = 1 (own key
+    only), W shorter and longer than a tile and an item, ragged lengths."""
+    L = EDGE_LENGTHS + [300, 520]
+    w = adhoc("sliding_edges", "sliding", "softmax", dtype, L, L, 2, D, window=window, seed=window + D + 5)
+    log(f"sliding edges {dtype} D={D} W={window}")
+    full_parity(w)
+
+
+@pytest.mark.parametrize("window", [64, 200, 1000])
+def test_sliding_window_long_samples(window):
+    L = [1500, 2049, 700, 64, 3001, 257]
+    w = adhoc("sliding_long", "sliding", "softmax", "bf16", L, L, 2, 128, window=window, seed=window + 9)
+    log(f"sliding long W={window}: N={w.total_q}")
+    full_parity(w)
 
 
 @pytest.mark.parametrize("window", [64, 256, 1024])
