@@ -62,3 +62,57 @@ def test_mx_dequantise_applies_scale_per_32_along_d():
     y = mx_dequantise(codes, scales)
     np.testing.assert_array_equal(y[0, 0, :32], 8.0)
     np.testing.assert_array_equal(y[0, 0, 32:], 0.25)
+
+
+# ---- encoder ---------------------------------------------------------------
+from oracle import encode_e4m3, mx_encode
+
+
+def test_e4m3_encode_matches_library_cast():
+    """Nearest e4m3fn value, ties to even: torch's float8_e4m3fn cast on float32
+    (a library routine) for values on, between and halfway between grid points."""
+    grid = decode_e4m3(np.arange(127, dtype=np.uint8))
+    mids = (grid[1:] + grid[:-1]) / 2
+    rng = np.random.default_rng(3)
+    vals = np.concatenate([grid, mids, rng.uniform(0, 448, 4000), rng.uniform(0, 2 ** -6, 500)])
+    vals = np.concatenate([vals, -vals]).astype(np.float32)
+    ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = encode_e4m3(vals)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_e4m3_encode_saturates_and_closed_forms():
+    assert encode_e4m3([448.0, 449.0, 1e9, -1e9]).tolist() == [0x7E, 0x7E, 0x7E, 0xFE]
+    assert encode_e4m3([0.0, 1.0, 2 ** -9, 3 * 2 ** -10]).tolist() == [0, 0x38, 1, 2]   # 1.5 ulp -> 2 (even)
+    assert encode_e4m3([1.0625]).tolist() == [0x38]      # halfway 1 and 1.125: even mantissa 0
+    assert encode_e4m3([1.1875]).tolist() == [0x3A]      # halfway 1.125 and 1.25: even mantissa 2
+
+
+def test_mx_encode_scale_rule_and_round_trip():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((7, 3, 64)) * np.exp2(rng.integers(-20, 20, (7, 3, 1)))
+    x[0, 0, :32] = 0.0                                   # all-zero block
+    x[1, 1, :32] = 0.0
+    x[1, 1, 5] = 2.0 ** -130                              # tiny block
+    x[2, 2, 32:] = 1.0
+    x[2, 2, 40] = 448.0 * 2 ** 3                          # amax 3584 = 1.75 * 2^11 -> E = 3
+    codes, scales = mx_encode(x)
+    assert scales[0, 0, 0] == 0 and not codes[0, 0, :32].any()
+    assert scales[1, 1, 0] == 0                           # E clamped to -127
+    assert scales[2, 2, 1] == 127 + 3
+    # the scale puts the block max in [2^8, 2^9): elements up to 448 steps are
+    # within half an e4m3 step (relative 2^-4, or half the subnormal step),
+    # larger ones saturate to +-448 steps
+    xr = mx_dequantise(codes, scales)
+    sc = np.repeat(np.exp2(scales.astype(np.float64) - 127), 32, axis=-1)
+    inside = np.abs(x) <= 448 * sc
+    err = np.abs(xr - x)
+    assert np.all(err[inside] <= np.maximum(np.abs(x) * 2 ** -4, sc * 2 ** -10)[inside])
+    np.testing.assert_array_equal(xr[~inside], np.sign(x[~inside]) * 448 * sc[~inside])
+    assert (~inside).any()
+    # and the oracle encoder agrees with the input generator's (torch-cast) encoder
+    from recsys_jagged_attention_amd.inputs import mx_encode_e4m3
+    c2, s2 = mx_encode_e4m3(x.astype(np.float32))
+    c1, s1 = mx_encode(x.astype(np.float32))
+    np.testing.assert_array_equal(c1, c2)
+    np.testing.assert_array_equal(s1, s2)
