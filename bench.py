@@ -55,6 +55,7 @@ class HipEvents:
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     def create(self) -> int:
         e = ctypes.c_void_p()
@@ -70,6 +71,10 @@ class HipEvents:
 
     def destroy(self, e: int):
         self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+    def record(self, e: int, stream: int):
+        if self.hip.hipEventRecord(ctypes.c_void_p(e), ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
 
 def blas_threads() -> int:
@@ -145,6 +150,89 @@ def load_traffic(kernel_tag: str, workload: str):
         return None
 
 
+def run_mx_quantize(args):
+    """Time the device MX quantiser on the block-window tensors (q, k, v in bf16,
+    three launches per step) and print one JSON line in GB/s of compulsory
+    bytes (2 read + 1 written per element, plus one scale byte per 32)."""
+    import torch
+
+    from recsys_jagged_attention_amd import mx_quantize
+    from recsys_jagged_attention_amd.inputs import make_workload
+
+    w = make_workload("block_window", seed=args.seed)
+    dev = torch.device("cuda:0")
+    xs = [torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in (w.q, w.k, w.v)]
+    n_el = sum(x.numel() for x in xs)
+    alg_bytes = n_el * 2 + n_el + n_el // 32
+    n_copies = int(max(2, min(8, math.ceil(args.rotate_bytes / alg_bytes))))
+    sets = [xs] + [[x.clone() for x in xs] for _ in range(n_copies - 1)]
+    outs = [[(torch.empty(x.shape, dtype=torch.uint8, device=dev),
+              torch.empty(x.shape[:-1] + (x.shape[-1] // 32,), dtype=torch.uint8, device=dev)) for x in xs]
+            for _ in range(n_copies)]
+    from recsys_jagged_attention_amd import _lib
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def step(i):
+        for x, (c, sc) in zip(sets[i % n_copies], outs[i % n_copies]):
+            st = _lib.jagged_attn_mx_quantize(x.data_ptr(), _lib.JA_BF16, x.numel() // x.shape[-1], x.shape[-1],
+                                              c.data_ptr(), sc.data_ptr(), stream)
+            if st != _lib.JA_OK:
+                raise _lib.JaggedAttnError(st, "jagged_attn_mx_quantize")
+
+    mx_quantize(xs[0])
+    ev = HipEvents()
+    K, W = args.steps, args.warmup
+    starts = [ev.create() for _ in range(K)]
+    stops = [ev.create() for _ in range(K)]
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev.record(starts[i], stream)
+        step(i)
+        ev.record(stops[i], stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern_s = float(np.mean([ev.elapsed_ms(starts[i], stops[i]) for i in range(K)])) * 1e-3
+    for e in starts + stops:
+        ev.destroy(e)
+    ms_per_step = (t1 - t0) * 1e3 / K
+    value = alg_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = alg_bytes / kern_s / 1e9
+    log(f"[bench] mx quantise: {ms_per_step * 1e3:.1f} us/step, kernels {kern_s * 1e6:.1f} us, "
+        f"{achieved:.0f} GB/s ({100 * achieved / PEAK_HBM_GBS:.1f}% of HBM)")
+    cpu = None
+    if not args.no_cpu_baseline:
+        import os as _os
+        import oracle
+        rows = w.q.reshape(-1, w.D)
+        n = min(len(rows), 20000)
+        t = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t < min(args.cpu_seconds, 10.0) or reps == 0:
+            oracle.mx_encode(rows[:n].astype(np.float64))
+            reps += 1
+        dt = time.perf_counter() - t
+        cpu = {"value": round(reps * n * w.D * (2 + 1 + 1 / 32) / dt / 1e9, 4), "unit": "GB/s",
+               "cores": len(_os.sched_getaffinity(0)), "kind": "oracle",
+               "sample": f"{n} rows of D={w.D} (block_window q), repeated {reps}x"}
+    line = {
+        "metric": "MX quantisation throughput (bf16 -> e4m3 + E8M0 per 32 along D), 1 MI355X",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "mx_quantize", "tensors": "block_window q, k, v", "elements": int(n_el),
+                   "D": w.D, "seed": w.seed},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "mx_quant_kernel<bf16>", "kernel_avg_us": round(kern_s * 1e6, 2),
+                     "algorithmic_bytes_per_launch": int(alg_bytes)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -159,7 +247,15 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 5 times (the reference "
                          "for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE counters) and exit")
+    ap.add_argument("--mx-quantize", action="store_true",
+                    help="time the device MX quantiser instead of the attention forward")
     args = ap.parse_args()
+
+    if args.mx_quantize:
+        if args.gpus != 1:
+            raise SystemExit("bench.py measures one GPU only")
+        run_mx_quantize(args)
+        return
 
     if args.copy_calibration:
         import torch

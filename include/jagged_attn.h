@@ -128,6 +128,23 @@ size_t jagged_attn_workspace_size(int B, int H, int D, int variant, int act,
                                   int window, int dtype, int32_t total_q,
                                   int32_t total_kv);
 
+/* MX quantisation on the device ("MXFP8による超低精度トレーニング" section:
+ * attention on microscaling FP8 inputs; the page gives no encoding rule, the
+ * one used is stated here).  x holds `rows` rows of D values, row-major and
+ * contiguous (for attention inputs rows = tokens x heads), as float32
+ * (dtype JA_F32) or bfloat16 (JA_BF16).  Writes codes [rows, D] (e4m3 "fn"
+ * bytes) and scales [rows, D/32] (E8M0 bytes): per 32 contiguous elements of a
+ * row, E = floor(log2(max |x|)) - 8 clamped to [-127, 127] (-127 for an
+ * all-zero block), scale byte E + 127, and each code the e4m3 value nearest
+ * to x / 2^E (ties to even) after saturating to +-448; NaN inputs are not
+ * supported.  The output is the exact input of jagged_attn_fwd with
+ * JA_MXFP8_E4M3.  All pointers are device memory owned by the caller, 16-byte
+ * aligned; nothing is allocated.  Asynchronous on `stream` (a hipStream_t or
+ * NULL).  Returns JA_OK, JA_EINVAL (null or misaligned pointer, rows < 0, D not
+ * a positive multiple of 32, dtype not JA_F32/JA_BF16) or JA_EHIP. */
+int jagged_attn_mx_quantize(const void *x, int dtype, int64_t rows, int D,
+                            uint8_t *codes, uint8_t *scales, void *stream);
+
 /* Synchronises `stream` (a hipStream_t or NULL) and returns the device status
  * word the last jagged_attn_fwd on this workspace wrote: JA_OK or
  * JA_EOFFSETS; JA_EHIP / JA_EINVAL if it cannot be read. */

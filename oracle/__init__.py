@@ -18,8 +18,8 @@ oracle computes exact gelu_tanh only.
 """
 from .gdpa import (gdpa_forward, gdpa_rows, gelu_tanh, rms_normalise,
                    block_window_allowed, sliding_window_allowed, attention_dense, attended_pairs)
-from .mx import decode_e4m3, decode_e8m0, mx_dequantise, encode_e4m3, mx_encode
+from .mx import decode_e4m3, decode_e8m0, mx_dequantise, encode_e4m3, mx_encode, e4m3_grid
 
 __all__ = ["gdpa_forward", "gdpa_rows", "gelu_tanh", "rms_normalise",
            "block_window_allowed", "sliding_window_allowed", "attention_dense", "attended_pairs",
-           "decode_e4m3", "decode_e8m0", "mx_dequantise", "encode_e4m3", "mx_encode"]
+           "decode_e4m3", "decode_e8m0", "mx_dequantise", "encode_e4m3", "mx_encode", "e4m3_grid"]

@@ -23,7 +23,7 @@ DTYPES = {"f32": JA_F32, "bf16": JA_BF16, "mxfp8": JA_MXFP8_E4M3}
 
 # Every function the header declares (checked by the CPU tests).
 EXPORTS = ("jagged_attn_fwd", "jagged_attn_workspace_size", "jagged_attn_check",
-           "jagged_attn_strerror", "jagged_attn_version")
+           "jagged_attn_strerror", "jagged_attn_version", "jagged_attn_mx_quantize")
 
 
 class JaIo(ctypes.Structure):
@@ -71,6 +71,9 @@ def load() -> ctypes.CDLL:
         lib.jagged_attn_strerror.argtypes = [ctypes.c_int]
         lib.jagged_attn_version.restype = ctypes.c_int
         lib.jagged_attn_version.argtypes = []
+        lib.jagged_attn_mx_quantize.restype = ctypes.c_int
+        lib.jagged_attn_mx_quantize.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         _LIB = lib
     return _LIB
 
@@ -95,3 +98,7 @@ def jagged_attn_fwd(q, k, v, q_offsets, kv_offsets, B, H, D, variant, act, windo
 
 def jagged_attn_check(workspace, stream) -> int:
     return int(load().jagged_attn_check(workspace, stream))
+
+
+def jagged_attn_mx_quantize(x, dtype, rows, D, codes, scales, stream) -> int:
+    return int(load().jagged_attn_mx_quantize(x, dtype, rows, D, codes, scales, stream))

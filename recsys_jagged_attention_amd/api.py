@@ -98,3 +98,24 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         if status != _lib.JA_OK:
             raise _lib.JaggedAttnError(status, "jagged_attn_check")
     return out
+
+
+def mx_quantize(x: torch.Tensor, stream: Optional[torch.cuda.Stream] = None):
+    """MX-encode x [..., D] (float32 or bfloat16 CUDA tensor, D a multiple of
+    32) on the device: returns (codes uint8 [..., D], scales uint8 [..., D/32]),
+    the MXFP8 input format of ``forward``."""
+    if x.dtype not in (torch.float32, torch.bfloat16) or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous float32 or bfloat16 CUDA tensor")
+    D = x.shape[-1]
+    if D % 32 or D == 0:
+        raise ValueError("the last dimension must be a positive multiple of 32")
+    rows = x.numel() // D
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(tuple(x.shape[:-1]) + (D // 32,), dtype=torch.uint8, device=x.device)
+    st = stream if stream is not None else torch.cuda.current_stream(x.device)
+    dtype = _lib.JA_F32 if x.dtype == torch.float32 else _lib.JA_BF16
+    status = _lib.jagged_attn_mx_quantize(x.data_ptr(), dtype, rows, D, codes.data_ptr(), scales.data_ptr(),
+                                          st.cuda_stream)
+    if status != _lib.JA_OK:
+        raise _lib.JaggedAttnError(status, "jagged_attn_mx_quantize")
+    return codes, scales

@@ -17,6 +17,10 @@ hipError_t launch_combine(int D, const CombineArgs& a, hipStream_t st);
 hipError_t launch_attn_f32(int D, int act, int window_mode, const AttnArgs& a, int grid, hipStream_t st);
 hipError_t launch_attn_pp(int D, int act, const AttnArgs& a, int num_cu, int64_t max_items, hipStream_t st);
 hipError_t launch_key_rms(int D, const void* k, int64_t rows, float eps, float* out, hipStream_t st);
+hipError_t launch_mx_quant(bool bf16, const void* x, int64_t n_blocks, uint8_t* codes, uint8_t* scales,
+                           hipStream_t st);
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 int pp_rows();
 
 namespace {
@@ -256,6 +260,20 @@ int jagged_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
     ca.act = act;
     if (launch_combine(D, ca, stream) != hipSuccess) return JA_EHIP;
   }
+  return JA_OK;
+}
+
+int jagged_attn_mx_quantize(const void* x, int dtype, int64_t rows, int D, uint8_t* codes, uint8_t* scales,
+                            void* stream) {
+  if (x == nullptr || codes == nullptr || scales == nullptr) return JA_EINVAL;
+  if (dtype != JA_F32 && dtype != JA_BF16) return JA_EINVAL;
+  if (rows < 0 || D <= 0 || D % kMxBlock != 0) return JA_EINVAL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return JA_EINVAL;
+  if (rows > (int64_t(1) << 40) / D) return JA_EINVAL;  // (keeps the grid in range)
+  const int64_t n_blocks = rows * (D / kMxBlock);
+  if (launch_mx_quant(dtype == JA_BF16, x, n_blocks, codes, scales, reinterpret_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return JA_EHIP;
   return JA_OK;
 }
 

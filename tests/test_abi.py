@@ -96,5 +96,19 @@ def test_fwd_host_validation():
     assert call(dtype=_lib.JA_MXFP8_E4M3, scales=True, ws_bytes=16) == _lib.JA_EWORKSPACE
 
 
+def test_mx_quantize_host_validation():
+    q = lambda x=4096, dt=_lib.JA_BF16, rows=4, D=64, c=4096, s=4096: _lib.jagged_attn_mx_quantize(
+        x, dt, rows, D, c, s, None)
+    assert q(x=0) == _lib.JA_EINVAL
+    assert q(c=0) == _lib.JA_EINVAL
+    assert q(s=0) == _lib.JA_EINVAL
+    assert q(dt=_lib.JA_MXFP8_E4M3) == _lib.JA_EINVAL
+    assert q(D=48) == _lib.JA_EINVAL
+    assert q(D=0) == _lib.JA_EINVAL
+    assert q(rows=-1) == _lib.JA_EINVAL
+    assert q(x=4100) == _lib.JA_EINVAL
+    assert q(rows=1 << 40) == _lib.JA_EINVAL
+
+
 def test_check_rejects_null_workspace():
     assert _lib.jagged_attn_check(None, None) == _lib.JA_EINVAL
