@@ -9,4 +9,4 @@ from ._lib import (JA_SELF, JA_CROSS, JA_PMA, JA_SLIDING, JA_SOFTMAX, JA_GELU_TA
                    JA_MXFP8_E4M3, JA_OK, JA_EINVAL, JA_EUNSUPPORTED, JA_EWORKSPACE, JA_EHIP,
                    JA_EOFFSETS, JaIo, JaggedAttnError, jagged_attn_fwd, jagged_attn_workspace_size,
                    jagged_attn_check, jagged_attn_version, strerror)
-from .api import forward, mx_quantize, Workspace  # noqa: F401
+from .api import forward, backward, mx_quantize, Workspace  # noqa: F401

@@ -23,7 +23,8 @@ DTYPES = {"f32": JA_F32, "bf16": JA_BF16, "mxfp8": JA_MXFP8_E4M3}
 
 # Every function the header declares (checked by the CPU tests).
 EXPORTS = ("jagged_attn_fwd", "jagged_attn_workspace_size", "jagged_attn_check",
-           "jagged_attn_strerror", "jagged_attn_version", "jagged_attn_mx_quantize")
+           "jagged_attn_strerror", "jagged_attn_version", "jagged_attn_mx_quantize",
+           "jagged_attn_bwd", "jagged_attn_bwd_workspace_size")
 
 
 class JaIo(ctypes.Structure):
@@ -71,6 +72,11 @@ def load() -> ctypes.CDLL:
         lib.jagged_attn_strerror.argtypes = [ctypes.c_int]
         lib.jagged_attn_version.restype = ctypes.c_int
         lib.jagged_attn_version.argtypes = []
+        lib.jagged_attn_bwd.restype = ctypes.c_int
+        lib.jagged_attn_bwd.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int] * 6 + [ctypes.c_void_p] * 3 + [
+            ctypes.POINTER(JaIo)]
+        lib.jagged_attn_bwd_workspace_size.restype = ctypes.c_size_t
+        lib.jagged_attn_bwd_workspace_size.argtypes = [ctypes.c_int] * 7 + [ctypes.c_int32] * 2
         lib.jagged_attn_mx_quantize.restype = ctypes.c_int
         lib.jagged_attn_mx_quantize.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
                                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
@@ -98,6 +104,16 @@ def jagged_attn_fwd(q, k, v, q_offsets, kv_offsets, B, H, D, variant, act, windo
 
 def jagged_attn_check(workspace, stream) -> int:
     return int(load().jagged_attn_check(workspace, stream))
+
+
+def jagged_attn_bwd_workspace_size(B, H, D, variant, act, window, dtype, total_q, total_kv) -> int:
+    return int(load().jagged_attn_bwd_workspace_size(B, H, D, variant, act, window, dtype, total_q, total_kv))
+
+
+def jagged_attn_bwd(q, k, v, dout, q_offsets, kv_offsets, B, H, D, variant, act, window, dq, dk, dv,
+                    io: JaIo) -> int:
+    return int(load().jagged_attn_bwd(q, k, v, dout, q_offsets, kv_offsets, B, H, D, variant, act, window,
+                                      dq, dk, dv, ctypes.byref(io)))
 
 
 def jagged_attn_mx_quantize(x, dtype, rows, D, codes, scales, stream) -> int:

@@ -119,3 +119,50 @@ def mx_quantize(x: torch.Tensor, stream: Optional[torch.cuda.Stream] = None):
     if status != _lib.JA_OK:
         raise _lib.JaggedAttnError(status, "jagged_attn_mx_quantize")
     return codes, scales
+
+
+def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor,
+             q_offsets: torch.Tensor, kv_offsets: torch.Tensor,
+             variant: str = "self", act: str = "softmax", window: int = 0, dtype: str = "bf16",
+             workspace: Optional[Workspace] = None, stream: Optional[torch.cuda.Stream] = None,
+             check: bool = False, events=None):
+    """Gradients of the softmax forward: returns float32 (dq, dk, dv) shaped
+    like q, k, v.  q/k/v/dout are "f32" or "bf16" tensors laid out as for
+    ``forward``."""
+    if dtype not in ("f32", "bf16"):
+        raise ValueError("backward takes f32 or bf16 inputs")
+    want = _IN_DTYPES[dtype]
+    for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+        if t.dtype != want or not t.is_cuda or not t.is_contiguous() or t.dim() != 3:
+            raise ValueError(f"{name} must be a contiguous 3-D {want} CUDA tensor")
+    Nq, H, D = q.shape
+    Nk = k.shape[0]
+    if dout.shape != q.shape or k.shape != (Nk, H, D) or v.shape != k.shape:
+        raise ValueError("dout must match q, and k, v must be [Nk, H, D]")
+    B = q_offsets.numel() - 1
+    v_id, a_id, d_id = _lib.VARIANTS[variant], _lib.ACTS[act], _lib.DTYPES[dtype]
+    nbytes = _lib.jagged_attn_bwd_workspace_size(B, H, D, v_id, a_id, window, d_id, Nq, Nk) or 256
+    ws = (workspace or Workspace(q.device)).get(nbytes)
+    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+    dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
+    io = _lib.JaIo()
+    io.dtype = d_id
+    io.workspace = ws.data_ptr()
+    io.workspace_bytes = ws.numel()
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    io.stream = st.cuda_stream
+    io.total_q = Nq
+    io.total_kv = Nk
+    if events is not None:
+        io.ev_start, io.ev_stop = events
+    status = _lib.jagged_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), q_offsets.data_ptr(),
+                                  kv_offsets.data_ptr(), B, H, D, v_id, a_id, window, dq.data_ptr(),
+                                  dk.data_ptr(), dv.data_ptr(), io)
+    if status != _lib.JA_OK:
+        raise _lib.JaggedAttnError(status, "jagged_attn_bwd")
+    if check:
+        status = _lib.jagged_attn_check(ws.data_ptr(), st.cuda_stream)
+        if status != _lib.JA_OK:
+            raise _lib.JaggedAttnError(status, "jagged_attn_check")
+    return dq, dk, dv

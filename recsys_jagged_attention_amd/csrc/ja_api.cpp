@@ -3,6 +3,7 @@
 // of the offsets, no synchronisation on the forward path.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 
@@ -17,6 +18,7 @@ hipError_t launch_combine(int D, const CombineArgs& a, hipStream_t st);
 hipError_t launch_attn_f32(int D, int act, int window_mode, const AttnArgs& a, int grid, hipStream_t st);
 hipError_t launch_attn_pp(int D, int act, const AttnArgs& a, int num_cu, int64_t max_items, hipStream_t st);
 hipError_t launch_key_rms(int D, const void* k, int64_t rows, float eps, float* out, hipStream_t st);
+hipError_t launch_attn_bwd(int D, bool bf16, int wmode, const BwdArgs& a, int grid_q, int grid_k, hipStream_t st);
 hipError_t launch_mx_quant(bool bf16, const void* x, int64_t n_blocks, uint8_t* codes, uint8_t* scales,
                            hipStream_t st);
 
@@ -126,6 +128,49 @@ Plan make_plan(int B, int H, int D, int variant, int act, int window, int dtype,
   if (p.shape == kShapePingPong && act != JA_SOFTMAX) off = align256(off + sizeof(float) * size_t(total_kv) * H);
   w.total = off;
   return p;
+}
+
+// Backward workspace: two plans of 64-row tiles (over the queries, and over
+// the keys with the offsets swapped) and one (lse, D) pair per query row and head.
+constexpr int kBwdRows = 64;
+struct BwdLayout {
+  size_t hdr_q, nsplit_q, pbase_q, items_q, hdr_k, nsplit_k, pbase_k, items_k, stats, total;
+  int64_t max_q, max_k;
+};
+
+BwdLayout bwd_layout(int B, int H, int32_t total_q, int32_t total_kv) {
+  BwdLayout L{};
+  L.max_q = int64_t(H) * (cdiv(total_q, kBwdRows) + B);
+  L.max_k = int64_t(H) * (cdiv(total_kv, kBwdRows) + B);
+  size_t off = 0;
+  L.hdr_q = off;
+  off = align256(off + sizeof(WsHeader));
+  L.nsplit_q = off;
+  off = align256(off + sizeof(int32_t) * size_t(B));
+  L.pbase_q = off;
+  off = align256(off + sizeof(int32_t) * size_t(B));
+  L.items_q = off;
+  off = align256(off + sizeof(WorkItem) * size_t(L.max_q));
+  L.hdr_k = off;
+  off = align256(off + sizeof(WsHeader));
+  L.nsplit_k = off;
+  off = align256(off + sizeof(int32_t) * size_t(B));
+  L.pbase_k = off;
+  off = align256(off + sizeof(int32_t) * size_t(B));
+  L.items_k = off;
+  off = align256(off + sizeof(WorkItem) * size_t(L.max_k));
+  L.stats = off;
+  off = align256(off + sizeof(float2) * size_t(total_q) * H);
+  L.total = off;
+  return L;
+}
+
+int validate_bwd(int B, int H, int D, int variant, int act, int window, int dtype, int32_t total_q,
+                 int32_t total_kv) {
+  const int st = validate(B, H, D, variant, act, window, dtype, total_q, total_kv);
+  if (st != JA_OK) return st;
+  if (act != JA_SOFTMAX || dtype == JA_MXFP8_E4M3) return JA_EUNSUPPORTED;
+  return JA_OK;
 }
 
 }  // namespace
@@ -260,6 +305,78 @@ int jagged_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
     ca.act = act;
     if (launch_combine(D, ca, stream) != hipSuccess) return JA_EHIP;
   }
+  return JA_OK;
+}
+
+size_t jagged_attn_bwd_workspace_size(int B, int H, int D, int variant, int act, int window, int dtype,
+                                      int32_t total_q, int32_t total_kv) {
+  if (validate_bwd(B, H, D, variant, act, window, dtype, total_q, total_kv) != JA_OK) return 0;
+  return bwd_layout(B, H, total_q, total_kv).total;
+}
+
+int jagged_attn_bwd(const void* q, const void* k, const void* v, const void* dout, const int32_t* q_offsets,
+                    const int32_t* kv_offsets, int B, int H, int D, int variant, int act, int window, float* dq,
+                    float* dk, float* dv, const ja_io* io) {
+  if (io == nullptr) return JA_EINVAL;
+  const int st = validate_bwd(B, H, D, variant, act, window, io->dtype, io->total_q, io->total_kv);
+  if (st != JA_OK) return st;
+  if (!q || !k || !v || !dout || !q_offsets || !kv_offsets || !dq || !dk || !dv) return JA_EINVAL;
+  const BwdLayout L = bwd_layout(B, H, io->total_q, io->total_kv);
+  if (io->workspace == nullptr || io->workspace_bytes < L.total) return JA_EWORKSPACE;
+  for (const void* p : {q, k, v, dout, static_cast<const void*>(dq), static_cast<const void*>(dk),
+                        static_cast<const void*>(dv), static_cast<const void*>(io->workspace)})
+    if (!aligned16(p)) return JA_EINVAL;
+
+  hipStream_t stream = reinterpret_cast<hipStream_t>(io->stream);
+  unsigned char* ws = reinterpret_cast<unsigned char*>(io->workspace);
+  const bool self = variant == JA_SELF || variant == JA_SLIDING;
+  for (int pass = 0; pass < 2; ++pass) {
+    // pass 0: query tiles; pass 1: key tiles (the same plan on swapped offsets)
+    PlanArgs pa{};
+    pa.qo = pass == 0 ? q_offsets : kv_offsets;
+    pa.ko = pass == 0 ? kv_offsets : q_offsets;
+    pa.B = B;
+    pa.H = H;
+    pa.total_q = pass == 0 ? io->total_q : io->total_kv;
+    pa.total_kv = pass == 0 ? io->total_kv : io->total_q;
+    pa.bm = kBwdRows;
+    pa.kvc = 0;
+    pa.self_check = self;
+    pa.max_items = pass == 0 ? L.max_q : L.max_k;
+    pa.max_slots = 0;
+    pa.hdr = reinterpret_cast<WsHeader*>(ws + (pass == 0 ? L.hdr_q : L.hdr_k));
+    pa.nsplit = reinterpret_cast<int32_t*>(ws + (pass == 0 ? L.nsplit_q : L.nsplit_k));
+    pa.pbase = reinterpret_cast<int32_t*>(ws + (pass == 0 ? L.pbase_q : L.pbase_k));
+    pa.items = reinterpret_cast<WorkItem*>(ws + (pass == 0 ? L.items_q : L.items_k));
+    if (launch_plan(pa, stream) != hipSuccess) return JA_EHIP;
+  }
+  BwdArgs ba{};
+  ba.q = q;
+  ba.k = k;
+  ba.v = v;
+  ba.dout = dout;
+  ba.dq = dq;
+  ba.dk = dk;
+  ba.dv = dv;
+  ba.hdr_q = reinterpret_cast<const WsHeader*>(ws + L.hdr_q);
+  ba.items_q = reinterpret_cast<const WorkItem*>(ws + L.items_q);
+  ba.hdr_k = reinterpret_cast<const WsHeader*>(ws + L.hdr_k);
+  ba.items_k = reinterpret_cast<const WorkItem*>(ws + L.items_k);
+  ba.stats = reinterpret_cast<float2*>(ws + L.stats);
+  ba.H = H;
+  ba.window_blocks = variant == JA_SELF ? window / kBlock : 0;
+  ba.window_tokens = variant == JA_SLIDING ? window : 0;
+  const float inv_sqrt_d = 1.0f / std::sqrt(float(D));
+  ba.inv_sqrt_d = inv_sqrt_d;
+  ba.c2 = inv_sqrt_d * 1.4426950408889634f;
+  const int wmode = variant == JA_SLIDING ? 2 : (ba.window_blocks > 0 ? 1 : 0);
+  const int grid_q = int(std::min<int64_t>(L.max_q > 0 ? L.max_q : 1, kMaxGrid));
+  const int grid_k = int(std::min<int64_t>(L.max_k > 0 ? L.max_k : 1, kMaxGrid));
+  if (io->ev_start && hipEventRecord(reinterpret_cast<hipEvent_t>(io->ev_start), stream) != hipSuccess)
+    return JA_EHIP;
+  if (launch_attn_bwd(D, io->dtype == JA_BF16, wmode, ba, grid_q, grid_k, stream) != hipSuccess) return JA_EHIP;
+  if (io->ev_stop && hipEventRecord(reinterpret_cast<hipEvent_t>(io->ev_stop), stream) != hipSuccess)
+    return JA_EHIP;
   return JA_OK;
 }
 

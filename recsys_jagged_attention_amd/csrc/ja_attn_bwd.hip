@@ -1,0 +1,229 @@
+// Backward of jagged softmax attention (training): dQ, dK, dV of the forward
+// as defined, by the chain rule (the pages describe the training system --
+// techfeed.io summary of "GEM Training: How Meta Doubled the Efficiency of
+// Its LLM-Scale Ads Foundation Model" -- but not its backward pass).  For one
+// (sample, head):
+//   P = softmax(Q K^T / sqrt(D)) on the allowed keys,
+//   dV = P^T dO,  dS = P * (dO V^T - rowsum(P * (dO V^T))),
+//   dQ = dS K / sqrt(D),  dK = dS^T Q / sqrt(D).
+// Nothing is kept from the forward: the row statistics are recomputed.
+//
+// fp32 VALU kernels, four lanes per row (D/4 dimensions each, dot products
+// finished by two lane shuffles):
+//  * bwd_q_kernel, one row per query: the row's max and sum (log-sum-exp,
+//    base 2), then D_i = sum_j p_ij (dO_i . v_j), then dQ_i; it leaves
+//    (lse_i, D_i) for the second kernel;
+//  * bwd_kv_kernel, one row per key: over the queries that see the key,
+//    dV_j += p_ij dO_i and dK_j += p_ij (dO_i . v_j - D_i) q_i.
+// Work items are the forward's 64-row query tiles (plan over q) and 64-row key
+// tiles (the same plan over the swapped offsets); no atomics.
+#include "ja_internal.h"
+#include "jagged_attn.h"
+
+namespace ja {
+
+namespace {
+
+constexpr int kBwdThreads = 256;  // 64 rows x 4 lanes
+constexpr int kLpr = 4;           // lanes per row
+
+template <typename T>
+__device__ __forceinline__ float ld(const T* p, int i) {
+  if constexpr (sizeof(T) == 2) return __uint_as_float(unsigned(reinterpret_cast<const uint16_t*>(p)[i]) << 16);
+  else return p[i];
+}
+
+__device__ __forceinline__ float row_sum(float x) {
+  x += __shfl_xor(x, 1, 64);
+  x += __shfl_xor(x, 2, 64);
+  return x;
+}
+
+// Keys of a query row (sample-local), [lo, hi).
+template <int WMODE>
+__device__ __forceinline__ void key_range(const BwdArgs& a, int qrow, int lk, int& lo, int& hi) {
+  lo = 0;
+  hi = lk;
+  if constexpr (WMODE == 1) {
+    const int blk = qrow / kBlock;
+    lo = max(0, blk - a.window_blocks + 1) * kBlock;
+    hi = min(lk, (blk + 1) * kBlock);
+  } else if constexpr (WMODE == 2) {
+    lo = max(0, qrow - a.window_tokens + 1);
+    hi = min(lk, qrow + 1);
+  }
+}
+
+// Queries of a key row (sample-local), [lo, hi): the inverse of key_range.
+template <int WMODE>
+__device__ __forceinline__ void query_range(const BwdArgs& a, int krow, int lq, int& lo, int& hi) {
+  lo = 0;
+  hi = lq;
+  if constexpr (WMODE == 1) {
+    const int blk = krow / kBlock;
+    lo = min(lq, blk * kBlock);
+    hi = min(lq, (blk + a.window_blocks) * kBlock);
+  } else if constexpr (WMODE == 2) {
+    lo = min(lq, krow);
+    hi = min(lq, krow + a.window_tokens);
+  }
+}
+
+template <int D, typename T, int WMODE>
+__global__ __launch_bounds__(kBwdThreads) void bwd_q_kernel(BwdArgs a) {
+  constexpr int DL = D / kLpr;
+  const T* qv = reinterpret_cast<const T*>(a.q);
+  const T* kv = reinterpret_cast<const T*>(a.k);
+  const T* vv = reinterpret_cast<const T*>(a.v);
+  const T* gv = reinterpret_cast<const T*>(a.dout);
+  const int part = threadIdx.x % kLpr;
+  const int n_items = a.hdr_q->n_items;
+  for (int idx = blockIdx.x; idx < n_items; idx += gridDim.x) {
+    const WorkItem it = a.items_q[idx];
+    const int qrow = it.q0 + int(threadIdx.x) / kLpr;
+    if (qrow >= it.lq) continue;  // (all four lanes of a row together)
+    const size_t qoff = (size_t(it.qbeg + qrow) * a.H + it.h) * D + part * DL;
+    float q[DL], g[DL], dq[DL];
+#pragma unroll
+    for (int d = 0; d < DL; ++d) {
+      q[d] = ld(qv + qoff, d);
+      g[d] = ld(gv + qoff, d);
+      dq[d] = 0.f;
+    }
+    int lo, hi;
+    key_range<WMODE>(a, qrow, it.lk, lo, hi);
+    auto krow = [&](const T* base, int j) { return base + (size_t(it.kbeg + j) * a.H + it.h) * D + part * DL; };
+    // row max and sum, base 2
+    float m = -__builtin_huge_valf(), l = 0.f;
+    for (int j = lo; j < hi; ++j) {
+      const T* kp = krow(kv, j);
+      float s = 0.f;
+#pragma unroll
+      for (int d = 0; d < DL; ++d) s = fmaf(q[d], ld(kp, d), s);
+      s = row_sum(s) * a.c2;
+      if (s > m) {
+        l *= exp2f(m - s);
+        m = s;
+      }
+      l += exp2f(s - m);
+    }
+    const float lse = hi > lo ? m + log2f(l) : 0.f;
+    // D_i = sum_j p_ij (dO_i . v_j)
+    float di = 0.f;
+    for (int j = lo; j < hi; ++j) {
+      const T* kp = krow(kv, j);
+      const T* vp = krow(vv, j);
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int d = 0; d < DL; ++d) {
+        s = fmaf(q[d], ld(kp, d), s);
+        dp = fmaf(g[d], ld(vp, d), dp);
+      }
+      const float p = exp2f(row_sum(s) * a.c2 - lse);
+      di = fmaf(p, row_sum(dp), di);
+    }
+    // dQ_i = sum_j p_ij (dO_i . v_j - D_i) k_j / sqrt(D)
+    for (int j = lo; j < hi; ++j) {
+      const T* kp = krow(kv, j);
+      const T* vp = krow(vv, j);
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int d = 0; d < DL; ++d) {
+        s = fmaf(q[d], ld(kp, d), s);
+        dp = fmaf(g[d], ld(vp, d), dp);
+      }
+      const float ds = exp2f(row_sum(s) * a.c2 - lse) * (row_sum(dp) - di);
+#pragma unroll
+      for (int d = 0; d < DL; ++d) dq[d] = fmaf(ds, ld(kp, d), dq[d]);
+    }
+    float* out = a.dq + qoff;
+#pragma unroll
+    for (int d = 0; d < DL; ++d) out[d] = dq[d] * a.inv_sqrt_d;
+    if (part == 0) a.stats[size_t(it.qbeg + qrow) * a.H + it.h] = make_float2(lse, di);
+  }
+}
+
+template <int D, typename T, int WMODE>
+__global__ __launch_bounds__(kBwdThreads) void bwd_kv_kernel(BwdArgs a) {
+  constexpr int DL = D / kLpr;
+  const T* qv = reinterpret_cast<const T*>(a.q);
+  const T* kv = reinterpret_cast<const T*>(a.k);
+  const T* vv = reinterpret_cast<const T*>(a.v);
+  const T* gv = reinterpret_cast<const T*>(a.dout);
+  const int part = threadIdx.x % kLpr;
+  const int n_items = a.hdr_k->n_items;
+  for (int idx = blockIdx.x; idx < n_items; idx += gridDim.x) {
+    // (items over key tiles: the plan ran on the swapped offsets, so the
+    // record's "query" fields describe keys and its "key" fields queries)
+    const WorkItem it = a.items_k[idx];
+    const int krow = it.q0 + int(threadIdx.x) / kLpr;
+    const int lk = it.lq, lq = it.lk, kbeg = it.qbeg, qbeg = it.kbeg;
+    if (krow >= lk) continue;
+    const size_t koff = (size_t(kbeg + krow) * a.H + it.h) * D + part * DL;
+    float k[DL], v[DL], dk[DL], dv[DL];
+#pragma unroll
+    for (int d = 0; d < DL; ++d) {
+      k[d] = ld(kv + koff, d);
+      v[d] = ld(vv + koff, d);
+      dk[d] = 0.f;
+      dv[d] = 0.f;
+    }
+    int lo, hi;
+    query_range<WMODE>(a, krow, lq, lo, hi);
+    for (int i = lo; i < hi; ++i) {
+      const size_t qoff = (size_t(qbeg + i) * a.H + it.h) * D + part * DL;
+      const float2 st = a.stats[size_t(qbeg + i) * a.H + it.h];
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int d = 0; d < DL; ++d) {
+        s = fmaf(ld(qv + qoff, d), k[d], s);
+        dp = fmaf(ld(gv + qoff, d), v[d], dp);
+      }
+      const float p = exp2f(row_sum(s) * a.c2 - st.x);
+      const float ds = p * (row_sum(dp) - st.y);
+#pragma unroll
+      for (int d = 0; d < DL; ++d) {
+        dv[d] = fmaf(p, ld(gv + qoff, d), dv[d]);
+        dk[d] = fmaf(ds, ld(qv + qoff, d), dk[d]);
+      }
+    }
+    float* odk = a.dk + koff;
+    float* odv = a.dv + koff;
+#pragma unroll
+    for (int d = 0; d < DL; ++d) {
+      odk[d] = dk[d] * a.inv_sqrt_d;
+      odv[d] = dv[d];
+    }
+  }
+}
+
+template <int D, typename T>
+hipError_t launch_d(int wmode, const BwdArgs& a, int grid_q, int grid_k, hipStream_t st) {
+  const dim3 bd(kBwdThreads);
+  if (wmode == 1) {
+    hipLaunchKernelGGL((bwd_q_kernel<D, T, 1>), dim3(grid_q), bd, 0, st, a);
+    hipLaunchKernelGGL((bwd_kv_kernel<D, T, 1>), dim3(grid_k), bd, 0, st, a);
+  } else if (wmode == 2) {
+    hipLaunchKernelGGL((bwd_q_kernel<D, T, 2>), dim3(grid_q), bd, 0, st, a);
+    hipLaunchKernelGGL((bwd_kv_kernel<D, T, 2>), dim3(grid_k), bd, 0, st, a);
+  } else {
+    hipLaunchKernelGGL((bwd_q_kernel<D, T, 0>), dim3(grid_q), bd, 0, st, a);
+    hipLaunchKernelGGL((bwd_kv_kernel<D, T, 0>), dim3(grid_k), bd, 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd(int D, bool bf16, int wmode, const BwdArgs& a, int grid_q, int grid_k, hipStream_t st) {
+  if (bf16) {
+    if (D == 32) return launch_d<32, __bf16>(wmode, a, grid_q, grid_k, st);
+    if (D == 64) return launch_d<64, __bf16>(wmode, a, grid_q, grid_k, st);
+    return launch_d<128, __bf16>(wmode, a, grid_q, grid_k, st);
+  }
+  if (D == 32) return launch_d<32, float>(wmode, a, grid_q, grid_k, st);
+  if (D == 64) return launch_d<64, float>(wmode, a, grid_q, grid_k, st);
+  return launch_d<128, float>(wmode, a, grid_q, grid_k, st);
+}
+
+}  // namespace ja

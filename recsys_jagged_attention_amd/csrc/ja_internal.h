@@ -104,6 +104,26 @@ struct AttnArgs {
   float eps;
 };
 
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  float* dq;
+  float* dk;
+  float* dv;
+  const WsHeader* hdr_q;    // plan over query tiles
+  const WorkItem* items_q;
+  const WsHeader* hdr_k;    // plan over key tiles (swapped offsets)
+  const WorkItem* items_k;
+  float2* stats;            // per (query row, head): log2-sum-exp of the scores, D_i
+  int H;
+  int window_blocks;
+  int window_tokens;
+  float c2;                 // log2(e) / sqrt(D)
+  float inv_sqrt_d;
+};
+
 struct CombineArgs {
   void* out;
   const int32_t* qo;

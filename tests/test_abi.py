@@ -96,6 +96,31 @@ def test_fwd_host_validation():
     assert call(dtype=_lib.JA_MXFP8_E4M3, scales=True, ws_bytes=16) == _lib.JA_EWORKSPACE
 
 
+def test_bwd_host_validation():
+    lib = _lib.load()
+    ok = _lib.jagged_attn_bwd_workspace_size(4, 2, 32, _lib.JA_SELF, _lib.JA_SOFTMAX, 0, _lib.JA_BF16, 100, 100)
+    assert ok > 0
+    assert _lib.jagged_attn_bwd_workspace_size(4, 2, 32, _lib.JA_CROSS, _lib.JA_GELU_TANH, 0, _lib.JA_BF16,
+                                               100, 50) == 0
+    assert _lib.jagged_attn_bwd_workspace_size(4, 2, 32, _lib.JA_SELF, _lib.JA_SOFTMAX, 0, _lib.JA_MXFP8_E4M3,
+                                               100, 100) == 0
+
+    def call(act=_lib.JA_SOFTMAX, dtype=_lib.JA_BF16, ptr=4096, ws_bytes=1 << 24):
+        j = _lib.JaIo()
+        j.dtype = dtype
+        j.total_q = j.total_kv = 10
+        j.workspace = 1 << 20
+        j.workspace_bytes = ws_bytes
+        return lib.jagged_attn_bwd(ptr, ptr, ptr, ptr, ptr, ptr, 2, 1, 32, _lib.JA_SELF, act, 0,
+                                   ptr, ptr, ptr, ctypes.byref(j))
+
+    assert call(act=_lib.JA_GELU_TANH) == _lib.JA_EUNSUPPORTED
+    assert call(dtype=_lib.JA_MXFP8_E4M3) == _lib.JA_EUNSUPPORTED
+    assert call(ptr=0) == _lib.JA_EINVAL
+    assert call(ptr=4100) == _lib.JA_EINVAL
+    assert call(ws_bytes=16) == _lib.JA_EWORKSPACE
+
+
 def test_mx_quantize_host_validation():
     q = lambda x=4096, dt=_lib.JA_BF16, rows=4, D=64, c=4096, s=4096: _lib.jagged_attn_mx_quantize(
         x, dt, rows, D, c, s, None)
