@@ -233,6 +233,89 @@ def run_mx_quantize(args):
     print(json.dumps(line), flush=True)
 
 
+PEAK_VALU_F32 = 157.3  # TFLOP/s, fp32 vector (packed FMA); non-packed FMA issue gives half
+
+
+def run_backward(args):
+    """Time the softmax backward (dQ, dK, dV) on a workload's tensors with a
+    seeded dout and print one JSON line.  Useful FLOPs: 8 D per attended pair
+    and head (dV, dP, dQ and dK); the kernels also recompute the scores."""
+    import torch
+
+    from recsys_jagged_attention_amd import backward, Workspace
+    from recsys_jagged_attention_amd import workload as wl
+    from recsys_jagged_attention_amd.inputs import make_workload, device_tensors
+
+    w = make_workload(args.workload, seed=args.seed)
+    if w.dtype not in ("f32", "bf16") or w.act != "softmax":
+        raise SystemExit("the backward covers softmax workloads with f32 or bf16 inputs")
+    dev = torch.device("cuda:0")
+    q, k, v, qo, ko, _ = device_tensors(w, dev)
+    dout = torch.from_numpy(np.random.default_rng(w.seed + 1).standard_normal(w.q.shape, dtype=np.float32)).to(
+        q.dtype).to(dev)
+    lq, lk = np.diff(w.q_offsets), np.diff(w.kv_offsets)
+    pairs = wl.attended_pairs(lq, lk, w.window, w.variant)
+    flops = 8 * w.D * w.H * pairs
+    wsp = Workspace(dev)
+    ev = HipEvents()
+    K, W = args.steps, args.warmup
+    starts = [ev.create() for _ in range(K)]
+    stops = [ev.create() for _ in range(K)]
+    run = lambda e=None: backward(q, k, v, dout, qo, ko, variant=w.variant, window=w.window, dtype=w.dtype,
+                                  workspace=wsp, events=e)
+    run()
+    backward(q, k, v, dout, qo, ko, variant=w.variant, window=w.window, dtype=w.dtype, workspace=wsp, check=True)
+    for _ in range(W):
+        run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        run((starts[i], stops[i]))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern_s = float(np.mean([ev.elapsed_ms(starts[i], stops[i]) for i in range(K)])) * 1e-3
+    for e in starts + stops:
+        ev.destroy(e)
+    ms_per_step = (t1 - t0) * 1e3 / K
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / kern_s / 1e12
+    log(f"[bench] backward {w.name}: {ms_per_step * 1e3:.1f} us/step, kernels {kern_s * 1e6:.1f} us, "
+        f"{achieved:.2f} useful TFLOP/s ({100 * achieved / PEAK_VALU_F32:.1f}% of fp32 vector peak)")
+    cpu = None
+    if not args.no_cpu_baseline:
+        import os as _os
+        import oracle
+        # whole samples, shortest first, until about the time budget is used
+        order = np.argsort(lq, kind="stable")
+        t = time.perf_counter()
+        done = 0
+        for b in order:
+            sl = slice(w.q_offsets[b], w.q_offsets[b + 1])
+            sk = slice(w.kv_offsets[b], w.kv_offsets[b + 1])
+            oracle.gdpa_backward(w.q[sl], w.k[sk], w.v[sk], dout[sl].float().cpu().numpy(),
+                                 [0, lq[b]], [0, lk[b]], w.variant, "softmax", w.window)
+            done += 8 * w.D * w.H * wl.attended_pairs([lq[b]], [lk[b]], w.window, w.variant)
+            if time.perf_counter() - t > min(args.cpu_seconds, 10.0):
+                break
+        dt = time.perf_counter() - t
+        cpu = {"value": round(done / dt / 1e12, 6), "unit": "TFLOPS", "cores": len(_os.sched_getaffinity(0)),
+               "kind": "oracle", "sample": f"{done / 8 / w.D / w.H:.0f} attended pairs x {w.H} heads"}
+    line = {
+        "metric": "useful TFLOPS of the softmax backward (dQ, dK, dV), jagged, 1 MI355X",
+        "value": round(value, 3), "unit": "TFLOPS", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "variant": w.variant, "B": w.B, "H": w.H, "D": w.D, "window": w.window,
+                   "total_q": w.total_q, "useful_gflop": round(flops / 1e9, 3), "seed": w.seed},
+        "roofline": {"bound": "alu", "achieved": round(achieved, 2), "peak": PEAK_VALU_F32, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_VALU_F32, 4), "traffic": None,
+                     "kernel": "bwd_q_kernel + bwd_kv_kernel", "kernel_avg_us": round(kern_s * 1e6, 2),
+                     "useful_flops_per_launch": int(flops)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -247,9 +330,17 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 5 times (the reference "
                          "for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE counters) and exit")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the softmax backward on the workload instead of the forward")
     ap.add_argument("--mx-quantize", action="store_true",
                     help="time the device MX quantiser instead of the attention forward")
     args = ap.parse_args()
+
+    if args.backward:
+        if args.gpus != 1:
+            raise SystemExit("bench.py measures one GPU only")
+        run_backward(args)
+        return
 
     if args.mx_quantize:
         if args.gpus != 1:

@@ -33,9 +33,15 @@ __device__ __forceinline__ float ld(const T* p, int i) {
   else return p[i];
 }
 
+// Sum over the four lanes of a row (a quad), by DPP quad permutations on the
+// VALU: lanes 1,0,3,2 then 2,3,0,1 of the quad.
+template <int CTRL>
+__device__ __forceinline__ float quad_perm(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
 __device__ __forceinline__ float row_sum(float x) {
-  x += __shfl_xor(x, 1, 64);
-  x += __shfl_xor(x, 2, 64);
+  x += quad_perm<0xB1>(x);  // lanes [1, 0, 3, 2] of the quad
+  x += quad_perm<0x4E>(x);  // lanes [2, 3, 0, 1]
   return x;
 }
 

@@ -88,8 +88,9 @@ __global__ __launch_bounds__(kQuantThreads) void mx_quant_kernel(const T* __rest
     float amax = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[c][i]));
-    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    // max over the block's four lanes (a quad): DPP quad permutations
+    amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(amax), 0xB1, 0xF, 0xF, true)));
+    amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(amax), 0x4E, 0xF, 0xF, true)));
     // E = floor(log2 amax) - 8 from the exponent field; a zero or subnormal
     // block max gives -127 (the clamp)
     const int ex = int((__float_as_uint(amax) >> 23) & 0xFFu);
