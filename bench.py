@@ -247,8 +247,8 @@ def run_backward(args):
     from recsys_jagged_attention_amd.inputs import make_workload, device_tensors
 
     w = make_workload(args.workload, seed=args.seed)
-    if w.dtype not in ("f32", "bf16") or w.act != "softmax":
-        raise SystemExit("the backward covers softmax workloads with f32 or bf16 inputs")
+    if w.dtype not in ("f32", "bf16") or w.act not in ("softmax", "gelu_tanh"):
+        raise SystemExit("the backward covers softmax and gelu_tanh workloads with f32 or bf16 inputs")
     dev = torch.device("cuda:0")
     q, k, v, qo, ko, _ = device_tensors(w, dev)
     dout = torch.from_numpy(np.random.default_rng(w.seed + 1).standard_normal(w.q.shape, dtype=np.float32)).to(
@@ -261,10 +261,11 @@ def run_backward(args):
     K, W = args.steps, args.warmup
     starts = [ev.create() for _ in range(K)]
     stops = [ev.create() for _ in range(K)]
-    run = lambda e=None: backward(q, k, v, dout, qo, ko, variant=w.variant, window=w.window, dtype=w.dtype,
-                                  workspace=wsp, events=e)
+    run = lambda e=None: backward(q, k, v, dout, qo, ko, variant=w.variant, act=w.act, window=w.window,
+                                  dtype=w.dtype, workspace=wsp, events=e)
     run()
-    backward(q, k, v, dout, qo, ko, variant=w.variant, window=w.window, dtype=w.dtype, workspace=wsp, check=True)
+    backward(q, k, v, dout, qo, ko, variant=w.variant, act=w.act, window=w.window, dtype=w.dtype, workspace=wsp,
+             check=True)
     for _ in range(W):
         run()
     torch.cuda.synchronize()
@@ -293,7 +294,7 @@ def run_backward(args):
             sl = slice(w.q_offsets[b], w.q_offsets[b + 1])
             sk = slice(w.kv_offsets[b], w.kv_offsets[b + 1])
             oracle.gdpa_backward(w.q[sl], w.k[sk], w.v[sk], dout[sl].float().cpu().numpy(),
-                                 [0, lq[b]], [0, lk[b]], w.variant, "softmax", w.window)
+                                 [0, lq[b]], [0, lk[b]], w.variant, w.act, w.window)
             done += 8 * w.D * w.H * wl.attended_pairs([lq[b]], [lk[b]], w.window, w.variant)
             if time.perf_counter() - t > min(args.cpu_seconds, 10.0):
                 break
@@ -301,12 +302,12 @@ def run_backward(args):
         cpu = {"value": round(done / dt / 1e12, 6), "unit": "TFLOPS", "cores": len(_os.sched_getaffinity(0)),
                "kind": "oracle", "sample": f"{done / 8 / w.D / w.H:.0f} attended pairs x {w.H} heads"}
     line = {
-        "metric": "useful TFLOPS of the softmax backward (dQ, dK, dV), jagged, 1 MI355X",
+        "metric": "useful TFLOPS of the attention backward (dQ, dK, dV), jagged, 1 MI355X",
         "value": round(value, 3), "unit": "TFLOPS", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": w.name, "variant": w.variant, "B": w.B, "H": w.H, "D": w.D, "window": w.window,
-                   "total_q": w.total_q, "useful_gflop": round(flops / 1e9, 3), "seed": w.seed},
+        "config": {"workload": w.name, "variant": w.variant, "act": w.act, "B": w.B, "H": w.H, "D": w.D,
+                   "window": w.window, "total_q": w.total_q, "useful_gflop": round(flops / 1e9, 3), "seed": w.seed},
         "roofline": {"bound": "alu", "achieved": round(achieved, 2), "peak": PEAK_VALU_F32, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_VALU_F32, 4), "traffic": None,
                      "kernel": "bwd_q_kernel + bwd_kv_kernel", "kernel_avg_us": round(kern_s * 1e6, 2),

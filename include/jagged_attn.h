@@ -128,23 +128,29 @@ size_t jagged_attn_workspace_size(int B, int H, int D, int variant, int act,
                                   int window, int dtype, int32_t total_q,
                                   int32_t total_kv);
 
-/* Backward of the softmax forward, for training (the pages describe the
- * training system but not its backward; this is the chain-rule derivative of
- * the forward as defined above).  For every sample and head, with P the
- * softmax weights of the forward:
- *   dV = P^T dO,  dS = P * (dO V^T - rowsum(P * (dO V^T))),
- *   dQ = dS K / sqrt(D),  dK = dS^T Q / sqrt(D).
+/* Backward of the forward, for training (the pages describe the training
+ * system but not its backward; this is the chain-rule derivative of the
+ * forward as defined above).  For every sample and head:
+ *   JA_SOFTMAX, with P the softmax weights of the forward:
+ *     dV = P^T dO,  dS = P * (dO V^T - rowsum(P * (dO V^T))),
+ *     dQ = dS K / sqrt(D),  dK = dS^T Q / sqrt(D);
+ *   JA_GELU_TANH, with Qn, Kn the RMS-normalised rows, S = Qn Kn^T / sqrt(D):
+ *     dV = gelu(S)^T dO / Lk,  dS = gelu'(S) * (dO V^T) / Lk,
+ *     dQn = dS Kn / sqrt(D),  dKn = dS^T Qn / sqrt(D), then through the
+ *     RMSNorm row by row: dx = r dxn - x r^3 (dxn . x) / D,
+ *     r = (mean(x^2) + eps)^(-1/2), eps = io->rms_eps (<= 0 -> 1e-6).
  * q, k, v: as for jagged_attn_fwd; dout: the gradient of out, laid out and
  * typed like q (JA_F32 or JA_BF16).  Writes float32 dq [total_q, H, D] and
  * dk, dv [total_kv, H, D] (every row written; rows of samples without keys
- * get zeros in dq, keys no query sees get zeros).  act must be JA_SOFTMAX;
- * variant, window and offsets as for jagged_attn_fwd (JA_SELF with or
- * without a block window, JA_SLIDING, JA_CROSS, JA_PMA).  Nothing from the
- * forward is needed: row statistics are recomputed.  Workspace of
- * jagged_attn_bwd_workspace_size() bytes in io->workspace; io->ev_start /
- * ev_stop, when set, bracket the two gradient kernels.  Asynchronous on
- * io->stream; errors as for jagged_attn_fwd (JA_EUNSUPPORTED for GELU acts
- * and MXFP8; offset errors through jagged_attn_check). */
+ * get zeros in dq, keys no query sees get zeros).  act: JA_SOFTMAX or
+ * JA_GELU_TANH; variant, window and offsets as for jagged_attn_fwd (JA_SELF
+ * with or without a block window, JA_SLIDING, JA_CROSS, JA_PMA; no window
+ * with GELU).  Nothing from the forward is needed: row statistics and RMS
+ * factors are recomputed.  Workspace of jagged_attn_bwd_workspace_size()
+ * bytes in io->workspace; io->ev_start / ev_stop, when set, bracket the
+ * gradient kernels.  Asynchronous on io->stream; errors as for
+ * jagged_attn_fwd (JA_EUNSUPPORTED for JA_GELU_POLY and MXFP8; offset errors
+ * through jagged_attn_check). */
 int jagged_attn_bwd(const void *q, const void *k, const void *v, const void *dout,
                     const int32_t *q_offsets, const int32_t *kv_offsets,
                     int B, int H, int D, int variant, int act, int window,

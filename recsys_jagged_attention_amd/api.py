@@ -124,11 +124,11 @@ def mx_quantize(x: torch.Tensor, stream: Optional[torch.cuda.Stream] = None):
 def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tensor,
              q_offsets: torch.Tensor, kv_offsets: torch.Tensor,
              variant: str = "self", act: str = "softmax", window: int = 0, dtype: str = "bf16",
-             workspace: Optional[Workspace] = None, stream: Optional[torch.cuda.Stream] = None,
-             check: bool = False, events=None):
-    """Gradients of the softmax forward: returns float32 (dq, dk, dv) shaped
-    like q, k, v.  q/k/v/dout are "f32" or "bf16" tensors laid out as for
-    ``forward``."""
+             workspace: Optional[Workspace] = None, rms_eps: float = 1e-6,
+             stream: Optional[torch.cuda.Stream] = None, check: bool = False, events=None):
+    """Gradients of the forward (act "softmax" or "gelu_tanh"): returns float32
+    (dq, dk, dv) shaped like q, k, v.  q/k/v/dout are "f32" or "bf16" tensors
+    laid out as for ``forward``."""
     if dtype not in ("f32", "bf16"):
         raise ValueError("backward takes f32 or bf16 inputs")
     want = _IN_DTYPES[dtype]
@@ -154,6 +154,7 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tens
     io.stream = st.cuda_stream
     io.total_q = Nq
     io.total_kv = Nk
+    io.rms_eps = rms_eps
     if events is not None:
         io.ev_start, io.ev_stop = events
     status = _lib.jagged_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), q_offsets.data_ptr(),

@@ -18,7 +18,8 @@ hipError_t launch_combine(int D, const CombineArgs& a, hipStream_t st);
 hipError_t launch_attn_f32(int D, int act, int window_mode, const AttnArgs& a, int grid, hipStream_t st);
 hipError_t launch_attn_pp(int D, int act, const AttnArgs& a, int num_cu, int64_t max_items, hipStream_t st);
 hipError_t launch_key_rms(int D, const void* k, int64_t rows, float eps, float* out, hipStream_t st);
-hipError_t launch_attn_bwd(int D, bool bf16, int wmode, const BwdArgs& a, int grid_q, int grid_k, hipStream_t st);
+hipError_t launch_attn_bwd(int D, bool bf16, int act, int wmode, const BwdArgs& a, int64_t rows_q, int64_t rows_k,
+                           int grid_q, int grid_k, hipStream_t st);
 hipError_t launch_mx_quant(bool bf16, const void* x, int64_t n_blocks, uint8_t* codes, uint8_t* scales,
                            hipStream_t st);
 
@@ -134,11 +135,11 @@ Plan make_plan(int B, int H, int D, int variant, int act, int window, int dtype,
 // the keys with the offsets swapped) and one (lse, D) pair per query row and head.
 constexpr int kBwdRows = 64;
 struct BwdLayout {
-  size_t hdr_q, nsplit_q, pbase_q, items_q, hdr_k, nsplit_k, pbase_k, items_k, stats, total;
+  size_t hdr_q, nsplit_q, pbase_q, items_q, hdr_k, nsplit_k, pbase_k, items_k, stats, rq, rk, total;
   int64_t max_q, max_k;
 };
 
-BwdLayout bwd_layout(int B, int H, int32_t total_q, int32_t total_kv) {
+BwdLayout bwd_layout(int B, int H, int act, int32_t total_q, int32_t total_kv) {
   BwdLayout L{};
   L.max_q = int64_t(H) * (cdiv(total_q, kBwdRows) + B);
   L.max_k = int64_t(H) * (cdiv(total_kv, kBwdRows) + B);
@@ -161,6 +162,13 @@ BwdLayout bwd_layout(int B, int H, int32_t total_q, int32_t total_kv) {
   off = align256(off + sizeof(WorkItem) * size_t(L.max_k));
   L.stats = off;
   off = align256(off + sizeof(float2) * size_t(total_q) * H);
+  L.rq = L.rk = off;
+  if (act != JA_SOFTMAX) {  // RMS factors of the query and key rows
+    L.rq = off;
+    off = align256(off + sizeof(float) * size_t(total_q) * H);
+    L.rk = off;
+    off = align256(off + sizeof(float) * size_t(total_kv) * H);
+  }
   L.total = off;
   return L;
 }
@@ -169,7 +177,7 @@ int validate_bwd(int B, int H, int D, int variant, int act, int window, int dtyp
                  int32_t total_kv) {
   const int st = validate(B, H, D, variant, act, window, dtype, total_q, total_kv);
   if (st != JA_OK) return st;
-  if (act != JA_SOFTMAX || dtype == JA_MXFP8_E4M3) return JA_EUNSUPPORTED;
+  if (act == JA_GELU_POLY || dtype == JA_MXFP8_E4M3) return JA_EUNSUPPORTED;
   return JA_OK;
 }
 
@@ -311,7 +319,7 @@ int jagged_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
 size_t jagged_attn_bwd_workspace_size(int B, int H, int D, int variant, int act, int window, int dtype,
                                       int32_t total_q, int32_t total_kv) {
   if (validate_bwd(B, H, D, variant, act, window, dtype, total_q, total_kv) != JA_OK) return 0;
-  return bwd_layout(B, H, total_q, total_kv).total;
+  return bwd_layout(B, H, act, total_q, total_kv).total;
 }
 
 int jagged_attn_bwd(const void* q, const void* k, const void* v, const void* dout, const int32_t* q_offsets,
@@ -321,7 +329,7 @@ int jagged_attn_bwd(const void* q, const void* k, const void* v, const void* dou
   const int st = validate_bwd(B, H, D, variant, act, window, io->dtype, io->total_q, io->total_kv);
   if (st != JA_OK) return st;
   if (!q || !k || !v || !dout || !q_offsets || !kv_offsets || !dq || !dk || !dv) return JA_EINVAL;
-  const BwdLayout L = bwd_layout(B, H, io->total_q, io->total_kv);
+  const BwdLayout L = bwd_layout(B, H, act, io->total_q, io->total_kv);
   if (io->workspace == nullptr || io->workspace_bytes < L.total) return JA_EWORKSPACE;
   for (const void* p : {q, k, v, dout, static_cast<const void*>(dq), static_cast<const void*>(dk),
                         static_cast<const void*>(dv), static_cast<const void*>(io->workspace)})
@@ -363,6 +371,9 @@ int jagged_attn_bwd(const void* q, const void* k, const void* v, const void* dou
   ba.hdr_k = reinterpret_cast<const WsHeader*>(ws + L.hdr_k);
   ba.items_k = reinterpret_cast<const WorkItem*>(ws + L.items_k);
   ba.stats = reinterpret_cast<float2*>(ws + L.stats);
+  ba.rq = reinterpret_cast<float*>(ws + L.rq);
+  ba.rk = reinterpret_cast<float*>(ws + L.rk);
+  ba.eps = io->rms_eps > 0.f ? io->rms_eps : 1e-6f;
   ba.H = H;
   ba.window_blocks = variant == JA_SELF ? window / kBlock : 0;
   ba.window_tokens = variant == JA_SLIDING ? window : 0;
@@ -374,7 +385,9 @@ int jagged_attn_bwd(const void* q, const void* k, const void* v, const void* dou
   const int grid_k = int(std::min<int64_t>(L.max_k > 0 ? L.max_k : 1, kMaxGrid));
   if (io->ev_start && hipEventRecord(reinterpret_cast<hipEvent_t>(io->ev_start), stream) != hipSuccess)
     return JA_EHIP;
-  if (launch_attn_bwd(D, io->dtype == JA_BF16, wmode, ba, grid_q, grid_k, stream) != hipSuccess) return JA_EHIP;
+  if (launch_attn_bwd(D, io->dtype == JA_BF16, act == JA_SOFTMAX ? ACT_SOFTMAX : ACT_GELU, wmode, ba,
+                      int64_t(io->total_q) * H, int64_t(io->total_kv) * H, grid_q, grid_k, stream) != hipSuccess)
+    return JA_EHIP;
   if (io->ev_stop && hipEventRecord(reinterpret_cast<hipEvent_t>(io->ev_stop), stream) != hipSuccess)
     return JA_EHIP;
   return JA_OK;

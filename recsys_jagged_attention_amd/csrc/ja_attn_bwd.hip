@@ -17,6 +17,15 @@
 //    dV_j += p_ij dO_i and dK_j += p_ij (dO_i . v_j - D_i) q_i.
 // Work items are the forward's 64-row query tiles (plan over q) and 64-row key
 // tiles (the same plan over the swapped offsets); no atomics.
+//
+// GELU scores (tanh form, QK-RMSNorm, no window): with Qn = rms(Q), Kn = rms(K),
+// S = Qn Kn^T / sqrt(D) and O = gelu(S) V / Lk,
+//   dV = gelu(S)^T dO / Lk,  dS = gelu'(S) * (dO V^T) / Lk,
+//   dQn = dS Kn / sqrt(D),   dKn = dS^T Qn / sqrt(D),
+// and through the RMSNorm, per row, dx = r dxn - x r^3 (dxn . x) / D with
+// r = (mean(x^2) + eps)^(-1/2).  No statistics pass is needed; bwd_rms_kernel
+// writes r for every query and key row first.
+#include "ja_device.h"
 #include "ja_internal.h"
 #include "jagged_attn.h"
 
@@ -43,6 +52,35 @@ __device__ __forceinline__ float row_sum(float x) {
   x += quad_perm<0xB1>(x);  // lanes [1, 0, 3, 2] of the quad
   x += quad_perm<0x4E>(x);  // lanes [2, 3, 0, 1]
   return x;
+}
+
+// gelu(x) = x t and gelu'(x) = t + 2 x t (1 - t) u'(x), where t = sigmoid(2u),
+// u = sqrt(2/pi) (x + 0.044715 x^3) (from 1 + tanh(u) = 2 sigmoid(2u)).
+__device__ __forceinline__ void gelu_and_grad(float x, float& g, float& gp) {
+  constexpr float kC = 0.7978845608028654f;  // sqrt(2/pi)
+  constexpr float kA = 0.044715f;
+  const float u = kC * fmaf(kA * x, x * x, x);
+  const float t = 1.0f / (1.0f + exp2f(-2.0f * 1.4426950408889634f * u));
+  g = x * t;
+  gp = fmaf(2.0f * x * t * (1.0f - t), kC * fmaf(3.0f * kA, x * x, 1.0f), t);
+}
+
+// RMS factor (mean(x^2) + eps)^(-1/2) of every row of a [rows, D] tensor,
+// four lanes per row.
+template <int D, typename T>
+__global__ __launch_bounds__(kBwdThreads) void bwd_rms_kernel(const T* x, int64_t rows, float eps, float* out) {
+  constexpr int DL = D / kLpr;
+  const int64_t r = int64_t(blockIdx.x) * (kBwdThreads / kLpr) + threadIdx.x / kLpr;
+  if (r >= rows) return;  // (all four lanes of a row together)
+  const T* p = x + r * D + (threadIdx.x % kLpr) * DL;
+  float ss = 0.f;
+#pragma unroll
+  for (int d = 0; d < DL; ++d) {
+    const float e = ld(p, d);
+    ss = fmaf(e, e, ss);
+  }
+  ss = row_sum(ss);
+  if (threadIdx.x % kLpr == 0) out[r] = 1.0f / sqrtf(ss * (1.0f / D) + eps);
 }
 
 // Keys of a query row (sample-local), [lo, hi).
@@ -75,7 +113,7 @@ __device__ __forceinline__ void query_range(const BwdArgs& a, int krow, int lq, 
   }
 }
 
-template <int D, typename T, int WMODE>
+template <int D, typename T, int WMODE, int ACT>
 __global__ __launch_bounds__(kBwdThreads) void bwd_q_kernel(BwdArgs a) {
   constexpr int DL = D / kLpr;
   const T* qv = reinterpret_cast<const T*>(a.q);
@@ -99,6 +137,39 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_kernel(BwdArgs a) {
     int lo, hi;
     key_range<WMODE>(a, qrow, it.lk, lo, hi);
     auto krow = [&](const T* base, int j) { return base + (size_t(it.kbeg + j) * a.H + it.h) * D + part * DL; };
+    if constexpr (ACT == ACT_GELU) {
+      // dQn_i = sum_j gelu'(s_ij) (dO_i . v_j) / Lk * Kn_j / sqrt(D), then the RMSNorm
+      const float ri = a.rq[size_t(it.qbeg + qrow) * a.H + it.h];
+      const float sc = ri * a.inv_sqrt_d;
+      const float inv_lk = 1.0f / float(it.lk);
+      for (int j = lo; j < hi; ++j) {
+        const T* kp = krow(kv, j);
+        const T* vp = krow(vv, j);
+        const float ck = a.rk[size_t(it.kbeg + j) * a.H + it.h];
+        float s = 0.f, dp = 0.f;
+#pragma unroll
+        for (int d = 0; d < DL; ++d) {
+          s = fmaf(q[d], ld(kp, d), s);
+          dp = fmaf(g[d], ld(vp, d), dp);
+        }
+        float gl, gp;
+        gelu_and_grad(row_sum(s) * sc * ck, gl, gp);
+        const float ds = gp * row_sum(dp) * inv_lk * ck;
+#pragma unroll
+        for (int d = 0; d < DL; ++d) dq[d] = fmaf(ds, ld(kp, d), dq[d]);
+      }
+      float dot = 0.f;
+#pragma unroll
+      for (int d = 0; d < DL; ++d) {
+        dq[d] *= a.inv_sqrt_d;
+        dot = fmaf(dq[d], q[d], dot);
+      }
+      const float c3 = ri * ri * ri * row_sum(dot) * (1.0f / D);
+      float* out = a.dq + qoff;
+#pragma unroll
+      for (int d = 0; d < DL; ++d) out[d] = fmaf(ri, dq[d], -q[d] * c3);
+      continue;
+    }
     // row max and sum, base 2
     float m = -__builtin_huge_valf(), l = 0.f;
     for (int j = lo; j < hi; ++j) {
@@ -149,7 +220,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_kernel(BwdArgs a) {
   }
 }
 
-template <int D, typename T, int WMODE>
+template <int D, typename T, int WMODE, int ACT>
 __global__ __launch_bounds__(kBwdThreads) void bwd_kv_kernel(BwdArgs a) {
   constexpr int DL = D / kLpr;
   const T* qv = reinterpret_cast<const T*>(a.q);
@@ -176,6 +247,46 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_kernel(BwdArgs a) {
     }
     int lo, hi;
     query_range<WMODE>(a, krow, lq, lo, hi);
+    if constexpr (ACT == ACT_GELU) {
+      // dV_j = sum_i gelu(s_ij) dO_i / Lk; dKn_j = sum_i gelu'(s_ij) (dO_i . v_j) / Lk * Qn_i / sqrt(D)
+      const float ck = a.rk[size_t(kbeg + krow) * a.H + it.h];
+      const float sc = ck * a.inv_sqrt_d;
+      const float inv_lk = 1.0f / float(lk);
+      for (int i = lo; i < hi; ++i) {
+        const size_t qoff = (size_t(qbeg + i) * a.H + it.h) * D + part * DL;
+        const float ri = a.rq[size_t(qbeg + i) * a.H + it.h];
+        float s = 0.f, dp = 0.f;
+#pragma unroll
+        for (int d = 0; d < DL; ++d) {
+          s = fmaf(ld(qv + qoff, d), k[d], s);
+          dp = fmaf(ld(gv + qoff, d), v[d], dp);
+        }
+        float gl, gp;
+        gelu_and_grad(row_sum(s) * sc * ri, gl, gp);
+        gl *= inv_lk;
+        const float ds = gp * row_sum(dp) * inv_lk * ri;
+#pragma unroll
+        for (int d = 0; d < DL; ++d) {
+          dv[d] = fmaf(gl, ld(gv + qoff, d), dv[d]);
+          dk[d] = fmaf(ds, ld(qv + qoff, d), dk[d]);
+        }
+      }
+      float dot = 0.f;
+#pragma unroll
+      for (int d = 0; d < DL; ++d) {
+        dk[d] *= a.inv_sqrt_d;
+        dot = fmaf(dk[d], k[d], dot);
+      }
+      const float c3 = ck * ck * ck * row_sum(dot) * (1.0f / D);
+      float* odk = a.dk + koff;
+      float* odv = a.dv + koff;
+#pragma unroll
+      for (int d = 0; d < DL; ++d) {
+        odk[d] = fmaf(ck, dk[d], -k[d] * c3);
+        odv[d] = dv[d];
+      }
+      continue;
+    }
     for (int i = lo; i < hi; ++i) {
       const size_t qoff = (size_t(qbeg + i) * a.H + it.h) * D + part * DL;
       const float2 st = a.stats[size_t(qbeg + i) * a.H + it.h];
@@ -203,33 +314,57 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_kv_kernel(BwdArgs a) {
   }
 }
 
-template <int D, typename T>
+template <int D, typename T, int ACT>
 hipError_t launch_d(int wmode, const BwdArgs& a, int grid_q, int grid_k, hipStream_t st) {
   const dim3 bd(kBwdThreads);
-  if (wmode == 1) {
-    hipLaunchKernelGGL((bwd_q_kernel<D, T, 1>), dim3(grid_q), bd, 0, st, a);
-    hipLaunchKernelGGL((bwd_kv_kernel<D, T, 1>), dim3(grid_k), bd, 0, st, a);
+  if constexpr (ACT == ACT_GELU) {  // (no window with GELU scores)
+    hipLaunchKernelGGL((bwd_q_kernel<D, T, 0, ACT>), dim3(grid_q), bd, 0, st, a);
+    hipLaunchKernelGGL((bwd_kv_kernel<D, T, 0, ACT>), dim3(grid_k), bd, 0, st, a);
+  } else if (wmode == 1) {
+    hipLaunchKernelGGL((bwd_q_kernel<D, T, 1, ACT>), dim3(grid_q), bd, 0, st, a);
+    hipLaunchKernelGGL((bwd_kv_kernel<D, T, 1, ACT>), dim3(grid_k), bd, 0, st, a);
   } else if (wmode == 2) {
-    hipLaunchKernelGGL((bwd_q_kernel<D, T, 2>), dim3(grid_q), bd, 0, st, a);
-    hipLaunchKernelGGL((bwd_kv_kernel<D, T, 2>), dim3(grid_k), bd, 0, st, a);
+    hipLaunchKernelGGL((bwd_q_kernel<D, T, 2, ACT>), dim3(grid_q), bd, 0, st, a);
+    hipLaunchKernelGGL((bwd_kv_kernel<D, T, 2, ACT>), dim3(grid_k), bd, 0, st, a);
   } else {
-    hipLaunchKernelGGL((bwd_q_kernel<D, T, 0>), dim3(grid_q), bd, 0, st, a);
-    hipLaunchKernelGGL((bwd_kv_kernel<D, T, 0>), dim3(grid_k), bd, 0, st, a);
+    hipLaunchKernelGGL((bwd_q_kernel<D, T, 0, ACT>), dim3(grid_q), bd, 0, st, a);
+    hipLaunchKernelGGL((bwd_kv_kernel<D, T, 0, ACT>), dim3(grid_k), bd, 0, st, a);
   }
   return hipGetLastError();
 }
 
+template <int D, typename T>
+hipError_t launch_rms(const void* x, int64_t rows, float eps, float* out, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  constexpr int kRowsPerBlock = kBwdThreads / kLpr;
+  hipLaunchKernelGGL((bwd_rms_kernel<D, T>), dim3(unsigned((rows + kRowsPerBlock - 1) / kRowsPerBlock)),
+                     dim3(kBwdThreads), 0, st, reinterpret_cast<const T*>(x), rows, eps, out);
+  return hipGetLastError();
+}
+
+template <int D, typename T>
+hipError_t launch_all(int act, int wmode, const BwdArgs& a, int64_t rows_q, int64_t rows_k, int grid_q,
+                      int grid_k, hipStream_t st) {
+  if (act != ACT_GELU) return launch_d<D, T, ACT_SOFTMAX>(wmode, a, grid_q, grid_k, st);
+  hipError_t e = launch_rms<D, T>(a.q, rows_q, a.eps, a.rq, st);
+  if (e != hipSuccess) return e;
+  e = launch_rms<D, T>(a.k, rows_k, a.eps, a.rk, st);
+  if (e != hipSuccess) return e;
+  return launch_d<D, T, ACT_GELU>(0, a, grid_q, grid_k, st);
+}
+
 }  // namespace
 
-hipError_t launch_attn_bwd(int D, bool bf16, int wmode, const BwdArgs& a, int grid_q, int grid_k, hipStream_t st) {
+hipError_t launch_attn_bwd(int D, bool bf16, int act, int wmode, const BwdArgs& a, int64_t rows_q, int64_t rows_k,
+                           int grid_q, int grid_k, hipStream_t st) {
   if (bf16) {
-    if (D == 32) return launch_d<32, __bf16>(wmode, a, grid_q, grid_k, st);
-    if (D == 64) return launch_d<64, __bf16>(wmode, a, grid_q, grid_k, st);
-    return launch_d<128, __bf16>(wmode, a, grid_q, grid_k, st);
+    if (D == 32) return launch_all<32, __bf16>(act, wmode, a, rows_q, rows_k, grid_q, grid_k, st);
+    if (D == 64) return launch_all<64, __bf16>(act, wmode, a, rows_q, rows_k, grid_q, grid_k, st);
+    return launch_all<128, __bf16>(act, wmode, a, rows_q, rows_k, grid_q, grid_k, st);
   }
-  if (D == 32) return launch_d<32, float>(wmode, a, grid_q, grid_k, st);
-  if (D == 64) return launch_d<64, float>(wmode, a, grid_q, grid_k, st);
-  return launch_d<128, float>(wmode, a, grid_q, grid_k, st);
+  if (D == 32) return launch_all<32, float>(act, wmode, a, rows_q, rows_k, grid_q, grid_k, st);
+  if (D == 64) return launch_all<64, float>(act, wmode, a, rows_q, rows_k, grid_q, grid_k, st);
+  return launch_all<128, float>(act, wmode, a, rows_q, rows_k, grid_q, grid_k, st);
 }
 
 }  // namespace ja

@@ -117,11 +117,14 @@ struct BwdArgs {
   const WsHeader* hdr_k;    // plan over key tiles (swapped offsets)
   const WorkItem* items_k;
   float2* stats;            // per (query row, head): log2-sum-exp of the scores, D_i
+  float* rq;                // GELU: RMS factor per (query row, head)
+  float* rk;                // GELU: RMS factor per (key row, head)
   int H;
   int window_blocks;
   int window_tokens;
   float c2;                 // log2(e) / sqrt(D)
   float inv_sqrt_d;
+  float eps;                // GELU: RMSNorm epsilon
 };
 
 struct CombineArgs {

@@ -100,8 +100,13 @@ def test_bwd_host_validation():
     lib = _lib.load()
     ok = _lib.jagged_attn_bwd_workspace_size(4, 2, 32, _lib.JA_SELF, _lib.JA_SOFTMAX, 0, _lib.JA_BF16, 100, 100)
     assert ok > 0
-    assert _lib.jagged_attn_bwd_workspace_size(4, 2, 32, _lib.JA_CROSS, _lib.JA_GELU_TANH, 0, _lib.JA_BF16,
+    soft = _lib.jagged_attn_bwd_workspace_size(4, 2, 32, _lib.JA_CROSS, _lib.JA_SOFTMAX, 0, _lib.JA_BF16, 100, 50)
+    gelu = _lib.jagged_attn_bwd_workspace_size(4, 2, 32, _lib.JA_CROSS, _lib.JA_GELU_TANH, 0, _lib.JA_BF16, 100, 50)
+    assert gelu >= soft + 4 * 2 * (100 + 50)  # + the RMS factors of every query and key row
+    assert _lib.jagged_attn_bwd_workspace_size(4, 2, 32, _lib.JA_CROSS, _lib.JA_GELU_POLY, 0, _lib.JA_BF16,
                                                100, 50) == 0
+    assert _lib.jagged_attn_bwd_workspace_size(4, 2, 32, _lib.JA_SELF, _lib.JA_GELU_TANH, 64, _lib.JA_BF16,
+                                               100, 100) == 0
     assert _lib.jagged_attn_bwd_workspace_size(4, 2, 32, _lib.JA_SELF, _lib.JA_SOFTMAX, 0, _lib.JA_MXFP8_E4M3,
                                                100, 100) == 0
 
@@ -114,7 +119,7 @@ def test_bwd_host_validation():
         return lib.jagged_attn_bwd(ptr, ptr, ptr, ptr, ptr, ptr, 2, 1, 32, _lib.JA_SELF, act, 0,
                                    ptr, ptr, ptr, ctypes.byref(j))
 
-    assert call(act=_lib.JA_GELU_TANH) == _lib.JA_EUNSUPPORTED
+    assert call(act=_lib.JA_GELU_POLY) == _lib.JA_EUNSUPPORTED
     assert call(dtype=_lib.JA_MXFP8_E4M3) == _lib.JA_EUNSUPPORTED
     assert call(ptr=0) == _lib.JA_EINVAL
     assert call(ptr=4100) == _lib.JA_EINVAL

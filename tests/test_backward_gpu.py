@@ -1,6 +1,6 @@
-"""GPU parity of the softmax backward (jagged_attn_bwd) against the float64
-oracle (oracle.gdpa_backward) on the same inputs: every variant, window kind,
-head dim and input dtype, with empty and ragged samples."""
+"""GPU parity of the backward (jagged_attn_bwd) against the float64 oracle
+(oracle.gdpa_backward) on the same inputs: every variant, window kind, head
+dim and input dtype, softmax and GELU scores, with empty and ragged samples."""
 import sys
 
 import numpy as np
@@ -23,16 +23,16 @@ def log(msg):
     sys.stdout.flush()
 
 
-def run(variant, window, dtype, qo, ko, q, k, v, seed=0):
+def run(variant, window, dtype, qo, ko, q, k, v, seed=0, act="softmax"):
     dout = np.random.default_rng(seed).standard_normal(q.shape).astype(np.float32)
     dt = torch.float32 if dtype == "f32" else torch.bfloat16
     tq, tk, tv, tg = (torch.from_numpy(x).to(dt) for x in (q, k, v, dout))
     exact = [t.to(torch.float64).numpy() for t in (tq, tk, tv, tg)]
     to = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
     dq, dk, dv = backward(tq.cuda(), tk.cuda(), tv.cuda(), tg.cuda(), to(qo), to(ko), variant=variant,
-                          window=window, dtype=dtype, check=True)
+                          act=act, window=window, dtype=dtype, check=True)
     torch.cuda.synchronize()
-    ref = oracle.gdpa_backward(exact[0], exact[1], exact[2], exact[3], qo, ko, variant, "softmax", window)
+    ref = oracle.gdpa_backward(exact[0], exact[1], exact[2], exact[3], qo, ko, variant, act, window)
     for name, g, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
         g = g.cpu().numpy().astype(np.float64)
         # (a gradient that is exactly zero -- dQ, dK with one key per query --
@@ -70,3 +70,25 @@ def test_block_window_workload_slice():
     w = make_workload("block_window", scale=0.06)
     log(f"backward block_window slice B={w.B} N={w.total_q}")
     run("self", w.window, "bf16", w.q_offsets, w.kv_offsets, w.q, w.k, w.v, seed=3)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("D", [32, 64, 128])
+def test_gelu_cross_pma_self(D, dtype):
+    """GELU scores with QK-RMSNorm: cross (long Q, short K/V), PMA and full self."""
+    qo, ko, q, k, v = random_jagged(50 + D, [300, 0, 17, 64, 129], [40, 9, 0, 1, 64], 2, D)
+    log(f"backward gelu cross D={D} {dtype}")
+    run("cross", 0, dtype, qo, ko, q, k, v, seed=4, act="gelu_tanh")
+    qo, ko, q, k, v = random_jagged(51 + D, [32, 32, 32], [500, 1, 0], 2, D)
+    log(f"backward gelu pma D={D} {dtype}")
+    run("pma", 0, dtype, qo, ko, q, k, v, seed=5, act="gelu_tanh")
+    qo, ko, q, k, v = random_jagged(52 + D, EDGE, EDGE, 2, D)
+    log(f"backward gelu self D={D} {dtype}")
+    run("self", 0, dtype, qo, ko, q, k, v, seed=6, act="gelu_tanh")
+
+
+def test_cross_gelu_workload_slice():
+    """A slice of the cross-GELU workload (long Q, 16-64 keys, D = 128, bf16)."""
+    w = make_workload("cross_gelu", scale=0.02)
+    log(f"backward cross_gelu slice B={w.B} Nq={w.total_q} Nk={w.total_kv}")
+    run("cross", 0, "bf16", w.q_offsets, w.kv_offsets, w.q, w.k, w.v, seed=7, act="gelu_tanh")
