@@ -20,6 +20,7 @@ hipError_t launch_attn_pp(int D, int act, const AttnArgs& a, int num_cu, int64_t
 hipError_t launch_key_rms(int D, const void* k, int64_t rows, float eps, float* out, hipStream_t st);
 hipError_t launch_attn_bwd(int D, bool bf16, int act, int wmode, const BwdArgs& a, int64_t rows_q, int64_t rows_k,
                            int grid_q, int grid_k, hipStream_t st);
+hipError_t launch_attn_bwd_mfma(int D, int wmode, const BwdArgs& a, int grid_q, int grid_k, hipStream_t st);
 hipError_t launch_mx_quant(bool bf16, const void* x, int64_t n_blocks, uint8_t* codes, uint8_t* scales,
                            hipStream_t st);
 
@@ -385,9 +386,13 @@ int jagged_attn_bwd(const void* q, const void* k, const void* v, const void* dou
   const int grid_k = int(std::min<int64_t>(L.max_k > 0 ? L.max_k : 1, kMaxGrid));
   if (io->ev_start && hipEventRecord(reinterpret_cast<hipEvent_t>(io->ev_start), stream) != hipSuccess)
     return JA_EHIP;
-  if (launch_attn_bwd(D, io->dtype == JA_BF16, act == JA_SOFTMAX ? ACT_SOFTMAX : ACT_GELU, wmode, ba,
-                      int64_t(io->total_q) * H, int64_t(io->total_kv) * H, grid_q, grid_k, stream) != hipSuccess)
-    return JA_EHIP;
+  // bf16 softmax on the matrix cores; fp32 inputs and GELU scores on the fp32 VALU kernels
+  const hipError_t e = io->dtype == JA_BF16 && act == JA_SOFTMAX
+                           ? launch_attn_bwd_mfma(D, wmode, ba, grid_q, grid_k, stream)
+                           : launch_attn_bwd(D, io->dtype == JA_BF16, act == JA_SOFTMAX ? ACT_SOFTMAX : ACT_GELU,
+                                             wmode, ba, int64_t(io->total_q) * H, int64_t(io->total_kv) * H, grid_q,
+                                             grid_k, stream);
+  if (e != hipSuccess) return JA_EHIP;
   if (io->ev_stop && hipEventRecord(reinterpret_cast<hipEvent_t>(io->ev_stop), stream) != hipSuccess)
     return JA_EHIP;
   return JA_OK;

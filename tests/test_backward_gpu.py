@@ -13,9 +13,15 @@ from recsys_jagged_attention_amd.inputs import random_jagged, make_workload
 
 pytestmark = pytest.mark.gpu
 
-# max |grad - ref| <= TOL * max(max |ref|, 1) per tensor (fp32 arithmetic on
-# both input dtypes; the inputs are unit normal)
-TOL = {"f32": 1e-5, "bf16": 1e-4}
+# max |grad - ref| <= tol * max(max |ref|, 1) per tensor; the inputs are unit
+# normal.  fp32 inputs and GELU scores run in fp32 arithmetic throughout
+# (1e-5, 1e-4 for bf16 inputs).  bf16 softmax runs on bf16 MFMA with P and dS
+# rounded to bf16 (relative error up to 2^-8 per element, as P in the bf16
+# forward), so it takes the bf16 forward's 1e-2.
+def tol(dtype, act):
+    if dtype == "f32":
+        return 1e-5
+    return 1e-2 if act == "softmax" else 1e-4
 
 
 def log(msg):
@@ -40,7 +46,8 @@ def run(variant, window, dtype, qo, ko, q, k, v, seed=0, act="softmax"):
         scale = max(np.abs(r).max(), 1.0)
         err = np.abs(g - r).max() / scale
         assert np.isfinite(g).all(), name
-        assert err <= TOL[dtype], f"{name}: rel err {err:.3e}"
+        log(f"  {name}: rel err {err:.3e}")
+        assert err <= tol(dtype, act), f"{name}: rel err {err:.3e}"
     return dq
 
 
