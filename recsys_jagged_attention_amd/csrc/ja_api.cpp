@@ -134,7 +134,8 @@ Plan make_plan(int B, int H, int D, int variant, int act, int window, int dtype,
 
 // Backward workspace: two plans of 64-row tiles (over the queries, and over
 // the keys with the offsets swapped) and one (lse, D) pair per query row and head.
-constexpr int kBwdRows = 64;
+constexpr int kBwdRows = 64;        // rows per backward work item (VALU kernels, MFMA key side)
+constexpr int kBwdRowsMfmaQ = 128;  // query rows per item of the MFMA dQ kernel (4 waves)
 struct BwdLayout {
   size_t hdr_q, nsplit_q, pbase_q, items_q, hdr_k, nsplit_k, pbase_k, items_k, stats, rq, rk, total;
   int64_t max_q, max_k;
@@ -339,6 +340,8 @@ int jagged_attn_bwd(const void* q, const void* k, const void* v, const void* dou
   hipStream_t stream = reinterpret_cast<hipStream_t>(io->stream);
   unsigned char* ws = reinterpret_cast<unsigned char*>(io->workspace);
   const bool self = variant == JA_SELF || variant == JA_SLIDING;
+  // bf16 softmax on the matrix cores; fp32 inputs and GELU scores on the fp32 VALU kernels
+  const bool mfma = io->dtype == JA_BF16 && act == JA_SOFTMAX;
   for (int pass = 0; pass < 2; ++pass) {
     // pass 0: query tiles; pass 1: key tiles (the same plan on swapped offsets)
     PlanArgs pa{};
@@ -348,7 +351,7 @@ int jagged_attn_bwd(const void* q, const void* k, const void* v, const void* dou
     pa.H = H;
     pa.total_q = pass == 0 ? io->total_q : io->total_kv;
     pa.total_kv = pass == 0 ? io->total_kv : io->total_q;
-    pa.bm = kBwdRows;
+    pa.bm = mfma && pass == 0 ? kBwdRowsMfmaQ : kBwdRows;
     pa.kvc = 0;
     pa.self_check = self;
     pa.max_items = pass == 0 ? L.max_q : L.max_k;
@@ -386,9 +389,7 @@ int jagged_attn_bwd(const void* q, const void* k, const void* v, const void* dou
   const int grid_k = int(std::min<int64_t>(L.max_k > 0 ? L.max_k : 1, kMaxGrid));
   if (io->ev_start && hipEventRecord(reinterpret_cast<hipEvent_t>(io->ev_start), stream) != hipSuccess)
     return JA_EHIP;
-  // bf16 softmax on the matrix cores; fp32 inputs and GELU scores on the fp32 VALU kernels
-  const hipError_t e = io->dtype == JA_BF16 && act == JA_SOFTMAX
-                           ? launch_attn_bwd_mfma(D, wmode, ba, grid_q, grid_k, stream)
+  const hipError_t e = mfma ? launch_attn_bwd_mfma(D, wmode, ba, grid_q, grid_k, stream)
                            : launch_attn_bwd(D, io->dtype == JA_BF16, act == JA_SOFTMAX ? ACT_SOFTMAX : ACT_GELU,
                                              wmode, ba, int64_t(io->total_q) * H, int64_t(io->total_kv) * H, grid_q,
                                              grid_k, stream);

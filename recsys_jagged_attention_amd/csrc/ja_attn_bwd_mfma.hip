@@ -5,15 +5,15 @@
 //   P = softmax(Q K^T / sqrt(D)),  dV = P^T dO,  dS = P * (dO V^T - D_i),
 //   D_i = rowsum(P * (dO V^T)),    dQ = dS K / sqrt(D),  dK = dS^T Q / sqrt(D).
 //
-// Two kernels of two waves each, 32 rows per wave, all products on
-// v_mfma_f32_32x32x16_bf16 with fp32 accumulation (P and dS enter their
-// products in bf16, as P does in the forward):
-//  * bwd_dq_mfma_kernel, 64 query rows per item.  Lane column = query.  Over
+// Two kernels, 32 rows per wave, all products on v_mfma_f32_32x32x16_bf16
+// with fp32 accumulation (P and dS enter their products in bf16, as P does in
+// the forward):
+//  * bwd_dq_mfma_kernel, 4 waves, 128 query rows per item.  Lane column = query.  Over
 //    the item's key tiles it forms S^T = K Q^T and dP^T = V dO^T; a first pass
 //    keeps the online max, sum and sum of p * dP (giving the log-sum-exp and
 //    D_i, stored for the second kernel), a second pass accumulates
 //    dQ^T += K^T dS^T.
-//  * bwd_dkv_mfma_kernel, 64 key rows per item (kept in LDS).  Lane column =
+//  * bwd_dkv_mfma_kernel, 2 waves, 64 key rows per item (kept in LDS).  Lane column =
 //    key.  Over the 32-query tiles that see the item it forms S = Q K^T and
 //    dP = dO V^T, P from the stored statistics, then dV^T += dO^T P and
 //    dK^T += Q^T dS.
@@ -21,15 +21,13 @@
 // registers of lane half h hold, for each 16-row step, the 8 contiguous rows
 // 8h..8h+7: exactly the B operand of the next product (no shuffle).  The
 // transposed A operands (K^T, dO^T, Q^T) come from ds_read_b64_tr_b16 on
-// row-major LDS tiles.  Plain synchronous tile loads; several workgroups per
-// CU hide their latency.
+// row-major LDS tiles (rows padded by 16 bytes).  Tiles arrive by
+// direct-to-LDS loads into two stages: tile s + 1 loads while tile s is used.
 #include "ja_mfma_util.h"
 #include "jagged_attn.h"
 
 namespace ja {
 namespace {
-
-constexpr int kMT = 128;  // two waves
 
 template <int D>
 struct BT {
@@ -37,20 +35,6 @@ struct BT {
   static constexpr int kS = D / 16;  // k-steps over D
   static constexpr int kT = D / 32;  // 32-row output tiles over D
 };
-
-// Rows [0, nrows) of a global [*, H, D] slice (row stride `gstride` elements)
-// into an LDS tile with row stride kRS; rows >= valid are zero-filled.
-template <int D, int NROWS>
-__device__ __forceinline__ void load_tile(__bf16* lds, const __bf16* g, size_t gstride, int valid) {
-  constexpr int kChunks = D / 8;
-#pragma unroll 4
-  for (int c = threadIdx.x; c < NROWS * kChunks; c += kMT) {
-    const int r = c / kChunks, cc = c % kChunks;
-    bf16x8 x = zero8();
-    if (r < valid) x = *reinterpret_cast<const bf16x8*>(g + size_t(r) * gstride + 8 * cc);
-    *reinterpret_cast<bf16x8*>(lds + r * BT<D>::kRS + 8 * cc) = x;
-  }
-}
 
 // A operand (row `row` of a row-major tile, k-step cc): lane half g supplies
 // dims (D/2) g + 8 cc .. +8.  B operands held in registers use the same split.
@@ -136,18 +120,62 @@ __device__ __forceinline__ bool allowed(const BwdArgs& a, int i, int j) {
   }
 }
 
+// Direct-to-LDS tile loads into the padded layout: slot L (16 bytes) of an
+// LDS tile is row L / kCpr, chunk L % kCpr; the last chunk of every row is
+// padding (it loads a duplicate) and the tile is rounded up to whole wave
+// instructions (1 KB each).  Rows at or past `valid` load row valid-1: finite
+// values whose weights are zero.
+template <int D, int NROWS>
+struct Dma {
+  static constexpr int kCpr = D / 8 + 1;                   // slots per padded row
+  static constexpr int kInstr = (NROWS * kCpr + 63) / 64;  // wave instructions per tile
+  static constexpr int kBytes = kInstr * 1024;
+  // instructions issued by wave w of nw (i = w, w + nw, ...)
+  static constexpr int count(int w, int nw) { return (kInstr - w + nw - 1) / nw; }
+};
+
+template <int D, int NROWS, int NW>
+__device__ __forceinline__ void dma_tile(unsigned lds, const void* g, unsigned grow_bytes, int valid, int wave,
+                                         int lane) {
+  using T = Dma<D, NROWS>;
+  for (int i = wave; i < T::kInstr; i += NW) {
+    const int slot = 64 * i + lane;
+    int row = slot / T::kCpr;
+    int c = slot - row * T::kCpr;
+    if (c == T::kCpr - 1) c = 0;
+    row = min(row, valid - 1);
+    lds_dma16(g, unsigned(row) * grow_bytes + 16u * unsigned(c), lds + 1024u * unsigned(i));
+  }
+}
+
+// Wait until at most N of this wave's VMEM instructions are outstanding (N < 64).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+constexpr int kQWaves = 4;  // dq kernel: 4 waves x 32 query rows (128-row items)
+constexpr int kKWaves = 2;  // dkv kernel: 2 waves x 32 key rows (64-row items)
+
 template <int D, int WMODE>
-__global__ __launch_bounds__(kMT) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_mfma_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_mfma_kernel(BwdArgs a) {
   using L = BT<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 ks[64 * L::kRS];
-  __shared__ __attribute__((aligned(16))) __bf16 vs[64 * L::kRS];
+  using T = Dma<D, 64>;
+  // per-wave DMA count of one K + V tile (every wave past the first issues the same number)
+  constexpr int kN0 = 2 * T::count(0, kQWaves), kN1 = 2 * T::count(1, kQWaves);
+  static_assert(T::count(1, kQWaves) == T::count(kQWaves - 1, kQWaves), "waves 1.. issue equally");
+  __shared__ __attribute__((aligned(1024))) unsigned char buf[2][2][T::kBytes];  // [stage][K, V]
   const __bf16* qg = reinterpret_cast<const __bf16*>(a.q);
   const __bf16* kg = reinterpret_cast<const __bf16*>(a.k);
   const __bf16* vg = reinterpret_cast<const __bf16*>(a.v);
   const __bf16* gg = reinterpret_cast<const __bf16*>(a.dout);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l32 = lane & 31, g = lane >> 5;
+  const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // (scalar: uniform loops)
   const int kp = key_perm(l32);
   const size_t gstride = size_t(a.H) * D;
+  const unsigned grow = unsigned(gstride) * 2u;
+  const unsigned lds0 = lds_addr_of(&buf[0][0][0]);
   const int n_items = a.hdr_q->n_items;
   for (int idx = blockIdx.x; idx < n_items; idx += gridDim.x) {
     const WorkItem it = a.items_q[idx];
@@ -162,21 +190,54 @@ __global__ __launch_bounds__(kMT) __attribute__((amdgpu_waves_per_eu(2))) void b
         qf[cc] = *reinterpret_cast<const bf16x8*>(qg + off + 8 * cc);
         gf[cc] = *reinterpret_cast<const bf16x8*>(gg + off + 8 * cc);
       }
+      // Wait here, before any tile load: the compiler then knows these are
+      // complete and puts no wait for them (which would also drain the
+      // untracked tile loads) inside the loops.
+      wait_vm<0>();
     }
-    int klo, khi, olo, ohi;
+    // this wave's key tiles [wt_lo, wt_hi) and the workgroup's [t_lo, t_hi)
+    int klo, khi;
     wave_keys<WMODE>(a, r0, it.lq, it.lk, klo, khi);
-    wave_keys<WMODE>(a, it.q0 + 32 * (1 - wave), it.lq, it.lk, olo, ohi);
     const int wt_lo = klo / 64, wt_hi = khi > klo ? (khi + 63) / 64 : wt_lo;
-    const int ot_lo = olo / 64, ot_hi = ohi > olo ? (ohi + 63) / 64 : ot_lo;
-    int t_lo = min(wt_hi > wt_lo ? wt_lo : 1 << 30, ot_hi > ot_lo ? ot_lo : 1 << 30);
-    const int t_hi = max(wt_hi > wt_lo ? wt_hi : 0, ot_hi > ot_lo ? ot_hi : 0);
+    int t_lo = 1 << 30, t_hi = 0;
+    for (int w = 0; w < kQWaves; ++w) {
+      int lo, hi;
+      wave_keys<WMODE>(a, it.q0 + 32 * w, it.lq, it.lk, lo, hi);
+      if (hi > lo) {
+        t_lo = min(t_lo, lo / 64);
+        t_hi = max(t_hi, (hi + 63) / 64);
+      }
+    }
     if (t_lo > t_hi) t_lo = t_hi;
+    const int nt = t_hi - t_lo;
     const __bf16* kbase = kg + size_t(it.kbeg) * gstride + size_t(it.h) * D;
     const __bf16* vbase = vg + size_t(it.kbeg) * gstride + size_t(it.h) * D;
 
+    // Each pass walks tiles t_lo .. t_hi - 1; tile s + 1 loads into the other
+    // stage while tile s is used.
+    auto issue = [&](int s) __attribute__((always_inline)) {
+      const int t = t_lo + s;
+      const int valid = min(64, it.lk - 64 * t);
+      const unsigned st = lds0 + unsigned(s & 1) * 2u * T::kBytes;
+      dma_tile<D, 64, kQWaves>(st, kbase + size_t(64 * t) * gstride, grow, valid, wave, lane);
+      dma_tile<D, 64, kQWaves>(st + T::kBytes, vbase + size_t(64 * t) * gstride, grow, valid, wave, lane);
+    };
+    // Start of step s: issue tile s + 1, wait for tile s, barrier.
+    auto step_begin = [&](int s) __attribute__((always_inline)) {
+      if (s + 1 < nt) {
+        issue(s + 1);
+        if (wave == 0) wait_vm<kN0>();
+        else wait_vm<kN1>();
+      } else {
+        wait_vm<0>();
+      }
+      lds_barrier();  // tile s is in LDS for every wave
+    };
+
     // Scores and dP^T of keys 64 t + 32 kb .. +32 for this wave's queries
     // (one 32-key block at a time keeps the live registers down).
-    auto scores = [&](int t, int kb, f32x16& s, f32x16& dp) __attribute__((always_inline)) {
+    auto scores = [&](const __bf16* ks, const __bf16* vs, int t, int kb, f32x16& s, f32x16& dp)
+                      __attribute__((always_inline)) {
       f32x16 x = {}, y = {};
 #pragma unroll
       for (int cc = 0; cc < L::kS; ++cc) {
@@ -193,40 +254,40 @@ __global__ __launch_bounds__(kMT) __attribute__((amdgpu_waves_per_eu(2))) void b
       s = x;
       dp = y;
     };
-    auto load_kv = [&](int t) __attribute__((always_inline)) {
-      __syncthreads();  // the previous tile's readers are done
-      const int valid = min(64, it.lk - 64 * t);
-      load_tile<D, 64>(ks, kbase + size_t(64 * t) * gstride, gstride, valid);
-      load_tile<D, 64>(vs, vbase + size_t(64 * t) * gstride, gstride, valid);
-      __syncthreads();
-    };
 
-    // Pass 1: log-sum-exp (base 2) and D_i = sum_j p_ij dP_ij.
+    // Pass 1: online max, sum and sum of p * dP -> log-sum-exp (base 2) and
+    // D_i = sum_j p_ij dP_ij of the row, for pass 2 and the dK/dV kernel.
     float m = -__builtin_huge_valf(), l = 0.f, acc = 0.f;
-    for (int t = t_lo; t < t_hi; ++t) {
-      load_kv(t);
-      if (t < wt_lo || t >= wt_hi) continue;
+    if (nt > 0) issue(0);
+    for (int s = 0; s < nt; ++s) {
+      step_begin(s);
+      const int t = t_lo + s;
+      if (t >= wt_lo && t < wt_hi) {
+        const __bf16* ks = reinterpret_cast<const __bf16*>(&buf[s & 1][0][0]);
+        const __bf16* vs = reinterpret_cast<const __bf16*>(&buf[s & 1][1][0]);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        f32x16 s, dp;
-        scores(t, kb, s, dp);
-        float mx = -__builtin_huge_valf();
+        for (int kb = 0; kb < 2; ++kb) {
+          f32x16 sc, dp;
+          scores(ks, vs, t, kb, sc, dp);
+          float mx = -__builtin_huge_valf();
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
-        const float mn = fmaxf(m, max_halves(mx));
-        // (no branch: the MFMAs of the next block run with the whole wave)
-        const float mref = mn == -__builtin_huge_valf() ? 0.f : mn;  // nothing allowed yet
-        const float sc = exp2f(m - mref);                             // m = -inf -> 0
-        l *= sc;
-        acc *= sc;
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[i]);
+          const float mn = fmaxf(m, max_halves(mx));
+          // (no branch: the MFMAs of the next block run with the whole wave)
+          const float mref = mn == -__builtin_huge_valf() ? 0.f : mn;  // nothing allowed yet
+          const float r = exp2f(m - mref);                              // m = -inf -> 0
+          l *= r;
+          acc *= r;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = exp2f(s[i] - mref);
-          l += p;
-          acc = fmaf(p, dp[i], acc);
+          for (int i = 0; i < 16; ++i) {
+            const float p = exp2f(sc[i] - mref);
+            l += p;
+            acc = fmaf(p, dp[i], acc);
+          }
+          m = mn;
         }
-        m = mn;
       }
+      lds_barrier();  // every wave is done with stage s & 1 before tile s + 2 loads into it
     }
     l = sum_halves(l);
     acc = sum_halves(acc);
@@ -238,24 +299,30 @@ __global__ __launch_bounds__(kMT) __attribute__((amdgpu_waves_per_eu(2))) void b
     f32x16 dq[L::kT];
 #pragma unroll
     for (int t2 = 0; t2 < L::kT; ++t2) dq[t2] = f32x16{};
-    for (int t = t_lo; t < t_hi; ++t) {
-      load_kv(t);
-      if (t < wt_lo || t >= wt_hi) continue;
+    if (nt > 0) issue(0);
+    for (int s = 0; s < nt; ++s) {
+      step_begin(s);
+      const int t = t_lo + s;
+      if (t >= wt_lo && t < wt_hi) {
+        const __bf16* ks = reinterpret_cast<const __bf16*>(&buf[s & 1][0][0]);
+        const __bf16* vs = reinterpret_cast<const __bf16*>(&buf[s & 1][1][0]);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        f32x16 s, dp;
-        scores(t, kb, s, dp);
+        for (int kb = 0; kb < 2; ++kb) {
+          f32x16 sc, dp;
+          scores(ks, vs, t, kb, sc, dp);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[i] = exp2f(s[i] - lse) * (dp[i] - di);
+          for (int i = 0; i < 16; ++i) sc[i] = exp2f(sc[i] - lse) * (dp[i] - di);
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const bf16x8 db = to_b(s, half);
+          for (int half = 0; half < 2; ++half) {
+            const bf16x8 db = to_b(sc, half);
 #pragma unroll
-          for (int t2 = 0; t2 < L::kT; ++t2)
-            dq[t2] = mfma_32x32x16(read_at<D>(ks, 32 * kb + 16 * half, t2, lane), db, dq[t2]);
-          __builtin_amdgcn_sched_barrier(0);  // (bounds the operand reads in flight: registers)
+            for (int t2 = 0; t2 < L::kT; ++t2)
+              dq[t2] = mfma_32x32x16(read_at<D>(ks, 32 * kb + 16 * half, t2, lane), db, dq[t2]);
+            __builtin_amdgcn_sched_barrier(0);  // (bounds the operand reads in flight: registers)
+          }
         }
       }
+      lds_barrier();  // every wave is done with stage s & 1 before tile s + 2 loads into it
     }
     if (qrow < it.lq) {
       float* out = a.dq + (size_t(it.qbeg + qrow) * a.H + it.h) * D;
@@ -275,20 +342,28 @@ __global__ __launch_bounds__(kMT) __attribute__((amdgpu_waves_per_eu(2))) void b
 }
 
 template <int D, int WMODE>
-__global__ __launch_bounds__(kMT) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkv_mfma_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * kKWaves) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkv_mfma_kernel(BwdArgs a) {
   using L = BT<D>;
-  __shared__ __attribute__((aligned(16))) __bf16 kst[64 * L::kRS];  // the item's keys and values
-  __shared__ __attribute__((aligned(16))) __bf16 vst[64 * L::kRS];
-  __shared__ __attribute__((aligned(16))) __bf16 qs[32 * L::kRS];   // one 32-query tile and its dO
-  __shared__ __attribute__((aligned(16))) __bf16 gs[32 * L::kRS];
-  __shared__ float2 st[32];
+  using TK = Dma<D, 64>;
+  using TQ = Dma<D, 32>;
+  // per-wave DMAs of one query step: Q and dO tiles, plus the statistics (wave 0)
+  constexpr int kN0 = 2 * TQ::count(0, kKWaves) + 1, kN1 = 2 * TQ::count(1, kKWaves);
+  __shared__ __attribute__((aligned(1024))) unsigned char kvb[2][TK::kBytes];    // the item's K, V
+  __shared__ __attribute__((aligned(1024))) unsigned char qb[2][2][TQ::kBytes];  // [stage][Q, dO]
+  __shared__ __attribute__((aligned(256))) float2 stb[2][32];                    // [stage] (lse, D_i)
   const __bf16* qg = reinterpret_cast<const __bf16*>(a.q);
   const __bf16* kg = reinterpret_cast<const __bf16*>(a.k);
   const __bf16* vg = reinterpret_cast<const __bf16*>(a.v);
   const __bf16* gg = reinterpret_cast<const __bf16*>(a.dout);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, l32 = lane & 31, g = lane >> 5;
+  const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // (scalar: uniform loops)
   const int kp = key_perm(l32);
   const size_t gstride = size_t(a.H) * D;
+  const unsigned grow = unsigned(gstride) * 2u;
+  const unsigned lds_kv = lds_addr_of(&kvb[0][0]), lds_q = lds_addr_of(&qb[0][0][0]);
+  const unsigned lds_st = lds_addr_of(&stb[0][0]);
+  const __bf16* kst = reinterpret_cast<const __bf16*>(&kvb[0][0]);
+  const __bf16* vst = reinterpret_cast<const __bf16*>(&kvb[1][0]);
   const int n_items = a.hdr_k->n_items;
   for (int idx = blockIdx.x; idx < n_items; idx += gridDim.x) {
     // (items over key tiles: the plan ran on the swapped offsets, so the
@@ -297,25 +372,37 @@ __global__ __launch_bounds__(kMT) __attribute__((amdgpu_waves_per_eu(2))) void b
     const int lk = it.lq, lq = it.lk, kbeg = it.qbeg, qbeg = it.kbeg;
     const int k0 = it.q0 + 32 * wave;
     const int krow = k0 + l32;
-    // K and V rows of the item stay in LDS (B operands read per use: the
-    // dK^T and dV^T accumulators take the registers).
-    __syncthreads();  // the previous item's readers are done
-    {
-      const int valid = min(64, lk - it.q0);
-      const size_t off = size_t(kbeg + it.q0) * gstride + size_t(it.h) * D;
-      load_tile<D, 64>(kst, kg + off, gstride, valid);
-      load_tile<D, 64>(vst, vg + off, gstride, valid);
-    }
-    int qlo, qhi, olo, ohi;
+    int qlo, qhi;
     wave_queries<WMODE>(a, k0, lq, lk, qlo, qhi);
-    wave_queries<WMODE>(a, it.q0 + 32 * (1 - wave), lq, lk, olo, ohi);
     const int wt_lo = qlo / 32, wt_hi = qhi > qlo ? (qhi + 31) / 32 : wt_lo;
-    const int ot_lo = olo / 32, ot_hi = ohi > olo ? (ohi + 31) / 32 : ot_lo;
-    int t_lo = min(wt_hi > wt_lo ? wt_lo : 1 << 30, ot_hi > ot_lo ? ot_lo : 1 << 30);
-    const int t_hi = max(wt_hi > wt_lo ? wt_hi : 0, ot_hi > ot_lo ? ot_hi : 0);
+    int t_lo = 1 << 30, t_hi = 0;
+    for (int w = 0; w < kKWaves; ++w) {
+      int lo, hi;
+      wave_queries<WMODE>(a, it.q0 + 32 * w, lq, lk, lo, hi);
+      if (hi > lo) {
+        t_lo = min(t_lo, lo / 32);
+        t_hi = max(t_hi, (hi + 31) / 32);
+      }
+    }
     if (t_lo > t_hi) t_lo = t_hi;
+    const int nt = t_hi - t_lo;
     const __bf16* qbase = qg + size_t(qbeg) * gstride + size_t(it.h) * D;
     const __bf16* gbase = gg + size_t(qbeg) * gstride + size_t(it.h) * D;
+    const float2* sbase = a.stats + size_t(qbeg) * a.H + it.h;
+
+    // Query tile t_lo + s into stage s & 1: Q, dO and the statistics.
+    auto issue_q = [&](int s) __attribute__((always_inline)) {
+      const int t = t_lo + s;
+      const int valid = min(32, lq - 32 * t);
+      const unsigned st = lds_q + unsigned(s & 1) * 2u * TQ::kBytes;
+      dma_tile<D, 32, kKWaves>(st, qbase + size_t(32 * t) * gstride, grow, valid, wave, lane);
+      dma_tile<D, 32, kKWaves>(st + TQ::kBytes, gbase + size_t(32 * t) * gstride, grow, valid, wave, lane);
+      if (wave == 0) {
+        const unsigned row = unsigned(min(lane >> 1, valid - 1));
+        lds_dma4(sbase + size_t(32 * t) * a.H, (row * unsigned(a.H)) * 8u + 4u * unsigned(lane & 1),
+                 lds_st + unsigned(s & 1) * 256u);
+      }
+    };
 
     f32x16 dk[L::kT], dv[L::kT];
 #pragma unroll
@@ -323,43 +410,57 @@ __global__ __launch_bounds__(kMT) __attribute__((amdgpu_waves_per_eu(2))) void b
       dk[t2] = f32x16{};
       dv[t2] = f32x16{};
     }
-    for (int t = t_lo; t < t_hi; ++t) {
-      __syncthreads();  // the previous tile's readers are done
-      const int valid = min(32, lq - 32 * t);
-      load_tile<D, 32>(qs, qbase + size_t(32 * t) * gstride, gstride, valid);
-      load_tile<D, 32>(gs, gbase + size_t(32 * t) * gstride, gstride, valid);
-      if (threadIdx.x < 32)
-        st[threadIdx.x] = int(threadIdx.x) < valid
-                              ? a.stats[size_t(qbeg + 32 * t + int(threadIdx.x)) * a.H + it.h]
-                              : make_float2(0.f, 0.f);
-      __syncthreads();
-      if (t < wt_lo || t >= wt_hi) continue;
-      f32x16 s = {}, dp = {};
-#pragma unroll
-      for (int cc = 0; cc < L::kS; ++cc) {
-        s = mfma_32x32x16(read_a<D>(qs, kp, g, cc), read_a<D>(kst, 32 * wave + l32, g, cc), s);
-        dp = mfma_32x32x16(read_a<D>(gs, kp, g, cc), read_a<D>(vst, 32 * wave + l32, g, cc), dp);
+    if (nt > 0) {
+      // the item's K and V rows stay in LDS (B operands read per use: the
+      // dK^T and dV^T accumulators take the registers)
+      const int valid = min(64, lk - it.q0);
+      const size_t off = size_t(kbeg + it.q0) * gstride + size_t(it.h) * D;
+      dma_tile<D, 64, kKWaves>(lds_kv, kg + off, grow, valid, wave, lane);
+      dma_tile<D, 64, kKWaves>(lds_kv + TK::kBytes, vg + off, grow, valid, wave, lane);
+      issue_q(0);
+    }
+    for (int s = 0; s < nt; ++s) {
+      if (s + 1 < nt) {
+        issue_q(s + 1);
+        if (wave == 0) wait_vm<kN0>();
+        else wait_vm<kN1>();
+      } else {
+        wait_vm<0>();
       }
+      lds_barrier();  // tile s (and the item's K, V) in LDS for every wave
+      const int t = t_lo + s;
+      if (t >= wt_lo && t < wt_hi) {
+        const __bf16* qs = reinterpret_cast<const __bf16*>(&qb[s & 1][0][0]);
+        const __bf16* gs = reinterpret_cast<const __bf16*>(&qb[s & 1][1][0]);
+        const float2* st = &stb[s & 1][0];
+        f32x16 sc = {}, dp = {};
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int qi = c_row(i, g);
-        const int q = 32 * t + qi;
-        const float2 sv = st[qi];
-        const bool ok = q < lq && krow < lk && allowed<WMODE>(a, q, krow);
-        const float p = ok ? exp2f(s[i] * a.c2 - sv.x) : 0.f;
-        s[i] = p;
-        dp[i] = p * (dp[i] - sv.y);
-      }
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        const bf16x8 pb = to_b(s, kc), db = to_b(dp, kc);
-#pragma unroll
-        for (int t2 = 0; t2 < L::kT; ++t2) {
-          dv[t2] = mfma_32x32x16(read_at<D>(gs, 16 * kc, t2, lane), pb, dv[t2]);
-          dk[t2] = mfma_32x32x16(read_at<D>(qs, 16 * kc, t2, lane), db, dk[t2]);
+        for (int cc = 0; cc < L::kS; ++cc) {
+          sc = mfma_32x32x16(read_a<D>(qs, kp, g, cc), read_a<D>(kst, 32 * wave + l32, g, cc), sc);
+          dp = mfma_32x32x16(read_a<D>(gs, kp, g, cc), read_a<D>(vst, 32 * wave + l32, g, cc), dp);
         }
-        __builtin_amdgcn_sched_barrier(0);  // (bounds the operand reads in flight: registers)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int qi = c_row(i, g);
+          const int q = 32 * t + qi;
+          const float2 sv = st[qi];
+          const bool ok = q < lq && krow < lk && allowed<WMODE>(a, q, krow);
+          const float p = ok ? exp2f(sc[i] * a.c2 - sv.x) : 0.f;
+          sc[i] = p;
+          dp[i] = p * (dp[i] - sv.y);
+        }
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+          const bf16x8 pb = to_b(sc, kc), db = to_b(dp, kc);
+#pragma unroll
+          for (int t2 = 0; t2 < L::kT; ++t2) {
+            dv[t2] = mfma_32x32x16(read_at<D>(gs, 16 * kc, t2, lane), pb, dv[t2]);
+            dk[t2] = mfma_32x32x16(read_at<D>(qs, 16 * kc, t2, lane), db, dk[t2]);
+          }
+          __builtin_amdgcn_sched_barrier(0);  // (bounds the operand reads in flight: registers)
+        }
       }
+      lds_barrier();  // every wave is done with stage s & 1 before tile s + 2 loads into it
     }
     if (krow < lk) {
       float* odk = a.dk + (size_t(kbeg + krow) * a.H + it.h) * D;
@@ -386,8 +487,8 @@ __global__ __launch_bounds__(kMT) __attribute__((amdgpu_waves_per_eu(2))) void b
 
 template <int D, int WMODE>
 hipError_t launch_w(const BwdArgs& a, int grid_q, int grid_k, hipStream_t st) {
-  hipLaunchKernelGGL((bwd_dq_mfma_kernel<D, WMODE>), dim3(grid_q), dim3(kMT), 0, st, a);
-  hipLaunchKernelGGL((bwd_dkv_mfma_kernel<D, WMODE>), dim3(grid_k), dim3(kMT), 0, st, a);
+  hipLaunchKernelGGL((bwd_dq_mfma_kernel<D, WMODE>), dim3(grid_q), dim3(64 * kQWaves), 0, st, a);
+  hipLaunchKernelGGL((bwd_dkv_mfma_kernel<D, WMODE>), dim3(grid_k), dim3(64 * kKWaves), 0, st, a);
   return hipGetLastError();
 }
 
