@@ -280,11 +280,11 @@ def run_backward(args):
     ms_per_step = (t1 - t0) * 1e3 / K
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / kern_s / 1e12
-    # bf16 softmax runs on bf16 MFMA; fp32 inputs and GELU scores on the fp32 VALU
-    on_mfma = w.dtype == "bf16" and w.act == "softmax"
+    # bf16 inputs run on bf16 MFMA; fp32 inputs on the fp32 VALU
+    on_mfma = w.dtype == "bf16"
     bound, peak = ("mfma", PEAK_TFLOPS["bf16"]) if on_mfma else ("alu", PEAK_VALU_F32)
-    kernels = ("bwd_dq_mfma_kernel + bwd_dkv_mfma_kernel" if on_mfma else
-               ("bwd_rms_kernel + " if w.act != "softmax" else "") + "bwd_q_kernel + bwd_kv_kernel")
+    kernels = (("bwd_rms_kernel + " if w.act != "softmax" else "") +
+               ("bwd_dq_mfma_kernel + bwd_dkv_mfma_kernel" if on_mfma else "bwd_q_kernel + bwd_kv_kernel"))
     log(f"[bench] backward {w.name}: {ms_per_step * 1e3:.1f} us/step, kernels {kern_s * 1e6:.1f} us, "
         f"{achieved:.2f} useful TFLOP/s ({100 * achieved / peak:.1f}% of the {bound} peak {peak})")
     cpu = None

@@ -20,7 +20,9 @@ hipError_t launch_attn_pp(int D, int act, const AttnArgs& a, int num_cu, int64_t
 hipError_t launch_key_rms(int D, const void* k, int64_t rows, float eps, float* out, hipStream_t st);
 hipError_t launch_attn_bwd(int D, bool bf16, int act, int wmode, const BwdArgs& a, int64_t rows_q, int64_t rows_k,
                            int grid_q, int grid_k, hipStream_t st);
-hipError_t launch_attn_bwd_mfma(int D, int wmode, const BwdArgs& a, int grid_q, int grid_k, hipStream_t st);
+hipError_t launch_attn_bwd_mfma(int D, int act, int wmode, const BwdArgs& a, int grid_q, int grid_k,
+                                hipStream_t st);
+hipError_t launch_bwd_rms(int D, bool bf16, const BwdArgs& a, int64_t rows_q, int64_t rows_k, hipStream_t st);
 hipError_t launch_mx_quant(bool bf16, const void* x, int64_t n_blocks, uint8_t* codes, uint8_t* scales,
                            hipStream_t st);
 
@@ -340,8 +342,8 @@ int jagged_attn_bwd(const void* q, const void* k, const void* v, const void* dou
   hipStream_t stream = reinterpret_cast<hipStream_t>(io->stream);
   unsigned char* ws = reinterpret_cast<unsigned char*>(io->workspace);
   const bool self = variant == JA_SELF || variant == JA_SLIDING;
-  // bf16 softmax on the matrix cores; fp32 inputs and GELU scores on the fp32 VALU kernels
-  const bool mfma = io->dtype == JA_BF16 && act == JA_SOFTMAX;
+  // bf16 inputs on the matrix cores; fp32 inputs on the fp32 VALU kernels
+  const bool mfma = io->dtype == JA_BF16;
   for (int pass = 0; pass < 2; ++pass) {
     // pass 0: query tiles; pass 1: key tiles (the same plan on swapped offsets)
     PlanArgs pa{};
@@ -389,7 +391,11 @@ int jagged_attn_bwd(const void* q, const void* k, const void* v, const void* dou
   const int grid_k = int(std::min<int64_t>(L.max_k > 0 ? L.max_k : 1, kMaxGrid));
   if (io->ev_start && hipEventRecord(reinterpret_cast<hipEvent_t>(io->ev_start), stream) != hipSuccess)
     return JA_EHIP;
-  const hipError_t e = mfma ? launch_attn_bwd_mfma(D, wmode, ba, grid_q, grid_k, stream)
+  if (mfma && act != JA_SOFTMAX &&
+      launch_bwd_rms(D, true, ba, int64_t(io->total_q) * H, int64_t(io->total_kv) * H, stream) != hipSuccess)
+    return JA_EHIP;
+  const hipError_t e = mfma ? launch_attn_bwd_mfma(D, act == JA_SOFTMAX ? ACT_SOFTMAX : ACT_GELU, wmode, ba,
+                                                   grid_q, grid_k, stream)
                            : launch_attn_bwd(D, io->dtype == JA_BF16, act == JA_SOFTMAX ? ACT_SOFTMAX : ACT_GELU,
                                              wmode, ba, int64_t(io->total_q) * H, int64_t(io->total_kv) * H, grid_q,
                                              grid_k, stream);

@@ -8,8 +8,9 @@
 //   dQ = dS K / sqrt(D),  dK = dS^T Q / sqrt(D).
 // Nothing is kept from the forward: the row statistics are recomputed.
 //
-// fp32 VALU kernels, four lanes per row (D/4 dimensions each, dot products
-// finished by two lane shuffles):
+// fp32 VALU kernels for fp32 inputs (bf16 inputs take the MFMA kernels of
+// ja_attn_bwd_mfma.hip), four lanes per row (D/4 dimensions each, dot
+// products finished by two lane shuffles):
 //  * bwd_q_kernel, one row per query: the row's max and sum (log-sum-exp,
 //    base 2), then D_i = sum_j p_ij (dO_i . v_j), then dQ_i; it leaves
 //    (lse_i, D_i) for the second kernel;
@@ -52,17 +53,6 @@ __device__ __forceinline__ float row_sum(float x) {
   x += quad_perm<0xB1>(x);  // lanes [1, 0, 3, 2] of the quad
   x += quad_perm<0x4E>(x);  // lanes [2, 3, 0, 1]
   return x;
-}
-
-// gelu(x) = x t and gelu'(x) = t + 2 x t (1 - t) u'(x), where t = sigmoid(2u),
-// u = sqrt(2/pi) (x + 0.044715 x^3) (from 1 + tanh(u) = 2 sigmoid(2u)).
-__device__ __forceinline__ void gelu_and_grad(float x, float& g, float& gp) {
-  constexpr float kC = 0.7978845608028654f;  // sqrt(2/pi)
-  constexpr float kA = 0.044715f;
-  const float u = kC * fmaf(kA * x, x * x, x);
-  const float t = 1.0f / (1.0f + exp2f(-2.0f * 1.4426950408889634f * u));
-  g = x * t;
-  gp = fmaf(2.0f * x * t * (1.0f - t), kC * fmaf(3.0f * kA, x * x, 1.0f), t);
 }
 
 // RMS factor (mean(x^2) + eps)^(-1/2) of every row of a [rows, D] tensor,
@@ -355,13 +345,31 @@ hipError_t launch_all(int act, int wmode, const BwdArgs& a, int64_t rows_q, int6
 
 }  // namespace
 
+// RMS factors of every query and key row (the GELU backward's prepass).
+hipError_t launch_bwd_rms(int D, bool bf16, const BwdArgs& a, int64_t rows_q, int64_t rows_k, hipStream_t st) {
+  hipError_t e;
+  if (bf16) {
+    e = D == 32 ? launch_rms<32, __bf16>(a.q, rows_q, a.eps, a.rq, st)
+        : D == 64 ? launch_rms<64, __bf16>(a.q, rows_q, a.eps, a.rq, st)
+                  : launch_rms<128, __bf16>(a.q, rows_q, a.eps, a.rq, st);
+    if (e != hipSuccess) return e;
+    return D == 32 ? launch_rms<32, __bf16>(a.k, rows_k, a.eps, a.rk, st)
+           : D == 64 ? launch_rms<64, __bf16>(a.k, rows_k, a.eps, a.rk, st)
+                     : launch_rms<128, __bf16>(a.k, rows_k, a.eps, a.rk, st);
+  }
+  e = D == 32 ? launch_rms<32, float>(a.q, rows_q, a.eps, a.rq, st)
+      : D == 64 ? launch_rms<64, float>(a.q, rows_q, a.eps, a.rq, st)
+                : launch_rms<128, float>(a.q, rows_q, a.eps, a.rq, st);
+  if (e != hipSuccess) return e;
+  return D == 32 ? launch_rms<32, float>(a.k, rows_k, a.eps, a.rk, st)
+         : D == 64 ? launch_rms<64, float>(a.k, rows_k, a.eps, a.rk, st)
+                   : launch_rms<128, float>(a.k, rows_k, a.eps, a.rk, st);
+}
+
+// fp32 inputs (bf16 inputs take the MFMA kernels of ja_attn_bwd_mfma.hip).
 hipError_t launch_attn_bwd(int D, bool bf16, int act, int wmode, const BwdArgs& a, int64_t rows_q, int64_t rows_k,
                            int grid_q, int grid_k, hipStream_t st) {
-  if (bf16) {
-    if (D == 32) return launch_all<32, __bf16>(act, wmode, a, rows_q, rows_k, grid_q, grid_k, st);
-    if (D == 64) return launch_all<64, __bf16>(act, wmode, a, rows_q, rows_k, grid_q, grid_k, st);
-    return launch_all<128, __bf16>(act, wmode, a, rows_q, rows_k, grid_q, grid_k, st);
-  }
+  if (bf16) return hipErrorInvalidValue;
   if (D == 32) return launch_all<32, float>(act, wmode, a, rows_q, rows_k, grid_q, grid_k, st);
   if (D == 64) return launch_all<64, float>(act, wmode, a, rows_q, rows_k, grid_q, grid_k, st);
   return launch_all<128, float>(act, wmode, a, rows_q, rows_k, grid_q, grid_k, st);

@@ -1,9 +1,14 @@
-// Backward of jagged softmax attention on bf16 MFMA (training; the chain rule
+// Backward of jagged attention on bf16 MFMA (training; the chain rule
 // of the forward as defined -- the pages, e.g. the techfeed.io summary of
 // "GEM Training: How Meta Doubled the Efficiency of Its LLM-Scale Ads
 // Foundation Model", describe the training system but not its backward):
 //   P = softmax(Q K^T / sqrt(D)),  dV = P^T dO,  dS = P * (dO V^T - D_i),
 //   D_i = rowsum(P * (dO V^T)),    dQ = dS K / sqrt(D),  dK = dS^T Q / sqrt(D).
+// GELU scores (QK-RMSNorm, no window; RMS factors r from a prepass):
+//   S = Qn Kn^T / sqrt(D), dV = gelu(S)^T dO / Lk, dS = gelu'(S) * (dO V^T) / Lk,
+//   dQn = dS Kn / sqrt(D), dKn = dS^T Qn / sqrt(D), dx = r dxn - x r^3 (dxn . x) / D;
+// the RMS factors are folded into the scores and into dS, so the products
+// take the raw bf16 rows, and the dQ kernel needs no first pass.
 //
 // Two kernels, 32 rows per wave, all products on v_mfma_f32_32x32x16_bf16
 // with fp32 accumulation (P and dS enter their products in bf16, as P does in
@@ -158,14 +163,17 @@ __device__ __forceinline__ void wait_vm() {
 constexpr int kQWaves = 4;  // dq kernel: 4 waves x 32 query rows (128-row items)
 constexpr int kKWaves = 2;  // dkv kernel: 2 waves x 32 key rows (64-row items)
 
-template <int D, int WMODE>
+template <int D, int WMODE, int ACT>
 __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_mfma_kernel(BwdArgs a) {
   using L = BT<D>;
   using T = Dma<D, 64>;
-  // per-wave DMA count of one K + V tile (every wave past the first issues the same number)
-  constexpr int kN0 = 2 * T::count(0, kQWaves), kN1 = 2 * T::count(1, kQWaves);
+  constexpr bool kGelu = ACT == ACT_GELU;
+  // per-wave DMA count of one K + V tile (every wave past the first issues the
+  // same number; with GELU wave 0 also loads the tile's key RMS factors)
+  constexpr int kN0 = 2 * T::count(0, kQWaves) + (kGelu ? 1 : 0), kN1 = 2 * T::count(1, kQWaves);
   static_assert(T::count(1, kQWaves) == T::count(kQWaves - 1, kQWaves), "waves 1.. issue equally");
   __shared__ __attribute__((aligned(1024))) unsigned char buf[2][2][T::kBytes];  // [stage][K, V]
+  __shared__ __attribute__((aligned(256))) float rkb[2][64];                    // GELU: [stage] key RMS factors
   const __bf16* qg = reinterpret_cast<const __bf16*>(a.q);
   const __bf16* kg = reinterpret_cast<const __bf16*>(a.k);
   const __bf16* vg = reinterpret_cast<const __bf16*>(a.v);
@@ -176,6 +184,7 @@ __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)
   const size_t gstride = size_t(a.H) * D;
   const unsigned grow = unsigned(gstride) * 2u;
   const unsigned lds0 = lds_addr_of(&buf[0][0][0]);
+  const unsigned lds_rk = lds_addr_of(&rkb[0][0]);
   const int n_items = a.hdr_q->n_items;
   for (int idx = blockIdx.x; idx < n_items; idx += gridDim.x) {
     const WorkItem it = a.items_q[idx];
@@ -221,6 +230,9 @@ __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)
       const unsigned st = lds0 + unsigned(s & 1) * 2u * T::kBytes;
       dma_tile<D, 64, kQWaves>(st, kbase + size_t(64 * t) * gstride, grow, valid, wave, lane);
       dma_tile<D, 64, kQWaves>(st + T::kBytes, vbase + size_t(64 * t) * gstride, grow, valid, wave, lane);
+      if (kGelu && wave == 0)
+        lds_dma4(a.rk + (size_t(it.kbeg) + 64 * t) * a.H + it.h, unsigned(min(lane, valid - 1) * a.H) * 4u,
+                 lds_rk + unsigned(s & 1) * 256u);
     };
     // Start of step s: issue tile s + 1, wait for tile s, barrier.
     auto step_begin = [&](int s) __attribute__((always_inline)) {
@@ -244,12 +256,14 @@ __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)
         x = mfma_32x32x16(read_a<D>(ks, 32 * kb + kp, g, cc), qf[cc], x);
         y = mfma_32x32x16(read_a<D>(vs, 32 * kb + kp, g, cc), gf[cc], y);
       }
-      // scale to log2 units; disallowed and ragged keys -> -inf
+      if constexpr (!kGelu) {
+        // scale to log2 units; disallowed and ragged keys -> -inf
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int j = 64 * t + 32 * kb + c_row(i, g);
-        const bool ok = j < it.lk && allowed<WMODE>(a, qrow, j);
-        x[i] = ok ? x[i] * a.c2 : -__builtin_huge_valf();
+        for (int i = 0; i < 16; ++i) {
+          const int j = 64 * t + 32 * kb + c_row(i, g);
+          const bool ok = j < it.lk && allowed<WMODE>(a, qrow, j);
+          x[i] = ok ? x[i] * a.c2 : -__builtin_huge_valf();
+        }
       }
       s = x;
       dp = y;
@@ -258,8 +272,8 @@ __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)
     // Pass 1: online max, sum and sum of p * dP -> log-sum-exp (base 2) and
     // D_i = sum_j p_ij dP_ij of the row, for pass 2 and the dK/dV kernel.
     float m = -__builtin_huge_valf(), l = 0.f, acc = 0.f;
-    if (nt > 0) issue(0);
-    for (int s = 0; s < nt; ++s) {
+    if (!kGelu && nt > 0) issue(0);
+    for (int s = 0; s < (kGelu ? 0 : nt); ++s) {
       step_begin(s);
       const int t = t_lo + s;
       if (t >= wt_lo && t < wt_hi) {
@@ -293,7 +307,11 @@ __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)
     acc = sum_halves(acc);
     const float lse = l > 0.f ? m + log2f(l) : 0.f;
     const float di = l > 0.f ? acc / l : 0.f;
-    if (g == 0 && qrow < it.lq) a.stats[size_t(it.qbeg + qrow) * a.H + it.h] = make_float2(lse, di);
+    if (!kGelu && g == 0 && qrow < it.lq) a.stats[size_t(it.qbeg + qrow) * a.H + it.h] = make_float2(lse, di);
+    // GELU: RMS factor of the query row, times 1/sqrt(D); 1/Lk
+    const float rsc = kGelu ? a.rq[size_t(it.qbeg + qr) * a.H + it.h] * a.inv_sqrt_d : 0.f;
+    const float inv_lk = kGelu ? 1.0f / float(max(it.lk, 1)) : 0.f;
+    if constexpr (kGelu) wait_vm<0>();  // (complete before the tile loads, as the Q fragments)
 
     // Pass 2: dQ^T += K^T dS^T.
     f32x16 dq[L::kT];
@@ -310,8 +328,21 @@ __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)
         for (int kb = 0; kb < 2; ++kb) {
           f32x16 sc, dp;
           scores(ks, vs, t, kb, sc, dp);
+          if constexpr (kGelu) {
+            // dSn = gelu'(s) dP / Lk, times the key's RMS factor (dQn = dSn Kn / sqrt(D))
+            const float* rk = &rkb[s & 1][0];
 #pragma unroll
-          for (int i = 0; i < 16; ++i) sc[i] = exp2f(sc[i] - lse) * (dp[i] - di);
+            for (int i = 0; i < 16; ++i) {
+              const int jl = 32 * kb + c_row(i, g);
+              const float ck = rk[jl];
+              float gl, gp;
+              gelu_and_grad(sc[i] * rsc * ck, gl, gp);
+              sc[i] = 64 * t + jl < it.lk ? gp * dp[i] * inv_lk * ck : 0.f;
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sc[i] = exp2f(sc[i] - lse) * (dp[i] - di);
+          }
 #pragma unroll
           for (int half = 0; half < 2; ++half) {
             const bf16x8 db = to_b(sc, half);
@@ -324,6 +355,29 @@ __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)
       }
       lds_barrier();  // every wave is done with stage s & 1 before tile s + 2 loads into it
     }
+#pragma unroll
+    for (int t2 = 0; t2 < L::kT; ++t2) dq[t2] *= a.inv_sqrt_d;
+    if constexpr (kGelu) {
+      // through the RMSNorm: dq = r dqn - q r^3 (dqn . q) / D; the lane holds
+      // dims 32 t2 + 8 gi + 4 g + 0..3, the other lane half the rest
+      const float r = a.rq[size_t(it.qbeg + qr) * a.H + it.h];
+      const __bf16* qrow_p = qg + (size_t(it.qbeg + qr) * a.H + it.h) * D;
+      float dot = 0.f;
+#pragma unroll
+      for (int t2 = 0; t2 < L::kT; ++t2)
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dot = fmaf(dq[t2][4 * gi + e], float(qrow_p[32 * t2 + 8 * gi + 4 * g + e]), dot);
+      const float c3 = r * r * r * sum_halves(dot) * (1.0f / D);
+#pragma unroll
+      for (int t2 = 0; t2 < L::kT; ++t2)
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            dq[t2][4 * gi + e] = fmaf(r, dq[t2][4 * gi + e], -float(qrow_p[32 * t2 + 8 * gi + 4 * g + e]) * c3);
+    }
     if (qrow < it.lq) {
       float* out = a.dq + (size_t(it.qbeg + qrow) * a.H + it.h) * D;
 #pragma unroll
@@ -331,26 +385,28 @@ __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi) {
           float4 w;
-          w.x = dq[t2][4 * gi + 0] * a.inv_sqrt_d;
-          w.y = dq[t2][4 * gi + 1] * a.inv_sqrt_d;
-          w.z = dq[t2][4 * gi + 2] * a.inv_sqrt_d;
-          w.w = dq[t2][4 * gi + 3] * a.inv_sqrt_d;
+          w.x = dq[t2][4 * gi + 0];
+          w.y = dq[t2][4 * gi + 1];
+          w.z = dq[t2][4 * gi + 2];
+          w.w = dq[t2][4 * gi + 3];
           *reinterpret_cast<float4*>(out + 32 * t2 + 8 * gi + 4 * g) = w;
         }
     }
   }
 }
 
-template <int D, int WMODE>
+template <int D, int WMODE, int ACT>
 __global__ __launch_bounds__(64 * kKWaves) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkv_mfma_kernel(BwdArgs a) {
   using L = BT<D>;
+  constexpr bool kGelu = ACT == ACT_GELU;
   using TK = Dma<D, 64>;
   using TQ = Dma<D, 32>;
-  // per-wave DMAs of one query step: Q and dO tiles, plus the statistics (wave 0)
+  // per-wave DMAs of one query step: Q and dO tiles, plus the statistics or,
+  // with GELU, the query RMS factors (wave 0)
   constexpr int kN0 = 2 * TQ::count(0, kKWaves) + 1, kN1 = 2 * TQ::count(1, kKWaves);
   __shared__ __attribute__((aligned(1024))) unsigned char kvb[2][TK::kBytes];    // the item's K, V
   __shared__ __attribute__((aligned(1024))) unsigned char qb[2][2][TQ::kBytes];  // [stage][Q, dO]
-  __shared__ __attribute__((aligned(256))) float2 stb[2][32];                    // [stage] (lse, D_i)
+  __shared__ __attribute__((aligned(256))) float2 stb[2][32];  // [stage] (lse, D_i); GELU: 64 floats, RMS factors
   const __bf16* qg = reinterpret_cast<const __bf16*>(a.q);
   const __bf16* kg = reinterpret_cast<const __bf16*>(a.k);
   const __bf16* vg = reinterpret_cast<const __bf16*>(a.v);
@@ -398,12 +454,23 @@ __global__ __launch_bounds__(64 * kKWaves) __attribute__((amdgpu_waves_per_eu(2)
       dma_tile<D, 32, kKWaves>(st, qbase + size_t(32 * t) * gstride, grow, valid, wave, lane);
       dma_tile<D, 32, kKWaves>(st + TQ::kBytes, gbase + size_t(32 * t) * gstride, grow, valid, wave, lane);
       if (wave == 0) {
-        const unsigned row = unsigned(min(lane >> 1, valid - 1));
-        lds_dma4(sbase + size_t(32 * t) * a.H, (row * unsigned(a.H)) * 8u + 4u * unsigned(lane & 1),
-                 lds_st + unsigned(s & 1) * 256u);
+        if constexpr (kGelu) {
+          const unsigned row = unsigned(min(lane, valid - 1));
+          lds_dma4(a.rq + (size_t(qbeg) + 32 * t) * a.H + it.h, row * unsigned(a.H) * 4u,
+                   lds_st + unsigned(s & 1) * 256u);
+        } else {
+          const unsigned row = unsigned(min(lane >> 1, valid - 1));
+          lds_dma4(sbase + size_t(32 * t) * a.H, (row * unsigned(a.H)) * 8u + 4u * unsigned(lane & 1),
+                   lds_st + unsigned(s & 1) * 256u);
+        }
       }
     };
 
+    // GELU: RMS factor of this lane's key row times 1/sqrt(D); 1/Lk
+    const int kr = min(krow, lk - 1);
+    const float csc = kGelu ? a.rk[size_t(kbeg + kr) * a.H + it.h] * a.inv_sqrt_d : 0.f;
+    const float inv_lk = kGelu ? 1.0f / float(lk) : 0.f;
+    if constexpr (kGelu) wait_vm<0>();  // (complete before the tile loads; see the dQ kernel)
     f32x16 dk[L::kT], dv[L::kT];
 #pragma unroll
     for (int t2 = 0; t2 < L::kT; ++t2) {
@@ -439,15 +506,31 @@ __global__ __launch_bounds__(64 * kKWaves) __attribute__((amdgpu_waves_per_eu(2)
           sc = mfma_32x32x16(read_a<D>(qs, kp, g, cc), read_a<D>(kst, 32 * wave + l32, g, cc), sc);
           dp = mfma_32x32x16(read_a<D>(gs, kp, g, cc), read_a<D>(vst, 32 * wave + l32, g, cc), dp);
         }
+        if constexpr (kGelu) {
+          // weights gelu(s) / Lk for dV, dSn = gelu'(s) dP / Lk times the
+          // query's RMS factor for dKn = dSn^T Qn / sqrt(D)
+          const float* rq = reinterpret_cast<const float*>(st);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int qi = c_row(i, g);
-          const int q = 32 * t + qi;
-          const float2 sv = st[qi];
-          const bool ok = q < lq && krow < lk && allowed<WMODE>(a, q, krow);
-          const float p = ok ? exp2f(sc[i] * a.c2 - sv.x) : 0.f;
-          sc[i] = p;
-          dp[i] = p * (dp[i] - sv.y);
+          for (int i = 0; i < 16; ++i) {
+            const int qi = c_row(i, g);
+            const float ri = rq[qi];
+            const bool ok = 32 * t + qi < lq && krow < lk;
+            float gl, gp;
+            gelu_and_grad(sc[i] * csc * ri, gl, gp);
+            sc[i] = ok ? gl * inv_lk : 0.f;
+            dp[i] = ok ? gp * dp[i] * inv_lk * ri : 0.f;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int qi = c_row(i, g);
+            const int q = 32 * t + qi;
+            const float2 sv = st[qi];
+            const bool ok = q < lq && krow < lk && allowed<WMODE>(a, q, krow);
+            const float p = ok ? exp2f(sc[i] * a.c2 - sv.x) : 0.f;
+            sc[i] = p;
+            dp[i] = p * (dp[i] - sv.y);
+          }
         }
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
@@ -462,6 +545,28 @@ __global__ __launch_bounds__(64 * kKWaves) __attribute__((amdgpu_waves_per_eu(2)
       }
       lds_barrier();  // every wave is done with stage s & 1 before tile s + 2 loads into it
     }
+#pragma unroll
+    for (int t2 = 0; t2 < L::kT; ++t2) dk[t2] *= a.inv_sqrt_d;
+    if constexpr (kGelu) {
+      // through the RMSNorm: dk = c dkn - k c^3 (dkn . k) / D (dims as in the dQ kernel)
+      const float c = a.rk[size_t(kbeg + kr) * a.H + it.h];
+      const __bf16* krow_p = kg + (size_t(kbeg + kr) * a.H + it.h) * D;
+      float dot = 0.f;
+#pragma unroll
+      for (int t2 = 0; t2 < L::kT; ++t2)
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dot = fmaf(dk[t2][4 * gi + e], float(krow_p[32 * t2 + 8 * gi + 4 * g + e]), dot);
+      const float c3 = c * c * c * sum_halves(dot) * (1.0f / D);
+#pragma unroll
+      for (int t2 = 0; t2 < L::kT; ++t2)
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            dk[t2][4 * gi + e] = fmaf(c, dk[t2][4 * gi + e], -float(krow_p[32 * t2 + 8 * gi + 4 * g + e]) * c3);
+    }
     if (krow < lk) {
       float* odk = a.dk + (size_t(kbeg + krow) * a.H + it.h) * D;
       float* odv = a.dv + (size_t(kbeg + krow) * a.H + it.h) * D;
@@ -470,10 +575,10 @@ __global__ __launch_bounds__(64 * kKWaves) __attribute__((amdgpu_waves_per_eu(2)
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi) {
           float4 wk, wv;
-          wk.x = dk[t2][4 * gi + 0] * a.inv_sqrt_d;
-          wk.y = dk[t2][4 * gi + 1] * a.inv_sqrt_d;
-          wk.z = dk[t2][4 * gi + 2] * a.inv_sqrt_d;
-          wk.w = dk[t2][4 * gi + 3] * a.inv_sqrt_d;
+          wk.x = dk[t2][4 * gi + 0];
+          wk.y = dk[t2][4 * gi + 1];
+          wk.z = dk[t2][4 * gi + 2];
+          wk.w = dk[t2][4 * gi + 3];
           wv.x = dv[t2][4 * gi + 0];
           wv.y = dv[t2][4 * gi + 1];
           wv.z = dv[t2][4 * gi + 2];
@@ -485,26 +590,28 @@ __global__ __launch_bounds__(64 * kKWaves) __attribute__((amdgpu_waves_per_eu(2)
   }
 }
 
-template <int D, int WMODE>
+template <int D, int WMODE, int ACT>
 hipError_t launch_w(const BwdArgs& a, int grid_q, int grid_k, hipStream_t st) {
-  hipLaunchKernelGGL((bwd_dq_mfma_kernel<D, WMODE>), dim3(grid_q), dim3(64 * kQWaves), 0, st, a);
-  hipLaunchKernelGGL((bwd_dkv_mfma_kernel<D, WMODE>), dim3(grid_k), dim3(64 * kKWaves), 0, st, a);
+  hipLaunchKernelGGL((bwd_dq_mfma_kernel<D, WMODE, ACT>), dim3(grid_q), dim3(64 * kQWaves), 0, st, a);
+  hipLaunchKernelGGL((bwd_dkv_mfma_kernel<D, WMODE, ACT>), dim3(grid_k), dim3(64 * kKWaves), 0, st, a);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_dm(int wmode, const BwdArgs& a, int grid_q, int grid_k, hipStream_t st) {
-  if (wmode == 1) return launch_w<D, 1>(a, grid_q, grid_k, st);
-  if (wmode == 2) return launch_w<D, 2>(a, grid_q, grid_k, st);
-  return launch_w<D, 0>(a, grid_q, grid_k, st);
+hipError_t launch_dm(int act, int wmode, const BwdArgs& a, int grid_q, int grid_k, hipStream_t st) {
+  if (act == ACT_GELU) return launch_w<D, 0, ACT_GELU>(a, grid_q, grid_k, st);  // (no window with GELU)
+  if (wmode == 1) return launch_w<D, 1, ACT_SOFTMAX>(a, grid_q, grid_k, st);
+  if (wmode == 2) return launch_w<D, 2, ACT_SOFTMAX>(a, grid_q, grid_k, st);
+  return launch_w<D, 0, ACT_SOFTMAX>(a, grid_q, grid_k, st);
 }
 
 }  // namespace
 
-hipError_t launch_attn_bwd_mfma(int D, int wmode, const BwdArgs& a, int grid_q, int grid_k, hipStream_t st) {
-  if (D == 32) return launch_dm<32>(wmode, a, grid_q, grid_k, st);
-  if (D == 64) return launch_dm<64>(wmode, a, grid_q, grid_k, st);
-  return launch_dm<128>(wmode, a, grid_q, grid_k, st);
+hipError_t launch_attn_bwd_mfma(int D, int act, int wmode, const BwdArgs& a, int grid_q, int grid_k,
+                                hipStream_t st) {
+  if (D == 32) return launch_dm<32>(act, wmode, a, grid_q, grid_k, st);
+  if (D == 64) return launch_dm<64>(act, wmode, a, grid_q, grid_k, st);
+  return launch_dm<128>(act, wmode, a, grid_q, grid_k, st);
 }
 
 }  // namespace ja

@@ -66,6 +66,18 @@ __device__ __forceinline__ float gelu_tanh(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// gelu(x) = x t and gelu'(x) = t + 2 x t (1 - t) u'(x), where t = sigmoid(2u),
+// u = sqrt(2/pi) (x + 0.044715 x^3) (from 1 + tanh(u) = 2 sigmoid(2u)); the
+// backward's form, with IEEE division and exp2f.
+__device__ __forceinline__ void gelu_and_grad(float x, float& g, float& gp) {
+  constexpr float kC = 0.7978845608028654f;  // sqrt(2/pi)
+  constexpr float kA = 0.044715f;
+  const float u = kC * fmaf(kA * x, x * x, x);
+  const float t = 1.0f / (1.0f + exp2f(-2.0f * 1.4426950408889634f * u));
+  g = x * t;
+  gp = fmaf(2.0f * x * t * (1.0f - t), kC * fmaf(3.0f * kA, x * x, 1.0f), t);
+}
+
 // The GELU of a score for the GELU-family activations.
 template <int ACT>
 __device__ __forceinline__ float gelu_act(float x) {
