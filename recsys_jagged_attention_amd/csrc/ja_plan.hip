@@ -76,6 +76,46 @@ struct SampleWork {
   double ck;    // estimated cost of one item (keys it touches + fixed overhead)
 };
 
+// Three running sums scanned together (one set of barriers): estimated cost,
+// items and partial slots (integer sums in doubles are exact below 2^53).
+struct Sums {
+  double cost, items, slots;
+};
+
+__device__ inline Sums wave_inclusive_scan3(Sums x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double c = __shfl_up(x.cost, o, 64), i = __shfl_up(x.items, o, 64), s = __shfl_up(x.slots, o, 64);
+    if (lane >= o) {
+      x.cost += c;
+      x.items += i;
+      x.slots += s;
+    }
+  }
+  return x;
+}
+
+// Exclusive scan of one Sums per thread over the block; returns the thread's
+// exclusive prefix and the block total.
+__device__ Sums block_exclusive_scan3(Sums x, Sums* s_warp, Sums* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const Sums inc = wave_inclusive_scan3(x);
+  if (lane == 63) s_warp[wave] = inc;
+  __syncthreads();
+  if (wave == 0) {
+    const Sums w = lane < kPlanWaves ? s_warp[lane] : Sums{0.0, 0.0, 0.0};
+    const Sums wi = wave_inclusive_scan3(w);
+    if (lane < kPlanWaves) s_warp[kPlanWaves + lane] = Sums{wi.cost - w.cost, wi.items - w.items, wi.slots - w.slots};
+    if (lane == kPlanWaves - 1) s_warp[2 * kPlanWaves] = wi;
+  }
+  __syncthreads();
+  const Sums base = s_warp[kPlanWaves + wave];
+  *total = s_warp[2 * kPlanWaves];
+  __syncthreads();
+  return Sums{inc.cost - x.cost + base.cost, inc.items - x.items + base.items, inc.slots - x.slots + base.slots};
+}
+
 __device__ inline SampleWork sample_work(const PlanArgs& a, int lq, int lk) {
   SampleWork w{0, 1, 0, 0, 0.0};
   if (lq <= 0) return w;
@@ -103,7 +143,7 @@ __device__ inline void fail(const PlanArgs& a, int status) {
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ int s_bad;
   __shared__ int s_iwarp[3 * kPlanWaves];
-  __shared__ double s_dwarp[3 * kPlanWaves];
+  __shared__ Sums s_swarp[2 * kPlanWaves + 1];
   __shared__ int s_bucket[kCostBuckets];  // cost order: item count, then next free position
   const int tid = threadIdx.x;
   if (tid == 0) {
@@ -114,10 +154,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 
   // Pass 1: validate; total items, partial slots and estimated cost.
   // Offsets start at 0, never decrease and end at the totals; self-attention
-  // needs identical query and key offsets.
+  // needs identical query and key offsets.  With at most one sample per
+  // thread (B <= kPlanThreads) the sample and its scan prefix are kept for
+  // pass 2.
   int bad = 0;
-  long long my_items = 0, my_slots = 0;
-  double my_cost = 0.0;
+  Sums mine{0.0, 0.0, 0.0};
+  SampleWork w0{0, 1, 0, 0, 0.0};
+  int qb0 = 0, lq0 = 0, kb0 = 0, lk0 = 0;
   for (int b = tid; b <= a.B; b += kPlanThreads) {
     const int q = a.qo[b], k = a.ko[b];
     if (b == 0 && (q != 0 || k != 0)) bad = 1;
@@ -127,24 +170,24 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       const int q1 = a.qo[b + 1], k1 = a.ko[b + 1];
       if (q1 < q || k1 < k) bad = 1;
       const SampleWork w = sample_work(a, q1 - q, k1 - k);
-      my_items += w.cnt;
-      my_slots += w.slots;
-      my_cost += w.cnt * w.ck;
+      mine.cost += w.cnt * w.ck;
+      mine.items += w.cnt;
+      mine.slots += w.slots;
       if (a.cost_order && w.cnt > 0) atomicAdd(&s_bucket[cost_bucket(a, k1 - k)], w.cnt);
+      if (b == tid) {
+        w0 = w;
+        qb0 = q;
+        lq0 = q1 - q;
+        kb0 = k;
+        lk0 = k1 - k;
+      }
     }
   }
   if (bad) atomicOr(&s_bad, 1);
-  double total_cost;
-  (void)block_exclusive_scan(my_cost, s_dwarp, &total_cost);
-  long long total_items_ll = 0, total_slots_ll = 0;
-  {
-    // int sums through the double scan are exact (< 2^53)
-    double ti, ts;
-    (void)block_exclusive_scan(double(my_items), s_dwarp, &ti);
-    (void)block_exclusive_scan(double(my_slots), s_dwarp, &ts);
-    total_items_ll = (long long)ti;
-    total_slots_ll = (long long)ts;
-  }
+  Sums total;
+  const Sums prefix = block_exclusive_scan3(mine, s_swarp, &total);
+  const double total_cost = total.cost;
+  const long long total_items_ll = (long long)total.items, total_slots_ll = (long long)total.slots;
   if (s_bad || total_items_ll > a.max_items || total_slots_ll > a.max_slots) {
     if (tid == 0) fail(a, JA_EOFFSETS);
     return;
@@ -159,7 +202,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     __syncthreads();
   }
 
-  // Pass 2: per chunk of 1024 samples, scan and write items, splits, slot
+  // Pass 2: per chunk of kPlanThreads samples, write items, splits, slot
   // bases and the XCD cut points.
   __shared__ int s_base[kPlanThreads];
   __shared__ int s_nqt[kPlanThreads];
@@ -169,20 +212,24 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   double cost_carry = 0.0;
   for (int base = 0; base < a.B; base += kPlanThreads) {
     const int b = base + tid;
-    SampleWork w{0, 1, 0, 0, 0.0};
-    int qb = 0, lq = 0, kb = 0, lk = 0;
-    if (b < a.B) {
-      qb = a.qo[b];
-      lq = a.qo[b + 1] - qb;
-      kb = a.ko[b];
-      lk = a.ko[b + 1] - kb;
-      w = sample_work(a, lq, lk);
+    SampleWork w = w0;
+    int qb = qb0, lq = lq0, kb = kb0, lk = lk0;
+    Sums pre = prefix, chunk = total;
+    if (base > 0 || a.B > kPlanThreads) {  // more than one chunk: reload and rescan
+      w = SampleWork{0, 1, 0, 0, 0.0};
+      qb = lq = kb = lk = 0;
+      if (b < a.B) {
+        qb = a.qo[b];
+        lq = a.qo[b + 1] - qb;
+        kb = a.ko[b];
+        lk = a.ko[b + 1] - kb;
+        w = sample_work(a, lq, lk);
+      }
+      pre = block_exclusive_scan3(Sums{w.cnt * w.ck, double(w.cnt), double(w.slots)}, s_swarp, &chunk);
     }
-    int items_total, slots_total;
-    double cost_total;
-    const int ibase = block_exclusive_scan(w.cnt, s_iwarp, &items_total) + item_carry;
-    const int sbase = block_exclusive_scan(w.slots, s_iwarp, &slots_total) + slot_carry;
-    const double cbase = block_exclusive_scan(w.cnt * w.ck, s_dwarp, &cost_total) + cost_carry;
+    const int ibase = int(pre.items) + item_carry;
+    const int sbase = int(pre.slots) + slot_carry;
+    const double cbase = pre.cost + cost_carry;
     if (b < a.B) {
       a.nsplit[b] = w.ns;
       a.pbase[b] = sbase;
@@ -210,15 +257,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     for (int p = tid; p < nchunk * a.H; p += kPlanThreads) {
       const int j = p / a.H, h = p - j * a.H;
       const int nq = s_nqt[j], nsj = s_ns[j];
-      const int qb = s_qb[j], lq = s_lq[j], kb = s_kb[j], lk = s_lk[j];
+      const int qbj = s_qb[j], lqj = s_lq[j], kbj = s_kb[j], lkj = s_lk[j];
       if (nq == 0) continue;
-      int ib = a.cost_order ? atomicAdd(&s_bucket[cost_bucket(a, lk)], nq * nsj) : s_base[j] + h * nq * nsj;
+      int ib = a.cost_order ? atomicAdd(&s_bucket[cost_bucket(a, lkj)], nq * nsj) : s_base[j] + h * nq * nsj;
       for (int qt = 0; qt < nq; ++qt)
-        for (int sp = 0; sp < nsj; ++sp) a.items[ib++] = WorkItem{base + j, h, qt * a.bm, sp, qb, lq, kb, lk};
+        for (int sp = 0; sp < nsj; ++sp) a.items[ib++] = WorkItem{base + j, h, qt * a.bm, sp, qbj, lqj, kbj, lkj};
     }
-    item_carry += items_total;
-    slot_carry += slots_total;
-    cost_carry += cost_total;
+    item_carry += int(chunk.items);
+    slot_carry += int(chunk.slots);
+    cost_carry += chunk.cost;
     __syncthreads();
   }
   if (tid == 0) {
