@@ -124,11 +124,27 @@ def cpu_baseline(w, budget_s: float):
     }
 
 
-def load_traffic(kernel_tag: str, workload: str):
-    """HBM bytes per launch from committed rocprofv3 counter summaries, only if
-    they were taken on the current kernel sources (matching source hash)."""
+# Source file of each forward kernel, and the headers every kernel file includes.
+KERNEL_SOURCE = {"attn_pp_kernel": "ja_attn_pp.hip", "attn_kernel": "ja_attn_mfma.hip",
+                 "attn_f32_kernel": "ja_attn_f32.hip"}
+KERNEL_HEADERS = ("ja_internal.h", "ja_device.h", "ja_mfma_util.h", "ja_gelu_poly.h")
+
+
+def kernel_source_hash(kernel_tag: str) -> str:
+    """sha256 over the dominant kernel's source file and the shared headers: a
+    counter summary is valid for exactly that code."""
     import hashlib
 
+    csrc = os.path.join(ROOT, "recsys_jagged_attention_amd", "csrc")
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCE[kernel_tag.split("<")[0]],) + KERNEL_HEADERS:
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()
+
+
+def load_traffic(kernel_tag: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, only if
+    they were taken on the current kernel source (matching source hash)."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
     if not os.path.exists(path):
         return None
@@ -137,12 +153,7 @@ def load_traffic(kernel_tag: str, workload: str):
         if ":" in line and not line.startswith("#"):
             a, b = line.split(":", 1)
             kv[a.strip()] = b.strip()
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "recsys_jagged_attention_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h", ".cpp", ".py")) and os.path.isfile(os.path.join(csrc, f)):
-            h.update(open(os.path.join(csrc, f), "rb").read())
-    if kv.get("source_sha256") != h.hexdigest() or kv.get("kernel") != kernel_tag:
+    if kv.get("source_sha256") != kernel_source_hash(kernel_tag) or kv.get("kernel") != kernel_tag:
         return None
     try:
         return float(kv["traffic_bytes_per_launch"])
