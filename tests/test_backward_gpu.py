@@ -97,3 +97,40 @@ def test_cross_gelu_workload_slice():
     w = make_workload("cross_gelu", scale=0.02)
     log(f"backward cross_gelu slice B={w.B} Nq={w.total_q} Nk={w.total_kv}")
     run("cross", 0, "bf16", w.q_offsets, w.kv_offsets, w.q, w.k, w.v, seed=7, act="gelu_tanh")
+
+
+@pytest.mark.parametrize("name", ["block_window", "full_self", "cross_gelu", "sliding_window", "pma"])
+def test_full_size_sampled(name):
+    """The whole workload at its full size, in the launch configuration the
+    benchmark times; the oracle recomputes dQ, dK, dV of a few (sample, head)
+    pairs -- the longest sample among them -- and every element of those is
+    compared."""
+    from recsys_jagged_attention_amd.inputs import cast_values
+
+    w = make_workload(name)
+    lq, lk = np.diff(w.q_offsets), np.diff(w.kv_offsets)
+    rng = np.random.default_rng(11)
+    picks = {(int(np.argmax(lq * np.maximum(lk, 1))), int(rng.integers(w.H)))}
+    while len(picks) < 3:
+        picks.add((int(rng.integers(w.B)), int(rng.integers(w.H))))
+    log(f"backward full-size {name}: B={w.B} Nq={w.total_q} Nk={w.k.shape[0]} pairs {sorted(picks)}")
+    dout = np.random.default_rng(12).standard_normal(w.q.shape).astype(np.float32)
+    dt = torch.bfloat16
+    tq, tk, tv, tg = (torch.from_numpy(x).to(dt).cuda() for x in (w.q, w.k, w.v, dout))
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+    dq, dk, dv = backward(tq, tk, tv, tg, to(w.q_offsets), to(w.kv_offsets), variant=w.variant, act=w.act,
+                          window=w.window, dtype="bf16", check=True)
+    torch.cuda.synchronize()
+    dq, dk, dv = (t.cpu().numpy().astype(np.float64) for t in (dq, dk, dv))
+    q, k, v, g = (cast_values(x, "bf16").astype(np.float64) for x in (w.q, w.k, w.v, dout))
+    for b, h in sorted(picks):
+        qs = slice(w.q_offsets[b], w.q_offsets[b + 1])
+        ks = slice(w.kv_offsets[b], w.kv_offsets[b + 1])
+        if w.act == "softmax":
+            ref = oracle.attention_dense_bwd(q[qs, h], k[ks, h], v[ks, h], g[qs, h], w.window, w.variant)
+        else:
+            ref = oracle.attention_dense_gelu_bwd(q[qs, h], k[ks, h], v[ks, h], g[qs, h])
+        for nm, got, r in zip(("dq", "dk", "dv"), (dq[qs, h], dk[ks, h], dv[ks, h]), ref):
+            err = np.abs(got - r).max() / max(np.abs(r).max(), 1.0) if r.size else 0.0
+            log(f"  sample {b} head {h} {nm}: rel err {err:.3e}")
+            assert np.isfinite(got).all() and err <= tol("bf16", w.act), f"{nm} b={b} h={h}: {err:.3e}"
