@@ -1,6 +1,7 @@
 /*
  * jagged_attn.h -- C ABI of the MI355X (gfx950) jagged generalized dot-product
- * attention forward library (libjagged_attn.so).
+ * attention library (libjagged_attn.so): the forward, its backward for
+ * training, and an on-device MX (e4m3 + E8M0) quantiser.
  *
  * What it computes.  For every sample b and head h of a jagged batch, with
  * Q (Lq x D) and K, V (Lk x D) the sample's rows of that head:
