@@ -28,6 +28,8 @@ hipError_t launch_mx_quant(bool bf16, const void* x, int64_t n_blocks, uint8_t* 
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 int pp_rows();
+int pp_pipe_rows();
+int pp_pipe_max_blocks();
 
 namespace {
 
@@ -96,6 +98,8 @@ Plan make_plan(int B, int H, int D, int variant, int act, int window, int dtype,
   } else if (dtype == JA_BF16 && variant != JA_PMA) {
     p.shape = kShapePingPong;  // self (with or without window) and cross: one tile stream, 8 waves x 32 rows
     p.bm = pp_rows();
+    // block windows of at most one 64-token block per wave pair: pipelined runs of query blocks
+    if (variant == JA_SELF && window > 0 && window / kBlock <= pp_pipe_max_blocks()) p.bm = pp_pipe_rows();
   } else if (window > 0) {
     p.shape = kShapeWindow;
     p.bm = 128;  // two 64-token query blocks

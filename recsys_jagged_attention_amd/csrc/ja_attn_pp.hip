@@ -19,6 +19,15 @@
 // tile steps; consecutive positions lie on one XCD, so the query tiles of one
 // (sample, head) mostly share its K/V through that XCD's L2.
 //
+// Block windows of at most four 64-token blocks run as a pipeline instead: an
+// item is a run of up to kPipeBlocks query blocks of one (sample, head), and
+// query block b belongs to the wave pair b mod 4 (32 rows per wave).  Every key
+// tile of the run is loaded once and serves the (up to four) query blocks
+// whose window holds it, so each step keeps every pair busy; when a pair's
+// block ends, its next block starts on the following tile, with its Q already
+// staged in LDS by direct loads issued two steps earlier (techfeed.io summary,
+// section "BlockAttention": attention confined to whole blocks within a window).
+//
 // LDS holds a ring of 4 tiles (K and V, plus the key scales of the GELU path):
 // in step s the waves read K_s and V_{s-1}, tile s+1 has landed and tile s+2
 // is loaded by direct-to-LDS loads issued between the score MFMAs.  The next
@@ -48,6 +57,10 @@ __device__ constexpr bf16x2v kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 // the load of four waves reading at once is several MFMAs long).
 constexpr int kPPAhead = 5;
 constexpr int kPPAheadS = 8;
+// Query blocks per work item of the block-window pipeline (and the most
+// window blocks it takes: one wave pair per block of a window).
+constexpr int kPipeBlocks = 16;
+constexpr int kPipePairs = kPPWaves / 2;
 
 template <int D, int ACT>
 struct PP {
@@ -71,23 +84,43 @@ struct PP {
 // Position in the tile stream: tile t of the k-th item of this workgroup
 // (k == n: past the end), the end of the item's tiles and its key count.
 // Windows: this wave computes tiles [wlo, whi] of the item, and its first
-// query row is r0 (sample-local).  Wave-uniform.
+// query row is r0 (sample-local).  Block-window pipeline: the item's first
+// tile is wlo, its query blocks are [r0, whi).  Wave-uniform.
 struct Cur {
   int k, t, te, lk;
   int wlo, whi, r0;
 };
 
 // Window modes of the tile stream.
-enum { kWinNone = 0, kWinBlock = 1, kWinSliding = 2 };
+enum { kWinNone = 0, kWinBlock = 1, kWinSliding = 2, kWinPipe = 3 };
+
+// Block-window pipeline, tile t of cursor cu for wave pair p: the query block
+// the pair works on (the first block >= t in the pair's residue class mod 4),
+// whether it sees tile t, and whether t is that block's first or last tile.
+struct PipeStep {
+  int b;
+  bool act, first, last;
+};
+__device__ __forceinline__ PipeStep pipe_step(const Cur& cu, int p, int nb) {
+  PipeStep r;
+  r.b = cu.t + ((p - cu.t) & (kPipePairs - 1));
+  r.act = r.b < cu.t + nb && r.b >= cu.r0 && r.b < cu.whi;
+  r.first = r.act && cu.t == max(r.b - nb + 1, 0);
+  r.last = r.act && cu.t == r.b;
+  return r;
+}
 
 __device__ __forceinline__ int ntiles_of(int lk) { return (lk + 63) >> 6; }
 
 // Where the tile loads of a cursor read: key row r of the item's head at
-// kb + r * row_bytes (values at vb + ...), GELU key scales at ksc[r * H].
+// kb + r * row_bytes (values at vb + ...), GELU key scales at ksc[r * H];
+// query row r at qb + r * row_bytes (lq rows).
 struct Src {
   const unsigned char* kb;
   const unsigned char* vb;
   const float* ksc;
+  const unsigned char* qb;
+  int lq;
 };
 
 typedef int i32x4v __attribute__((ext_vector_type(4)));
@@ -96,6 +129,7 @@ typedef __attribute__((address_space(3))) const i32x4v lds_i32x4;
 struct PPCtx {
   const WorkItem* items;
   lds_i32x4* cache;       // LDS copy of this workgroup's first kPPItemCache records (2 x 16 B each)
+  const unsigned char* q;
   const unsigned char* k;
   const unsigned char* v;
   const float* kscale;
@@ -117,7 +151,11 @@ __device__ __forceinline__ WorkItem load_record(const PPCtx& c, int k) {
     const i32x4v u = c.cache[2 * k], x = c.cache[2 * k + 1];
     w = WorkItem{u[0], u[1], u[2], u[3], x[0], x[1], x[2], x[3]};
   } else {
+    // (rare: more than kPPItemCache items per workgroup) waited for here, so
+    // that no load is pending where the two paths meet -- the compiler would
+    // otherwise wait there for every load in flight, tile prefetches included
     w = c.items[item_index(c, k)];
+    wait_vmcnt(0);
   }
   w.h = __builtin_amdgcn_readfirstlane(w.h);
   w.q0 = __builtin_amdgcn_readfirstlane(w.q0);
@@ -135,6 +173,8 @@ __device__ __forceinline__ Src make_src(const PPCtx& c, const WorkItem& w) {
   r.kb = uniform_ptr(c.k + off);
   r.vb = uniform_ptr(c.v + off);
   r.ksc = c.kscale ? uniform_ptr(c.kscale + size_t(w.kbeg) * c.H + w.h) : nullptr;
+  r.qb = uniform_ptr(c.q + (size_t(w.qbeg) * c.H + w.h) * size_t(2 * D));
+  r.lq = w.lq;
   return r;
 }
 
@@ -177,6 +217,14 @@ __device__ __forceinline__ void advance(const PPCtx& c, Cur& cu, Src& src, int w
       const int r0 = w.q0 + 32 * wave, wblk = r0 / kBlock;
       cu.wlo = wblk - nb + 1;
       cu.whi = r0 < w.lq ? wblk : -1;
+    } else if constexpr (WMODE == kWinPipe) {
+      // query blocks [c0b, ce) and the key tiles from nb - 1 blocks before c0b
+      const int c0b = w.q0 / kBlock, ce = min(c0b + kPipeBlocks, (w.lq + kBlock - 1) / kBlock);
+      t_lo = max(0, c0b - nb + 1);
+      t_end = min(t_end, ce);
+      cu.wlo = t_lo;
+      cu.whi = ce;
+      cu.r0 = c0b;
     } else if constexpr (WMODE == kWinSliding) {
       t_lo = max(0, w.q0 - wt + 1) / kBlock;
       t_end = min(t_end, (min(w.q0 + kPPRows, w.lq) + kBlock - 1) / kBlock);
@@ -201,7 +249,14 @@ template <int D, int ACT, int WMODE>
 __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
   using K = PP<D, ACT>;
   constexpr int kQChunks = K::kQChunks, kOTiles = K::kOTiles, kRowBytes = K::kRowBytes;
-  __shared__ __attribute__((aligned(1024))) unsigned char ring[K::kRing * K::kStageBytes];
+  constexpr bool kPipe = WMODE == kWinPipe;
+  // LDS: a ring of kRing stages of (K, V[, key scales]).  The pipeline instead
+  // keeps K in 3 stages (tiles s, s+1, s+2: K_{s-1} is dead once the scores
+  // of tile s-1 are taken), V in 4 (s-1 .. s+2) and two Q blocks (the block
+  // starting on the next tile, alternating by tile parity).
+  constexpr int kPipeV = 3 * K::kTileBytes, kPipeQ = 7 * K::kTileBytes;
+  constexpr int kRingBytes = kPipe ? 9 * K::kTileBytes : K::kRing * K::kStageBytes;
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[kRingBytes];
   __shared__ WorkItem cache[kPPItemCache];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -213,6 +268,7 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
   PPCtx c;
   c.items = a.items;
   c.cache = (lds_i32x4*)(cache);
+  c.q = reinterpret_cast<const unsigned char*>(a.q);
   c.k = reinterpret_cast<const unsigned char*>(a.k);
   c.v = reinterpret_cast<const unsigned char*>(a.v);
   c.kscale = a.kscale;
@@ -245,9 +301,10 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
   Cur c2 = c1;
   advance<D, WMODE>(c, c2, src, wave, lane, nb, wt);
 
-  // Loads of the loading cursor's tile into ring stage `st`.  Job j moves 1 KB
-  // segment wave + 8j of K|V; rows of a ragged tile are clamped to its last key.
-  auto tile_job = [&](const Cur& cu, const Src& sr, int st, int j) __attribute__((always_inline)) {
+  // Loads of the loading cursor's tile into LDS (K at byte kdst of the ring, V
+  // at vdst).  Job j moves 1 KB segment wave + 8j of K|V; rows of a ragged tile
+  // are clamped to its last key.
+  auto tile_job = [&](const Cur& cu, const Src& sr, int kdst, int vdst, int j) __attribute__((always_inline)) {
     const int key0 = 64 * cu.t;
     const int lim = min(63, cu.lk - 1 - key0);
     const int sg = wave + kPPWaves * j;
@@ -258,7 +315,38 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
     const int phys = lane % K::kChunksPerRow;
     const int ch = phys ^ (is_v ? swz_v<D>(row) : swz_k<D>(row));
     const unsigned off = __umul24(unsigned(min(row, lim)), c.row_bytes) + 16u * unsigned(ch);
-    lds_dma16(tile, off, lds_addr_of(ring) + st * K::kStageBytes + (is_v ? K::kTileBytes : 0) + seg * 1024);
+    lds_dma16(tile, off, lds_addr_of(ring) + (is_v ? vdst : kdst) + seg * 1024);
+  };
+  // Pipeline: the 64 query rows of block bq of the loading cursor's item into
+  // Q slot `slot` (rows past the sample repeat its last row), laid out like a
+  // K tile.  Waves past the block's 1 KB segments issue nothing.
+  auto q_block_job = [&](const Src& sr, int bq, int slot) __attribute__((always_inline)) {
+    // (the lane id is read here by volatile asm, so that the lane offsets are
+    // formed at this point instead of being hoisted out of the stream loop and
+    // kept live -- or spilled -- across it)
+    int lid;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lid));
+#pragma unroll
+    for (int j = 0; j < (K::kSegsLd + kPPWaves - 1) / kPPWaves; ++j) {
+      const int seg = wave + kPPWaves * j;
+      if (seg < K::kSegsLd) {
+        const int r0 = kBlock * bq;
+        const int lim = min(63, sr.lq - 1 - r0);
+        const int row = seg * K::kRowsPerSeg + lid / K::kChunksPerRow;
+        const int ch = (lid % K::kChunksPerRow) ^ swz_k<D>(row);
+        const unsigned off = __umul24(unsigned(min(row, lim)), c.row_bytes) + 16u * unsigned(ch);
+        lds_dma16(sr.qb + size_t(r0) * c.row_bytes, off, lds_addr_of(ring) + kPipeQ + slot * K::kTileBytes + seg * 1024);
+      }
+    }
+  };
+  // Pipeline: stage the Q block that starts on the loading cursor's tile, when
+  // that tile is not its item's first (the first tile's blocks load Q
+  // directly), into the Q slot of the tile's parity.
+  auto q_stage = [&](const Cur& cu, const Src& sr) __attribute__((always_inline)) {
+    if constexpr (kPipe) {
+      const int bq = cu.t + nb - 1;
+      if (cu.k < c.n && cu.t > cu.wlo && bq < cu.whi) q_block_job(sr, bq, cu.t & 1);
+    }
   };
   auto tile_scales = [&](const Cur& cu, const Src& sr, int st) __attribute__((always_inline)) {
     if constexpr (ACT != ACT_SOFTMAX) {
@@ -282,12 +370,26 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
   }
   const float c2s = a.score_scale;  // softmax: log2(e)/sqrt(D); GELU: 1/sqrt(D)
 
+  // LDS byte offsets of the K and V tiles of stream tile s.
+  auto k_at = [&](int s) __attribute__((always_inline)) {
+    return kPipe ? (s % 3) * K::kTileBytes : (s % K::kRing) * K::kStageBytes;
+  };
+  auto v_at = [&](int s) __attribute__((always_inline)) {
+    return kPipe ? kPipeV + (s % 4) * K::kTileBytes : (s % K::kRing) * K::kStageBytes + K::kTileBytes;
+  };
+  const int pair = wave >> 1;
+  // First query row (sample-local) of this wave in the scores' item.
+  auto wave_row0 = [&](const Cur& cu, int q0) __attribute__((always_inline)) {
+    if constexpr (kPipe) return kBlock * pipe_step(cu, pair, nb).b + 32 * (wave & 1);
+    else return q0 + 32 * wave;
+  };
+
   // Q fragments of the scores' item: lane holds dims [(D/2)g, (D/2)g + D/2) of
   // query row q0 + 32*wave + l32 (rows past the sample load its last row).
   bf16x8 qf[kQChunks];
-  auto load_q = [&](int k) __attribute__((always_inline)) {
-    const WorkItem it = load_record(c, k);
-    const int qrow = min(it.q0 + 32 * wave + l32, it.lq - 1);
+  auto load_q = [&](const Cur& cu) __attribute__((always_inline)) {
+    const WorkItem it = load_record(c, cu.k);
+    const int qrow = min(wave_row0(cu, it.q0) + l32, it.lq - 1);
     const __bf16* src_q = reinterpret_cast<const __bf16*>(a.q) + (size_t(it.qbeg + qrow) * a.H + it.h) * D + (D / 2) * g;
 #pragma unroll
     for (int cc = 0; cc < kQChunks; ++cc) qf[cc] = *reinterpret_cast<const bf16x8*>(src_q + 8 * cc);
@@ -305,14 +407,16 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
     }
   };
 
-  // Prologue: tiles 0 and 1 in flight, Q of the first item.
+  // Prologue: tiles 0 and 1 in flight, Q of the first item (pipeline: and of
+  // the block starting on tile 1).
 #pragma unroll
-  for (int j = 0; j < K::kDmaJobs; ++j) tile_job(c0, src0, 0, j);
+  for (int j = 0; j < K::kDmaJobs; ++j) tile_job(c0, src0, k_at(0), v_at(0), j);
   tile_scales(c0, src0, 0);
 #pragma unroll
-  for (int j = 0; j < K::kDmaJobs; ++j) tile_job(c1, src1, 1, j);
+  for (int j = 0; j < K::kDmaJobs; ++j) tile_job(c1, src1, k_at(1), v_at(1), j);
   tile_scales(c1, src1, 1);
-  load_q(c0.k);
+  q_stage(c1, src1);
+  load_q(c0);
   wait_vmcnt(0);  // (nothing may be pending on the loop's entry edge, see below)
   bool q_fresh = true;  // Q was (re)loaded for c0's item: GELU needs its RMS factor
 
@@ -329,6 +433,7 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
   bool pv_act = true;  // this wave computed tile s-1 (block windows)
   int pv_nvalid = 64;  // keys of tile s-1 inside its sample
   int pv_key0 = 0, pv_r0 = 0;  // sliding window: tile s-1's first key, this wave's first row
+  int pv_row0 = 0;   // pipeline: first row of this wave's block at tile s-1
 
   // Softmax / GELU of the score tile `sc` (nvalid keys; sliding window: keys
   // key0.. of the tile against rows r0.. of this wave), written to pb as bf16.
@@ -418,18 +523,23 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
 
   // Output rows of the k-th item: O / l (softmax) or O / Lk (GELU), then reset.
   // Returns whether this wave issued its kStoresPerWave stores.
-  auto epilogue = [&](int k) __attribute__((always_inline)) {
+  auto epilogue = [&](int k, int prow0) __attribute__((always_inline)) {
     const WorkItem it = load_record(c, k);
-    const int qrow = it.q0 + 32 * wave + l32;
+    const int row0 = kPipe ? prow0 : it.q0 + 32 * wave;
+    const int qrow = row0 + l32;
     float scale;
     if constexpr (ACT == ACT_SOFTMAX) {
       const float l_tot = sum_halves(l);
-      scale = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+      scale = l_tot > 0.f ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
     } else {
-      scale = 1.0f / float(it.lk);
+      scale = __builtin_amdgcn_rcpf(float(it.lk));
     }
     if (qrow < it.lq) {
-      __bf16* orow = reinterpret_cast<__bf16*>(a.out) + (size_t(it.qbeg + qrow) * a.H + it.h) * D + (D / 2) * g;
+      // wave-uniform row base (scalar registers) + 32-bit lane offset: no
+      // 64-bit lane address stays live across the stream loop
+      unsigned char* ob = const_cast<unsigned char*>(
+          uniform_ptr(reinterpret_cast<const unsigned char*>(a.out) + (size_t(it.qbeg + row0) * a.H + it.h) * size_t(2 * D)));
+      const unsigned loff = unsigned(l32) * c.row_bytes + unsigned(D * g);
 #pragma unroll
       for (int t = 0; t < kOTiles; ++t)
 #pragma unroll
@@ -437,7 +547,7 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
           bf16x8 ov;
 #pragma unroll
           for (int j = 0; j < 8; ++j) ov[j] = (__bf16)(o[t][i + j] * scale);
-          *reinterpret_cast<bf16x8*>(orow + 16 * t + i) = ov;
+          *reinterpret_cast<bf16x8*>(ob + loff + 2 * (16 * t + i)) = ov;
         }
     }
 #pragma unroll
@@ -446,17 +556,21 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
       for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
     m = -__builtin_huge_valf();
     l = 0.f;
-    return it.q0 + 32 * wave < it.lq;  // (lane 0 stores)
+    return row0 < it.lq;  // (lane 0 stores)
   };
 
   bool stores_pending = false;  // the output stores of the last step follow its tile loads
   for (int s = 0;; ++s) {
     // Tile s has landed once only the loads of tile s+1 (and the output
-    // stores issued after them) can still be pending.
+    // stores issued after them) can still be pending; so has the pipeline's
+    // Q block of the last step (issued before them).
     if (stores_pending) wait_vmcnt(K::kVmemPerTile + K::kStoresPerWave);
     else wait_vmcnt(K::kVmemPerTile);
     lds_barrier();
     const int st_s = s % K::kRing, st_prev = (s + K::kRing - 1) % K::kRing, st_pf = (s + 2) % K::kRing;
+    // Q block starting on tile s+2 (read in step s+1): issued before this
+    // step's tile loads, so the next step's wait covers it.
+    q_stage(c2, src);
 
     // ---- late waves' VALU phase, then O += V_{s-1} P_{s-1}.
     auto head = [&]() __attribute__((always_inline)) {
@@ -470,7 +584,7 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
           // 4*kOTiles MFMAs (16-key chunk kc, output tile t), the V^T operand
           // read kAhead MFMAs early: one wave issues them alone, so the LDS
           // transpose-read latency is not hidden by a second wave.
-          const unsigned char* vs = ring + st_prev * K::kStageBytes + K::kTileBytes;
+          const unsigned char* vs = ring + v_at(s - 1);  // (s > 0)
           auto vread = [&](int i) __attribute__((always_inline)) {
             const int kc = i / kOTiles, t = i % kOTiles;
             const unsigned char* p0 = vs + v_row + kc * 16 * kRowBytes + v_col[t];
@@ -505,7 +619,7 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
         // Output of an item whose last tile was s-1.  These stores are newer
         // than the loads of tile s+1 (issued in the previous step), so the
         // next step's wait for that tile can let them run on.
-        if (pv_last) stores_pending = epilogue(pv_k);
+        if (pv_last) stores_pending = epilogue(pv_k, pv_row0);
       }
     };
     // A new item starts with tile s: its Q is loaded and waited for here, in
@@ -513,7 +627,7 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
     // branches meet would make the compiler wait for all later loads -- the
     // tile loads it does not know about -- at every step's scores.
     if (s > 0 && c0.k < c.n && c0.k != pv_k) {
-      load_q(c0.k);
+      load_q(c0);
       wait_vmcnt(0);
       q_fresh = true;
     }
@@ -527,12 +641,16 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
     // Loads of tile s+2 (into the stage that held tile s-2, last read in the
     // previous step): between the MFMAs of the second score half, or all at
     // once for a wave that skips the tile.
-    const bool act = WMODE == kWinNone || (c0.t >= c0.wlo && c0.t <= c0.whi);  // this wave computes tile s
+    PipeStep ps{0, false, false, false};
+    if constexpr (kPipe) ps = pipe_step(c0, pair, nb);
+    // this wave computes tile s
+    const bool act = WMODE == kWinNone || (kPipe ? ps.act : (c0.t >= c0.wlo && c0.t <= c0.whi));
+    const int pf_k = k_at(s + 2), pf_v = v_at(s + 2);
     if (!act) {
 #pragma unroll
-      for (int j = 0; j < K::kDmaJobs; ++j) tile_job(c2, src, st_pf, j);
+      for (int j = 0; j < K::kDmaJobs; ++j) tile_job(c2, src, pf_k, pf_v, j);
     } else {
-      const unsigned char* ks = ring + st_s * K::kStageBytes;
+      const unsigned char* ks = ring + k_at(s);
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
@@ -554,7 +672,7 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
         if (i + kAhead < kNS) kop[i % kAhead] = kread(i + kAhead);
         sc[i / kQChunks] = mfma_32x32x16(op, qf[i % kQChunks], sc[i / kQChunks]);
         constexpr int kPer = kQChunks / K::kDmaJobs;
-        if (i >= kQChunks && (i - kQChunks) % kPer == kPer - 1) tile_job(c2, src, st_pf, (i - kQChunks) / kPer);
+        if (i >= kQChunks && (i - kQChunks) % kPer == kPer - 1) tile_job(c2, src, pf_k, pf_v, (i - kQChunks) / kPer);
       }
       // keep the reads kAhead MFMAs early and the MFMAs in order
       __builtin_amdgcn_sched_group_barrier(kSgDsRead, kAhead, 1);
@@ -566,7 +684,20 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
     }
     tile_scales(c2, src, st_pf);
     __builtin_amdgcn_s_setprio(0);
-    const bool s_last = c0.t == c0.te - 1;
+    if constexpr (kPipe) {
+      // This wave's next block starts on tile s+1 of the same item: its Q was
+      // staged in LDS (in the previous step) and replaces the fragments the
+      // scores above have consumed.
+      const PipeStep pn = pipe_step(c1, pair, nb);
+      if (c1.k == c0.k && pn.first && c1.t > c1.wlo) {
+        const unsigned char* qs = ring + kPipeQ + (c1.t & 1) * K::kTileBytes;
+        const int row = 32 * (wave & 1) + l32;
+#pragma unroll
+        for (int cc = 0; cc < kQChunks; ++cc)
+          qf[cc] = *reinterpret_cast<const bf16x8*>(qs + row * kRowBytes + 16 * ((kQChunks * g + cc) ^ swz_k<D>(row)));
+      }
+    }
+    const bool s_last = kPipe ? ps.last : c0.t == c0.te - 1;
     const int nvalid = min(64, c0.lk - 64 * c0.t);
     if (!late && act) vphase(nvalid, st_s, 64 * c0.t, c0.r0);
     pv_k = c0.k;
@@ -575,6 +706,7 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
     pv_nvalid = nvalid;
     pv_key0 = 64 * c0.t;
     pv_r0 = c0.r0;
+    if constexpr (kPipe) pv_row0 = kBlock * ps.b + 32 * (wave & 1);
     c0 = c1;
     c1 = c2;
     advance<D, WMODE>(c, c2, src, wave, lane, nb, wt);
@@ -584,6 +716,8 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
 }  // namespace
 
 int pp_rows() { return kPPRows; }
+int pp_pipe_rows() { return kBlock * kPipeBlocks; }
+int pp_pipe_max_blocks() { return kPipePairs; }
 
 hipError_t launch_attn_pp(int D, int act, const AttnArgs& a, int num_cu, int64_t max_items, hipStream_t st) {
   // One workgroup per CU (the tile ring takes most of the LDS), a multiple of the XCD count.
@@ -597,6 +731,10 @@ hipError_t launch_attn_pp(int D, int act, const AttnArgs& a, int num_cu, int64_t
     if (D == 32) hipLaunchKernelGGL((attn_pp_kernel<32, ACT_SOFTMAX, kWinSliding>), gd, bd, 0, st, a);
     else if (D == 64) hipLaunchKernelGGL((attn_pp_kernel<64, ACT_SOFTMAX, kWinSliding>), gd, bd, 0, st, a);
     else hipLaunchKernelGGL((attn_pp_kernel<128, ACT_SOFTMAX, kWinSliding>), gd, bd, 0, st, a);
+  } else if (a.window_blocks > 0 && a.window_blocks <= kPipePairs) {  // (softmax only)
+    if (D == 32) hipLaunchKernelGGL((attn_pp_kernel<32, ACT_SOFTMAX, kWinPipe>), gd, bd, 0, st, a);
+    else if (D == 64) hipLaunchKernelGGL((attn_pp_kernel<64, ACT_SOFTMAX, kWinPipe>), gd, bd, 0, st, a);
+    else hipLaunchKernelGGL((attn_pp_kernel<128, ACT_SOFTMAX, kWinPipe>), gd, bd, 0, st, a);
   } else if (a.window_blocks > 0) {  // (softmax only)
     if (D == 32) hipLaunchKernelGGL((attn_pp_kernel<32, ACT_SOFTMAX, kWinBlock>), gd, bd, 0, st, a);
     else if (D == 64) hipLaunchKernelGGL((attn_pp_kernel<64, ACT_SOFTMAX, kWinBlock>), gd, bd, 0, st, a);

@@ -27,13 +27,29 @@ constexpr int kPlanThreads = 1024;
 constexpr int kPlanWaves = kPlanThreads / 64;
 constexpr int kCostBuckets = kPlanThreads;  // cost order: bucket = key tiles, clamped
 
-// Key tiles an item of the sample walks: all of them, or with a block window
-// at most the window plus the item's other query blocks.
-__device__ inline int cost_bucket(const PlanArgs& a, int lk) {
-  int t = (lk + kBlock - 1) / kBlock;
-  if (a.window_blocks > 0) t = min(t, a.window_blocks + a.bm / kBlock - 1);
-  if (a.window_tokens > 0) t = min(t, (a.window_tokens + a.bm - 2) / kBlock + 2);
-  return min(t, kCostBuckets - 1);
+// Cost bucket of query tile qt of a sample: the key tiles the tile-stream
+// kernel walks for that item (all of the sample's, or with a window those from
+// the first one a query of the item sees to the item's last query block).
+__device__ inline int cost_bucket(const PlanArgs& a, int qt, int lq, int lk) {
+  int te = (lk + kBlock - 1) / kBlock, tl = 0;
+  if (a.window_blocks > 0 || a.window_tokens > 0) {
+    const int q0 = qt * a.bm;
+    te = min(te, (min(q0 + a.bm, lq) + kBlock - 1) / kBlock);
+    tl = a.window_blocks > 0 ? max(0, q0 / kBlock - a.window_blocks + 1) : max(0, q0 - a.window_tokens + 1) / kBlock;
+  }
+  return min(max(te - tl, 0), kCostBuckets - 1);
+}
+
+// Length of the run of query tiles from qt on that share qt's cost bucket,
+// found without visiting them one by one: without a window every item walks
+// the same tiles; with one, the full items past the window's clamp at the
+// sample's first key walk the same number, and the first and last items are
+// runs of their own.
+__device__ inline int cost_run(const PlanArgs& a, int qt, int nqt) {
+  if (a.window_blocks <= 0 && a.window_tokens <= 0) return nqt - qt;
+  const int span = a.window_blocks > 0 ? (a.window_blocks - 1) * kBlock : a.window_tokens - 1;
+  const int qt_mid = (span + a.bm - 1) / a.bm;  // first query tile whose window is unclamped
+  return (qt >= qt_mid && qt < nqt - 1) ? nqt - 1 - qt : 1;
 }
 
 template <typename T>
@@ -173,7 +189,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       mine.cost += w.cnt * w.ck;
       mine.items += w.cnt;
       mine.slots += w.slots;
-      if (a.cost_order && w.cnt > 0) atomicAdd(&s_bucket[cost_bucket(a, k1 - k)], w.cnt);
+      if (a.cost_order && w.cnt > 0)
+        for (int qt = 0; qt < w.nqt;) {
+          const int run = cost_run(a, qt, w.nqt);
+          atomicAdd(&s_bucket[cost_bucket(a, qt, q1 - q, k1 - k)], run * a.H * w.ns);
+          qt += run;
+        }
       if (b == tid) {
         w0 = w;
         qb0 = q;
@@ -259,9 +280,20 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       const int nq = s_nqt[j], nsj = s_ns[j];
       const int qbj = s_qb[j], lqj = s_lq[j], kbj = s_kb[j], lkj = s_lk[j];
       if (nq == 0) continue;
-      int ib = a.cost_order ? atomicAdd(&s_bucket[cost_bucket(a, lkj)], nq * nsj) : s_base[j] + h * nq * nsj;
-      for (int qt = 0; qt < nq; ++qt)
-        for (int sp = 0; sp < nsj; ++sp) a.items[ib++] = WorkItem{base + j, h, qt * a.bm, sp, qbj, lqj, kbj, lkj};
+      if (a.cost_order) {
+        // each run of equal cost takes consecutive places in its bucket
+        for (int qt0 = 0; qt0 < nq;) {
+          const int run = cost_run(a, qt0, nq);
+          int ib = atomicAdd(&s_bucket[cost_bucket(a, qt0, lqj, lkj)], run * nsj);
+          for (int qt = qt0; qt < qt0 + run; ++qt)
+            for (int sp = 0; sp < nsj; ++sp) a.items[ib++] = WorkItem{base + j, h, qt * a.bm, sp, qbj, lqj, kbj, lkj};
+          qt0 += run;
+        }
+      } else {
+        int ib = s_base[j] + h * nq * nsj;
+        for (int qt = 0; qt < nq; ++qt)
+          for (int sp = 0; sp < nsj; ++sp) a.items[ib++] = WorkItem{base + j, h, qt * a.bm, sp, qbj, lqj, kbj, lkj};
+      }
     }
     item_carry += int(chunk.items);
     slot_carry += int(chunk.slots);

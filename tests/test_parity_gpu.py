@@ -176,7 +176,7 @@ def test_sliding_window_long_samples(window):
     full_parity(w)
 
 
-@pytest.mark.parametrize("window", [64, 256, 1024])
+@pytest.mark.parametrize("window", [64, 128, 192, 256, 320, 1024])
 def test_block_window_long_samples(window):
     """Block windows on samples of many 256-row items: items whose first key
     tile lies several blocks before their first query block, windows shorter
@@ -185,6 +185,21 @@ def test_block_window_long_samples(window):
     w = adhoc("window_long", "self", "softmax", "bf16", L, L, 2, 128, window=window, seed=window + 7)
     log(f"block window long W={window}: N={w.total_q}")
     full_parity(w)
+
+
+def test_block_window_pipeline_many_items():
+    """Block windows of up to four blocks run as pipelined runs of query blocks:
+    about 330 runs per workgroup (short samples, 80 heads), more than a
+    workgroup stages in LDS, so later runs are read from the workspace; every
+    window size of the pipeline on one batch would take four calls, so the
+    three-block window stands for them (the others are in the edge tests)."""
+    rng = np.random.Generator(np.random.PCG64(81))
+    B = 1024
+    L = rng.integers(1, 300, size=B).tolist()
+    w = adhoc("pipe_many", "self", "softmax", "bf16", L, L, 80, 32, window=192, seed=82)
+    log(f"pipeline many items: B={B} H=80 N={w.total_q}")
+    out = run_gpu(w)
+    sampled_parity(w, out, n=160)
 
 
 @pytest.mark.parametrize("act", ["softmax", "gelu_tanh"])
