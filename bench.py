@@ -33,7 +33,7 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "useful TFLOPS (unpadded) & % bf16 MFMA peak, jagged GDPA fwd, 1 MI355X"
 KERNEL_NAME = {  # dominant kernel per workload (template instance)
     "tiny_full": "attn_f32_kernel<32,softmax,nowindow>",
-    "block_window": "attn_pp_kernel<128,softmax,window>",
+    "block_window": "attn_pp_kernel<128,softmax,block_pipeline>",
     "full_self": "attn_pp_kernel<128,softmax>",
     "cross_gelu": "attn_pp_kernel<128,gelu>",
     "pma": "attn_kernel<64,NWQ=1,NWK=4,softmax,bf16,split>",
