@@ -16,7 +16,8 @@ hipError_t launch_attn_mfma(int D, int in, int shape, int act, const AttnArgs& a
                             int64_t max_items, hipStream_t st);
 hipError_t launch_combine(int D, const CombineArgs& a, hipStream_t st);
 hipError_t launch_attn_f32(int D, int act, int window_mode, const AttnArgs& a, int grid, hipStream_t st);
-hipError_t launch_attn_pp(int D, int act, const AttnArgs& a, int num_cu, int64_t max_items, hipStream_t st);
+hipError_t launch_attn_pp(int D, int act, bool cross, const AttnArgs& a, int num_cu, int64_t max_items,
+                          hipStream_t st);
 hipError_t launch_key_rms(int D, const void* k, int64_t rows, float eps, float* out, hipStream_t st);
 hipError_t launch_attn_bwd(int D, bool bf16, int act, int wmode, const BwdArgs& a, int64_t rows_q, int64_t rows_k,
                            int grid_q, int grid_k, hipStream_t st);
@@ -297,7 +298,7 @@ int jagged_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
   if (p.shape == kShapeF32) {
     e = launch_attn_f32(D, act, variant == JA_SLIDING ? 2 : (window > 0 ? 1 : 0), aa, grid, stream);
   } else if (p.shape == kShapePingPong) {
-    e = launch_attn_pp(D, act, aa, device_cus(), p.ws.max_items, stream);
+    e = launch_attn_pp(D, act, variant == JA_CROSS, aa, device_cus(), p.ws.max_items, stream);
 
   } else {
     const int in = io->dtype == JA_BF16 ? IN_BF16 : IN_MX;

@@ -245,7 +245,12 @@ __device__ __forceinline__ void advance(const PPCtx& c, Cur& cu, Src& src, int w
   cu.t = 0;  // past the end: tile 0 of the last item visited
 }
 
-template <int D, int ACT, int WMODE>
+// QPF (cross-attention): the Q of the item starting on the next tile is loaded
+// into the Q registers as soon as this step's scores have consumed them, and
+// waited for only before that item's scores.  With the short K/V of
+// cross-attention almost every step starts an item, and loading Q at the item
+// start left every wave waiting for HBM once per step.
+template <int D, int ACT, int WMODE, bool QPF>
 __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
   using K = PP<D, ACT>;
   constexpr int kQChunks = K::kQChunks, kOTiles = K::kOTiles, kRowBytes = K::kRowBytes;
@@ -560,12 +565,13 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
   };
 
   bool stores_pending = false;  // the output stores of the last step follow its tile loads
+  bool q_ahead = false;         // QPF: the last step loaded the next item's Q after its tile loads
   for (int s = 0;; ++s) {
     // Tile s has landed once only the loads of tile s+1 (and the output
-    // stores issued after them) can still be pending; so has the pipeline's
-    // Q block of the last step (issued before them).
-    if (stores_pending) wait_vmcnt(K::kVmemPerTile + K::kStoresPerWave);
-    else wait_vmcnt(K::kVmemPerTile);
+    // stores issued after them, and a Q prefetched after them) can still be
+    // pending; so has the pipeline's Q block of the last step (issued before
+    // them).
+    wait_vmcnt(K::kVmemPerTile + (stores_pending ? K::kStoresPerWave : 0) + (q_ahead ? kQChunks : 0));
     lds_barrier();
     const int st_s = s % K::kRing, st_prev = (s + K::kRing - 1) % K::kRing, st_pf = (s + 2) % K::kRing;
     // Q block starting on tile s+2 (read in step s+1): issued before this
@@ -627,14 +633,21 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
     // branches meet would make the compiler wait for all later loads -- the
     // tile loads it does not know about -- at every step's scores.
     if (s > 0 && c0.k < c.n && c0.k != pv_k) {
-      load_q(c0);
-      wait_vmcnt(0);
+      if constexpr (!QPF) {
+        load_q(c0);
+        wait_vmcnt(0);
+      }
       q_fresh = true;
     }
     stores_pending = false;
     head();
     if (c0.k >= c.n) break;
     if (q_fresh) {
+      // QPF: the item's Q was loaded at the end of the last step; only the
+      // output stores of this step's head can have been issued after it
+      // (the compiler adds its own wait for the Q registers here, which also
+      // covers those stores)
+      if constexpr (QPF) wait_vmcnt(stores_pending ? K::kStoresPerWave : 0);
       q_rms();
       q_fresh = false;
     }
@@ -683,6 +696,12 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
       }
     }
     tile_scales(c2, src, st_pf);
+    if constexpr (QPF) {
+      // the scores above have consumed Q: load the next item's (one branch,
+      // waited for by count, see above)
+      q_ahead = c1.k != c0.k && c1.k < c.n;
+      if (q_ahead) load_q(c1);
+    }
     __builtin_amdgcn_s_setprio(0);
     if constexpr (kPipe) {
       // This wave's next block starts on tile s+1 of the same item: its Q was
@@ -715,11 +734,18 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
 
 }  // namespace
 
+template <int D, int ACT>
+void launch_none(bool cross, dim3 gd, dim3 bd, hipStream_t st, const AttnArgs& a) {
+  if (cross) hipLaunchKernelGGL((attn_pp_kernel<D, ACT, kWinNone, true>), gd, bd, 0, st, a);
+  else hipLaunchKernelGGL((attn_pp_kernel<D, ACT, kWinNone, false>), gd, bd, 0, st, a);
+}
+
 int pp_rows() { return kPPRows; }
 int pp_pipe_rows() { return kBlock * kPipeBlocks; }
 int pp_pipe_max_blocks() { return kPipePairs; }
 
-hipError_t launch_attn_pp(int D, int act, const AttnArgs& a, int num_cu, int64_t max_items, hipStream_t st) {
+hipError_t launch_attn_pp(int D, int act, bool cross, const AttnArgs& a, int num_cu, int64_t max_items,
+                          hipStream_t st) {
   // One workgroup per CU (the tile ring takes most of the LDS), a multiple of the XCD count.
   int64_t grid = num_cu;
   const int64_t need = ((max_items + kXcds - 1) / kXcds) * kXcds;
@@ -728,29 +754,29 @@ hipError_t launch_attn_pp(int D, int act, const AttnArgs& a, int num_cu, int64_t
   if (grid < kXcds) grid = kXcds;
   const dim3 gd(static_cast<unsigned>(grid)), bd(64 * kPPWaves);
   if (a.window_tokens > 0) {  // (softmax only)
-    if (D == 32) hipLaunchKernelGGL((attn_pp_kernel<32, ACT_SOFTMAX, kWinSliding>), gd, bd, 0, st, a);
-    else if (D == 64) hipLaunchKernelGGL((attn_pp_kernel<64, ACT_SOFTMAX, kWinSliding>), gd, bd, 0, st, a);
-    else hipLaunchKernelGGL((attn_pp_kernel<128, ACT_SOFTMAX, kWinSliding>), gd, bd, 0, st, a);
+    if (D == 32) hipLaunchKernelGGL((attn_pp_kernel<32, ACT_SOFTMAX, kWinSliding, false>), gd, bd, 0, st, a);
+    else if (D == 64) hipLaunchKernelGGL((attn_pp_kernel<64, ACT_SOFTMAX, kWinSliding, false>), gd, bd, 0, st, a);
+    else hipLaunchKernelGGL((attn_pp_kernel<128, ACT_SOFTMAX, kWinSliding, false>), gd, bd, 0, st, a);
   } else if (a.window_blocks > 0 && a.window_blocks <= kPipePairs) {  // (softmax only)
-    if (D == 32) hipLaunchKernelGGL((attn_pp_kernel<32, ACT_SOFTMAX, kWinPipe>), gd, bd, 0, st, a);
-    else if (D == 64) hipLaunchKernelGGL((attn_pp_kernel<64, ACT_SOFTMAX, kWinPipe>), gd, bd, 0, st, a);
-    else hipLaunchKernelGGL((attn_pp_kernel<128, ACT_SOFTMAX, kWinPipe>), gd, bd, 0, st, a);
+    if (D == 32) hipLaunchKernelGGL((attn_pp_kernel<32, ACT_SOFTMAX, kWinPipe, false>), gd, bd, 0, st, a);
+    else if (D == 64) hipLaunchKernelGGL((attn_pp_kernel<64, ACT_SOFTMAX, kWinPipe, false>), gd, bd, 0, st, a);
+    else hipLaunchKernelGGL((attn_pp_kernel<128, ACT_SOFTMAX, kWinPipe, false>), gd, bd, 0, st, a);
   } else if (a.window_blocks > 0) {  // (softmax only)
-    if (D == 32) hipLaunchKernelGGL((attn_pp_kernel<32, ACT_SOFTMAX, kWinBlock>), gd, bd, 0, st, a);
-    else if (D == 64) hipLaunchKernelGGL((attn_pp_kernel<64, ACT_SOFTMAX, kWinBlock>), gd, bd, 0, st, a);
-    else hipLaunchKernelGGL((attn_pp_kernel<128, ACT_SOFTMAX, kWinBlock>), gd, bd, 0, st, a);
+    if (D == 32) hipLaunchKernelGGL((attn_pp_kernel<32, ACT_SOFTMAX, kWinBlock, false>), gd, bd, 0, st, a);
+    else if (D == 64) hipLaunchKernelGGL((attn_pp_kernel<64, ACT_SOFTMAX, kWinBlock, false>), gd, bd, 0, st, a);
+    else hipLaunchKernelGGL((attn_pp_kernel<128, ACT_SOFTMAX, kWinBlock, false>), gd, bd, 0, st, a);
   } else if (act == ACT_SOFTMAX) {
-    if (D == 32) hipLaunchKernelGGL((attn_pp_kernel<32, ACT_SOFTMAX, kWinNone>), gd, bd, 0, st, a);
-    else if (D == 64) hipLaunchKernelGGL((attn_pp_kernel<64, ACT_SOFTMAX, kWinNone>), gd, bd, 0, st, a);
-    else hipLaunchKernelGGL((attn_pp_kernel<128, ACT_SOFTMAX, kWinNone>), gd, bd, 0, st, a);
+    if (D == 32) launch_none<32, ACT_SOFTMAX>(cross, gd, bd, st, a);
+    else if (D == 64) launch_none<64, ACT_SOFTMAX>(cross, gd, bd, st, a);
+    else launch_none<128, ACT_SOFTMAX>(cross, gd, bd, st, a);
   } else if (act == ACT_GELU_POLY) {
-    if (D == 32) hipLaunchKernelGGL((attn_pp_kernel<32, ACT_GELU_POLY, kWinNone>), gd, bd, 0, st, a);
-    else if (D == 64) hipLaunchKernelGGL((attn_pp_kernel<64, ACT_GELU_POLY, kWinNone>), gd, bd, 0, st, a);
-    else hipLaunchKernelGGL((attn_pp_kernel<128, ACT_GELU_POLY, kWinNone>), gd, bd, 0, st, a);
+    if (D == 32) launch_none<32, ACT_GELU_POLY>(cross, gd, bd, st, a);
+    else if (D == 64) launch_none<64, ACT_GELU_POLY>(cross, gd, bd, st, a);
+    else launch_none<128, ACT_GELU_POLY>(cross, gd, bd, st, a);
   } else {
-    if (D == 32) hipLaunchKernelGGL((attn_pp_kernel<32, ACT_GELU, kWinNone>), gd, bd, 0, st, a);
-    else if (D == 64) hipLaunchKernelGGL((attn_pp_kernel<64, ACT_GELU, kWinNone>), gd, bd, 0, st, a);
-    else hipLaunchKernelGGL((attn_pp_kernel<128, ACT_GELU, kWinNone>), gd, bd, 0, st, a);
+    if (D == 32) launch_none<32, ACT_GELU>(cross, gd, bd, st, a);
+    else if (D == 64) launch_none<64, ACT_GELU>(cross, gd, bd, st, a);
+    else launch_none<128, ACT_GELU>(cross, gd, bd, st, a);
   }
   return hipGetLastError();
 }

@@ -121,7 +121,8 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
   switch (n) {
     JA_VMCNT(0) JA_VMCNT(1) JA_VMCNT(2) JA_VMCNT(3) JA_VMCNT(4) JA_VMCNT(5) JA_VMCNT(6) JA_VMCNT(7)
     JA_VMCNT(8) JA_VMCNT(9) JA_VMCNT(10) JA_VMCNT(11) JA_VMCNT(12) JA_VMCNT(13) JA_VMCNT(14)
-    JA_VMCNT(15) JA_VMCNT(16)
+    JA_VMCNT(15) JA_VMCNT(16) JA_VMCNT(17) JA_VMCNT(18) JA_VMCNT(19) JA_VMCNT(20) JA_VMCNT(21)
+    JA_VMCNT(22) JA_VMCNT(23) JA_VMCNT(24)
     default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
   }
 #undef JA_VMCNT
