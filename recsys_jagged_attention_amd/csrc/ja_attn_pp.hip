@@ -283,6 +283,10 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
   // [x G/8, (x+1) G/8) are the workgroups of XCD x)
   c.G = gridDim.x;
   c.pos = int(blockIdx.x % kXcds) * (c.G / kXcds) + int(blockIdx.x) / kXcds;
+  // (the pipeline's runs share few key tiles: dealing consecutive runs to
+  // one XCD only concentrates their loads there, so positions follow the
+  // workgroup id and spread over the XCDs)
+  if constexpr (WMODE == kWinPipe) c.pos = int(blockIdx.x);
   {
     const int full = n_all / c.G;  // complete rounds
     c.n = full + (item_index(c, full) < n_all ? 1 : 0);
