@@ -187,6 +187,17 @@ def test_block_window_long_samples(window):
     full_parity(w)
 
 
+@pytest.mark.parametrize("D,window", [(32, 256), (64, 256), (64, 64), (32, 192)])
+def test_block_window_pipeline_long_samples_small_d(D, window):
+    """Block windows of up to four blocks at D = 32 and 64 on samples longer
+    than one pipelined run of 16 query blocks (1024 rows): runs that start
+    past a sample's first block walk a halo of nb - 1 tiles before it."""
+    L = [1500, 2049, 700, 3001, 1025, 64]
+    w = adhoc("pipe_long_small_d", "self", "softmax", "bf16", L, L, 3, D, window=window, seed=window + D + 11)
+    log(f"pipeline long samples D={D} W={window}: N={w.total_q}")
+    full_parity(w)
+
+
 def test_block_window_pipeline_many_items():
     """Block windows of up to four blocks run as pipelined runs of query blocks:
     about 330 runs per workgroup (short samples, 80 heads), more than a
