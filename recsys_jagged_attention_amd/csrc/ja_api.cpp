@@ -18,7 +18,6 @@ hipError_t launch_combine(int D, const CombineArgs& a, hipStream_t st);
 hipError_t launch_attn_f32(int D, int act, int window_mode, const AttnArgs& a, int grid, hipStream_t st);
 hipError_t launch_attn_pp(int D, int act, bool cross, const AttnArgs& a, int num_cu, int64_t max_items,
                           hipStream_t st);
-hipError_t launch_key_rms(int D, const void* k, int64_t rows, float eps, float* out, hipStream_t st);
 hipError_t launch_attn_bwd(int D, bool bf16, int act, int wmode, const BwdArgs& a, int64_t rows_q, int64_t rows_k,
                            int grid_q, int grid_k, hipStream_t st);
 hipError_t launch_attn_bwd_mfma(int D, int act, int wmode, const BwdArgs& a, int grid_q, int grid_k,
@@ -259,6 +258,17 @@ int jagged_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
   pa.nsplit = nsplit;
   pa.pbase = pbase;
   pa.items = items;
+  const float rms_eps = io->rms_eps > 0.f ? io->rms_eps : 1e-6f;
+  float* ksc = nullptr;
+  if (p.shape == kShapePingPong && act != JA_SOFTMAX) {
+    // the key RMS factors are computed by extra workgroups of the plan launch
+    ksc = reinterpret_cast<float*>(ws + p.ws.kscale_off);
+    pa.krms_k = k;
+    pa.krms_rows = int64_t(io->total_kv) * H;
+    pa.krms_d = D;
+    pa.krms_eps = rms_eps;
+    pa.krms_out = ksc;
+  }
   if (launch_plan(pa, stream) != hipSuccess) return JA_EHIP;
 
   AttnArgs aa{};
@@ -281,13 +291,8 @@ int jagged_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
   aa.window_blocks = variant == JA_SLIDING ? 0 : window / kBlock;
   aa.window_tokens = variant == JA_SLIDING ? window : 0;
   aa.kvc = p.kvc;
-  aa.eps = io->rms_eps > 0.f ? io->rms_eps : 1e-6f;
-  aa.kscale = nullptr;
-  if (p.shape == kShapePingPong && act != JA_SOFTMAX) {
-    float* ksc = reinterpret_cast<float*>(ws + p.ws.kscale_off);
-    if (launch_key_rms(D, k, int64_t(io->total_kv) * H, aa.eps, ksc, stream) != hipSuccess) return JA_EHIP;
-    aa.kscale = ksc;
-  }
+  aa.eps = rms_eps;
+  aa.kscale = ksc;
   const float inv_sqrt_d = 1.0f / std::sqrt(float(D));
   aa.score_scale = act == JA_SOFTMAX ? inv_sqrt_d * 1.4426950408889634f : inv_sqrt_d;
 

@@ -786,38 +786,3 @@ hipError_t launch_attn_pp(int D, int act, bool cross, const AttnArgs& a, int num
 }
 
 }  // namespace ja
-
-namespace ja {
-namespace {
-
-// RMS factor (mean over D of k^2 + eps)^(-1/2) of every (key row, head): the
-// QK-RMSNorm of the keys as a per-key scale (techfeed.io GDPA section: Q and
-// K are RMS-normalised before the GELU scores).  One thread per row.
-template <int D>
-__global__ __launch_bounds__(256) void key_rms_kernel(const __bf16* k, int64_t rows, float eps, float* out) {
-  const int64_t r = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (r >= rows) return;
-  const bf16x8* p = reinterpret_cast<const bf16x8*>(k + r * D);
-  float ss = 0.f;
-#pragma unroll
-  for (int c = 0; c < D / 8; ++c) {
-    const bf16x8 x = p[c];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) ss = fmaf(float(x[j]), float(x[j]), ss);
-  }
-  out[r] = __builtin_amdgcn_rsqf(ss * (1.0f / D) + eps);
-}
-
-}  // namespace
-
-hipError_t launch_key_rms(int D, const void* k, int64_t rows, float eps, float* out, hipStream_t st) {
-  if (rows <= 0) return hipSuccess;
-  const dim3 gd(unsigned((rows + 255) / 256)), bd(256);
-  const __bf16* kp = reinterpret_cast<const __bf16*>(k);
-  if (D == 32) hipLaunchKernelGGL((key_rms_kernel<32>), gd, bd, 0, st, kp, rows, eps, out);
-  else if (D == 64) hipLaunchKernelGGL((key_rms_kernel<64>), gd, bd, 0, st, kp, rows, eps, out);
-  else hipLaunchKernelGGL((key_rms_kernel<128>), gd, bd, 0, st, kp, rows, eps, out);
-  return hipGetLastError();
-}
-
-}  // namespace ja

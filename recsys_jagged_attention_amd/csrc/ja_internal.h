@@ -77,6 +77,14 @@ struct PlanArgs {
   int32_t* nsplit;
   int32_t* pbase;
   WorkItem* items;
+  // Side job of the same launch (GELU scores on the tile stream): the RMS
+  // factor (mean over D of k^2 + eps)^(-1/2) of each of krms_rows bf16 key
+  // rows of krms_d elements into krms_out, by workgroups 1.. (0 rows: none).
+  const void* krms_k;
+  int64_t krms_rows;
+  int krms_d;
+  float krms_eps;
+  float* krms_out;
 };
 
 struct AttnArgs {

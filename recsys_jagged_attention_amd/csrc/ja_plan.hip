@@ -156,7 +156,33 @@ __device__ inline void fail(const PlanArgs& a, int status) {
 
 }  // namespace
 
+// RMS factor of key row r (QK-RMSNorm of the keys as a per-key scale of the
+// GELU scores: techfeed.io summary, GDPA section).  One thread per row.
+template <int D>
+__device__ void key_rms_row(const PlanArgs& a, int64_t r) {
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  const bf16x8* p = reinterpret_cast<const bf16x8*>(reinterpret_cast<const __bf16*>(a.krms_k) + r * D);
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < D / 8; ++c) {
+    const bf16x8 x = p[c];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ss = fmaf(float(x[j]), float(x[j]), ss);
+  }
+  a.krms_out[r] = __builtin_amdgcn_rsqf(ss * (1.0f / D) + a.krms_eps);
+}
+
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
+  if (blockIdx.x > 0) {
+    // the key RMS side job: rows (blockIdx.x - 1) * kPlanThreads + tid
+    const int64_t r = int64_t(blockIdx.x - 1) * kPlanThreads + threadIdx.x;
+    if (r < a.krms_rows) {
+      if (a.krms_d == 32) key_rms_row<32>(a, r);
+      else if (a.krms_d == 64) key_rms_row<64>(a, r);
+      else key_rms_row<128>(a, r);
+    }
+    return;
+  }
   __shared__ int s_bad;
   __shared__ int s_iwarp[3 * kPlanWaves];
   __shared__ Sums s_swarp[2 * kPlanWaves + 1];
@@ -312,7 +338,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 }
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, a);
+  const int64_t side = a.krms_rows > 0 ? (a.krms_rows + kPlanThreads - 1) / kPlanThreads : 0;
+  hipLaunchKernelGGL(plan_kernel, dim3(unsigned(1 + side)), dim3(kPlanThreads), 0, st, a);
   return hipGetLastError();
 }
 
