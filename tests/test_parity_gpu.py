@@ -64,6 +64,18 @@ def test_self_full_edges(D, dtype):
 
 
 @pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("act,dtype", [("gelu_tanh", "bf16"), ("gelu_poly", "bf16"), ("gelu_tanh", "f32")])
+def test_self_gelu(D, act, dtype):
+    """Full self-attention with QK-RMSNorm and GELU scores: ragged and empty
+    samples plus samples of several 256-row items, so that the key RMS factors
+    (computed beside the plan) span more than one workgroup of rows."""
+    L = EDGE_LENGTHS + [700, 1100]
+    w = adhoc("self_gelu", "self", act, dtype, L, L, 2, D, seed=D + 17)
+    log(f"self gelu D={D} {act} {dtype}")
+    full_parity(w)
+
+
+@pytest.mark.parametrize("D", [32, 64, 128])
 @pytest.mark.parametrize("window", [64, 128, 256, 512])
 def test_block_window_edges(D, window):
     w = adhoc("window_edges", "self", "softmax", "bf16", EDGE_LENGTHS + [300, 520], EDGE_LENGTHS + [300, 520],
