@@ -210,6 +210,32 @@ def test_block_window_pipeline_long_samples_small_d(D, window):
     full_parity(w)
 
 
+@pytest.mark.parametrize("case", ["block_pipeline", "cross", "pma", "f32_self"])
+def test_more_samples_than_plan_threads(case):
+    """Batches of more samples than the plan kernel has threads (1024): the
+    plan rescans the offsets chunk by chunk, carries item and slot counts
+    across chunks, and (cost order) buckets every chunk's items by their own
+    tile counts.  Rows are sampled across the whole batch."""
+    rng = np.random.Generator(np.random.PCG64(91))
+    B = 2500
+    if case == "block_pipeline":
+        L = rng.integers(1, 200, size=B).tolist()
+        w = adhoc("plan_chunks_pipe", "self", "softmax", "bf16", L, L, 2, 32, window=128, seed=92)
+    elif case == "cross":
+        lq = rng.integers(1, 40, size=B).tolist()
+        lk = rng.integers(0, 80, size=B).tolist()
+        w = adhoc("plan_chunks_cross", "cross", "gelu_tanh", "bf16", lq, lk, 2, 32, seed=93)
+    elif case == "pma":
+        lk = rng.integers(1, 3000, size=B).tolist()
+        w = adhoc("plan_chunks_pma", "pma", "softmax", "bf16", [32] * B, lk, 2, 64, seed=94)
+    else:
+        L = rng.integers(1, 100, size=B).tolist()
+        w = adhoc("plan_chunks_f32", "self", "softmax", "f32", L, L, 2, 32, seed=95)
+    log(f"more samples than plan threads, {case}: B={B} Nq={w.total_q} Nk={w.total_kv}")
+    out = run_gpu(w)
+    sampled_parity(w, out, n=240)
+
+
 def test_block_window_pipeline_many_items():
     """Block windows of up to four blocks run as pipelined runs of query blocks:
     about 330 runs per workgroup (short samples, 80 heads), more than a
