@@ -38,7 +38,9 @@
  *   offsets[B] == total_q / total_kv.  Sample b owns rows [off[b], off[b+1]).
  *   JA_SELF and JA_SLIDING need q_offsets and kv_offsets to hold the same
  *   values (the same pointer may be passed twice).  Buffers need 16-byte
- *   alignment.
+ *   alignment.  In jagged_attn_fwd, q, out and q_scale may be NULL when
+ *   total_q == 0, and k, v, k_scale and v_scale when total_kv == 0 (empty
+ *   tensors); the offsets are always required.
  *
  * Ownership.  The caller owns every buffer, including the workspace.  The
  * library allocates nothing inside jagged_attn_fwd and keeps only a per-device

@@ -222,8 +222,13 @@ int jagged_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
   if (io == nullptr) return JA_EINVAL;
   const int st = validate(B, H, D, variant, act, window, io->dtype, io->total_q, io->total_kv);
   if (st != JA_OK) return st;
-  if (!q || !k || !v || !q_offsets || !kv_offsets || !out) return JA_EINVAL;
-  if (io->dtype == JA_MXFP8_E4M3 && (!io->q_scale || !io->k_scale || !io->v_scale)) return JA_EINVAL;
+  if (!q_offsets || !kv_offsets) return JA_EINVAL;
+  // Empty tensors may come with null data pointers: no kernel reads q or
+  // writes out without query rows, nor reads k or v without key rows.
+  const bool has_q = io->total_q > 0, has_kv = io->total_kv > 0;
+  if ((has_q && (!q || !out)) || (has_kv && (!k || !v))) return JA_EINVAL;
+  if (io->dtype == JA_MXFP8_E4M3 && ((has_q && !io->q_scale) || (has_kv && (!io->k_scale || !io->v_scale))))
+    return JA_EINVAL;
   const Plan p = make_plan(B, H, D, variant, act, window, io->dtype, io->total_q, io->total_kv);
   if (io->workspace == nullptr || io->workspace_bytes < p.ws.total) return JA_EWORKSPACE;
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v) |

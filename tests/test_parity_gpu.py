@@ -210,6 +210,33 @@ def test_block_window_pipeline_long_samples_small_d(D, window):
     full_parity(w)
 
 
+@pytest.mark.parametrize("variant,act,dtype,window", [
+    ("self", "softmax", "bf16", 0), ("self", "softmax", "f32", 0), ("self", "softmax", "bf16", 256),
+    ("self", "gelu_tanh", "bf16", 0), ("cross", "gelu_tanh", "bf16", 0), ("pma", "softmax", "bf16", 0),
+    ("sliding", "softmax", "bf16", 100), ("self", "softmax", "mxfp8", 256)])
+def test_batch_of_empty_samples(variant, act, dtype, window):
+    """Every sample empty (no query and no key rows): the call succeeds with
+    empty tensors, whose data pointers may be null, and returns no rows."""
+    L = [0, 0, 0]
+    w = adhoc("all_empty", variant, act, dtype, L, L, 2, 64 if dtype != "mxfp8" else 128, window=window, seed=3)
+    log(f"empty batch {variant} {act} {dtype} W={window}")
+    out = run_gpu(w)
+    assert out.shape == (0, 2, w.D)
+
+
+@pytest.mark.parametrize("variant,act,dtype", [
+    ("cross", "softmax", "bf16"), ("cross", "gelu_tanh", "bf16"), ("pma", "softmax", "bf16"),
+    ("cross", "gelu_tanh", "mxfp8"), ("pma", "gelu_tanh", "mxfp8"), ("cross", "softmax", "f32")])
+def test_every_sample_without_keys(variant, act, dtype):
+    """Queries but no key rows at all (total_kv = 0): every output row is 0."""
+    lq = [32, 32, 32] if variant == "pma" else [5, 300, 64]
+    w = adhoc("no_keys", variant, act, dtype, lq, [0, 0, 0], 2, 128, seed=4)
+    log(f"no keys {variant} {act} {dtype}")
+    out = run_gpu(w)
+    assert out.shape == (sum(lq), 2, 128)
+    assert np.all(out == 0)
+
+
 @pytest.mark.parametrize("case", ["block_pipeline", "cross", "pma", "f32_self"])
 def test_more_samples_than_plan_threads(case):
     """Batches of more samples than the plan kernel has threads (1024): the
