@@ -85,9 +85,12 @@ def sampled_parity(w, out, n=96, seed=0):
     qo, ko = w.q_offsets, w.kv_offsets
     ref = []
     vmax = 0.0
+    decoded = {}  # sample -> its q, k, v (decoding a long MX sample takes seconds)
     for t, h in rows:
         b = int(np.searchsorted(qo, t, side="right") - 1)
-        sub = _sample_values(w, b)
+        if b not in decoded:
+            decoded[b] = _sample_values(w, b)
+        sub = decoded[b]
         vmax = max(vmax, float(np.abs(sub[2]).max()) if sub[2].size else 0.0)
         ref.append(oracle.gdpa_rows(*sub, [(t - int(qo[b]), h)], w.variant, oracle_act(w.act), w.window)[0])
     ref = np.stack(ref)

@@ -237,6 +237,26 @@ def test_every_sample_without_keys(variant, act, dtype):
     assert np.all(out == 0)
 
 
+@pytest.mark.parametrize("variant,act,dtype,window", [
+    ("self", "softmax", "bf16", 256), ("self", "softmax", "bf16", 0), ("cross", "gelu_tanh", "bf16", 0),
+    ("pma", "softmax", "bf16", 0), ("self", "softmax", "f32", 0), ("self", "softmax", "mxfp8", 0)])
+def test_most_heads(variant, act, dtype, window):
+    """H = 4096, the most heads the library takes, at D = 128: a token row of
+    q, k or v is 1 MiB (2 MiB in fp32), the largest row stride any kernel
+    addresses; ragged samples of a few tiles."""
+    H = 4096
+    if variant == "pma":
+        lq, lk = [32, 7], [70, 130]
+    elif variant == "cross":
+        lq, lk = [70, 5], [64, 3]
+    else:
+        lq = lk = [70, 5]
+    w = adhoc("most_heads", variant, act, dtype, lq, lk, H, 128, window=window, seed=13)
+    log(f"H={H} {variant} {act} {dtype} W={window}")
+    out = run_gpu(w)
+    sampled_parity(w, out, n=200)
+
+
 @pytest.mark.parametrize("case", ["block_pipeline", "cross", "pma", "f32_self"])
 def test_more_samples_than_plan_threads(case):
     """Batches of more samples than the plan kernel has threads (1024): the
