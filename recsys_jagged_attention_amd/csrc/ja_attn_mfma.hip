@@ -340,13 +340,24 @@ __global__ __launch_bounds__(64 * NWQ * NWK, QSUB == 2 ? 1 : 2) void attn_kernel
   const size_t rs = size_t(a.H) * D;
 
   // Items [xcd_begin[x], xcd_begin[x+1]) belong to XCD x = blockIdx.x % 8.
+  // Key splits (PMA) come sorted by their key tiles, most first, and are dealt
+  // in rounds of gridDim.x, forward on even rounds and backward on odd ones:
+  // their costs differ by two orders of magnitude, and contiguous ranges left
+  // the slowest workgroup at 1.5x the mean.
   const int n = a.hdr->n_items;
   const int x = blockIdx.x % kXcds;
   const int beg = min(a.hdr->xcd_begin[x], n);
   const int end = min(max(a.hdr->xcd_begin[x + 1], beg), n);
   const int stride = gridDim.x / kXcds;
-  int idx = beg + int(blockIdx.x) / kXcds;
-  if (idx >= end) return;
+  const int G = int(gridDim.x), pos = int(blockIdx.x);
+  auto dealt = [&](int k) { return k * G + ((k & 1) ? G - 1 - pos : pos); };
+  int n_mine = 0, k_mine = 0;  // (key splits) items of this workgroup, and which one is current
+  if constexpr (SPLIT) {
+    const int full = n / G;
+    n_mine = full + (dealt(full) < n ? 1 : 0);
+  }
+  int idx = SPLIT ? dealt(0) : beg + int(blockIdx.x) / kXcds;
+  if (SPLIT ? n_mine == 0 : idx >= end) return;
 
   // Lane-constant LDS byte offsets of the MFMA operand reads.
   const int kp = key_perm(l32);
@@ -450,8 +461,8 @@ __global__ __launch_bounds__(64 * NWQ * NWK, QSUB == 2 ? 1 : 2) void attn_kernel
       }
     }
 
-    const int next_idx = idx + stride;
-    const bool has_next = next_idx < end;
+    const bool has_next = SPLIT ? k_mine + 1 < n_mine : idx + stride < end;
+    const int next_idx = SPLIT ? (has_next ? dealt(k_mine + 1) : idx) : idx + stride;
     Item nxt = cur;
     if (has_next) nxt = K::make_item(a, a.items[next_idx], rs);
 
@@ -770,6 +781,7 @@ __global__ __launch_bounds__(64 * NWQ * NWK, QSUB == 2 ? 1 : 2) void attn_kernel
     if (!has_next) break;
     idx = next_idx;
     cur = nxt;
+    ++k_mine;
   }
 }
 

@@ -40,6 +40,9 @@ __device__ inline int cost_bucket(const PlanArgs& a, int qt, int lq, int lk) {
   return min(max(te - tl, 0), kCostBuckets - 1);
 }
 
+// Cost bucket of a key-split item of `keys` keys (one query tile): its key tiles.
+__device__ inline int split_bucket(int keys) { return min((keys + kBlock - 1) / kBlock, kCostBuckets - 1); }
+
 // Length of the run of query tiles from qt on that share qt's cost bucket,
 // found without visiting them one by one: without a window every item walks
 // the same tiles; with one, the full items past the window's clamp at the
@@ -215,7 +218,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       mine.cost += w.cnt * w.ck;
       mine.items += w.cnt;
       mine.slots += w.slots;
-      if (a.cost_order && w.cnt > 0)
+      if (a.cost_order && w.cnt > 0 && w.ns > 1) {
+        // key splits (one query tile): ns - 1 chunks of kvc keys, then the rest
+        atomicAdd(&s_bucket[split_bucket(a.kvc)], (w.ns - 1) * a.H);
+        atomicAdd(&s_bucket[split_bucket(k1 - k - (w.ns - 1) * a.kvc)], a.H);
+      } else if (a.cost_order && w.cnt > 0)
         for (int qt = 0; qt < w.nqt;) {
           const int run = cost_run(a, qt, w.nqt);
           atomicAdd(&s_bucket[cost_bucket(a, qt, q1 - q, k1 - k)], run * a.H * w.ns);
@@ -306,7 +313,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       const int nq = s_nqt[j], nsj = s_ns[j];
       const int qbj = s_qb[j], lqj = s_lq[j], kbj = s_kb[j], lkj = s_lk[j];
       if (nq == 0) continue;
-      if (a.cost_order) {
+      if (a.cost_order && nsj > 1) {
+        // key splits of the sample's one query tile: the full chunks, then the rest
+        int ib = atomicAdd(&s_bucket[split_bucket(a.kvc)], nsj - 1);
+        for (int sp = 0; sp < nsj - 1; ++sp) a.items[ib++] = WorkItem{base + j, h, 0, sp, qbj, lqj, kbj, lkj};
+        ib = atomicAdd(&s_bucket[split_bucket(lkj - (nsj - 1) * a.kvc)], 1);
+        a.items[ib] = WorkItem{base + j, h, 0, nsj - 1, qbj, lqj, kbj, lkj};
+      } else if (a.cost_order) {
         // each run of equal cost takes consecutive places in its bucket
         for (int qt0 = 0; qt0 < nq;) {
           const int run = cost_run(a, qt0, nq);
