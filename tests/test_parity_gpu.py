@@ -97,7 +97,9 @@ def test_cross_edges(D, act):
 @pytest.mark.parametrize("D", [32, 64, 128])
 @pytest.mark.parametrize("act", ["softmax", "gelu_tanh"])
 def test_pma_edges(D, act):
-    lk = [0, 1, 63, 64, 65, 511, 512, 513, 1500, 4097]
+    # the key chunk is 512 here: 512 keys fit one chunk, 513 and 4097 leave a
+    # one-key last chunk, 1024 two full ones
+    lk = [0, 1, 63, 64, 65, 511, 512, 513, 1024, 1500, 4097]
     lq = [32] * len(lk)
     lq[2] = 7                # fewer seeds than a tile
     w = adhoc("pma_edges", "pma", act, "bf16", lq, lk, 2, D, seed=D + 11)
