@@ -256,7 +256,7 @@ int jagged_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
   pa.self_check = variant == JA_SELF || variant == JA_SLIDING;
   pa.window_blocks = variant == JA_SLIDING ? 0 : window / kBlock;
   pa.window_tokens = variant == JA_SLIDING ? window : 0;
-  pa.cost_order = p.shape == kShapePingPong || p.shape == kShapeKvSplit;
+  pa.cost_order = p.shape == kShapePingPong || p.shape == kShapeKvSplit || p.shape == kShapeWindow;
   pa.max_items = p.ws.max_items;
   pa.max_slots = p.ws.max_slots;
   pa.hdr = hdr;
@@ -296,6 +296,7 @@ int jagged_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
   aa.window_blocks = variant == JA_SLIDING ? 0 : window / kBlock;
   aa.window_tokens = variant == JA_SLIDING ? window : 0;
   aa.kvc = p.kvc;
+  aa.dealt = p.shape == kShapeKvSplit || p.shape == kShapeWindow;
   aa.eps = rms_eps;
   aa.kscale = ksc;
   const float inv_sqrt_d = 1.0f / std::sqrt(float(D));

@@ -339,25 +339,30 @@ __global__ __launch_bounds__(64 * NWQ * NWK, QSUB == 2 ? 1 : 2) void attn_kernel
   const int l32 = lane & 31, g = lane >> 5;
   const size_t rs = size_t(a.H) * D;
 
-  // Items [xcd_begin[x], xcd_begin[x+1]) belong to XCD x = blockIdx.x % 8.
-  // Key splits (PMA) come sorted by their key tiles, most first, and are dealt
-  // in rounds of gridDim.x, forward on even rounds and backward on odd ones:
-  // their costs differ by two orders of magnitude, and contiguous ranges left
-  // the slowest workgroup at 1.5x the mean.
+  // Without dealing, items [xcd_begin[x], xcd_begin[x+1]) belong to XCD
+  // x = blockIdx.x % 8.  Key splits (PMA) and windows come sorted by their key
+  // tiles, most first, and are dealt in rounds of gridDim.x, forward on even
+  // rounds and backward on odd ones: PMA costs differ by two orders of
+  // magnitude, and contiguous ranges left the slowest workgroup at 1.5x the
+  // mean.  Windows deal over positions that run XCD by XCD (the grid is a
+  // multiple of 8): neighbouring query tiles share key tiles, and dealt over
+  // plain workgroup ids they read 1.7x the bytes from HBM.
   const int n = a.hdr->n_items;
   const int x = blockIdx.x % kXcds;
   const int beg = min(a.hdr->xcd_begin[x], n);
   const int end = min(max(a.hdr->xcd_begin[x + 1], beg), n);
   const int stride = gridDim.x / kXcds;
-  const int G = int(gridDim.x), pos = int(blockIdx.x);
+  const bool deal = a.dealt != 0;
+  const int G = int(gridDim.x);
+  const int pos = SPLIT ? int(blockIdx.x) : x * stride + int(blockIdx.x) / kXcds;
   auto dealt = [&](int k) { return k * G + ((k & 1) ? G - 1 - pos : pos); };
-  int n_mine = 0, k_mine = 0;  // (key splits) items of this workgroup, and which one is current
-  if constexpr (SPLIT) {
+  int n_mine = 0, k_mine = 0;  // (dealing) items of this workgroup, and which one is current
+  if (deal) {
     const int full = n / G;
     n_mine = full + (dealt(full) < n ? 1 : 0);
   }
-  int idx = SPLIT ? dealt(0) : beg + int(blockIdx.x) / kXcds;
-  if (SPLIT ? n_mine == 0 : idx >= end) return;
+  int idx = deal ? dealt(0) : beg + int(blockIdx.x) / kXcds;
+  if (deal ? n_mine == 0 : idx >= end) return;
 
   // Lane-constant LDS byte offsets of the MFMA operand reads.
   const int kp = key_perm(l32);
@@ -461,8 +466,8 @@ __global__ __launch_bounds__(64 * NWQ * NWK, QSUB == 2 ? 1 : 2) void attn_kernel
       }
     }
 
-    const bool has_next = SPLIT ? k_mine + 1 < n_mine : idx + stride < end;
-    const int next_idx = SPLIT ? (has_next ? dealt(k_mine + 1) : idx) : idx + stride;
+    const bool has_next = deal ? k_mine + 1 < n_mine : idx + stride < end;
+    const int next_idx = deal ? (has_next ? dealt(k_mine + 1) : idx) : idx + stride;
     Item nxt = cur;
     if (has_next) nxt = K::make_item(a, a.items[next_idx], rs);
 

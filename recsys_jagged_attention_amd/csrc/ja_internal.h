@@ -108,6 +108,7 @@ struct AttnArgs {
   int window_blocks;  // 0 = no window
   int window_tokens;  // sliding window in tokens (0 = none)
   int kvc;
+  int dealt;          // items come sorted by cost, most first, and are dealt in alternating rounds
   float score_scale;  // softmax: log2(e)/sqrt(D); GELU: 1/sqrt(D)
   float eps;
 };
