@@ -7,9 +7,11 @@ HBM.  Several copies of the batch are cycled so that no step reads data a
 previous step left in the 256 MB last-level cache.
 
 Prints ONE JSON line: useful (unpadded) TFLOPS of the whole job, the
-roofline of the dominant (attention) kernel timed live with HIP events
-recorded around that kernel's launch, and the float64 CPU oracle timed on a
-bounded sample of the same workload.
+roofline of the dominant (attention) kernel timed live with HIP events that
+its own dispatch writes (start and end), the step period between consecutive
+steps, the float64 CPU oracle timed on a bounded sample of the same workload,
+and the error of the last timed step's output against the oracle on that
+sample.
 
   python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload block_window]
 """
@@ -77,6 +79,54 @@ class HipEvents:
             raise RuntimeError("hipEventRecord failed")
 
 
+def device_info() -> dict:
+    """Compute units and the engine clock the HIP runtime reports (kHz -> MHz)."""
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipDeviceGetAttribute.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.c_int, ctypes.c_int]
+    hip.hipGetDevice.argtypes = [ctypes.POINTER(ctypes.c_int)]
+    dev = ctypes.c_int()
+    hip.hipGetDevice(ctypes.byref(dev))
+    info = {}
+    # hipDeviceAttribute_t values of the ROCm headers
+    for name, attr in (("compute_units", "hipDeviceAttributeMultiprocessorCount"),
+                       ("clock_mhz", "hipDeviceAttributeClockRate")):
+        v = ctypes.c_int()
+        code = HIP_ATTR.get(attr)
+        if code is not None and hip.hipDeviceGetAttribute(ctypes.byref(v), code, dev.value) == 0:
+            info[name] = v.value // 1000 if name == "clock_mhz" else v.value
+    return info
+
+
+def _hip_attr_codes() -> dict:
+    """Enum values of hipDeviceAttribute_t, read from the installed HIP header."""
+    import re
+    try:
+        src = open("/opt/rocm/include/hip/hip_runtime_api.h").read()
+    except OSError:
+        return {}
+    body = src[src.index("typedef enum hipDeviceAttribute_t {") + len("typedef enum hipDeviceAttribute_t {"):]
+    body = body[:body.index("} hipDeviceAttribute_t;")]
+    body = re.sub(r"//[^\n]*", "", body)
+    codes, idx = {}, -1
+    for entry in body.split(","):
+        entry = entry.strip()
+        if not entry:
+            continue
+        m = re.fullmatch(r"(\w+)\s*(?:=\s*(\w+))?", entry)
+        if not m:
+            continue
+        if m.group(2) is not None:
+            g = m.group(2)
+            idx = int(g, 0) if g[0].isdigit() else codes[g]
+        else:
+            idx += 1
+        codes[m.group(1)] = idx
+    return codes
+
+
+HIP_ATTR = _hip_attr_codes()
+
+
 def blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
@@ -86,9 +136,11 @@ def blas_threads() -> int:
         return 1
 
 
-def cpu_baseline(w, budget_s: float):
+def cpu_baseline(w, budget_s: float, gpu_out=None):
     """Time the float64 oracle on whole samples of the workload (seeded order)
-    until about budget_s seconds of CPU work; report useful TFLOPS."""
+    until about budget_s seconds of CPU work; report useful TFLOPS.  With the
+    output of a timed GPU step (``gpu_out``, float64 [total_q, H, D]), also
+    report max|O_gpu - O_ref| / max|O_ref| over the samples the oracle ran."""
     import oracle
     from recsys_jagged_attention_amd.inputs import cast_values
     from recsys_jagged_attention_amd import workload as wl
@@ -96,6 +148,7 @@ def cpu_baseline(w, budget_s: float):
     rng = np.random.Generator(np.random.PCG64(w.seed + 7))
     order = rng.permutation(w.B)
     spent, flops, used = 0.0, 0, []
+    err_num, ref_max = 0.0, 0.0
     for b in order:
         q0, q1 = int(w.q_offsets[b]), int(w.q_offsets[b + 1])
         k0, k1 = int(w.kv_offsets[b]), int(w.kv_offsets[b + 1])
@@ -108,13 +161,16 @@ def cpu_baseline(w, budget_s: float):
                        for x in (w.q[q0:q1], w.k[k0:k1], w.v[k0:k1]))
         qo, ko = np.array([0, q1 - q0]), np.array([0, k1 - k0])
         t0 = time.perf_counter()
-        oracle.gdpa_forward(q, k, v, qo, ko, w.variant, w.act, w.window)
+        ref = oracle.gdpa_forward(q, k, v, qo, ko, w.variant, w.act, w.window)
         spent += time.perf_counter() - t0
+        if gpu_out is not None and ref.size:
+            err_num = max(err_num, float(np.abs(gpu_out[q0:q1] - ref).max()))
+            ref_max = max(ref_max, float(np.abs(ref).max()))
         flops += wl.useful_flops([q1 - q0], [k1 - k0], w.H, w.D, w.window, w.variant)
         used.append(int(b))
         if spent >= budget_s:
             break
-    return {
+    res = {
         "value": flops / spent / 1e12 if spent > 0 else None,
         "unit": "TFLOPS",
         "cores": blas_threads(),
@@ -122,6 +178,11 @@ def cpu_baseline(w, budget_s: float):
         "sample": f"{len(used)} of {w.B} samples of the {w.name} batch (seeded order), "
                   f"{flops / 1e9:.2f} useful GFLOP in {spent:.1f} s, numpy float64",
     }
+    parity = None
+    if gpu_out is not None and ref_max > 0:
+        parity = {"max_abs_err_over_max_ref": err_num / ref_max, "samples": len(used),
+                  "rows": int(sum(int(w.q_offsets[b + 1] - w.q_offsets[b]) for b in used)) * w.H}
+    return res, parity
 
 
 # Source file of each forward kernel, and the headers every kernel file includes.
@@ -142,10 +203,15 @@ def kernel_source_hash(kernel_tag: str) -> str:
     return h.hexdigest()
 
 
+def profile_path(kernel_tag: str, workload: str) -> str:
+    """The committed rocprofv3 summary of a kernel on a workload."""
+    return os.path.join(ROOT, "profiles", f"{kernel_tag.split('<')[0]}_{workload}.txt")
+
+
 def load_traffic(kernel_tag: str, workload: str):
     """HBM bytes per launch from committed rocprofv3 counter summaries, only if
     they were taken on the current kernel source (matching source hash)."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    path = profile_path(kernel_tag, workload)
     if not os.path.exists(path):
         return None
     kv = {}
@@ -432,7 +498,11 @@ def main():
         step(i, (starts[i], stops[i]))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    kern_ms = [ev.elapsed_ms(starts[i], stops[i]) for i in range(K)]
+    # kernel durations (start and end stamps of each attention dispatch), and
+    # the step period: the time between the ends of consecutive steps'
+    # attention kernels (plan, gaps and attention of one step, back to back)
+    kern_ms = np.array([ev.elapsed_ms(starts[i], stops[i]) for i in range(K)])
+    period_ms = np.array([ev.elapsed_ms(stops[i - 1], stops[i]) for i in range(1, K)])
     for e in starts + stops:
         ev.destroy(e)
     ms_per_step = (t1 - t0) * 1e3 / K
@@ -452,17 +522,24 @@ def main():
     roof["traffic"] = load_traffic(kernel_tag, w.name)
     roof["kernel"] = kernel_tag
     roof["kernel_avg_us"] = round(kern_avg_s * 1e6, 2)
+    roof["kernel_us"] = {"median": round(float(np.median(kern_ms)) * 1e3, 2),
+                         "min": round(float(np.min(kern_ms)) * 1e3, 2),
+                         "p90": round(float(np.percentile(kern_ms, 90)) * 1e3, 2)}
     roof["algorithmic_bytes_per_launch"] = int(alg_bytes)
     roof["useful_flops_per_launch"] = int(flops)
+    roof["frac_of_peak_flops"] = round(flops / kern_avg_s / 1e12 / PEAK_TFLOPS[w.dtype], 4)
     log(f"[bench] {ms_per_step * 1e3:.1f} us/step, kernel {kern_avg_s * 1e6:.1f} us, "
         f"{value:.1f} useful TFLOPS, {roof['achieved']} {roof['unit']} ({roof['frac'] * 100:.1f}% of peak)")
 
-    cpu = None
+    cpu, parity = None, None
     if not args.no_cpu_baseline:
         t_cpu = time.perf_counter()
-        cpu = cpu_baseline(w, args.cpu_seconds)
+        last = outs[(K - 1) % n_copies].float().cpu().numpy().astype(np.float64)  # output of the last timed step
+        cpu, parity = cpu_baseline(w, args.cpu_seconds, gpu_out=last)
         log(f"[bench] cpu oracle baseline {cpu['value']:.4g} TFLOPS on {cpu['cores']} threads "
-            f"({time.perf_counter() - t_cpu:.1f}s)")
+            f"({time.perf_counter() - t_cpu:.1f}s); timed output vs oracle {parity}")
+    dev_info = device_info()
+    padded = wl.padded_dense_flops(lq, lk, w.H, w.D, w.window)
 
     line = {
         "metric": METRIC,
@@ -478,9 +555,15 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "pct_bf16_peak": round(100 * value / PEAK_TFLOPS["bf16"], 2),
+        "step_us": {"median": round(float(np.median(period_ms)) * 1e3, 2) if K > 1 else None,
+                    "min": round(float(np.min(period_ms)) * 1e3, 2) if K > 1 else None,
+                    "p90": round(float(np.percentile(period_ms, 90)) * 1e3, 2) if K > 1 else None},
         "config": {"workload": w.name, "variant": w.variant, "act": w.act, "B": w.B, "H": w.H, "D": w.D,
                    "window": w.window, "total_q": w.total_q, "total_kv": w.total_kv, "seed": w.seed,
-                   "useful_gflop": round(flops / 1e9, 3), "parallelism": "single GPU"},
+                   "useful_gflop": round(flops / 1e9, 3), "padded_dense_gflop": round(padded / 1e9, 3),
+                   "parallelism": "single GPU"},
+        "device": dev_info,
+        "parity": parity,
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -111,10 +111,21 @@ typedef struct ja_io {
   int32_t total_kv;          /* rows of k/v    (= kv_offsets[B])                */
   float rms_eps;             /* GELU acts: RMSNorm epsilon; <= 0 -> 1e-6        */
   void *ev_start;            /* optional profiling hipEvent_t pair (or NULL):   */
-  void *ev_stop;             /* recorded on `stream` right before and right     */
-                             /* after the attention kernel (not the plan or the */
-                             /* split-merge kernel), so its duration can be     */
-                             /* timed without a profiler                        */
+  void *ev_stop;             /* written by the attention kernel's own dispatch  */
+                             /* (its start and end; not the plan or the         */
+                             /* split-merge kernel), so the kernel can be timed */
+                             /* without a profiler and without extra packets    */
+  int32_t max_workgroups;    /* 0: the library's choice (every resident slot of */
+                             /* the device); > 0: at most this many workgroups  */
+                             /* for the attention kernel, rounded down to a     */
+                             /* multiple of 8 (at least 8), e.g. to leave CUs   */
+                             /* to concurrent work.  Results are bitwise        */
+                             /* identical for every grid.  < 0: JA_EINVAL       */
+  int32_t *status;           /* optional device int32 owned by the caller (4-B  */
+                             /* aligned): the device writes the call's status   */
+                             /* word (JA_OK or JA_EOFFSETS) there as well, on   */
+                             /* the stream, so it can be read back without      */
+                             /* jagged_attn_check; NULL: not written            */
 } ja_io;
 
 /* The forward pass.  Arguments as described above; window is 0 (no window) or
@@ -151,7 +162,8 @@ size_t jagged_attn_workspace_size(int B, int H, int D, int variant, int act,
  * with GELU).  Nothing from the forward is needed: row statistics and RMS
  * factors are recomputed.  Workspace of jagged_attn_bwd_workspace_size()
  * bytes in io->workspace; io->ev_start / ev_stop, when set, bracket the
- * gradient kernels.  Asynchronous on io->stream; errors as for
+ * gradient kernels (recorded around them on the stream); io->status as for
+ * jagged_attn_fwd; io->max_workgroups is not used.  Asynchronous on io->stream; errors as for
  * jagged_attn_fwd (JA_EUNSUPPORTED for JA_GELU_POLY and MXFP8; offset errors
  * through jagged_attn_check). */
 int jagged_attn_bwd(const void *q, const void *k, const void *v, const void *dout,

@@ -41,6 +41,8 @@ class JaIo(ctypes.Structure):
         ("rms_eps", ctypes.c_float),
         ("ev_start", ctypes.c_void_p),
         ("ev_stop", ctypes.c_void_p),
+        ("max_workgroups", ctypes.c_int32),
+        ("status", ctypes.c_void_p),
     ]
 
 

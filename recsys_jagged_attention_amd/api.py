@@ -34,16 +34,26 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             variant: str = "self", act: str = "softmax", window: int = 0,
             dtype: str = "bf16", scales=None, out: Optional[torch.Tensor] = None,
             workspace: Optional[Workspace] = None, rms_eps: float = 1e-6,
-            stream: Optional[torch.cuda.Stream] = None, check: bool = False,
-            events=None) -> torch.Tensor:
+            stream: Optional[torch.cuda.Stream] = None, check: Optional[bool] = None,
+            events=None, max_workgroups: int = 0, status: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Jagged GDPA forward.  q [Nq,H,D], k/v [Nk,H,D] on one GPU; offsets int32 [B+1].
 
     dtype "f32"/"bf16": q/k/v of that dtype; "mxfp8": uint8 e4m3 codes with
     ``scales=(q_scale, k_scale, v_scale)`` uint8 [rows,H,D/32].  Output is
-    float32 for "f32", else bfloat16.  With ``check=True`` the call
-    synchronises and raises on a device-side status (e.g. bad offsets).
-    ``events=(start, stop)`` are raw hipEvent_t handles recorded around the
-    attention kernel."""
+    float32 for "f32", else bfloat16.
+
+    The call is asynchronous on ``stream`` (default: the current stream).
+    Offsets are validated on the device; the output is unspecified unless that
+    status is JA_OK.  With ``check=True`` the call synchronises and raises on
+    a device-side status (e.g. bad offsets).  ``check`` defaults to True when
+    no ``workspace`` is passed (the status lives in the temporary workspace,
+    which is released on return) and to False otherwise; a caller that keeps
+    its workspace can check later with ``jagged_attn_check``, or pass
+    ``status`` (a 1-element int32 CUDA tensor the device writes the status
+    word into).  ``events=(start, stop)`` are raw hipEvent_t handles the
+    attention kernel's dispatch writes its start and end into.
+    ``max_workgroups`` caps the attention kernel's grid (0: every resident
+    slot); results do not depend on it."""
     if dtype not in _IN_DTYPES:
         raise ValueError(f"dtype must be one of {list(_IN_DTYPES)}")
     want = _IN_DTYPES[dtype]
@@ -61,16 +71,24 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if kv_offsets.numel() != B + 1:
         raise ValueError("q_offsets and kv_offsets must both have B+1 entries")
     out_dtype = torch.float32 if dtype == "f32" else torch.bfloat16
-    if out is None:
-        out = torch.empty((Nq, H, D), dtype=out_dtype, device=q.device)
-    elif out.shape != (Nq, H, D) or out.dtype != out_dtype or not out.is_contiguous():
-        raise ValueError("out has the wrong shape or dtype")
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    if check is None:
+        check = workspace is None
     v_id, a_id, d_id = _lib.VARIANTS[variant], _lib.ACTS[act], _lib.DTYPES[dtype]
     nbytes = _lib.jagged_attn_workspace_size(B, H, D, v_id, a_id, window, d_id, Nq, Nk)
     if nbytes == 0:
         # invalid or unsupported arguments: let the library report which
         nbytes = 256
-    ws = (workspace or Workspace(q.device)).get(nbytes)
+    # Temporaries are allocated on the launch stream: the caching allocator
+    # then reuses their blocks only for work ordered after these kernels.
+    with torch.cuda.stream(st):
+        if out is None:
+            out = torch.empty((Nq, H, D), dtype=out_dtype, device=q.device)
+        ws = (workspace or Workspace(q.device)).get(nbytes)
+    if out.shape != (Nq, H, D) or out.dtype != out_dtype or not out.is_contiguous():
+        raise ValueError("out has the wrong shape or dtype")
+    if status is not None and (status.dtype != torch.int32 or not status.is_cuda or status.numel() < 1):
+        raise ValueError("status must be an int32 CUDA tensor")
     io = _lib.JaIo()
     io.dtype = d_id
     if dtype == "mxfp8":
@@ -82,21 +100,23 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         io.q_scale, io.k_scale, io.v_scale = (s.data_ptr() for s in scales)
     io.workspace = ws.data_ptr()
     io.workspace_bytes = ws.numel()
-    st = stream if stream is not None else torch.cuda.current_stream(q.device)
     io.stream = st.cuda_stream
     io.total_q = Nq
     io.total_kv = Nk
     io.rms_eps = rms_eps
+    io.max_workgroups = max_workgroups
+    if status is not None:
+        io.status = status.data_ptr()
     if events is not None:
         io.ev_start, io.ev_stop = events   # raw hipEvent_t handles (ints)
-    status = _lib.jagged_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), q_offsets.data_ptr(),
-                                  kv_offsets.data_ptr(), B, H, D, v_id, a_id, window, out.data_ptr(), io)
-    if status != _lib.JA_OK:
-        raise _lib.JaggedAttnError(status, "jagged_attn_fwd")
+    rc = _lib.jagged_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), q_offsets.data_ptr(),
+                              kv_offsets.data_ptr(), B, H, D, v_id, a_id, window, out.data_ptr(), io)
+    if rc != _lib.JA_OK:
+        raise _lib.JaggedAttnError(rc, "jagged_attn_fwd")
     if check:
-        status = _lib.jagged_attn_check(ws.data_ptr(), st.cuda_stream)
-        if status != _lib.JA_OK:
-            raise _lib.JaggedAttnError(status, "jagged_attn_check")
+        rc = _lib.jagged_attn_check(ws.data_ptr(), st.cuda_stream)
+        if rc != _lib.JA_OK:
+            raise _lib.JaggedAttnError(rc, "jagged_attn_check")
     return out
 
 
@@ -110,9 +130,10 @@ def mx_quantize(x: torch.Tensor, stream: Optional[torch.cuda.Stream] = None):
     if D % 32 or D == 0:
         raise ValueError("the last dimension must be a positive multiple of 32")
     rows = x.numel() // D
-    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
-    scales = torch.empty(tuple(x.shape[:-1]) + (D // 32,), dtype=torch.uint8, device=x.device)
     st = stream if stream is not None else torch.cuda.current_stream(x.device)
+    with torch.cuda.stream(st):
+        codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+        scales = torch.empty(tuple(x.shape[:-1]) + (D // 32,), dtype=torch.uint8, device=x.device)
     dtype = _lib.JA_F32 if x.dtype == torch.float32 else _lib.JA_BF16
     status = _lib.jagged_attn_mx_quantize(x.data_ptr(), dtype, rows, D, codes.data_ptr(), scales.data_ptr(),
                                           st.cuda_stream)
@@ -125,10 +146,10 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tens
              q_offsets: torch.Tensor, kv_offsets: torch.Tensor,
              variant: str = "self", act: str = "softmax", window: int = 0, dtype: str = "bf16",
              workspace: Optional[Workspace] = None, rms_eps: float = 1e-6,
-             stream: Optional[torch.cuda.Stream] = None, check: bool = False, events=None):
+             stream: Optional[torch.cuda.Stream] = None, check: Optional[bool] = None, events=None):
     """Gradients of the forward (act "softmax" or "gelu_tanh"): returns float32
     (dq, dk, dv) shaped like q, k, v.  q/k/v/dout are "f32" or "bf16" tensors
-    laid out as for ``forward``."""
+    laid out as for ``forward``; ``stream`` and ``check`` as for ``forward``."""
     if dtype not in ("f32", "bf16"):
         raise ValueError("backward takes f32 or bf16 inputs")
     want = _IN_DTYPES[dtype]
@@ -142,28 +163,31 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tens
     B = q_offsets.numel() - 1
     v_id, a_id, d_id = _lib.VARIANTS[variant], _lib.ACTS[act], _lib.DTYPES[dtype]
     nbytes = _lib.jagged_attn_bwd_workspace_size(B, H, D, v_id, a_id, window, d_id, Nq, Nk) or 256
-    ws = (workspace or Workspace(q.device)).get(nbytes)
-    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-    dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
-    dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    if check is None:
+        check = workspace is None
+    with torch.cuda.stream(st):  # (temporaries on the launch stream, as in forward)
+        ws = (workspace or Workspace(q.device)).get(nbytes)
+        dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+        dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
     io = _lib.JaIo()
     io.dtype = d_id
     io.workspace = ws.data_ptr()
     io.workspace_bytes = ws.numel()
-    st = stream if stream is not None else torch.cuda.current_stream(q.device)
     io.stream = st.cuda_stream
     io.total_q = Nq
     io.total_kv = Nk
     io.rms_eps = rms_eps
     if events is not None:
         io.ev_start, io.ev_stop = events
-    status = _lib.jagged_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), q_offsets.data_ptr(),
-                                  kv_offsets.data_ptr(), B, H, D, v_id, a_id, window, dq.data_ptr(),
-                                  dk.data_ptr(), dv.data_ptr(), io)
-    if status != _lib.JA_OK:
-        raise _lib.JaggedAttnError(status, "jagged_attn_bwd")
+    rc = _lib.jagged_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), q_offsets.data_ptr(),
+                              kv_offsets.data_ptr(), B, H, D, v_id, a_id, window, dq.data_ptr(),
+                              dk.data_ptr(), dv.data_ptr(), io)
+    if rc != _lib.JA_OK:
+        raise _lib.JaggedAttnError(rc, "jagged_attn_bwd")
     if check:
-        status = _lib.jagged_attn_check(ws.data_ptr(), st.cuda_stream)
-        if status != _lib.JA_OK:
-            raise _lib.JaggedAttnError(status, "jagged_attn_check")
+        rc = _lib.jagged_attn_check(ws.data_ptr(), st.cuda_stream)
+        if rc != _lib.JA_OK:
+            raise _lib.JaggedAttnError(rc, "jagged_attn_check")
     return dq, dk, dv

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 
@@ -13,11 +14,12 @@
 namespace ja {
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st);
 hipError_t launch_attn_mfma(int D, int in, int shape, int act, const AttnArgs& a, int num_cu,
-                            int64_t max_items, hipStream_t st);
+                            int64_t max_items, int64_t grid_cap, const KTiming& tm, hipStream_t st);
 hipError_t launch_combine(int D, const CombineArgs& a, hipStream_t st);
-hipError_t launch_attn_f32(int D, int act, int window_mode, const AttnArgs& a, int grid, hipStream_t st);
+hipError_t launch_attn_f32(int D, int act, int window_mode, const AttnArgs& a, int grid, const KTiming& tm,
+                           hipStream_t st);
 hipError_t launch_attn_pp(int D, int act, bool cross, const AttnArgs& a, int num_cu, int64_t max_items,
-                          hipStream_t st);
+                          int64_t grid_cap, const KTiming& tm, hipStream_t st);
 hipError_t launch_attn_bwd(int D, bool bf16, int act, int wmode, const BwdArgs& a, int64_t rows_q, int64_t rows_k,
                            int grid_q, int grid_k, hipStream_t st);
 hipError_t launch_attn_bwd_mfma(int D, int act, int wmode, const BwdArgs& a, int grid_q, int grid_k,
@@ -46,17 +48,29 @@ struct Plan {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Compute units of the current device (cached per device id).
-int device_cus() {
-  static int cus[64] = {0};
+// Compute units of the current device.  Cached per device id for the first
+// kMaxCachedDevices ids (relaxed atomics: concurrent first calls on one device
+// may both query it and store the same value); other ids are queried each call.
+constexpr int kMaxCachedDevices = 64;
+hipError_t device_cus(int* cus) {
+  static std::atomic<int> cache[kMaxCachedDevices];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
-    cus[dev] = n;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxCachedDevices) {
+    const int n = cache[dev].load(std::memory_order_relaxed);
+    if (n > 0) {
+      *cus = n;
+      return hipSuccess;
+    }
   }
-  return cus[dev];
+  int n = 0;
+  e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (n < 1) return hipErrorInvalidDevice;
+  if (dev >= 0 && dev < kMaxCachedDevices) cache[dev].store(n, std::memory_order_relaxed);
+  *cus = n;
+  return hipSuccess;
 }
 
 // Key chunk for the key-split shape: about 2048 work items per call, a
@@ -138,6 +152,136 @@ Plan make_plan(int B, int H, int D, int variant, int act, int window, int dtype,
   return p;
 }
 
+}  // namespace
+
+// The forward on a given workspace (the caller's, or the library's own
+// scratch): validation, plan launch, attention launch [, split merge].
+int fwd_impl(const void* q, const void* k, const void* v, const int32_t* q_offsets, const int32_t* kv_offsets,
+             int B, int H, int D, int variant, int act, int window, void* out, const ja_io& io, void* workspace,
+             size_t workspace_bytes) {
+  const int st = validate(B, H, D, variant, act, window, io.dtype, io.total_q, io.total_kv);
+  if (st != JA_OK) return st;
+  if (!q_offsets || !kv_offsets) return JA_EINVAL;
+  if (io.max_workgroups < 0) return JA_EINVAL;
+  // Empty tensors may come with null data pointers: no kernel reads q or
+  // writes out without query rows, nor reads k or v without key rows.
+  const bool has_q = io.total_q > 0, has_kv = io.total_kv > 0;
+  if ((has_q && (!q || !out)) || (has_kv && (!k || !v))) return JA_EINVAL;
+  if (io.dtype == JA_MXFP8_E4M3 && ((has_q && !io.q_scale) || (has_kv && (!io.k_scale || !io.v_scale))))
+    return JA_EINVAL;
+  const Plan p = make_plan(B, H, D, variant, act, window, io.dtype, io.total_q, io.total_kv);
+  if (workspace == nullptr || workspace_bytes < p.ws.total) return JA_EWORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v) |
+       reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(workspace)) & 15)
+    return JA_EINVAL;
+  if (reinterpret_cast<uintptr_t>(io.status) & 3) return JA_EINVAL;
+  int num_cu = 0;
+  if (device_cus(&num_cu) != hipSuccess) return JA_EHIP;
+
+  hipStream_t stream = reinterpret_cast<hipStream_t>(io.stream);
+  unsigned char* ws = reinterpret_cast<unsigned char*>(workspace);
+  WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
+  int32_t* nsplit = reinterpret_cast<int32_t*>(ws + p.ws.nsplit_off);
+  int32_t* pbase = reinterpret_cast<int32_t*>(ws + p.ws.pbase_off);
+  WorkItem* items = reinterpret_cast<WorkItem*>(ws + p.ws.items_off);
+  float* part_o = reinterpret_cast<float*>(ws + p.ws.part_o_off);
+  float2* part_ml = reinterpret_cast<float2*>(ws + p.ws.part_ml_off);
+
+  PlanArgs pa{};
+  pa.qo = q_offsets;
+  pa.ko = kv_offsets;
+  pa.B = B;
+  pa.H = H;
+  pa.total_q = io.total_q;
+  pa.total_kv = io.total_kv;
+  pa.bm = p.bm;
+  pa.kvc = p.kvc;
+  pa.self_check = variant == JA_SELF || variant == JA_SLIDING;
+  pa.window_blocks = variant == JA_SLIDING ? 0 : window / kBlock;
+  pa.window_tokens = variant == JA_SLIDING ? window : 0;
+  pa.cost_order = p.shape == kShapePingPong || p.shape == kShapeKvSplit || p.shape == kShapeWindow;
+  pa.max_items = p.ws.max_items;
+  pa.max_slots = p.ws.max_slots;
+  pa.hdr = hdr;
+  pa.status_out = io.status;
+  pa.nsplit = nsplit;
+  pa.pbase = pbase;
+  pa.items = items;
+  const float rms_eps = io.rms_eps > 0.f ? io.rms_eps : 1e-6f;
+  float* ksc = nullptr;
+  if (p.shape == kShapePingPong && act != JA_SOFTMAX) {
+    // the key RMS factors are computed by extra workgroups of the plan launch
+    ksc = reinterpret_cast<float*>(ws + p.ws.kscale_off);
+    pa.krms_k = k;
+    pa.krms_rows = int64_t(io.total_kv) * H;
+    pa.krms_d = D;
+    pa.krms_eps = rms_eps;
+    pa.krms_out = ksc;
+  }
+  if (launch_plan(pa, stream) != hipSuccess) return JA_EHIP;
+
+  AttnArgs aa{};
+  aa.q = q;
+  aa.k = k;
+  aa.v = v;
+  aa.qs = io.q_scale;
+  aa.ks = io.k_scale;
+  aa.vs = io.v_scale;
+  aa.out = out;
+  aa.qo = q_offsets;
+  aa.ko = kv_offsets;
+  aa.hdr = hdr;
+  aa.items = items;
+  aa.nsplit = nsplit;
+  aa.pbase = pbase;
+  aa.part_o = part_o;
+  aa.part_ml = part_ml;
+  aa.H = H;
+  aa.window_blocks = variant == JA_SLIDING ? 0 : window / kBlock;
+  aa.window_tokens = variant == JA_SLIDING ? window : 0;
+  aa.kvc = p.kvc;
+  aa.dealt = p.shape == kShapeKvSplit || p.shape == kShapeWindow;
+  aa.eps = rms_eps;
+  aa.kscale = ksc;
+  const float inv_sqrt_d = 1.0f / std::sqrt(float(D));
+  aa.score_scale = act == JA_SOFTMAX ? inv_sqrt_d * 1.4426950408889634f : inv_sqrt_d;
+
+  // (the events are written by the attention kernel's own dispatch)
+  const KTiming tm{reinterpret_cast<hipEvent_t>(io.ev_start), reinterpret_cast<hipEvent_t>(io.ev_stop)};
+  const int64_t cap = io.max_workgroups;
+  hipError_t e;
+  if (p.shape == kShapeF32) {
+    // (a grid-stride loop over the items: capped like the persistent kernels)
+    int64_t grid = std::min<int64_t>(p.ws.max_items > 0 ? p.ws.max_items : 1, kMaxGrid);
+    if (cap > 0) grid = std::min(grid, std::max<int64_t>(kXcds, cap / kXcds * kXcds));
+    e = launch_attn_f32(D, act, variant == JA_SLIDING ? 2 : (window > 0 ? 1 : 0), aa, int(grid), tm, stream);
+  } else if (p.shape == kShapePingPong) {
+    e = launch_attn_pp(D, act, variant == JA_CROSS, aa, num_cu, p.ws.max_items, cap, tm, stream);
+  } else {
+    const int in = io.dtype == JA_BF16 ? IN_BF16 : IN_MX;
+    e = launch_attn_mfma(D, in, p.shape, act, aa, num_cu, p.ws.max_items, cap, tm, stream);
+  }
+  if (e != hipSuccess) return JA_EHIP;
+  if (p.shape == kShapeKvSplit) {
+    CombineArgs ca{};
+    ca.out = out;
+    ca.qo = q_offsets;
+    ca.ko = kv_offsets;
+    ca.hdr = hdr;
+    ca.nsplit = nsplit;
+    ca.pbase = pbase;
+    ca.part_o = part_o;
+    ca.part_ml = part_ml;
+    ca.B = B;
+    ca.H = H;
+    ca.act = act;
+    if (launch_combine(D, ca, stream) != hipSuccess) return JA_EHIP;
+  }
+  return JA_OK;
+}
+
+namespace {
+
 // Backward workspace: two plans of 64-row tiles (over the queries, and over
 // the keys with the offsets swapped) and one (lse, D) pair per query row and head.
 constexpr int kBwdRows = 64;        // rows per backward work item (VALU kernels, MFMA key side)
@@ -196,7 +340,7 @@ using namespace ja;
 
 extern "C" {
 
-int jagged_attn_version(void) { return 100; }
+int jagged_attn_version(void) { return 101; }
 
 const char* jagged_attn_strerror(int status) {
   switch (status) {
@@ -220,120 +364,8 @@ int jagged_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
                     const int32_t* kv_offsets, int B, int H, int D, int variant, int act, int window,
                     void* out, const ja_io* io) {
   if (io == nullptr) return JA_EINVAL;
-  const int st = validate(B, H, D, variant, act, window, io->dtype, io->total_q, io->total_kv);
-  if (st != JA_OK) return st;
-  if (!q_offsets || !kv_offsets) return JA_EINVAL;
-  // Empty tensors may come with null data pointers: no kernel reads q or
-  // writes out without query rows, nor reads k or v without key rows.
-  const bool has_q = io->total_q > 0, has_kv = io->total_kv > 0;
-  if ((has_q && (!q || !out)) || (has_kv && (!k || !v))) return JA_EINVAL;
-  if (io->dtype == JA_MXFP8_E4M3 && ((has_q && !io->q_scale) || (has_kv && (!io->k_scale || !io->v_scale))))
-    return JA_EINVAL;
-  const Plan p = make_plan(B, H, D, variant, act, window, io->dtype, io->total_q, io->total_kv);
-  if (io->workspace == nullptr || io->workspace_bytes < p.ws.total) return JA_EWORKSPACE;
-  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) | reinterpret_cast<uintptr_t>(v) |
-       reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(io->workspace)) & 15)
-    return JA_EINVAL;
-
-  hipStream_t stream = reinterpret_cast<hipStream_t>(io->stream);
-  unsigned char* ws = reinterpret_cast<unsigned char*>(io->workspace);
-  WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
-  int32_t* nsplit = reinterpret_cast<int32_t*>(ws + p.ws.nsplit_off);
-  int32_t* pbase = reinterpret_cast<int32_t*>(ws + p.ws.pbase_off);
-  WorkItem* items = reinterpret_cast<WorkItem*>(ws + p.ws.items_off);
-  float* part_o = reinterpret_cast<float*>(ws + p.ws.part_o_off);
-  float2* part_ml = reinterpret_cast<float2*>(ws + p.ws.part_ml_off);
-
-  PlanArgs pa{};
-  pa.qo = q_offsets;
-  pa.ko = kv_offsets;
-  pa.B = B;
-  pa.H = H;
-  pa.total_q = io->total_q;
-  pa.total_kv = io->total_kv;
-  pa.bm = p.bm;
-  pa.kvc = p.kvc;
-  pa.self_check = variant == JA_SELF || variant == JA_SLIDING;
-  pa.window_blocks = variant == JA_SLIDING ? 0 : window / kBlock;
-  pa.window_tokens = variant == JA_SLIDING ? window : 0;
-  pa.cost_order = p.shape == kShapePingPong || p.shape == kShapeKvSplit || p.shape == kShapeWindow;
-  pa.max_items = p.ws.max_items;
-  pa.max_slots = p.ws.max_slots;
-  pa.hdr = hdr;
-  pa.nsplit = nsplit;
-  pa.pbase = pbase;
-  pa.items = items;
-  const float rms_eps = io->rms_eps > 0.f ? io->rms_eps : 1e-6f;
-  float* ksc = nullptr;
-  if (p.shape == kShapePingPong && act != JA_SOFTMAX) {
-    // the key RMS factors are computed by extra workgroups of the plan launch
-    ksc = reinterpret_cast<float*>(ws + p.ws.kscale_off);
-    pa.krms_k = k;
-    pa.krms_rows = int64_t(io->total_kv) * H;
-    pa.krms_d = D;
-    pa.krms_eps = rms_eps;
-    pa.krms_out = ksc;
-  }
-  if (launch_plan(pa, stream) != hipSuccess) return JA_EHIP;
-
-  AttnArgs aa{};
-  aa.q = q;
-  aa.k = k;
-  aa.v = v;
-  aa.qs = io->q_scale;
-  aa.ks = io->k_scale;
-  aa.vs = io->v_scale;
-  aa.out = out;
-  aa.qo = q_offsets;
-  aa.ko = kv_offsets;
-  aa.hdr = hdr;
-  aa.items = items;
-  aa.nsplit = nsplit;
-  aa.pbase = pbase;
-  aa.part_o = part_o;
-  aa.part_ml = part_ml;
-  aa.H = H;
-  aa.window_blocks = variant == JA_SLIDING ? 0 : window / kBlock;
-  aa.window_tokens = variant == JA_SLIDING ? window : 0;
-  aa.kvc = p.kvc;
-  aa.dealt = p.shape == kShapeKvSplit || p.shape == kShapeWindow;
-  aa.eps = rms_eps;
-  aa.kscale = ksc;
-  const float inv_sqrt_d = 1.0f / std::sqrt(float(D));
-  aa.score_scale = act == JA_SOFTMAX ? inv_sqrt_d * 1.4426950408889634f : inv_sqrt_d;
-
-  const int grid = int(p.ws.max_items < kMaxGrid ? (p.ws.max_items > 0 ? p.ws.max_items : 1) : kMaxGrid);
-  if (io->ev_start && hipEventRecord(reinterpret_cast<hipEvent_t>(io->ev_start), stream) != hipSuccess)
-    return JA_EHIP;
-  hipError_t e;
-  if (p.shape == kShapeF32) {
-    e = launch_attn_f32(D, act, variant == JA_SLIDING ? 2 : (window > 0 ? 1 : 0), aa, grid, stream);
-  } else if (p.shape == kShapePingPong) {
-    e = launch_attn_pp(D, act, variant == JA_CROSS, aa, device_cus(), p.ws.max_items, stream);
-
-  } else {
-    const int in = io->dtype == JA_BF16 ? IN_BF16 : IN_MX;
-    e = launch_attn_mfma(D, in, p.shape, act, aa, device_cus(), p.ws.max_items, stream);
-  }
-  if (e != hipSuccess) return JA_EHIP;
-  if (io->ev_stop && hipEventRecord(reinterpret_cast<hipEvent_t>(io->ev_stop), stream) != hipSuccess)
-    return JA_EHIP;
-  if (p.shape == kShapeKvSplit) {
-    CombineArgs ca{};
-    ca.out = out;
-    ca.qo = q_offsets;
-    ca.ko = kv_offsets;
-    ca.hdr = hdr;
-    ca.nsplit = nsplit;
-    ca.pbase = pbase;
-    ca.part_o = part_o;
-    ca.part_ml = part_ml;
-    ca.B = B;
-    ca.H = H;
-    ca.act = act;
-    if (launch_combine(D, ca, stream) != hipSuccess) return JA_EHIP;
-  }
-  return JA_OK;
+  return fwd_impl(q, k, v, q_offsets, kv_offsets, B, H, D, variant, act, window, out, *io, io->workspace,
+                  io->workspace_bytes);
 }
 
 size_t jagged_attn_bwd_workspace_size(int B, int H, int D, int variant, int act, int window, int dtype,
@@ -354,6 +386,7 @@ int jagged_attn_bwd(const void* q, const void* k, const void* v, const void* dou
   for (const void* p : {q, k, v, dout, static_cast<const void*>(dq), static_cast<const void*>(dk),
                         static_cast<const void*>(dv), static_cast<const void*>(io->workspace)})
     if (!aligned16(p)) return JA_EINVAL;
+  if (reinterpret_cast<uintptr_t>(io->status) & 3) return JA_EINVAL;
 
   hipStream_t stream = reinterpret_cast<hipStream_t>(io->stream);
   unsigned char* ws = reinterpret_cast<unsigned char*>(io->workspace);
@@ -375,6 +408,7 @@ int jagged_attn_bwd(const void* q, const void* k, const void* v, const void* dou
     pa.max_items = pass == 0 ? L.max_q : L.max_k;
     pa.max_slots = 0;
     pa.hdr = reinterpret_cast<WsHeader*>(ws + (pass == 0 ? L.hdr_q : L.hdr_k));
+    pa.status_out = io->status;  // (both plans check the same offsets)
     pa.nsplit = reinterpret_cast<int32_t*>(ws + (pass == 0 ? L.nsplit_q : L.nsplit_k));
     pa.pbase = reinterpret_cast<int32_t*>(ws + (pass == 0 ? L.pbase_q : L.pbase_k));
     pa.items = reinterpret_cast<WorkItem*>(ws + (pass == 0 ? L.items_q : L.items_k));

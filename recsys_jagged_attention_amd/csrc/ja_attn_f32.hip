@@ -103,26 +103,23 @@ __global__ __launch_bounds__(kF32Rows) void attn_f32_kernel(AttnArgs a) {
 }
 
 template <int D>
-hipError_t launch_d(int act, int window_mode, const AttnArgs& a, int grid, hipStream_t st) {
-  if (act == ACT_GELU)
-    hipLaunchKernelGGL((attn_f32_kernel<D, ACT_GELU, 0>), dim3(grid), dim3(kF32Rows), 0, st, a);
-  else if (act == ACT_GELU_POLY)
-    hipLaunchKernelGGL((attn_f32_kernel<D, ACT_GELU_POLY, 0>), dim3(grid), dim3(kF32Rows), 0, st, a);
-  else if (window_mode == 1)
-    hipLaunchKernelGGL((attn_f32_kernel<D, ACT_SOFTMAX, 1>), dim3(grid), dim3(kF32Rows), 0, st, a);
-  else if (window_mode == 2)
-    hipLaunchKernelGGL((attn_f32_kernel<D, ACT_SOFTMAX, 2>), dim3(grid), dim3(kF32Rows), 0, st, a);
-  else
-    hipLaunchKernelGGL((attn_f32_kernel<D, ACT_SOFTMAX, 0>), dim3(grid), dim3(kF32Rows), 0, st, a);
-  return hipGetLastError();
+hipError_t launch_d(int act, int window_mode, const AttnArgs& a, int grid, const KTiming& tm, hipStream_t st) {
+  const dim3 gd(grid), bd(kF32Rows);
+  if (act == ACT_GELU) return launch1(attn_f32_kernel<D, ACT_GELU, 0>, gd, bd, st, a, tm);
+  if (act == ACT_GELU_POLY) return launch1(attn_f32_kernel<D, ACT_GELU_POLY, 0>, gd, bd, st, a, tm);
+  if (window_mode == 1) return launch1(attn_f32_kernel<D, ACT_SOFTMAX, 1>, gd, bd, st, a, tm);
+  if (window_mode == 2) return launch1(attn_f32_kernel<D, ACT_SOFTMAX, 2>, gd, bd, st, a, tm);
+  return launch1(attn_f32_kernel<D, ACT_SOFTMAX, 0>, gd, bd, st, a, tm);
 }
 
 }  // namespace
 
-hipError_t launch_attn_f32(int D, int act, int window_mode, const AttnArgs& a, int grid, hipStream_t st) {
-  if (D == 32) return launch_d<32>(act, window_mode, a, grid, st);
-  if (D == 64) return launch_d<64>(act, window_mode, a, grid, st);
-  return launch_d<128>(act, window_mode, a, grid, st);
+// grid: workgroups of the grid-stride loop over the work items.
+hipError_t launch_attn_f32(int D, int act, int window_mode, const AttnArgs& a, int grid, const KTiming& tm,
+                           hipStream_t st) {
+  if (D == 32) return launch_d<32>(act, window_mode, a, grid, tm, st);
+  if (D == 64) return launch_d<64>(act, window_mode, a, grid, tm, st);
+  return launch_d<128>(act, window_mode, a, grid, tm, st);
 }
 
 }  // namespace ja

@@ -40,6 +40,7 @@
 // activation input, no correction stage); the block window needs no element
 // mask because 64-key tiles coincide with the 64-token blocks (same page,
 // "BlockAttention"); only a sample's ragged last tile is masked.
+#include <atomic>
 #include <type_traits>
 
 #include "ja_device.h"
@@ -840,50 +841,48 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   }
 }
 
-// Workgroups resident per CU for one kernel instance (queried once).
+// Workgroups resident per CU for one kernel instance (queried once; concurrent
+// first calls may both query, and store the same value).
 template <int D, int NWQ, int NWK, int QSUB, int ACT, int IN, bool WINDOW, bool SPLIT>
 int resident_per_cu() {
-  static int cached = 0;
-  if (cached == 0) {
-    int n = 0;
+  static std::atomic<int> cached{0};
+  int n = cached.load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
             &n, attn_kernel<D, NWQ, NWK, QSUB, ACT, IN, WINDOW, SPLIT>, 64 * NWQ * NWK, 0) != hipSuccess ||
         n < 1)
       n = 1;
-    cached = n;
+    cached.store(n, std::memory_order_relaxed);
   }
-  return cached;
+  return n;
 }
 
 template <int D, int NWQ, int NWK, int QSUB, int ACT, int IN, bool WINDOW, bool SPLIT>
-hipError_t launch(const AttnArgs& a, int num_cu, int64_t max_items, hipStream_t st) {
+hipError_t launch(const AttnArgs& a, int num_cu, int64_t max_items, int64_t grid_cap, const KTiming& tm,
+                  hipStream_t st) {
   // Persistent grid: each resident slot once, a multiple of the XCD count.
-  int64_t grid = int64_t(num_cu) * resident_per_cu<D, NWQ, NWK, QSUB, ACT, IN, WINDOW, SPLIT>();
-  const int64_t need = ((max_items + kXcds - 1) / kXcds) * kXcds;
-  if (grid > need) grid = need;
-  grid = (grid / kXcds) * kXcds;
-  if (grid < kXcds) grid = kXcds;
-  hipLaunchKernelGGL((attn_kernel<D, NWQ, NWK, QSUB, ACT, IN, WINDOW, SPLIT>), dim3(unsigned(grid)),
-                     dim3(64 * NWQ * NWK), 0, st, a);
-  return hipGetLastError();
+  const int64_t slots = int64_t(num_cu) * resident_per_cu<D, NWQ, NWK, QSUB, ACT, IN, WINDOW, SPLIT>();
+  const int64_t grid = persistent_grid(slots, max_items, grid_cap);
+  return launch1(attn_kernel<D, NWQ, NWK, QSUB, ACT, IN, WINDOW, SPLIT>, dim3(unsigned(grid)), dim3(64 * NWQ * NWK),
+                 st, a, tm);
 }
 
 template <int D, int IN>
-hipError_t launch_for_shape(int shape, int act, const AttnArgs& a, int num_cu, int64_t max_items,
-                            hipStream_t st) {
+hipError_t launch_for_shape(int shape, int act, const AttnArgs& a, int num_cu, int64_t max_items, int64_t cap,
+                            const KTiming& tm, hipStream_t st) {
   switch (shape) {
     case 0:  // query-tiled (self full, cross): 4 waves x 32 rows
-      if (act == ACT_SOFTMAX) return launch<D, 4, 1, 1, ACT_SOFTMAX, IN, false, false>(a, num_cu, max_items, st);
-      if (act == ACT_GELU_POLY) return launch<D, 4, 1, 1, ACT_GELU_POLY, IN, false, false>(a, num_cu, max_items, st);
-      return launch<D, 4, 1, 1, ACT_GELU, IN, false, false>(a, num_cu, max_items, st);
+      if (act == ACT_SOFTMAX) return launch<D, 4, 1, 1, ACT_SOFTMAX, IN, false, false>(a, num_cu, max_items, cap, tm, st);
+      if (act == ACT_GELU_POLY) return launch<D, 4, 1, 1, ACT_GELU_POLY, IN, false, false>(a, num_cu, max_items, cap, tm, st);
+      return launch<D, 4, 1, 1, ACT_GELU, IN, false, false>(a, num_cu, max_items, cap, tm, st);
     case 1:  // block window (softmax only): 4 waves x 32 rows on two 64-token query blocks
-      return launch<D, 4, 1, 1, ACT_SOFTMAX, IN, true, false>(a, num_cu, max_items, st);
+      return launch<D, 4, 1, 1, ACT_SOFTMAX, IN, true, false>(a, num_cu, max_items, cap, tm, st);
     case 3:  // full self-attention: 8 waves x 32 rows share every key tile
-      return launch<D, 8, 1, 1, ACT_SOFTMAX, IN, false, false>(a, num_cu, max_items, st);
+      return launch<D, 8, 1, 1, ACT_SOFTMAX, IN, false, false>(a, num_cu, max_items, cap, tm, st);
     default:  // key-split (PMA): 1 query group of 32 rows x 4 key groups
-      if (act == ACT_SOFTMAX) return launch<D, 1, 4, 1, ACT_SOFTMAX, IN, false, true>(a, num_cu, max_items, st);
-      if (act == ACT_GELU_POLY) return launch<D, 1, 4, 1, ACT_GELU_POLY, IN, false, true>(a, num_cu, max_items, st);
-      return launch<D, 1, 4, 1, ACT_GELU, IN, false, true>(a, num_cu, max_items, st);
+      if (act == ACT_SOFTMAX) return launch<D, 1, 4, 1, ACT_SOFTMAX, IN, false, true>(a, num_cu, max_items, cap, tm, st);
+      if (act == ACT_GELU_POLY) return launch<D, 1, 4, 1, ACT_GELU_POLY, IN, false, true>(a, num_cu, max_items, cap, tm, st);
+      return launch<D, 1, 4, 1, ACT_GELU, IN, false, true>(a, num_cu, max_items, cap, tm, st);
   }
 }
 
@@ -891,15 +890,15 @@ hipError_t launch_for_shape(int shape, int act, const AttnArgs& a, int num_cu, i
 
 // shape: 0 = query-tiled, 1 = block window, 2 = key-split, 3 = full self-attention.
 hipError_t launch_attn_mfma(int D, int in, int shape, int act, const AttnArgs& a, int num_cu,
-                            int64_t max_items, hipStream_t st) {
+                            int64_t max_items, int64_t grid_cap, const KTiming& tm, hipStream_t st) {
   if (in == IN_BF16) {
-    if (D == 32) return launch_for_shape<32, IN_BF16>(shape, act, a, num_cu, max_items, st);
-    if (D == 64) return launch_for_shape<64, IN_BF16>(shape, act, a, num_cu, max_items, st);
-    return launch_for_shape<128, IN_BF16>(shape, act, a, num_cu, max_items, st);
+    if (D == 32) return launch_for_shape<32, IN_BF16>(shape, act, a, num_cu, max_items, grid_cap, tm, st);
+    if (D == 64) return launch_for_shape<64, IN_BF16>(shape, act, a, num_cu, max_items, grid_cap, tm, st);
+    return launch_for_shape<128, IN_BF16>(shape, act, a, num_cu, max_items, grid_cap, tm, st);
   }
-  if (D == 32) return launch_for_shape<32, IN_MX>(shape, act, a, num_cu, max_items, st);
-  if (D == 64) return launch_for_shape<64, IN_MX>(shape, act, a, num_cu, max_items, st);
-  return launch_for_shape<128, IN_MX8>(shape, act, a, num_cu, max_items, st);
+  if (D == 32) return launch_for_shape<32, IN_MX>(shape, act, a, num_cu, max_items, grid_cap, tm, st);
+  if (D == 64) return launch_for_shape<64, IN_MX>(shape, act, a, num_cu, max_items, grid_cap, tm, st);
+  return launch_for_shape<128, IN_MX8>(shape, act, a, num_cu, max_items, grid_cap, tm, st);
 }
 
 hipError_t launch_combine(int D, const CombineArgs& a, hipStream_t st) {

@@ -739,9 +739,22 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
 }  // namespace
 
 template <int D, int ACT>
-void launch_none(bool cross, dim3 gd, dim3 bd, hipStream_t st, const AttnArgs& a) {
-  if (cross) hipLaunchKernelGGL((attn_pp_kernel<D, ACT, kWinNone, true>), gd, bd, 0, st, a);
-  else hipLaunchKernelGGL((attn_pp_kernel<D, ACT, kWinNone, false>), gd, bd, 0, st, a);
+hipError_t launch_none(bool cross, dim3 gd, dim3 bd, hipStream_t st, const AttnArgs& a, const KTiming& tm) {
+  if (cross) return launch1(attn_pp_kernel<D, ACT, kWinNone, true>, gd, bd, st, a, tm);
+  return launch1(attn_pp_kernel<D, ACT, kWinNone, false>, gd, bd, st, a, tm);
+}
+
+template <int D>
+hipError_t launch_d(int act, bool cross, dim3 gd, dim3 bd, hipStream_t st, const AttnArgs& a, const KTiming& tm) {
+  if (a.window_tokens > 0)  // (softmax only)
+    return launch1(attn_pp_kernel<D, ACT_SOFTMAX, kWinSliding, false>, gd, bd, st, a, tm);
+  if (a.window_blocks > 0 && a.window_blocks <= kPipePairs)  // (softmax only)
+    return launch1(attn_pp_kernel<D, ACT_SOFTMAX, kWinPipe, false>, gd, bd, st, a, tm);
+  if (a.window_blocks > 0)  // (softmax only)
+    return launch1(attn_pp_kernel<D, ACT_SOFTMAX, kWinBlock, false>, gd, bd, st, a, tm);
+  if (act == ACT_SOFTMAX) return launch_none<D, ACT_SOFTMAX>(cross, gd, bd, st, a, tm);
+  if (act == ACT_GELU_POLY) return launch_none<D, ACT_GELU_POLY>(cross, gd, bd, st, a, tm);
+  return launch_none<D, ACT_GELU>(cross, gd, bd, st, a, tm);
 }
 
 int pp_rows() { return kPPRows; }
@@ -749,40 +762,12 @@ int pp_pipe_rows() { return kBlock * kPipeBlocks; }
 int pp_pipe_max_blocks() { return kPipePairs; }
 
 hipError_t launch_attn_pp(int D, int act, bool cross, const AttnArgs& a, int num_cu, int64_t max_items,
-                          hipStream_t st) {
+                          int64_t grid_cap, const KTiming& tm, hipStream_t st) {
   // One workgroup per CU (the tile ring takes most of the LDS), a multiple of the XCD count.
-  int64_t grid = num_cu;
-  const int64_t need = ((max_items + kXcds - 1) / kXcds) * kXcds;
-  if (grid > need) grid = need;
-  grid = (grid / kXcds) * kXcds;
-  if (grid < kXcds) grid = kXcds;
-  const dim3 gd(static_cast<unsigned>(grid)), bd(64 * kPPWaves);
-  if (a.window_tokens > 0) {  // (softmax only)
-    if (D == 32) hipLaunchKernelGGL((attn_pp_kernel<32, ACT_SOFTMAX, kWinSliding, false>), gd, bd, 0, st, a);
-    else if (D == 64) hipLaunchKernelGGL((attn_pp_kernel<64, ACT_SOFTMAX, kWinSliding, false>), gd, bd, 0, st, a);
-    else hipLaunchKernelGGL((attn_pp_kernel<128, ACT_SOFTMAX, kWinSliding, false>), gd, bd, 0, st, a);
-  } else if (a.window_blocks > 0 && a.window_blocks <= kPipePairs) {  // (softmax only)
-    if (D == 32) hipLaunchKernelGGL((attn_pp_kernel<32, ACT_SOFTMAX, kWinPipe, false>), gd, bd, 0, st, a);
-    else if (D == 64) hipLaunchKernelGGL((attn_pp_kernel<64, ACT_SOFTMAX, kWinPipe, false>), gd, bd, 0, st, a);
-    else hipLaunchKernelGGL((attn_pp_kernel<128, ACT_SOFTMAX, kWinPipe, false>), gd, bd, 0, st, a);
-  } else if (a.window_blocks > 0) {  // (softmax only)
-    if (D == 32) hipLaunchKernelGGL((attn_pp_kernel<32, ACT_SOFTMAX, kWinBlock, false>), gd, bd, 0, st, a);
-    else if (D == 64) hipLaunchKernelGGL((attn_pp_kernel<64, ACT_SOFTMAX, kWinBlock, false>), gd, bd, 0, st, a);
-    else hipLaunchKernelGGL((attn_pp_kernel<128, ACT_SOFTMAX, kWinBlock, false>), gd, bd, 0, st, a);
-  } else if (act == ACT_SOFTMAX) {
-    if (D == 32) launch_none<32, ACT_SOFTMAX>(cross, gd, bd, st, a);
-    else if (D == 64) launch_none<64, ACT_SOFTMAX>(cross, gd, bd, st, a);
-    else launch_none<128, ACT_SOFTMAX>(cross, gd, bd, st, a);
-  } else if (act == ACT_GELU_POLY) {
-    if (D == 32) launch_none<32, ACT_GELU_POLY>(cross, gd, bd, st, a);
-    else if (D == 64) launch_none<64, ACT_GELU_POLY>(cross, gd, bd, st, a);
-    else launch_none<128, ACT_GELU_POLY>(cross, gd, bd, st, a);
-  } else {
-    if (D == 32) launch_none<32, ACT_GELU>(cross, gd, bd, st, a);
-    else if (D == 64) launch_none<64, ACT_GELU>(cross, gd, bd, st, a);
-    else launch_none<128, ACT_GELU>(cross, gd, bd, st, a);
-  }
-  return hipGetLastError();
+  const dim3 gd(static_cast<unsigned>(persistent_grid(num_cu, max_items, grid_cap))), bd(64 * kPPWaves);
+  if (D == 32) return launch_d<32>(act, cross, gd, bd, st, a, tm);
+  if (D == 64) return launch_d<64>(act, cross, gd, bd, st, a, tm);
+  return launch_d<128>(act, cross, gd, bd, st, a, tm);
 }
 
 }  // namespace ja

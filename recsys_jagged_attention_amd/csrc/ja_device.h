@@ -1,6 +1,8 @@
 // Device helpers for the gfx950 (CDNA4) jagged attention kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
+
 #include "ja_gelu_poly.h"
 #include "ja_internal.h"
 
@@ -54,6 +56,18 @@ __device__ __forceinline__ bf16x8 decode_mx8(u32x2 codes, unsigned scale_byte) {
     r[j] = (__bf16)(v * s);
   }
   return r;
+}
+
+// Launch a kernel of one by-value argument on `st`; with events in `tm` the
+// dispatch itself records its start and end time into them (no separate
+// event packets around the launch).
+template <typename A>
+inline hipError_t launch1(void (*kernel)(A), dim3 grid, dim3 block, hipStream_t st, const A& arg,
+                          const KTiming& tm) {
+  void* args[] = {const_cast<A*>(&arg)};
+  if (tm.start || tm.stop)
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, 0, st, tm.start, tm.stop, 0);
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, 0, st);
 }
 
 // gelu_tanh(x) = x * sigmoid(2u), u = sqrt(2/pi) (x + 0.044715 x^3):

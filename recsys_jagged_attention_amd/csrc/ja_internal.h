@@ -35,7 +35,7 @@ struct WsHeader {
   int32_t status;              // JA_OK or JA_EOFFSETS, written by the plan kernel
   int32_t n_items;             // work items for the attention kernel
   int32_t n_slots;             // partial slots in use
-  int32_t pad0;
+  int32_t items_off;           // byte offset of the item list from the header (read back by tests)
   int32_t xcd_begin[kXcds + 1];  // items [xcd_begin[x], xcd_begin[x+1]) run on XCD x
                                  // (sample order; not used with cost order)
   int32_t pad[64 - 4 - (kXcds + 1)];
@@ -74,6 +74,7 @@ struct PlanArgs {
   int cost_order;      // 1: items sorted by key tiles, most first (xcd_begin unused)
   int64_t max_items, max_slots;
   WsHeader* hdr;
+  int32_t* status_out;  // optional copy of the status word (caller's device memory), or null
   int32_t* nsplit;
   int32_t* pbase;
   WorkItem* items;
@@ -112,6 +113,25 @@ struct AttnArgs {
   float score_scale;  // softmax: log2(e)/sqrt(D); GELU: 1/sqrt(D)
   float eps;
 };
+
+// Events that time one kernel from its own dispatch packet (hipExtLaunchKernel
+// writes the dispatch's start and end timestamps into them; null: untimed).
+struct KTiming {
+  hipEvent_t start;
+  hipEvent_t stop;
+};
+
+// Launch geometry shared by the persistent kernels: at most `cap` workgroups
+// (0: no cap), a multiple of the XCD count and at least one per XCD.
+inline int64_t persistent_grid(int64_t slots, int64_t max_items, int64_t cap) {
+  int64_t grid = slots;
+  const int64_t need = ((max_items + kXcds - 1) / kXcds) * kXcds;
+  if (grid > need) grid = need;
+  if (cap > 0 && grid > cap) grid = cap;
+  grid = (grid / kXcds) * kXcds;
+  if (grid < kXcds) grid = kXcds;
+  return grid;
+}
 
 struct BwdArgs {
   const void* q;

@@ -150,8 +150,16 @@ __device__ inline SampleWork sample_work(const PlanArgs& a, int lq, int lk) {
   return w;
 }
 
-__device__ inline void fail(const PlanArgs& a, int status) {
+// The header's item-list offset and status word (also copied to the caller's
+// status word when one is given).
+__device__ inline void set_status(const PlanArgs& a, int status) {
+  a.hdr->items_off = int32_t(reinterpret_cast<const char*>(a.items) - reinterpret_cast<const char*>(a.hdr));
   a.hdr->status = status;
+  if (a.status_out) *a.status_out = status;
+}
+
+__device__ inline void fail(const PlanArgs& a, int status) {
+  set_status(a, status);
   a.hdr->n_items = 0;
   a.hdr->n_slots = 0;
   for (int x = 0; x <= kXcds; ++x) a.hdr->xcd_begin[x] = 0;
@@ -340,7 +348,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     __syncthreads();
   }
   if (tid == 0) {
-    a.hdr->status = JA_OK;
+    set_status(a, JA_OK);
     a.hdr->n_items = item_carry;
     a.hdr->n_slots = slot_carry;
     a.hdr->xcd_begin[0] = 0;

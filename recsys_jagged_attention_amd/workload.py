@@ -50,3 +50,17 @@ def compulsory_bytes(total_q: int, total_kv: int, H: int, D: int, in_bytes: floa
     if mx_scales:
         b += (elems_q + 2 * elems_kv) // 32
     return int(b)
+
+
+def padded_dense_flops(lq, lk, H: int, D: int, window: int = 0) -> int:
+    """FLOPs of the same attention on a batch padded to the longest sample
+    (every sample Lq_max query rows; each row Lk_max keys, or the window's
+    keys when there is a window): what a padded dense kernel would spend."""
+    lq = np.asarray(lq, dtype=np.int64)
+    lk = np.asarray(lk, dtype=np.int64)
+    if lq.size == 0:
+        return 0
+    keys = int(lk.max())
+    if window > 0:
+        keys = min(keys, int(window))
+    return int(4 * D * H * lq.size * int(lq.max()) * keys)

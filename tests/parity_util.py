@@ -51,8 +51,8 @@ def rel_err(got, ref):
     return float(np.abs(got - ref).max() / scale)
 
 
-def full_parity(w):
-    got = run_gpu(w)
+def full_parity(w, **kw):
+    got = run_gpu(w, **kw)
     q, k, v = oracle_values(w)
     ref = oracle.gdpa_forward(q, k, v, w.q_offsets, w.kv_offsets, w.variant, oracle_act(w.act), w.window)
     assert np.all(np.isfinite(got))

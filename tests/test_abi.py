@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     lib = _lib.load()
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert _lib.jagged_attn_version() == 100
+    assert _lib.jagged_attn_version() == 101
 
 
 def test_strerror_covers_all_codes():

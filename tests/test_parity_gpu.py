@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import oracle
-from recsys_jagged_attention_amd import forward, JaggedAttnError, JA_EOFFSETS
+from recsys_jagged_attention_amd import forward, JaggedAttnError, JA_EOFFSETS, Workspace
 from recsys_jagged_attention_amd.inputs import (Workload, make_workload, random_jagged,
                                                 device_tensors, mx_encode_e4m3)
 from parity_util import TOL, full_parity, run_gpu, sampled_parity, rel_err, oracle_values
@@ -42,14 +42,25 @@ def test_workload_small_full_parity(name, scale):
     log(f"  rel err {err:.3e}")
 
 
-@pytest.mark.parametrize("name", ["block_window", "cross_gelu", "pma", "mxfp8_window", "full_self",
-                                  "sliding_window"])
-def test_workload_full_size_sampled(name):
+@pytest.mark.parametrize("name", ["block_window", "full_self", "cross_gelu", "pma", "mxfp8_window",
+                                  "sliding_window", "tiny_full"])
+def test_workload_full_size_every_element(name):
+    """Every workload at its full size, in the launch configuration the
+    benchmark times, compared element by element with the whole-batch oracle."""
     w = make_workload(name)
     log(f"full-size {name} B={w.B} Nq={w.total_q} Nk={w.total_kv}")
-    out = run_gpu(w)
-    err = sampled_parity(w, out)
-    log(f"  sampled rel err {err:.3e}")
+    err = full_parity(w)
+    log(f"  rel err {err:.3e}")
+
+
+@pytest.mark.parametrize("window", [64, 128, 512])
+def test_mxfp8_full_size_other_windows(window):
+    """The MXFP8 workload's tensors under block windows of 1, 2 and 8 blocks
+    (the workload itself uses 4), every element against the oracle."""
+    w = dataclasses.replace(make_workload("mxfp8_window"), window=window)
+    log(f"mxfp8 full size W={window}")
+    err = full_parity(w)
+    log(f"  rel err {err:.3e}")
 
 
 EDGE_LENGTHS = [0, 1, 31, 32, 33, 63, 64, 65, 127, 128, 129, 200]
@@ -360,6 +371,16 @@ def test_bad_offsets_reported_by_device():
         with pytest.raises(JaggedAttnError) as e:
             forward(q, k, v, a.cuda(), b.cuda(), variant="cross", act="softmax", check=True)
         assert e.value.status == JA_EOFFSETS
+        # the same status through the caller's status word, without jagged_attn_check
+        st = torch.full((1,), 12345, dtype=torch.int32, device="cuda")
+        forward(q, k, v, a.cuda(), b.cuda(), variant="cross", act="softmax", workspace=Workspace("cuda"),
+                check=False, status=st)
+        torch.cuda.synchronize()
+        assert int(st.item()) == JA_EOFFSETS
+    st = torch.full((1,), 12345, dtype=torch.int32, device="cuda")
+    forward(q, k, v, qo, ko, variant="cross", act="softmax", workspace=Workspace("cuda"), check=False, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
     # self-attention with different query/key offsets
     with pytest.raises(JaggedAttnError) as e:
         forward(q[:11], q[:11], q[:11], torch.tensor([0, 5, 11], dtype=torch.int32, device="cuda"),
@@ -367,3 +388,19 @@ def test_bad_offsets_reported_by_device():
     assert e.value.status == JA_EOFFSETS
     # valid offsets after an error: the status is reset and results are right
     full_parity(w)
+
+
+def test_non_current_stream_without_workspace():
+    """A call on a stream other than the current one, with no workspace given:
+    the temporary workspace and output belong to that stream, so the result
+    is right when read after that stream is synchronised."""
+    w = adhoc("side_stream", "cross", "gelu_tanh", "bf16", [300, 5, 1000], [64, 17, 33], 4, 128, seed=21)
+    q, k, v, qo, ko, _ = device_tensors(w, "cuda")
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    outs = [forward(q, k, v, qo, ko, variant="cross", act="gelu_tanh", stream=side, check=False) for _ in range(4)]
+    side.synchronize()
+    qq, kk, vv = oracle_values(w)
+    ref = oracle.gdpa_forward(qq, kk, vv, w.q_offsets, w.kv_offsets, "cross", "gelu_tanh", 0)
+    for o in outs:
+        assert rel_err(o.float().cpu().numpy().astype(np.float64), ref) <= TOL["bf16"]
