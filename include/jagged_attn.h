@@ -136,6 +136,25 @@ int jagged_attn_fwd(const void *q, const void *k, const void *v,
                     int B, int H, int D, int variant, int act, int window,
                     void *out, const ja_io *io);
 
+/* jagged_attn_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, serving loops and harnesses that forbid allocation): the
+ * same computation, arguments and errors, except that io->workspace must be
+ * NULL and io->workspace_bytes 0 (JA_EINVAL otherwise).  The workspace is the
+ * library's own device array of 64 MiB, one per GPU the library runs on, held
+ * until the process ends; a call whose jagged_attn_workspace_size() exceeds
+ * 64 MiB returns JA_EWORKSPACE before anything is launched.  The first call
+ * on a device looks the array's address up on that device (device ids 0..63;
+ * others give JA_EUNSUPPORTED).  Nothing is allocated, on the host or the
+ * device.  Every call on one GPU shares that GPU's array, which keeps the
+ * last call's contents (no call needs it cleared): calls that overlap on one
+ * GPU -- on different streams, or from different threads -- race and must be
+ * ordered by the caller.  Device-detected offset errors are reported through
+ * io->status (jagged_attn_check needs a caller workspace). */
+int jagged_attn_fwd_noalloc(const void *q, const void *k, const void *v,
+                            const int32_t *q_offsets, const int32_t *kv_offsets,
+                            int B, int H, int D, int variant, int act, int window,
+                            void *out, const ja_io *io);
+
 /* Bytes of workspace jagged_attn_fwd needs for these arguments (0 on invalid
  * arguments).  Depends on the arguments only, not on the device. */
 size_t jagged_attn_workspace_size(int B, int H, int D, int variant, int act,

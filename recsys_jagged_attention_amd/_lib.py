@@ -22,7 +22,7 @@ ACTS = {"softmax": JA_SOFTMAX, "gelu_tanh": JA_GELU_TANH, "gelu_poly": JA_GELU_P
 DTYPES = {"f32": JA_F32, "bf16": JA_BF16, "mxfp8": JA_MXFP8_E4M3}
 
 # Every function the header declares (checked by the CPU tests).
-EXPORTS = ("jagged_attn_fwd", "jagged_attn_workspace_size", "jagged_attn_check",
+EXPORTS = ("jagged_attn_fwd", "jagged_attn_fwd_noalloc", "jagged_attn_workspace_size", "jagged_attn_check",
            "jagged_attn_strerror", "jagged_attn_version", "jagged_attn_mx_quantize",
            "jagged_attn_bwd", "jagged_attn_bwd_workspace_size")
 
@@ -66,6 +66,8 @@ def load() -> ctypes.CDLL:
         lib.jagged_attn_fwd.restype = ctypes.c_int
         lib.jagged_attn_fwd.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 + [
             ctypes.c_void_p, ctypes.POINTER(JaIo)]
+        lib.jagged_attn_fwd_noalloc.restype = ctypes.c_int
+        lib.jagged_attn_fwd_noalloc.argtypes = lib.jagged_attn_fwd.argtypes
         lib.jagged_attn_workspace_size.restype = ctypes.c_size_t
         lib.jagged_attn_workspace_size.argtypes = [ctypes.c_int] * 7 + [ctypes.c_int32] * 2
         lib.jagged_attn_check.restype = ctypes.c_int
@@ -102,6 +104,12 @@ def jagged_attn_fwd(q, k, v, q_offsets, kv_offsets, B, H, D, variant, act, windo
     """Raw call: pointers are ints (device addresses), returns the status code."""
     return int(load().jagged_attn_fwd(q, k, v, q_offsets, kv_offsets, B, H, D, variant, act, window,
                                       out, ctypes.byref(io)))
+
+
+def jagged_attn_fwd_noalloc(q, k, v, q_offsets, kv_offsets, B, H, D, variant, act, window, out, io: JaIo) -> int:
+    """Raw call of the no-allocation forward (io.workspace must be 0)."""
+    return int(load().jagged_attn_fwd_noalloc(q, k, v, q_offsets, kv_offsets, B, H, D, variant, act, window,
+                                              out, ctypes.byref(io)))
 
 
 def jagged_attn_check(workspace, stream) -> int:

@@ -19,7 +19,7 @@ LIB = os.path.join(HERE, "libjagged_attn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["ja_plan.hip", "ja_attn_mfma.hip", "ja_attn_pp.hip", "ja_attn_f32.hip", "ja_mx_quant.hip", "ja_attn_bwd.hip", "ja_attn_bwd_mfma.hip", "ja_api.cpp"]
+SOURCES = ["ja_plan.hip", "ja_attn_mfma.hip", "ja_attn_pp.hip", "ja_attn_f32.hip", "ja_mx_quant.hip", "ja_attn_bwd.hip", "ja_attn_bwd_mfma.hip", "ja_noalloc.hip", "ja_api.cpp"]
 
 COMMON = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+struct ja_io;
+
 namespace ja {
 
 constexpr int kBlock = 64;        // token block of block-aligned attention
@@ -167,5 +169,12 @@ struct CombineArgs {
   const float2* part_ml;
   int B, H, act;
 };
+
+// The forward on a given workspace (ja_api.cpp): validation, plan and
+// attention launches on io.stream; the workspace is `workspace_bytes` of
+// device memory (the caller's, or the library's own scratch).
+int fwd_impl(const void* q, const void* k, const void* v, const int32_t* q_offsets, const int32_t* kv_offsets,
+             int B, int H, int D, int variant, int act, int window, void* out, const ::ja_io& io, void* workspace,
+             size_t workspace_bytes);
 
 }  // namespace ja

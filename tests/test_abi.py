@@ -142,3 +142,26 @@ def test_mx_quantize_host_validation():
 
 def test_check_rejects_null_workspace():
     assert _lib.jagged_attn_check(None, None) == _lib.JA_EINVAL
+
+
+def test_noalloc_host_validation():
+    """The no-allocation forward rejects a caller workspace and batches whose
+    workspace exceeds its 64 MiB scratch, before any HIP call."""
+    lib = _lib.load()
+    j = _lib.JaIo()
+    j.dtype = _lib.JA_BF16
+    j.total_q = j.total_kv = 1 << 24
+    big = lib.jagged_attn_fwd_noalloc(4096, 4096, 4096, 4096, 4096, 4096, 64, 64, _lib.JA_PMA, _lib.JA_SOFTMAX, 0,
+                                      4096, ctypes.byref(j))
+    assert big == _lib.JA_EWORKSPACE
+    j.total_q = j.total_kv = 10
+    j.workspace, j.workspace_bytes = 1 << 20, 1 << 20
+    assert lib.jagged_attn_fwd_noalloc(4096, 4096, 4096, 4096, 4096, 2, 1, 32, 0, 0, 0, 4096,
+                                       ctypes.byref(j)) == _lib.JA_EINVAL
+    j.workspace, j.workspace_bytes = None, 0
+    assert lib.jagged_attn_fwd_noalloc(4096, 4096, 4096, 4096, 4096, 0, 1, 32, 0, 0, 0, 4096,
+                                       ctypes.byref(j)) == _lib.JA_EINVAL       # B < 1
+    assert lib.jagged_attn_fwd_noalloc(4096, 4096, 4096, 4096, 4096, 2, 1, 48, 0, 0, 0, 4096,
+                                       ctypes.byref(j)) == _lib.JA_EUNSUPPORTED  # D
+    assert lib.jagged_attn_fwd_noalloc(4096, 4096, 4096, 4096, 4096, 2, 1, 32, 0, 0, 0, 4096,
+                                       None) == _lib.JA_EINVAL

@@ -1,0 +1,88 @@
+"""jagged_attn_fwd_noalloc (the forward on the library's own device scratch,
+for callers that cannot allocate) against jagged_attn_fwd on a caller
+workspace, through the C ABI: the outputs agree bit for bit and both are within
+the oracle's tolerance, over consecutive calls whose second input is smaller
+than the first (the scratch keeps the first call's contents)."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from recsys_jagged_attention_amd import _lib
+from recsys_jagged_attention_amd.inputs import make_workload, device_tensors
+
+from parity_util import TOL, oracle_values, oracle_act, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def call(fn, w, tensors, out, workspace=None, status=None):
+    q, k, v, qo, ko, scales = tensors
+    io = _lib.JaIo()
+    io.dtype = _lib.DTYPES[w.dtype]
+    if scales is not None:
+        io.q_scale, io.k_scale, io.v_scale = (s.data_ptr() for s in scales)
+    if workspace is not None:
+        io.workspace = workspace.data_ptr()
+        io.workspace_bytes = workspace.numel()
+    io.stream = torch.cuda.current_stream().cuda_stream
+    io.total_q, io.total_kv = w.total_q, w.total_kv
+    if status is not None:
+        io.status = status.data_ptr()
+    return fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), qo.data_ptr(), ko.data_ptr(), w.B, w.H, w.D,
+              _lib.VARIANTS[w.variant], _lib.ACTS[w.act], w.window, out.data_ptr(), io)
+
+
+def run_both(w):
+    tensors = device_tensors(w, "cuda")
+    dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    out_ws = torch.full((w.total_q, w.H, w.D), float("nan"), dtype=dt, device="cuda")
+    out_na = torch.full((w.total_q, w.H, w.D), float("nan"), dtype=dt, device="cuda")
+    nbytes = _lib.jagged_attn_workspace_size(w.B, w.H, w.D, _lib.VARIANTS[w.variant], _lib.ACTS[w.act], w.window,
+                                             _lib.DTYPES[w.dtype], w.total_q, w.total_kv)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    status = torch.full((1,), 999, dtype=torch.int32, device="cuda")
+    assert call(_lib.load().jagged_attn_fwd, w, tensors, out_ws, workspace=ws) == _lib.JA_OK
+    assert call(_lib.load().jagged_attn_fwd_noalloc, w, tensors, out_na, status=status) == _lib.JA_OK
+    torch.cuda.synchronize()
+    assert int(status.item()) == _lib.JA_OK
+    a, b = out_ws.cpu(), out_na.cpu()
+    assert torch.equal(a.view(torch.int16) if dt == torch.bfloat16 else a.view(torch.int32),
+                       b.view(torch.int16) if dt == torch.bfloat16 else b.view(torch.int32))
+    q, k, v = oracle_values(w)
+    ref = oracle.gdpa_forward(q, k, v, w.q_offsets, w.kv_offsets, w.variant, oracle_act(w.act), w.window)
+    err = rel_err(b.float().numpy().astype(np.float64), ref)
+    print(f"noalloc {w.name} B={w.B} Nq={w.total_q}: ws {nbytes} B, rel err {err:.2e}", flush=True)
+    assert err <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("first,second", [(("pma", 0.3), ("pma", 0.05)),
+                                          (("cross_gelu", 0.1), ("block_window", 0.05)),
+                                          (("mxfp8_window", 0.2), ("tiny_full", 1.0))])
+def test_noalloc_matches_workspace_entry_point(first, second):
+    run_both(make_workload(first[0], scale=first[1]))
+    run_both(make_workload(second[0], scale=second[1]))
+
+
+def test_noalloc_argument_errors():
+    w = make_workload("tiny_full")
+    tensors = device_tensors(w, "cuda")
+    out = torch.empty((w.total_q, w.H, w.D), dtype=torch.float32, device="cuda")
+    fn = _lib.load().jagged_attn_fwd_noalloc
+    ws = torch.empty(4096, dtype=torch.uint8, device="cuda")
+    assert call(fn, w, tensors, out, workspace=ws) == _lib.JA_EINVAL          # a workspace was passed
+    # a batch whose workspace exceeds the scratch (64 MiB): rejected before any launch
+    io = _lib.JaIo()
+    io.dtype = _lib.JA_BF16
+    io.total_q, io.total_kv = 1 << 24, 1 << 24
+    rc = fn(4096, 4096, 4096, 4096, 4096, 4096, 64, 64, _lib.JA_PMA, _lib.JA_SOFTMAX, 0, 4096, ctypes.byref(io))
+    assert rc == _lib.JA_EWORKSPACE
+    # bad offsets: reported through the status word
+    bad = torch.tensor([0, 5, 3, int(w.total_q), int(w.total_q)], dtype=torch.int32, device="cuda")
+    q, k, v, qo, ko, sc = tensors
+    status = torch.full((1,), 999, dtype=torch.int32, device="cuda")
+    assert call(fn, w, (q, k, v, bad, bad, sc), out, status=status) == _lib.JA_OK
+    torch.cuda.synchronize()
+    assert int(status.item()) == _lib.JA_EOFFSETS
