@@ -39,7 +39,8 @@ KERNEL_NAME = {  # dominant kernel per workload (template instance)
     "full_self": "attn_pp_kernel<128,softmax>",
     "cross_gelu": "attn_pp_kernel<128,gelu>",
     "pma": "attn_kernel<64,NWQ=1,NWK=4,softmax,bf16,split>",
-    "mxfp8_window": "attn_kernel<128,NWQ=4,NWK=1,softmax,mx,window>",
+    "mxfp8_window": "attn_pp_kernel<128,softmax,block_pipeline,mx8>",
+    "mxfp8_full": "attn_pp_kernel<128,softmax,mx8>",
     "sliding_window": "attn_pp_kernel<128,softmax,sliding>",
 }
 

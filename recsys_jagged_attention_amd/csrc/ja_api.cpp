@@ -18,8 +18,9 @@ hipError_t launch_attn_mfma(int D, int in, int shape, int act, const AttnArgs& a
 hipError_t launch_combine(int D, const CombineArgs& a, hipStream_t st);
 hipError_t launch_attn_f32(int D, int act, int window_mode, const AttnArgs& a, int grid, const KTiming& tm,
                            hipStream_t st);
-hipError_t launch_attn_pp(int D, int act, bool cross, const AttnArgs& a, int num_cu, int64_t max_items,
+hipError_t launch_attn_pp(int D, int act, bool cross, bool mx8, const AttnArgs& a, int num_cu, int64_t max_items,
                           int64_t grid_cap, const KTiming& tm, hipStream_t st);
+bool pp_takes_mx8(int D, int act, bool self, int window_blocks);
 hipError_t launch_attn_bwd(int D, bool bf16, int act, int wmode, const BwdArgs& a, int64_t rows_q, int64_t rows_k,
                            int grid_q, int grid_k, hipStream_t st);
 hipError_t launch_attn_bwd_mfma(int D, int act, int wmode, const BwdArgs& a, int grid_q, int grid_k,
@@ -109,8 +110,11 @@ Plan make_plan(int B, int H, int D, int variant, int act, int window, int dtype,
   if (dtype == JA_F32) {
     p.shape = kShapeF32;
     p.bm = 64;
-  } else if (dtype == JA_BF16 && variant != JA_PMA) {
-    p.shape = kShapePingPong;  // self (with or without window) and cross: one tile stream, 8 waves x 32 rows
+  } else if ((dtype == JA_BF16 && variant != JA_PMA) ||
+             (dtype == JA_MXFP8_E4M3 && variant == JA_SELF && pp_takes_mx8(D, act, true, window / kBlock))) {
+    // bf16 self (with or without window) and cross, and MX self-attention at
+    // D = 128 (full, or windows of up to four blocks): one tile stream, 8 waves x 32 rows
+    p.shape = kShapePingPong;
     p.bm = pp_rows();
     // block windows of at most one 64-token block per wave pair: pipelined runs of query blocks
     if (variant == JA_SELF && window > 0 && window / kBlock <= pp_pipe_max_blocks()) p.bm = pp_pipe_rows();
@@ -256,7 +260,8 @@ int fwd_impl(const void* q, const void* k, const void* v, const int32_t* q_offse
     if (cap > 0) grid = std::min(grid, std::max<int64_t>(kXcds, cap / kXcds * kXcds));
     e = launch_attn_f32(D, act, variant == JA_SLIDING ? 2 : (window > 0 ? 1 : 0), aa, int(grid), tm, stream);
   } else if (p.shape == kShapePingPong) {
-    e = launch_attn_pp(D, act, variant == JA_CROSS, aa, num_cu, p.ws.max_items, cap, tm, stream);
+    e = launch_attn_pp(D, act, variant == JA_CROSS, io.dtype == JA_MXFP8_E4M3, aa, num_cu, p.ws.max_items, cap, tm,
+                       stream);
   } else {
     const int in = io.dtype == JA_BF16 ? IN_BF16 : IN_MX;
     e = launch_attn_mfma(D, in, p.shape, act, aa, num_cu, p.ws.max_items, cap, tm, stream);

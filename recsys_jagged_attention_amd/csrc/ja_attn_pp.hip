@@ -62,23 +62,43 @@ constexpr int kPPAheadS = 8;
 constexpr int kPipeBlocks = 16;
 constexpr int kPipePairs = kPPWaves / 2;
 
-template <int D, int ACT>
+template <int D, int ACT, int IN>
 struct PP {
+  // IN_BF16: K, V and Q tiles are bf16 rows loaded as they are.  IN_MX8
+  // (D = 128, softmax): e4m3 code rows plus one E8M0 scale byte per 32
+  // elements; the scores take the codes on the block-scaled fp8 MFMA and V is
+  // converted exactly to a bf16 tile in LDS for O += V P.
+  static constexpr bool kMx8 = IN == IN_MX8;
   static constexpr int kNT = 64 * kPPWaves;
-  static constexpr int kRowBytes = 2 * D;
+  static constexpr int kRowBytes = 2 * D;  // one bf16 row in LDS
   static constexpr int kTileBytes = 64 * kRowBytes;
   static constexpr int kKsOff = 2 * kTileBytes;  // GELU: 64 fp32 key scales after K and V
   static constexpr int kStageBytes = 2 * kTileBytes + (ACT != ACT_SOFTMAX ? 256 : 0);
   static constexpr int kRing = 4;
   static constexpr int kQChunks = D / 16;
   static constexpr int kOTiles = D / 32;
-  static constexpr int kSegsLd = kTileBytes / 1024;
-  static constexpr int kRowsPerSeg = 1024 / kRowBytes;
-  static constexpr int kChunksPerRow = kRowBytes / 16;
+  static constexpr int kLdRow = kMx8 ? D : 2 * D;  // bytes of one loaded row (codes: 1 per element)
+  static constexpr int kLdTile = 64 * kLdRow;
+  static constexpr int kSegsLd = kLdTile / 1024;
+  static constexpr int kRowsPerSeg = 1024 / kLdRow;
+  static constexpr int kChunksPerRow = kLdRow / 16;
   static constexpr int kDmaJobs = 2 * kSegsLd / kPPWaves;  // 1 KB loads per wave per tile
-  static constexpr int kVmemPerTile = kDmaJobs + (ACT != ACT_SOFTMAX ? 1 : 0);
+  // (every wave also loads a scale row per tile: GELU key scales, MX8 K or V scales)
+  static constexpr int kVmemPerTile = kDmaJobs + (ACT != ACT_SOFTMAX || kMx8 ? 1 : 0);
   static constexpr int kStoresPerWave = 2 * kOTiles;  // 16-byte output stores per lane of an item
   static_assert((2 * kSegsLd) % kPPWaves == 0, "tile segments must split evenly over the waves");
+  static_assert(!kMx8 || (D == 128 && ACT == ACT_SOFTMAX), "the fp8 tile stream takes D = 128 softmax");
+  // MX8 LDS layout: K codes and V codes of tiles s, s+1, s+2 (3 stages each)
+  // with their scale rows (4 bytes per key), the bf16 V of tiles s-1 and s,
+  // and two staged Q blocks (codes + scale rows).  256-byte aligned pieces.
+  static constexpr int kMxKc = 0;
+  static constexpr int kMxKs = kMxKc + 3 * kLdTile;
+  static constexpr int kMxVc = kMxKs + 3 * 256;
+  static constexpr int kMxVs = kMxVc + 3 * kLdTile;
+  static constexpr int kMxVb = kMxVs + 3 * 256;
+  static constexpr int kMxQc = kMxVb + 2 * kTileBytes;
+  static constexpr int kMxQs = kMxQc + 2 * kLdTile;
+  static constexpr int kMxBytes = kMxQs + 2 * 256;
 };
 
 // Position in the tile stream: tile t of the k-th item of this workgroup
@@ -120,6 +140,9 @@ struct Src {
   const unsigned char* vb;
   const float* ksc;
   const unsigned char* qb;
+  const unsigned char* ksb;  // MX8: scale rows of key row 0 (K and V) and query row 0
+  const unsigned char* vsb;
+  const unsigned char* qsb;
   int lq;
 };
 
@@ -132,11 +155,14 @@ struct PPCtx {
   const unsigned char* q;
   const unsigned char* k;
   const unsigned char* v;
+  const unsigned char* qs;  // MX8 scale bytes
+  const unsigned char* ks;
+  const unsigned char* vs;
   const float* kscale;
   __bf16* out;
   int H;
   int G, pos, n;          // item k of this workgroup is item_index(k), k < n
-  unsigned row_bytes;
+  unsigned row_bytes;  // bytes between a head's input rows (bf16: 2 H D; MX8 codes: H D)
 };
 
 // Round k deals items [kG, kG + G) to positions 0..G-1, in reverse order on odd rounds.
@@ -166,14 +192,21 @@ __device__ __forceinline__ WorkItem load_record(const PPCtx& c, int k) {
   return w;
 }
 
-template <int D>
+template <int D, int IN>
 __device__ __forceinline__ Src make_src(const PPCtx& c, const WorkItem& w) {
-  const size_t off = (size_t(w.kbeg) * c.H + w.h) * size_t(2 * D);
+  constexpr size_t kElt = IN == IN_MX8 ? 1 : 2;  // bytes per element
+  const size_t krow = size_t(w.kbeg) * c.H + w.h, qrow = size_t(w.qbeg) * c.H + w.h;
   Src r;
-  r.kb = uniform_ptr(c.k + off);
-  r.vb = uniform_ptr(c.v + off);
-  r.ksc = c.kscale ? uniform_ptr(c.kscale + size_t(w.kbeg) * c.H + w.h) : nullptr;
-  r.qb = uniform_ptr(c.q + (size_t(w.qbeg) * c.H + w.h) * size_t(2 * D));
+  r.kb = uniform_ptr(c.k + krow * (kElt * D));
+  r.vb = uniform_ptr(c.v + krow * (kElt * D));
+  r.ksc = c.kscale ? uniform_ptr(c.kscale + krow) : nullptr;
+  r.qb = uniform_ptr(c.q + qrow * (kElt * D));
+  r.ksb = r.vsb = r.qsb = nullptr;
+  if constexpr (IN == IN_MX8) {
+    r.ksb = uniform_ptr(c.ks + krow * (D / kMxBlock));
+    r.vsb = uniform_ptr(c.vs + krow * (D / kMxBlock));
+    r.qsb = uniform_ptr(c.qs + qrow * (D / kMxBlock));
+  }
   r.lq = w.lq;
   return r;
 }
@@ -204,7 +237,7 @@ __device__ __forceinline__ void write_zero_rows(const PPCtx& c, const WorkItem& 
 // Training: ...", section "BlockAttention").  With a sliding window of wt
 // tokens (query i sees keys i-wt+1 .. i) the tiles run from the one holding
 // key q0-wt+1 to the one holding the item's last query.
-template <int D, int WMODE>
+template <int D, int WMODE, int IN>
 __device__ __forceinline__ void advance(const PPCtx& c, Cur& cu, Src& src, int wave, int lane, int nb, int wt) {
   if (cu.k >= c.n) return;
   if (++cu.t < cu.te) return;
@@ -237,7 +270,7 @@ __device__ __forceinline__ void advance(const PPCtx& c, Cur& cu, Src& src, int w
       cu.t = t_lo;
       cu.te = t_end;
       cu.lk = w.lk;
-      src = make_src<D>(c, w);
+      src = make_src<D, IN>(c, w);
       return;
     }
     write_zero_rows<D>(c, w, wave, lane);
@@ -250,17 +283,19 @@ __device__ __forceinline__ void advance(const PPCtx& c, Cur& cu, Src& src, int w
 // waited for only before that item's scores.  With the short K/V of
 // cross-attention almost every step starts an item, and loading Q at the item
 // start left every wave waiting for HBM once per step.
-template <int D, int ACT, int WMODE, bool QPF>
+template <int D, int ACT, int WMODE, bool QPF, int IN>
 __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
-  using K = PP<D, ACT>;
+  using K = PP<D, ACT, IN>;
   constexpr int kQChunks = K::kQChunks, kOTiles = K::kOTiles, kRowBytes = K::kRowBytes;
   constexpr bool kPipe = WMODE == kWinPipe;
+  constexpr bool kMx8 = K::kMx8;
   // LDS: a ring of kRing stages of (K, V[, key scales]).  The pipeline instead
   // keeps K in 3 stages (tiles s, s+1, s+2: K_{s-1} is dead once the scores
   // of tile s-1 are taken), V in 4 (s-1 .. s+2) and two Q blocks (the block
   // starting on the next tile, alternating by tile parity).
   constexpr int kPipeV = 3 * K::kTileBytes, kPipeQ = 7 * K::kTileBytes;
-  constexpr int kRingBytes = kPipe ? 9 * K::kTileBytes : K::kRing * K::kStageBytes;
+  // MX8: see PP::kMx*.
+  constexpr int kRingBytes = kMx8 ? K::kMxBytes : (kPipe ? 9 * K::kTileBytes : K::kRing * K::kStageBytes);
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kRingBytes];
   __shared__ WorkItem cache[kPPItemCache];
 
@@ -276,6 +311,9 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
   c.q = reinterpret_cast<const unsigned char*>(a.q);
   c.k = reinterpret_cast<const unsigned char*>(a.k);
   c.v = reinterpret_cast<const unsigned char*>(a.v);
+  c.qs = a.qs;
+  c.ks = a.ks;
+  c.vs = a.vs;
   c.kscale = a.kscale;
   c.out = reinterpret_cast<__bf16*>(a.out);
   c.H = a.H;
@@ -291,7 +329,8 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
     const int full = n_all / c.G;  // complete rounds
     c.n = full + (item_index(c, full) < n_all ? 1 : 0);
   }
-  c.row_bytes = 2u * unsigned(a.H) * D;
+  c.row_bytes = (kMx8 ? 1u : 2u) * unsigned(a.H) * D;  // bytes between a head's rows
+  const unsigned srow = unsigned(a.H) * (D / kMxBlock);  // MX8: scale bytes between rows
   if (c.n == 0) return;
   for (int k = tid; k < min(c.n, kPPItemCache); k += K::kNT) cache[k] = a.items[item_index(c, k)];
   __syncthreads();
@@ -301,14 +340,14 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
   const int nb = a.window_blocks, wt = a.window_tokens;
   Cur c0{-1, 0, 0, 0, 0, 0, 0};
   Src src{};
-  advance<D, WMODE>(c, c0, src, wave, lane, nb, wt);
+  advance<D, WMODE, IN>(c, c0, src, wave, lane, nb, wt);
   if (c0.k >= c.n) return;
   const Src src0 = src;
   Cur c1 = c0;
-  advance<D, WMODE>(c, c1, src, wave, lane, nb, wt);
+  advance<D, WMODE, IN>(c, c1, src, wave, lane, nb, wt);
   const Src src1 = src;
   Cur c2 = c1;
-  advance<D, WMODE>(c, c2, src, wave, lane, nb, wt);
+  advance<D, WMODE, IN>(c, c2, src, wave, lane, nb, wt);
 
   // Loads of the loading cursor's tile into LDS (K at byte kdst of the ring, V
   // at vdst).  Job j moves 1 KB segment wave + 8j of K|V; rows of a ragged tile
@@ -322,7 +361,9 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
     const unsigned char* tile = (is_v ? sr.vb : sr.kb) + size_t(key0) * c.row_bytes;
     const int row = seg * K::kRowsPerSeg + lane / K::kChunksPerRow;
     const int phys = lane % K::kChunksPerRow;
-    const int ch = phys ^ (is_v ? swz_v<D>(row) : swz_k<D>(row));
+    int ch;
+    if constexpr (kMx8) ch = phys ^ swz_c<D>(row);
+    else ch = phys ^ (is_v ? swz_v<D>(row) : swz_k<D>(row));
     const unsigned off = __umul24(unsigned(min(row, lim)), c.row_bytes) + 16u * unsigned(ch);
     lds_dma16(tile, off, lds_addr_of(ring) + (is_v ? vdst : kdst) + seg * 1024);
   };
@@ -342,9 +383,18 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
         const int r0 = kBlock * bq;
         const int lim = min(63, sr.lq - 1 - r0);
         const int row = seg * K::kRowsPerSeg + lid / K::kChunksPerRow;
-        const int ch = (lid % K::kChunksPerRow) ^ swz_k<D>(row);
+        const int ch = (lid % K::kChunksPerRow) ^ (kMx8 ? swz_c<D>(row) : swz_k<D>(row));
         const unsigned off = __umul24(unsigned(min(row, lim)), c.row_bytes) + 16u * unsigned(ch);
-        lds_dma16(sr.qb + size_t(r0) * c.row_bytes, off, lds_addr_of(ring) + kPipeQ + slot * K::kTileBytes + seg * 1024);
+        const int qdst = kMx8 ? K::kMxQc + slot * K::kLdTile : kPipeQ + slot * K::kTileBytes;
+        lds_dma16(sr.qb + size_t(r0) * c.row_bytes, off, lds_addr_of(ring) + qdst + seg * 1024);
+      }
+    }
+    if constexpr (kMx8) {
+      // the block's scale rows (4 bytes per query row), by wave 0
+      if (wave == 0) {
+        const int r0 = kBlock * bq;
+        const unsigned r = unsigned(min(lid, sr.lq - 1 - r0));
+        lds_dma4(sr.qsb + size_t(r0) * srow, r * srow, lds_addr_of(ring) + K::kMxQs + slot * 256);
       }
     }
   };
@@ -355,6 +405,18 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
     if constexpr (kPipe) {
       const int bq = cu.t + nb - 1;
       if (cu.k < c.n && cu.t > cu.wlo && bq < cu.whi) q_block_job(sr, bq, cu.t & 1);
+    }
+  };
+  // MX8: the K (even waves) or V (odd waves) scale rows of the loading
+  // cursor's tile into the scale slot of stream tile s (every wave issues one
+  // load per tile, so the waits count the same loads on every wave).
+  auto mx_scales = [&](const Cur& cu, const Src& sr, int s) __attribute__((always_inline)) {
+    if constexpr (kMx8) {
+      const int key0 = 64 * cu.t;
+      const unsigned r = unsigned(min(lane, cu.lk - 1 - key0));
+      const bool is_v = wave & 1;
+      lds_dma4((is_v ? sr.vsb : sr.ksb) + size_t(key0) * srow, r * srow,
+               lds_addr_of(ring) + (is_v ? K::kMxVs : K::kMxKs) + (s % 3) * 256);
     }
   };
   auto tile_scales = [&](const Cur& cu, const Src& sr, int st) __attribute__((always_inline)) {
@@ -380,11 +442,19 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
   const float c2s = a.score_scale;  // softmax: log2(e)/sqrt(D); GELU: 1/sqrt(D)
 
   // LDS byte offsets of the K and V tiles of stream tile s.
+  // (MX8: k_at is the K code tile, vc_at the V code tile the loads fill, v_at
+  // the converted bf16 V tile that O += V P reads)
   auto k_at = [&](int s) __attribute__((always_inline)) {
+    if constexpr (kMx8) return K::kMxKc + (s % 3) * K::kLdTile;
     return kPipe ? (s % 3) * K::kTileBytes : (s % K::kRing) * K::kStageBytes;
   };
   auto v_at = [&](int s) __attribute__((always_inline)) {
+    if constexpr (kMx8) return K::kMxVb + (s & 1) * K::kTileBytes;
     return kPipe ? kPipeV + (s % 4) * K::kTileBytes : (s % K::kRing) * K::kStageBytes + K::kTileBytes;
+  };
+  auto vc_at = [&](int s) __attribute__((always_inline)) {
+    if constexpr (kMx8) return K::kMxVc + (s % 3) * K::kLdTile;
+    return v_at(s);
   };
   const int pair = wave >> 1;
   // First query row (sample-local) of this wave in the scores' item.
@@ -395,13 +465,36 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
 
   // Q fragments of the scores' item: lane holds dims [(D/2)g, (D/2)g + D/2) of
   // query row q0 + 32*wave + l32 (rows past the sample load its last row).
-  bf16x8 qf[kQChunks];
+  // MX8: qc[c] holds the 64-element chunk c of the row as the fp8 MFMA's B
+  // operand (lane-half g: elements 64c+16g+[0,16) and 64c+32+16g+[0,16)), qsc[c]
+  // the scale byte of 32-element block 2c+g.
+  constexpr int kMxC = D / 64;
+  bf16x8 qf[kMx8 ? 1 : kQChunks];
+  i32x8 qc[kMx8 ? kMxC : 1];
+  int qsc[kMx8 ? kMxC : 1];
   auto load_q = [&](const Cur& cu) __attribute__((always_inline)) {
     const WorkItem it = load_record(c, cu.k);
     const int qrow = min(wave_row0(cu, it.q0) + l32, it.lq - 1);
-    const __bf16* src_q = reinterpret_cast<const __bf16*>(a.q) + (size_t(it.qbeg + qrow) * a.H + it.h) * D + (D / 2) * g;
+    const size_t row = size_t(it.qbeg + qrow) * a.H + it.h;
+    if constexpr (kMx8) {
+      const unsigned char* src = c.q + row * D;
+      const unsigned sw = *reinterpret_cast<const unsigned*>(c.qs + row * (D / kMxBlock));
 #pragma unroll
-    for (int cc = 0; cc < kQChunks; ++cc) qf[cc] = *reinterpret_cast<const bf16x8*>(src_q + 8 * cc);
+      for (int cc = 0; cc < kMxC; ++cc) {
+        const u32x4 w0 = *reinterpret_cast<const u32x4*>(src + 64 * cc + 16 * g);
+        const u32x4 w1 = *reinterpret_cast<const u32x4*>(src + 64 * cc + 32 + 16 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          qc[cc][i] = int(w0[i]);
+          qc[cc][4 + i] = int(w1[i]);
+        }
+        qsc[cc] = int((sw >> (8 * (2 * cc + g))) & 0xFFu);
+      }
+    } else {
+      const __bf16* src_q = reinterpret_cast<const __bf16*>(a.q) + row * D + (D / 2) * g;
+#pragma unroll
+      for (int cc = 0; cc < kQChunks; ++cc) qf[cc] = *reinterpret_cast<const bf16x8*>(src_q + 8 * cc);
+    }
   };
   float rq = 1.f;  // GELU: RMS factor of the query row times 1/sqrt(D)
   auto q_rms = [&]() __attribute__((always_inline)) {
@@ -419,11 +512,13 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
   // Prologue: tiles 0 and 1 in flight, Q of the first item (pipeline: and of
   // the block starting on tile 1).
 #pragma unroll
-  for (int j = 0; j < K::kDmaJobs; ++j) tile_job(c0, src0, k_at(0), v_at(0), j);
+  for (int j = 0; j < K::kDmaJobs; ++j) tile_job(c0, src0, k_at(0), vc_at(0), j);
   tile_scales(c0, src0, 0);
+  mx_scales(c0, src0, 0);
 #pragma unroll
-  for (int j = 0; j < K::kDmaJobs; ++j) tile_job(c1, src1, k_at(1), v_at(1), j);
+  for (int j = 0; j < K::kDmaJobs; ++j) tile_job(c1, src1, k_at(1), vc_at(1), j);
   tile_scales(c1, src1, 1);
+  mx_scales(c1, src1, 1);
   q_stage(c1, src1);
   load_q(c0);
   wait_vmcnt(0);  // (nothing may be pending on the loop's entry edge, see below)
@@ -548,7 +643,8 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
       // 64-bit lane address stays live across the stream loop
       unsigned char* ob = const_cast<unsigned char*>(
           uniform_ptr(reinterpret_cast<const unsigned char*>(a.out) + (size_t(it.qbeg + row0) * a.H + it.h) * size_t(2 * D)));
-      const unsigned loff = unsigned(l32) * c.row_bytes + unsigned(D * g);
+      // (out is bf16 whatever the input format: 2 H D bytes between a head's rows)
+      const unsigned loff = unsigned(l32) * (2u * unsigned(a.H) * D) + unsigned(D * g);
 #pragma unroll
       for (int t = 0; t < kOTiles; ++t)
 #pragma unroll
@@ -662,10 +758,48 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
     if constexpr (kPipe) ps = pipe_step(c0, pair, nb);
     // this wave computes tile s
     const bool act = WMODE == kWinNone || (kPipe ? ps.act : (c0.t >= c0.wlo && c0.t <= c0.whi));
-    const int pf_k = k_at(s + 2), pf_v = v_at(s + 2);
+    const int pf_k = k_at(s + 2), pf_v = vc_at(s + 2);
     if (!act) {
 #pragma unroll
       for (int j = 0; j < K::kDmaJobs; ++j) tile_job(c2, src, pf_k, pf_v, j);
+    } else if constexpr (kMx8) {
+      // Block-scaled fp8 scores: four 32x32x64 MFMAs (key half st, 64-element
+      // chunk c of D), A = the key row's codes from LDS (laid out like the query
+      // operand), its scale byte from the tile's scale rows.  All operands are
+      // read before the first MFMA; the tile loads go between the MFMAs of the
+      // second half.
+      const unsigned char* ks = ring + k_at(s);
+      const unsigned char* kss = ring + K::kMxKs + (s % 3) * 256;
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[st][i] = 0.f;
+      i32x8 kop[2 * kMxC];
+#pragma unroll
+      for (int i = 0; i < 2 * kMxC; ++i) {
+        const int krow = 32 * (i / kMxC) + kp, cc = i % kMxC;
+        const u32x4 w0 = *reinterpret_cast<const u32x4*>(ks + krow * D + 16 * ((4 * cc + g) ^ swz_c<D>(krow)));
+        const u32x4 w1 = *reinterpret_cast<const u32x4*>(ks + krow * D + 16 * ((4 * cc + 2 + g) ^ swz_c<D>(krow)));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          kop[i][j] = int(w0[j]);
+          kop[i][4 + j] = int(w1[j]);
+        }
+      }
+      const unsigned ksw0 = *reinterpret_cast<const unsigned*>(kss + 4 * kp);
+      const unsigned ksw1 = *reinterpret_cast<const unsigned*>(kss + 4 * (32 + kp));
+#pragma unroll
+      for (int i = 0; i < 2 * kMxC; ++i) {
+        const int st = i / kMxC, cc = i % kMxC;
+        const int kscl = int(((st ? ksw1 : ksw0) >> (8 * (2 * cc + g))) & 0xFFu);
+        sc[st] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop[i], qc[cc], sc[st], 0, 0, 0, kscl, 0, qsc[cc]);
+        constexpr int kPer = kMxC / K::kDmaJobs > 0 ? kMxC / K::kDmaJobs : 1;
+        if (i >= kMxC && (i - kMxC) % kPer == kPer - 1) tile_job(c2, src, pf_k, pf_v, (i - kMxC) / kPer);
+      }
+      // keep the operand reads ahead of the MFMAs
+      __builtin_amdgcn_sched_group_barrier(kSgDsRead, 4 * kMxC + 2, 1);
+#pragma unroll
+      for (int i = 0; i < 2 * kMxC; ++i) __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 1);
     } else {
       const unsigned char* ks = ring + k_at(s);
 #pragma unroll
@@ -700,6 +834,7 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
       }
     }
     tile_scales(c2, src, st_pf);
+    mx_scales(c2, src, s + 2);
     if constexpr (QPF) {
       // the scores above have consumed Q: load the next item's (one branch,
       // waited for by count, see above)
@@ -713,12 +848,50 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
       // scores above have consumed.
       const PipeStep pn = pipe_step(c1, pair, nb);
       if (c1.k == c0.k && pn.first && c1.t > c1.wlo) {
-        const unsigned char* qs = ring + kPipeQ + (c1.t & 1) * K::kTileBytes;
         const int row = 32 * (wave & 1) + l32;
+        if constexpr (kMx8) {
+          const unsigned char* qs = ring + K::kMxQc + (c1.t & 1) * K::kLdTile;
+          const unsigned sw = *reinterpret_cast<const unsigned*>(ring + K::kMxQs + (c1.t & 1) * 256 + 4 * row);
 #pragma unroll
-        for (int cc = 0; cc < kQChunks; ++cc)
-          qf[cc] = *reinterpret_cast<const bf16x8*>(qs + row * kRowBytes + 16 * ((kQChunks * g + cc) ^ swz_k<D>(row)));
+          for (int cc = 0; cc < kMxC; ++cc) {
+            const u32x4 w0 = *reinterpret_cast<const u32x4*>(qs + row * D + 16 * ((4 * cc + g) ^ swz_c<D>(row)));
+            const u32x4 w1 = *reinterpret_cast<const u32x4*>(qs + row * D + 16 * ((4 * cc + 2 + g) ^ swz_c<D>(row)));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              qc[cc][j] = int(w0[j]);
+              qc[cc][4 + j] = int(w1[j]);
+            }
+            qsc[cc] = int((sw >> (8 * (2 * cc + g))) & 0xFFu);
+          }
+        } else {
+          const unsigned char* qs = ring + kPipeQ + (c1.t & 1) * K::kTileBytes;
+#pragma unroll
+          for (int cc = 0; cc < kQChunks; ++cc)
+            qf[cc] = *reinterpret_cast<const bf16x8*>(qs + row * kRowBytes + 16 * ((kQChunks * g + cc) ^ swz_k<D>(row)));
+        }
       }
+    }
+    if constexpr (kMx8) {
+      // V of tile s (landed at the top of this step) to bf16, exactly (4-bit
+      // e4m3 significands times a power of two), by every thread: 16 codes of
+      // one row each, into the bf16 slot O += V P reads in the next step.
+      // (that slot last held tile s-2, read in the previous step)
+      const int row = tid >> 3, j16 = tid & 7;
+      const unsigned char* vcs = ring + vc_at(s);
+      const u32x4 w = *reinterpret_cast<const u32x4*>(vcs + row * D + 16 * (j16 ^ swz_c<D>(row)));
+      const unsigned sw = *reinterpret_cast<const unsigned*>(ring + K::kMxVs + (s % 3) * 256 + 4 * row);
+      const float scl = e8m0_to_float(sw >> (8 * (j16 >> 1)));
+      u32x4 o0, o1;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        o0[2 * i] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], scl, false));
+        o0[2 * i + 1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], scl, true));
+        o1[2 * i] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 + i], scl, false));
+        o1[2 * i + 1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 + i], scl, true));
+      }
+      unsigned char* vb = ring + v_at(s) + row * kRowBytes;
+      *reinterpret_cast<u32x4*>(vb + 16 * ((2 * j16) ^ swz_v<D>(row))) = o0;
+      *reinterpret_cast<u32x4*>(vb + 16 * ((2 * j16 + 1) ^ swz_v<D>(row))) = o1;
     }
     const bool s_last = kPipe ? ps.last : c0.t == c0.te - 1;
     const int nvalid = min(64, c0.lk - 64 * c0.t);
@@ -732,7 +905,7 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
     if constexpr (kPipe) pv_row0 = kBlock * ps.b + 32 * (wave & 1);
     c0 = c1;
     c1 = c2;
-    advance<D, WMODE>(c, c2, src, wave, lane, nb, wt);
+    advance<D, WMODE, IN>(c, c2, src, wave, lane, nb, wt);
   }
 }
 
@@ -740,31 +913,43 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
 
 template <int D, int ACT>
 hipError_t launch_none(bool cross, dim3 gd, dim3 bd, hipStream_t st, const AttnArgs& a, const KTiming& tm) {
-  if (cross) return launch1(attn_pp_kernel<D, ACT, kWinNone, true>, gd, bd, st, a, tm);
-  return launch1(attn_pp_kernel<D, ACT, kWinNone, false>, gd, bd, st, a, tm);
+  if (cross) return launch1(attn_pp_kernel<D, ACT, kWinNone, true, IN_BF16>, gd, bd, st, a, tm);
+  return launch1(attn_pp_kernel<D, ACT, kWinNone, false, IN_BF16>, gd, bd, st, a, tm);
 }
 
 template <int D>
 hipError_t launch_d(int act, bool cross, dim3 gd, dim3 bd, hipStream_t st, const AttnArgs& a, const KTiming& tm) {
   if (a.window_tokens > 0)  // (softmax only)
-    return launch1(attn_pp_kernel<D, ACT_SOFTMAX, kWinSliding, false>, gd, bd, st, a, tm);
+    return launch1(attn_pp_kernel<D, ACT_SOFTMAX, kWinSliding, false, IN_BF16>, gd, bd, st, a, tm);
   if (a.window_blocks > 0 && a.window_blocks <= kPipePairs)  // (softmax only)
-    return launch1(attn_pp_kernel<D, ACT_SOFTMAX, kWinPipe, false>, gd, bd, st, a, tm);
+    return launch1(attn_pp_kernel<D, ACT_SOFTMAX, kWinPipe, false, IN_BF16>, gd, bd, st, a, tm);
   if (a.window_blocks > 0)  // (softmax only)
-    return launch1(attn_pp_kernel<D, ACT_SOFTMAX, kWinBlock, false>, gd, bd, st, a, tm);
+    return launch1(attn_pp_kernel<D, ACT_SOFTMAX, kWinBlock, false, IN_BF16>, gd, bd, st, a, tm);
   if (act == ACT_SOFTMAX) return launch_none<D, ACT_SOFTMAX>(cross, gd, bd, st, a, tm);
   if (act == ACT_GELU_POLY) return launch_none<D, ACT_GELU_POLY>(cross, gd, bd, st, a, tm);
   return launch_none<D, ACT_GELU>(cross, gd, bd, st, a, tm);
+}
+
+// MX8 inputs (D = 128, softmax self-attention): full, or block windows of up to four blocks.
+hipError_t launch_mx8(dim3 gd, dim3 bd, hipStream_t st, const AttnArgs& a, const KTiming& tm) {
+  if (a.window_blocks > 0)
+    return launch1(attn_pp_kernel<128, ACT_SOFTMAX, kWinPipe, false, IN_MX8>, gd, bd, st, a, tm);
+  return launch1(attn_pp_kernel<128, ACT_SOFTMAX, kWinNone, false, IN_MX8>, gd, bd, st, a, tm);
 }
 
 int pp_rows() { return kPPRows; }
 int pp_pipe_rows() { return kBlock * kPipeBlocks; }
 int pp_pipe_max_blocks() { return kPipePairs; }
 
-hipError_t launch_attn_pp(int D, int act, bool cross, const AttnArgs& a, int num_cu, int64_t max_items,
+bool pp_takes_mx8(int D, int act, bool self, int window_blocks) {
+  return D == 128 && act == ACT_SOFTMAX && self && window_blocks <= kPipePairs;
+}
+
+hipError_t launch_attn_pp(int D, int act, bool cross, bool mx8, const AttnArgs& a, int num_cu, int64_t max_items,
                           int64_t grid_cap, const KTiming& tm, hipStream_t st) {
   // One workgroup per CU (the tile ring takes most of the LDS), a multiple of the XCD count.
   const dim3 gd(static_cast<unsigned>(persistent_grid(num_cu, max_items, grid_cap))), bd(64 * kPPWaves);
+  if (mx8) return launch_mx8(gd, bd, st, a, tm);
   if (D == 32) return launch_d<32>(act, cross, gd, bd, st, a, tm);
   if (D == 64) return launch_d<64>(act, cross, gd, bd, st, a, tm);
   return launch_d<128>(act, cross, gd, bd, st, a, tm);

@@ -13,6 +13,8 @@ techfeed.io, "なぜLLM向けのインフラをそのまま使えないのか"])
 * ``cross_gelu``     : B=256, Lq~logU[256,8192], Lkv~U{16..64}, H=4, D=128, bf16, RMSNorm+GELU
 * ``pma``            : B=512, 32 seeds/sample, Lkv: 5% logU[8193,16384], rest logU[64,8192], H=8, D=64
 * ``mxfp8_window``   : block_window lengths/values quantised to e4m3 + E8M0 (one scale per 32 along D)
+* ``mxfp8_full``     : the mxfp8_window inputs with no window (full self-attention on MX inputs)
+* ``sliding_window`` : the block_window tensors under a 256-token sliding window
 
 Every generator takes an explicit integer seed and uses numpy's PCG64.
 """
@@ -130,9 +132,10 @@ class Workload:
         return int(self.kv_offsets[-1])
 
 
-WORKLOADS = ("tiny_full", "block_window", "full_self", "cross_gelu", "pma", "mxfp8_window", "sliding_window")
+WORKLOADS = ("tiny_full", "block_window", "full_self", "cross_gelu", "pma", "mxfp8_window", "mxfp8_full",
+             "sliding_window")
 DEFAULT_SEED = {"tiny_full": 1001, "block_window": 1002, "full_self": 1002,
-                "cross_gelu": 1003, "pma": 1004, "mxfp8_window": 1002, "sliding_window": 1002}
+                "cross_gelu": 1003, "pma": 1004, "mxfp8_window": 1002, "mxfp8_full": 1002, "sliding_window": 1002}
 
 
 def make_workload(name: str, seed: Optional[int] = None, scale: float = 1.0) -> Workload:
@@ -152,7 +155,7 @@ def make_workload(name: str, seed: Optional[int] = None, scale: float = 1.0) -> 
         k = normal_values(rng, int(off[-1]), H, D)
         v = normal_values(rng, int(off[-1]), H, D)
         return Workload(name, "self", "softmax", "f32", B, H, D, 0, off, off, q, k, v, seed)
-    if name in ("block_window", "full_self", "mxfp8_window", "sliding_window"):
+    if name in ("block_window", "full_self", "mxfp8_window", "mxfp8_full", "sliding_window"):
         B, H, D = nb(64), 8, 128
         L = lengths_loguniform(rng, B, 100, 4096)
         off = offsets_from_lengths(L)
@@ -160,8 +163,8 @@ def make_workload(name: str, seed: Optional[int] = None, scale: float = 1.0) -> 
         q = normal_values(rng, n, H, D)
         k = normal_values(rng, n, H, D)
         v = normal_values(rng, n, H, D)
-        window = 0 if name == "full_self" else 256  # (sliding_window: 256 tokens)
-        dtype = "mxfp8" if name == "mxfp8_window" else "bf16"
+        window = 0 if name in ("full_self", "mxfp8_full") else 256  # (sliding_window: 256 tokens)
+        dtype = "mxfp8" if name in ("mxfp8_window", "mxfp8_full") else "bf16"
         variant = "sliding" if name == "sliding_window" else "self"
         w = Workload(name, variant, "softmax", dtype, B, H, D, window, off, off, q, k, v, seed)
         if dtype == "mxfp8":

@@ -404,3 +404,25 @@ def test_non_current_stream_without_workspace():
     ref = oracle.gdpa_forward(qq, kk, vv, w.q_offsets, w.kv_offsets, "cross", "gelu_tanh", 0)
     for o in outs:
         assert rel_err(o.float().cpu().numpy().astype(np.float64), ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("window", [0, 64, 128, 192, 256])
+def test_mxfp8_tile_stream_long_samples(window):
+    """MXFP8 self-attention at D = 128 on the tile stream (fp8 scores, V
+    converted to bf16 in LDS): full attention and block windows of one to four
+    blocks on samples of several pipelined runs (1024 rows), ragged tails and
+    a one-block sample."""
+    L = [1500, 2049, 700, 64, 3001, 257, 1]
+    w = adhoc("mx_stream_long", "self", "softmax", "mxfp8", L, L, 3, 128, window=window, seed=window + 41)
+    log(f"mxfp8 tile stream W={window}: N={w.total_q}")
+    full_parity(w)
+
+
+def test_mxfp8_pipeline_many_items():
+    """The MXFP8 block pipeline with more runs than a workgroup stages in LDS
+    (short samples, 40 heads, grid capped at 16 workgroups)."""
+    rng = np.random.Generator(np.random.PCG64(83))
+    L = rng.integers(1, 300, size=300).tolist()
+    w = adhoc("mx_pipe_many", "self", "softmax", "mxfp8", L, L, 40, 128, window=256, seed=84)
+    log(f"mxfp8 pipeline many items: N={w.total_q}")
+    full_parity(w, max_workgroups=16)

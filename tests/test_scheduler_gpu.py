@@ -46,7 +46,9 @@ def schedule(w):
         return 64, 0, False
     if w.variant == "pma":
         return 32, key_chunk(w.H, w.total_kv), True
-    if w.dtype == "bf16":
+    tile_stream = w.dtype == "bf16" or (w.D == 128 and w.variant == "self" and w.act == "softmax"
+                                        and w.window <= 4 * BLOCK)
+    if tile_stream:
         if w.variant == "self" and 0 < w.window <= 4 * BLOCK:
             return 1024, 0, True       # block-window pipeline: runs of 16 query blocks
         return 256, 0, True            # tile stream
@@ -118,7 +120,10 @@ CASES = {
     "sliding": ("sliding", "softmax", "bf16", [0, 1, 300, 1000, 0, 513], None, 2, 32, 100),
     "key_split": ("pma", "softmax", "bf16", [32, 32, 0, 7, 32, 32], [0, 513, 100, 70000, 20000, 64], 4, 64, 0),
     "mx_window": ("self", "softmax", "mxfp8", [0, 1, 128, 129, 700, 0, 64], None, 2, 128, 256),
+    "mx_window_long": ("self", "softmax", "mxfp8", [0, 1, 128, 129, 700, 0, 64], None, 2, 128, 512),
+    "mx_window_d64": ("self", "softmax", "mxfp8", [0, 1, 128, 129, 700, 0, 64], None, 2, 64, 128),
     "mx_full": ("self", "softmax", "mxfp8", [0, 1, 300, 256, 0], None, 2, 128, 0),
+    "mx_cross": ("cross", "softmax", "mxfp8", [0, 1, 300, 256, 9], [5, 0, 70, 200, 1], 2, 128, 0),
     "f32": ("self", "softmax", "f32", [0, 1, 63, 64, 65, 200, 0], None, 2, 32, 0),
 }
 
