@@ -414,6 +414,8 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 5 times (the reference "
                          "for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE counters) and exit")
+    ap.add_argument("--fp8-pv", action="store_true",
+                    help="MXFP8 workloads: O += P V on the fp8 MFMA too (P and V requantised along the keys)")
     ap.add_argument("--backward", action="store_true",
                     help="time the softmax backward on the workload instead of the forward")
     ap.add_argument("--mx-quantize", action="store_true",
@@ -486,10 +488,10 @@ def main():
     def step(i, events=None):
         qq, kk, vv, ss = sets[i % n_copies]
         forward(qq, kk, vv, qo, ko, variant=w.variant, act=w.act, window=w.window, dtype=w.dtype,
-                scales=ss, out=outs[i % n_copies], workspace=wsp, events=events)
+                scales=ss, out=outs[i % n_copies], workspace=wsp, events=events, fp8_pv=args.fp8_pv)
 
     forward(q, k, v, qo, ko, variant=w.variant, act=w.act, window=w.window, dtype=w.dtype,
-            scales=scales, out=outs[0], workspace=wsp, check=True)   # validates offsets once
+            scales=scales, out=outs[0], workspace=wsp, check=True, fp8_pv=args.fp8_pv)  # validates offsets once
     for i in range(W):
         step(i)
     torch.cuda.synchronize()
@@ -512,6 +514,10 @@ def main():
     intensity = flops / alg_bytes
     ridge = PEAK_TFLOPS[w.dtype] * 1e12 / (PEAK_HBM_GBS * 1e9)
     kernel_tag = KERNEL_NAME[w.name]
+    if args.fp8_pv:
+        if not kernel_tag.endswith(",mx8>"):
+            raise SystemExit("--fp8-pv applies to the MXFP8 self-attention workloads")
+        kernel_tag = kernel_tag[:-1] + ",fp8pv>"
     if intensity < ridge:
         achieved = alg_bytes / kern_avg_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -532,6 +538,17 @@ def main():
     log(f"[bench] {ms_per_step * 1e3:.1f} us/step, kernel {kern_avg_s * 1e6:.1f} us, "
         f"{value:.1f} useful TFLOPS, {roof['achieved']} {roof['unit']} ({roof['frac'] * 100:.1f}% of peak)")
 
+    # one more (untimed) call with the softmax's diagnostic counters: how often
+    # the lazy reference max had to move after a query block's first tile
+    softmax_stats = None
+    if w.act == "softmax" and kernel_tag.startswith("attn_pp_kernel"):
+        st = torch.zeros(3, dtype=torch.int64, device=dev)
+        forward(q, k, v, qo, ko, variant=w.variant, act=w.act, window=w.window, dtype=w.dtype,
+                scales=scales, out=outs[0], workspace=wsp, softmax_stats=st, fp8_pv=args.fp8_pv)
+        torch.cuda.synchronize()
+        tiles, first, later = (int(x) for x in st.cpu())
+        softmax_stats = {"wave_tiles": tiles, "first_tile_max_passes": first, "later_rescales": later,
+                         "later_rescale_frac": round(later / max(tiles, 1), 6)}
     cpu, parity = None, None
     if not args.no_cpu_baseline:
         t_cpu = time.perf_counter()
@@ -562,9 +579,10 @@ def main():
         "config": {"workload": w.name, "variant": w.variant, "act": w.act, "B": w.B, "H": w.H, "D": w.D,
                    "window": w.window, "total_q": w.total_q, "total_kv": w.total_kv, "seed": w.seed,
                    "useful_gflop": round(flops / 1e9, 3), "padded_dense_gflop": round(padded / 1e9, 3),
-                   "parallelism": "single GPU"},
+                   "fp8_pv": bool(args.fp8_pv), "parallelism": "single GPU"},
         "device": dev_info,
         "parity": parity,
+        "softmax_stats": softmax_stats,
         "roofline": roof,
         "cpu_baseline": cpu,
     }

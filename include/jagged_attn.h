@@ -126,6 +126,27 @@ typedef struct ja_io {
                              /* word (JA_OK or JA_EOFFSETS) there as well, on   */
                              /* the stream, so it can be read back without      */
                              /* jagged_attn_check; NULL: not written            */
+  uint64_t *softmax_stats;   /* optional device uint64[3], diagnostics: when    */
+                             /* non-NULL the tile-stream softmax (bf16 and MX   */
+                             /* self- and cross-attention) adds, per wave and   */
+                             /* 64-key tile, 1 to [0] (tiles), and 1 to [1] when */
+                             /* it had to find the tile's max because the rows  */
+                             /* had no reference yet (a query block's first     */
+                             /* tile) or to [2] when a later tile moved the     */
+                             /* reference up and rescaled O; other kernels and  */
+                             /* the caller's zeroing: untouched.  Costs atomics. */
+  int32_t fp8_pv;            /* JA_MXFP8_E4M3 only: nonzero runs O += P V on    */
+                             /* the block-scaled fp8 MFMA too ("MXFP8..."       */
+                             /* section: attention in microscaling fp8).  V is  */
+                             /* requantised per tile along the keys (scale of a */
+                             /* 32-key x 32-dim block = the largest of its keys' */
+                             /* MX scales, codes shifted down and rounded to    */
+                             /* nearest even) and P per query and 32 keys       */
+                             /* (scale 2^(floor(log2 max) - 7)); the row sum    */
+                             /* adds the quantised weights.  Less exact than    */
+                             /* the default (V exact in bf16, P in bf16).       */
+                             /* Not available in this version: every call with */
+                             /* it set returns JA_EUNSUPPORTED.                 */
 } ja_io;
 
 /* The forward pass.  Arguments as described above; window is 0 (no window) or

@@ -43,6 +43,8 @@ class JaIo(ctypes.Structure):
         ("ev_stop", ctypes.c_void_p),
         ("max_workgroups", ctypes.c_int32),
         ("status", ctypes.c_void_p),
+        ("softmax_stats", ctypes.c_void_p),
+        ("fp8_pv", ctypes.c_int32),
     ]
 
 

@@ -35,7 +35,8 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             dtype: str = "bf16", scales=None, out: Optional[torch.Tensor] = None,
             workspace: Optional[Workspace] = None, rms_eps: float = 1e-6,
             stream: Optional[torch.cuda.Stream] = None, check: Optional[bool] = None,
-            events=None, max_workgroups: int = 0, status: Optional[torch.Tensor] = None) -> torch.Tensor:
+            events=None, max_workgroups: int = 0, status: Optional[torch.Tensor] = None,
+            softmax_stats: Optional[torch.Tensor] = None, fp8_pv: bool = False) -> torch.Tensor:
     """Jagged GDPA forward.  q [Nq,H,D], k/v [Nk,H,D] on one GPU; offsets int32 [B+1].
 
     dtype "f32"/"bf16": q/k/v of that dtype; "mxfp8": uint8 e4m3 codes with
@@ -53,7 +54,11 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     word into).  ``events=(start, stop)`` are raw hipEvent_t handles the
     attention kernel's dispatch writes its start and end into.
     ``max_workgroups`` caps the attention kernel's grid (0: every resident
-    slot); results do not depend on it."""
+    slot); results do not depend on it.  ``softmax_stats`` (3 int64 on the
+    device, diagnostics) receives the tile-stream softmax's counts: tiles,
+    first-tile max passes, later rescales.  ``fp8_pv`` (MXFP8 self-attention
+    at D = 128) runs O += P V on the fp8 MFMA too, with P and V requantised
+    along the keys."""
     if dtype not in _IN_DTYPES:
         raise ValueError(f"dtype must be one of {list(_IN_DTYPES)}")
     want = _IN_DTYPES[dtype]
@@ -105,8 +110,13 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     io.total_kv = Nk
     io.rms_eps = rms_eps
     io.max_workgroups = max_workgroups
+    io.fp8_pv = 1 if fp8_pv else 0
     if status is not None:
         io.status = status.data_ptr()
+    if softmax_stats is not None:
+        if softmax_stats.dtype != torch.int64 or not softmax_stats.is_cuda or softmax_stats.numel() < 3:
+            raise ValueError("softmax_stats must be an int64 CUDA tensor of 3 elements")
+        io.softmax_stats = softmax_stats.data_ptr()
     if events is not None:
         io.ev_start, io.ev_stop = events   # raw hipEvent_t handles (ints)
     rc = _lib.jagged_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), q_offsets.data_ptr(),

@@ -68,7 +68,10 @@ struct PP {
   // (D = 128, softmax): e4m3 code rows plus one E8M0 scale byte per 32
   // elements; the scores take the codes on the block-scaled fp8 MFMA and V is
   // converted exactly to a bf16 tile in LDS for O += V P.
-  static constexpr bool kMx8 = IN == IN_MX8;
+  static constexpr bool kMx8 = IN == IN_MX8 || IN == IN_MX8P;
+  // IN_MX8P: O += V P on the block-scaled fp8 MFMA as well (P and V
+  // requantised with one E8M0 scale per 32 keys, see the kernel).
+  static constexpr bool kPv8 = IN == IN_MX8P;
   static constexpr int kNT = 64 * kPPWaves;
   static constexpr int kRowBytes = 2 * D;  // one bf16 row in LDS
   static constexpr int kTileBytes = 64 * kRowBytes;
@@ -89,14 +92,18 @@ struct PP {
   static_assert((2 * kSegsLd) % kPPWaves == 0, "tile segments must split evenly over the waves");
   static_assert(!kMx8 || (D == 128 && ACT == ACT_SOFTMAX), "the fp8 tile stream takes D = 128 softmax");
   // MX8 LDS layout: K codes and V codes of tiles s, s+1, s+2 (3 stages each)
-  // with their scale rows (4 bytes per key), the bf16 V of tiles s-1 and s,
-  // and two staged Q blocks (codes + scale rows).  256-byte aligned pieces.
+  // with their scale rows (4 bytes per key), the converted V of tiles s-1 and
+  // s (bf16; fp8 P V: dim-major requantised codes, D rows of 64 bytes, plus 8
+  // scale bytes per tile), and two staged Q blocks (codes + scale rows).
+  // 256-byte aligned pieces.
   static constexpr int kMxKc = 0;
   static constexpr int kMxKs = kMxKc + 3 * kLdTile;
   static constexpr int kMxVc = kMxKs + 3 * 256;
   static constexpr int kMxVs = kMxVc + 3 * kLdTile;
   static constexpr int kMxVb = kMxVs + 3 * 256;
-  static constexpr int kMxQc = kMxVb + 2 * kTileBytes;
+  static constexpr int kMxVtBytes = 64 * D;  // fp8 P V: one requantised V^T tile
+  static constexpr int kMxVts = kMxVb + 2 * kMxVtBytes;
+  static constexpr int kMxQc = kMxVb + (kPv8 ? 2 * kMxVtBytes + 256 : 2 * kTileBytes);
   static constexpr int kMxQs = kMxQc + 2 * kLdTile;
   static constexpr int kMxBytes = kMxQs + 2 * 256;
 };
@@ -288,7 +295,7 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
   using K = PP<D, ACT, IN>;
   constexpr int kQChunks = K::kQChunks, kOTiles = K::kOTiles, kRowBytes = K::kRowBytes;
   constexpr bool kPipe = WMODE == kWinPipe;
-  constexpr bool kMx8 = K::kMx8;
+  constexpr bool kMx8 = K::kMx8, kPv8 = K::kPv8;
   // LDS: a ring of kRing stages of (K, V[, key scales]).  The pipeline instead
   // keeps K in 3 stages (tiles s, s+1, s+2: K_{s-1} is dead once the scores
   // of tile s-1 are taken), V in 4 (s-1 .. s+2) and two Q blocks (the block
@@ -449,6 +456,7 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
     return kPipe ? (s % 3) * K::kTileBytes : (s % K::kRing) * K::kStageBytes;
   };
   auto v_at = [&](int s) __attribute__((always_inline)) {
+    if constexpr (kPv8) return K::kMxVb + (s & 1) * K::kMxVtBytes;
     if constexpr (kMx8) return K::kMxVb + (s & 1) * K::kTileBytes;
     return kPipe ? kPipeV + (s % 4) * K::kTileBytes : (s % K::kRing) * K::kStageBytes + K::kTileBytes;
   };
@@ -531,7 +539,12 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
     for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
   float m = -__builtin_huge_valf(), l = 0.f;
   f32x16 sc[2];      // score tile: S^T halves (keys 32*st + 16*(i/8) + 8g + i%8)
-  bf16x8 pb[4];      // P of the previous tile, 16-key chunks kc
+  bf16x8 pb[kPv8 ? 1 : 4];  // P of the previous tile, 16-key chunks kc
+  // fp8 P V: P of the previous tile as e4m3 codes, the fp8 MFMA's B operand
+  // (bytes 0-15: the keys of sc[0], 16-31: those of sc[1], in register order),
+  // and its two scale bytes (keys 0-31, 32-63)
+  i32x8 pq;
+  unsigned psc = 0;
   int pv_k = c0.k;   // item of tile s-1
   bool pv_last = false;
   bool pv_act = true;  // this wave computed tile s-1 (block windows)
@@ -570,17 +583,28 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
       }
       // p = 2^(s c - m c) into pb; returns this lane's sum of the bf16 p
       // (the weights P V uses), two at a time on the dot unit.
+      // (fp8 P V: p in fp32 into pf; the sum is of the fp32 p, for the
+      // reference check only -- l takes the sum of the quantised weights)
+      float pf[kPv8 ? 32 : 1];
       auto exps = [&](float mc) __attribute__((always_inline)) {
         float part[4] = {0.f, 0.f, 0.f, 0.f};  // (four chains)
+        if constexpr (kPv8) {
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc)
-#pragma unroll
-          for (int j = 0; j < 8; j += 2) {
-            pb[kc][j] = (__bf16)fast_exp2(fmaf(sc[kc >> 1][8 * (kc & 1) + j], c2s, -mc));
-            pb[kc][j + 1] = (__bf16)fast_exp2(fmaf(sc[kc >> 1][8 * (kc & 1) + j + 1], c2s, -mc));
-            const bf16x2v pr = {pb[kc][j], pb[kc][j + 1]};
-            part[j / 2] = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, part[j / 2], false);
+          for (int i = 0; i < 32; ++i) {
+            pf[i] = fast_exp2(fmaf(sc[i >> 4][i & 15], c2s, -mc));
+            part[i & 3] += pf[i];
           }
+        } else {
+#pragma unroll
+          for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+            for (int j = 0; j < 8; j += 2) {
+              pb[kc][j] = (__bf16)fast_exp2(fmaf(sc[kc >> 1][8 * (kc & 1) + j], c2s, -mc));
+              pb[kc][j + 1] = (__bf16)fast_exp2(fmaf(sc[kc >> 1][8 * (kc & 1) + j + 1], c2s, -mc));
+              const bf16x2v pr = {pb[kc][j], pb[kc][j + 1]};
+              part[j / 2] = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, part[j / 2], false);
+            }
+        }
         return (part[0] + part[1]) + (part[2] + part[3]);
       };
       // Lazy reference max: the exponentials are taken against the current
@@ -594,7 +618,15 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
       const bool fresh = __any(m == -__builtin_huge_valf());
       float part = 0.f;
       if (!fresh) part = exps(m * c2s);
-      if (fresh || __any(!(part <= kPartCap))) {
+      const bool moved = fresh || __any(!(part <= kPartCap));
+      if (a.stats) {
+        // diagnostics: tiles, first-tile max passes, later rescales (per wave and tile)
+        if (lane == 0) {
+          atomicAdd(a.stats, 1ull);
+          if (moved) atomicAdd(a.stats + (fresh ? 1 : 2), 1ull);
+        }
+      }
+      if (moved) {
         float mt = -__builtin_huge_valf();
 #pragma unroll
         for (int st = 0; st < 2; ++st)
@@ -610,6 +642,37 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
           for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
         m = m_new;
         part = exps(m == -__builtin_huge_valf() ? 0.f : m * c2s);
+      }
+      if constexpr (kPv8) {
+        // P to e4m3 with one E8M0 scale per 32 keys (row, key block kb = the
+        // registers of sc[kb], shared by the two lane halves): 2^(floor(log2
+        // max) - 7), so every scaled weight is below 256 (no saturation
+        // needed); l adds the quantised weights, so the weights O uses are
+        // normalised exactly.
+        float lq = 0.f;
+        psc = 0;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          float amax = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) amax = fmaxf(amax, pf[16 * kb + i]);
+          amax = max_halves(amax);
+          const int sb = max(int((__float_as_uint(amax) >> 23) & 0xFFu) - 7, 0);
+          const float scl = sb ? __uint_as_float(unsigned(sb) << 23) : __uint_as_float(0x00400000u);
+#pragma unroll
+          for (int wd = 0; wd < 4; ++wd) {
+            const float* pw = pf + 16 * kb + 4 * wd;
+            s16x2 cw = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(s16x2{0, 0}, pw[0], pw[1], scl, false);
+            cw = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(cw, pw[2], pw[3], scl, true);
+            const unsigned u = __builtin_bit_cast(unsigned, cw);
+            pq[4 * kb + wd] = int(u);
+            const f32x2 d0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(u, scl, false);
+            const f32x2 d1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(u, scl, true);
+            lq += (d0[0] + d0[1]) + (d1[0] + d1[1]);
+          }
+          psc |= unsigned(sb) << (8 * kb);
+        }
+        part = lq;
       }
       l += part;
     } else {
@@ -686,7 +749,33 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
       // soon as it can take one.
       __builtin_amdgcn_s_setprio(2);
       if (s > 0) {
-        if (WMODE == kWinNone || pv_act) {
+        if (kPv8 && (WMODE == kWinNone || pv_act)) {
+          // fp8 O^T += V^T P^T: one 32x32x64 MFMA per output tile t over all 64
+          // keys.  A row r is head dim dim_perm(t, r) (the output layout of
+          // the bf16 product), its bytes the requantised V^T codes of the keys
+          // in the order of P's registers; lane half g gives the scale of key
+          // block g of its row, P's scale of key block g.
+          const unsigned char* vt = ring + v_at(s - 1);
+          const unsigned vsw = *reinterpret_cast<const unsigned*>(ring + K::kMxVts + ((s - 1) & 1) * 8 + 4 * g);
+          const int psg = int((psc >> (8 * g)) & 0xFFu);
+          i32x8 aop[kOTiles];
+#pragma unroll
+          for (int t = 0; t < kOTiles; ++t) {
+            const int d = dim_perm<D>(t, l32);
+            const u32x4 w0 = *reinterpret_cast<const u32x4*>(vt + d * 64 + 16 * (g ^ vt_swz(d)));
+            const u32x4 w1 = *reinterpret_cast<const u32x4*>(vt + d * 64 + 16 * ((2 + g) ^ vt_swz(d)));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              aop[t][j] = int(w0[j]);
+              aop[t][4 + j] = int(w1[j]);
+            }
+          }
+#pragma unroll
+          for (int t = 0; t < kOTiles; ++t) {
+            const int sa = int((vsw >> (8 * (dim_perm<D>(t, l32) / kMxBlock))) & 0xFFu);
+            o[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop[t], pq, o[t], 0, 0, 0, sa, 0, psg);
+          }
+        } else if (WMODE == kWinNone || pv_act) {
           // 4*kOTiles MFMAs (16-key chunk kc, output tile t), the V^T operand
           // read kAhead MFMAs early: one wave issues them alone, so the LDS
           // transpose-read latency is not hidden by a second wave.
@@ -871,7 +960,55 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
         }
       }
     }
-    if constexpr (kMx8) {
+    if constexpr (kPv8) {
+      // V of tile s (landed at the top of this step) requantised along the
+      // keys for the fp8 O += V P, into the V^T slot the next step reads.
+      // Wave w takes keys 32 kb .. +32 (kb = w / 4) and head dims 32 b .. +32
+      // (b = w % 4); lane (kg, dg) 4 keys x 4 dims.  The new scale of (kb, b)
+      // is the largest of the 32 keys' MX scales of block b, so a code only
+      // moves down by the difference of exponents (exact unless it then falls
+      // below e4m3's smallest subnormal), rounded to nearest even.  A 4 x 4
+      // byte transpose turns 4 key rows into 4 dim rows of 4 keys each.
+      const int kb = wave >> 2, b = wave & 3, kg = lane & 7, dg = lane >> 3;
+      const unsigned char* vcs = ring + vc_at(s);
+      const unsigned char* vss = ring + K::kMxVs + (s % 3) * 256;
+      unsigned r[4];
+      int e[4], emax = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int k = 32 * kb + 4 * kg + i;
+        r[i] = *reinterpret_cast<const unsigned*>(vcs + k * D + 16 * ((2 * b + (dg >> 2)) ^ swz_c<D>(k)) + 4 * (dg & 3));
+        e[i] = int((*reinterpret_cast<const unsigned*>(vss + 4 * k) >> (8 * b)) & 0xFFu);
+        emax = max(emax, e[i]);
+      }
+      emax = max(emax, __shfl_xor(emax, 1, 64));
+      emax = max(emax, __shfl_xor(emax, 2, 64));
+      emax = max(emax, __shfl_xor(emax, 4, 64));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float down = __uint_as_float(unsigned(max(127 - (emax - e[i]), 0)) << 23);  // 2^(e - emax)
+        const f32x2 x0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(r[i], down, false);
+        const f32x2 x1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(r[i], down, true);
+        s16x2 cw = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(s16x2{0, 0}, x0[0], x0[1], 1.0f, false);
+        cw = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(cw, x1[0], x1[1], 1.0f, true);
+        r[i] = __builtin_bit_cast(unsigned, cw);
+      }
+      // byte j of r[i] is (key i, dim j) -> col[j] byte i
+      const unsigned lo01 = __builtin_amdgcn_perm(r[1], r[0], 0x05010400u), hi01 = __builtin_amdgcn_perm(r[1], r[0], 0x07030602u);
+      const unsigned lo23 = __builtin_amdgcn_perm(r[3], r[2], 0x05010400u), hi23 = __builtin_amdgcn_perm(r[3], r[2], 0x07030602u);
+      const unsigned col[4] = {__builtin_amdgcn_perm(lo23, lo01, 0x05040100u), __builtin_amdgcn_perm(lo23, lo01, 0x07060302u),
+                               __builtin_amdgcn_perm(hi23, hi01, 0x05040100u), __builtin_amdgcn_perm(hi23, hi01, 0x07060302u)};
+      // keys 32 kb + 16 a + 8 g' + r sit at position 32 kb + 16 g' + 8 a + r of a
+      // V^T row (P's register order): bits 1 and 2 of the key group swap
+      const int pos = 32 * kb + 4 * ((kg & 1) | ((kg & 2) << 1) | ((kg & 4) >> 1));
+      unsigned char* vt = ring + v_at(s);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = 32 * b + 4 * dg + i;
+        *reinterpret_cast<unsigned*>(vt + d * 64 + 16 * ((pos >> 4) ^ vt_swz(d)) + (pos & 15)) = col[i];
+      }
+      if (lane == 0) ring[K::kMxVts + (s & 1) * 8 + 4 * kb + b] = (unsigned char)emax;
+    } else if constexpr (kMx8) {
       // V of tile s (landed at the top of this step) to bf16, exactly (4-bit
       // e4m3 significands times a power of two), by every thread: 16 codes of
       // one row each, into the bf16 slot O += V P reads in the next step.
@@ -930,7 +1067,9 @@ hipError_t launch_d(int act, bool cross, dim3 gd, dim3 bd, hipStream_t st, const
   return launch_none<D, ACT_GELU>(cross, gd, bd, st, a, tm);
 }
 
-// MX8 inputs (D = 128, softmax self-attention): full, or block windows of up to four blocks.
+// MX8 inputs (D = 128, softmax self-attention): full, or block windows of up
+// to four blocks.  (The IN_MX8P form -- P V on the fp8 MFMA -- is not
+// instantiated: it faulted the GPU on its first run, cause not found.)
 hipError_t launch_mx8(dim3 gd, dim3 bd, hipStream_t st, const AttnArgs& a, const KTiming& tm) {
   if (a.window_blocks > 0)
     return launch1(attn_pp_kernel<128, ACT_SOFTMAX, kWinPipe, false, IN_MX8>, gd, bd, st, a, tm);
@@ -945,11 +1084,12 @@ bool pp_takes_mx8(int D, int act, bool self, int window_blocks) {
   return D == 128 && act == ACT_SOFTMAX && self && window_blocks <= kPipePairs;
 }
 
-hipError_t launch_attn_pp(int D, int act, bool cross, bool mx8, const AttnArgs& a, int num_cu, int64_t max_items,
+// in: IN_BF16 or IN_MX8 (the MX form only where pp_takes_mx8 holds).
+hipError_t launch_attn_pp(int D, int act, bool cross, int in, const AttnArgs& a, int num_cu, int64_t max_items,
                           int64_t grid_cap, const KTiming& tm, hipStream_t st) {
   // One workgroup per CU (the tile ring takes most of the LDS), a multiple of the XCD count.
   const dim3 gd(static_cast<unsigned>(persistent_grid(num_cu, max_items, grid_cap))), bd(64 * kPPWaves);
-  if (mx8) return launch_mx8(gd, bd, st, a, tm);
+  if (in != IN_BF16) return launch_mx8(gd, bd, st, a, tm);
   if (D == 32) return launch_d<32>(act, cross, gd, bd, st, a, tm);
   if (D == 64) return launch_d<64>(act, cross, gd, bd, st, a, tm);
   return launch_d<128>(act, cross, gd, bd, st, a, tm);

@@ -19,8 +19,9 @@ constexpr int kPmaRows = 32;      // query rows per key-split work item
 // GELU scores: tanh form (exp + rcp) or the ALU-only polynomial (ja_gelu_poly.h).
 enum Act { ACT_SOFTMAX = 0, ACT_GELU = 1, ACT_GELU_POLY = 2 };
 // IN_MX: MX-fp8 decoded to bf16 on load; IN_MX8 (D = 128): fp8 codes stay fp8
-// for block-scaled fp8 MFMA on QK^T, V is converted to bf16 in LDS.
-enum In { IN_F32 = 0, IN_BF16 = 1, IN_MX = 2, IN_MX8 = 3 };
+// for block-scaled fp8 MFMA on QK^T, V is converted to bf16 in LDS; IN_MX8P:
+// as IN_MX8, with P V on the fp8 MFMA too (P and V requantised along the keys).
+enum In { IN_F32 = 0, IN_BF16 = 1, IN_MX = 2, IN_MX8 = 3, IN_MX8P = 4 };
 
 // ---------------------------------------------------------------------------
 // Workspace layout (caller-owned device memory; every section 256-B aligned)
@@ -114,6 +115,7 @@ struct AttnArgs {
   int dealt;          // items come sorted by cost, most first, and are dealt in alternating rounds
   float score_scale;  // softmax: log2(e)/sqrt(D); GELU: 1/sqrt(D)
   float eps;
+  unsigned long long* stats;  // optional softmax counters (tile stream): tiles, max passes, rescales
 };
 
 // Events that time one kernel from its own dispatch packet (hipExtLaunchKernel

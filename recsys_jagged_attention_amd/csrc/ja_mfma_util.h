@@ -108,6 +108,13 @@ __device__ __forceinline__ float e8m0_to_float(unsigned e) {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// 16-byte chunk swizzle of a requantised V^T tile (head-dim rows of 64 key
+// bytes): the 16 lanes of an fp8 P V operand read -- head dims r%4 + 4*bit2 +
+// 64*bit6 of dim_perm -- land on 16 distinct bank groups.
+__device__ __forceinline__ int vt_swz(int d) { return (((d >> 6) & 1) << 1) | ((d >> 2) & 1); }
 
 __device__ __forceinline__ unsigned lds_addr_of(const void* p) {
   return static_cast<unsigned>(reinterpret_cast<uintptr_t>(

@@ -71,7 +71,7 @@ hipError_t launch_attn_mfma(int, int, int, int, const AttnArgs&, int num_cu, int
 bool pp_takes_mx8(int D, int act, bool self, int window_blocks) {
   return D == 128 && act == 0 && self && window_blocks <= 4;
 }
-hipError_t launch_attn_pp(int, int, bool, bool, const AttnArgs&, int num_cu, int64_t, int64_t, const KTiming&,
+hipError_t launch_attn_pp(int, int, bool, int, const AttnArgs&, int num_cu, int64_t, int64_t, const KTiming&,
                           hipStream_t) {
   expect_cus(num_cu);
   return hipSuccess;

@@ -10,6 +10,8 @@ from recsys_jagged_attention_amd.inputs import cast_values, device_tensors
 # max|O_gpu - O_ref| <= TOL * max|O_ref|  (fp32 / bf16 / MXFP8 against the
 # oracle run on the dequantised inputs)
 TOL = {"f32": 1e-5, "bf16": 1e-2, "mxfp8": 5e-2}
+# fp8 P V (MXFP8 option): P and V requantised along the keys; the same bound
+# as the MXFP8 path, against the oracle on the dequantised inputs
 # JA_GELU_POLY approximates gelu_tanh: the oracle evaluates the exact tanh form
 # and the bound grows by the activation error, |gelu_poly - gelu_tanh| <= 5e-4
 # (tests/test_gelu_poly.py), which moves O = (1/Lk) sum_j g_j v_j by at most

@@ -66,9 +66,10 @@ def test_workspace_grows_with_key_split_partials():
 
 
 def call(B=2, H=1, D=32, variant=0, act=0, window=0, dtype=0, tq=10, tk=10, ws_bytes=1 << 20,
-         ptr=4096, io=True, scales=False):
+         ptr=4096, io=True, scales=False, fp8_pv=0):
     j = _lib.JaIo()
     j.dtype = dtype
+    j.fp8_pv = fp8_pv
     j.total_q, j.total_kv = tq, tk
     j.workspace = 1 << 20
     j.workspace_bytes = ws_bytes
@@ -94,6 +95,8 @@ def test_fwd_host_validation():
     assert call(ws_bytes=16) == _lib.JA_EWORKSPACE
     assert call(ptr=4100) == _lib.JA_EINVAL                            # misaligned
     assert call(dtype=_lib.JA_MXFP8_E4M3, scales=True, ws_bytes=16) == _lib.JA_EWORKSPACE
+    assert call(fp8_pv=1) == _lib.JA_EUNSUPPORTED                      # fp8 P V: switched off
+    assert call(fp8_pv=1, dtype=_lib.JA_MXFP8_E4M3, scales=True, D=128) == _lib.JA_EUNSUPPORTED
 
 
 def test_bwd_host_validation():

@@ -426,3 +426,77 @@ def test_mxfp8_pipeline_many_items():
     w = adhoc("mx_pipe_many", "self", "softmax", "mxfp8", L, L, 40, 128, window=256, seed=84)
     log(f"mxfp8 pipeline many items: N={w.total_q}")
     full_parity(w, max_workgroups=16)
+
+
+@pytest.mark.parametrize("name,scale", [("block_window", 0.2), ("mxfp8_window", 0.2), ("full_self", 0.1)])
+def test_softmax_stats_count_every_tile(name, scale):
+    """The tile-stream softmax's diagnostic counters: every (wave, key tile) the
+    schedule assigns is processed exactly once, and the reference max is found
+    once per wave and query block (a block pipeline's block, or a 256-row item
+    without a window); later rescales are reported, not bounded."""
+    w = make_workload(name, scale=scale)
+    q, k, v, qo, ko, scales = device_tensors(w, "cuda")
+    st = torch.zeros(3, dtype=torch.int64, device="cuda")
+    forward(q, k, v, qo, ko, variant=w.variant, act=w.act, window=w.window, dtype=w.dtype, scales=scales,
+            softmax_stats=st, check=True)
+    torch.cuda.synchronize()
+    tiles, first, later = (int(x) for x in st.cpu())
+    lens = np.diff(w.q_offsets)
+    want_tiles = want_first = 0
+    for L in lens.tolist():
+        nblk = -(-L // 64)
+        if w.window:  # pipeline: a wave pair per 64-row block, min(nb, b + 1) tiles each
+            nb = w.window // 64
+            want_tiles += 2 * w.H * sum(min(nb, b + 1) for b in range(nblk))
+            want_first += 2 * w.H * nblk
+        else:         # 256-row items, 8 waves each walk all of the sample's tiles
+            items = -(-L // 256)
+            want_tiles += 8 * w.H * items * nblk
+            want_first += 8 * w.H * items
+    log(f"{name}: tiles {tiles} first-tile max passes {first} later rescales {later} "
+        f"({later / max(tiles, 1):.2e} of tiles)")
+    assert tiles == want_tiles and first == want_first
+
+
+@pytest.mark.skip(reason="fp8 P V is switched off (JA_EUNSUPPORTED): its kernel faulted the GPU on its "
+                         "first run and the cause has not been found")
+@pytest.mark.parametrize("name", ["mxfp8_window", "mxfp8_full"])
+def test_fp8_pv_full_size_every_element(name):
+    """fp8 P V (P and V requantised along the keys, O += V P on the
+    block-scaled fp8 MFMA) on the MXFP8 workloads at full size, every element
+    against the oracle on the dequantised inputs, at the MXFP8 bound."""
+    w = make_workload(name)
+    log(f"fp8 P V full size {name}: N={w.total_q}")
+    err = full_parity(w, fp8_pv=True)
+    log(f"  rel err {err:.3e}")
+
+
+@pytest.mark.skip(reason="fp8 P V is switched off (JA_EUNSUPPORTED): its kernel faulted the GPU on its "
+                         "first run and the cause has not been found")
+@pytest.mark.parametrize("window", [0, 64, 128, 192, 256])
+def test_fp8_pv_long_samples(window):
+    """fp8 P V on samples of several runs and items, ragged tails (masked keys
+    inside a quantisation block) and a one-key sample."""
+    L = [1500, 2049, 700, 64, 3001, 257, 1, 33]
+    w = adhoc("fp8pv_long", "self", "softmax", "mxfp8", L, L, 3, 128, window=window, seed=window + 61)
+    log(f"fp8 P V W={window}: N={w.total_q}")
+    full_parity(w, fp8_pv=True)
+
+
+@pytest.mark.skip(reason="fp8 P V is switched off (JA_EUNSUPPORTED): its kernel faulted the GPU on its "
+                         "first run and the cause has not been found")
+def test_fp8_pv_block_scales_far_apart():
+    """V rows whose 32-element blocks carry scales 2^-5 .. 2^5 apart: the
+    requantised V keeps the largest key scale of each block, the others shift
+    down; and a sample whose weights concentrate on one key (Q aligned with
+    one key row) -- the quantised weights still sum to the row's normaliser."""
+    D = 128
+    L = [70, 300, 129]
+    qo, ko, q, k, v = random_jagged(95, L, L, 2, D)
+    s_ = np.array([-5, 3, 5, -2], dtype=np.float64)
+    v = (v * np.repeat(2.0 ** s_, D // 4).astype(np.float32)
+         * (2.0 ** np.random.default_rng(3).integers(-4, 5, size=(v.shape[0], 1, 1))).astype(np.float32))
+    q[:70] = 4.0 * k[5]  # sample 0: every query close to key 5
+    w = Workload("fp8pv_spread", "self", "softmax", "mxfp8", len(L), 2, D, 0, qo, ko, q, k, v, 95)
+    w.mx = {n: mx_encode_e4m3(x) for n, x in (("q", q), ("k", k), ("v", v))}
+    full_parity(w, fp8_pv=True)
