@@ -414,6 +414,8 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 5 times (the reference "
                          "for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE counters) and exit")
+    ap.add_argument("--event-every", type=int, default=5,
+                    help="time the attention kernel (dispatch events) on every N-th timed step")
     ap.add_argument("--fp8-pv", action="store_true",
                     help="MXFP8 workloads: O += P V on the fp8 MFMA too (P and V requantised along the keys)")
     ap.add_argument("--backward", action="store_true",
@@ -482,8 +484,13 @@ def main():
     wsp = Workspace(dev)
     ev = HipEvents()
     K, W = args.steps, args.warmup
-    starts = [ev.create() for _ in range(K)]
-    stops = [ev.create() for _ in range(K)]
+    # the attention kernel's dispatch writes start/stop events on every
+    # `event_every`-th timed step (each timed dispatch costs a few us of
+    # stream time, so timing every step would slow the steps it measures)
+    E = max(1, args.event_every)
+    timed = list(range(0, K, E))
+    starts = {i: ev.create() for i in timed}
+    stops = {i: ev.create() for i in timed}
 
     def step(i, events=None):
         qq, kk, vv, ss = sets[i % n_copies]
@@ -498,15 +505,16 @@ def main():
     log(f"[bench] warmup done ({W} steps), timing {K} steps over {n_copies} input copies")
     t0 = time.perf_counter()
     for i in range(K):
-        step(i, (starts[i], stops[i]))
+        step(i, (starts[i], stops[i]) if i in starts else None)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    # kernel durations (start and end stamps of each attention dispatch), and
-    # the step period: the time between the ends of consecutive steps'
-    # attention kernels (plan, gaps and attention of one step, back to back)
-    kern_ms = np.array([ev.elapsed_ms(starts[i], stops[i]) for i in range(K)])
-    period_ms = np.array([ev.elapsed_ms(stops[i - 1], stops[i]) for i in range(1, K)])
-    for e in starts + stops:
+    # kernel durations (start and end stamps of the sampled attention
+    # dispatches), and the step period: the time between the ends of two
+    # sampled steps' attention kernels over the steps between them (every
+    # kernel of a step, back to back)
+    kern_ms = np.array([ev.elapsed_ms(starts[i], stops[i]) for i in timed])
+    period_ms = np.array([ev.elapsed_ms(stops[a], stops[b]) / (b - a) for a, b in zip(timed, timed[1:])])
+    for e in list(starts.values()) + list(stops.values()):
         ev.destroy(e)
     ms_per_step = (t1 - t0) * 1e3 / K
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -538,6 +546,16 @@ def main():
     log(f"[bench] {ms_per_step * 1e3:.1f} us/step, kernel {kern_avg_s * 1e6:.1f} us, "
         f"{value:.1f} useful TFLOPS, {roof['achieved']} {roof['unit']} ({roof['frac'] * 100:.1f}% of peak)")
 
+    # launch diagnostics (after the timed region): the host's time to enqueue K
+    # steps, and the time per step of K steps launched without events
+    t_e0 = time.perf_counter()
+    for i in range(K):
+        step(i)
+    t_e1 = time.perf_counter()
+    torch.cuda.synchronize()
+    t_e2 = time.perf_counter()
+    launch_diag = {"host_enqueue_us_per_step": round((t_e1 - t_e0) * 1e6 / K, 2),
+                   "no_event_us_per_step": round((t_e2 - t_e0) * 1e6 / K, 2)}
     # one more (untimed) call with the softmax's diagnostic counters: how often
     # the lazy reference max had to move after a query block's first tile
     softmax_stats = None
@@ -573,9 +591,10 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "pct_bf16_peak": round(100 * value / PEAK_TFLOPS["bf16"], 2),
-        "step_us": {"median": round(float(np.median(period_ms)) * 1e3, 2) if K > 1 else None,
-                    "min": round(float(np.min(period_ms)) * 1e3, 2) if K > 1 else None,
-                    "p90": round(float(np.percentile(period_ms, 90)) * 1e3, 2) if K > 1 else None},
+        "step_us": {"median": round(float(np.median(period_ms)) * 1e3, 2) if len(period_ms) else None,
+                    "min": round(float(np.min(period_ms)) * 1e3, 2) if len(period_ms) else None,
+                    "p90": round(float(np.percentile(period_ms, 90)) * 1e3, 2) if len(period_ms) else None,
+                    "kernel_events_every": E},
         "config": {"workload": w.name, "variant": w.variant, "act": w.act, "B": w.B, "H": w.H, "D": w.D,
                    "window": w.window, "total_q": w.total_q, "total_kv": w.total_kv, "seed": w.seed,
                    "useful_gflop": round(flops / 1e9, 3), "padded_dense_gflop": round(padded / 1e9, 3),
@@ -583,6 +602,7 @@ def main():
         "device": dev_info,
         "parity": parity,
         "softmax_stats": softmax_stats,
+        "launch": launch_diag,
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -33,6 +33,9 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 int pp_rows();
 int pp_pipe_rows();
 int pp_pipe_max_blocks();
+int pp_item_cache();
+int pp_enum_max_runs();
+int pp_enum_max_offsets();
 
 namespace {
 
@@ -227,7 +230,20 @@ int fwd_impl(const void* q, const void* k, const void* v, const int32_t* q_offse
     pa.krms_eps = rms_eps;
     pa.krms_out = ksc;
   }
-  if (launch_plan(pa, stream) != hipSuccess) return JA_EHIP;
+  // The softmax tile stream enumerates its own items (no plan launch) when
+  // every sample fits one thread of the workgroup, a sample has at most
+  // pp_enum_max_runs() runs of equal cost, and each workgroup's items fit its
+  // LDS item cache.
+  const int64_t cap = io.max_workgroups;
+  bool inplan = false;
+  if (p.shape == kShapePingPong && act == JA_SOFTMAX && B + 1 <= pp_enum_max_offsets()) {
+    const int span = pa.window_blocks > 0 ? (pa.window_blocks - 1) * kBlock
+                                          : (pa.window_tokens > 0 ? pa.window_tokens - 1 : 0);
+    const int64_t qt_mid = cdiv(span, p.bm);
+    const int64_t grid = persistent_grid(num_cu, p.ws.max_items, cap);
+    inplan = qt_mid + 2 <= pp_enum_max_runs() && p.ws.max_items <= int64_t(pp_item_cache()) * grid;
+  }
+  if (!inplan && launch_plan(pa, stream) != hipSuccess) return JA_EHIP;
 
   AttnArgs aa{};
   aa.q = q;
@@ -253,12 +269,18 @@ int fwd_impl(const void* q, const void* k, const void* v, const int32_t* q_offse
   aa.eps = rms_eps;
   aa.kscale = ksc;
   aa.stats = reinterpret_cast<unsigned long long*>(io.softmax_stats);
+  aa.inplan = inplan ? 1 : 0;
+  aa.B = B;
+  aa.bm = p.bm;
+  aa.self_check = pa.self_check;
+  aa.total_q = io.total_q;
+  aa.total_kv = io.total_kv;
+  aa.status_out = io.status;
   const float inv_sqrt_d = 1.0f / std::sqrt(float(D));
   aa.score_scale = act == JA_SOFTMAX ? inv_sqrt_d * 1.4426950408889634f : inv_sqrt_d;
 
   // (the events are written by the attention kernel's own dispatch)
   const KTiming tm{reinterpret_cast<hipEvent_t>(io.ev_start), reinterpret_cast<hipEvent_t>(io.ev_stop)};
-  const int64_t cap = io.max_workgroups;
   hipError_t e;
   if (p.shape == kShapeF32) {
     // (a grid-stride loop over the items: capped like the persistent kernels)

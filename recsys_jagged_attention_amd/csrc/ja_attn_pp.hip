@@ -37,6 +37,7 @@
 // kernel (ja_attn_mfma.hip).
 #include "ja_device.h"
 #include "ja_mfma_util.h"
+#include "ja_sched.h"
 #include "jagged_attn.h"
 
 namespace ja {
@@ -285,6 +286,193 @@ __device__ __forceinline__ void advance(const PPCtx& c, Cur& cu, Src& src, int w
   cu.t = 0;  // past the end: tile 0 of the last item visited
 }
 
+// ---- The tile stream's own work enumeration (no plan launch) --------------
+// Every workgroup reads the B+1 offsets, checks them, and computes the same
+// item order the plan kernel's counting sort gives in effect -- items sorted
+// by the key tiles they walk, most first -- with a deterministic order inside
+// a cost bucket (by wave, then lane = sample, then run), so that every
+// workgroup finds the same positions without talking to the others.  It keeps
+// the records of its own positions (dealt in alternating rounds) in the LDS
+// item cache and writes them to the workspace item list; workgroup 0 writes
+// the header.  One thread per sample (B + 1 <= 512 offsets); a sample has at
+// most kMaxRuns runs of equal cost (the host checks the window against bm).
+constexpr int kMaxRuns = 4;
+
+// Exclusive prefix sum over the wave's 64 lanes on the DPP network (no LDS
+// trips): row_shr 1, 2, 4, 8 scan each row of 16 lanes (a lane without a
+// source adds 0), row_bcast 15 and 31 carry the row totals into the rows above.
+__device__ __forceinline__ int wave_excl_scan(int x) {
+  int v = x;
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 (rows 1, 3)
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 (rows 2, 3)
+  return v - x;
+}
+
+// Returns the number of items of the call (every workgroup gets the same), or
+// -1 if the offsets are invalid.  `lds` is scratch of at least
+// (9 * kCostBuckets + 16) ints (the tile ring, not yet in use).
+__device__ int enumerate_items(const AttnArgs& a, int* lds, WorkItem* cache, int G, int pos) {
+  const int tid = threadIdx.x, wave = tid >> 6;
+  int* s_cnt = lds;                          // [8][kCostBuckets]: item counts per wave, then wave bases
+  int* s_start = lds + 8 * kCostBuckets;     // [kCostBuckets]: first position of each bucket
+  int* s_wsum = s_start + kCostBuckets;      // [8 + 1]: block scan of the bucket totals
+  // this thread's sample: offsets checked as the plan kernel checks them (the
+  // loads are issued first, so that their latency covers the zeroing below)
+  const int b = tid;
+  int q = 0, k = 0, q1 = 0, k1 = 0;
+  if (b <= a.B) {
+    q = a.qo[b];
+    k = a.ko[b];
+    if (b < a.B) {
+      q1 = a.qo[b + 1];
+      k1 = a.ko[b + 1];
+    }
+  }
+  for (int i = tid; i < 8 * kCostBuckets; i += kPPWaves * 64) s_cnt[i] = 0;
+  int bad = 0, qb = 0, lq = 0, kb = 0, lk = 0;
+  if (b <= a.B) {
+    if (b == 0 && (q != 0 || k != 0)) bad = 1;
+    if (b == a.B && (q != a.total_q || k != a.total_kv)) bad = 1;
+    if (a.self_check && q != k) bad = 1;
+    if (b < a.B) {
+      if (q1 < q || k1 < k) bad = 1;
+      qb = q;
+      lq = q1 - q;
+      kb = k;
+      lk = k1 - k;
+    }
+  }
+  if (__syncthreads_or(bad)) {
+    if (blockIdx.x == 0 && tid == 0) {
+      WsHeader* hdr = const_cast<WsHeader*>(a.hdr);
+      hdr->items_off = int32_t(reinterpret_cast<const char*>(a.items) - reinterpret_cast<const char*>(a.hdr));
+      hdr->n_items = 0;
+      hdr->n_slots = 0;
+      hdr->status = JA_EOFFSETS;
+      if (a.status_out) *a.status_out = JA_EOFFSETS;
+    }
+    return -1;
+  }
+  // runs of equal cost: (bucket, items = run x H, first query tile, run length)
+  int eb[kMaxRuns], en[kMaxRuns], eq[kMaxRuns], er[kMaxRuns];
+  int ne = 0;
+  {
+    const int nqt = (b < a.B && lq > 0) ? (lq + a.bm - 1) / a.bm : 0;
+    int qt = 0;
+#pragma unroll
+    for (int e = 0; e < kMaxRuns; ++e) {
+      eb[e] = en[e] = eq[e] = er[e] = 0;
+      if (qt < nqt) {
+        const int run = cost_run(a, qt, nqt);
+        eb[e] = cost_bucket(a, qt, lq, lk);
+        en[e] = run * a.H;
+        eq[e] = qt;
+        er[e] = run;
+        atomicAdd(&s_cnt[wave * kCostBuckets + eb[e]], en[e]);
+        ne = e + 1;
+        qt += run;
+      }
+    }
+  }
+  __syncthreads();
+  // per bucket: the waves' exclusive bases (in place) and the total; then the
+  // buckets' start positions, most tiles first (thread t: descending ranks 2t, 2t+1)
+  int tot[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int beta = kCostBuckets - 1 - (2 * tid + j);
+    int run = 0;
+#pragma unroll
+    for (int w = 0; w < kPPWaves; ++w) {
+      const int c = s_cnt[w * kCostBuckets + beta];
+      s_cnt[w * kCostBuckets + beta] = run;
+      run += c;
+    }
+    tot[j] = run;
+  }
+  {
+    const int pair = tot[0] + tot[1];
+    const int inc = wave_excl_scan(pair) + pair;
+    if ((tid & 63) == 63) s_wsum[wave] = inc;
+    __syncthreads();
+    int wbase = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < kPPWaves; ++w) {
+      const int t = s_wsum[w];
+      if (w < wave) wbase += t;
+      all += t;
+    }
+    const int excl = wbase + inc - pair;
+    s_start[kCostBuckets - 1 - 2 * tid] = excl;
+    s_start[kCostBuckets - 2 - 2 * tid] = excl + tot[0];
+    if (tid == 0) s_wsum[kPPWaves] = all;
+  }
+  __syncthreads();
+  const int n_all = s_wsum[kPPWaves];
+  // positions of this lane's runs: bucket start + wave base + the items of
+  // lower lanes (and earlier runs of this lane) in the same bucket, one
+  // bucket of the wave at a time
+  int pe[kMaxRuns];
+#pragma unroll
+  for (int e = 0; e < kMaxRuns; ++e) pe[e] = e < ne ? s_start[eb[e]] + s_cnt[wave * kCostBuckets + eb[e]] : 0;
+  unsigned pend = (1u << ne) - 1u;
+  while (true) {
+    const unsigned long long bal = __ballot(pend != 0u);
+    if (bal == 0ull) break;
+    int fb = -1;
+#pragma unroll
+    for (int e = kMaxRuns - 1; e >= 0; --e)
+      if ((pend >> e) & 1u) fb = eb[e];
+    const int beta = __builtin_amdgcn_readlane(fb, int(__builtin_ctzll(bal)));
+    int mine = 0, off[kMaxRuns];
+    unsigned took = 0u;
+#pragma unroll
+    for (int e = 0; e < kMaxRuns; ++e) {
+      off[e] = mine;
+      if (((pend >> e) & 1u) && eb[e] == beta) {
+        mine += en[e];
+        took |= 1u << e;
+      }
+    }
+    // (pe[e] holds the bucket's start plus this wave's base for it)
+    const int pre = wave_excl_scan(mine);
+#pragma unroll
+    for (int e = 0; e < kMaxRuns; ++e)
+      if ((took >> e) & 1u) pe[e] += pre + off[e];
+    pend &= ~took;
+  }
+  // this workgroup's positions p_k = k G + (k odd ? G-1-pos : pos) inside each run's range
+#pragma unroll
+  for (int e = 0; e < kMaxRuns; ++e) {
+    if (e < ne) {
+      const int P = pe[e], n = en[e];
+      for (int k = P / G; k * G <= P + n - 1; ++k) {
+        const int p = k * G + ((k & 1) ? G - 1 - pos : pos);
+        if (p >= P && p < P + n && p < n_all) {
+          const int i = p - P, h = i / er[e], qt = eq[e] + i % er[e];
+          const WorkItem w{b, h, qt * a.bm, 0, qb, lq, kb, lk};
+          if (k < kPPItemCache) cache[k] = w;
+          const_cast<WorkItem*>(a.items)[p] = w;  // the workspace list (read back by diagnostics)
+        }
+      }
+    }
+  }
+  if (blockIdx.x == 0 && tid == 0) {
+    WsHeader* hdr = const_cast<WsHeader*>(a.hdr);
+    hdr->items_off = int32_t(reinterpret_cast<const char*>(a.items) - reinterpret_cast<const char*>(a.hdr));
+    hdr->n_items = n_all;
+    hdr->n_slots = 0;
+    hdr->status = JA_OK;
+    if (a.status_out) *a.status_out = JA_OK;
+  }
+  __syncthreads();
+  return n_all;
+}
+
 // QPF (cross-attention): the Q of the item starting on the next tile is loaded
 // into the Q registers as soon as this step's scores have consumed them, and
 // waited for only before that item's scores.  With the short K/V of
@@ -302,7 +490,10 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
   // starting on the next tile, alternating by tile parity).
   constexpr int kPipeV = 3 * K::kTileBytes, kPipeQ = 7 * K::kTileBytes;
   // MX8: see PP::kMx*.
-  constexpr int kRingBytes = kMx8 ? K::kMxBytes : (kPipe ? 9 * K::kTileBytes : K::kRing * K::kStageBytes);
+  // (the ring is also the scratch of the in-kernel item enumeration)
+  constexpr int kTileRing = kMx8 ? K::kMxBytes : (kPipe ? 9 * K::kTileBytes : K::kRing * K::kStageBytes);
+  constexpr int kEnumBytes = 4 * (9 * kCostBuckets + 16);
+  constexpr int kRingBytes = kTileRing > kEnumBytes ? kTileRing : kEnumBytes;
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kRingBytes];
   __shared__ WorkItem cache[kPPItemCache];
 
@@ -311,7 +502,6 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
   const int l32 = lane & 31, g = lane >> 5;
   const bool late = wave >= 4;  // VALU phase before the MFMA phase
 
-  const int n_all = a.hdr->n_items;
   PPCtx c;
   c.items = a.items;
   c.cache = (lds_i32x4*)(cache);
@@ -332,6 +522,14 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
   // one XCD only concentrates their loads there, so positions follow the
   // workgroup id and spread over the XCDs)
   if constexpr (WMODE == kWinPipe) c.pos = int(blockIdx.x);
+  int n_all;
+  if (a.inplan) {
+    // (softmax only: no key RMS factors are needed from a plan launch)
+    n_all = enumerate_items(a, reinterpret_cast<int*>(ring), cache, c.G, c.pos);
+    if (n_all < 0) return;
+  } else {
+    n_all = a.hdr->n_items;
+  }
   {
     const int full = n_all / c.G;  // complete rounds
     c.n = full + (item_index(c, full) < n_all ? 1 : 0);
@@ -339,8 +537,10 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
   c.row_bytes = (kMx8 ? 1u : 2u) * unsigned(a.H) * D;  // bytes between a head's rows
   const unsigned srow = unsigned(a.H) * (D / kMxBlock);  // MX8: scale bytes between rows
   if (c.n == 0) return;
-  for (int k = tid; k < min(c.n, kPPItemCache); k += K::kNT) cache[k] = a.items[item_index(c, k)];
-  __syncthreads();
+  if (!a.inplan) {
+    for (int k = tid; k < min(c.n, kPPItemCache); k += K::kNT) cache[k] = a.items[item_index(c, k)];
+    __syncthreads();
+  }
 
   // Stream cursors: tile s (scores), s+1, s+2 (being loaded); only the
   // loading cursor carries the addresses of its item.
@@ -1077,6 +1277,9 @@ hipError_t launch_mx8(dim3 gd, dim3 bd, hipStream_t st, const AttnArgs& a, const
 }
 
 int pp_rows() { return kPPRows; }
+int pp_item_cache() { return kPPItemCache; }
+int pp_enum_max_runs() { return kMaxRuns; }
+int pp_enum_max_offsets() { return 64 * kPPWaves; }
 int pp_pipe_rows() { return kBlock * kPipeBlocks; }
 int pp_pipe_max_blocks() { return kPipePairs; }
 

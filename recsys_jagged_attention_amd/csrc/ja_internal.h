@@ -116,6 +116,13 @@ struct AttnArgs {
   float score_scale;  // softmax: log2(e)/sqrt(D); GELU: 1/sqrt(D)
   float eps;
   unsigned long long* stats;  // optional softmax counters (tile stream): tiles, max passes, rescales
+  // Tile stream without a plan launch (inplan = 1): every workgroup checks the
+  // offsets and enumerates its own items; workgroup 0 writes the header (and
+  // status_out).  B + 1 <= 512 offsets, bm query rows per item.
+  int inplan;
+  int B, bm, self_check;
+  int32_t total_q, total_kv;
+  int32_t* status_out;
 };
 
 // Events that time one kernel from its own dispatch packet (hipExtLaunchKernel

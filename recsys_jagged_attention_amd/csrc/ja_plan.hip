@@ -17,6 +17,7 @@
 // rounds gives every workgroup about the same number of tile steps; the items
 // of one (sample, head) stay adjacent.
 #include "ja_internal.h"
+#include "ja_sched.h"
 #include "jagged_attn.h"
 
 namespace ja {
@@ -25,35 +26,10 @@ namespace {
 
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanWaves = kPlanThreads / 64;
-constexpr int kCostBuckets = kPlanThreads;  // cost order: bucket = key tiles, clamped
-
-// Cost bucket of query tile qt of a sample: the key tiles the tile-stream
-// kernel walks for that item (all of the sample's, or with a window those from
-// the first one a query of the item sees to the item's last query block).
-__device__ inline int cost_bucket(const PlanArgs& a, int qt, int lq, int lk) {
-  int te = (lk + kBlock - 1) / kBlock, tl = 0;
-  if (a.window_blocks > 0 || a.window_tokens > 0) {
-    const int q0 = qt * a.bm;
-    te = min(te, (min(q0 + a.bm, lq) + kBlock - 1) / kBlock);
-    tl = a.window_blocks > 0 ? max(0, q0 / kBlock - a.window_blocks + 1) : max(0, q0 - a.window_tokens + 1) / kBlock;
-  }
-  return min(max(te - tl, 0), kCostBuckets - 1);
-}
+static_assert(kCostBuckets == kPlanThreads, "one cost bucket per plan thread");
 
 // Cost bucket of a key-split item of `keys` keys (one query tile): its key tiles.
 __device__ inline int split_bucket(int keys) { return min((keys + kBlock - 1) / kBlock, kCostBuckets - 1); }
-
-// Length of the run of query tiles from qt on that share qt's cost bucket,
-// found without visiting them one by one: without a window every item walks
-// the same tiles; with one, the full items past the window's clamp at the
-// sample's first key walk the same number, and the first and last items are
-// runs of their own.
-__device__ inline int cost_run(const PlanArgs& a, int qt, int nqt) {
-  if (a.window_blocks <= 0 && a.window_tokens <= 0) return nqt - qt;
-  const int span = a.window_blocks > 0 ? (a.window_blocks - 1) * kBlock : a.window_tokens - 1;
-  const int qt_mid = (span + a.bm - 1) / a.bm;  // first query tile whose window is unclamped
-  return (qt >= qt_mid && qt < nqt - 1) ? nqt - 1 - qt : 1;
-}
 
 template <typename T>
 __device__ inline T wave_inclusive_scan(T x) {

@@ -59,6 +59,9 @@ namespace ja {
 int pp_rows() { return 256; }
 int pp_pipe_rows() { return 1024; }
 int pp_pipe_max_blocks() { return 4; }
+int pp_item_cache() { return 256; }
+int pp_enum_max_runs() { return 4; }
+int pp_enum_max_offsets() { return 512; }
 hipError_t launch_plan(const PlanArgs& a, hipStream_t) {
   if (!a.hdr || !a.items || a.max_items < 0) g_errors.fetch_add(1);
   return hipSuccess;
