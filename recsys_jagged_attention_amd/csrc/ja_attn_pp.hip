@@ -915,7 +915,7 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
           bf16x8 ov;
 #pragma unroll
           for (int j = 0; j < 8; ++j) ov[j] = (__bf16)(o[t][i + j] * scale);
-          *reinterpret_cast<bf16x8*>(ob + loff + 2 * (16 * t + i)) = ov;
+          store_global16(ob + loff + 2 * (16 * t + i), ov);
         }
     }
 #pragma unroll

@@ -94,6 +94,15 @@ __device__ __forceinline__ const T* uniform_ptr(const T* p) {
   return reinterpret_cast<const T*>((hi << 32) | lo);
 }
 
+// 16-byte store through a pointer marked global.  A pointer rebuilt from
+// integers (as above) has lost its address space, and the compiler would emit
+// a flat store; flat operations count on the LDS counter too and may complete
+// out of order with LDS reads, so while one is pending every wait for an LDS
+// read must drain all of them (lgkmcnt(0)) instead of waiting by count.
+__device__ __forceinline__ void store_global16(void* p, bf16x8 v) {
+  *reinterpret_cast<__attribute__((address_space(1))) bf16x8*>(reinterpret_cast<uintptr_t>(p)) = v;
+}
+
 // 16-byte chunk swizzle of an fp8 code tile (D bytes per row) for the fp8
 // MFMA operand reads: rows sharing a bank set get distinct chunk slots.
 template <int D>
