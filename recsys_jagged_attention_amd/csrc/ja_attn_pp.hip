@@ -35,6 +35,8 @@
 // run on.  Operand
 // layouts, swizzles and the transposed score tile are those of the main MFMA
 // kernel (ja_attn_mfma.hip).
+#include <type_traits>
+
 #include "ja_device.h"
 #include "ja_mfma_util.h"
 #include "ja_sched.h"
@@ -290,12 +292,14 @@ __device__ __forceinline__ void advance(const PPCtx& c, Cur& cu, Src& src, int w
 // Every workgroup reads the B+1 offsets, checks them, and computes the same
 // item order the plan kernel's counting sort gives in effect -- items sorted
 // by the key tiles they walk, most first -- with a deterministic order inside
-// a cost bucket (by wave, then lane = sample, then run), so that every
-// workgroup finds the same positions without talking to the others.  It keeps
-// the records of its own positions (dealt in alternating rounds) in the LDS
-// item cache and writes them to the workspace item list; workgroup 0 writes
-// the header.  One thread per sample (B + 1 <= 512 offsets); a sample has at
-// most kMaxRuns runs of equal cost (the host checks the window against bm).
+// a cost bucket (by wave, then lane, then run), so that every workgroup finds
+// the same positions without talking to the others.  It keeps the records of
+// its own positions (dealt in alternating rounds) in the LDS item cache and
+// writes them to the workspace item list; workgroup 0 writes the header.  One
+// thread per sample (B + 1 <= 512 offsets), sample b on lane b / 8 of wave
+// b % 8: a few samples spread over all eight waves rank their runs in parallel
+// (the ranking loop takes one pass per distinct cost in a wave).  A sample has
+// at most kMaxRuns runs of equal cost (the host checks the window against bm).
 constexpr int kMaxRuns = 4;
 
 // Exclusive prefix sum over the wave's 64 lanes on the DPP network (no LDS
@@ -317,12 +321,13 @@ __device__ __forceinline__ int wave_excl_scan(int x) {
 // (9 * kCostBuckets + 16) ints (the tile ring, not yet in use).
 __device__ int enumerate_items(const AttnArgs& a, int* lds, WorkItem* cache, int G, int pos) {
   const int tid = threadIdx.x, wave = tid >> 6;
+  static_assert(kPPWaves == 8, "sample b sits on lane b / 8 of wave b % 8");
   int* s_cnt = lds;                          // [8][kCostBuckets]: item counts per wave, then wave bases
   int* s_start = lds + 8 * kCostBuckets;     // [kCostBuckets]: first position of each bucket
   int* s_wsum = s_start + kCostBuckets;      // [8 + 1]: block scan of the bucket totals
   // this thread's sample: offsets checked as the plan kernel checks them (the
   // loads are issued first, so that their latency covers the zeroing below)
-  const int b = tid;
+  const int b = (tid & 63) * kPPWaves + wave;
   int q = 0, k = 0, q1 = 0, k1 = 0;
   if (b <= a.B) {
     q = a.qo[b];
@@ -737,6 +742,9 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
   for (int t = 0; t < kOTiles; ++t)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
+  // O restarts at zero with the next item: its first P V takes C = 0 instead
+  // of the 64 accumulator registers being cleared (the epilogue sets this)
+  bool o_zero = false;
   float m = -__builtin_huge_valf(), l = 0.f;
   f32x16 sc[2];      // score tile: S^T halves (keys 32*st + 16*(i/8) + 8g + i%8)
   bf16x8 pb[kPv8 ? 1 : 4];  // P of the previous tile, 16-key chunks kc
@@ -836,10 +844,12 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
         const float m_new = fmaxf(m, mt);
         const float alpha = m == -__builtin_huge_valf() ? 0.f : fast_exp2((m - m_new) * c2s);
         l *= alpha;
+        if (!o_zero) {
 #pragma unroll
-        for (int t = 0; t < kOTiles; ++t)
+          for (int t = 0; t < kOTiles; ++t)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
+            for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
+        }
         m = m_new;
         part = exps(m == -__builtin_huge_valf() ? 0.f : m * c2s);
       }
@@ -888,7 +898,8 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
     }
   };
 
-  // Output rows of the k-th item: O / l (softmax) or O / Lk (GELU), then reset.
+  // Output rows of the k-th item: O / l (softmax) or O / Lk (GELU), then reset
+  // (O by the next P V, see o_zero).
   // Returns whether this wave issued its kStoresPerWave stores.
   auto epilogue = [&](int k, int prow0) __attribute__((always_inline)) {
     const WorkItem it = load_record(c, k);
@@ -918,10 +929,7 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
           store_global16(ob + loff + 2 * (16 * t + i), ov);
         }
     }
-#pragma unroll
-    for (int t = 0; t < kOTiles; ++t)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
+    o_zero = true;
     m = -__builtin_huge_valf();
     l = 0.f;
     return row0 < it.lq;  // (lane 0 stores)
@@ -970,11 +978,13 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
               aop[t][4 + j] = int(w1[j]);
             }
           }
+          const f32x16 zero{};
 #pragma unroll
           for (int t = 0; t < kOTiles; ++t) {
             const int sa = int((vsw >> (8 * (dim_perm<D>(t, l32) / kMxBlock))) & 0xFFu);
-            o[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop[t], pq, o[t], 0, 0, 0, sa, 0, psg);
+            o[t] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop[t], pq, o_zero ? zero : o[t], 0, 0, 0, sa, 0, psg);
           }
+          o_zero = false;
         } else if (WMODE == kWinNone || pv_act) {
           // 4*kOTiles MFMAs (16-key chunk kc, output tile t), the V^T operand
           // read kAhead MFMAs early: one wave issues them alone, so the LDS
@@ -994,22 +1004,34 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
             return __builtin_bit_cast(bf16x8, w);
           };
           constexpr int kN = 4 * kOTiles, kAhead = kN < kPPAhead ? kN : kPPAhead;
-          bf16x8 vop[kAhead];
+          // (one copy per value of `fresh`: the first chunk's MFMAs of an item
+          // take C = 0)
+          auto pv_tile = [&](auto fresh) __attribute__((always_inline)) {
+            bf16x8 vop[kAhead];
 #pragma unroll
-          for (int i = 0; i < kAhead; ++i) vop[i] = vread(i);
+            for (int i = 0; i < kAhead; ++i) vop[i] = vread(i);
 #pragma unroll
-          for (int i = 0; i < kN; ++i) {
-            const bf16x8 op = vop[i % kAhead];
-            if (i + kAhead < kN) vop[i % kAhead] = vread(i + kAhead);
-            o[i % kOTiles] = mfma_32x32x16(op, pb[i / kOTiles], o[i % kOTiles]);
-          }
-          // keep the reads kAhead MFMAs early (the scheduler would sink them)
-          __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2 * kAhead, 0);
+            for (int i = 0; i < kN; ++i) {
+              const bf16x8 op = vop[i % kAhead];
+              if (i + kAhead < kN) vop[i % kAhead] = vread(i + kAhead);
+              if (decltype(fresh)::value && i < kOTiles)
+                o[i % kOTiles] = mfma_32x32x16(op, pb[i / kOTiles], f32x16{});
+              else
+                o[i % kOTiles] = mfma_32x32x16(op, pb[i / kOTiles], o[i % kOTiles]);
+            }
+            // keep the reads kAhead MFMAs early (the scheduler would sink them)
+            __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2 * kAhead, 0);
 #pragma unroll
-          for (int i = 0; i < kN; ++i) {
-            __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-            if (i + kAhead < kN) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
-          }
+            for (int i = 0; i < kN; ++i) {
+              __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+              if (i + kAhead < kN) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+            }
+          };
+          if (o_zero)
+            pv_tile(std::true_type{});
+          else
+            pv_tile(std::false_type{});
+          o_zero = false;
         }
         // Output of an item whose last tile was s-1.  These stores are newer
         // than the loads of tile s+1 (issued in the previous step), so the
