@@ -54,8 +54,6 @@ constexpr int kSgMfma = 0x008, kSgDsRead = 0x100;
 // Softmax: a lane's sum of one tile's exponentials (32 keys) against the lazy
 // reference max may reach 2^12 before the reference moves up.
 constexpr float kPartCap = 4096.0f;
-typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-__device__ constexpr bf16x2v kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 // MFMA operands are read this many MFMAs before their use (LDS latency under
 // the load of four waves reading at once is several MFMAs long).
 constexpr int kPPAhead = 5;
@@ -789,8 +787,12 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
             }
         }
       }
-      // p = 2^(s c - m c) into pb; returns this lane's sum of the bf16 p
-      // (the weights P V uses), two at a time on the dot unit.
+      // p = 2^(s c - m c) into pb (bf16); returns this lane's sum of the fp32
+      // p, by plain adds: a dot-product sum of the bf16 pairs competes with
+      // the other wave's MFMAs for the SIMD and cost a fifth of the step,
+      // while the adds hide behind them.  (The bf16 rounding of each weight
+      // is unbiased, and l differs from the sum of the rounded weights by far
+      // less than that rounding.)
       // (fp8 P V: p in fp32 into pf; the sum is of the fp32 p, for the
       // reference check only -- l takes the sum of the quantised weights)
       float pf[kPv8 ? 32 : 1];
@@ -807,10 +809,11 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
           for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
             for (int j = 0; j < 8; j += 2) {
-              pb[kc][j] = (__bf16)fast_exp2(fmaf(sc[kc >> 1][8 * (kc & 1) + j], c2s, -mc));
-              pb[kc][j + 1] = (__bf16)fast_exp2(fmaf(sc[kc >> 1][8 * (kc & 1) + j + 1], c2s, -mc));
-              const bf16x2v pr = {pb[kc][j], pb[kc][j + 1]};
-              part[j / 2] = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, part[j / 2], false);
+              const float e0 = fast_exp2(fmaf(sc[kc >> 1][8 * (kc & 1) + j], c2s, -mc));
+              const float e1 = fast_exp2(fmaf(sc[kc >> 1][8 * (kc & 1) + j + 1], c2s, -mc));
+              pb[kc][j] = (__bf16)e0;
+              pb[kc][j + 1] = (__bf16)e1;
+              part[j / 2] += e0 + e1;
             }
         }
         return (part[0] + part[1]) + (part[2] + part[3]);
