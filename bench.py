@@ -188,8 +188,9 @@ def cpu_baseline(w, budget_s: float, gpu_out=None):
 
 # Source file of each forward kernel, and the headers every kernel file includes.
 KERNEL_SOURCE = {"attn_pp_kernel": "ja_attn_pp.hip", "attn_kernel": "ja_attn_mfma.hip",
-                 "attn_f32_kernel": "ja_attn_f32.hip"}
-KERNEL_HEADERS = ("ja_internal.h", "ja_device.h", "ja_mfma_util.h", "ja_gelu_poly.h")
+                 "attn_f32_kernel": "ja_attn_f32.hip", "bwd_mfma_kernels": "ja_attn_bwd_mfma.hip",
+                 "mx_quant_kernel": "ja_mx_quant.hip"}
+KERNEL_HEADERS = ("ja_internal.h", "ja_device.h", "ja_mfma_util.h", "ja_gelu_poly.h", "ja_sched.h")
 
 
 def kernel_source_hash(kernel_tag: str) -> str:

@@ -134,7 +134,8 @@ typedef struct ja_io {
                              /* had no reference yet (a query block's first     */
                              /* tile) or to [2] when a later tile moved the     */
                              /* reference up and rescaled O; other kernels and  */
-                             /* the caller's zeroing: untouched.  Costs atomics. */
+                             /* the caller's zeroing: untouched.  Each wave adds */
+                             /* its counts once, when it ends.                  */
   int32_t fp8_pv;            /* JA_MXFP8_E4M3 only: nonzero runs O += P V on    */
                              /* the block-scaled fp8 MFMA too ("MXFP8..."       */
                              /* section: attention in microscaling fp8).  V is  */

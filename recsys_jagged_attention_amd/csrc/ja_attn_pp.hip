@@ -743,6 +743,12 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
   // O restarts at zero with the next item: its first P V takes C = 0 instead
   // of the 64 accumulator registers being cleared (the epilogue sets this)
   bool o_zero = false;
+  // softmax diagnostics (a.stats), kept in vector registers (made so by the
+  // asm): wave-uniform scalars would add to the scalar register spills
+  unsigned st_tiles, st_first, st_later;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(st_tiles));
+  asm volatile("v_mov_b32 %0, 0" : "=v"(st_first));
+  asm volatile("v_mov_b32 %0, 0" : "=v"(st_later));
   float m = -__builtin_huge_valf(), l = 0.f;
   f32x16 sc[2];      // score tile: S^T halves (keys 32*st + 16*(i/8) + 8g + i%8)
   bf16x8 pb[kPv8 ? 1 : 4];  // P of the previous tile, 16-key chunks kc
@@ -831,11 +837,10 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
       if (!fresh) part = exps(m * c2s);
       const bool moved = fresh || __any(!(part <= kPartCap));
       if (a.stats) {
-        // diagnostics: tiles, first-tile max passes, later rescales (per wave and tile)
-        if (lane == 0) {
-          atomicAdd(a.stats, 1ull);
-          if (moved) atomicAdd(a.stats + (fresh ? 1 : 2), 1ull);
-        }
+        // diagnostics: tiles, first-tile max passes, later rescales (per wave
+        // and tile; added to the caller's counters once, at the wave's end)
+        ++st_tiles;
+        if (moved) ++(fresh ? st_first : st_later);
       }
       if (moved) {
         float mt = -__builtin_huge_valf();
@@ -1268,6 +1273,11 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
     c0 = c1;
     c1 = c2;
     advance<D, WMODE, IN>(c, c2, src, wave, lane, nb, wt);
+  }
+  if (a.stats && lane == 0 && st_tiles) {
+    atomicAdd(a.stats, (unsigned long long)st_tiles);
+    atomicAdd(a.stats + 1, (unsigned long long)st_first);
+    atomicAdd(a.stats + 2, (unsigned long long)st_later);
   }
 }
 
