@@ -521,10 +521,12 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
   // [x G/8, (x+1) G/8) are the workgroups of XCD x)
   c.G = gridDim.x;
   c.pos = int(blockIdx.x % kXcds) * (c.G / kXcds) + int(blockIdx.x) / kXcds;
-  // (the pipeline's runs share few key tiles: dealing consecutive runs to
-  // one XCD only concentrates their loads there, so positions follow the
-  // workgroup id and spread over the XCDs)
-  if constexpr (WMODE == kWinPipe) c.pos = int(blockIdx.x);
+  // (the bf16 pipeline's runs share few key tiles: dealing consecutive runs
+  // to one XCD only concentrates their loads there, so positions follow the
+  // workgroup id and spread over the XCDs.  MX8 keeps the XCD grouping: the
+  // heads of a token share their 128-byte lines of scale bytes, and
+  // consecutive items are the heads of one sample)
+  if constexpr (WMODE == kWinPipe && !kMx8) c.pos = int(blockIdx.x);
   int n_all;
   if (a.inplan) {
     // (softmax only: no key RMS factors are needed from a plan launch)
