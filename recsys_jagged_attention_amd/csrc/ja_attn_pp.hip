@@ -487,6 +487,7 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
   constexpr int kQChunks = K::kQChunks, kOTiles = K::kOTiles, kRowBytes = K::kRowBytes;
   constexpr bool kPipe = WMODE == kWinPipe;
   constexpr bool kMx8 = K::kMx8, kPv8 = K::kPv8;
+  constexpr bool kLateEpi = QPF;  // an item's output after the next item's scores
   // LDS: a ring of kRing stages of (K, V[, key scales]).  The pipeline instead
   // keeps K in 3 stages (tiles s, s+1, s+2: K_{s-1} is dead once the scores
   // of tile s-1 are taken), V in 4 (s-1 .. s+2) and two Q blocks (the block
@@ -1043,10 +1044,12 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
             pv_tile(std::false_type{});
           o_zero = false;
         }
-        // Output of an item whose last tile was s-1.  These stores are newer
-        // than the loads of tile s+1 (issued in the previous step), so the
-        // next step's wait for that tile can let them run on.
-        if (pv_last) stores_pending = epilogue(pv_k, pv_row0);
+        // Output of an item whose last tile was s-1 (cross-attention: after
+        // this step's scores, below).  These stores are newer than the loads
+        // of tile s+1 (issued in the previous step), so the next step's wait
+        // for that tile can let them run on.
+        if constexpr (!kLateEpi)
+          if (pv_last) stores_pending = epilogue(pv_k, pv_row0);
       }
     };
     // A new item starts with tile s: its Q is loaded and waited for here, in
@@ -1062,13 +1065,16 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
     }
     stores_pending = false;
     head();
-    if (c0.k >= c.n) break;
+    if (c0.k >= c.n) {
+      if constexpr (kLateEpi)
+        if (s > 0 && pv_last) epilogue(pv_k, pv_row0);
+      break;
+    }
     if (q_fresh) {
-      // QPF: the item's Q was loaded at the end of the last step; only the
-      // output stores of this step's head can have been issued after it
-      // (the compiler adds its own wait for the Q registers here, which also
-      // covers those stores)
-      if constexpr (QPF) wait_vmcnt(stores_pending ? K::kStoresPerWave : 0);
+      // QPF: the item's Q was loaded at the end of the last step, after every
+      // other load and store still in flight (the compiler adds its own wait
+      // for the Q registers here as well)
+      if constexpr (QPF) wait_vmcnt(kLateEpi ? 0 : (stores_pending ? K::kStoresPerWave : 0));
       q_rms();
       q_fresh = false;
     }
@@ -1154,6 +1160,11 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
         if (i + kAhead < kNS) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 1);
       }
     }
+    // Cross-attention (every step ends an item): the output of the item whose
+    // last tile was s-1 after this step's scores, whose MFMAs keep the matrix
+    // core busy while its first instructions wait for O += V P just issued.
+    if constexpr (kLateEpi)
+      if (s > 0 && pv_last) stores_pending = epilogue(pv_k, pv_row0);
     tile_scales(c2, src, st_pf);
     mx_scales(c2, src, s + 2);
     if constexpr (QPF) {
