@@ -157,3 +157,24 @@ def test_device_items_many_samples():
     assert sorted(got) == sorted(expected_items(w, bm, kvc))
     cost = [walked_tiles(w, it, bm, kvc) for it in got]
     assert all(a >= b for a, b in zip(cost, cost[1:]))
+
+
+@pytest.mark.parametrize("window", [0, 256])
+def test_device_items_in_kernel_enumeration_at_its_sample_limit(window):
+    """511 samples (the most the tile stream enumerates in its own prologue):
+    every wave holds samples, and with a block window a sample has up to three
+    runs of equal cost.  Skewed lengths put items in many cost buckets; the
+    item list must still equal the host enumeration, in cost order."""
+    rng = np.random.Generator(np.random.PCG64(41 + window))
+    B = 511
+    L = np.floor(np.exp(rng.uniform(0.0, np.log(3001.0), size=B))).astype(int)
+    L[rng.integers(0, B, size=40)] = 0  # empty samples among them
+    L = L.tolist()
+    w = adhoc("self", "softmax", "bf16", L, L, 2, 32, window=window, seed=42 + window)
+    bm, kvc, _ = schedule(w)
+    got = device_items(w)
+    want = expected_items(w, bm, kvc)
+    assert len(got) == len(set(got)), "an item appears twice"
+    assert sorted(got) == sorted(want)
+    cost = [walked_tiles(w, it, bm, kvc) for it in got]
+    assert all(a >= b for a, b in zip(cost, cost[1:])), "items are not in decreasing cost order"
