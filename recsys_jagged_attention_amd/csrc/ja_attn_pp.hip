@@ -897,14 +897,18 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
       }
       l += part;
     } else {
+      // (keys past the sample in a ragged tile need no mask: their V rows
+      // are zero, see the top of the step, and their weights are finite)
       const float* ksl = reinterpret_cast<const float*>(ring + stage * K::kStageBytes + K::kKsOff);
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < 8; j += 2) {
           const int kk = 32 * (kc >> 1) + 16 * ((kc & 1)) + 8 * g + j;
-          const float gl = gelu_act<ACT>(sc[kc >> 1][8 * (kc & 1) + j] * rq * ksl[kk]);
-          pb[kc][j] = (__bf16)((!ragged || kk < nvalid) ? gl : 0.f);
+          const float g0 = gelu_act<ACT>(sc[kc >> 1][8 * (kc & 1) + j] * rq * ksl[kk]);
+          const float g1 = gelu_act<ACT>(sc[kc >> 1][8 * (kc & 1) + j + 1] * rq * ksl[kk + 1]);
+          pb[kc][j] = (__bf16)g0;
+          pb[kc][j + 1] = (__bf16)g1;
         }
     }
   };
@@ -956,6 +960,21 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
     wait_vmcnt(K::kVmemPerTile + (stores_pending ? K::kStoresPerWave : 0) + (q_ahead ? kQChunks : 0));
     lds_barrier();
     const int st_s = s % K::kRing, st_prev = (s + K::kRing - 1) % K::kRing, st_pf = (s + 2) % K::kRing;
+    if constexpr (ACT != ACT_SOFTMAX) {
+      // GELU: the V rows of tile s (landed above) past the sample's last key,
+      // which the loads filled with copies of the last key, to zero.  O += V P
+      // reads them in the next step (after its barrier), and a zero row makes
+      // the weight of a key past the sample irrelevant, so the activation
+      // needs no mask (GELU keeps no row sum, and its weights stay finite).
+      const int nv = c0.lk - kBlock * c0.t;
+      if (c0.k < c.n && nv < kBlock) {
+        unsigned char* vz = ring + v_at(s);
+        constexpr int kChunks = kRowBytes / 16;
+#pragma unroll
+        for (int e = tid; e < kBlock * kChunks; e += K::kNT)
+          if (e / kChunks >= nv) *reinterpret_cast<u32x4*>(vz + 16 * e) = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
     // Q block starting on tile s+2 (read in step s+1): issued before this
     // step's tile loads, so the next step's wait covers it.
     q_stage(c2, src);
