@@ -55,6 +55,12 @@
  * workspace and then skips all work (out is left unspecified); read it with
  * jagged_attn_check.  Output contents are unspecified whenever the status is
  * not JA_OK.
+ *
+ * Debug mode.  With the environment variable JA_DEBUG set to anything but
+ * "0" (read once per process), jagged_attn_fwd, jagged_attn_fwd_noalloc,
+ * jagged_attn_bwd and jagged_attn_mx_quantize synchronise their stream before
+ * returning and return the device status themselves: JA_EOFFSETS for offsets
+ * the device rejected, JA_EHIP for a launch or runtime fault, else JA_OK.
  */
 #ifndef JAGGED_ATTN_H
 #define JAGGED_ATTN_H

@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 
 #include "ja_internal.h"
@@ -369,6 +370,30 @@ int validate_bwd(int B, int H, int D, int variant, int act, int window, int dtyp
 }  // namespace
 }  // namespace ja
 
+namespace ja {
+
+bool debug_sync() {
+  // (a function-local static: initialised once, thread-safely)
+  static const bool on = [] {
+    const char* e = std::getenv("JA_DEBUG");
+    return e != nullptr && e[0] != '\0' && std::strcmp(e, "0") != 0;
+  }();
+  return on;
+}
+
+int debug_status(hipStream_t stream, const void* st0, const void* st1) {
+  if (hipStreamSynchronize(stream) != hipSuccess) return JA_EHIP;
+  for (const void* p : {st0, st1}) {
+    if (p == nullptr) continue;
+    int32_t status = 0;
+    if (hipMemcpy(&status, p, sizeof(status), hipMemcpyDeviceToHost) != hipSuccess) return JA_EHIP;
+    if (status != JA_OK) return status;
+  }
+  return JA_OK;
+}
+
+}  // namespace ja
+
 using namespace ja;
 
 extern "C" {
@@ -397,8 +422,11 @@ int jagged_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
                     const int32_t* kv_offsets, int B, int H, int D, int variant, int act, int window,
                     void* out, const ja_io* io) {
   if (io == nullptr) return JA_EINVAL;
-  return fwd_impl(q, k, v, q_offsets, kv_offsets, B, H, D, variant, act, window, out, *io, io->workspace,
-                  io->workspace_bytes);
+  const int st = fwd_impl(q, k, v, q_offsets, kv_offsets, B, H, D, variant, act, window, out, *io, io->workspace,
+                          io->workspace_bytes);
+  if (st != JA_OK || !debug_sync()) return st;
+  // (the workspace starts with the plan header, whose first word is the status)
+  return debug_status(reinterpret_cast<hipStream_t>(io->stream), io->workspace, nullptr);
 }
 
 size_t jagged_attn_bwd_workspace_size(int B, int H, int D, int variant, int act, int window, int dtype,
@@ -485,6 +513,7 @@ int jagged_attn_bwd(const void* q, const void* k, const void* v, const void* dou
   if (e != hipSuccess) return JA_EHIP;
   if (io->ev_stop && hipEventRecord(reinterpret_cast<hipEvent_t>(io->ev_stop), stream) != hipSuccess)
     return JA_EHIP;
+  if (debug_sync()) return debug_status(stream, ws + L.hdr_q, ws + L.hdr_k);
   return JA_OK;
 }
 
@@ -499,6 +528,7 @@ int jagged_attn_mx_quantize(const void* x, int dtype, int64_t rows, int D, uint8
   if (launch_mx_quant(dtype == JA_BF16, x, n_blocks, codes, scales, reinterpret_cast<hipStream_t>(stream)) !=
       hipSuccess)
     return JA_EHIP;
+  if (debug_sync()) return debug_status(reinterpret_cast<hipStream_t>(stream), nullptr, nullptr);
   return JA_OK;
 }
 

@@ -186,4 +186,14 @@ int fwd_impl(const void* q, const void* k, const void* v, const int32_t* q_offse
              int B, int H, int D, int variant, int act, int window, void* out, const ::ja_io& io, void* workspace,
              size_t workspace_bytes);
 
+// Debug mode (environment variable JA_DEBUG set to anything but "0", read
+// once per process): every entry point that launches work synchronises its
+// stream before returning and reports the device status (offset errors,
+// launch and runtime faults) as its own return value.
+bool debug_sync();
+
+// Debug mode: synchronise `stream` and return the status word(s) at the given
+// device addresses (NULL entries are skipped); JA_EHIP if the stream failed.
+int debug_status(hipStream_t stream, const void* st0, const void* st1);
+
 }  // namespace ja

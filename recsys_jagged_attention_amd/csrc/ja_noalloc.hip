@@ -68,6 +68,8 @@ extern "C" int jagged_attn_fwd_noalloc(const void* q, const void* k, const void*
   // Nothing in the workspace needs to start at zero: the plan kernel writes
   // the header, the items and the split table of this call before any other
   // kernel reads them, and partials are written before they are merged.
-  return ja::fwd_impl(q, k, v, q_offsets, kv_offsets, B, H, D, variant, act, window, out, *io, ws,
-                      ja::kScratchBytes);
+  const int fst = ja::fwd_impl(q, k, v, q_offsets, kv_offsets, B, H, D, variant, act, window, out, *io, ws,
+                               ja::kScratchBytes);
+  if (fst != JA_OK || !ja::debug_sync()) return fst;
+  return ja::debug_status(reinterpret_cast<hipStream_t>(io->stream), ws, nullptr);
 }
