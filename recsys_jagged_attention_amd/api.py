@@ -56,9 +56,10 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     ``max_workgroups`` caps the attention kernel's grid (0: every resident
     slot); results do not depend on it.  ``softmax_stats`` (3 int64 on the
     device, diagnostics) receives the tile-stream softmax's counts: tiles,
-    first-tile max passes, later rescales.  ``fp8_pv`` (MXFP8 self-attention
-    at D = 128) runs O += P V on the fp8 MFMA too, with P and V requantised
-    along the keys."""
+    first-tile max passes, later rescales.  ``fp8_pv`` asks for O += P V on
+    the fp8 MFMA too (MXFP8 self-attention at D = 128, P and V requantised
+    along the keys); this version does not provide it and raises
+    JaggedAttnError with JA_EUNSUPPORTED."""
     if dtype not in _IN_DTYPES:
         raise ValueError(f"dtype must be one of {list(_IN_DTYPES)}")
     want = _IN_DTYPES[dtype]
