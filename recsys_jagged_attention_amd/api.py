@@ -157,10 +157,13 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tens
              q_offsets: torch.Tensor, kv_offsets: torch.Tensor,
              variant: str = "self", act: str = "softmax", window: int = 0, dtype: str = "bf16",
              workspace: Optional[Workspace] = None, rms_eps: float = 1e-6,
-             stream: Optional[torch.cuda.Stream] = None, check: Optional[bool] = None, events=None):
+             stream: Optional[torch.cuda.Stream] = None, check: Optional[bool] = None, events=None,
+             out=None):
     """Gradients of the forward (act "softmax" or "gelu_tanh"): returns float32
     (dq, dk, dv) shaped like q, k, v.  q/k/v/dout are "f32" or "bf16" tensors
-    laid out as for ``forward``; ``stream`` and ``check`` as for ``forward``."""
+    laid out as for ``forward``; ``stream`` and ``check`` as for ``forward``.
+    ``out=(dq, dk, dv)`` gives the (contiguous float32) outputs; every element
+    of them is written."""
     if dtype not in ("f32", "bf16"):
         raise ValueError("backward takes f32 or bf16 inputs")
     want = _IN_DTYPES[dtype]
@@ -179,9 +182,15 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tens
         check = workspace is None
     with torch.cuda.stream(st):  # (temporaries on the launch stream, as in forward)
         ws = (workspace or Workspace(q.device)).get(nbytes)
-        dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-        dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
-        dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
+        if out is None:
+            dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+            dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+            dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
+        else:
+            dq, dk, dv = out
+            for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+                if t.dtype != torch.float32 or t.shape != ref.shape or not t.is_contiguous() or not t.is_cuda:
+                    raise ValueError(f"{name} must be a contiguous float32 CUDA tensor shaped like its input")
     io = _lib.JaIo()
     io.dtype = d_id
     io.workspace = ws.data_ptr()

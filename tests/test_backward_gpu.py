@@ -134,3 +134,37 @@ def test_full_size_sampled(name):
             err = np.abs(got - r).max() / max(np.abs(r).max(), 1.0) if r.size else 0.0
             log(f"  sample {b} head {h} {nm}: rel err {err:.3e}")
             assert np.isfinite(got).all() and err <= tol("bf16", w.act), f"{nm} b={b} h={h}: {err:.3e}"
+
+
+@pytest.mark.parametrize("variant,act,window,dtype", [
+    ("self", "softmax", 256, "bf16"), ("self", "softmax", 0, "bf16"), ("sliding", "softmax", 100, "bf16"),
+    ("cross", "gelu_tanh", 0, "bf16"), ("pma", "softmax", 0, "bf16"), ("self", "softmax", 128, "f32"),
+    ("cross", "softmax", 0, "f32")])
+def test_every_gradient_element_written_once_and_repeatable(variant, act, window, dtype):
+    """dQ, dK and dV in NaN-filled buffers with NaN guard bands on both sides:
+    every element is written (rows of samples without keys, and keys no query
+    sees, get zeros), nothing is written outside, and two calls give bitwise
+    equal gradients (no atomics, a fixed order)."""
+    lq = [0, 1, 65, 200, 3] if variant != "pma" else [32, 32, 32, 32, 32]
+    lk = [5, 0, 130, 64, 1] if variant in ("cross", "pma") else lq
+    qo, ko, q, k, v = random_jagged(17, lq, lk, 2, 64)
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    tq, tk, tv = (torch.from_numpy(x).to(dt).cuda() for x in (q, k, v))
+    tg = torch.from_numpy(np.random.default_rng(5).standard_normal(q.shape).astype(np.float32)).to(dt).cuda()
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+    pad = 4096
+    runs = []
+    for rep in range(2):
+        bigs = [torch.full((t.numel() + 2 * pad,), float("nan"), dtype=torch.float32, device="cuda")
+                for t in (tq, tk, tv)]
+        outs = tuple(b[pad:pad + t.numel()].view(t.shape) for b, t in zip(bigs, (tq, tk, tv)))
+        backward(tq, tk, tv, tg, to(qo), to(ko), variant=variant, act=act, window=window, dtype=dtype,
+                 check=True, out=outs)
+        torch.cuda.synchronize()
+        for name, b, o in zip(("dq", "dk", "dv"), bigs, outs):
+            assert torch.isnan(b[:pad]).all() and torch.isnan(b[-pad:]).all(), f"{name}: write outside"
+            assert not torch.isnan(o).any(), f"{name}: an element was not written"
+        runs.append([o.clone() for o in outs])
+    log(f"{variant} {act} W={window} {dtype}: every element written, repeatable")
+    for a, b in zip(*runs):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
