@@ -17,7 +17,8 @@ the pages' unspecified "6th-order Taylor" GELU approximation is unpinned: the
 oracle computes exact gelu_tanh only.
 """
 from .gdpa import (gdpa_forward, gdpa_rows, gelu_tanh, rms_normalise,
-                   block_window_allowed, sliding_window_allowed, attention_dense, attended_pairs)
+                   block_window_allowed, sliding_window_allowed, attention_dense, attended_pairs,
+                   attention_lse, gdpa_lse)
 from .gdpa_bwd import (gdpa_backward, attention_dense_bwd, attention_dense_gelu_bwd, gelu_tanh_grad,
                        rms_normalise_bwd)
 from .mx import decode_e4m3, decode_e8m0, mx_dequantise, encode_e4m3, mx_encode, e4m3_grid
@@ -25,4 +26,5 @@ from .mx import decode_e4m3, decode_e8m0, mx_dequantise, encode_e4m3, mx_encode,
 __all__ = ["gdpa_backward", "attention_dense_bwd", "attention_dense_gelu_bwd", "gelu_tanh_grad",
            "rms_normalise_bwd", "gdpa_forward", "gdpa_rows", "gelu_tanh", "rms_normalise",
            "block_window_allowed", "sliding_window_allowed", "attention_dense", "attended_pairs",
+           "attention_lse", "gdpa_lse",
            "decode_e4m3", "decode_e8m0", "mx_dequantise", "encode_e4m3", "mx_encode", "e4m3_grid"]

@@ -115,6 +115,38 @@ def attention_dense(Q, K, V, act: str, window: int = 0, eps: float = DEFAULT_EPS
     raise ValueError(f"unknown activation {act!r}")
 
 
+def attention_lse(Q, K, window: int = 0, variant: str = "self"):
+    """One (sample, head) of softmax attention: the natural log-sum-exp over the
+    allowed keys of the scaled scores, log sum_j exp(q_i . k_j / sqrt(D)), per
+    query row [Lq]; -inf for a row that sees no key (Lk == 0).  With it the
+    softmax weights are exp(s_ij - lse_i) -- what the backward needs from the
+    forward besides the output."""
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    lq, d = Q.shape
+    lk = K.shape[0]
+    if lk == 0:
+        return np.full(lq, -np.inf)
+    S = (Q @ K.T) / math.sqrt(d)
+    S = np.where(allowed_keys(lq, lk, window, variant), S, -np.inf)
+    m = S.max(axis=1)
+    return m + np.log(np.exp(S - m[:, None]).sum(axis=1))
+
+
+def gdpa_lse(q, k, q_offsets, kv_offsets, variant: str = "self", window: int = 0) -> np.ndarray:
+    """Softmax attention's log-sum-exp per query row and head: float64 [Nq, H]
+    (attention_lse of every sample and head)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    qo, ko = _check(q, k, k, q_offsets, kv_offsets, variant, "softmax", window)
+    out = np.zeros(q.shape[:2], dtype=np.float64)
+    for b in range(len(qo) - 1):
+        for h in range(q.shape[1]):
+            out[qo[b]:qo[b + 1], h] = attention_lse(q[qo[b]:qo[b + 1], h, :], k[ko[b]:ko[b + 1], h, :],
+                                                    window, variant)
+    return out
+
+
 def _check(q, k, v, q_offsets, kv_offsets, variant, act, window):
     qo = np.asarray(q_offsets, dtype=np.int64)
     ko = np.asarray(kv_offsets, dtype=np.int64)
