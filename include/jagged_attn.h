@@ -154,6 +154,19 @@ typedef struct ja_io {
                              /* the default (V exact in bf16, P in bf16).       */
                              /* Not available in this version: every call with */
                              /* it set returns JA_EUNSUPPORTED.                 */
+  float *lse;                /* optional device float32 [total_q, H] owned by   */
+                             /* the caller (4-byte aligned), softmax only: the  */
+                             /* forward writes, per query row and head, the     */
+                             /* natural log-sum-exp of its scaled scores over   */
+                             /* the keys the row attends,                       */
+                             /* log sum_j exp(q.k_j / sqrt(D)), or -inf for a   */
+                             /* row without keys.  Written by the tile-stream   */
+                             /* and fp32 shapes: every fp32 call, bf16 calls    */
+                             /* other than PMA, and MXFP8 self-attention at     */
+                             /* D = 128 (full, or windows of up to four         */
+                             /* blocks).  bf16 PMA and the other MXFP8 calls    */
+                             /* with it set return JA_EUNSUPPORTED, GELU calls  */
+                             /* JA_EINVAL.  NULL: not written.                  */
 } ja_io;
 
 /* The forward pass.  Arguments as described above; window is 0 (no window) or

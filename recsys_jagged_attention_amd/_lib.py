@@ -45,6 +45,7 @@ class JaIo(ctypes.Structure):
         ("status", ctypes.c_void_p),
         ("softmax_stats", ctypes.c_void_p),
         ("fp8_pv", ctypes.c_int32),
+        ("lse", ctypes.c_void_p),
     ]
 
 

@@ -36,7 +36,8 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             workspace: Optional[Workspace] = None, rms_eps: float = 1e-6,
             stream: Optional[torch.cuda.Stream] = None, check: Optional[bool] = None,
             events=None, max_workgroups: int = 0, status: Optional[torch.Tensor] = None,
-            softmax_stats: Optional[torch.Tensor] = None, fp8_pv: bool = False) -> torch.Tensor:
+            softmax_stats: Optional[torch.Tensor] = None, fp8_pv: bool = False,
+            lse: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Jagged GDPA forward.  q [Nq,H,D], k/v [Nk,H,D] on one GPU; offsets int32 [B+1].
 
     dtype "f32"/"bf16": q/k/v of that dtype; "mxfp8": uint8 e4m3 codes with
@@ -59,7 +60,10 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     first-tile max passes, later rescales.  ``fp8_pv`` asks for O += P V on
     the fp8 MFMA too (MXFP8 self-attention at D = 128, P and V requantised
     along the keys); this version does not provide it and raises
-    JaggedAttnError with JA_EUNSUPPORTED."""
+    JaggedAttnError with JA_EUNSUPPORTED.  ``lse`` (a contiguous float32
+    [Nq, H] CUDA tensor, softmax only) receives each query row's natural
+    log-sum-exp of its scaled scores, -inf for rows without keys; bf16 PMA and
+    MXFP8 calls other than D = 128 self-attention raise JA_EUNSUPPORTED."""
     if dtype not in _IN_DTYPES:
         raise ValueError(f"dtype must be one of {list(_IN_DTYPES)}")
     want = _IN_DTYPES[dtype]
@@ -114,6 +118,10 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     io.fp8_pv = 1 if fp8_pv else 0
     if status is not None:
         io.status = status.data_ptr()
+    if lse is not None:
+        if lse.dtype != torch.float32 or not lse.is_cuda or lse.shape != (Nq, H) or not lse.is_contiguous():
+            raise ValueError("lse must be a contiguous float32 [Nq, H] CUDA tensor")
+        io.lse = lse.data_ptr()
     if softmax_stats is not None:
         if softmax_stats.dtype != torch.int64 or not softmax_stats.is_cuda or softmax_stats.numel() < 3:
             raise ValueError("softmax_stats must be an int64 CUDA tensor of 3 elements")

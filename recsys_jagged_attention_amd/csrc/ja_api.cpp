@@ -175,6 +175,12 @@ int fwd_impl(const void* q, const void* k, const void* v, const int32_t* q_offse
   // the GPU on its first run and the cause has not been found, so no call
   // launches it.
   if (io.fp8_pv) return JA_EUNSUPPORTED;
+  // the log-sum-exp output: softmax only, from the tile-stream and fp32 shapes
+  if (io.lse != nullptr) {
+    if (act != JA_SOFTMAX || (reinterpret_cast<uintptr_t>(io.lse) & 3)) return JA_EINVAL;
+    const int shape = make_plan(B, H, D, variant, act, window, io.dtype, io.total_q, io.total_kv).shape;
+    if (shape != kShapePingPong && shape != kShapeF32) return JA_EUNSUPPORTED;
+  }
   // Empty tensors may come with null data pointers: no kernel reads q or
   // writes out without query rows, nor reads k or v without key rows.
   const bool has_q = io.total_q > 0, has_kv = io.total_kv > 0;
@@ -270,6 +276,7 @@ int fwd_impl(const void* q, const void* k, const void* v, const int32_t* q_offse
   aa.eps = rms_eps;
   aa.kscale = ksc;
   aa.stats = reinterpret_cast<unsigned long long*>(io.softmax_stats);
+  aa.lse = io.lse;
   aa.inplan = inplan ? 1 : 0;
   aa.B = B;
   aa.bm = p.bm;

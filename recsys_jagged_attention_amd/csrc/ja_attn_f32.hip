@@ -34,11 +34,15 @@ struct F32Shape {
   static constexpr int kWaves = D == 128 ? 4 : 8;  // key chunks per item (LDS: kWaves x 64 x (D+1) floats)
   static constexpr int kStride = D + 1;            // floats per partial row in LDS (odd: no bank conflicts)
   static constexpr int kStage = 32;                // keys staged per round (2 x 32 x D floats fit 64 x (D+1))
+  // waves per SIMD the registers must leave room for: at D = 32 two
+  // workgroups per CU (LDS: 2 x 71.5 KB), else one
+  static constexpr int kMinWavesPerSimd = D == 32 ? 4 : 1;
 };
 
 // WMODE: 0 all keys, 1 block window, 2 token sliding window.
 template <int D, int ACT, int WMODE>
-__global__ __launch_bounds__(64 * F32Shape<D>::kWaves) void attn_f32_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * F32Shape<D>::kWaves, F32Shape<D>::kMinWavesPerSimd) void attn_f32_kernel(
+    AttnArgs a) {
   constexpr int NW = F32Shape<D>::kWaves, kS = F32Shape<D>::kStride;
   __shared__ __attribute__((aligned(16))) float s_o[NW * kF32Rows * kS];
   __shared__ float s_m[NW * kF32Rows], s_l[NW * kF32Rows];
@@ -171,6 +175,11 @@ __global__ __launch_bounds__(64 * F32Shape<D>::kWaves) void attn_f32_kernel(Attn
           lt = fmaf(c[w], s_l[w * kF32Rows + r], lt);
         }
         scale = lt > 0.f ? 1.0f / lt : 0.f;
+        // log-sum-exp output: m is in log2 units of the scaled scores, so
+        // ln(sum_j exp(s_j / sqrt(D))) = (mx + log2 lt) ln 2 (-inf without keys)
+        if (a.lse != nullptr && dg == 0 && orow < lq)
+          a.lse[size_t(qbeg + orow) * a.H + h] =
+              lt > 0.f ? (mx + log2f(lt)) * 0.69314718055994531f : -__builtin_huge_valf();
       } else {
 #pragma unroll
         for (int w = 0; w < NW; ++w) c[w] = 1.f;

@@ -168,6 +168,7 @@ struct PPCtx {
   const unsigned char* vs;
   const float* kscale;
   __bf16* out;
+  float* lse;             // optional natural log-sum-exp per (query row, head) (softmax)
   int H;
   int G, pos, n;          // item k of this workgroup is item_index(k), k < n
   unsigned row_bytes;  // bytes between a head's input rows (bf16: 2 H D; MX8 codes: H D)
@@ -219,11 +220,13 @@ __device__ __forceinline__ Src make_src(const PPCtx& c, const WorkItem& w) {
   return r;
 }
 
-// Rows [32*wave, 32*wave + 32) of an item with no keys: the output is zero.
+// Rows [32*wave, 32*wave + 32) of an item with no keys: the output is zero
+// (and the log-sum-exp over no keys -inf).
 template <int D>
 __device__ __forceinline__ void write_zero_rows(const PPCtx& c, const WorkItem& it, int wave, int lane) {
   const int qrow = it.q0 + 32 * wave + (lane & 31);
   if (qrow >= it.lq) return;
+  if (c.lse != nullptr && lane < 32) c.lse[size_t(it.qbeg + qrow) * c.H + it.h] = -__builtin_huge_valf();
   __bf16* orow = c.out + (size_t(it.qbeg + qrow) * c.H + it.h) * D + (D / 2) * (lane >> 5);
   bf16x8 z;
 #pragma unroll
@@ -517,6 +520,7 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
   c.vs = a.vs;
   c.kscale = a.kscale;
   c.out = reinterpret_cast<__bf16*>(a.out);
+  c.lse = a.lse;
   c.H = a.H;
   // (the grid is a multiple of 8 and workgroup w runs on XCD w % 8: positions
   // [x G/8, (x+1) G/8) are the workgroups of XCD x)
@@ -914,8 +918,14 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
   };
 
   // Output rows of the k-th item: O / l (softmax) or O / Lk (GELU), then reset
-  // (O by the next P V, see o_zero).
-  // Returns whether this wave issued its kStoresPerWave stores.
+  // (O by the next P V, see o_zero).  Softmax with a log-sum-exp output: each
+  // row also gets ln(sum_j exp(s_j / sqrt(D))) = (m c + log2 l) ln 2, m being
+  // the reference max of the raw scores s and c = log2(e)/sqrt(D) (both lane
+  // halves hold the same m and l bit for bit and store the same value).
+  // Returns whether this wave issued its kStoresPerWave output stores.  (The
+  // log-sum-exp store is not counted: the next wait then lets one op fewer
+  // run on -- the first load of the next tile -- which is safe; an exact
+  // count would cost the wait a run-time switch at every step.)
   auto epilogue = [&](int k, int prow0) __attribute__((always_inline)) {
     const WorkItem it = load_record(c, k);
     const int row0 = kPipe ? prow0 : it.q0 + 32 * wave;
@@ -924,6 +934,8 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
     if constexpr (ACT == ACT_SOFTMAX) {
       const float l_tot = sum_halves(l);
       scale = l_tot > 0.f ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
+      if (c.lse != nullptr && qrow < it.lq)
+        c.lse[size_t(it.qbeg + qrow) * a.H + it.h] = (m * c2s + __log2f(l_tot)) * 0.69314718055994531f;
     } else {
       scale = __builtin_amdgcn_rcpf(float(it.lk));
     }

@@ -116,6 +116,7 @@ struct AttnArgs {
   float score_scale;  // softmax: log2(e)/sqrt(D); GELU: 1/sqrt(D)
   float eps;
   unsigned long long* stats;  // optional softmax counters (tile stream): tiles, max passes, rescales
+  float* lse;                  // optional softmax log-sum-exp per query row and head (natural log)
   // Tile stream without a plan launch (inplan = 1): every workgroup checks the
   // offsets and enumerates its own items; workgroup 0 writes the header (and
   // status_out).  B + 1 <= 512 offsets, bm query rows per item.

@@ -66,10 +66,11 @@ def test_workspace_grows_with_key_split_partials():
 
 
 def call(B=2, H=1, D=32, variant=0, act=0, window=0, dtype=0, tq=10, tk=10, ws_bytes=1 << 20,
-         ptr=4096, io=True, scales=False, fp8_pv=0):
+         ptr=4096, io=True, scales=False, fp8_pv=0, lse=None):
     j = _lib.JaIo()
     j.dtype = dtype
     j.fp8_pv = fp8_pv
+    j.lse = lse
     j.total_q, j.total_kv = tq, tk
     j.workspace = 1 << 20
     j.workspace_bytes = ws_bytes
@@ -97,6 +98,12 @@ def test_fwd_host_validation():
     assert call(dtype=_lib.JA_MXFP8_E4M3, scales=True, ws_bytes=16) == _lib.JA_EWORKSPACE
     assert call(fp8_pv=1) == _lib.JA_EUNSUPPORTED                      # fp8 P V: switched off
     assert call(fp8_pv=1, dtype=_lib.JA_MXFP8_E4M3, scales=True, D=128) == _lib.JA_EUNSUPPORTED
+    # the log-sum-exp output: softmax only, 4-byte aligned, tile-stream and fp32 shapes only
+    assert call(lse=4096, variant=_lib.JA_CROSS, act=_lib.JA_GELU_TANH, tk=7) == _lib.JA_EINVAL
+    assert call(lse=4098) == _lib.JA_EINVAL
+    assert call(lse=4096, variant=_lib.JA_PMA, dtype=_lib.JA_BF16, tk=70) == _lib.JA_EUNSUPPORTED
+    assert call(lse=4096, dtype=_lib.JA_MXFP8_E4M3, scales=True, D=64) == _lib.JA_EUNSUPPORTED
+    assert call(lse=4096, dtype=_lib.JA_MXFP8_E4M3, scales=True, D=128, window=320) == _lib.JA_EUNSUPPORTED
 
 
 def test_bwd_host_validation():
