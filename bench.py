@@ -321,7 +321,7 @@ def run_backward(args):
     and head (dV, dP, dQ and dK); the kernels also recompute the scores."""
     import torch
 
-    from recsys_jagged_attention_amd import backward, Workspace
+    from recsys_jagged_attention_amd import backward, forward, Workspace
     from recsys_jagged_attention_amd import workload as wl
     from recsys_jagged_attention_amd.inputs import make_workload, device_tensors
 
@@ -340,11 +340,21 @@ def run_backward(args):
     K, W = args.steps, args.warmup
     starts = [ev.create() for _ in range(K)]
     stops = [ev.create() for _ in range(K)]
+    saved = {}
+    if args.saved_stats:
+        # the forward's output and log-sum-exp, as a training step keeps them
+        # (computed once, outside the timed region)
+        if w.act != "softmax":
+            raise SystemExit("--saved-stats takes a softmax workload")
+        lse = torch.empty((w.total_q, w.H), dtype=torch.float32, device=dev)
+        o = forward(q, k, v, qo, ko, variant=w.variant, act=w.act, window=w.window, dtype=w.dtype, check=True,
+                    lse=lse)
+        saved = {"lse": lse, "fwd_out": o}
     run = lambda e=None: backward(q, k, v, dout, qo, ko, variant=w.variant, act=w.act, window=w.window,
-                                  dtype=w.dtype, workspace=wsp, events=e)
+                                  dtype=w.dtype, workspace=wsp, events=e, **saved)
     run()
     backward(q, k, v, dout, qo, ko, variant=w.variant, act=w.act, window=w.window, dtype=w.dtype, workspace=wsp,
-             check=True)
+             check=True, **saved)
     for _ in range(W):
         run()
     torch.cuda.synchronize()
@@ -391,7 +401,8 @@ def run_backward(args):
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "variant": w.variant, "act": w.act, "B": w.B, "H": w.H, "D": w.D,
-                   "window": w.window, "total_q": w.total_q, "useful_gflop": round(flops / 1e9, 3), "seed": w.seed},
+                   "window": w.window, "total_q": w.total_q, "useful_gflop": round(flops / 1e9, 3), "seed": w.seed,
+                   "row_stats": "from the forward" if saved else "recomputed"},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": None,
                      "kernel": kernels, "kernel_avg_us": round(kern_s * 1e6, 2),
@@ -421,6 +432,8 @@ def main():
                     help="MXFP8 workloads: O += P V on the fp8 MFMA too (P and V requantised along the keys)")
     ap.add_argument("--backward", action="store_true",
                     help="time the softmax backward on the workload instead of the forward")
+    ap.add_argument("--saved-stats", action="store_true",
+                    help="with --backward: hand the forward's output and log-sum-exp to the backward")
     ap.add_argument("--mx-quantize", action="store_true",
                     help="time the device MX quantiser instead of the attention forward")
     args = ap.parse_args()

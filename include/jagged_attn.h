@@ -167,6 +167,11 @@ typedef struct ja_io {
                              /* blocks).  bf16 PMA and the other MXFP8 calls    */
                              /* with it set return JA_EUNSUPPORTED, GELU calls  */
                              /* JA_EINVAL.  NULL: not written.                  */
+                             /* jagged_attn_bwd reads it instead (see there).   */
+  const void *fwd_out;       /* jagged_attn_bwd only, optional: the forward's   */
+                             /* output for the same arguments ([total_q, H, D], */
+                             /* the input dtype, 16-byte aligned), given with   */
+                             /* lse; jagged_attn_fwd ignores it.                */
 } ja_io;
 
 /* The forward pass.  Arguments as described above; window is 0 (no window) or
@@ -220,7 +225,13 @@ size_t jagged_attn_workspace_size(int B, int H, int D, int variant, int act,
  * JA_GELU_TANH; variant, window and offsets as for jagged_attn_fwd (JA_SELF
  * with or without a block window, JA_SLIDING, JA_CROSS, JA_PMA; no window
  * with GELU).  Nothing from the forward is needed: row statistics and RMS
- * factors are recomputed.  Workspace of jagged_attn_bwd_workspace_size()
+ * factors are recomputed.  A softmax call may hand over the forward's
+ * io->lse and io->fwd_out (both or neither; JA_EINVAL otherwise, and for GELU
+ * acts): the backward then takes each row's log-sum-exp from lse and
+ * D_i = sum_j P_ij dP_ij as dO_i . O_i from fwd_out, and skips the pass over
+ * the keys that recomputes them.  The gradients are those of the softmax
+ * with that log-sum-exp; O rounded to bf16 moves D_i by about 2^-9 of
+ * |dO_i| |O_i|.  Workspace of jagged_attn_bwd_workspace_size()
  * bytes in io->workspace; io->ev_start / ev_stop, when set, bracket the
  * gradient kernels (recorded around them on the stream); io->status as for
  * jagged_attn_fwd; io->max_workgroups is not used.  Asynchronous on io->stream; errors as for

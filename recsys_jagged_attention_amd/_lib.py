@@ -46,6 +46,7 @@ class JaIo(ctypes.Structure):
         ("softmax_stats", ctypes.c_void_p),
         ("fp8_pv", ctypes.c_int32),
         ("lse", ctypes.c_void_p),
+        ("fwd_out", ctypes.c_void_p),
     ]
 
 

@@ -166,12 +166,14 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tens
              variant: str = "self", act: str = "softmax", window: int = 0, dtype: str = "bf16",
              workspace: Optional[Workspace] = None, rms_eps: float = 1e-6,
              stream: Optional[torch.cuda.Stream] = None, check: Optional[bool] = None, events=None,
-             out=None):
+             out=None, lse: Optional[torch.Tensor] = None, fwd_out: Optional[torch.Tensor] = None):
     """Gradients of the forward (act "softmax" or "gelu_tanh"): returns float32
     (dq, dk, dv) shaped like q, k, v.  q/k/v/dout are "f32" or "bf16" tensors
     laid out as for ``forward``; ``stream`` and ``check`` as for ``forward``.
     ``out=(dq, dk, dv)`` gives the (contiguous float32) outputs; every element
-    of them is written."""
+    of them is written.  Softmax only: ``lse`` (the forward's float32 [Nq, H]
+    log-sum-exp) and ``fwd_out`` (its output) together let the backward skip
+    recomputing the row statistics."""
     if dtype not in ("f32", "bf16"):
         raise ValueError("backward takes f32 or bf16 inputs")
     want = _IN_DTYPES[dtype]
@@ -209,6 +211,15 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, dout: torch.Tens
     io.rms_eps = rms_eps
     if events is not None:
         io.ev_start, io.ev_stop = events
+    if lse is not None or fwd_out is not None:
+        if lse is None or fwd_out is None:
+            raise ValueError("lse and fwd_out go together")
+        if lse.dtype != torch.float32 or not lse.is_cuda or lse.shape != (Nq, H) or not lse.is_contiguous():
+            raise ValueError("lse must be a contiguous float32 [Nq, H] CUDA tensor")
+        if fwd_out.dtype != want or not fwd_out.is_cuda or fwd_out.shape != q.shape or not fwd_out.is_contiguous():
+            raise ValueError(f"fwd_out must be a contiguous {want} CUDA tensor shaped like q")
+        io.lse = lse.data_ptr()
+        io.fwd_out = fwd_out.data_ptr()
     rc = _lib.jagged_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), q_offsets.data_ptr(),
                               kv_offsets.data_ptr(), B, H, D, v_id, a_id, window, dq.data_ptr(),
                               dk.data_ptr(), dv.data_ptr(), io)

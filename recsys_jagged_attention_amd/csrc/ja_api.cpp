@@ -455,6 +455,11 @@ int jagged_attn_bwd(const void* q, const void* k, const void* v, const void* dou
                         static_cast<const void*>(dv), static_cast<const void*>(io->workspace)})
     if (!aligned16(p)) return JA_EINVAL;
   if (reinterpret_cast<uintptr_t>(io->status) & 3) return JA_EINVAL;
+  // the forward's log-sum-exp and output: both or neither, softmax only
+  if ((io->lse != nullptr) != (io->fwd_out != nullptr)) return JA_EINVAL;
+  if (io->lse != nullptr &&
+      (act != JA_SOFTMAX || (reinterpret_cast<uintptr_t>(io->lse) & 3) || !aligned16(io->fwd_out)))
+    return JA_EINVAL;
 
   hipStream_t stream = reinterpret_cast<hipStream_t>(io->stream);
   unsigned char* ws = reinterpret_cast<unsigned char*>(io->workspace);
@@ -495,6 +500,8 @@ int jagged_attn_bwd(const void* q, const void* k, const void* v, const void* dou
   ba.hdr_k = reinterpret_cast<const WsHeader*>(ws + L.hdr_k);
   ba.items_k = reinterpret_cast<const WorkItem*>(ws + L.items_k);
   ba.stats = reinterpret_cast<float2*>(ws + L.stats);
+  ba.lse_in = io->lse;
+  ba.o_in = io->fwd_out;
   ba.rq = reinterpret_cast<float*>(ws + L.rq);
   ba.rk = reinterpret_cast<float*>(ws + L.rk);
   ba.eps = io->rms_eps > 0.f ? io->rms_eps : 1e-6f;

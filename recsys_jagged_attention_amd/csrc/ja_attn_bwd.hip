@@ -160,34 +160,45 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_q_kernel(BwdArgs a) {
       for (int d = 0; d < DL; ++d) out[d] = fmaf(ri, dq[d], -q[d] * c3);
       continue;
     }
-    // row max and sum, base 2
-    float m = -__builtin_huge_valf(), l = 0.f;
-    for (int j = lo; j < hi; ++j) {
-      const T* kp = krow(kv, j);
-      float s = 0.f;
+    float lse, di = 0.f;
+    if (a.lse_in != nullptr) {
+      // the forward's log-sum-exp (natural log -> base 2 of the scaled
+      // scores; a row without keys takes 0) and D_i = dO_i . O_i
+      const float ln = a.lse_in[size_t(it.qbeg + qrow) * a.H + it.h];
+      lse = ln > -__builtin_huge_valf() ? ln * 1.4426950408889634f : 0.f;
+      const T* op = reinterpret_cast<const T*>(a.o_in) + qoff;
 #pragma unroll
-      for (int d = 0; d < DL; ++d) s = fmaf(q[d], ld(kp, d), s);
-      s = row_sum(s) * a.c2;
-      if (s > m) {
-        l *= exp2f(m - s);
-        m = s;
-      }
-      l += exp2f(s - m);
-    }
-    const float lse = hi > lo ? m + log2f(l) : 0.f;
-    // D_i = sum_j p_ij (dO_i . v_j)
-    float di = 0.f;
-    for (int j = lo; j < hi; ++j) {
-      const T* kp = krow(kv, j);
-      const T* vp = krow(vv, j);
-      float s = 0.f, dp = 0.f;
+      for (int d = 0; d < DL; ++d) di = fmaf(g[d], ld(op, d), di);
+      di = row_sum(di);
+    } else {
+      // row max and sum, base 2
+      float m = -__builtin_huge_valf(), l = 0.f;
+      for (int j = lo; j < hi; ++j) {
+        const T* kp = krow(kv, j);
+        float s = 0.f;
 #pragma unroll
-      for (int d = 0; d < DL; ++d) {
-        s = fmaf(q[d], ld(kp, d), s);
-        dp = fmaf(g[d], ld(vp, d), dp);
+        for (int d = 0; d < DL; ++d) s = fmaf(q[d], ld(kp, d), s);
+        s = row_sum(s) * a.c2;
+        if (s > m) {
+          l *= exp2f(m - s);
+          m = s;
+        }
+        l += exp2f(s - m);
       }
-      const float p = exp2f(row_sum(s) * a.c2 - lse);
-      di = fmaf(p, row_sum(dp), di);
+      lse = hi > lo ? m + log2f(l) : 0.f;
+      // D_i = sum_j p_ij (dO_i . v_j)
+      for (int j = lo; j < hi; ++j) {
+        const T* kp = krow(kv, j);
+        const T* vp = krow(vv, j);
+        float s = 0.f, dp = 0.f;
+#pragma unroll
+        for (int d = 0; d < DL; ++d) {
+          s = fmaf(q[d], ld(kp, d), s);
+          dp = fmaf(g[d], ld(vp, d), dp);
+        }
+        const float p = exp2f(row_sum(s) * a.c2 - lse);
+        di = fmaf(p, row_sum(dp), di);
+      }
     }
     // dQ_i = sum_j p_ij (dO_i . v_j - D_i) k_j / sqrt(D)
     for (int j = lo; j < hi; ++j) {

@@ -192,12 +192,26 @@ __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)
     const int qrow = r0 + l32;
     const int qr = min(qrow, it.lq - 1);
     bf16x8 qf[L::kS], gf[L::kS];
+    // With the forward's log-sum-exp and output: D_i = dO_i . O_i (this lane's
+    // half of the row; the halves are added below) instead of the first pass.
+    const bool saved = !kGelu && a.lse_in != nullptr;
+    float dot_o = 0.f, lse_ln = 0.f;
     {
       const size_t off = (size_t(it.qbeg + qr) * a.H + it.h) * D + (D / 2) * g;
 #pragma unroll
       for (int cc = 0; cc < L::kS; ++cc) {
         qf[cc] = *reinterpret_cast<const bf16x8*>(qg + off + 8 * cc);
         gf[cc] = *reinterpret_cast<const bf16x8*>(gg + off + 8 * cc);
+      }
+      if (saved) {
+        lse_ln = a.lse_in[size_t(it.qbeg + qr) * a.H + it.h];
+        const __bf16* og = reinterpret_cast<const __bf16*>(a.o_in) + off;
+#pragma unroll
+        for (int cc = 0; cc < L::kS; ++cc) {
+          const bf16x8 o8 = *reinterpret_cast<const bf16x8*>(og + 8 * cc);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) dot_o = fmaf(float(gf[cc][j]), float(o8[j]), dot_o);
+        }
       }
       // Wait here, before any tile load: the compiler then knows these are
       // complete and puts no wait for them (which would also drain the
@@ -272,8 +286,8 @@ __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)
     // Pass 1: online max, sum and sum of p * dP -> log-sum-exp (base 2) and
     // D_i = sum_j p_ij dP_ij of the row, for pass 2 and the dK/dV kernel.
     float m = -__builtin_huge_valf(), l = 0.f, acc = 0.f;
-    if (!kGelu && nt > 0) issue(0);
-    for (int s = 0; s < (kGelu ? 0 : nt); ++s) {
+    if (!kGelu && !saved && nt > 0) issue(0);
+    for (int s = 0; s < (kGelu || saved ? 0 : nt); ++s) {
       step_begin(s);
       const int t = t_lo + s;
       if (t >= wt_lo && t < wt_hi) {
@@ -303,10 +317,18 @@ __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)
       }
       lds_barrier();  // every wave is done with stage s & 1 before tile s + 2 loads into it
     }
-    l = sum_halves(l);
-    acc = sum_halves(acc);
-    const float lse = l > 0.f ? m + log2f(l) : 0.f;
-    const float di = l > 0.f ? acc / l : 0.f;
+    float lse, di;
+    if (saved) {
+      // natural log -> log2 units of the scaled scores; a row without keys
+      // (-inf) takes 0, as below, so that its masked weights stay 0
+      lse = lse_ln > -__builtin_huge_valf() ? lse_ln * 1.4426950408889634f : 0.f;
+      di = sum_halves(dot_o);
+    } else {
+      l = sum_halves(l);
+      acc = sum_halves(acc);
+      lse = l > 0.f ? m + log2f(l) : 0.f;
+      di = l > 0.f ? acc / l : 0.f;
+    }
     if (!kGelu && g == 0 && qrow < it.lq) a.stats[size_t(it.qbeg + qrow) * a.H + it.h] = make_float2(lse, di);
     // GELU: RMS factor of the query row, times 1/sqrt(D); 1/Lk
     const float rsc = kGelu ? a.rq[size_t(it.qbeg + qr) * a.H + it.h] * a.inv_sqrt_d : 0.f;

@@ -158,6 +158,8 @@ struct BwdArgs {
   const WsHeader* hdr_k;    // plan over key tiles (swapped offsets)
   const WorkItem* items_k;
   float2* stats;            // per (query row, head): log2-sum-exp of the scores, D_i
+  const float* lse_in;      // optional (softmax): the forward's natural log-sum-exp per (query row, head)
+  const void* o_in;         // with lse_in: the forward's output (input dtype), for D_i = dO_i . O_i
   float* rq;                // GELU: RMS factor per (query row, head)
   float* rk;                // GELU: RMS factor per (key row, head)
   int H;

@@ -120,9 +120,10 @@ def test_bwd_host_validation():
     assert _lib.jagged_attn_bwd_workspace_size(4, 2, 32, _lib.JA_SELF, _lib.JA_SOFTMAX, 0, _lib.JA_MXFP8_E4M3,
                                                100, 100) == 0
 
-    def call(act=_lib.JA_SOFTMAX, dtype=_lib.JA_BF16, ptr=4096, ws_bytes=1 << 24):
+    def call(act=_lib.JA_SOFTMAX, dtype=_lib.JA_BF16, ptr=4096, ws_bytes=1 << 24, lse=None, fwd_out=None):
         j = _lib.JaIo()
         j.dtype = dtype
+        j.lse, j.fwd_out = lse, fwd_out
         j.total_q = j.total_kv = 10
         j.workspace = 1 << 20
         j.workspace_bytes = ws_bytes
@@ -134,6 +135,12 @@ def test_bwd_host_validation():
     assert call(ptr=0) == _lib.JA_EINVAL
     assert call(ptr=4100) == _lib.JA_EINVAL
     assert call(ws_bytes=16) == _lib.JA_EWORKSPACE
+    # the forward's log-sum-exp and output: both or neither, softmax, aligned
+    assert call(lse=4096) == _lib.JA_EINVAL
+    assert call(fwd_out=4096) == _lib.JA_EINVAL
+    assert call(act=_lib.JA_GELU_TANH, lse=4096, fwd_out=4096) == _lib.JA_EINVAL
+    assert call(lse=4098, fwd_out=4096) == _lib.JA_EINVAL
+    assert call(lse=4096, fwd_out=4104) == _lib.JA_EINVAL
 
 
 def test_mx_quantize_host_validation():
