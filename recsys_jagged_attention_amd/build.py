@@ -27,10 +27,17 @@ COMMON = [
     "-I", INCLUDE, "-I", CSRC,
 ]
 
+# Per-source flags.  The dK/dV kernel keeps 128 fp32 accumulators per lane
+# across its query loop: with the MFMAs in their AGPR form the register
+# allocator moved them between AGPRs and VGPRs at every query step (about 600
+# v_accvgpr moves per 32 MFMAs, which made the kernel VALU-bound); the VGPR
+# form keeps everything in the 256 VGPRs, with no moves and no spills.
+EXTRA = {"ja_attn_bwd_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -271,11 +271,19 @@ __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)
         y = mfma_32x32x16(read_a<D>(vs, 32 * kb + kp, g, cc), gf[cc], y);
       }
       if constexpr (!kGelu) {
-        // scale to log2 units; disallowed and ragged keys -> -inf
+        // scale to log2 units; disallowed and ragged keys -> -inf.  (Branch
+        // free: bitwise tests, no short circuit.  A block window is uniform
+        // here: the wave's 32 queries share a block, and so do the tile's keys.)
+        bool uok = true;
+        if constexpr (WMODE == 1) {
+          const int bi = r0 / kBlock, bj = t;
+          uok = bj <= bi && bi - bj < a.window_blocks;
+        }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int j = 64 * t + 32 * kb + c_row(i, g);
-          const bool ok = j < it.lk && allowed<WMODE>(a, qrow, j);
+          bool ok = uok & (j < it.lk);
+          if constexpr (WMODE == 2) ok = ok & (j <= qrow) & (qrow - j < a.window_tokens);
           x[i] = ok ? x[i] * a.c2 : -__builtin_huge_valf();
         }
       }
@@ -303,12 +311,12 @@ __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)
           const float mn = fmaxf(m, max_halves(mx));
           // (no branch: the MFMAs of the next block run with the whole wave)
           const float mref = mn == -__builtin_huge_valf() ? 0.f : mn;  // nothing allowed yet
-          const float r = exp2f(m - mref);                              // m = -inf -> 0
+          const float r = fast_exp2(m - mref);                          // m = -inf -> 0
           l *= r;
           acc *= r;
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const float p = exp2f(sc[i] - mref);
+            const float p = fast_exp2(sc[i] - mref);
             l += p;
             acc = fmaf(p, dp[i], acc);
           }
@@ -363,7 +371,7 @@ __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)
             }
           } else {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) sc[i] = exp2f(sc[i] - lse) * (dp[i] - di);
+            for (int i = 0; i < 16; ++i) sc[i] = fast_exp2(sc[i] - lse) * (dp[i] - di);
           }
 #pragma unroll
           for (int half = 0; half < 2; ++half) {
@@ -543,13 +551,28 @@ __global__ __launch_bounds__(64 * kKWaves) __attribute__((amdgpu_waves_per_eu(2)
             dp[i] = ok ? gp * dp[i] * inv_lk * ri : 0.f;
           }
         } else {
+          // Mask without branches (bitwise tests, statistics read for every
+          // element, a masked element takes exp2(-inf) = 0).  A block window
+          // is the same for the step's 32 queries (one block: 32 t .. 32 t + 31
+          // lie in block t / 2) and this lane's key.
+          bool kok = krow < lk;
+          if constexpr (WMODE == 1) {
+            const int bq = t >> 1, bk = krow / kBlock;
+            kok = kok && bk <= bq && bq - bk < a.window_blocks;
+          }
+          const int qn = lq - 32 * t;  // queries of the step that exist: qi < qn
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int qi = c_row(i, g);
-            const int q = 32 * t + qi;
             const float2 sv = st[qi];
-            const bool ok = q < lq && krow < lk && allowed<WMODE>(a, q, krow);
-            const float p = ok ? exp2f(sc[i] * a.c2 - sv.x) : 0.f;
+            bool ok = kok & (qi < qn);
+            if constexpr (WMODE == 2) {
+              const int q = 32 * t + qi;
+              ok = ok & (krow <= q) & (q - krow < a.window_tokens);
+            }
+            // (the mask enters as an added 0 or -inf: a select with the LDS
+            // value as an operand would be turned into a branch around its load)
+            const float p = fast_exp2(fmaf(sc[i], a.c2, -sv.x) + (ok ? 0.f : -__builtin_huge_valf()));
             sc[i] = p;
             dp[i] = p * (dp[i] - sv.y);
           }
