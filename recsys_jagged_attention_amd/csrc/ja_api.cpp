@@ -26,6 +26,7 @@ hipError_t launch_attn_bwd(int D, bool bf16, int act, int wmode, const BwdArgs& 
                            int grid_q, int grid_k, hipStream_t st);
 hipError_t launch_attn_bwd_mfma(int D, int act, int wmode, const BwdArgs& a, int grid_q, int grid_k,
                                 hipStream_t st);
+int bwd_dkv_rows(int wmode);  // key rows per item of the MFMA dK/dV kernel
 hipError_t launch_bwd_rms(int D, bool bf16, const BwdArgs& a, int64_t rows_q, int64_t rows_k, hipStream_t st);
 hipError_t launch_mx_quant(bool bf16, const void* x, int64_t n_blocks, uint8_t* codes, uint8_t* scales,
                            hipStream_t st);
@@ -466,6 +467,7 @@ int jagged_attn_bwd(const void* q, const void* k, const void* v, const void* dou
   const bool self = variant == JA_SELF || variant == JA_SLIDING;
   // bf16 inputs on the matrix cores; fp32 inputs on the fp32 VALU kernels
   const bool mfma = io->dtype == JA_BF16;
+  const int wmode = variant == JA_SLIDING ? 2 : (variant == JA_SELF && window > 0 ? 1 : 0);
   for (int pass = 0; pass < 2; ++pass) {
     // pass 0: query tiles; pass 1: key tiles (the same plan on swapped offsets)
     PlanArgs pa{};
@@ -475,7 +477,7 @@ int jagged_attn_bwd(const void* q, const void* k, const void* v, const void* dou
     pa.H = H;
     pa.total_q = pass == 0 ? io->total_q : io->total_kv;
     pa.total_kv = pass == 0 ? io->total_kv : io->total_q;
-    pa.bm = mfma && pass == 0 ? kBwdRowsMfmaQ : kBwdRows;
+    pa.bm = mfma ? (pass == 0 ? kBwdRowsMfmaQ : bwd_dkv_rows(wmode)) : kBwdRows;
     pa.kvc = 0;
     pa.self_check = self;
     pa.max_items = pass == 0 ? L.max_q : L.max_k;
@@ -511,7 +513,6 @@ int jagged_attn_bwd(const void* q, const void* k, const void* v, const void* dou
   const float inv_sqrt_d = 1.0f / std::sqrt(float(D));
   ba.inv_sqrt_d = inv_sqrt_d;
   ba.c2 = inv_sqrt_d * 1.4426950408889634f;
-  const int wmode = variant == JA_SLIDING ? 2 : (ba.window_blocks > 0 ? 1 : 0);
   const int grid_q = int(std::min<int64_t>(L.max_q > 0 ? L.max_q : 1, kMaxGrid));
   const int grid_k = int(std::min<int64_t>(L.max_k > 0 ? L.max_k : 1, kMaxGrid));
   if (io->ev_start && hipEventRecord(reinterpret_cast<hipEvent_t>(io->ev_start), stream) != hipSuccess)

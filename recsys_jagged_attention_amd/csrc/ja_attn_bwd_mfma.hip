@@ -161,7 +161,32 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 constexpr int kQWaves = 4;  // dq kernel: 4 waves x 32 query rows (128-row items)
-constexpr int kKWaves = 2;  // dkv kernel: 2 waves x 32 key rows (64-row items)
+// dK/dV kernel shape: waves x 32 key rows per item, and query-tile stages.
+// Without a window, 4 waves (128-row items, 123 KB of LDS at D = 128) and
+// three stages: two query tiles load while one is used, and each tile serves
+// 128 keys.  With a window, the four waves' query ranges would differ (their
+// union walks tiles that half of them skip), so 2 waves (64-row items) and
+// two stages.
+constexpr int dkv_waves(int wmode) { return wmode == 0 ? 4 : 2; }
+constexpr int dkv_stages(int wmode) { return wmode == 0 ? 3 : 2; }
+
+// Loads wave w of the dK/dV kernel issues for one query tile: its share of
+// the Q and dO tiles, plus the statistics (or GELU: RMS factor) row on wave 0.
+template <int D, int KW>
+constexpr int dkv_step_loads(int w) {
+  return 2 * Dma<D, 32>::count(w, KW) + (w == 0 ? 1 : 0);
+}
+
+// Wait until at most one query tile's loads of this wave are outstanding
+// (the wave index is uniform: a scalar branch to an immediate wait).
+template <int D, int KW>
+__device__ __forceinline__ void wait_dkv_one_step(int wave) {
+  static_assert(KW == 2 || KW == 4, "two or four waves");
+  if (wave == 0) wait_vm<dkv_step_loads<D, KW>(0)>();
+  else if (KW == 2 || wave == 1) wait_vm<dkv_step_loads<D, KW>(1)>();
+  else if (wave == 2) wait_vm<dkv_step_loads<D, KW>(2)>();
+  else wait_vm<dkv_step_loads<D, KW>(3)>();
+}
 
 template <int D, int WMODE, int ACT>
 __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_mfma_kernel(BwdArgs a) {
@@ -426,17 +451,18 @@ __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)
 }
 
 template <int D, int WMODE, int ACT>
-__global__ __launch_bounds__(64 * kKWaves) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkv_mfma_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * dkv_waves(WMODE)) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkv_mfma_kernel(
+    BwdArgs a) {
+  constexpr int kKWaves = dkv_waves(WMODE), kKStages = dkv_stages(WMODE);
   using L = BT<D>;
   constexpr bool kGelu = ACT == ACT_GELU;
-  using TK = Dma<D, 64>;
+  using TK = Dma<D, 32 * kKWaves>;
   using TQ = Dma<D, 32>;
-  // per-wave DMAs of one query step: Q and dO tiles, plus the statistics or,
-  // with GELU, the query RMS factors (wave 0)
-  constexpr int kN0 = 2 * TQ::count(0, kKWaves) + 1, kN1 = 2 * TQ::count(1, kKWaves);
-  __shared__ __attribute__((aligned(1024))) unsigned char kvb[2][TK::kBytes];    // the item's K, V
-  __shared__ __attribute__((aligned(1024))) unsigned char qb[2][2][TQ::kBytes];  // [stage][Q, dO]
-  __shared__ __attribute__((aligned(256))) float2 stb[2][32];  // [stage] (lse, D_i); GELU: 64 floats, RMS factors
+  // LDS: the item's K and V (32 kKWaves rows), and kKStages stages of a
+  // 32-row query tile (Q, dO, statistics)
+  __shared__ __attribute__((aligned(1024))) unsigned char kvb[2][TK::kBytes];           // the item's K, V
+  __shared__ __attribute__((aligned(1024))) unsigned char qb[kKStages][2][TQ::kBytes];  // [stage][Q, dO]
+  __shared__ __attribute__((aligned(256))) float2 stb[kKStages][32];  // [stage] (lse, D_i); GELU: RMS factors
   const __bf16* qg = reinterpret_cast<const __bf16*>(a.q);
   const __bf16* kg = reinterpret_cast<const __bf16*>(a.k);
   const __bf16* vg = reinterpret_cast<const __bf16*>(a.v);
@@ -476,22 +502,23 @@ __global__ __launch_bounds__(64 * kKWaves) __attribute__((amdgpu_waves_per_eu(2)
     const __bf16* gbase = gg + size_t(qbeg) * gstride + size_t(it.h) * D;
     const float2* sbase = a.stats + size_t(qbeg) * a.H + it.h;
 
-    // Query tile t_lo + s into stage s & 1: Q, dO and the statistics.
+    // Query tile t_lo + s into stage s % kKStages: Q, dO and the statistics.
     auto issue_q = [&](int s) __attribute__((always_inline)) {
       const int t = t_lo + s;
       const int valid = min(32, lq - 32 * t);
-      const unsigned st = lds_q + unsigned(s & 1) * 2u * TQ::kBytes;
+      const unsigned stage = unsigned(s % kKStages);
+      const unsigned st = lds_q + stage * 2u * TQ::kBytes;
       dma_tile<D, 32, kKWaves>(st, qbase + size_t(32 * t) * gstride, grow, valid, wave, lane);
       dma_tile<D, 32, kKWaves>(st + TQ::kBytes, gbase + size_t(32 * t) * gstride, grow, valid, wave, lane);
       if (wave == 0) {
         if constexpr (kGelu) {
           const unsigned row = unsigned(min(lane, valid - 1));
           lds_dma4(a.rq + (size_t(qbeg) + 32 * t) * a.H + it.h, row * unsigned(a.H) * 4u,
-                   lds_st + unsigned(s & 1) * 256u);
+                   lds_st + stage * 256u);
         } else {
           const unsigned row = unsigned(min(lane >> 1, valid - 1));
           lds_dma4(sbase + size_t(32 * t) * a.H, (row * unsigned(a.H)) * 8u + 4u * unsigned(lane & 1),
-                   lds_st + unsigned(s & 1) * 256u);
+                   lds_st + stage * 256u);
         }
       }
     };
@@ -509,27 +536,31 @@ __global__ __launch_bounds__(64 * kKWaves) __attribute__((amdgpu_waves_per_eu(2)
     }
     if (nt > 0) {
       // the item's K and V rows stay in LDS (B operands read per use: the
-      // dK^T and dV^T accumulators take the registers)
-      const int valid = min(64, lk - it.q0);
+      // dK^T and dV^T accumulators take the registers); query tiles
+      // 0 .. kKStages - 2 start loading
+      const int valid = min(32 * kKWaves, lk - it.q0);
       const size_t off = size_t(kbeg + it.q0) * gstride + size_t(it.h) * D;
-      dma_tile<D, 64, kKWaves>(lds_kv, kg + off, grow, valid, wave, lane);
-      dma_tile<D, 64, kKWaves>(lds_kv + TK::kBytes, vg + off, grow, valid, wave, lane);
+      dma_tile<D, 32 * kKWaves, kKWaves>(lds_kv, kg + off, grow, valid, wave, lane);
+      dma_tile<D, 32 * kKWaves, kKWaves>(lds_kv + TK::kBytes, vg + off, grow, valid, wave, lane);
       issue_q(0);
+      if (kKStages == 3 && nt > 1) issue_q(1);
     }
     for (int s = 0; s < nt; ++s) {
-      if (s + 1 < nt) {
-        issue_q(s + 1);
-        if (wave == 0) wait_vm<kN0>();
-        else wait_vm<kN1>();
-      } else {
-        wait_vm<0>();
-      }
-      lds_barrier();  // tile s (and the item's K, V) in LDS for every wave
+      // Tile s has landed once only the loads of the tiles after it are
+      // outstanding (loads complete in order; the item's K and V came first):
+      // with three stages tile s + 1 may still load, with two none is issued.
+      if (kKStages == 3 && s + 1 < nt) wait_dkv_one_step<D, kKWaves>(wave);
+      else wait_vm<0>();
+      // Tile s (and the item's K, V) in LDS for every wave, and every wave is
+      // done with step s - 1: its stage takes tile s + kKStages - 1 now.
+      lds_barrier();
+      if (s + kKStages - 1 < nt) issue_q(s + kKStages - 1);
       const int t = t_lo + s;
+      const int stage = s % kKStages;
       if (t >= wt_lo && t < wt_hi) {
-        const __bf16* qs = reinterpret_cast<const __bf16*>(&qb[s & 1][0][0]);
-        const __bf16* gs = reinterpret_cast<const __bf16*>(&qb[s & 1][1][0]);
-        const float2* st = &stb[s & 1][0];
+        const __bf16* qs = reinterpret_cast<const __bf16*>(&qb[stage][0][0]);
+        const __bf16* gs = reinterpret_cast<const __bf16*>(&qb[stage][1][0]);
+        const float2* st = &stb[stage][0];
         f32x16 sc = {}, dp = {};
 #pragma unroll
         for (int cc = 0; cc < L::kS; ++cc) {
@@ -588,8 +619,8 @@ __global__ __launch_bounds__(64 * kKWaves) __attribute__((amdgpu_waves_per_eu(2)
           __builtin_amdgcn_sched_barrier(0);  // (bounds the operand reads in flight: registers)
         }
       }
-      lds_barrier();  // every wave is done with stage s & 1 before tile s + 2 loads into it
     }
+    lds_barrier();  // every wave is done with the item's LDS before the next item's loads
 #pragma unroll
     for (int t2 = 0; t2 < L::kT; ++t2) dk[t2] *= a.inv_sqrt_d;
     if constexpr (kGelu) {
@@ -638,7 +669,7 @@ __global__ __launch_bounds__(64 * kKWaves) __attribute__((amdgpu_waves_per_eu(2)
 template <int D, int WMODE, int ACT>
 hipError_t launch_w(const BwdArgs& a, int grid_q, int grid_k, hipStream_t st) {
   hipLaunchKernelGGL((bwd_dq_mfma_kernel<D, WMODE, ACT>), dim3(grid_q), dim3(64 * kQWaves), 0, st, a);
-  hipLaunchKernelGGL((bwd_dkv_mfma_kernel<D, WMODE, ACT>), dim3(grid_k), dim3(64 * kKWaves), 0, st, a);
+  hipLaunchKernelGGL((bwd_dkv_mfma_kernel<D, WMODE, ACT>), dim3(grid_k), dim3(64 * dkv_waves(WMODE)), 0, st, a);
   return hipGetLastError();
 }
 
@@ -651,6 +682,8 @@ hipError_t launch_dm(int act, int wmode, const BwdArgs& a, int grid_q, int grid_
 }
 
 }  // namespace
+
+int bwd_dkv_rows(int wmode) { return 32 * dkv_waves(wmode); }
 
 hipError_t launch_attn_bwd_mfma(int D, int act, int wmode, const BwdArgs& a, int grid_q, int grid_k,
                                 hipStream_t st) {

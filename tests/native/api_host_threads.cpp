@@ -89,6 +89,7 @@ hipError_t launch_attn_bwd(int, bool, int, int, const BwdArgs&, int64_t, int64_t
   return hipSuccess;
 }
 hipError_t launch_attn_bwd_mfma(int, int, int, const BwdArgs&, int, int, hipStream_t) { return hipSuccess; }
+int bwd_dkv_rows(int wmode) { return wmode == 0 ? 128 : 64; }
 hipError_t launch_bwd_rms(int, bool, const BwdArgs&, int64_t, int64_t, hipStream_t) { return hipSuccess; }
 hipError_t launch_mx_quant(bool, const void*, int64_t, uint8_t*, uint8_t*, hipStream_t) { return hipSuccess; }
 }  // namespace ja
