@@ -316,9 +316,11 @@ PEAK_VALU_F32 = 157.3  # TFLOP/s, fp32 vector (packed FMA); non-packed FMA issue
 
 
 def run_backward(args):
-    """Time the softmax backward (dQ, dK, dV) on a workload's tensors with a
-    seeded dout and print one JSON line.  Useful FLOPs: 8 D per attended pair
-    and head (dV, dP, dQ and dK); the kernels also recompute the scores."""
+    """Time the backward (dQ, dK, dV) on a workload's tensors with a seeded
+    dout and print one JSON line.  Softmax workloads hand the backward the
+    forward's output and log-sum-exp (computed once, untimed) unless
+    --recompute-stats.  Useful FLOPs: 8 D per attended pair and head (dV, dP,
+    dQ and dK); the kernels also recompute the scores."""
     import torch
 
     from recsys_jagged_attention_amd import backward, forward, Workspace
@@ -341,11 +343,9 @@ def run_backward(args):
     starts = [ev.create() for _ in range(K)]
     stops = [ev.create() for _ in range(K)]
     saved = {}
-    if args.saved_stats:
+    if w.act == "softmax" and not args.recompute_stats:
         # the forward's output and log-sum-exp, as a training step keeps them
         # (computed once, outside the timed region)
-        if w.act != "softmax":
-            raise SystemExit("--saved-stats takes a softmax workload")
         lse = torch.empty((w.total_q, w.H), dtype=torch.float32, device=dev)
         o = forward(q, k, v, qo, ko, variant=w.variant, act=w.act, window=w.window, dtype=w.dtype, check=True,
                     lse=lse)
@@ -432,8 +432,9 @@ def main():
                     help="MXFP8 workloads: O += P V on the fp8 MFMA too (P and V requantised along the keys)")
     ap.add_argument("--backward", action="store_true",
                     help="time the softmax backward on the workload instead of the forward")
-    ap.add_argument("--saved-stats", action="store_true",
-                    help="with --backward: hand the forward's output and log-sum-exp to the backward")
+    ap.add_argument("--recompute-stats", action="store_true",
+                    help="with --backward on a softmax workload: recompute the row statistics instead of "
+                         "handing the backward the forward's output and log-sum-exp (the default)")
     ap.add_argument("--mx-quantize", action="store_true",
                     help="time the device MX quantiser instead of the attention forward")
     args = ap.parse_args()
