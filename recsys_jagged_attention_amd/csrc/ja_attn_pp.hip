@@ -168,7 +168,9 @@ struct PPCtx {
   const unsigned char* vs;
   const float* kscale;
   __bf16* out;
-  float* lse;             // optional natural log-sum-exp per (query row, head) (softmax)
+  // optional natural log-sum-exp per (query row, head) (softmax): the
+  // pointer's halves, held in VGPRs (see lse_ptr)
+  unsigned lse_lo, lse_hi;
   int H;
   int G, pos, n;          // item k of this workgroup is item_index(k), k < n
   unsigned row_bytes;  // bytes between a head's input rows (bf16: 2 H D; MX8 codes: H D)
@@ -220,13 +222,21 @@ __device__ __forceinline__ Src make_src(const PPCtx& c, const WorkItem& w) {
   return r;
 }
 
+// The log-sum-exp output pointer (null: none).  Its halves pass through an
+// empty asm that puts them in VGPRs: the tile loop's scalar registers are
+// fully used, and a pointer kept there spilled others to VGPR lanes (more
+// v_readlane/v_writelane in the loop even when no log-sum-exp is asked for).
+__device__ __forceinline__ float* lse_ptr(const PPCtx& c) {
+  return reinterpret_cast<float*>((uint64_t(c.lse_hi) << 32) | c.lse_lo);
+}
+
 // Rows [32*wave, 32*wave + 32) of an item with no keys: the output is zero
 // (and the log-sum-exp over no keys -inf).
 template <int D>
 __device__ __forceinline__ void write_zero_rows(const PPCtx& c, const WorkItem& it, int wave, int lane) {
   const int qrow = it.q0 + 32 * wave + (lane & 31);
   if (qrow >= it.lq) return;
-  if (c.lse != nullptr && lane < 32) c.lse[size_t(it.qbeg + qrow) * c.H + it.h] = -__builtin_huge_valf();
+  if ((c.lse_lo | c.lse_hi) != 0u && lane < 32) lse_ptr(c)[size_t(it.qbeg + qrow) * c.H + it.h] = -__builtin_huge_valf();
   __bf16* orow = c.out + (size_t(it.qbeg + qrow) * c.H + it.h) * D + (D / 2) * (lane >> 5);
   bf16x8 z;
 #pragma unroll
@@ -520,7 +530,9 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
   c.vs = a.vs;
   c.kscale = a.kscale;
   c.out = reinterpret_cast<__bf16*>(a.out);
-  c.lse = a.lse;
+  c.lse_lo = unsigned(reinterpret_cast<uintptr_t>(a.lse));
+  c.lse_hi = unsigned(reinterpret_cast<uintptr_t>(a.lse) >> 32);
+  asm volatile("" : "+v"(c.lse_lo), "+v"(c.lse_hi));
   c.H = a.H;
   // (the grid is a multiple of 8 and workgroup w runs on XCD w % 8: positions
   // [x G/8, (x+1) G/8) are the workgroups of XCD x)
@@ -934,8 +946,8 @@ __global__ __launch_bounds__(64 * kPPWaves, 1) void attn_pp_kernel(AttnArgs a) {
     if constexpr (ACT == ACT_SOFTMAX) {
       const float l_tot = sum_halves(l);
       scale = l_tot > 0.f ? __builtin_amdgcn_rcpf(l_tot) : 0.f;
-      if (c.lse != nullptr && qrow < it.lq)
-        c.lse[size_t(it.qbeg + qrow) * a.H + it.h] = (m * c2s + __log2f(l_tot)) * 0.69314718055994531f;
+      if ((c.lse_lo | c.lse_hi) != 0u && qrow < it.lq)
+        lse_ptr(c)[size_t(it.qbeg + qrow) * a.H + it.h] = (m * c2s + __log2f(l_tot)) * 0.69314718055994531f;
     } else {
       scale = __builtin_amdgcn_rcpf(float(it.lk));
     }
