@@ -14,6 +14,7 @@
 
 namespace ja {
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st);
+hipError_t launch_plan_pair(const PlanArgs& a, const PlanArgs& b, hipStream_t st);
 hipError_t launch_attn_mfma(int D, int in, int shape, int act, const AttnArgs& a, int num_cu,
                             int64_t max_items, int64_t grid_cap, const KTiming& tm, hipStream_t st);
 hipError_t launch_combine(int D, const CombineArgs& a, hipStream_t st);
@@ -468,9 +469,12 @@ int jagged_attn_bwd(const void* q, const void* k, const void* v, const void* dou
   // bf16 inputs on the matrix cores; fp32 inputs on the fp32 VALU kernels
   const bool mfma = io->dtype == JA_BF16;
   const int wmode = variant == JA_SLIDING ? 2 : (variant == JA_SELF && window > 0 ? 1 : 0);
+  // Two plans, in one launch: over query tiles, and over key tiles (the same
+  // plan on swapped offsets).
+  PlanArgs plans[2];
   for (int pass = 0; pass < 2; ++pass) {
-    // pass 0: query tiles; pass 1: key tiles (the same plan on swapped offsets)
-    PlanArgs pa{};
+    PlanArgs& pa = plans[pass];
+    pa = PlanArgs{};
     pa.qo = pass == 0 ? q_offsets : kv_offsets;
     pa.ko = pass == 0 ? kv_offsets : q_offsets;
     pa.B = B;
@@ -487,8 +491,8 @@ int jagged_attn_bwd(const void* q, const void* k, const void* v, const void* dou
     pa.nsplit = reinterpret_cast<int32_t*>(ws + (pass == 0 ? L.nsplit_q : L.nsplit_k));
     pa.pbase = reinterpret_cast<int32_t*>(ws + (pass == 0 ? L.pbase_q : L.pbase_k));
     pa.items = reinterpret_cast<WorkItem*>(ws + (pass == 0 ? L.items_q : L.items_k));
-    if (launch_plan(pa, stream) != hipSuccess) return JA_EHIP;
   }
+  if (launch_plan_pair(plans[0], plans[1], stream) != hipSuccess) return JA_EHIP;
   BwdArgs ba{};
   ba.q = q;
   ba.k = k;

@@ -159,17 +159,8 @@ __device__ void key_rms_row(const PlanArgs& a, int64_t r) {
   a.krms_out[r] = __builtin_amdgcn_rsqf(ss * (1.0f / D) + a.krms_eps);
 }
 
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
-  if (blockIdx.x > 0) {
-    // the key RMS side job: rows (blockIdx.x - 1) * kPlanThreads + tid
-    const int64_t r = int64_t(blockIdx.x - 1) * kPlanThreads + threadIdx.x;
-    if (r < a.krms_rows) {
-      if (a.krms_d == 32) key_rms_row<32>(a, r);
-      else if (a.krms_d == 64) key_rms_row<64>(a, r);
-      else key_rms_row<128>(a, r);
-    }
-    return;
-  }
+// One plan, by one workgroup.
+__device__ __forceinline__ void plan_main(const PlanArgs& a) {
   __shared__ int s_bad;
   __shared__ int s_iwarp[3 * kPlanWaves];
   __shared__ Sums s_swarp[2 * kPlanWaves + 1];
@@ -332,6 +323,32 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     if (total_cost <= 0.0)
       for (int x = 1; x < kXcds; ++x) a.hdr->xcd_begin[x] = 0;
   }
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
+  if (blockIdx.x > 0) {
+    // the key RMS side job: rows (blockIdx.x - 1) * kPlanThreads + tid
+    const int64_t r = int64_t(blockIdx.x - 1) * kPlanThreads + threadIdx.x;
+    if (r < a.krms_rows) {
+      if (a.krms_d == 32) key_rms_row<32>(a, r);
+      else if (a.krms_d == 64) key_rms_row<64>(a, r);
+      else key_rms_row<128>(a, r);
+    }
+    return;
+  }
+  plan_main(a);
+}
+
+// Two independent plans in one launch (the backward's plans over query tiles
+// and over key tiles): workgroup 0 takes the first, workgroup 1 the second.
+__global__ __launch_bounds__(kPlanThreads) void plan_pair_kernel(PlanArgs a, PlanArgs b) {
+  plan_main(blockIdx.x == 0 ? a : b);
+}
+
+hipError_t launch_plan_pair(const PlanArgs& a, const PlanArgs& b, hipStream_t st) {
+  if (a.krms_rows > 0 || b.krms_rows > 0) return hipErrorInvalidValue;  // (no side job here)
+  hipLaunchKernelGGL(plan_pair_kernel, dim3(2), dim3(kPlanThreads), 0, st, a, b);
+  return hipGetLastError();
 }
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t st) {

@@ -66,6 +66,10 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t) {
   if (!a.hdr || !a.items || a.max_items < 0) g_errors.fetch_add(1);
   return hipSuccess;
 }
+hipError_t launch_plan_pair(const PlanArgs& a, const PlanArgs& b, hipStream_t st) {
+  launch_plan(a, st);
+  return launch_plan(b, st);
+}
 hipError_t launch_attn_mfma(int, int, int, int, const AttnArgs&, int num_cu, int64_t, int64_t, const KTiming&,
                             hipStream_t) {
   expect_cus(num_cu);
