@@ -346,10 +346,16 @@ def run_backward(args):
     if w.act == "softmax" and not args.recompute_stats:
         # the forward's output and log-sum-exp, as a training step keeps them
         # (computed once, outside the timed region)
+        # (bf16 PMA's key-split forward gives no log-sum-exp: recomputed there)
+        from recsys_jagged_attention_amd import JaggedAttnError, JA_EUNSUPPORTED
         lse = torch.empty((w.total_q, w.H), dtype=torch.float32, device=dev)
-        o = forward(q, k, v, qo, ko, variant=w.variant, act=w.act, window=w.window, dtype=w.dtype, check=True,
-                    lse=lse)
-        saved = {"lse": lse, "fwd_out": o}
+        try:
+            o = forward(q, k, v, qo, ko, variant=w.variant, act=w.act, window=w.window, dtype=w.dtype, check=True,
+                        lse=lse)
+            saved = {"lse": lse, "fwd_out": o}
+        except JaggedAttnError as e:
+            if e.status != JA_EUNSUPPORTED:
+                raise
     run = lambda e=None: backward(q, k, v, dout, qo, ko, variant=w.variant, act=w.act, window=w.window,
                                   dtype=w.dtype, workspace=wsp, events=e, **saved)
     run()

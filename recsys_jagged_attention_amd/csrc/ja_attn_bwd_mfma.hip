@@ -161,14 +161,15 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 constexpr int kQWaves = 4;  // dq kernel: 4 waves x 32 query rows (128-row items)
-// dK/dV kernel shape: waves x 32 key rows per item, and query-tile stages.
-// Without a window, 4 waves (128-row items, 123 KB of LDS at D = 128) and
-// three stages: two query tiles load while one is used, and each tile serves
-// 128 keys.  With a window, the four waves' query ranges would differ (their
-// union walks tiles that half of them skip), so 2 waves (64-row items) and
-// two stages.
-constexpr int dkv_waves(int wmode) { return wmode == 0 ? 4 : 2; }
-constexpr int dkv_stages(int wmode) { return wmode == 0 ? 3 : 2; }
+// dK/dV kernel shape: KW waves x 32 key rows per item, and query-tile stages.
+// KW = 4 (no window, long key runs): 128-row items, 123 KB of LDS at D = 128,
+// and three stages, two query tiles loading while one is used, each tile
+// serving 128 keys.  KW = 2 otherwise: with a window the four waves' query
+// ranges would differ (their union walks tiles that half of them skip), and
+// with short key runs (cross-attention's 16-64 keys) half of a 128-row item's
+// waves would hold the CU's LDS with nothing to do; 64-row items and two
+// stages, two workgroups per CU.
+constexpr int dkv_stages(int kw) { return kw == 4 ? 3 : 2; }
 
 // Loads wave w of the dK/dV kernel issues for one query tile: its share of
 // the Q and dO tiles, plus the statistics (or GELU: RMS factor) row on wave 0.
@@ -450,10 +451,10 @@ __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)
   }
 }
 
-template <int D, int WMODE, int ACT>
-__global__ __launch_bounds__(64 * dkv_waves(WMODE)) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkv_mfma_kernel(
-    BwdArgs a) {
-  constexpr int kKWaves = dkv_waves(WMODE), kKStages = dkv_stages(WMODE);
+template <int D, int WMODE, int ACT, int KW>
+__global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkv_mfma_kernel(BwdArgs a) {
+  constexpr int kKWaves = KW, kKStages = dkv_stages(KW);
+  static_assert(KW == 2 || (KW == 4 && WMODE == 0), "four waves only without a window");
   using L = BT<D>;
   constexpr bool kGelu = ACT == ACT_GELU;
   using TK = Dma<D, 32 * kKWaves>;
@@ -667,29 +668,40 @@ __global__ __launch_bounds__(64 * dkv_waves(WMODE)) __attribute__((amdgpu_waves_
 }
 
 template <int D, int WMODE, int ACT>
-hipError_t launch_w(const BwdArgs& a, int grid_q, int grid_k, hipStream_t st) {
+hipError_t launch_w(const BwdArgs& a, int grid_q, int grid_k, bool wide, hipStream_t st) {
   hipLaunchKernelGGL((bwd_dq_mfma_kernel<D, WMODE, ACT>), dim3(grid_q), dim3(64 * kQWaves), 0, st, a);
-  hipLaunchKernelGGL((bwd_dkv_mfma_kernel<D, WMODE, ACT>), dim3(grid_k), dim3(64 * dkv_waves(WMODE)), 0, st, a);
+  if constexpr (WMODE == 0) {
+    if (wide) {
+      hipLaunchKernelGGL((bwd_dkv_mfma_kernel<D, WMODE, ACT, 4>), dim3(grid_k), dim3(64 * 4), 0, st, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((bwd_dkv_mfma_kernel<D, WMODE, ACT, 2>), dim3(grid_k), dim3(64 * 2), 0, st, a);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_dm(int act, int wmode, const BwdArgs& a, int grid_q, int grid_k, hipStream_t st) {
-  if (act == ACT_GELU) return launch_w<D, 0, ACT_GELU>(a, grid_q, grid_k, st);  // (no window with GELU)
-  if (wmode == 1) return launch_w<D, 1, ACT_SOFTMAX>(a, grid_q, grid_k, st);
-  if (wmode == 2) return launch_w<D, 2, ACT_SOFTMAX>(a, grid_q, grid_k, st);
-  return launch_w<D, 0, ACT_SOFTMAX>(a, grid_q, grid_k, st);
+hipError_t launch_dm(int act, int wmode, const BwdArgs& a, int grid_q, int grid_k, bool wide, hipStream_t st) {
+  if (act == ACT_GELU) return launch_w<D, 0, ACT_GELU>(a, grid_q, grid_k, wide, st);  // (no window with GELU)
+  if (wmode == 1) return launch_w<D, 1, ACT_SOFTMAX>(a, grid_q, grid_k, false, st);
+  if (wmode == 2) return launch_w<D, 2, ACT_SOFTMAX>(a, grid_q, grid_k, false, st);
+  return launch_w<D, 0, ACT_SOFTMAX>(a, grid_q, grid_k, wide, st);
 }
 
 }  // namespace
 
-int bwd_dkv_rows(int wmode) { return 32 * dkv_waves(wmode); }
+bool bwd_dkv_wide(int wmode, int B, int32_t total_kv) {
+  // four waves only without a window and with key runs of 128 or more on average
+  return wmode == 0 && int64_t(total_kv) >= int64_t(128) * B;
+}
 
-hipError_t launch_attn_bwd_mfma(int D, int act, int wmode, const BwdArgs& a, int grid_q, int grid_k,
+int bwd_dkv_rows(bool wide) { return wide ? 128 : 64; }
+
+hipError_t launch_attn_bwd_mfma(int D, int act, int wmode, const BwdArgs& a, int grid_q, int grid_k, bool wide,
                                 hipStream_t st) {
-  if (D == 32) return launch_dm<32>(act, wmode, a, grid_q, grid_k, st);
-  if (D == 64) return launch_dm<64>(act, wmode, a, grid_q, grid_k, st);
-  return launch_dm<128>(act, wmode, a, grid_q, grid_k, st);
+  if (D == 32) return launch_dm<32>(act, wmode, a, grid_q, grid_k, wide, st);
+  if (D == 64) return launch_dm<64>(act, wmode, a, grid_q, grid_k, wide, st);
+  return launch_dm<128>(act, wmode, a, grid_q, grid_k, wide, st);
 }
 
 }  // namespace ja

@@ -62,6 +62,19 @@ def test_self_variants(variant, window, D, dtype):
     run(variant, window, dtype, qo, ko, q, k, v, seed=window)
 
 
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("variant,act", [("self", "softmax"), ("cross", "softmax"), ("cross", "gelu_tanh")])
+def test_long_key_runs(variant, act, D):
+    """Key runs of 128 or more on average: the MFMA dK/dV kernel's 4-wave,
+    128-key-item shape (shorter runs and windows take the 2-wave shape, which
+    the edge-length cases cover)."""
+    lq = [300, 129, 0, 200, 513]
+    lk = lq if variant == "self" else [260, 1, 0, 190, 400]
+    qo, ko, q, k, v = random_jagged(60 + D, lq, lk, 2, D)
+    log(f"backward long key runs {variant} {act} D={D}")
+    run(variant, 0, "bf16", qo, ko, q, k, v, seed=9, act=act)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_cross_and_pma(dtype):
     qo, ko, q, k, v = random_jagged(41, [300, 0, 17, 64], [40, 9, 0, 1], 2, 64)
