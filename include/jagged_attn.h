@@ -160,13 +160,12 @@ typedef struct ja_io {
                              /* natural log-sum-exp of its scaled scores over   */
                              /* the keys the row attends,                       */
                              /* log sum_j exp(q.k_j / sqrt(D)), or -inf for a   */
-                             /* row without keys.  Written by the tile-stream   */
-                             /* and fp32 shapes: every fp32 call, bf16 calls    */
-                             /* other than PMA, and MXFP8 self-attention at     */
-                             /* D = 128 (full, or windows of up to four         */
-                             /* blocks).  bf16 PMA and the other MXFP8 calls    */
-                             /* with it set return JA_EUNSUPPORTED, GELU calls  */
-                             /* JA_EINVAL.  NULL: not written.                  */
+                             /* row without keys.  Every fp32 and bf16 call,    */
+                             /* and MXFP8 PMA and self-attention at D = 128     */
+                             /* (full, or windows of up to four blocks); the    */
+                             /* other MXFP8 calls with it set return            */
+                             /* JA_EUNSUPPORTED, GELU calls JA_EINVAL.  NULL:   */
+                             /* not written.                                    */
                              /* jagged_attn_bwd reads it instead (see there).   */
   const void *fwd_out;       /* jagged_attn_bwd only, optional: the forward's   */
                              /* output for the same arguments ([total_q, H, D], */

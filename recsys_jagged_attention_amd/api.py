@@ -62,8 +62,9 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     along the keys); this version does not provide it and raises
     JaggedAttnError with JA_EUNSUPPORTED.  ``lse`` (a contiguous float32
     [Nq, H] CUDA tensor, softmax only) receives each query row's natural
-    log-sum-exp of its scaled scores, -inf for rows without keys; bf16 PMA and
-    MXFP8 calls other than D = 128 self-attention raise JA_EUNSUPPORTED."""
+    log-sum-exp of its scaled scores, -inf for rows without keys (MXFP8 calls
+    other than PMA and D = 128 self-attention with windows of at most four
+    blocks raise JA_EUNSUPPORTED)."""
     if dtype not in _IN_DTYPES:
         raise ValueError(f"dtype must be one of {list(_IN_DTYPES)}")
     want = _IN_DTYPES[dtype]

@@ -178,11 +178,12 @@ int fwd_impl(const void* q, const void* k, const void* v, const int32_t* q_offse
   // the GPU on its first run and the cause has not been found, so no call
   // launches it.
   if (io.fp8_pv) return JA_EUNSUPPORTED;
-  // the log-sum-exp output: softmax only, from the tile-stream and fp32 shapes
+  // the log-sum-exp output: softmax only, written by the tile-stream, fp32 and
+  // key-split (PMA) shapes
   if (io.lse != nullptr) {
     if (act != JA_SOFTMAX || (reinterpret_cast<uintptr_t>(io.lse) & 3)) return JA_EINVAL;
     const int shape = make_plan(B, H, D, variant, act, window, io.dtype, io.total_q, io.total_kv).shape;
-    if (shape != kShapePingPong && shape != kShapeF32) return JA_EUNSUPPORTED;
+    if (shape != kShapePingPong && shape != kShapeF32 && shape != kShapeKvSplit) return JA_EUNSUPPORTED;
   }
   // Empty tensors may come with null data pointers: no kernel reads q or
   // writes out without query rows, nor reads k or v without key rows.
@@ -316,6 +317,7 @@ int fwd_impl(const void* q, const void* k, const void* v, const int32_t* q_offse
     ca.pbase = pbase;
     ca.part_o = part_o;
     ca.part_ml = part_ml;
+    ca.lse = io.lse;
     ca.B = B;
     ca.H = H;
     ca.act = act;

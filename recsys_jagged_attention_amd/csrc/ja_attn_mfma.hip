@@ -781,6 +781,16 @@ __global__ __launch_bounds__(64 * NWQ * NWK, QSUB == 2 ? 1 : 2) void attn_kernel
               for (int j = 0; j < 8; ++j) ov[j] = (__bf16)(o[qs][t][i + j] * scale);
               *reinterpret_cast<bf16x8*>(orow + 16 * t + i) = ov;
             }
+          if constexpr (ACT == ACT_SOFTMAX && SPLIT) {
+            // log-sum-exp output of the key-split (PMA) shape, for a sample
+            // taken whole: ln sum_j exp(s_j / sqrt(D)) = (m c2 + log2 l) ln 2,
+            // m the row's reference max of the raw scores (-inf without keys).
+            // (Not in the other instances: at D = 32 / 64 with MX inputs the
+            // store cost them a third of their occupancy.)
+            if (a.lse != nullptr && g == 0)
+              a.lse[size_t(cur.qbeg + qrow) * a.H + cur.h] =
+                  l_tot > 0.f ? (m[qs] * c2 + __log2f(l_tot)) * 0.69314718055994531f : -__builtin_huge_valf();
+          }
         }
       }
     }
@@ -826,6 +836,10 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
         for (int j = 0; j < 8; ++j) acc[j] = fmaf(w, po[j], acc[j]);
       }
       scale = lsum > 0.f ? 1.0f / lsum : 0.f;
+      // log-sum-exp output (the partial maxima are in base-2 units)
+      if (a.lse != nullptr && c == 0)
+        a.lse[size_t(qbeg + r) * a.H + h] = lsum > 0.f ? (mu + __log2f(lsum)) * 0.69314718055994531f
+                                                        : -__builtin_huge_valf();
     } else {
       for (int s = 0; s < ns; ++s) {
         const float* po = a.part_o + ((slot0 + s) * kPmaRows + r) * D + 8 * c;

@@ -179,6 +179,7 @@ struct CombineArgs {
   const int32_t* pbase;
   const float* part_o;
   const float2* part_ml;
+  float* lse;  // optional log-sum-exp output (softmax)
   int B, H, act;
 };
 

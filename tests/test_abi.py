@@ -98,10 +98,11 @@ def test_fwd_host_validation():
     assert call(dtype=_lib.JA_MXFP8_E4M3, scales=True, ws_bytes=16) == _lib.JA_EWORKSPACE
     assert call(fp8_pv=1) == _lib.JA_EUNSUPPORTED                      # fp8 P V: switched off
     assert call(fp8_pv=1, dtype=_lib.JA_MXFP8_E4M3, scales=True, D=128) == _lib.JA_EUNSUPPORTED
-    # the log-sum-exp output: softmax only, 4-byte aligned, tile-stream and fp32 shapes only
+    # the log-sum-exp output: softmax only, 4-byte aligned
     assert call(lse=4096, variant=_lib.JA_CROSS, act=_lib.JA_GELU_TANH, tk=7) == _lib.JA_EINVAL
+    assert call(lse=4096, variant=_lib.JA_PMA, act=_lib.JA_GELU_TANH, dtype=_lib.JA_BF16, tk=70) == _lib.JA_EINVAL
     assert call(lse=4098) == _lib.JA_EINVAL
-    assert call(lse=4096, variant=_lib.JA_PMA, dtype=_lib.JA_BF16, tk=70) == _lib.JA_EUNSUPPORTED
+    assert call(lse=4098, variant=_lib.JA_PMA, dtype=_lib.JA_BF16, tk=70) == _lib.JA_EINVAL
     assert call(lse=4096, dtype=_lib.JA_MXFP8_E4M3, scales=True, D=64) == _lib.JA_EUNSUPPORTED
     assert call(lse=4096, dtype=_lib.JA_MXFP8_E4M3, scales=True, D=128, window=320) == _lib.JA_EUNSUPPORTED
 

@@ -104,6 +104,17 @@ def test_lse_cross_with_keyless_samples(dtype, D):
     log(f"  max err {check_lse(w):.3e}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "mxfp8"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_lse_pma_key_split(dtype, D):
+    """The key-split shape: samples long enough to be split (the merge writes
+    the log-sum-exp), short ones taken whole (the attention kernel writes it),
+    and a sample without keys (-inf)."""
+    w = adhoc("pma", dtype, [32, 32, 32, 32, 32], [0, 100, 1500, 4100, 33], 2, D, seed=D + 13)
+    log(f"lse pma {dtype} D={D}")
+    log(f"  max err {check_lse(w):.3e}")
+
+
 def test_lse_f32_pma():
     w = adhoc("pma", "f32", [32, 32, 32, 32], [0, 100, 700, 33], 2, 64, seed=11)
     log("lse f32 pma")
@@ -117,7 +128,7 @@ def test_lse_mxfp8_self(window):
     log(f"  max err {check_lse(w):.3e}")
 
 
-@pytest.mark.parametrize("name", ["block_window", "full_self", "sliding_window"])
+@pytest.mark.parametrize("name", ["block_window", "full_self", "sliding_window", "pma"])
 def test_lse_full_size(name):
     """The softmax workloads at their full sizes, every row against the oracle."""
     w = make_workload(name)
