@@ -27,7 +27,7 @@ hipError_t launch_attn_bwd(int D, bool bf16, int act, int wmode, const BwdArgs& 
                            int grid_q, int grid_k, hipStream_t st);
 hipError_t launch_attn_bwd_mfma(int D, int act, int wmode, const BwdArgs& a, int grid_q, int grid_k, bool wide,
                                 hipStream_t st);
-bool bwd_dkv_wide(int wmode, int B, int32_t total_kv);  // the 4-wave shape of the MFMA dK/dV kernel?
+bool bwd_dkv_wide(int act, int wmode, int B, int32_t total_kv);  // the 4-wave shape of the MFMA dK/dV kernel?
 int bwd_dkv_rows(bool wide);                            // key rows per item of that kernel
 hipError_t launch_bwd_rms(int D, bool bf16, const BwdArgs& a, int64_t rows_q, int64_t rows_k, hipStream_t st);
 hipError_t launch_mx_quant(bool bf16, const void* x, int64_t n_blocks, uint8_t* codes, uint8_t* scales,
@@ -472,7 +472,7 @@ int jagged_attn_bwd(const void* q, const void* k, const void* v, const void* dou
   // bf16 inputs on the matrix cores; fp32 inputs on the fp32 VALU kernels
   const bool mfma = io->dtype == JA_BF16;
   const int wmode = variant == JA_SLIDING ? 2 : (variant == JA_SELF && window > 0 ? 1 : 0);
-  const bool wide = bwd_dkv_wide(wmode, B, io->total_kv);
+  const bool wide = bwd_dkv_wide(act == JA_SOFTMAX ? ACT_SOFTMAX : ACT_GELU, wmode, B, io->total_kv);
   // Two plans, in one launch: over query tiles, and over key tiles (the same
   // plan on swapped offsets).
   PlanArgs plans[2];

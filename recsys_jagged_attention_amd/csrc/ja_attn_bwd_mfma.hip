@@ -667,9 +667,181 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(2))) vo
   }
 }
 
+// Softmax dK/dV with the work of a 32-key group split over a wave pair: the
+// "V wave" forms S = Q K^T, the weights P from the stored statistics, and
+// accumulates dV^T += dO^T P; the "K wave" forms dP = dO V^T, takes P through
+// LDS, and accumulates dK^T += Q^T dS with dS = P (dP - D_i).  Each wave holds
+// 64 accumulators and issues 16 MFMAs per query step, so two workgroups of
+// 4 waves (64-key items, 78.5 KB of LDS at D = 128) share a CU: two waves per
+// SIMD, one's VALU work under the other's MFMAs (the one-wave-per-SIMD form
+// above leaves both exposed).  Query tiles in two stages; the next tile's
+// loads are issued after the step's first barrier, into the stage every wave
+// has finished with.
+constexpr int kPairWaves = 4;  // 2 pairs x (V wave, K wave), 32 keys per pair
+
+template <int D, int WMODE>
+__global__ __launch_bounds__(64 * kPairWaves) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkv_pair_kernel(
+    BwdArgs a) {
+  using L = BT<D>;
+  using TK = Dma<D, 64>;
+  using TQ = Dma<D, 32>;
+  __shared__ __attribute__((aligned(1024))) unsigned char kvb[2][TK::kBytes];    // the item's K, V (64 rows)
+  __shared__ __attribute__((aligned(1024))) unsigned char qb[2][2][TQ::kBytes];  // [stage][Q, dO]
+  __shared__ __attribute__((aligned(256))) float2 stb[2][32];                    // [stage] (lse, D_i)
+  __shared__ __attribute__((aligned(256))) float pxb[2][16][64];                 // [pair] P, lane-major
+  const __bf16* qg = reinterpret_cast<const __bf16*>(a.q);
+  const __bf16* kg = reinterpret_cast<const __bf16*>(a.k);
+  const __bf16* vg = reinterpret_cast<const __bf16*>(a.v);
+  const __bf16* gg = reinterpret_cast<const __bf16*>(a.dout);
+  const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // (scalar: uniform branches)
+  const int pair = wave >> 1;
+  const bool vwave = (wave & 1) == 0;
+  const int kp = key_perm(l32);
+  const size_t gstride = size_t(a.H) * D;
+  const unsigned grow = unsigned(gstride) * 2u;
+  const unsigned lds_kv = lds_addr_of(&kvb[0][0]), lds_q = lds_addr_of(&qb[0][0][0]);
+  const unsigned lds_st = lds_addr_of(&stb[0][0]);
+  const __bf16* kst = reinterpret_cast<const __bf16*>(&kvb[0][0]);
+  const __bf16* vst = reinterpret_cast<const __bf16*>(&kvb[1][0]);
+  float* px = &pxb[pair][0][0];
+  const int n_items = a.hdr_k->n_items;
+  for (int idx = blockIdx.x; idx < n_items; idx += gridDim.x) {
+    // (items over key tiles: the plan ran on the swapped offsets)
+    const WorkItem it = a.items_k[idx];
+    const int lk = it.lq, lq = it.lk, kbeg = it.qbeg, qbeg = it.kbeg;
+    const int k0 = it.q0 + 32 * pair;
+    const int krow = k0 + l32;
+    int qlo, qhi;
+    wave_queries<WMODE>(a, k0, lq, lk, qlo, qhi);
+    const int wt_lo = qlo / 32, wt_hi = qhi > qlo ? (qhi + 31) / 32 : wt_lo;
+    int t_lo = 1 << 30, t_hi = 0;
+    for (int pp = 0; pp < 2; ++pp) {
+      int lo, hi;
+      wave_queries<WMODE>(a, it.q0 + 32 * pp, lq, lk, lo, hi);
+      if (hi > lo) {
+        t_lo = min(t_lo, lo / 32);
+        t_hi = max(t_hi, (hi + 31) / 32);
+      }
+    }
+    if (t_lo > t_hi) t_lo = t_hi;
+    const int nt = t_hi - t_lo;
+    const __bf16* qbase = qg + size_t(qbeg) * gstride + size_t(it.h) * D;
+    const __bf16* gbase = gg + size_t(qbeg) * gstride + size_t(it.h) * D;
+    const float2* sbase = a.stats + size_t(qbeg) * a.H + it.h;
+
+    // Query tile t_lo + s into stage s & 1: Q, dO and the statistics.
+    auto issue_q = [&](int s) __attribute__((always_inline)) {
+      const int t = t_lo + s;
+      const int valid = min(32, lq - 32 * t);
+      const unsigned stage = unsigned(s & 1);
+      const unsigned st = lds_q + stage * 2u * TQ::kBytes;
+      dma_tile<D, 32, kPairWaves>(st, qbase + size_t(32 * t) * gstride, grow, valid, wave, lane);
+      dma_tile<D, 32, kPairWaves>(st + TQ::kBytes, gbase + size_t(32 * t) * gstride, grow, valid, wave, lane);
+      if (wave == 0) {
+        const unsigned row = unsigned(min(lane >> 1, valid - 1));
+        lds_dma4(sbase + size_t(32 * t) * a.H, (row * unsigned(a.H)) * 8u + 4u * unsigned(lane & 1),
+                 lds_st + stage * 256u);
+      }
+    };
+
+    f32x16 acc[L::kT];  // dV^T (V wave) or dK^T (K wave) of the pair's 32 keys
+#pragma unroll
+    for (int t2 = 0; t2 < L::kT; ++t2) acc[t2] = f32x16{};
+    if (nt > 0) {
+      const int valid = min(64, lk - it.q0);
+      const size_t off = size_t(kbeg + it.q0) * gstride + size_t(it.h) * D;
+      dma_tile<D, 64, kPairWaves>(lds_kv, kg + off, grow, valid, wave, lane);
+      dma_tile<D, 64, kPairWaves>(lds_kv + TK::kBytes, vg + off, grow, valid, wave, lane);
+      issue_q(0);
+    }
+    // the pair's key range is uniform over its window per step: a block
+    // window tests it once (the step's 32 queries lie in block t / 2)
+    for (int s = 0; s < nt; ++s) {
+      wait_vm<0>();   // tile s (and the item's K, V): nothing else is in flight
+      lds_barrier();  // ... in LDS for every wave; every wave is done with step s - 1
+      if (s + 1 < nt) issue_q(s + 1);
+      const int t = t_lo + s;
+      const int stage = s & 1;
+      const bool active = t >= wt_lo && t < wt_hi;
+      const __bf16* qs = reinterpret_cast<const __bf16*>(&qb[stage][0][0]);
+      const __bf16* gs = reinterpret_cast<const __bf16*>(&qb[stage][1][0]);
+      const float2* st = &stb[stage][0];
+      f32x16 x = {};
+      if (active) {
+        // V wave: S = Q K^T; K wave: dP = dO V^T (key as lane column)
+        const __bf16* as = vwave ? qs : gs;
+        const __bf16* bs = vwave ? kst : vst;
+#pragma unroll
+        for (int cc = 0; cc < L::kS; ++cc)
+          x = mfma_32x32x16(read_a<D>(as, kp, g, cc), read_a<D>(bs, 32 * pair + l32, g, cc), x);
+        if (vwave) {
+          // P from the stored log-sum-exp, masked without branches (the
+          // mask enters as an added 0 or -inf under the raw exp2)
+          bool kok = krow < lk;
+          if constexpr (WMODE == 1) {
+            const int bq = t >> 1, bk = krow / kBlock;
+            kok = kok && bk <= bq && bq - bk < a.window_blocks;
+          }
+          const int qn = lq - 32 * t;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int qi = c_row(i, g);
+            const float2 sv = st[qi];
+            bool ok = kok & (qi < qn);
+            if constexpr (WMODE == 2) {
+              const int q = 32 * t + qi;
+              ok = ok & (krow <= q) & (q - krow < a.window_tokens);
+            }
+            x[i] = fast_exp2(fmaf(x[i], a.c2, -sv.x) + (ok ? 0.f : -__builtin_huge_valf()));
+            px[64 * i + lane] = x[i];
+          }
+        }
+      }
+      lds_barrier();  // P of the step in LDS for the pair's K wave
+      if (active) {
+        if (!vwave) {
+          // dS = P (dP - D_i)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) x[i] = px[64 * i + lane] * (x[i] - st[c_row(i, g)].y);
+        }
+        // V wave: dV^T += dO^T P; K wave: dK^T += Q^T dS
+        const __bf16* ts = vwave ? gs : qs;
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+          const bf16x8 xb = to_b(x, kc);
+#pragma unroll
+          for (int t2 = 0; t2 < L::kT; ++t2) acc[t2] = mfma_32x32x16(read_at<D>(ts, 16 * kc, t2, lane), xb, acc[t2]);
+        }
+      }
+    }
+    lds_barrier();  // every wave is done with the item's LDS before the next item's loads
+    if (krow < lk) {
+      float* o = (vwave ? a.dv : a.dk) + (size_t(kbeg + krow) * a.H + it.h) * D;
+      const float sc = vwave ? 1.f : a.inv_sqrt_d;
+#pragma unroll
+      for (int t2 = 0; t2 < L::kT; ++t2)
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+          float4 w;
+          w.x = acc[t2][4 * gi + 0] * sc;
+          w.y = acc[t2][4 * gi + 1] * sc;
+          w.z = acc[t2][4 * gi + 2] * sc;
+          w.w = acc[t2][4 * gi + 3] * sc;
+          *reinterpret_cast<float4*>(o + 32 * t2 + 8 * gi + 4 * g) = w;
+        }
+    }
+  }
+}
+
 template <int D, int WMODE, int ACT>
 hipError_t launch_w(const BwdArgs& a, int grid_q, int grid_k, bool wide, hipStream_t st) {
   hipLaunchKernelGGL((bwd_dq_mfma_kernel<D, WMODE, ACT>), dim3(grid_q), dim3(64 * kQWaves), 0, st, a);
+  if constexpr (ACT == ACT_SOFTMAX) {
+    // softmax: the pair-split kernel (64-key items)
+    hipLaunchKernelGGL((bwd_dkv_pair_kernel<D, WMODE>), dim3(grid_k), dim3(64 * kPairWaves), 0, st, a);
+    return hipGetLastError();
+  }
   if constexpr (WMODE == 0) {
     if (wide) {
       hipLaunchKernelGGL((bwd_dkv_mfma_kernel<D, WMODE, ACT, 4>), dim3(grid_k), dim3(64 * 4), 0, st, a);
@@ -690,9 +862,10 @@ hipError_t launch_dm(int act, int wmode, const BwdArgs& a, int grid_q, int grid_
 
 }  // namespace
 
-bool bwd_dkv_wide(int wmode, int B, int32_t total_kv) {
-  // four waves only without a window and with key runs of 128 or more on average
-  return wmode == 0 && int64_t(total_kv) >= int64_t(128) * B;
+bool bwd_dkv_wide(int act, int wmode, int B, int32_t total_kv) {
+  // GELU: four waves only without a window and with key runs of 128 or more
+  // on average (softmax takes the pair-split kernel, 64-key items)
+  return act == ACT_GELU && wmode == 0 && int64_t(total_kv) >= int64_t(128) * B;
 }
 
 int bwd_dkv_rows(bool wide) { return wide ? 128 : 64; }
