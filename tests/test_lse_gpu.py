@@ -7,8 +7,9 @@ arithmetic only: scores accumulated in fp32, exp2 within 1 ulp, a row sum of
 at most a few thousand fp32 terms (relative error below 2^-24 per term added,
 well under 1e-4 in total) and log2 within 1 ulp.  |lse_gpu - lse_ref| <= 2e-4
 (+ 1e-6 |lse_ref|) bounds that with margin.  Rows without keys are -inf on
-both sides, and asking for the log-sum-exp leaves the output bit for bit as it
-is without it."""
+both sides, nothing is written outside the buffer (NaN guard bands), and
+asking for the log-sum-exp leaves the output bit for bit as it is without
+it."""
 import sys
 
 import numpy as np
@@ -38,12 +39,21 @@ def adhoc(variant, dtype, lq, lk, H, D, window=0, seed=0):
     return w
 
 
+PAD = 4096  # NaN guard band on each side of the log-sum-exp buffer
+
+
 def run(w, with_lse=True):
     q, k, v, qo, ko, scales = device_tensors(w, "cuda")
-    lse = torch.full((w.total_q, w.H), float("nan"), dtype=torch.float32, device="cuda") if with_lse else None
+    lse = None
+    if with_lse:
+        n = w.total_q * w.H
+        big = torch.full((n + 2 * PAD,), float("nan"), dtype=torch.float32, device="cuda")
+        lse = big[PAD:PAD + n].view(w.total_q, w.H)
     out = forward(q, k, v, qo, ko, variant=w.variant, act=w.act, window=w.window, dtype=w.dtype,
                   scales=scales, check=True, lse=lse)
     torch.cuda.synchronize()
+    if with_lse:
+        assert torch.isnan(big[:PAD]).all() and torch.isnan(big[-PAD:]).all(), "log-sum-exp written outside"
     return out.cpu(), (lse.cpu().numpy().astype(np.float64) if with_lse else None)
 
 
