@@ -40,7 +40,8 @@
  *   values (the same pointer may be passed twice).  Buffers need 16-byte
  *   alignment.  In jagged_attn_fwd, q, out and q_scale may be NULL when
  *   total_q == 0, and k, v, k_scale and v_scale when total_kv == 0 (empty
- *   tensors); the offsets are always required.
+ *   tensors); in jagged_attn_bwd likewise q, dout and dq, and k, v, dk and
+ *   dv; the offsets are always required.
  *
  * Ownership.  The caller owns every buffer, including the workspace.  The
  * library allocates nothing inside jagged_attn_fwd and keeps only a per-device

@@ -453,7 +453,12 @@ int jagged_attn_bwd(const void* q, const void* k, const void* v, const void* dou
   if (io == nullptr) return JA_EINVAL;
   const int st = validate_bwd(B, H, D, variant, act, window, io->dtype, io->total_q, io->total_kv);
   if (st != JA_OK) return st;
-  if (!q || !k || !v || !dout || !q_offsets || !kv_offsets || !dq || !dk || !dv) return JA_EINVAL;
+  if (!q_offsets || !kv_offsets) return JA_EINVAL;
+  // Empty tensors may come with null data pointers, as in the forward: no
+  // kernel touches q, dout, dq without query rows, nor k, v, dk, dv without
+  // key rows.
+  if ((io->total_q > 0 && (!q || !dout || !dq)) || (io->total_kv > 0 && (!k || !v || !dk || !dv)))
+    return JA_EINVAL;
   const BwdLayout L = bwd_layout(B, H, act, io->total_q, io->total_kv);
   if (io->workspace == nullptr || io->workspace_bytes < L.total) return JA_EWORKSPACE;
   for (const void* p : {q, k, v, dout, static_cast<const void*>(dq), static_cast<const void*>(dk),

@@ -41,6 +41,9 @@ def run(variant, window, dtype, qo, ko, q, k, v, seed=0, act="softmax"):
         g = g.cpu().numpy().astype(np.float64)
         # (a gradient that is exactly zero -- dQ, dK with one key per query --
         # is compared against the inputs' unit scale instead)
+        if r.size == 0:  # (no rows: an empty gradient)
+            assert g.size == 0, name
+            continue
         scale = max(np.abs(r).max(), 1.0)
         err = np.abs(g - r).max() / scale
         assert np.isfinite(g).all(), name
@@ -73,6 +76,19 @@ def test_long_key_runs(variant, act, D):
     qo, ko, q, k, v = random_jagged(60 + D, lq, lk, 2, D)
     log(f"backward long key runs {variant} {act} D={D}")
     run(variant, 0, "bf16", qo, ko, q, k, v, seed=9, act=act)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_empty_key_or_query_tensors(dtype):
+    """No key rows at all (dQ is zero, dK and dV are empty) and no query rows
+    at all (dK and dV are zero): empty tensors, whose data pointers may be
+    null, are accepted as in the forward."""
+    qo, ko, q, k, v = random_jagged(71, [5, 40], [0, 0], 2, 64)
+    log(f"backward cross without keys {dtype}")
+    run("cross", 0, dtype, qo, ko, q, k, v, seed=11)
+    qo, ko, q, k, v = random_jagged(72, [0, 0], [10, 70], 2, 64)
+    log(f"backward cross without queries {dtype}")
+    run("cross", 0, dtype, qo, ko, q, k, v, seed=12)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
