@@ -258,7 +258,8 @@ size_t jagged_attn_bwd_workspace_size(int B, int H, int D, int variant, int act,
  * to x / 2^E (ties to even) after saturating to +-448; NaN inputs are not
  * supported.  The output is the exact input of jagged_attn_fwd with
  * JA_MXFP8_E4M3.  All pointers are device memory owned by the caller, 16-byte
- * aligned; nothing is allocated.  Asynchronous on `stream` (a hipStream_t or
+ * aligned (and may be NULL when rows == 0: nothing is done); nothing is
+ * allocated.  Asynchronous on `stream` (a hipStream_t or
  * NULL).  Returns JA_OK, JA_EINVAL (null or misaligned pointer, rows < 0, D not
  * a positive multiple of 32, dtype not JA_F32/JA_BF16) or JA_EHIP. */
 int jagged_attn_mx_quantize(const void *x, int dtype, int64_t rows, int D,

@@ -547,11 +547,13 @@ int jagged_attn_bwd(const void* q, const void* k, const void* v, const void* dou
 
 int jagged_attn_mx_quantize(const void* x, int dtype, int64_t rows, int D, uint8_t* codes, uint8_t* scales,
                             void* stream) {
-  if (x == nullptr || codes == nullptr || scales == nullptr) return JA_EINVAL;
   if (dtype != JA_F32 && dtype != JA_BF16) return JA_EINVAL;
   if (rows < 0 || D <= 0 || D % kMxBlock != 0) return JA_EINVAL;
+  // (no rows: nothing to do, and empty tensors may come with null pointers)
+  if (rows > 0 && (x == nullptr || codes == nullptr || scales == nullptr)) return JA_EINVAL;
   if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return JA_EINVAL;
   if (rows > (int64_t(1) << 40) / D) return JA_EINVAL;  // (keeps the grid in range)
+  if (rows == 0) return JA_OK;
   const int64_t n_blocks = rows * (D / kMxBlock);
   if (launch_mx_quant(dtype == JA_BF16, x, n_blocks, codes, scales, reinterpret_cast<hipStream_t>(stream)) !=
       hipSuccess)

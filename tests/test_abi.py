@@ -155,6 +155,7 @@ def test_mx_quantize_host_validation():
     assert q(D=0) == _lib.JA_EINVAL
     assert q(rows=-1) == _lib.JA_EINVAL
     assert q(x=4100) == _lib.JA_EINVAL
+    assert q(rows=0, x=0, c=0, s=0) == _lib.JA_OK  # no rows: nothing to do (empty tensors)
     assert q(rows=1 << 40) == _lib.JA_EINVAL
 
 
