@@ -110,3 +110,83 @@ def test_random_shape_forward_lse_backward(seed):
             log(f"  {form} {name} rel err {e:.3e}")
             assert np.isfinite(g.cpu().numpy()).all(), f"{form} {name} not finite"
             assert e <= gtol, f"{form} {name}: {e:.3e}"
+
+
+def draw_other(seed):
+    """GELU scores (no window) and MXFP8 inputs."""
+    rng = rng_for(2000 + seed)
+    kind = ["gelu", "mx"][seed % 2]
+    kinds = ["self", "cross", "pma"] if kind == "gelu" else ["self", "self_window", "cross", "pma"]
+    variant = kinds[int(rng.integers(len(kinds)))]
+    D = int(rng.choice([32, 64, 128]))
+    H = int(rng.integers(1, 4))
+    B = int(rng.integers(1, 9))
+    window = 64 * int(rng.integers(1, 9)) if variant == "self_window" else 0
+    if variant == "pma":
+        lq = [32] * B
+        lk = [int(rng.choice(LENGTHS + [700, 1500])) for _ in range(B)]
+    elif variant == "cross":
+        lq = [int(rng.choice(LENGTHS)) for _ in range(B)]
+        lk = [int(rng.choice([0, 1, 16, 40, 64, 65])) for _ in range(B)]
+        if sum(lq) == 0:
+            lq[0] = 33
+    else:
+        lq = [int(rng.choice(LENGTHS)) for _ in range(B)]
+        if sum(lq) == 0:
+            lq[0] = 33
+        lk = lq
+    act = "gelu_tanh" if kind == "gelu" else ["softmax", "gelu_tanh"][int(rng.integers(2))]
+    if window:
+        act = "softmax"
+    dtype = ["bf16", "f32"][int(rng.integers(2))] if kind == "gelu" else "mxfp8"
+    return ("self" if variant == "self_window" else variant), window, D, dtype, act, H, lq, lk
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shape_gelu_and_mxfp8(seed):
+    """GELU scores (forward and backward) and MXFP8 inputs (forward, and the
+    log-sum-exp where the shape gives it) on seeded random shapes."""
+    from recsys_jagged_attention_amd import JaggedAttnError, JA_EUNSUPPORTED
+    from recsys_jagged_attention_amd.inputs import Workload, mx_encode_e4m3, device_tensors
+    from parity_util import full_parity, oracle_values
+
+    variant, window, D, dtype, act, H, lq, lk = draw_other(seed)
+    log(f"seed {seed}: {variant} W={window} D={D} {dtype} {act} H={H} lq={lq} lk={lk}")
+    qo, ko, q, k, v = random_jagged(seed + 177, lq, lk, H, D)
+    w = Workload("random", variant, act, dtype, len(lq), H, D, window, qo, ko, q, k, v, seed)
+    if dtype == "mxfp8":
+        w.mx = {n: mx_encode_e4m3(x) for n, x in (("q", q), ("k", k), ("v", v))}
+    log(f"  out rel err {full_parity(w):.3e}")
+    if dtype == "mxfp8" and act == "softmax":
+        tq, tk, tv, tqo, tko, scales = device_tensors(w, "cuda")
+        lse = torch.empty((w.total_q, H), dtype=torch.float32, device="cuda")
+        try:
+            forward(tq, tk, tv, tqo, tko, variant=variant, act=act, window=window, dtype=dtype, scales=scales,
+                    check=True, lse=lse)
+        except JaggedAttnError as e:
+            assert e.status == JA_EUNSUPPORTED
+            log("  (no log-sum-exp for this MXFP8 shape)")
+        else:
+            oq, ok_, _ = oracle_values(w)
+            ref = oracle.gdpa_lse(oq, ok_, qo, ko, variant, window)
+            got = lse.cpu().numpy().astype(np.float64)
+            assert np.array_equal(got == -np.inf, ref == -np.inf)
+            fin = ref != -np.inf
+            lerr = float(np.abs(got[fin] - ref[fin]).max()) if fin.any() else 0.0
+            log(f"  lse abs err {lerr:.3e}")
+            assert lerr <= 2e-4 + 1e-6 * float(np.abs(ref[fin]).max() if fin.any() else 0.0)
+    if act == "gelu_tanh" and dtype != "mxfp8":
+        dout = rng_for(seed + 9).standard_normal(q.shape).astype(np.float32)
+        tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+        tq, tk, tv, tg = (torch.from_numpy(x).to(tdt) for x in (q, k, v, dout))
+        exact = [t.to(torch.float64).numpy() for t in (tq, tk, tv, tg)]
+        to = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+        grads = backward(tq.cuda(), tk.cuda(), tv.cuda(), tg.cuda(), to(qo), to(ko), variant=variant, act=act,
+                         dtype=dtype, check=True)
+        torch.cuda.synchronize()
+        gref = oracle.gdpa_backward(exact[0], exact[1], exact[2], exact[3], qo, ko, variant, act, 0)
+        gtol = 1e-5 if dtype == "f32" else 1e-2
+        for name, g, r in zip(("dq", "dk", "dv"), grads, gref):
+            e = rel(g.cpu().numpy().astype(np.float64), r, floor=1.0)
+            log(f"  {name} rel err {e:.3e}")
+            assert np.isfinite(g.cpu().numpy()).all() and e <= gtol, f"{name}: {e:.3e}"
