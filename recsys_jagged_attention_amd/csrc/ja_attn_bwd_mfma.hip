@@ -667,10 +667,13 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(2))) vo
   }
 }
 
-// Softmax dK/dV with the work of a 32-key group split over a wave pair: the
-// "V wave" forms S = Q K^T, the weights P from the stored statistics, and
-// accumulates dV^T += dO^T P; the "K wave" forms dP = dO V^T, takes P through
-// LDS, and accumulates dK^T += Q^T dS with dS = P (dP - D_i).  Each wave holds
+// dK/dV with the work of a 32-key group split over a wave pair: the "V wave"
+// forms S = Q K^T and the weights W (softmax: P from the stored statistics;
+// GELU: gelu(s) / Lk on the RMS-normalised scores) and accumulates
+// dV^T += dO^T W; the "K wave" forms dP = dO V^T, takes a factor F through
+// LDS (softmax: P; GELU: gelu'(s) r_q / Lk) and accumulates dK^T += Q^T dS
+// with dS = P (dP - D_i) (softmax) or F dP (GELU; dK then goes through the
+// key RMSNorm's backward).  Each wave holds
 // 64 accumulators and issues 16 MFMAs per query step, so two workgroups of
 // 4 waves (64-key items, 78.5 KB of LDS at D = 128) share a CU: two waves per
 // SIMD, one's VALU work under the other's MFMAs (the one-wave-per-SIMD form
@@ -679,16 +682,18 @@ __global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(2))) vo
 // has finished with.
 constexpr int kPairWaves = 4;  // 2 pairs x (V wave, K wave), 32 keys per pair
 
-template <int D, int WMODE>
+template <int D, int WMODE, int ACT>
 __global__ __launch_bounds__(64 * kPairWaves) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkv_pair_kernel(
     BwdArgs a) {
   using L = BT<D>;
+  constexpr bool kGelu = ACT == ACT_GELU;
+  static_assert(!kGelu || WMODE == 0, "GELU takes no window");
   using TK = Dma<D, 64>;
   using TQ = Dma<D, 32>;
   __shared__ __attribute__((aligned(1024))) unsigned char kvb[2][TK::kBytes];    // the item's K, V (64 rows)
   __shared__ __attribute__((aligned(1024))) unsigned char qb[2][2][TQ::kBytes];  // [stage][Q, dO]
-  __shared__ __attribute__((aligned(256))) float2 stb[2][32];                    // [stage] (lse, D_i)
-  __shared__ __attribute__((aligned(256))) float pxb[2][16][64];                 // [pair] P, lane-major
+  __shared__ __attribute__((aligned(256))) float2 stb[2][32];  // [stage] (lse, D_i); GELU: 64 floats, RMS factors
+  __shared__ __attribute__((aligned(256))) float pxb[2][16][64];  // [pair] P or the GELU factor, lane-major
   const __bf16* qg = reinterpret_cast<const __bf16*>(a.q);
   const __bf16* kg = reinterpret_cast<const __bf16*>(a.k);
   const __bf16* vg = reinterpret_cast<const __bf16*>(a.v);
@@ -739,11 +744,23 @@ __global__ __launch_bounds__(64 * kPairWaves) __attribute__((amdgpu_waves_per_eu
       dma_tile<D, 32, kPairWaves>(st, qbase + size_t(32 * t) * gstride, grow, valid, wave, lane);
       dma_tile<D, 32, kPairWaves>(st + TQ::kBytes, gbase + size_t(32 * t) * gstride, grow, valid, wave, lane);
       if (wave == 0) {
-        const unsigned row = unsigned(min(lane >> 1, valid - 1));
-        lds_dma4(sbase + size_t(32 * t) * a.H, (row * unsigned(a.H)) * 8u + 4u * unsigned(lane & 1),
-                 lds_st + stage * 256u);
+        if constexpr (kGelu) {
+          const unsigned row = unsigned(min(lane, valid - 1));
+          lds_dma4(a.rq + (size_t(qbeg) + 32 * t) * a.H + it.h, row * unsigned(a.H) * 4u, lds_st + stage * 256u);
+        } else {
+          const unsigned row = unsigned(min(lane >> 1, valid - 1));
+          lds_dma4(sbase + size_t(32 * t) * a.H, (row * unsigned(a.H)) * 8u + 4u * unsigned(lane & 1),
+                   lds_st + stage * 256u);
+        }
       }
     };
+
+    // GELU: RMS factor of this lane's key row times 1/sqrt(D); 1/Lk (loaded
+    // and waited for before the tile loads, see the dQ kernel)
+    const int kr = min(krow, lk - 1);
+    const float csc = kGelu ? a.rk[size_t(kbeg + kr) * a.H + it.h] * a.inv_sqrt_d : 0.f;
+    const float inv_lk = kGelu ? 1.0f / float(lk) : 0.f;
+    if constexpr (kGelu) wait_vm<0>();
 
     f32x16 acc[L::kT];  // dV^T (V wave) or dK^T (K wave) of the pair's 32 keys
 #pragma unroll
@@ -775,7 +792,20 @@ __global__ __launch_bounds__(64 * kPairWaves) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
         for (int cc = 0; cc < L::kS; ++cc)
           x = mfma_32x32x16(read_a<D>(as, kp, g, cc), read_a<D>(bs, 32 * pair + l32, g, cc), x);
-        if (vwave) {
+        if (vwave && kGelu) {
+          // W = gelu(s) / Lk for dV; F = gelu'(s) r_q / Lk for the K wave
+          const float* rq = reinterpret_cast<const float*>(st);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int qi = c_row(i, g);
+            const float ri = rq[qi];
+            const bool ok = 32 * t + qi < lq && krow < lk;
+            float gl, gp;
+            gelu_and_grad(x[i] * csc * ri, gl, gp);
+            x[i] = ok ? gl * inv_lk : 0.f;
+            px[64 * i + lane] = ok ? gp * inv_lk * ri : 0.f;
+          }
+        } else if (vwave) {
           // P from the stored log-sum-exp, masked without branches (the
           // mask enters as an added 0 or -inf under the raw exp2)
           bool kok = krow < lk;
@@ -801,9 +831,12 @@ __global__ __launch_bounds__(64 * kPairWaves) __attribute__((amdgpu_waves_per_eu
       lds_barrier();  // P of the step in LDS for the pair's K wave
       if (active) {
         if (!vwave) {
-          // dS = P (dP - D_i)
+          // dS = P (dP - D_i); GELU: F dP
 #pragma unroll
-          for (int i = 0; i < 16; ++i) x[i] = px[64 * i + lane] * (x[i] - st[c_row(i, g)].y);
+          for (int i = 0; i < 16; ++i) {
+            if constexpr (kGelu) x[i] = px[64 * i + lane] * x[i];
+            else x[i] = px[64 * i + lane] * (x[i] - st[c_row(i, g)].y);
+          }
         }
         // V wave: dV^T += dO^T P; K wave: dK^T += Q^T dS
         const __bf16* ts = vwave ? gs : qs;
@@ -816,18 +849,43 @@ __global__ __launch_bounds__(64 * kPairWaves) __attribute__((amdgpu_waves_per_eu
       }
     }
     lds_barrier();  // every wave is done with the item's LDS before the next item's loads
+    // dV^T is acc; dK^T is acc / sqrt(D) (GELU: then through the RMSNorm)
+    float osc = vwave ? 1.f : a.inv_sqrt_d;
+    if (kGelu && !vwave) {
+      // dk = c dKn - k c^3 (dKn . k) / D, dKn = acc / sqrt(D), c the key's RMS
+      // factor (the lane holds dims 32 t2 + 8 gi + 4 g + 0..3)
+      const float c = a.rk[size_t(kbeg + kr) * a.H + it.h];
+      const __bf16* krow_p = kg + (size_t(kbeg + kr) * a.H + it.h) * D;
+      float dot = 0.f;
+#pragma unroll
+      for (int t2 = 0; t2 < L::kT; ++t2) {
+        acc[t2] *= osc;
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dot = fmaf(acc[t2][4 * gi + e], float(krow_p[32 * t2 + 8 * gi + 4 * g + e]), dot);
+      }
+      const float c3 = c * c * c * sum_halves(dot) * (1.0f / D);
+#pragma unroll
+      for (int t2 = 0; t2 < L::kT; ++t2)
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[t2][4 * gi + e] = fmaf(c, acc[t2][4 * gi + e], -float(krow_p[32 * t2 + 8 * gi + 4 * g + e]) * c3);
+      osc = 1.f;
+    }
     if (krow < lk) {
       float* o = (vwave ? a.dv : a.dk) + (size_t(kbeg + krow) * a.H + it.h) * D;
-      const float sc = vwave ? 1.f : a.inv_sqrt_d;
 #pragma unroll
       for (int t2 = 0; t2 < L::kT; ++t2)
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi) {
           float4 w;
-          w.x = acc[t2][4 * gi + 0] * sc;
-          w.y = acc[t2][4 * gi + 1] * sc;
-          w.z = acc[t2][4 * gi + 2] * sc;
-          w.w = acc[t2][4 * gi + 3] * sc;
+          w.x = acc[t2][4 * gi + 0] * osc;
+          w.y = acc[t2][4 * gi + 1] * osc;
+          w.z = acc[t2][4 * gi + 2] * osc;
+          w.w = acc[t2][4 * gi + 3] * osc;
           *reinterpret_cast<float4*>(o + 32 * t2 + 8 * gi + 4 * g) = w;
         }
     }
@@ -837,18 +895,15 @@ __global__ __launch_bounds__(64 * kPairWaves) __attribute__((amdgpu_waves_per_eu
 template <int D, int WMODE, int ACT>
 hipError_t launch_w(const BwdArgs& a, int grid_q, int grid_k, bool wide, hipStream_t st) {
   hipLaunchKernelGGL((bwd_dq_mfma_kernel<D, WMODE, ACT>), dim3(grid_q), dim3(64 * kQWaves), 0, st, a);
-  if constexpr (ACT == ACT_SOFTMAX) {
-    // softmax: the pair-split kernel (64-key items)
-    hipLaunchKernelGGL((bwd_dkv_pair_kernel<D, WMODE>), dim3(grid_k), dim3(64 * kPairWaves), 0, st, a);
-    return hipGetLastError();
-  }
-  if constexpr (WMODE == 0) {
+  if constexpr (ACT == ACT_GELU && WMODE == 0) {
     if (wide) {
+      // GELU with long key runs: one wave per 32 keys, 128-key items, three stages
       hipLaunchKernelGGL((bwd_dkv_mfma_kernel<D, WMODE, ACT, 4>), dim3(grid_k), dim3(64 * 4), 0, st, a);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((bwd_dkv_mfma_kernel<D, WMODE, ACT, 2>), dim3(grid_k), dim3(64 * 2), 0, st, a);
+  // the pair-split kernel (64-key items): softmax, and GELU with short key runs
+  hipLaunchKernelGGL((bwd_dkv_pair_kernel<D, WMODE, ACT>), dim3(grid_k), dim3(64 * kPairWaves), 0, st, a);
   return hipGetLastError();
 }
 
