@@ -2,7 +2,8 @@
 for callers that cannot allocate) against jagged_attn_fwd on a caller
 workspace, through the C ABI: the outputs agree bit for bit and both are within
 the oracle's tolerance, over consecutive calls whose second input is smaller
-than the first (the scratch keeps the first call's contents)."""
+than the first (the scratch keeps the first call's contents).  Softmax calls
+also ask for the log-sum-exp output, which must agree bit for bit as well."""
 import ctypes
 
 import numpy as np
@@ -18,7 +19,7 @@ from parity_util import TOL, oracle_values, oracle_act, rel_err
 pytestmark = pytest.mark.gpu
 
 
-def call(fn, w, tensors, out, workspace=None, status=None):
+def call(fn, w, tensors, out, workspace=None, status=None, lse=None):
     q, k, v, qo, ko, scales = tensors
     io = _lib.JaIo()
     io.dtype = _lib.DTYPES[w.dtype]
@@ -31,6 +32,8 @@ def call(fn, w, tensors, out, workspace=None, status=None):
     io.total_q, io.total_kv = w.total_q, w.total_kv
     if status is not None:
         io.status = status.data_ptr()
+    if lse is not None:
+        io.lse = lse.data_ptr()
     return fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), qo.data_ptr(), ko.data_ptr(), w.B, w.H, w.D,
               _lib.VARIANTS[w.variant], _lib.ACTS[w.act], w.window, out.data_ptr(), io)
 
@@ -44,10 +47,16 @@ def run_both(w):
                                              _lib.DTYPES[w.dtype], w.total_q, w.total_kv)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     status = torch.full((1,), 999, dtype=torch.int32, device="cuda")
-    assert call(_lib.load().jagged_attn_fwd, w, tensors, out_ws, workspace=ws) == _lib.JA_OK
-    assert call(_lib.load().jagged_attn_fwd_noalloc, w, tensors, out_na, status=status) == _lib.JA_OK
+    soft = w.act == "softmax"
+    lse_ws, lse_na = ((torch.full((w.total_q, w.H), float("nan"), dtype=torch.float32, device="cuda")
+                       for _ in range(2)) if soft else (None, None))
+    assert call(_lib.load().jagged_attn_fwd, w, tensors, out_ws, workspace=ws, lse=lse_ws) == _lib.JA_OK
+    assert call(_lib.load().jagged_attn_fwd_noalloc, w, tensors, out_na, status=status, lse=lse_na) == _lib.JA_OK
     torch.cuda.synchronize()
     assert int(status.item()) == _lib.JA_OK
+    if soft:
+        assert not torch.isnan(lse_na).any()
+        assert torch.equal(lse_ws.view(torch.int32), lse_na.view(torch.int32))
     a, b = out_ws.cpu(), out_na.cpu()
     assert torch.equal(a.view(torch.int16) if dt == torch.bfloat16 else a.view(torch.int32),
                        b.view(torch.int16) if dt == torch.bfloat16 else b.view(torch.int32))
