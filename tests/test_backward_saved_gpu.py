@@ -77,10 +77,13 @@ def test_saved_cross_with_keyless_samples(dtype):
     run_saved("cross", 0, dtype, qo, ko, q, k, v, seed=1)
 
 
-def test_saved_f32_pma():
-    qo, ko, q, k, v = random_jagged(44, [32, 32, 32], [500, 1, 0], 2, 64)
-    log("saved backward pma f32")
-    run_saved("pma", 0, "f32", qo, ko, q, k, v, seed=2)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_saved_pma(dtype):
+    """PMA, with key runs long enough to be split (the merge kernel writes
+    their log-sum-exp), short ones and none."""
+    qo, ko, q, k, v = random_jagged(44, [32, 32, 32, 32], [500, 1, 0, 4100], 2, 64)
+    log(f"saved backward pma {dtype}")
+    run_saved("pma", 0, dtype, qo, ko, q, k, v, seed=2)
 
 
 def test_saved_block_window_workload_slice():
