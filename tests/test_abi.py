@@ -184,3 +184,23 @@ def test_noalloc_host_validation():
                                        ctypes.byref(j)) == _lib.JA_EUNSUPPORTED  # D
     assert lib.jagged_attn_fwd_noalloc(4096, 4096, 4096, 4096, 4096, 2, 1, 32, 0, 0, 0, 4096,
                                        None) == _lib.JA_EINVAL
+
+
+def test_ja_io_layout_matches_the_header(tmp_path):
+    """The ctypes mirror of ja_io (_lib.JaIo) has the header's field order,
+    offsets and size: a C program built from include/jagged_attn.h prints
+    offsetof of every field and sizeof(ja_io)."""
+    import subprocess
+    names = [f[0] for f in _lib.JaIo._fields_]
+    src = tmp_path / "layout.c"
+    body = "\n".join(f'  printf("{n} %zu\\n", offsetof(ja_io, {n}));' for n in names)
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "jagged_attn.h"\n'
+                   f'int main(void) {{\n{body}\n  printf("sizeof %zu\\n", sizeof(ja_io));\n  return 0;\n}}\n')
+    exe = tmp_path / "layout"
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run(["gcc", "-std=c99", "-I", inc, str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = dict(line.split() for line in out if line.strip())
+    for n in names:
+        assert int(got[n]) == getattr(_lib.JaIo, n).offset, n
+    assert int(got["sizeof"]) == ctypes.sizeof(_lib.JaIo)
