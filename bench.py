@@ -379,7 +379,7 @@ def run_backward(args):
     on_mfma = w.dtype == "bf16"
     bound, peak = ("mfma", PEAK_TFLOPS["bf16"]) if on_mfma else ("alu", PEAK_VALU_F32)
     kernels = (("bwd_rms_kernel + " if w.act != "softmax" else "") +
-               ("bwd_dq_mfma_kernel + bwd_dkv_pair_kernel (GELU with long key runs: bwd_dkv_mfma_kernel)"
+               ("bwd_dq_mfma_kernel + bwd_dkv_pair_kernel"
                 if on_mfma else "bwd_q_kernel + bwd_kv_kernel"))
     log(f"[bench] backward {w.name}: {ms_per_step * 1e3:.1f} us/step, kernels {kern_s * 1e6:.1f} us, "
         f"{achieved:.2f} useful TFLOP/s ({100 * achieved / peak:.1f}% of the {bound} peak {peak})")

@@ -25,10 +25,8 @@ hipError_t launch_attn_pp(int D, int act, bool cross, int in, const AttnArgs& a,
 bool pp_takes_mx8(int D, int act, bool self, int window_blocks);
 hipError_t launch_attn_bwd(int D, bool bf16, int act, int wmode, const BwdArgs& a, int64_t rows_q, int64_t rows_k,
                            int grid_q, int grid_k, hipStream_t st);
-hipError_t launch_attn_bwd_mfma(int D, int act, int wmode, const BwdArgs& a, int grid_q, int grid_k, bool wide,
+hipError_t launch_attn_bwd_mfma(int D, int act, int wmode, const BwdArgs& a, int grid_q, int grid_k,
                                 hipStream_t st);
-bool bwd_dkv_wide(int act, int wmode, int B, int32_t total_kv);  // the 4-wave shape of the MFMA dK/dV kernel?
-int bwd_dkv_rows(bool wide);                            // key rows per item of that kernel
 hipError_t launch_bwd_rms(int D, bool bf16, const BwdArgs& a, int64_t rows_q, int64_t rows_k, hipStream_t st);
 hipError_t launch_mx_quant(bool bf16, const void* x, int64_t n_blocks, uint8_t* codes, uint8_t* scales,
                            hipStream_t st);
@@ -477,7 +475,6 @@ int jagged_attn_bwd(const void* q, const void* k, const void* v, const void* dou
   // bf16 inputs on the matrix cores; fp32 inputs on the fp32 VALU kernels
   const bool mfma = io->dtype == JA_BF16;
   const int wmode = variant == JA_SLIDING ? 2 : (variant == JA_SELF && window > 0 ? 1 : 0);
-  const bool wide = bwd_dkv_wide(act == JA_SOFTMAX ? ACT_SOFTMAX : ACT_GELU, wmode, B, io->total_kv);
   // Two plans, in one launch: over query tiles, and over key tiles (the same
   // plan on swapped offsets).
   PlanArgs plans[2];
@@ -490,7 +487,7 @@ int jagged_attn_bwd(const void* q, const void* k, const void* v, const void* dou
     pa.H = H;
     pa.total_q = pass == 0 ? io->total_q : io->total_kv;
     pa.total_kv = pass == 0 ? io->total_kv : io->total_q;
-    pa.bm = mfma ? (pass == 0 ? kBwdRowsMfmaQ : bwd_dkv_rows(wide)) : kBwdRows;
+    pa.bm = mfma && pass == 0 ? kBwdRowsMfmaQ : kBwdRows;
     pa.kvc = 0;
     pa.self_check = self;
     pa.max_items = pass == 0 ? L.max_q : L.max_k;
@@ -534,7 +531,7 @@ int jagged_attn_bwd(const void* q, const void* k, const void* v, const void* dou
       launch_bwd_rms(D, true, ba, int64_t(io->total_q) * H, int64_t(io->total_kv) * H, stream) != hipSuccess)
     return JA_EHIP;
   const hipError_t e = mfma ? launch_attn_bwd_mfma(D, act == JA_SOFTMAX ? ACT_SOFTMAX : ACT_GELU, wmode, ba,
-                                                   grid_q, grid_k, wide, stream)
+                                                   grid_q, grid_k, stream)
                            : launch_attn_bwd(D, io->dtype == JA_BF16, act == JA_SOFTMAX ? ACT_SOFTMAX : ACT_GELU,
                                              wmode, ba, int64_t(io->total_q) * H, int64_t(io->total_kv) * H, grid_q,
                                              grid_k, stream);

@@ -18,10 +18,11 @@
 //    keeps the online max, sum and sum of p * dP (giving the log-sum-exp and
 //    D_i, stored for the second kernel), a second pass accumulates
 //    dQ^T += K^T dS^T.
-//  * bwd_dkv_mfma_kernel, 2 waves, 64 key rows per item (kept in LDS).  Lane column =
-//    key.  Over the 32-query tiles that see the item it forms S = Q K^T and
-//    dP = dO V^T, P from the stored statistics, then dV^T += dO^T P and
-//    dK^T += Q^T dS.
+//  * bwd_dkv_pair_kernel, 4 waves, 64 key rows per item (kept in LDS).  Lane
+//    column = key.  Each 32-key group is split over a wave pair: over the
+//    32-query tiles that see the item, one wave forms S = Q K^T, the weights
+//    and dV^T += dO^T W, the other dP = dO V^T and, with a factor handed over
+//    through LDS, dK^T += Q^T dS.
 // The score products read their A rows in key_perm order so that the result
 // registers of lane half h hold, for each 16-row step, the 8 contiguous rows
 // 8h..8h+7: exactly the B operand of the next product (no shuffle).  The
@@ -161,33 +162,6 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 constexpr int kQWaves = 4;  // dq kernel: 4 waves x 32 query rows (128-row items)
-// dK/dV kernel shape: KW waves x 32 key rows per item, and query-tile stages.
-// KW = 4 (no window, long key runs): 128-row items, 123 KB of LDS at D = 128,
-// and three stages, two query tiles loading while one is used, each tile
-// serving 128 keys.  KW = 2 otherwise: with a window the four waves' query
-// ranges would differ (their union walks tiles that half of them skip), and
-// with short key runs (cross-attention's 16-64 keys) half of a 128-row item's
-// waves would hold the CU's LDS with nothing to do; 64-row items and two
-// stages, two workgroups per CU.
-constexpr int dkv_stages(int kw) { return kw == 4 ? 3 : 2; }
-
-// Loads wave w of the dK/dV kernel issues for one query tile: its share of
-// the Q and dO tiles, plus the statistics (or GELU: RMS factor) row on wave 0.
-template <int D, int KW>
-constexpr int dkv_step_loads(int w) {
-  return 2 * Dma<D, 32>::count(w, KW) + (w == 0 ? 1 : 0);
-}
-
-// Wait until at most one query tile's loads of this wave are outstanding
-// (the wave index is uniform: a scalar branch to an immediate wait).
-template <int D, int KW>
-__device__ __forceinline__ void wait_dkv_one_step(int wave) {
-  static_assert(KW == 2 || KW == 4, "two or four waves");
-  if (wave == 0) wait_vm<dkv_step_loads<D, KW>(0)>();
-  else if (KW == 2 || wave == 1) wait_vm<dkv_step_loads<D, KW>(1)>();
-  else if (wave == 2) wait_vm<dkv_step_loads<D, KW>(2)>();
-  else wait_vm<dkv_step_loads<D, KW>(3)>();
-}
 
 template <int D, int WMODE, int ACT>
 __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_mfma_kernel(BwdArgs a) {
@@ -451,235 +425,19 @@ __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)
   }
 }
 
-template <int D, int WMODE, int ACT, int KW>
-__global__ __launch_bounds__(64 * KW) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dkv_mfma_kernel(BwdArgs a) {
-  constexpr int kKWaves = KW, kKStages = dkv_stages(KW);
-  static_assert(KW == 2 || (KW == 4 && WMODE == 0), "four waves only without a window");
-  using L = BT<D>;
-  constexpr bool kGelu = ACT == ACT_GELU;
-  using TK = Dma<D, 32 * kKWaves>;
-  using TQ = Dma<D, 32>;
-  // LDS: the item's K and V (32 kKWaves rows), and kKStages stages of a
-  // 32-row query tile (Q, dO, statistics)
-  __shared__ __attribute__((aligned(1024))) unsigned char kvb[2][TK::kBytes];           // the item's K, V
-  __shared__ __attribute__((aligned(1024))) unsigned char qb[kKStages][2][TQ::kBytes];  // [stage][Q, dO]
-  __shared__ __attribute__((aligned(256))) float2 stb[kKStages][32];  // [stage] (lse, D_i); GELU: RMS factors
-  const __bf16* qg = reinterpret_cast<const __bf16*>(a.q);
-  const __bf16* kg = reinterpret_cast<const __bf16*>(a.k);
-  const __bf16* vg = reinterpret_cast<const __bf16*>(a.v);
-  const __bf16* gg = reinterpret_cast<const __bf16*>(a.dout);
-  const int lane = threadIdx.x & 63, l32 = lane & 31, g = lane >> 5;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // (scalar: uniform loops)
-  const int kp = key_perm(l32);
-  const size_t gstride = size_t(a.H) * D;
-  const unsigned grow = unsigned(gstride) * 2u;
-  const unsigned lds_kv = lds_addr_of(&kvb[0][0]), lds_q = lds_addr_of(&qb[0][0][0]);
-  const unsigned lds_st = lds_addr_of(&stb[0][0]);
-  const __bf16* kst = reinterpret_cast<const __bf16*>(&kvb[0][0]);
-  const __bf16* vst = reinterpret_cast<const __bf16*>(&kvb[1][0]);
-  const int n_items = a.hdr_k->n_items;
-  for (int idx = blockIdx.x; idx < n_items; idx += gridDim.x) {
-    // (items over key tiles: the plan ran on the swapped offsets, so the
-    // record's "query" fields describe keys and its "key" fields queries)
-    const WorkItem it = a.items_k[idx];
-    const int lk = it.lq, lq = it.lk, kbeg = it.qbeg, qbeg = it.kbeg;
-    const int k0 = it.q0 + 32 * wave;
-    const int krow = k0 + l32;
-    int qlo, qhi;
-    wave_queries<WMODE>(a, k0, lq, lk, qlo, qhi);
-    const int wt_lo = qlo / 32, wt_hi = qhi > qlo ? (qhi + 31) / 32 : wt_lo;
-    int t_lo = 1 << 30, t_hi = 0;
-    for (int w = 0; w < kKWaves; ++w) {
-      int lo, hi;
-      wave_queries<WMODE>(a, it.q0 + 32 * w, lq, lk, lo, hi);
-      if (hi > lo) {
-        t_lo = min(t_lo, lo / 32);
-        t_hi = max(t_hi, (hi + 31) / 32);
-      }
-    }
-    if (t_lo > t_hi) t_lo = t_hi;
-    const int nt = t_hi - t_lo;
-    const __bf16* qbase = qg + size_t(qbeg) * gstride + size_t(it.h) * D;
-    const __bf16* gbase = gg + size_t(qbeg) * gstride + size_t(it.h) * D;
-    const float2* sbase = a.stats + size_t(qbeg) * a.H + it.h;
-
-    // Query tile t_lo + s into stage s % kKStages: Q, dO and the statistics.
-    auto issue_q = [&](int s) __attribute__((always_inline)) {
-      const int t = t_lo + s;
-      const int valid = min(32, lq - 32 * t);
-      const unsigned stage = unsigned(s % kKStages);
-      const unsigned st = lds_q + stage * 2u * TQ::kBytes;
-      dma_tile<D, 32, kKWaves>(st, qbase + size_t(32 * t) * gstride, grow, valid, wave, lane);
-      dma_tile<D, 32, kKWaves>(st + TQ::kBytes, gbase + size_t(32 * t) * gstride, grow, valid, wave, lane);
-      if (wave == 0) {
-        if constexpr (kGelu) {
-          const unsigned row = unsigned(min(lane, valid - 1));
-          lds_dma4(a.rq + (size_t(qbeg) + 32 * t) * a.H + it.h, row * unsigned(a.H) * 4u,
-                   lds_st + stage * 256u);
-        } else {
-          const unsigned row = unsigned(min(lane >> 1, valid - 1));
-          lds_dma4(sbase + size_t(32 * t) * a.H, (row * unsigned(a.H)) * 8u + 4u * unsigned(lane & 1),
-                   lds_st + stage * 256u);
-        }
-      }
-    };
-
-    // GELU: RMS factor of this lane's key row times 1/sqrt(D); 1/Lk
-    const int kr = min(krow, lk - 1);
-    const float csc = kGelu ? a.rk[size_t(kbeg + kr) * a.H + it.h] * a.inv_sqrt_d : 0.f;
-    const float inv_lk = kGelu ? 1.0f / float(lk) : 0.f;
-    if constexpr (kGelu) wait_vm<0>();  // (complete before the tile loads; see the dQ kernel)
-    f32x16 dk[L::kT], dv[L::kT];
-#pragma unroll
-    for (int t2 = 0; t2 < L::kT; ++t2) {
-      dk[t2] = f32x16{};
-      dv[t2] = f32x16{};
-    }
-    if (nt > 0) {
-      // the item's K and V rows stay in LDS (B operands read per use: the
-      // dK^T and dV^T accumulators take the registers); query tiles
-      // 0 .. kKStages - 2 start loading
-      const int valid = min(32 * kKWaves, lk - it.q0);
-      const size_t off = size_t(kbeg + it.q0) * gstride + size_t(it.h) * D;
-      dma_tile<D, 32 * kKWaves, kKWaves>(lds_kv, kg + off, grow, valid, wave, lane);
-      dma_tile<D, 32 * kKWaves, kKWaves>(lds_kv + TK::kBytes, vg + off, grow, valid, wave, lane);
-      issue_q(0);
-      if (kKStages == 3 && nt > 1) issue_q(1);
-    }
-    for (int s = 0; s < nt; ++s) {
-      // Tile s has landed once only the loads of the tiles after it are
-      // outstanding (loads complete in order; the item's K and V came first):
-      // with three stages tile s + 1 may still load, with two none is issued.
-      if (kKStages == 3 && s + 1 < nt) wait_dkv_one_step<D, kKWaves>(wave);
-      else wait_vm<0>();
-      // Tile s (and the item's K, V) in LDS for every wave, and every wave is
-      // done with step s - 1: its stage takes tile s + kKStages - 1 now.
-      lds_barrier();
-      if (s + kKStages - 1 < nt) issue_q(s + kKStages - 1);
-      const int t = t_lo + s;
-      const int stage = s % kKStages;
-      if (t >= wt_lo && t < wt_hi) {
-        const __bf16* qs = reinterpret_cast<const __bf16*>(&qb[stage][0][0]);
-        const __bf16* gs = reinterpret_cast<const __bf16*>(&qb[stage][1][0]);
-        const float2* st = &stb[stage][0];
-        f32x16 sc = {}, dp = {};
-#pragma unroll
-        for (int cc = 0; cc < L::kS; ++cc) {
-          sc = mfma_32x32x16(read_a<D>(qs, kp, g, cc), read_a<D>(kst, 32 * wave + l32, g, cc), sc);
-          dp = mfma_32x32x16(read_a<D>(gs, kp, g, cc), read_a<D>(vst, 32 * wave + l32, g, cc), dp);
-        }
-        if constexpr (kGelu) {
-          // weights gelu(s) / Lk for dV, dSn = gelu'(s) dP / Lk times the
-          // query's RMS factor for dKn = dSn^T Qn / sqrt(D)
-          const float* rq = reinterpret_cast<const float*>(st);
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int qi = c_row(i, g);
-            const float ri = rq[qi];
-            const bool ok = 32 * t + qi < lq && krow < lk;
-            float gl, gp;
-            gelu_and_grad(sc[i] * csc * ri, gl, gp);
-            sc[i] = ok ? gl * inv_lk : 0.f;
-            dp[i] = ok ? gp * dp[i] * inv_lk * ri : 0.f;
-          }
-        } else {
-          // Mask without branches (bitwise tests, statistics read for every
-          // element, a masked element takes exp2(-inf) = 0).  A block window
-          // is the same for the step's 32 queries (one block: 32 t .. 32 t + 31
-          // lie in block t / 2) and this lane's key.
-          bool kok = krow < lk;
-          if constexpr (WMODE == 1) {
-            const int bq = t >> 1, bk = krow / kBlock;
-            kok = kok && bk <= bq && bq - bk < a.window_blocks;
-          }
-          const int qn = lq - 32 * t;  // queries of the step that exist: qi < qn
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int qi = c_row(i, g);
-            const float2 sv = st[qi];
-            bool ok = kok & (qi < qn);
-            if constexpr (WMODE == 2) {
-              const int q = 32 * t + qi;
-              ok = ok & (krow <= q) & (q - krow < a.window_tokens);
-            }
-            // (the mask enters as an added 0 or -inf: a select with the LDS
-            // value as an operand would be turned into a branch around its load)
-            const float p = fast_exp2(fmaf(sc[i], a.c2, -sv.x) + (ok ? 0.f : -__builtin_huge_valf()));
-            sc[i] = p;
-            dp[i] = p * (dp[i] - sv.y);
-          }
-        }
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-          const bf16x8 pb = to_b(sc, kc), db = to_b(dp, kc);
-#pragma unroll
-          for (int t2 = 0; t2 < L::kT; ++t2) {
-            dv[t2] = mfma_32x32x16(read_at<D>(gs, 16 * kc, t2, lane), pb, dv[t2]);
-            dk[t2] = mfma_32x32x16(read_at<D>(qs, 16 * kc, t2, lane), db, dk[t2]);
-          }
-          __builtin_amdgcn_sched_barrier(0);  // (bounds the operand reads in flight: registers)
-        }
-      }
-    }
-    lds_barrier();  // every wave is done with the item's LDS before the next item's loads
-#pragma unroll
-    for (int t2 = 0; t2 < L::kT; ++t2) dk[t2] *= a.inv_sqrt_d;
-    if constexpr (kGelu) {
-      // through the RMSNorm: dk = c dkn - k c^3 (dkn . k) / D (dims as in the dQ kernel)
-      const float c = a.rk[size_t(kbeg + kr) * a.H + it.h];
-      const __bf16* krow_p = kg + (size_t(kbeg + kr) * a.H + it.h) * D;
-      float dot = 0.f;
-#pragma unroll
-      for (int t2 = 0; t2 < L::kT; ++t2)
-#pragma unroll
-        for (int gi = 0; gi < 4; ++gi)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) dot = fmaf(dk[t2][4 * gi + e], float(krow_p[32 * t2 + 8 * gi + 4 * g + e]), dot);
-      const float c3 = c * c * c * sum_halves(dot) * (1.0f / D);
-#pragma unroll
-      for (int t2 = 0; t2 < L::kT; ++t2)
-#pragma unroll
-        for (int gi = 0; gi < 4; ++gi)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            dk[t2][4 * gi + e] = fmaf(c, dk[t2][4 * gi + e], -float(krow_p[32 * t2 + 8 * gi + 4 * g + e]) * c3);
-    }
-    if (krow < lk) {
-      float* odk = a.dk + (size_t(kbeg + krow) * a.H + it.h) * D;
-      float* odv = a.dv + (size_t(kbeg + krow) * a.H + it.h) * D;
-#pragma unroll
-      for (int t2 = 0; t2 < L::kT; ++t2)
-#pragma unroll
-        for (int gi = 0; gi < 4; ++gi) {
-          float4 wk, wv;
-          wk.x = dk[t2][4 * gi + 0];
-          wk.y = dk[t2][4 * gi + 1];
-          wk.z = dk[t2][4 * gi + 2];
-          wk.w = dk[t2][4 * gi + 3];
-          wv.x = dv[t2][4 * gi + 0];
-          wv.y = dv[t2][4 * gi + 1];
-          wv.z = dv[t2][4 * gi + 2];
-          wv.w = dv[t2][4 * gi + 3];
-          *reinterpret_cast<float4*>(odk + 32 * t2 + 8 * gi + 4 * g) = wk;
-          *reinterpret_cast<float4*>(odv + 32 * t2 + 8 * gi + 4 * g) = wv;
-        }
-    }
-  }
-}
-
 // dK/dV with the work of a 32-key group split over a wave pair: the "V wave"
 // forms S = Q K^T and the weights W (softmax: P from the stored statistics;
 // GELU: gelu(s) / Lk on the RMS-normalised scores) and accumulates
 // dV^T += dO^T W; the "K wave" forms dP = dO V^T, takes a factor F through
 // LDS (softmax: P; GELU: gelu'(s) r_q / Lk) and accumulates dK^T += Q^T dS
 // with dS = P (dP - D_i) (softmax) or F dP (GELU; dK then goes through the
-// key RMSNorm's backward).  Each wave holds
-// 64 accumulators and issues 16 MFMAs per query step, so two workgroups of
-// 4 waves (64-key items, 78.5 KB of LDS at D = 128) share a CU: two waves per
-// SIMD, one's VALU work under the other's MFMAs (the one-wave-per-SIMD form
-// above leaves both exposed).  Query tiles in two stages; the next tile's
-// loads are issued after the step's first barrier, into the stage every wave
-// has finished with.
+// key RMSNorm's backward).  Each wave holds 64 accumulators and issues 16
+// MFMAs per query step, so two workgroups of 4 waves (64-key items, 78.5 KB
+// of LDS at D = 128) share a CU: two waves per SIMD, one's VALU work under the
+// other's MFMAs (one wave forming all four products of its keys holds 128
+// accumulators and runs alone on its SIMD).  Query tiles in two stages; the
+// next tile's loads are issued after the step's first barrier, into the stage
+// every wave has finished with.
 constexpr int kPairWaves = 4;  // 2 pairs x (V wave, K wave), 32 keys per pair
 
 template <int D, int WMODE, int ACT>
@@ -893,43 +651,27 @@ __global__ __launch_bounds__(64 * kPairWaves) __attribute__((amdgpu_waves_per_eu
 }
 
 template <int D, int WMODE, int ACT>
-hipError_t launch_w(const BwdArgs& a, int grid_q, int grid_k, bool wide, hipStream_t st) {
+hipError_t launch_w(const BwdArgs& a, int grid_q, int grid_k, hipStream_t st) {
   hipLaunchKernelGGL((bwd_dq_mfma_kernel<D, WMODE, ACT>), dim3(grid_q), dim3(64 * kQWaves), 0, st, a);
-  if constexpr (ACT == ACT_GELU && WMODE == 0) {
-    if (wide) {
-      // GELU with long key runs: one wave per 32 keys, 128-key items, three stages
-      hipLaunchKernelGGL((bwd_dkv_mfma_kernel<D, WMODE, ACT, 4>), dim3(grid_k), dim3(64 * 4), 0, st, a);
-      return hipGetLastError();
-    }
-  }
-  // the pair-split kernel (64-key items): softmax, and GELU with short key runs
   hipLaunchKernelGGL((bwd_dkv_pair_kernel<D, WMODE, ACT>), dim3(grid_k), dim3(64 * kPairWaves), 0, st, a);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_dm(int act, int wmode, const BwdArgs& a, int grid_q, int grid_k, bool wide, hipStream_t st) {
-  if (act == ACT_GELU) return launch_w<D, 0, ACT_GELU>(a, grid_q, grid_k, wide, st);  // (no window with GELU)
-  if (wmode == 1) return launch_w<D, 1, ACT_SOFTMAX>(a, grid_q, grid_k, false, st);
-  if (wmode == 2) return launch_w<D, 2, ACT_SOFTMAX>(a, grid_q, grid_k, false, st);
-  return launch_w<D, 0, ACT_SOFTMAX>(a, grid_q, grid_k, wide, st);
+hipError_t launch_dm(int act, int wmode, const BwdArgs& a, int grid_q, int grid_k, hipStream_t st) {
+  if (act == ACT_GELU) return launch_w<D, 0, ACT_GELU>(a, grid_q, grid_k, st);  // (no window with GELU)
+  if (wmode == 1) return launch_w<D, 1, ACT_SOFTMAX>(a, grid_q, grid_k, st);
+  if (wmode == 2) return launch_w<D, 2, ACT_SOFTMAX>(a, grid_q, grid_k, st);
+  return launch_w<D, 0, ACT_SOFTMAX>(a, grid_q, grid_k, st);
 }
 
 }  // namespace
 
-bool bwd_dkv_wide(int act, int wmode, int B, int32_t total_kv) {
-  // GELU: four waves only without a window and with key runs of 128 or more
-  // on average (softmax takes the pair-split kernel, 64-key items)
-  return act == ACT_GELU && wmode == 0 && int64_t(total_kv) >= int64_t(128) * B;
-}
-
-int bwd_dkv_rows(bool wide) { return wide ? 128 : 64; }
-
-hipError_t launch_attn_bwd_mfma(int D, int act, int wmode, const BwdArgs& a, int grid_q, int grid_k, bool wide,
+hipError_t launch_attn_bwd_mfma(int D, int act, int wmode, const BwdArgs& a, int grid_q, int grid_k,
                                 hipStream_t st) {
-  if (D == 32) return launch_dm<32>(act, wmode, a, grid_q, grid_k, wide, st);
-  if (D == 64) return launch_dm<64>(act, wmode, a, grid_q, grid_k, wide, st);
-  return launch_dm<128>(act, wmode, a, grid_q, grid_k, wide, st);
+  if (D == 32) return launch_dm<32>(act, wmode, a, grid_q, grid_k, st);
+  if (D == 64) return launch_dm<64>(act, wmode, a, grid_q, grid_k, st);
+  return launch_dm<128>(act, wmode, a, grid_q, grid_k, st);
 }
 
 }  // namespace ja

@@ -92,11 +92,7 @@ hipError_t launch_combine(int, const CombineArgs&, hipStream_t) { return hipSucc
 hipError_t launch_attn_bwd(int, bool, int, int, const BwdArgs&, int64_t, int64_t, int, int, hipStream_t) {
   return hipSuccess;
 }
-hipError_t launch_attn_bwd_mfma(int, int, int, const BwdArgs&, int, int, bool, hipStream_t) { return hipSuccess; }
-bool bwd_dkv_wide(int act, int wmode, int B, int32_t total_kv) {
-  return act != 0 && wmode == 0 && int64_t(total_kv) >= int64_t(128) * B;
-}
-int bwd_dkv_rows(bool wide) { return wide ? 128 : 64; }
+hipError_t launch_attn_bwd_mfma(int, int, int, const BwdArgs&, int, int, hipStream_t) { return hipSuccess; }
 hipError_t launch_bwd_rms(int, bool, const BwdArgs&, int64_t, int64_t, hipStream_t) { return hipSuccess; }
 hipError_t launch_mx_quant(bool, const void*, int64_t, uint8_t*, uint8_t*, hipStream_t) { return hipSuccess; }
 }  // namespace ja
